@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark: grouped / pointer-array bf16 GEMM, W4A16 GEMM and implicit-GEMM
+conv fprop on one MI355X.
+
+A step is one pointer-array GEMM launch over L = 16 separately allocated
+M = N = K = 1024 bf16 problems (beta = 0): the library's dense mainloop run
+by its persistent scheduler.  The inputs rotate through enough distinct
+copies that every step reads its operands from HBM, not from the 256 MB
+Infinity Cache.  The JSON line also reports the other workloads (grouped
+fp16, MoE grouped bf16, W4A16 at M = 16 / 128 / 1024 / 4096, conv fprop),
+each against its own roofline, and the fp64 CPU oracle timed on a bounded
+sample of the headline workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_16 = 2516.6  # TFLOP/s, dense fp16 / bf16: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_HBM = 8000.0  # GB/s
+MALL_BYTES = 256 << 20
+ROTATE_TARGET = 512 << 20
+METRIC = "TFLOP/s and % of MFMA peak: grouped bf16 GEMM, w4a16 GEMM, conv fprop"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def copies_for(ws_bytes: int) -> int:
+    return 1 if ws_bytes >= ROTATE_TARGET else int(math.ceil(ROTATE_TARGET / ws_bytes))
+
+
+def time_launches(torch, fn, n_copies, warmup, iters):
+    """Average ms per launch over `iters` back-to-back launches (cycling over
+    the rotating copies), HIP events on the launch stream."""
+    for i in range(warmup):
+        fn(i % n_copies)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(iters):
+        fn(i % n_copies)
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / iters
+
+
+def roof(flops, bytes_, ms):
+    t = ms * 1e-3
+    tf = flops / t / 1e12
+    gbs = bytes_ / t / 1e9
+    return dict(us=round(ms * 1e3, 3), tflops=round(tf, 2), frac_mfma=round(tf / PEAK_MFMA_16, 4),
+                gbps=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM, 4),
+                roofline_frac=round(max(flops / (PEAK_MFMA_16 * 1e12), bytes_ / (PEAK_HBM * 1e9)) / t, 4))
+
+
+def t16(torch, bits, dtype, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(dtype).to(dev)
+
+
+# --------------------------------------------------------------------------
+def setup_ptr_array(torch, gmi, gi, dev, L=16, M=1024, N=1024, K=1024):
+    A, B = gi.ptr_array_bf16(L=L, M=M, N=N, K=K)
+    ws = 3 * L * M * K * 2
+    R = copies_for(ws)
+    sets = []
+    for r in range(R):
+        Ad = [t16(torch, a, torch.bfloat16, dev) for a in A]
+        Bd = [t16(torch, b, torch.bfloat16, dev) for b in B]
+        Dd = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+        sets.append((gmi.pointer_array(Ad, dev), gmi.pointer_array(Bd, dev), gmi.pointer_array(Dd, dev), Ad, Bd, Dd))
+
+    def fn(i):
+        pa, pb, pd = sets[i][:3]
+        gmi.gemm_ptr_array(L, M, N, K, pa, K, pb, K, None, N, pd, N, torch.bfloat16, 1.0, 0.0)
+
+    return fn, R, 2.0 * L * M * N * K, ws, (A, B, sets)
+
+
+def cpu_baseline(gi, A, B, budget_s=12.0):
+    """The oracle, as it stands, on batches of the headline workload (cycling
+    over the 16) until about budget_s of host time has been spent."""
+    import oracle
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    done, flops, t0 = 0, 0.0, time.perf_counter()
+    while True:
+        oracle.gemm(A[done % len(A)], B[done % len(B)], dtype="bf16")
+        done += 1
+        flops += 2.0 * A[0].shape[0] * B[0].shape[0] * A[0].shape[1]
+        if time.perf_counter() - t0 > budget_s:
+            break
+    sec = time.perf_counter() - t0
+    return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} batch products of 1024^3 bf16 inputs in fp64 (cycling over the 16 batches), "
+                      f"{sec:.1f} s"}
+
+
+def bench_workloads(torch, gmi, gi, dev, args):
+    out = {}
+    # 1. grouped fp16, 4 groups, beta 0.5 (launch-latency bound)
+    probs = gi.grouped_f16()
+    As = [t16(torch, p["A"], torch.float16, dev) for p in probs]
+    Bs = [t16(torch, p["B"], torch.float16, dev) for p in probs]
+    Cs = [t16(torch, p["C"], torch.float16, dev) for p in probs]
+    Ds = [torch.empty((p["M"], p["N"]), dtype=torch.float16, device=dev) for p in probs]
+    table = gmi.make_problems(As, Bs, Cs, Ds)
+    wsb = torch.empty(gmi.workspace_bytes(4), dtype=torch.uint8, device=dev)
+    fl = sum(2.0 * p["M"] * p["N"] * p["K"] for p in probs)
+    by = sum(2 * (p["M"] * p["K"] + p["N"] * p["K"] + 2 * p["M"] * p["N"]) for p in probs)
+    ms = time_launches(torch, lambda i: gmi.gemm_grouped_raw(table, 4, gmi.GMI_F16, 1.0, 0.5, wsb), 1, 20, 500)
+    out["grouped_f16_4groups"] = dict(roof(fl, by, ms), bound="launch")
+    log("bench: grouped fp16 done")
+
+    # 3. MoE grouped bf16, 16384 tokens over 128 experts, N 2048, K 4096
+    counts = gi.moe_counts()
+    N, K = 2048, 4096
+    A = t16(torch, gi.moe_activations(), torch.bfloat16, dev)
+    D = torch.empty((int(counts.sum()), N), dtype=torch.bfloat16, device=dev)
+    Bw = [t16(torch, gi.moe_expert_weight(g), torch.bfloat16, dev) for g in range(len(counts))]
+    off = np.concatenate([[0], np.cumsum(counts)])
+    table = gmi.make_problems([A[off[g]:off[g + 1]] for g in range(128)], Bw, [None] * 128,
+                              [D[off[g]:off[g + 1]] for g in range(128)])
+    wsb = torch.empty(gmi.workspace_bytes(128), dtype=torch.uint8, device=dev)
+    fl = 2.0 * counts.sum() * N * K
+    by = 2 * (counts.sum() * K + int((counts > 0).sum()) * N * K + counts.sum() * N)
+    ms = time_launches(torch, lambda i: gmi.gemm_grouped_raw(table, 128, gmi.GMI_BF16, 1.0, 0.0, wsb), 1, 3, 10)
+    out["moe_grouped_bf16"] = dict(roof(fl, by, ms), bound="hbm")
+    del Bw, A, D
+    torch.cuda.empty_cache()
+    log("bench: MoE grouped done")
+
+    # 4. W4A16, N = K = 8192, g = 128
+    w = gi.w4a16(M=16)
+    base_pp = gmi.prepack_w4(torch.from_numpy(w["W"]).to(dev), 8192, 8192)
+    S = t16(torch, w["scales"], torch.float16, dev)
+    Z = torch.from_numpy(w["zeros"]).to(dev)
+    rx = np.random.default_rng(0)
+    for M in (16, 128, 1024, 4096):
+        X = t16(torch, gi.w4a16(M=M, N=16, K=8192)["X"], torch.float16, dev)
+        ws = 8192 * 8192 // 2 + S.numel() * 2 + Z.numel() + 2 * M * 8192 * 2
+        R = copies_for(ws)
+        sets = [(base_pp.clone(), S.clone(), Z.clone(), X.clone(), torch.empty((M, 8192), dtype=torch.float16,
+                                                                                device=dev)) for _ in range(R)]
+
+        def fn(i, sets=sets):
+            pp, s, z, x, y = sets[i]
+            gmi.gemm_w4a16(x, pp, s, z, 128, 8192, Y=y)
+
+        ms = time_launches(torch, fn, R, 5, max(20, R * 2))
+        bound = "hbm" if M <= 64 else "mfma"
+        out[f"w4a16_M{M}"] = dict(roof(2.0 * M * 8192 * 8192, ws, ms), bound=bound)
+        del sets
+    del rx
+    log("bench: W4A16 done")
+
+    # 5. conv fprop bf16 32x56x56x256, 3x3x256 -> 256, pad 1
+    x, wf = gi.conv_fprop_bf16()
+    xd, wd = t16(torch, x, torch.bfloat16, dev), t16(torch, wf, torch.bfloat16, dev)
+    ws = 2 * (x.size + wf.size + 32 * 56 * 56 * 256)
+    R = copies_for(ws)
+    sets = [(xd.clone(), wd.clone(), torch.empty((32, 56, 56, 256), dtype=torch.bfloat16, device=dev))
+            for _ in range(R)]
+    ms = time_launches(torch, lambda i: gmi.conv2d_fprop(sets[i][0], sets[i][1], pad=(1, 1), y=sets[i][2]), R, 5,
+                       max(20, 2 * R))
+    out["conv_fprop_bf16"] = dict(roof(2.0 * 100352 * 256 * 2304, ws, ms), bound="mfma")
+    log("bench: conv done")
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--headline-only", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this library's kernels run on a single device and there is no "
+              "multi-GPU path to time (--gpus must be 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gmi_inputs as gi
+    import grouped_mixed_input_amd as gmi
+
+    if not gmi.LIB_PATH.exists():
+        from __graft_entry__ import build
+
+        build()
+    gmi.lib()
+    dev = torch.device("cuda:0")
+    log("bench: building inputs")
+    fn, R, flops, ws, keep = setup_ptr_array(torch, gmi, gi, dev)
+    log(f"bench: headline rotates {R} copies of {ws / 2**20:.0f} MiB")
+    for i in range(args.warmup):
+        fn(i % R)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        fn(i % R)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"bench: headline {ms * 1e3:.1f} us/step, {tflops:.1f} TFLOP/s")
+
+    result = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "pointer-array bf16 GEMM, L=16 separately allocated M=N=K=1024 problems, "
+                               "beta=0, fp32 accumulate, bf16 D", "L": 16, "M": 1024, "N": 1024, "K": 1024,
+                   "cache": f"cold: {R} rotating copies of the {ws / 2**20:.0f} MiB working set"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_16, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_MFMA_16, 4), "traffic": None,
+                     "kernel": "k_gemm_ptr_array<TileCfg<256,256,2,2>, bf16>"},
+    }
+    if not args.headline_only:
+        result["workloads"] = bench_workloads(torch, gmi, gi, dev, args)
+    if not args.no_cpu_baseline:
+        log("bench: timing the oracle on the host")
+        result["cpu_baseline"] = cpu_baseline(gi, keep[0], keep[1])
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,182 @@
+"""grouped_mixed_input_amd -- grouped, mixed-input (W4A16) and implicit-conv GEMM
+for AMD MI355X (gfx950).
+
+A thin ctypes binding over the C ABI of ``libgmi.so`` (declared in
+``include/gmi.h``).  Functions here only marshal torch tensors into device
+pointers, sizes and the current HIP stream; every step of the computation runs
+in the library's HIP kernels.  There is no fallback: if ``libgmi.so`` has not
+been built, importing the binding's functions raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import pathlib
+
+import torch
+
+_PKG = pathlib.Path(__file__).resolve().parent
+LIB_PATH = _PKG / "libgmi.so"
+
+GMI_OK, GMI_ERR_INVALID_ARG, GMI_ERR_UNSUPPORTED, GMI_ERR_MISALIGNED, GMI_ERR_WORKSPACE, GMI_ERR_HIP = range(6)
+STATUS_NAMES = ["GMI_OK", "GMI_ERR_INVALID_ARG", "GMI_ERR_UNSUPPORTED", "GMI_ERR_MISALIGNED", "GMI_ERR_WORKSPACE",
+                "GMI_ERR_HIP"]
+GMI_F16, GMI_BF16 = 0, 1
+_DT = {torch.float16: GMI_F16, torch.bfloat16: GMI_BF16}
+
+
+class GmiError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        name = STATUS_NAMES[status] if 0 <= status < len(STATUS_NAMES) else str(status)
+        super().__init__(f"{name}: {message}")
+
+
+class Problem(ctypes.Structure):
+    """Mirror of gmi_problem."""
+    _fields_ = [("M", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("lda", ctypes.c_int64), ("ldb", ctypes.c_int64), ("ldc", ctypes.c_int64), ("ldd", ctypes.c_int64),
+                ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("C", ctypes.c_void_p), ("D", ctypes.c_void_p)]
+
+
+_lib = None
+_i32, _i64, _f32, _p, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+
+def lib() -> ctypes.CDLL:
+    """Load libgmi.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not LIB_PATH.exists():
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                           "python -m grouped_mixed_input_amd.build")
+    L = ctypes.CDLL(str(LIB_PATH))
+    L.gmi_last_error.restype = ctypes.c_char_p
+    L.gmi_last_error.argtypes = []
+    L.gmi_workspace_bytes.restype = _sz
+    L.gmi_workspace_bytes.argtypes = [_i32]
+    L.gmi_gemm_grouped.restype = ctypes.c_int
+    L.gmi_gemm_grouped.argtypes = [ctypes.POINTER(Problem), _i32, ctypes.c_int, _f32, _f32, _p, _sz, _p]
+    L.gmi_gemm_ptr_array.restype = ctypes.c_int
+    L.gmi_gemm_ptr_array.argtypes = [_i32, _i32, _i32, _i32, _p, _i64, _p, _i64, _p, _i64, _p, _i64, ctypes.c_int,
+                                     _f32, _f32, _p]
+    L.gmi_prepack_w4_bytes.restype = _sz
+    L.gmi_prepack_w4_bytes.argtypes = [_i32, _i32]
+    L.gmi_prepack_w4.restype = ctypes.c_int
+    L.gmi_prepack_w4.argtypes = [_p, _i32, _i32, _p, _p]
+    L.gmi_gemm_w4a16.restype = ctypes.c_int
+    L.gmi_gemm_w4a16.argtypes = [_i32, _i32, _i32, _p, _i64, _p, _p, _p, _i32, _p, _i64, _p]
+    L.gmi_conv2d_fprop_implicit.restype = ctypes.c_int
+    L.gmi_conv2d_fprop_implicit.argtypes = [_i32] * 13 + [_p, _p, _p, _p, ctypes.c_int, _f32, _f32, _p]
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != GMI_OK:
+        raise GmiError(status, lib().gmi_last_error().decode())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _ld(t: torch.Tensor) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with unit stride along its rows")
+    return t.stride(0)
+
+
+# ---------------------------------------------------------------- grouped
+def workspace_bytes(count: int) -> int:
+    return lib().gmi_workspace_bytes(count)
+
+
+def make_problems(As, Bs, Cs, Ds) -> "ctypes.Array":
+    """gmi_problem array from lists of tensors: A [M][K], B [N][K] (column-major
+    B, i.e. row n of the tensor is column n), C / D [M][N] (C may be None)."""
+    arr = (Problem * len(As))()
+    for i, (a, b, c, d) in enumerate(zip(As, Bs, Cs, Ds)):
+        M, N = d.shape
+        K = a.shape[1]
+        arr[i] = Problem(M, N, K, _ld(a), _ld(b), _ld(c) if c is not None else 0, _ld(d),
+                         _ptr(a), _ptr(b), _ptr(c), _ptr(d))
+    return arr
+
+
+def gemm_grouped(As, Bs, Cs, Ds, alpha=1.0, beta=0.0, workspace=None, stream=None):
+    """D_g = alpha A_g B_g + beta C_g for every g, in one launch."""
+    dt = _DT[Ds[0].dtype]
+    probs = make_problems(As, Bs, Cs if Cs is not None else [None] * len(As), Ds)
+    need = workspace_bytes(len(As))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=Ds[0].device)
+    _check(lib().gmi_gemm_grouped(probs, len(As), dt, alpha, beta, workspace.data_ptr(), workspace.numel(),
+                                  _stream(stream)))
+    return Ds
+
+
+def gemm_grouped_raw(problems, count, dtype, alpha, beta, workspace, stream=None):
+    """Call with a prepared gmi_problem array (no per-call marshalling)."""
+    _check(lib().gmi_gemm_grouped(problems, count, dtype, alpha, beta, workspace.data_ptr(), workspace.numel(),
+                                  _stream(stream)))
+
+
+# ---------------------------------------------------------------- ptr-array
+def pointer_array(tensors, device) -> torch.Tensor:
+    """Device array (int64) of the tensors' device addresses."""
+    return torch.tensor([t.data_ptr() for t in tensors], dtype=torch.int64, device=device)
+
+
+def gemm_ptr_array(L, M, N, K, A_ptrs, lda, B_ptrs, ldb, C_ptrs, ldc, D_ptrs, ldd, dtype, alpha=1.0, beta=0.0,
+                   stream=None):
+    """Pointer-array GEMM; *_ptrs are device int64 tensors of L addresses."""
+    _check(lib().gmi_gemm_ptr_array(L, M, N, K, _ptr(A_ptrs), lda, _ptr(B_ptrs), ldb, _ptr(C_ptrs), ldc,
+                                    _ptr(D_ptrs), ldd, _DT[dtype] if dtype in _DT else dtype, alpha, beta,
+                                    _stream(stream)))
+
+
+# ---------------------------------------------------------------- W4A16
+def prepack_w4(w_u4: torch.Tensor, N: int, K: int, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Prepack a uint4 weight stored [N][K/2] (uint8) into the kernels' order."""
+    if out is None:
+        out = torch.empty(lib().gmi_prepack_w4_bytes(N, K), dtype=torch.uint8, device=w_u4.device)
+    _check(lib().gmi_prepack_w4(w_u4.data_ptr(), N, K, out.data_ptr(), _stream(stream)))
+    return out
+
+
+def gemm_w4a16(X: torch.Tensor, w_prepacked: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
+               group_size: int, N: int, Y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Y = X W^T with X fp16 [M][K], scales fp16 [K/g][N], zeros uint8 [K/g][N/2]."""
+    M, K = X.shape
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    _check(lib().gmi_gemm_w4a16(M, N, K, X.data_ptr(), _ld(X), w_prepacked.data_ptr(), scales.data_ptr(),
+                                zeros.data_ptr(), group_size, Y.data_ptr(), _ld(Y), _stream(stream)))
+    return Y
+
+
+# ---------------------------------------------------------------- conv
+def conv_out_size(H, R, pad, stride, dil):
+    return (H + 2 * pad - dil * (R - 1) - 1) // stride + 1
+
+
+def conv2d_fprop(x: torch.Tensor, w: torch.Tensor, pad=(0, 0), stride=(1, 1), dil=(1, 1), c_in=None, alpha=1.0,
+                 beta=0.0, y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Implicit-GEMM cross-correlation: x NHWC, w KRSC -> y NPQK."""
+    N, H, W, C = x.shape
+    K, R, S, _ = w.shape
+    if y is None:
+        P = conv_out_size(H, R, pad[0], stride[0], dil[0])
+        Q = conv_out_size(W, S, pad[1], stride[1], dil[1])
+        y = torch.empty((N, max(P, 0), max(Q, 0), K), dtype=x.dtype, device=x.device)
+    _check(lib().gmi_conv2d_fprop_implicit(N, H, W, C, K, R, S, pad[0], pad[1], stride[0], stride[1], dil[0], dil[1],
+                                           x.data_ptr(), w.data_ptr(), _ptr(c_in), y.data_ptr(), _DT[x.dtype], alpha,
+                                           beta, _stream(stream)))
+    return y

@@ -1,0 +1,294 @@
+// gmi_api.hip -- the C ABI: argument validation (every rule checked on the
+// host before any HIP call), descriptor staging, tile-shape choice, launch.
+//
+// The checks restate the preconditions of the pages' can_implement functions:
+// problem mode and rank, 128-bit alignment of every operand
+// (sm90_gemm_array_tma_warpspecialized_cooperative.hpp, machete_mainloop.cuh),
+// the group-size rules and the presence of scales and zeros
+// (machete_mainloop.cuh), and the convolution rules -- channel-innermost
+// tensors, traversal stride 1..8, cross-correlation, groups == 1
+// (sm100_implicit_gemm_umma_warpspecialized.hpp).
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "../../include/gmi.h"
+#include "gmi_internal.hpp"
+
+namespace gmi {
+
+static thread_local std::string g_last_error;
+
+static gmi_status fail(gmi_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+static gmi_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return GMI_OK;
+  return fail(GMI_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+static bool dtype_ok(gmi_dtype d) { return d == GMI_F16 || d == GMI_BF16; }
+
+// Tile shape for a list of problems: 256x256 when it alone fills every CU,
+// then 256x128, else 128x128 (two resident workgroups per CU).
+template <class F>
+static int choose_shape(F tiles_at) {
+  const int64_t cus = device_cu_count();
+  if (tiles_at(256, 256) >= cus) return TILE_256x256;
+  if (tiles_at(256, 128) >= cus) return TILE_256x128;
+  return TILE_128x128;
+}
+
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace gmi
+
+using namespace gmi;
+
+extern "C" {
+
+const char* gmi_last_error(void) { return g_last_error.c_str(); }
+
+size_t gmi_workspace_bytes(int32_t problem_count) {
+  if (problem_count < 0) return 0;
+  return kWorkspaceHeader + sizeof(GroupDesc) * (size_t)problem_count;
+}
+
+gmi_status gmi_gemm_grouped(const gmi_problem* problems, int32_t count, gmi_dtype dtype, float alpha, float beta,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (count < 0) return fail(GMI_ERR_INVALID_ARG, "gemm_grouped: count %d < 0", count);
+  if (count > 0 && !problems) return fail(GMI_ERR_INVALID_ARG, "gemm_grouped: problems is NULL");
+  if (!dtype_ok(dtype)) return fail(GMI_ERR_UNSUPPORTED, "gemm_grouped: dtype %d not supported", (int)dtype);
+  const bool use_c = beta != 0.0f;
+  int live = 0;
+  for (int32_t g = 0; g < count; ++g) {
+    const gmi_problem& p = problems[g];
+    if (p.M < 0 || p.N < 0 || p.K < 0)
+      return fail(GMI_ERR_INVALID_ARG, "gemm_grouped: problem %d has a negative size (%d, %d, %d)", g, p.M, p.N, p.K);
+    if (p.M == 0 || p.N == 0) continue;
+    ++live;
+    if (!p.D || (p.K > 0 && (!p.A || !p.B)) || (use_c && !p.C))
+      return fail(GMI_ERR_INVALID_ARG, "gemm_grouped: problem %d has a NULL operand", g);
+    if ((p.K > 0 && (p.lda < p.K || p.ldb < p.K)) || p.ldd < p.N || (use_c && p.ldc < p.N))
+      return fail(GMI_ERR_INVALID_ARG, "gemm_grouped: problem %d has a leading dimension below its row width", g);
+    if ((p.K > 0 && (!aligned16(p.A) || !aligned16(p.B) || p.lda % 8 || p.ldb % 8)) || !aligned16(p.D) ||
+        p.ldd % 8 || (use_c && (!aligned16(p.C) || p.ldc % 8)))
+      return fail(GMI_ERR_MISALIGNED, "gemm_grouped: problem %d: pointers must be 16-byte aligned, ld multiples of 8",
+                  g);
+  }
+  if (live == 0) return GMI_OK;
+  if (!workspace || workspace_bytes < gmi_workspace_bytes(live))
+    return fail(GMI_ERR_WORKSPACE, "gemm_grouped: workspace of %zu bytes, %zu needed", workspace_bytes,
+                gmi_workspace_bytes(live));
+  if (!aligned16(workspace)) return fail(GMI_ERR_MISALIGNED, "gemm_grouped: workspace must be 16-byte aligned");
+
+  const int shape = choose_shape([&](int bm, int bn) {
+    int64_t t = 0;
+    for (int32_t g = 0; g < count; ++g)
+      if (problems[g].M > 0 && problems[g].N > 0) t += cdiv(problems[g].M, bm) * cdiv(problems[g].N, bn);
+    return t;
+  });
+  const int bm = tile_bm(shape), bn = tile_bn(shape);
+  std::vector<GroupDesc> desc;
+  desc.reserve(live);
+  int64_t tiles = 0;
+  for (int32_t g = 0; g < count; ++g) {
+    const gmi_problem& p = problems[g];
+    if (p.M == 0 || p.N == 0) continue;
+    GroupDesc d;
+    d.A = (const uint16_t*)p.A;
+    d.B = (const uint16_t*)p.B;
+    d.C = use_c ? (const uint16_t*)p.C : nullptr;
+    d.D = (uint16_t*)p.D;
+    d.lda = p.lda;
+    d.ldb = p.ldb;
+    d.ldc = p.ldc;
+    d.ldd = p.ldd;
+    d.M = p.M;
+    d.N = p.N;
+    d.K = p.K;
+    d.tile_start = (int32_t)tiles;
+    tiles += cdiv(p.M, bm) * cdiv(p.N, bn);
+    if (tiles > INT32_MAX) return fail(GMI_ERR_INVALID_ARG, "gemm_grouped: more than 2^31 - 1 output tiles");
+    desc.push_back(d);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  GroupDesc* dev_desc = (GroupDesc*)((char*)workspace + kWorkspaceHeader);
+  // pageable source: the copy completes before the call returns, so the
+  // host table may be reused immediately
+  gmi_status st = hip_status(
+      hipMemcpyAsync(dev_desc, desc.data(), sizeof(GroupDesc) * desc.size(), hipMemcpyHostToDevice, s),
+      "gemm_grouped: staging the problem table");
+  if (st != GMI_OK) return st;
+  return hip_status(launch_grouped(dev_desc, live, (int)tiles, shape, (int)dtype, alpha, beta, s),
+                    "gemm_grouped: launch");
+}
+
+gmi_status gmi_gemm_ptr_array(int32_t L, int32_t M, int32_t N, int32_t K, const void* const* A, int64_t lda,
+                              const void* const* B, int64_t ldb, const void* const* C, int64_t ldc, void* const* D,
+                              int64_t ldd, gmi_dtype dtype, float alpha, float beta, void* stream) {
+  g_last_error.clear();
+  if (L < 0 || M < 0 || N < 0 || K < 0)
+    return fail(GMI_ERR_INVALID_ARG, "gemm_ptr_array: negative size (L %d, M %d, N %d, K %d)", L, M, N, K);
+  if (!dtype_ok(dtype)) return fail(GMI_ERR_UNSUPPORTED, "gemm_ptr_array: dtype %d not supported", (int)dtype);
+  if (L == 0 || M == 0 || N == 0) return GMI_OK;
+  const bool use_c = beta != 0.0f;
+  if (!D || (K > 0 && (!A || !B)) || (use_c && !C))
+    return fail(GMI_ERR_INVALID_ARG, "gemm_ptr_array: NULL pointer array");
+  if ((K > 0 && (lda < K || ldb < K)) || ldd < N || (use_c && ldc < N))
+    return fail(GMI_ERR_INVALID_ARG, "gemm_ptr_array: leading dimension below its row width");
+  if ((K > 0 && (lda % 8 || ldb % 8)) || ldd % 8 || (use_c && ldc % 8))
+    return fail(GMI_ERR_MISALIGNED, "gemm_ptr_array: leading dimensions must be multiples of 8");
+  if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)D | (uintptr_t)(use_c ? C : nullptr)) & 7u)
+    return fail(GMI_ERR_MISALIGNED, "gemm_ptr_array: pointer arrays must be 8-byte aligned");
+  const int shape = choose_shape([&](int bm, int bn) { return (int64_t)L * cdiv(M, bm) * cdiv(N, bn); });
+  if ((int64_t)L * cdiv(M, tile_bm(shape)) * cdiv(N, tile_bn(shape)) > INT32_MAX)
+    return fail(GMI_ERR_INVALID_ARG, "gemm_ptr_array: more than 2^31 - 1 output tiles");
+  PtrArrayLaunch p;
+  p.A = (const uint16_t* const*)A;
+  p.B = (const uint16_t* const*)B;
+  p.C = use_c ? (const uint16_t* const*)C : nullptr;
+  p.D = (uint16_t* const*)D;
+  p.lda = lda;
+  p.ldb = ldb;
+  p.ldc = ldc;
+  p.ldd = ldd;
+  p.L = L;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  return hip_status(launch_ptr_array(p, shape, (int)dtype, alpha, beta, (hipStream_t)stream),
+                    "gemm_ptr_array: launch");
+}
+
+size_t gmi_prepack_w4_bytes(int32_t N, int32_t K) {
+  if (N < 0 || K < 0) return 0;
+  return (size_t)N * (size_t)K / 2;
+}
+
+gmi_status gmi_prepack_w4(const uint8_t* w_u4, int32_t N, int32_t K, uint8_t* w_prepacked, void* stream) {
+  g_last_error.clear();
+  if (N < 0 || K < 0) return fail(GMI_ERR_INVALID_ARG, "prepack_w4: negative size (N %d, K %d)", N, K);
+  if (N % 16 || K % 128) return fail(GMI_ERR_UNSUPPORTED, "prepack_w4: needs N %% 16 == 0 and K %% 128 == 0");
+  if (N == 0 || K == 0) return GMI_OK;
+  if (!w_u4 || !w_prepacked) return fail(GMI_ERR_INVALID_ARG, "prepack_w4: NULL pointer");
+  if (!aligned16(w_u4) || !aligned16(w_prepacked))
+    return fail(GMI_ERR_MISALIGNED, "prepack_w4: pointers must be 16-byte aligned");
+  const size_t bytes = gmi_prepack_w4_bytes(N, K);
+  if (w_u4 < w_prepacked + bytes && w_prepacked < w_u4 + bytes)
+    return fail(GMI_ERR_INVALID_ARG, "prepack_w4: input and output overlap");
+  return hip_status(launch_prepack_w4(w_u4, N, K, w_prepacked, (hipStream_t)stream), "prepack_w4: launch");
+}
+
+gmi_status gmi_gemm_w4a16(int32_t M, int32_t N, int32_t K, const void* X, int64_t ldx, const uint8_t* w_prepacked,
+                          const void* scales, const uint8_t* zeros, int32_t group_size, void* Y, int64_t ldy,
+                          void* stream) {
+  g_last_error.clear();
+  if (M < 0 || N < 0 || K < 0) return fail(GMI_ERR_INVALID_ARG, "gemm_w4a16: negative size (%d, %d, %d)", M, N, K);
+  if (N % 16 || K % 128)
+    return fail(GMI_ERR_UNSUPPORTED, "gemm_w4a16: needs N %% 16 == 0 and K %% 128 == 0 (prepack blocks)");
+  if (group_size <= 0) return fail(GMI_ERR_INVALID_ARG, "gemm_w4a16: group_size %d <= 0", group_size);
+  if (K > 0 && K % group_size)
+    return fail(GMI_ERR_INVALID_ARG, "gemm_w4a16: K %d is not a multiple of group_size %d", K, group_size);
+  if (group_size != K && group_size % 128)
+    return fail(GMI_ERR_UNSUPPORTED, "gemm_w4a16: group_size must equal K or be a multiple of 128");
+  if (M == 0 || N == 0) return GMI_OK;
+  if (!Y || (K > 0 && (!X || !w_prepacked || !scales || !zeros)))
+    return fail(GMI_ERR_INVALID_ARG, "gemm_w4a16: NULL pointer");
+  if ((K > 0 && ldx < K) || ldy < N) return fail(GMI_ERR_INVALID_ARG, "gemm_w4a16: ldx < K or ldy < N");
+  if (!aligned16(Y) || ldy % 8 ||
+      (K > 0 && (!aligned16(X) || !aligned16(w_prepacked) || !aligned16(scales) || !aligned16(zeros) || ldx % 8)))
+    return fail(GMI_ERR_MISALIGNED, "gemm_w4a16: pointers must be 16-byte aligned, ld multiples of 8");
+  W4Launch a;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.group = group_size;
+  a.X = (const uint16_t*)X;
+  a.ldx = ldx;
+  a.w = w_prepacked;
+  a.scales = (const uint16_t*)scales;
+  a.zeros = zeros;
+  a.Y = (uint16_t*)Y;
+  a.ldy = ldy;
+  return hip_status(launch_w4a16(a, (hipStream_t)stream), "gemm_w4a16: launch");
+}
+
+gmi_status gmi_conv2d_fprop_implicit(int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int32_t R, int32_t S,
+                                     int32_t pad_h, int32_t pad_w, int32_t stride_h, int32_t stride_w, int32_t dil_h,
+                                     int32_t dil_w, const void* x, const void* w, const void* c_in, void* y,
+                                     gmi_dtype dtype, float alpha, float beta, void* stream) {
+  g_last_error.clear();
+  if (N < 0 || H < 1 || W < 1 || C < 1 || K < 1 || R < 1 || S < 1)
+    return fail(GMI_ERR_INVALID_ARG, "conv2d_fprop: sizes must be positive (N >= 0)");
+  if (pad_h < 0 || pad_w < 0 || stride_h < 1 || stride_w < 1 || dil_h < 1 || dil_w < 1)
+    return fail(GMI_ERR_INVALID_ARG, "conv2d_fprop: padding >= 0, stride >= 1 and dilation >= 1 required");
+  if (stride_h > 8 || stride_w > 8)
+    return fail(GMI_ERR_UNSUPPORTED, "conv2d_fprop: traversal stride must be in [1, 8]");
+  if (!dtype_ok(dtype)) return fail(GMI_ERR_UNSUPPORTED, "conv2d_fprop: dtype %d not supported", (int)dtype);
+  if (C % 8 || K % 8)
+    return fail(GMI_ERR_MISALIGNED, "conv2d_fprop: C and K must be multiples of 8 (128-bit channel runs)");
+  const int64_t P = ((int64_t)H + 2 * (int64_t)pad_h - (int64_t)dil_h * (R - 1) - 1) / stride_h + 1;
+  const int64_t Q = ((int64_t)W + 2 * (int64_t)pad_w - (int64_t)dil_w * (S - 1) - 1) / stride_w + 1;
+  if ((int64_t)H + 2 * (int64_t)pad_h - (int64_t)dil_h * (R - 1) - 1 < 0 ||
+      (int64_t)W + 2 * (int64_t)pad_w - (int64_t)dil_w * (S - 1) - 1 < 0 || P < 1 || Q < 1)
+    return fail(GMI_ERR_INVALID_ARG, "conv2d_fprop: the filter does not fit the padded image (P, Q < 1)");
+  if ((int64_t)N * P * Q > INT32_MAX || (int64_t)N * H * W > INT32_MAX || (int64_t)R * S * C > INT32_MAX)
+    return fail(GMI_ERR_INVALID_ARG, "conv2d_fprop: problem too large for 32-bit pixel / tap indices");
+  if (N == 0) return GMI_OK;
+  const bool use_c = beta != 0.0f;
+  if (!x || !w || !y || (use_c && !c_in)) return fail(GMI_ERR_INVALID_ARG, "conv2d_fprop: NULL pointer");
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (use_c && !aligned16(c_in)))
+    return fail(GMI_ERR_MISALIGNED, "conv2d_fprop: pointers must be 16-byte aligned");
+  ConvLaunch a;
+  a.x = (const uint16_t*)x;
+  a.w = (const uint16_t*)w;
+  a.c = use_c ? (const uint16_t*)c_in : nullptr;
+  a.y = (uint16_t*)y;
+  a.N = N;
+  a.H = H;
+  a.W = W;
+  a.C = C;
+  a.K = K;
+  a.R = R;
+  a.S = S;
+  a.P = (int)P;
+  a.Q = (int)Q;
+  a.ph = pad_h;
+  a.pw = pad_w;
+  a.sh = stride_h;
+  a.sw = stride_w;
+  a.dh = dil_h;
+  a.dw = dil_w;
+  const int64_t Mg = (int64_t)N * P * Q;
+  const int shape = choose_shape([&](int bm, int bn) { return cdiv(Mg, bm) * cdiv(K, bn); });
+  return hip_status(launch_conv_fprop(a, shape, (int)dtype, alpha, beta, (hipStream_t)stream),
+                    "conv2d_fprop: launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// gmi_internal.hpp -- host-side declarations shared by the C-ABI layer and
+// the kernel translation units: launch descriptors and launcher functions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gmi {
+
+// One problem of a grouped launch, as staged into the device workspace.
+struct GroupDesc {
+  const uint16_t* A;
+  const uint16_t* B;
+  const uint16_t* C;
+  uint16_t* D;
+  int64_t lda, ldb, ldc, ldd;
+  int32_t M, N, K;
+  int32_t tile_start;  // first tile id of this problem (exclusive prefix sum)
+};
+static_assert(sizeof(GroupDesc) == 80, "descriptor layout is part of the workspace contract");
+constexpr size_t kWorkspaceHeader = 256;
+
+// Tile shapes of the dense mainloop (BM x BN, 4 waves).
+enum TileShape { TILE_256x256 = 0, TILE_128x128 = 1, TILE_256x128 = 2 };
+inline int tile_bm(int s) { return s == TILE_128x128 ? 128 : 256; }
+inline int tile_bn(int s) { return s == TILE_256x256 ? 256 : 128; }
+inline int tile_wgs_per_cu(int s) { return s == TILE_128x128 ? 2 : 1; }
+
+struct PtrArrayLaunch {
+  const uint16_t* const* A;
+  const uint16_t* const* B;
+  const uint16_t* const* C;
+  uint16_t* const* D;
+  int64_t lda, ldb, ldc, ldd;
+  int L, M, N, K;
+};
+
+struct ConvLaunch {
+  const uint16_t* x;
+  const uint16_t* w;
+  const uint16_t* c;
+  uint16_t* y;
+  int N, H, W, C, K, R, S, P, Q, ph, pw, sh, sw, dh, dw;
+};
+
+struct W4Launch {
+  int M, N, K, group;
+  const uint16_t* X;
+  int64_t ldx;
+  const uint8_t* w;
+  const uint16_t* scales;
+  const uint8_t* zeros;
+  uint16_t* Y;
+  int64_t ldy;
+};
+
+int device_cu_count();  // cached per device
+
+hipError_t launch_grouped(const GroupDesc* desc_dev, int count, int total_tiles, int shape, int dtype, float alpha,
+                          float beta, hipStream_t stream);
+hipError_t launch_ptr_array(const PtrArrayLaunch& a, int shape, int dtype, float alpha, float beta,
+                            hipStream_t stream);
+hipError_t launch_conv_fprop(const ConvLaunch& a, int shape, int dtype, float alpha, float beta, hipStream_t stream);
+hipError_t launch_prepack_w4(const uint8_t* w, int N, int K, uint8_t* out, hipStream_t stream);
+hipError_t launch_w4a16(const W4Launch& a, hipStream_t stream);
+
+}  // namespace gmi

@@ -1,0 +1,94 @@
+// kernels_conv.hip -- implicit-GEMM conv2d forward.
+//
+// The linearised problem of the page sm100_implicit_gemm_umma_warpspecialized.hpp
+// (get_problem_shape_MNKL for fprop): M = N*P*Q output pixels, N = K filters,
+// K = R*S*C taps.  The activation operand is gathered tile by tile from NHWC
+// (ConvLoader: padding, traversal stride and dilation folded into the address,
+// zero outside the image); the KRSC filter is already the column-major B
+// operand with leading dimension R*S*C; the output rows are NPQK.
+#include "gmi_device.hpp"
+#include "gmi_internal.hpp"
+
+namespace gmi {
+
+struct ConvArgs {
+  ConvGeom g;
+  const uint16_t* w;
+  const uint16_t* c;
+  uint16_t* y;
+  int M, Nk;  // GEMM M and N
+  int tiles_n, total_tiles;
+  float alpha, beta;
+};
+
+// Tile ids run n-tile fastest: the few n-tiles of a pixel block are
+// consecutive, so one XCD gathers each activation panel once into its L2.
+template <class Cfg, int DT>
+__global__ __launch_bounds__(Cfg::THREADS) void k_conv_fprop(ConvArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
+  const int G = gridDim.x;
+  for (int base = 0; base < a.total_tiles; base += G) {
+    const int tile = base + remap_slot(blockIdx.x, G);
+    if (tile >= a.total_tiles) break;
+    Tile t;
+    t.M = a.M;
+    t.N = a.Nk;
+    t.K = a.g.Kg;
+    t.m0 = (tile / a.tiles_n) * Cfg::BM;
+    t.n0 = (tile % a.tiles_n) * Cfg::BN;
+    t.C = a.c;
+    t.ldc = a.Nk;
+    t.D = a.y;
+    t.ldd = a.Nk;
+    ConvLoader<Cfg::BM, Cfg::THREADS> al;
+    DenseLoader<Cfg::BN, Cfg::THREADS> bl;
+    al.init(a.g, t.m0, t.M);
+    bl.init(a.w, a.g.Kg, t.n0, t.N, t.K);
+    f32x16 acc[Cfg::TM][Cfg::TN];
+    mainloop<Cfg, DT>(lds, al, bl, (t.K + BK - 1) / BK, acc);
+    epilogue<Cfg, DT>(t, acc, a.alpha, a.beta);
+  }
+}
+
+using ConvCfg256 = TileCfg<256, 256, 2, 2>;
+using ConvCfg128 = TileCfg<128, 128, 2, 2>;
+using ConvCfg256x128 = TileCfg<256, 128, 2, 2>;
+
+hipError_t launch_conv_fprop(const ConvLaunch& p, int shape, int dtype, float alpha, float beta,
+                             hipStream_t stream) {
+  ConvArgs a;
+  a.g = ConvGeom{p.x, p.H, p.W, p.C, p.S, p.P, p.Q, p.ph, p.pw, p.sh, p.sw, p.dh, p.dw, p.R * p.S * p.C};
+  a.w = p.w;
+  a.c = p.c;
+  a.y = p.y;
+  a.M = p.N * p.P * p.Q;
+  a.Nk = p.K;
+  const int bm = tile_bm(shape), bn = tile_bn(shape);
+  a.tiles_n = (p.K + bn - 1) / bn;
+  a.total_tiles = ((a.M + bm - 1) / bm) * a.tiles_n;
+  a.alpha = alpha;
+  a.beta = beta;
+  const int resident = device_cu_count() * tile_wgs_per_cu(shape);
+  int grid = (a.total_tiles + XCDS - 1) / XCDS * XCDS;
+  if (grid > resident) grid = resident / XCDS * XCDS;
+  if (grid < XCDS) grid = XCDS;
+  if (shape == TILE_256x256) {
+    if (dtype == DT_F16)
+      hipLaunchKernelGGL((k_conv_fprop<ConvCfg256, DT_F16>), dim3(grid), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_conv_fprop<ConvCfg256, DT_BF16>), dim3(grid), dim3(256), 0, stream, a);
+  } else if (shape == TILE_256x128) {
+    if (dtype == DT_F16)
+      hipLaunchKernelGGL((k_conv_fprop<ConvCfg256x128, DT_F16>), dim3(grid), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_conv_fprop<ConvCfg256x128, DT_BF16>), dim3(grid), dim3(256), 0, stream, a);
+  } else {
+    if (dtype == DT_F16)
+      hipLaunchKernelGGL((k_conv_fprop<ConvCfg128, DT_F16>), dim3(grid), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_conv_fprop<ConvCfg128, DT_BF16>), dim3(grid), dim3(256), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace gmi

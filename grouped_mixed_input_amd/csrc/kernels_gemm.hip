@@ -1,0 +1,152 @@
+// kernels_gemm.hip -- persistent grouped and pointer-array GEMM kernels.
+//
+// Both follow the persistent work-tile loop of the page
+// sm90_gemm_array_tma_warpspecialized_cooperative.hpp (operator(): take the
+// initial work tile, exit when it is invalid, and for every tile refresh the
+// problem shape of its group / batch before running the k-loop and the
+// epilogue).  Grouped problems carry their own shape and strides; the array
+// mode shares one shape and one stride per operand over L batches.
+#include "gmi_device.hpp"
+#include "gmi_internal.hpp"
+
+namespace gmi {
+
+template <class Cfg, int DT>
+__device__ __forceinline__ void run_tile(char* lds, const Tile& t, float alpha, float beta) {
+  DenseLoader<Cfg::BM, Cfg::THREADS> al;
+  DenseLoader<Cfg::BN, Cfg::THREADS> bl;
+  al.init(t.A, t.lda, t.m0, t.M, t.K);
+  bl.init(t.B, t.ldb, t.n0, t.N, t.K);
+  f32x16 acc[Cfg::TM][Cfg::TN];
+  mainloop<Cfg, DT>(lds, al, bl, (t.K + BK - 1) / BK, acc);
+  epilogue<Cfg, DT>(t, acc, alpha, beta);
+}
+
+struct GroupedArgs {
+  const GroupDesc* desc;
+  int count, total_tiles;
+  float alpha, beta;
+};
+
+// Tile ids are laid out problem after problem; inside a problem the m-tile
+// index runs fastest, so consecutive tiles (one XCD's share of a round) reuse
+// the same B panel -- the expert weight in a mixture-of-experts layer.
+template <class Cfg, int DT>
+__global__ __launch_bounds__(Cfg::THREADS) void k_gemm_grouped(GroupedArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
+  const int G = gridDim.x;
+  int g = 0;
+  for (int base = 0; base < a.total_tiles; base += G) {
+    const int tile = base + remap_slot(blockIdx.x, G);
+    if (tile >= a.total_tiles) break;
+    while (g + 1 < a.count && a.desc[g + 1].tile_start <= tile) ++g;
+    const GroupDesc& d = a.desc[g];
+    const int local = tile - d.tile_start;
+    const int tiles_m = (d.M + Cfg::BM - 1) / Cfg::BM;
+    Tile t;
+    t.M = d.M;
+    t.N = d.N;
+    t.K = d.K;
+    t.m0 = (local % tiles_m) * Cfg::BM;
+    t.n0 = (local / tiles_m) * Cfg::BN;
+    t.A = d.A;
+    t.lda = d.lda;
+    t.B = d.B;
+    t.ldb = d.ldb;
+    t.C = d.C;
+    t.ldc = d.ldc;
+    t.D = d.D;
+    t.ldd = d.ldd;
+    run_tile<Cfg, DT>(lds, t, a.alpha, a.beta);
+  }
+}
+
+struct PtrArrayArgs {
+  PtrArrayLaunch p;
+  int tiles_m, tiles_per_batch, total_tiles;
+  float alpha, beta;
+};
+
+template <class Cfg, int DT>
+__global__ __launch_bounds__(Cfg::THREADS) void k_gemm_ptr_array(PtrArrayArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
+  const int G = gridDim.x;
+  for (int base = 0; base < a.total_tiles; base += G) {
+    const int tile = base + remap_slot(blockIdx.x, G);
+    if (tile >= a.total_tiles) break;
+    const int l = tile / a.tiles_per_batch, local = tile - l * a.tiles_per_batch;
+    Tile t;
+    t.M = a.p.M;
+    t.N = a.p.N;
+    t.K = a.p.K;
+    t.m0 = (local % a.tiles_m) * Cfg::BM;
+    t.n0 = (local / a.tiles_m) * Cfg::BN;
+    t.A = a.p.A[l];
+    t.lda = a.p.lda;
+    t.B = a.p.B[l];
+    t.ldb = a.p.ldb;
+    t.C = a.beta != 0.0f ? a.p.C[l] : nullptr;
+    t.ldc = a.p.ldc;
+    t.D = a.p.D[l];
+    t.ldd = a.p.ldd;
+    run_tile<Cfg, DT>(lds, t, a.alpha, a.beta);
+  }
+}
+
+using Cfg256 = TileCfg<256, 256, 2, 2>;
+using Cfg128 = TileCfg<128, 128, 2, 2>;
+using Cfg256x128 = TileCfg<256, 128, 2, 2>;
+
+// Persistent grid: a whole number of XCD rounds, no more workgroups than can
+// be resident at once and no more than the tiles need.
+static int persistent_grid(int total_tiles, int shape) {
+  const int resident = device_cu_count() * tile_wgs_per_cu(shape);
+  int g = (total_tiles + XCDS - 1) / XCDS * XCDS;
+  if (g > resident) g = resident / XCDS * XCDS;
+  return g < XCDS ? XCDS : g;
+}
+
+// Instantiate and launch KER for the tile shape and element type.
+#define GMI_DISPATCH(KER, shape, dtype, grid, args, stream)                                                   \
+  do {                                                                                                      \
+    if ((shape) == TILE_256x256) {                                                                          \
+      if ((dtype) == DT_F16)                                                                                \
+        hipLaunchKernelGGL((KER<Cfg256, DT_F16>), dim3(grid), dim3(Cfg256::THREADS), 0, stream, args);      \
+      else                                                                                                  \
+        hipLaunchKernelGGL((KER<Cfg256, DT_BF16>), dim3(grid), dim3(Cfg256::THREADS), 0, stream, args);     \
+    } else if ((shape) == TILE_256x128) {                                                                   \
+      if ((dtype) == DT_F16)                                                                                \
+        hipLaunchKernelGGL((KER<Cfg256x128, DT_F16>), dim3(grid), dim3(Cfg256x128::THREADS), 0, stream, args);  \
+      else                                                                                                  \
+        hipLaunchKernelGGL((KER<Cfg256x128, DT_BF16>), dim3(grid), dim3(Cfg256x128::THREADS), 0, stream, args); \
+    } else {                                                                                                \
+      if ((dtype) == DT_F16)                                                                                \
+        hipLaunchKernelGGL((KER<Cfg128, DT_F16>), dim3(grid), dim3(Cfg128::THREADS), 0, stream, args);      \
+      else                                                                                                  \
+        hipLaunchKernelGGL((KER<Cfg128, DT_BF16>), dim3(grid), dim3(Cfg128::THREADS), 0, stream, args);     \
+    }                                                                                                       \
+  } while (0)
+
+hipError_t launch_grouped(const GroupDesc* desc_dev, int count, int total_tiles, int shape, int dtype, float alpha,
+                          float beta, hipStream_t stream) {
+  GroupedArgs a{desc_dev, count, total_tiles, alpha, beta};
+  const int grid = persistent_grid(total_tiles, shape);
+  GMI_DISPATCH(k_gemm_grouped, shape, dtype, grid, a, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_ptr_array(const PtrArrayLaunch& p, int shape, int dtype, float alpha, float beta,
+                            hipStream_t stream) {
+  PtrArrayArgs a;
+  a.p = p;
+  a.tiles_m = (p.M + tile_bm(shape) - 1) / tile_bm(shape);
+  a.tiles_per_batch = a.tiles_m * ((p.N + tile_bn(shape) - 1) / tile_bn(shape));
+  a.total_tiles = a.tiles_per_batch * p.L;
+  a.alpha = alpha;
+  a.beta = beta;
+  const int grid = persistent_grid(a.total_tiles, shape);
+  GMI_DISPATCH(k_gemm_ptr_array, shape, dtype, grid, a, stream);
+  return hipGetLastError();
+}
+
+}  // namespace gmi

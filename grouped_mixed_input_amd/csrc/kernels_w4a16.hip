@@ -1,0 +1,225 @@
+// kernels_w4a16.hip -- mixed-input GEMM Y = X W^T with prepacked uint4 W.
+//
+// The page machete_mainloop.cuh computes the transposed problem so that the
+// narrow weight becomes the register-sourced operand, prepacks it so that one
+// thread's values for several matrix instructions come from one 128-bit load,
+// and dequantises it in registers (convert, scale, zero) right before the
+// multiply.  Here:
+//   * k_prepack_w4 reorders the plain [N][K/2] uint4 weight once.
+//   * k_w4a16_skinny (M <= 64) streams the prepacked weight straight from HBM
+//     into VGPRs -- one 16-byte load per lane is one 16-row x 128-k block, i.e.
+//     four v_mfma_f32_16x16x32_f16 A fragments -- with the weight rows on the
+//     MFMA's M side and the tokens on its N side (the same swap as the page).
+//     The waves of a workgroup split K and reduce through LDS.
+//   * k_w4a16_tiled (M > 64) is the dense mainloop with the weight loader
+//     (W4Loader) dequantising into the LDS B tile.
+#include "gmi_device.hpp"
+#include "gmi_internal.hpp"
+
+namespace gmi {
+
+// ---------------------------------------------------------------------------
+// Prepack: one thread per 32-bit output word.  Output word (block b, lane L,
+// word j) holds row n = 16 (b / kblocks) + L % 16, k = 128 (b % kblocks) +
+// 32 j + 8 (L / 16) + e for e = 0..7: the 4 input bytes of that run, with
+// the even elements (low nibbles) gathered into bits 0-15 and the odd ones
+// (high nibbles) into bits 16-31.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_prepack_w4(const uint8_t* __restrict__ w, int N, int K,
+                                                    uint32_t* __restrict__ out) {
+  const int64_t words = (int64_t)N * K / 8;
+  const int kblocks = K / 128;
+  for (int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; id < words; id += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t b = id / 256;
+    const int within = (int)(id % 256);
+    const int L = within / 4, j = within % 4;
+    const int64_t n = (b / kblocks) * 16 + (L % 16);
+    const int64_t k = (b % kblocks) * 128 + 32 * j + 8 * (L / 16);
+    const uint32_t u = *(const uint32_t*)(w + n * (K / 2) + k / 2);
+    uint32_t lo = u & 0x0F0F0F0Fu, hi = (u >> 4) & 0x0F0F0F0Fu;
+    lo = (lo | (lo >> 4)) & 0x00FF00FFu;
+    lo = (lo | (lo >> 8)) & 0x0000FFFFu;
+    hi = (hi | (hi >> 4)) & 0x00FF00FFu;
+    hi = (hi | (hi >> 8)) & 0x0000FFFFu;
+    out[id] = lo | (hi << 16);
+  }
+}
+
+hipError_t launch_prepack_w4(const uint8_t* w, int N, int K, uint8_t* out, hipStream_t stream) {
+  const int64_t words = (int64_t)N * K / 8;
+  int64_t blocks = (words + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(k_prepack_w4, dim3((unsigned)blocks), dim3(256), 0, stream, w, N, K, (uint32_t*)out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Skinny-M kernel.  Workgroup = KW waves over NB 16-row weight blocks; wave w
+// owns a contiguous range of 128-wide k-blocks.  Per k-block a lane loads, per
+// weight block, its 16 prepacked bytes (row L % 16, k-group L / 16 of the four
+// 32-k sub-blocks) plus that row's scale and zero, and, per 16-token tile, the
+// matching four 16-byte X fragments (token L % 16, same k-groups).  The next
+// k-block's loads are issued before the current one is multiplied.
+// ---------------------------------------------------------------------------
+template <int NB, int MT>
+struct SkinnyStage {
+  u32x4 w[NB];
+  uint32_t sz[NB];
+  u32x4 x[MT][4];
+};
+
+template <int NB, int MT>
+__device__ __forceinline__ void skinny_load(SkinnyStage<NB, MT>& st, const W4Launch& a, int n_base, int kb,
+                                            int kblocks, int lane) {
+  const int r = lane & 15, h = lane >> 4;
+  const int grp = (kb * 128) / a.group;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n = n_base + nb * 16 + r;
+    if (n_base + nb * 16 < a.N) {
+      st.w[nb] = *(const u32x4*)(a.w + ((int64_t)((n_base / 16 + nb) * kblocks + kb) * 1024 + lane * 16));
+      const uint32_t s = a.scales[(int64_t)grp * a.N + n];
+      const uint32_t z = (a.zeros[(int64_t)grp * (a.N / 2) + n / 2] >> ((n & 1) * 4)) & 15u;
+      st.sz[nb] = s | (z << 16);
+    } else {
+      st.w[nb] = u32x4{0, 0, 0, 0};
+      st.sz[nb] = 0;
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int tok = mt * 16 + r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (tok < a.M)
+        st.x[mt][j] = *(const u32x4*)(a.X + (int64_t)tok * a.ldx + kb * 128 + j * 32 + h * 8);
+      else
+        st.x[mt][j] = u32x4{0, 0, 0, 0};
+    }
+  }
+}
+
+template <int NB, int MT>
+__device__ __forceinline__ void skinny_mma(const SkinnyStage<NB, MT>& st, f32x4 (&acc)[NB][MT]) {
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const f16x2 ss = scale_pair(st.sz[nb] & 0xffffu), zz = zero_pair(st.sz[nb] >> 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4 wf = dequant8(st.w[nb][j], zz, ss);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = mfma16<DT_F16>(wf, st.x[mt][j], acc[nb][mt]);
+    }
+  }
+}
+
+template <int NB, int KW, int MT>
+__global__ __launch_bounds__(64 * KW) void k_w4a16_skinny(W4Launch a) {
+  __shared__ f32x4 red[KW][NB * MT * 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n_base = blockIdx.x * NB * 16;
+  const int kblocks = a.K / 128;
+  const int per = (kblocks + KW - 1) / KW;
+  const int kb0 = wave * per;
+  const int kb1 = kb0 + per < kblocks ? kb0 + per : kblocks;
+
+  f32x4 acc[NB][MT];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = f32x4{0, 0, 0, 0};
+
+  if (kb0 < kb1) {
+    SkinnyStage<NB, MT> cur, nxt;
+    skinny_load<NB, MT>(cur, a, n_base, kb0, kblocks, lane);
+    for (int kb = kb0; kb < kb1; ++kb) {
+      if (kb + 1 < kb1) skinny_load<NB, MT>(nxt, a, n_base, kb + 1, kblocks, lane);
+      skinny_mma<NB, MT>(cur, acc);
+      cur = nxt;
+    }
+  }
+
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) red[wave][(nb * MT + mt) * 64 + lane] = acc[nb][mt];
+  __syncthreads();
+
+  // lane-quad q of (nb, mt): rows n = n_base + 16 nb + 4 (q / 16) + {0..3}, token 16 mt + q % 16
+  for (int idx = threadIdx.x; idx < NB * MT * 64; idx += 64 * KW) {
+    f32x4 s = red[0][idx];
+#pragma unroll
+    for (int w = 1; w < KW; ++w) s += red[w][idx];
+    const int nb = idx / (MT * 64), mt = (idx / 64) % MT, q = idx % 64;
+    const int n = n_base + nb * 16 + 4 * (q / 16), tok = mt * 16 + (q % 16);
+    if (tok < a.M && n < a.N) {
+      *(u32x2*)(a.Y + (int64_t)tok * a.ldy + n) = u32x2{to_bits<DT_F16>(s[0]) | (to_bits<DT_F16>(s[1]) << 16),
+                                                        to_bits<DT_F16>(s[2]) | (to_bits<DT_F16>(s[3]) << 16)};
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Large-M kernel: the dense mainloop, X as the A operand, the prepacked
+// weight (dequantised on its way into LDS) as the column-major B operand.
+// ---------------------------------------------------------------------------
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::THREADS) void k_w4a16_tiled(W4Launch a, int tiles_m, int total_tiles) {
+  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
+  const int G = gridDim.x;
+  const W4Geom g{a.w, a.scales, a.zeros, a.N, a.K, a.group};
+  for (int base = 0; base < total_tiles; base += G) {
+    const int tile = base + remap_slot(blockIdx.x, G);
+    if (tile >= total_tiles) break;
+    Tile t;
+    t.M = a.M;
+    t.N = a.N;
+    t.K = a.K;
+    t.m0 = (tile % tiles_m) * Cfg::BM;
+    t.n0 = (tile / tiles_m) * Cfg::BN;
+    t.C = nullptr;
+    t.ldc = 0;
+    t.D = a.Y;
+    t.ldd = a.ldy;
+    DenseLoader<Cfg::BM, Cfg::THREADS> al;
+    W4Loader<Cfg::BN, Cfg::THREADS> bl;
+    al.init(a.X, a.ldx, t.m0, t.M, t.K);
+    bl.init(g, t.n0);
+    f32x16 acc[Cfg::TM][Cfg::TN];
+    mainloop<Cfg, DT_F16>(lds, al, bl, t.K / BK, acc);
+    epilogue<Cfg, DT_F16>(t, acc, 1.0f, 0.0f);
+  }
+}
+
+using W4Cfg256 = TileCfg<256, 256, 2, 2>;
+using W4Cfg128 = TileCfg<128, 128, 2, 2>;
+
+hipError_t launch_w4a16(const W4Launch& a, hipStream_t stream) {
+  if (a.M <= 64) {
+    constexpr int NB = 2, KW = 8;
+    const dim3 grid((a.N + NB * 16 - 1) / (NB * 16)), block(64 * KW);
+    if (a.M <= 16)
+      hipLaunchKernelGGL((k_w4a16_skinny<NB, KW, 1>), grid, block, 0, stream, a);
+    else if (a.M <= 32)
+      hipLaunchKernelGGL((k_w4a16_skinny<NB, KW, 2>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_w4a16_skinny<NB, KW, 4>), grid, block, 0, stream, a);
+    return hipGetLastError();
+  }
+  const int cus = device_cu_count();
+  const int t256 = ((a.M + 255) / 256) * ((a.N + 255) / 256);
+  const bool big = t256 >= cus;
+  const int bm = big ? 256 : 128, bn = big ? 256 : 128;
+  const int tiles_m = (a.M + bm - 1) / bm;
+  const int total = tiles_m * ((a.N + bn - 1) / bn);
+  const int resident = cus * (big ? 1 : 2);
+  int grid = (total + XCDS - 1) / XCDS * XCDS;
+  if (grid > resident) grid = resident / XCDS * XCDS;
+  if (big)
+    hipLaunchKernelGGL((k_w4a16_tiled<W4Cfg256>), dim3(grid), dim3(W4Cfg256::THREADS), 0, stream, a, tiles_m, total);
+  else
+    hipLaunchKernelGGL((k_w4a16_tiled<W4Cfg128>), dim3(grid), dim3(W4Cfg128::THREADS), 0, stream, a, tiles_m, total);
+  return hipGetLastError();
+}
+
+}  // namespace gmi

@@ -1,0 +1,174 @@
+/*
+ * gmi.h -- grouped, mixed-input and implicit-convolution GEMM on AMD MI355X
+ * (gfx950).  Plain C ABI: device pointers, host sizes, no exceptions.
+ *
+ * One tiled GEMM mainloop computes D = alpha * A B + beta * C with fp32
+ * accumulation.  A persistent tile scheduler runs it over a list of problems
+ * (grouped: a shape and leading dimensions per problem; pointer-array: one
+ * shape, one pointer per batch).  The same mainloop serves two variants: a
+ * mixed-input product Y = X W^T whose 4-bit weights are prepacked once and
+ * dequantised in registers with per-group scales and zero points, and an
+ * implicit-GEMM convolution forward pass that addresses an NHWC activation
+ * and a KRSC filter directly instead of building an im2col buffer.
+ *
+ * Conventions shared by every call
+ *   - Memory.  Every tensor argument is a device pointer to caller-owned
+ *     memory, except where a parameter says "host".  The library allocates
+ *     nothing and keeps no pointer after a call returns.
+ *   - Ordering.  Work is enqueued on `stream` (a hipStream_t; NULL is the
+ *     null stream) and the call returns without synchronising.
+ *   - Layouts.  Leading dimensions and strides count elements.  A is
+ *     row-major [M][lda] (K contiguous); B is column-major, column n at
+ *     B + n * ldb (K contiguous); C and D are row-major [M][ldc / ldd]
+ *     (N contiguous).
+ *   - Rounding.  The fp32 result alpha * acc + beta * C is rounded to the
+ *     output type to nearest, ties to even.  beta == 0 means C is never read.
+ *   - Alignment.  Base pointers of A, B, C, D, X, Y, W, x, w, y must be
+ *     16-byte aligned and every leading dimension a multiple of 8 elements
+ *     (128-bit accesses), else GMI_ERR_MISALIGNED.
+ *   - Errors.  Every argument is checked on the host before any HIP call; a
+ *     failed check returns a status, records a message for gmi_last_error()
+ *     and launches nothing.  A failed launch returns GMI_ERR_HIP.
+ *   - Aliasing.  D may be C exactly (same pointer and leading dimension);
+ *     any other overlap between an output and an input is undefined.
+ */
+#ifndef GMI_H
+#define GMI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GMI_OK = 0,
+  GMI_ERR_INVALID_ARG = 1, /* negative size, NULL pointer, ld too small, ... */
+  GMI_ERR_UNSUPPORTED = 2, /* valid request outside what the kernels cover  */
+  GMI_ERR_MISALIGNED = 3,  /* pointer or leading dimension not 128-bit aligned */
+  GMI_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required   */
+  GMI_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed   */
+} gmi_status;
+
+typedef enum { GMI_F16 = 0, GMI_BF16 = 1 } gmi_dtype;
+
+/* One problem of a grouped GEMM (host memory; the pointers are device
+ * pointers).  Mirrors the per-group problem shape (M, N, K) and the per-group
+ * strides of the grouped mode on the page
+ * sm90_gemm_array_tma_warpspecialized_cooperative.hpp (Arguments; the
+ * grouped-vs-array distinction of its stride types).  A problem with M == 0
+ * or N == 0 is a valid no-op and its pointers may be NULL.  K == 0 gives
+ * D = beta * C. */
+typedef struct {
+  int32_t M, N, K;
+  int64_t lda, ldb, ldc, ldd; /* lda >= K, ldb >= K, ldc >= N (if C read), ldd >= N */
+  const void* A;
+  const void* B;
+  const void* C; /* may be NULL iff beta == 0 */
+  void* D;
+} gmi_problem;
+
+/* Device workspace needed by gmi_gemm_grouped for `problem_count` problems:
+ * the per-problem descriptor table (80 bytes each) plus a 256-byte header.
+ * Returns 0 for a negative count. */
+size_t gmi_workspace_bytes(int32_t problem_count);
+
+/* Grouped GEMM: D_g = alpha * A_g B_g + beta * C_g for g < count, all in one
+ * persistent launch.  Follows the grouped problem mode of
+ * sm90_gemm_array_tma_warpspecialized_cooperative.hpp (problem_shape per
+ * group, per-group strides, persistent tile loop with a per-group shape
+ * refresh; can_implement).
+ *   problems   host array of `count` descriptors; it may be reused as soon as
+ *              the call returns (the table is staged into `workspace`).
+ *   dtype      element type of A, B, C and D (fp16 or bf16); fp32 accumulate.
+ *   workspace  device buffer of at least gmi_workspace_bytes(count) bytes,
+ *              16-byte aligned; overwritten by the call and read by the kernel
+ *              until it completes on `stream`.
+ * count == 0, or all problems empty, launches nothing and returns GMI_OK. */
+gmi_status gmi_gemm_grouped(const gmi_problem* problems, int32_t count, gmi_dtype dtype, float alpha,
+                            float beta, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Pointer-array batched GEMM: L problems of one shape (M, N, K) and shared
+ * leading dimensions, each operand a separate device buffer.  The pointer
+ * arrays themselves are device arrays of L device pointers.  Follows the
+ * array problem mode (rank-4 problem shape (M, N, K, L), one stride per
+ * operand shared by all batches) of
+ * sm90_gemm_array_tma_warpspecialized_cooperative.hpp.
+ *   C        may be NULL iff beta == 0; otherwise L valid pointers.
+ * No workspace is needed. */
+gmi_status gmi_gemm_ptr_array(int32_t L, int32_t M, int32_t N, int32_t K, const void* const* A, int64_t lda,
+                              const void* const* B, int64_t ldb, const void* const* C, int64_t ldc,
+                              void* const* D, int64_t ldd, gmi_dtype dtype, float alpha, float beta,
+                              void* stream);
+
+/* Size in bytes of a prepacked uint4 weight: N * K / 2. */
+size_t gmi_prepack_w4_bytes(int32_t N, int32_t K);
+
+/* Prepack a uint4 weight W, logically [N][K] (Y = X W^T), from its plain
+ * packed form [N][K/2] bytes (element (n, k) in byte n*K/2 + k/2, even k in
+ * the low nibble) into the order the W4A16 kernels consume.  The design note
+ * of machete_mainloop.cuh motivates it: reorder the narrow operand once so
+ * that each lane's values for several consecutive matrix instructions arrive
+ * in one 128-bit load.  The permutation (requires N % 16 == 0, K % 128 == 0):
+ *   block b = (n/16) * (K/128) + k/128, 1024 bytes at offset 1024 b;
+ *   inside a block, lane L = 16 * ((k % 32) / 8) + n % 16 owns 16 bytes at
+ *   16 L: four little-endian 32-bit words, word j = (k % 128) / 32, each
+ *   holding the 8 consecutive k = 8 * ((k % 32) / 8) + e of its row, element
+ *   e in nibble slot e/2 + 4 (e % 2) (even elements in bits 0-15, odd ones in
+ *   bits 16-31).
+ * A bijection on the N*K/2 bytes; `w_u4` and `w_prepacked` must not overlap. */
+gmi_status gmi_prepack_w4(const uint8_t* w_u4, int32_t N, int32_t K, uint8_t* w_prepacked, void* stream);
+
+/* Mixed-input GEMM Y = X W^T, 4-bit weights with per-group scales and zero
+ * points: w[n][k] = (q[n][k] - z[k/g][n]) * s[k/g][n], the conversion mode
+ * "convert, scale, add zero" of machete_mainloop.cuh (ConversionMode
+ * ConvertAndScaleWithZero; scale_k = ceil(K / group_size) from
+ * to_underlying_arguments; transform_A_kblock).  The zero point is read here
+ * as an unsigned 4-bit offset subtracted before scaling.  Each weight is
+ * dequantised to fp16 as RN16((q - z) * s), then multiplied with X in fp16
+ * with fp32 accumulation; Y is rounded to fp16.
+ *   X            fp16 [M][ldx], ldx >= K.
+ *   w_prepacked  gmi_prepack_w4 output for the [N][K] weight.
+ *   scales       fp16 [K/group_size][N] (n contiguous).
+ *   zeros        uint4 [K/group_size][N/2] bytes, even n in the low nibble.
+ *   group_size   > 0, K % group_size == 0, and group_size == K or
+ *                group_size % 128 == 0 (the page's rule: the group size is K
+ *                or a whole number of K tiles).
+ *   Y            fp16 [M][ldy], ldy >= N.
+ * Requires N % 16 == 0, K % 128 == 0, scales and zeros 16-byte aligned. */
+gmi_status gmi_gemm_w4a16(int32_t M, int32_t N, int32_t K, const void* X, int64_t ldx, const uint8_t* w_prepacked,
+                          const void* scales, const uint8_t* zeros, int32_t group_size, void* Y, int64_t ldy,
+                          void* stream);
+
+/* Implicit-GEMM conv2d forward (cross-correlation, groups == 1):
+ *   y[n][p][q][k] = alpha * sum_{r,s,c} x[n][p*sh - ph + r*dh][q*sw - pw + s*dw][c] * w[k][r][s][c]
+ *                   + beta * c_in[n][p][q][k]
+ * taps outside the image read as 0.  P = (H + 2 ph - dh (R-1) - 1) / sh + 1,
+ * Q likewise.  The GEMM view is M = N*P*Q, N = K, K = R*S*C with (r, s, c),
+ * c fastest, so the KRSC filter is the column-major B operand unchanged.
+ * Follows sm100_implicit_gemm_umma_warpspecialized.hpp: the activation
+ * addressed through im2col with padding, traversal stride and dilation
+ * (get_tma_load_a_instance), the linearised problem shape
+ * (get_problem_shape_MNKL), and can_implement (cross-correlation only,
+ * channel-innermost tensors, traversal stride 1..8).
+ *   x      NHWC, w KRSC, c_in and y NPQK (all packed), element type dtype.
+ *   c_in   may be NULL iff beta == 0.
+ * Requires C % 8 == 0 and K % 8 == 0 (128-bit channel runs, else
+ * GMI_ERR_MISALIGNED), stride in [1, 8] (a larger stride gives
+ * GMI_ERR_UNSUPPORTED), dilation >= 1, padding >= 0, P >= 1, Q >= 1, and
+ * N*P*Q, N*H*W below 2^31. */
+gmi_status gmi_conv2d_fprop_implicit(int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int32_t R, int32_t S,
+                                     int32_t pad_h, int32_t pad_w, int32_t stride_h, int32_t stride_w,
+                                     int32_t dil_h, int32_t dil_w, const void* x, const void* w, const void* c_in,
+                                     void* y, gmi_dtype dtype, float alpha, float beta, void* stream);
+
+/* Text of the last failed check or HIP error on the calling thread ("" if
+ * none).  The pointer stays valid until the next gmi_* call on that thread. */
+const char* gmi_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GMI_H */

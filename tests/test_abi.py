@@ -1,0 +1,169 @@
+"""The C ABI without a GPU: libgmi.so loads, exports every function that
+include/gmi.h declares, and rejects each invalid request with its status and
+a message before any HIP call (validation is host code that runs first)."""
+import ctypes
+import pathlib
+import re
+
+import pytest
+
+ROOT = pathlib.Path(__file__).resolve().parents[1]
+
+
+@pytest.fixture(scope="module")
+def gmi():
+    import grouped_mixed_input_amd as g
+
+    if not g.LIB_PATH.exists():
+        from grouped_mixed_input_amd import build
+
+        build.build()
+    g.lib()
+    return g
+
+
+def declared_functions():
+    text = (ROOT / "include" / "gmi.h").read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gmi_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ["gmi_gemm_grouped", "gmi_gemm_ptr_array", "gmi_prepack_w4", "gmi_gemm_w4a16",
+                 "gmi_conv2d_fprop_implicit", "gmi_workspace_bytes", "gmi_prepack_w4_bytes", "gmi_last_error"]:
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(gmi):
+    lib = ctypes.CDLL(str(gmi.LIB_PATH))
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_size_helpers(gmi):
+    L = gmi.lib()
+    assert L.gmi_workspace_bytes(0) == 256
+    assert L.gmi_workspace_bytes(128) == 256 + 80 * 128
+    assert L.gmi_workspace_bytes(-1) == 0
+    assert L.gmi_prepack_w4_bytes(8192, 8192) == 8192 * 8192 // 2
+    assert L.gmi_prepack_w4_bytes(-1, 4) == 0
+
+
+A16 = 0x10000  # fake, 16-byte aligned device addresses: never dereferenced by a rejected call
+
+
+def _grouped(gmi, probs, dtype=0, beta=0.0, ws=A16 * 64, ws_bytes=1 << 20):
+    arr = (gmi.Problem * len(probs))(*probs) if probs else None
+    st = gmi.lib().gmi_gemm_grouped(arr, len(probs), dtype, 1.0, beta, ws, ws_bytes, None)
+    return st, gmi.lib().gmi_last_error().decode()
+
+
+def P(gmi, M=64, N=64, K=64, lda=64, ldb=64, ldc=64, ldd=64, A=A16, B=A16 * 2, C=A16 * 3, D=A16 * 4):
+    return gmi.Problem(M, N, K, lda, ldb, ldc, ldd, A, B, C, D)
+
+
+def test_grouped_validation(gmi):
+    ok_ws = 1 << 20
+    assert _grouped(gmi, [P(gmi, M=-1)])[0] == gmi.GMI_ERR_INVALID_ARG
+    st, msg = _grouped(gmi, [P(gmi, lda=32)])
+    assert st == gmi.GMI_ERR_INVALID_ARG and "leading dimension" in msg
+    assert _grouped(gmi, [P(gmi, A=None)])[0] == gmi.GMI_ERR_INVALID_ARG
+    assert _grouped(gmi, [P(gmi, C=None)], beta=1.0)[0] == gmi.GMI_ERR_INVALID_ARG
+    assert _grouped(gmi, [P(gmi, A=A16 + 8)])[0] == gmi.GMI_ERR_MISALIGNED
+    assert _grouped(gmi, [P(gmi, lda=68)])[0] == gmi.GMI_ERR_MISALIGNED
+    assert _grouped(gmi, [P(gmi, ldc=60, C=A16 * 3)], beta=0.5)[0] == gmi.GMI_ERR_INVALID_ARG
+    assert _grouped(gmi, [P(gmi)], dtype=7)[0] == gmi.GMI_ERR_UNSUPPORTED
+    st, msg = _grouped(gmi, [P(gmi), P(gmi)], ws_bytes=100)
+    assert st == gmi.GMI_ERR_WORKSPACE and "workspace" in msg
+    assert _grouped(gmi, [P(gmi)], ws=0, ws_bytes=ok_ws)[0] == gmi.GMI_ERR_WORKSPACE
+    assert _grouped(gmi, [P(gmi)], ws=A16 + 4)[0] == gmi.GMI_ERR_MISALIGNED
+    # negative count / NULL table
+    assert gmi.lib().gmi_gemm_grouped(None, -1, 0, 1.0, 0.0, A16, ok_ws, None) == gmi.GMI_ERR_INVALID_ARG
+    assert gmi.lib().gmi_gemm_grouped(None, 2, 0, 1.0, 0.0, A16, ok_ws, None) == gmi.GMI_ERR_INVALID_ARG
+
+
+def test_grouped_empty_requests_launch_nothing(gmi):
+    # zero problems, or only empty ones with NULL pointers: OK without a GPU call
+    assert gmi.lib().gmi_gemm_grouped(None, 0, 0, 1.0, 0.0, None, 0, None) == gmi.GMI_OK
+    empty = [P(gmi, M=0, A=None, B=None, C=None, D=None), P(gmi, N=0, A=None, B=None, C=None, D=None)]
+    assert _grouped(gmi, empty, ws=0, ws_bytes=0)[0] == gmi.GMI_OK
+
+
+def _ptr(gmi, L=2, M=64, N=64, K=64, A=A16, lda=64, B=A16, ldb=64, C=None, ldc=64, D=A16, ldd=64, dt=1, beta=0.0):
+    return gmi.lib().gmi_gemm_ptr_array(L, M, N, K, A, lda, B, ldb, C, ldc, D, ldd, dt, 1.0, beta, None)
+
+
+def test_ptr_array_validation(gmi):
+    assert _ptr(gmi, L=-1) == gmi.GMI_ERR_INVALID_ARG
+    assert _ptr(gmi, K=-3) == gmi.GMI_ERR_INVALID_ARG
+    assert _ptr(gmi, dt=5) == gmi.GMI_ERR_UNSUPPORTED
+    assert _ptr(gmi, A=None) == gmi.GMI_ERR_INVALID_ARG
+    assert _ptr(gmi, beta=1.0) == gmi.GMI_ERR_INVALID_ARG  # C required when beta != 0
+    assert _ptr(gmi, ldb=56) == gmi.GMI_ERR_INVALID_ARG
+    assert _ptr(gmi, ldd=72 + 4) == gmi.GMI_ERR_MISALIGNED
+    assert _ptr(gmi, A=A16 + 4) == gmi.GMI_ERR_MISALIGNED
+    assert _ptr(gmi, L=0, A=None, B=None, D=None) == gmi.GMI_OK
+
+
+def test_prepack_validation(gmi):
+    L = gmi.lib()
+    assert L.gmi_prepack_w4(A16, -16, 128, A16 * 8, None) == gmi.GMI_ERR_INVALID_ARG
+    assert L.gmi_prepack_w4(A16, 24, 128, A16 * 8, None) == gmi.GMI_ERR_UNSUPPORTED
+    assert L.gmi_prepack_w4(A16, 16, 192, A16 * 8, None) == gmi.GMI_ERR_UNSUPPORTED
+    assert L.gmi_prepack_w4(None, 16, 128, A16 * 8, None) == gmi.GMI_ERR_INVALID_ARG
+    assert L.gmi_prepack_w4(A16 + 2, 16, 128, A16 * 8, None) == gmi.GMI_ERR_MISALIGNED
+    assert L.gmi_prepack_w4(A16, 16, 128, A16 + 512, None) == gmi.GMI_ERR_INVALID_ARG  # overlap
+    assert L.gmi_prepack_w4(None, 0, 128, None, None) == gmi.GMI_OK
+
+
+def _w4(gmi, M=16, N=64, K=256, X=A16, ldx=256, W=A16 * 2, S=A16 * 3, Z=A16 * 4, g=128, Y=A16 * 5, ldy=64):
+    return gmi.lib().gmi_gemm_w4a16(M, N, K, X, ldx, W, S, Z, g, Y, ldy, None)
+
+
+def test_w4a16_validation(gmi):
+    assert _w4(gmi, M=-1) == gmi.GMI_ERR_INVALID_ARG
+    assert _w4(gmi, N=24) == gmi.GMI_ERR_UNSUPPORTED
+    assert _w4(gmi, K=200, ldx=200) == gmi.GMI_ERR_UNSUPPORTED
+    assert _w4(gmi, g=0) == gmi.GMI_ERR_INVALID_ARG
+    assert _w4(gmi, g=96) == gmi.GMI_ERR_INVALID_ARG  # K % g != 0
+    assert _w4(gmi, K=384, ldx=384, g=192) == gmi.GMI_ERR_UNSUPPORTED  # neither K nor a multiple of 128
+    assert _w4(gmi, Z=None) == gmi.GMI_ERR_INVALID_ARG  # zero points required
+    assert _w4(gmi, S=None) == gmi.GMI_ERR_INVALID_ARG
+    assert _w4(gmi, ldx=128) == gmi.GMI_ERR_INVALID_ARG
+    assert _w4(gmi, ldy=60) == gmi.GMI_ERR_INVALID_ARG
+    assert _w4(gmi, ldy=68) == gmi.GMI_ERR_MISALIGNED
+    assert _w4(gmi, S=A16 + 2) == gmi.GMI_ERR_MISALIGNED
+    assert _w4(gmi, M=0, X=None, W=None, S=None, Z=None, Y=None) == gmi.GMI_OK
+
+
+def _conv(gmi, N=2, H=8, W=8, C=16, K=16, R=3, S=3, ph=1, pw=1, sh=1, sw=1, dh=1, dw=1, x=A16, w=A16 * 2,
+          c=None, y=A16 * 3, dt=1, beta=0.0):
+    return gmi.lib().gmi_conv2d_fprop_implicit(N, H, W, C, K, R, S, ph, pw, sh, sw, dh, dw, x, w, c, y, dt, 1.0,
+                                               beta, None)
+
+
+def test_conv_validation(gmi):
+    assert _conv(gmi, N=-1) == gmi.GMI_ERR_INVALID_ARG
+    assert _conv(gmi, C=0) == gmi.GMI_ERR_INVALID_ARG
+    assert _conv(gmi, ph=-1) == gmi.GMI_ERR_INVALID_ARG
+    assert _conv(gmi, sh=0) == gmi.GMI_ERR_INVALID_ARG
+    assert _conv(gmi, sw=9) == gmi.GMI_ERR_UNSUPPORTED  # traversal stride limited to 1..8
+    assert _conv(gmi, dh=0) == gmi.GMI_ERR_INVALID_ARG
+    assert _conv(gmi, C=12) == gmi.GMI_ERR_MISALIGNED
+    assert _conv(gmi, K=20) == gmi.GMI_ERR_MISALIGNED
+    assert _conv(gmi, dt=3) == gmi.GMI_ERR_UNSUPPORTED
+    assert _conv(gmi, H=2, R=5, ph=0) == gmi.GMI_ERR_INVALID_ARG  # filter larger than the padded image
+    assert _conv(gmi, x=None) == gmi.GMI_ERR_INVALID_ARG
+    assert _conv(gmi, beta=1.0) == gmi.GMI_ERR_INVALID_ARG  # c_in required
+    assert _conv(gmi, y=A16 + 8) == gmi.GMI_ERR_MISALIGNED
+    assert _conv(gmi, N=0, x=None, w=None, y=None) == gmi.GMI_OK
+
+
+def test_errors_raise_through_the_binding(gmi):
+    import torch
+
+    with pytest.raises(gmi.GmiError, match="GMI_ERR_MISALIGNED"):
+        gmi.gemm_w4a16(torch.empty((16, 256), dtype=torch.float16), torch.empty(16384, dtype=torch.uint8),
+                       torch.empty((2, 64), dtype=torch.float16), torch.empty((2, 32), dtype=torch.uint8), 128, 64,
+                       Y=torch.empty((16, 68), dtype=torch.float16)[:, 2:66], stream=0)
