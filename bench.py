@@ -227,7 +227,7 @@ def main():
                    "cache": f"cold: {R} rotating copies of the {ws / 2**20:.0f} MiB working set"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_16, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_MFMA_16, 4), "traffic": None,
-                     "kernel": "k_gemm_ptr_array<TileCfg<256,256,2,2>, bf16>"},
+                     "kernel": "k_gemm_ptr_array<TileCfg<256,256,2,2,32,4>, bf16, false>"},
     }
     if not args.headline_only:
         result["workloads"] = bench_workloads(torch, gmi, gi, dev, args)

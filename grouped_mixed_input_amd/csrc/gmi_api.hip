@@ -11,6 +11,7 @@
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 #include <vector>
 
@@ -51,12 +52,27 @@ int device_cu_count() {
 }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Operands are read through buffer resources with 32-bit byte offsets: a
+// 256-row tile of any operand must span less than 2^32 bytes.
+constexpr int64_t kMaxLd = int64_t(1) << 22;
 static bool dtype_ok(gmi_dtype d) { return d == GMI_F16 || d == GMI_BF16; }
 
 // Tile shape for a list of problems: 256x256 when it alone fills every CU,
 // then 256x128, else 128x128 (two resident workgroups per CU).
+// GMI_FORCE_TILE=0|1|2 (256x256, 128x128, 256x128) overrides the choice; it
+// exists for tile-shape sweeps in benchmarks.
+static int forced_shape() {
+  static const int f = [] {
+    const char* e = getenv("GMI_FORCE_TILE");
+    return (e && e[0] >= '0' && e[0] <= '2' && e[1] == 0) ? e[0] - '0' : -1;
+  }();
+  return f;
+}
+
 template <class F>
 static int choose_shape(F tiles_at) {
+  if (forced_shape() >= 0) return forced_shape();
   const int64_t cus = device_cu_count();
   if (tiles_at(256, 256) >= cus) return TILE_256x256;
   if (tiles_at(256, 128) >= cus) return TILE_256x128;
@@ -96,6 +112,8 @@ gmi_status gmi_gemm_grouped(const gmi_problem* problems, int32_t count, gmi_dtyp
       return fail(GMI_ERR_INVALID_ARG, "gemm_grouped: problem %d has a NULL operand", g);
     if ((p.K > 0 && (p.lda < p.K || p.ldb < p.K)) || p.ldd < p.N || (use_c && p.ldc < p.N))
       return fail(GMI_ERR_INVALID_ARG, "gemm_grouped: problem %d has a leading dimension below its row width", g);
+    if (p.lda > kMaxLd || p.ldb > kMaxLd || p.ldd > kMaxLd || (use_c && p.ldc > kMaxLd))
+      return fail(GMI_ERR_UNSUPPORTED, "gemm_grouped: problem %d: a leading dimension above 2^22 elements", g);
     if ((p.K > 0 && (!aligned16(p.A) || !aligned16(p.B) || p.lda % 8 || p.ldb % 8)) || !aligned16(p.D) ||
         p.ldd % 8 || (use_c && (!aligned16(p.C) || p.ldc % 8)))
       return fail(GMI_ERR_MISALIGNED, "gemm_grouped: problem %d: pointers must be 16-byte aligned, ld multiples of 8",
@@ -117,9 +135,11 @@ gmi_status gmi_gemm_grouped(const gmi_problem* problems, int32_t count, gmi_dtyp
   std::vector<GroupDesc> desc;
   desc.reserve(live);
   int64_t tiles = 0;
+  bool ktail = false;
   for (int32_t g = 0; g < count; ++g) {
     const gmi_problem& p = problems[g];
     if (p.M == 0 || p.N == 0) continue;
+    ktail = ktail || (p.K % 8) != 0;
     GroupDesc d;
     d.A = (const uint16_t*)p.A;
     d.B = (const uint16_t*)p.B;
@@ -145,7 +165,7 @@ gmi_status gmi_gemm_grouped(const gmi_problem* problems, int32_t count, gmi_dtyp
       hipMemcpyAsync(dev_desc, desc.data(), sizeof(GroupDesc) * desc.size(), hipMemcpyHostToDevice, s),
       "gemm_grouped: staging the problem table");
   if (st != GMI_OK) return st;
-  return hip_status(launch_grouped(dev_desc, live, (int)tiles, shape, (int)dtype, alpha, beta, s),
+  return hip_status(launch_grouped(dev_desc, live, (int)tiles, shape, (int)dtype, ktail, alpha, beta, s),
                     "gemm_grouped: launch");
 }
 
@@ -164,6 +184,8 @@ gmi_status gmi_gemm_ptr_array(int32_t L, int32_t M, int32_t N, int32_t K, const 
     return fail(GMI_ERR_INVALID_ARG, "gemm_ptr_array: leading dimension below its row width");
   if ((K > 0 && (lda % 8 || ldb % 8)) || ldd % 8 || (use_c && ldc % 8))
     return fail(GMI_ERR_MISALIGNED, "gemm_ptr_array: leading dimensions must be multiples of 8");
+  if (lda > kMaxLd || ldb > kMaxLd || ldd > kMaxLd || (use_c && ldc > kMaxLd))
+    return fail(GMI_ERR_UNSUPPORTED, "gemm_ptr_array: a leading dimension above 2^22 elements");
   if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)D | (uintptr_t)(use_c ? C : nullptr)) & 7u)
     return fail(GMI_ERR_MISALIGNED, "gemm_ptr_array: pointer arrays must be 8-byte aligned");
   const int shape = choose_shape([&](int bm, int bn) { return (int64_t)L * cdiv(M, bm) * cdiv(N, bn); });
@@ -217,6 +239,8 @@ gmi_status gmi_gemm_w4a16(int32_t M, int32_t N, int32_t K, const void* X, int64_
     return fail(GMI_ERR_INVALID_ARG, "gemm_w4a16: K %d is not a multiple of group_size %d", K, group_size);
   if (group_size != K && group_size % 128)
     return fail(GMI_ERR_UNSUPPORTED, "gemm_w4a16: group_size must equal K or be a multiple of 128");
+  if ((int64_t)N * K / 2 > INT32_MAX || (int64_t)M * ldx * 2 > INT32_MAX || ldy > kMaxLd)
+    return fail(GMI_ERR_UNSUPPORTED, "gemm_w4a16: W (N*K/2 bytes) and X (M*ldx*2 bytes) must stay below 2^31 bytes");
   if (M == 0 || N == 0) return GMI_OK;
   if (!Y || (K > 0 && (!X || !w_prepacked || !scales || !zeros)))
     return fail(GMI_ERR_INVALID_ARG, "gemm_w4a16: NULL pointer");
@@ -260,6 +284,8 @@ gmi_status gmi_conv2d_fprop_implicit(int32_t N, int32_t H, int32_t W, int32_t C,
     return fail(GMI_ERR_INVALID_ARG, "conv2d_fprop: the filter does not fit the padded image (P, Q < 1)");
   if ((int64_t)N * P * Q > INT32_MAX || (int64_t)N * H * W > INT32_MAX || (int64_t)R * S * C > INT32_MAX)
     return fail(GMI_ERR_INVALID_ARG, "conv2d_fprop: problem too large for 32-bit pixel / tap indices");
+  if ((int64_t)N * H * W * C * 2 > INT32_MAX || (int64_t)R * S * C > kMaxLd || K > kMaxLd)
+    return fail(GMI_ERR_UNSUPPORTED, "conv2d_fprop: activation above 2^31 bytes or R*S*C above 2^22");
   if (N == 0) return GMI_OK;
   const bool use_c = beta != 0.0f;
   if (!x || !w || !y || (use_c && !c_in)) return fail(GMI_ERR_INVALID_ARG, "conv2d_fprop: NULL pointer");

@@ -1,14 +1,16 @@
 // gmi_device.hpp -- device building blocks shared by every kernel of the
-// library: element types, gfx950 MFMA wrappers, the LDS tile layout, operand
-// loaders (dense, implicit-conv, prepacked uint4), the tiled mainloop, the
-// alpha/beta epilogue and the persistent tile walk.
+// library: element types, gfx950 MFMA wrappers, buffer and direct-to-LDS
+// memory access, the LDS tile layout, operand loaders (dense, implicit-conv,
+// prepacked uint4), the multi-stage mainloop, the alpha/beta epilogue and the
+// persistent tile walk.
 //
 // The mainloop follows the structure of the persistent grouped GEMM kernel on
 // the page sm90_gemm_array_tma_warpspecialized_cooperative.hpp (operator():
 // a work-tile loop, a k-tile loop that accumulates in fp32 starting from
 // zero, an epilogue store per tile) rebuilt for CDNA4: every wave both loads
-// and computes, operands are staged global -> VGPR -> LDS in two ping-pong
-// buffers, and v_mfma_f32_32x32x16_{f16,bf16} consumes 128-bit LDS reads.
+// and computes; operand k-tiles stream from memory straight into a ring of
+// LDS stages (buffer_load ... lds), several k-tiles ahead of the multiply;
+// v_mfma_f32_32x32x16_{f16,bf16} consumes conflict-free 128-bit LDS reads.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -70,27 +72,115 @@ __device__ __forceinline__ float from_bits(uint32_t b) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS operand tile: rows of 64 k values (128 bytes = eight 16-byte chunks).
-// Chunk c of row r lives at chunk slot c ^ (r & 7), so the eight rows read by
-// any eight consecutive lanes of a fragment load fall in distinct slots.
+// Buffer access.  A buffer resource (4 SGPRs: base, size in bytes) is
+// wave-uniform; each lane adds a 32-bit byte offset.  A load at or past the
+// size returns zeros and a store there is dropped, which zero-fills the rows
+// of a tile that lie past the end of an operand and any lane pointed at OOB.
 // ---------------------------------------------------------------------------
-constexpr int BK = 64;
-__device__ __forceinline__ int lds_off(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t OOB = 0x80000000u;  // offset past every resource this library builds
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // base and size are wave-uniform by construction; readfirstlane makes that
+  // visible to the compiler so the resource lives in SGPRs
+  const uint64_t a = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+typedef __attribute__((address_space(1))) u32x2 gu32x2;  // global-memory pointer target
+typedef __attribute__((address_space(3))) void lds_void;
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at
+// dst + 16 l (dst wave-uniform).  Completion is counted by vmcnt.
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t off, char* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, (int)off, 0, 0, 0);
+}
+// as dma16, with a wave-uniform byte offset soff added to the lane offset
+__device__ __forceinline__ void dma16s(rsrc_t r, uint32_t off, uint32_t soff, char* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, (int)off, (int)soff, 0, 0);
+}
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ u32x2 buf_load8(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buf_load2(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint32_t buf_load1(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store8(rsrc_t r, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store2(rsrc_t r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, (int)off, 0, 0);
+}
+
+// s_waitcnt: gfx9 encoding, vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8
+template <int N>
+__device__ __forceinline__ void wait_vm_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+__device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07F); }  // lgkmcnt(0)
+
+// Zero the 16-bit elements e >= n (0 <= n < 8) of an 8-element chunk.
+__device__ __forceinline__ u32x4 mask_tail(u32x4 v, int n) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int e = 2 * w;
+    const uint32_t keep = (e + 1 < n) ? 0xffffffffu : (e < n ? 0x0000ffffu : 0u);
+    v[w] &= keep;
+  }
+  return v;
+}
 
 // ---------------------------------------------------------------------------
-// Tile configuration: BM x BN output tile, 4 waves arranged WM_ x WN_.
+// Tile configuration: BM x BN output tile, 4 waves arranged WAVES_M x
+// WAVES_N, BK k per stage, STAGES LDS stages in a ring.
+//
+// LDS operand tile: rows of BK values (ROWB = 2 BK bytes, CPR 16-byte chunks).
+// gfx950's LDS serves 256 bytes (64 four-byte banks) per cycle; a 128-bit
+// read is conflict-free when each group of 16 lanes covers all 64 banks.  A
+// fragment read has 16 lanes on 16 consecutive rows and one chunk c; a bank
+// line holds RPL = 256 / ROWB consecutive rows, so chunk c of row r goes to
+// slot c ^ ((r / RPL) % CPR): the rows sharing a bank position within their
+// lines get distinct slots.
 // ---------------------------------------------------------------------------
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int STAGES_>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
+  // workgroups one CU holds: LDS-bound (160 KB); the kernels' launch bounds
+  // hold the registers to match (waves per SIMD = workgroups per CU)
+  static constexpr int WGS_PER_CU = (160 * 1024) / (STAGES_ * (BM_ + BN_) * BK_ * 2) >= 2 ? 2 : 1;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
   static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;  // wave tile
   static constexpr int TM = WTM / 32, TN = WTN / 32;            // 32x32 blocks per wave
-  static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+  static constexpr int ROWB = BK * 2, CPR = ROWB / 16, RPL = 256 / ROWB;
+  static constexpr int RPI = 1024 / ROWB;  // rows moved by one 1 KB wave copy
+  static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static_assert(BK == 32 || BK == 64, "k-tile of 32 or 64");
+  static_assert(THREADS == 256, "4 waves");
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
+  static_assert(STAGES >= 2 && LDS_BYTES <= 160 * 1024, "LDS budget");
+  __device__ static __forceinline__ int swz(int row) { return (row / RPL) % CPR; }
+  __device__ static __forceinline__ int off(int row, int chunk) { return row * ROWB + ((chunk ^ swz(row)) << 4); }
+  // direct-to-LDS copies: instruction i of wave w fills rows RPI (4 i + w) + l / CPR;
+  // lane l writes slot l % CPR of its row, i.e. k-chunk (l % CPR) ^ swz(row)
+  __device__ static __forceinline__ int dma_row(int i, int lane) { return RPI * (4 * i + wave_id()) + lane / CPR; }
+  __device__ static __forceinline__ int dma_chunk(int lane) { return (lane % CPR) ^ swz(dma_row(0, lane)); }
+  // wave-uniform (scalar) LDS destination of copy i
+  __device__ static __forceinline__ char* dma_dst(char* tile, int i) { return tile + (4 * i + wave_id()) * 1024; }
 };
 
 // One output tile of one GEMM problem, as the persistent walk hands it out.
@@ -108,90 +198,156 @@ struct Tile {
 };
 
 // ---------------------------------------------------------------------------
-// Dense K-contiguous operand loader: ROWS rows x 64 k per k-tile.  Thread t
-// moves chunk t % 8 of rows t / 8 + i * (THREADS / 8), 16 bytes each.
-// Rows past `rows_valid` and k past K read as zero.
+// Dense K-contiguous operand (direct to LDS): ROWS rows x BK k per k-tile
+// through a buffer resource spanning exactly the tile's rows inside the
+// problem, so rows past the end land as zeros.  Chunks at or past K are
+// pointed out of range; a chunk that straddles K (K % 8 != 0, KTAIL) is
+// masked in LDS after it lands.
 // ---------------------------------------------------------------------------
-template <int ROWS, int THREADS>
+template <class Cfg, int ROWS, bool KTAIL = false>
 struct DenseLoader {
-  static constexpr int RPP = THREADS / 8;
-  static constexpr int P = ROWS / RPP;
-  static_assert(ROWS % RPP == 0, "rows must be a multiple of THREADS / 8");
-  struct Regs {
-    u32x4 v[P];
+  static constexpr bool kDMA = true;
+  static constexpr bool kFIX = KTAIL;  // fix_tail may write LDS
+  static constexpr int P = ROWS * Cfg::ROWB / 4096;  // 1 KB copies per wave per k-tile
+  static_assert(P >= 1 && ROWS % (4 * Cfg::RPI) == 0, "rows must fill whole copy passes");
+  rsrc_t rs;
+  uint32_t voff[P];  // lane offset of copy i within k-tile 0, bytes
+  int K, nk;
+  // per-k-tile state: the scalar k-tile offset (clamped to the last k-tile, so
+  // copies past the end re-read valid data), and, for a K that is not a
+  // multiple of BK, the lanes whose chunk starts past K
+  struct Prep {
+    uint32_t soff;
+    uint32_t vo[P];  // lane offset of copy i, or OOB for a chunk past K
   };
-  const uint16_t* p0;  // row (t / 8) of this tile, or null when no row is valid
-  int64_t step;        // RPP rows, in elements
-  int nvalid;          // passes whose row is inside the problem
-  int K;
 
   __device__ __forceinline__ void init(const uint16_t* base, int64_t ld, int row0, int rows, int K_) {
-    int r = threadIdx.x / 8;
-    int left = rows - row0 - r;  // rows available from this thread's first row
-    nvalid = left <= 0 ? 0 : (left + RPP - 1) / RPP;
-    if (nvalid > P) nvalid = P;
-    p0 = base + (int64_t)(row0 + r) * ld + (threadIdx.x & 7) * 8;
-    step = (int64_t)RPP * ld;
+    int left = rows - row0;
+    if (left > ROWS) left = ROWS;
+    if (left < 0) left = 0;
+    rs = make_rsrc(base + (int64_t)row0 * ld, (uint32_t)left * (uint32_t)ld * 2u);
+    const int lane = threadIdx.x & 63;
+    const uint32_t v0 = (uint32_t)Cfg::dma_row(0, lane) * (uint32_t)ld * 2u + (uint32_t)Cfg::dma_chunk(lane) * 16u;
+    const uint32_t step = 4u * Cfg::RPI * (uint32_t)ld * 2u;
+#pragma unroll
+    for (int i = 0; i < P; ++i) voff[i] = v0 + i * step;
     K = K_;
+    nk = (K_ + Cfg::BK - 1) / Cfg::BK;
   }
 
-  __device__ __forceinline__ void load(int kt, Regs& rg) const {
-    u32x4(&v)[P] = rg.v;
-    const int kc = kt * BK + (threadIdx.x & 7) * 8;
+  __device__ __forceinline__ Prep prep(int kt) const {
+    const int ke = kt < nk ? kt : nk - 1;
+    Prep p;
+    p.soff = (uint32_t)ke * Cfg::ROWB;
+    const bool in = (ke * Cfg::BK + Cfg::dma_chunk(threadIdx.x & 63) * 8) < K;
+#pragma unroll
+    for (int i = 0; i < P; ++i) p.vo[i] = in ? voff[i] : OOB;
+    return p;
+  }
+  // copy i of the prepared k-tile: rows past the problem land as zeros (the
+  // lane offset is past the resource), and so do chunks at or past K
+  __device__ __forceinline__ void issue_one(int i, const Prep& p, char* tile) const {
+    dma16s(rs, p.vo[i], p.soff, Cfg::dma_dst(tile, i));
+  }
+  __device__ __forceinline__ void issue(int kt, char* tile) const {
+    const Prep p = prep(kt);
+#pragma unroll
+    for (int i = 0; i < P; ++i) issue_one(i, p, tile);
+  }
+
+  // after k-tile kt has landed: zero the elements >= K of a straddling chunk
+  __device__ __forceinline__ void fix_tail(int kt, char* tile) const {
+    if constexpr (!KTAIL) return;
+    if ((K & 7) == 0 || kt >= nk || (kt + 1) * Cfg::BK <= K) return;
+    const int lane = threadIdx.x & 63;
+    const int n = K - (kt * Cfg::BK + Cfg::dma_chunk(lane) * 8);
+    if (n <= 0 || n >= 8) return;
 #pragma unroll
     for (int i = 0; i < P; ++i) {
-      const uint16_t* p = p0 + i * step + kt * BK;
-      if (i < nvalid && kc + 8 <= K) {
-        v[i] = *(const u32x4*)p;
-      } else if (i < nvalid && kc < K) {
-        uint32_t h[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = (kc + e < K) ? p[e] : 0u;
-        v[i] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-      } else {
-        v[i] = u32x4{0, 0, 0, 0};
-      }
+      u32x4* p = (u32x4*)(Cfg::dma_dst(tile, i) + lane * 16);
+      *p = mask_tail(*p, n);
     }
-  }
-
-  __device__ __forceinline__ void store(char* lds, const Regs& rg) const {
-#pragma unroll
-    for (int i = 0; i < P; ++i) *(u32x4*)(lds + lds_off(threadIdx.x / 8 + i * RPP, threadIdx.x & 7)) = rg.v[i];
   }
 };
 
 // ---------------------------------------------------------------------------
-// Implicit-GEMM convolution A operand (fprop).  GEMM row m is output pixel
-// (n, p, q), m = (n P + p) Q + q; GEMM column k is filter tap (r, s, c),
-// k = (r S + s) C + c.  Element (m, k) is x[n][p sh - ph + r dh][q sw - pw + s dw][c]
-// or 0 outside the image -- the im2col view of the activation that the page
+// Dense K-contiguous operand, register-staged: the same rows and chunks as
+// DenseLoader, moved with buffer_load_dwordx4 into VGPRs and ds_write_b128
+// into the swizzled LDS tile after the current stage's multiplies.  Thread t
+// moves chunk t % CPR of rows t / CPR + i * (256 / CPR).
+// ---------------------------------------------------------------------------
+template <class Cfg, int ROWS, bool KTAIL = false>
+struct DenseRegLoader {
+  static constexpr bool kDMA = false;
+  static constexpr bool kFIX = false;
+  static constexpr int RPP = Cfg::THREADS / Cfg::CPR;  // rows per pass
+  static constexpr int P = ROWS / RPP;
+  static_assert(ROWS % RPP == 0, "rows must fill whole passes");
+  struct Regs {
+    u32x4 v[P];
+  };
+  rsrc_t rs;
+  uint32_t voff, step;
+  int K;
+
+  __device__ __forceinline__ void init(const uint16_t* base, int64_t ld, int row0, int rows, int K_) {
+    int left = rows - row0;
+    if (left > ROWS) left = ROWS;
+    if (left < 0) left = 0;
+    rs = make_rsrc(base + (int64_t)row0 * ld, (uint32_t)left * (uint32_t)ld * 2u);
+    voff = (uint32_t)(threadIdx.x / Cfg::CPR) * (uint32_t)ld * 2u + (threadIdx.x % Cfg::CPR) * 16u;
+    step = (uint32_t)RPP * (uint32_t)ld * 2u;
+    K = K_;
+  }
+  __device__ __forceinline__ void load(int kt, Regs& rg) const {
+    const int kc = kt * Cfg::BK + (int)(threadIdx.x % Cfg::CPR) * 8;
+    const int n = K - kc;
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const u32x4 v = buf_load16(rs, n > 0 ? voff + i * step + (uint32_t)kt * Cfg::ROWB : OOB);
+      rg.v[i] = (!KTAIL || n >= 8) ? v : mask_tail(v, n);
+    }
+  }
+  __device__ __forceinline__ void store(char* tile, const Regs& rg) const {
+#pragma unroll
+    for (int i = 0; i < P; ++i)
+      *(u32x4*)(tile + Cfg::off(threadIdx.x / Cfg::CPR + i * RPP, threadIdx.x % Cfg::CPR)) = rg.v[i];
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Implicit-GEMM convolution A operand (fprop, direct to LDS).  GEMM row m is
+// output pixel (n, p, q), m = (n P + p) Q + q; GEMM column k is filter tap
+// (r, s, c), k = (r S + s) C + c.  Element (m, k) is
+// x[n][p sh - ph + r dh][q sw - pw + s dw][c], or 0 outside the image -- the
+// im2col view of the activation that the page
 // sm100_implicit_gemm_umma_warpspecialized.hpp builds from the padding,
 // traversal stride and dilation (get_tma_load_a_instance), formed here by
 // address arithmetic instead.  With C % 8 == 0 a 16-byte chunk never
-// straddles two taps, so each chunk is one aligned 128-bit load or zero.
+// straddles two taps, so each chunk is one aligned 128-bit copy or zero.
 // ---------------------------------------------------------------------------
 struct ConvGeom {
   const uint16_t* x;
+  uint32_t x_bytes;  // N * H * W * C * 2 (< 2^31)
   int H, W, C, S;
   int P, Q;
   int ph, pw, sh, sw, dh, dw;
   int Kg;  // R * S * C
 };
 
-template <int ROWS, int THREADS>
+template <class Cfg, int ROWS>
 struct ConvLoader {
-  static constexpr int RPP = THREADS / 8;
-  static constexpr int P = ROWS / RPP;
-  struct Regs {
-    u32x4 v[P];
-  };
-  const uint16_t* x;
+  static constexpr bool kDMA = true;
+  static constexpr bool kFIX = false;
+  static constexpr int P = ROWS * Cfg::ROWB / 4096;
+  static_assert(P >= 1 && ROWS % (4 * Cfg::RPI) == 0, "rows must fill whole copy passes");
+  rsrc_t rs;
   int H, W, C, S, dh, dw, Kg;
-  int pix[P];     // first pixel of the row's image: n * H * W
+  int pix[P];        // first pixel of the row's image: n * H * W
   int h0[P], w0[P];  // input coordinates of tap (0, 0); far negative for rows past M
 
   __device__ __forceinline__ void init(const ConvGeom& g, int m0, int M) {
-    x = g.x;
+    rs = make_rsrc(g.x, g.x_bytes);
     H = g.H;
     W = g.W;
     C = g.C;
@@ -200,9 +356,10 @@ struct ConvLoader {
     dw = g.dw;
     Kg = g.Kg;
     const int PQ = g.P * g.Q;
+    const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < P; ++i) {
-      const int m = m0 + threadIdx.x / 8 + i * RPP;
+      const int m = m0 + Cfg::dma_row(i, lane);
       if (m < M) {
         const int n = m / PQ, rem = m - n * PQ;
         const int p = rem / g.Q, q = rem - p * g.Q;
@@ -217,29 +374,29 @@ struct ConvLoader {
     }
   }
 
-  __device__ __forceinline__ void load(int kt, Regs& rg) const {
-    const int kc = kt * BK + (threadIdx.x & 7) * 8;
-    if (kc >= Kg) {
-#pragma unroll
-      for (int i = 0; i < P; ++i) rg.v[i] = u32x4{0, 0, 0, 0};
-      return;
-    }
-    const int rs = kc / C, c = kc - rs * C;
-    const int r = rs / S, s = rs - r * S;
-#pragma unroll
-    for (int i = 0; i < P; ++i) {
-      const int ih = h0[i] + r * dh, iw = w0[i] + s * dw;
-      if ((unsigned)ih < (unsigned)H && (unsigned)iw < (unsigned)W)
-        rg.v[i] = *(const u32x4*)(x + (int64_t)(pix[i] + ih * W + iw) * C + c);
-      else
-        rg.v[i] = u32x4{0, 0, 0, 0};
-    }
+  // per-k-tile state: this lane's tap (r, s) offsets and channel; copies past
+  // the last k-tile land as zeros
+  struct Prep {
+    int dr, ds, c;
+    bool kin;
+  };
+  __device__ __forceinline__ Prep prep(int kt) const {
+    const int kc = kt * Cfg::BK + Cfg::dma_chunk(threadIdx.x & 63) * 8;
+    const int rsx = kc / C, c = kc - rsx * C;
+    const int r = rsx / S, s = rsx - r * S;
+    return Prep{r * dh, s * dw, c, kc < Kg};
   }
-
-  __device__ __forceinline__ void store(char* lds, const Regs& rg) const {
-#pragma unroll
-    for (int i = 0; i < P; ++i) *(u32x4*)(lds + lds_off(threadIdx.x / 8 + i * RPP, threadIdx.x & 7)) = rg.v[i];
+  __device__ __forceinline__ void issue_one(int i, const Prep& p, char* tile) const {
+    const int ih = h0[i] + p.dr, iw = w0[i] + p.ds;
+    const bool in = p.kin && (unsigned)ih < (unsigned)H && (unsigned)iw < (unsigned)W;
+    dma16(rs, in ? (uint32_t)((pix[i] + ih * W + iw) * C + p.c) * 2u : OOB, Cfg::dma_dst(tile, i));
   }
+  __device__ __forceinline__ void issue(int kt, char* tile) const {
+    const Prep p = prep(kt);
+#pragma unroll
+    for (int i = 0; i < P; ++i) issue_one(i, p, tile);
+  }
+  __device__ __forceinline__ void fix_tail(int, char*) const {}  // C % 8 == 0: chunks never straddle K
 };
 
 // ---------------------------------------------------------------------------
@@ -280,164 +437,363 @@ struct W4Geom {
 };
 
 // ---------------------------------------------------------------------------
-// Prepacked uint4 weight as the B operand (rows n, 64 k per k-tile): a k-tile
-// takes words j = 2 (kt % 2) + {0, 1} of every lane entry of the 16-row blocks
-// it covers -- 8 bytes per entry -- plus each entry's scale and zero.  The
-// dequantisation runs when the registers are written to LDS, so it overlaps
-// the matrix instructions of the other waves.
+// Prepacked uint4 weight as the B operand (rows n, BK = 64 k per k-tile): a
+// k-tile takes words j = 2 (kt % 2) + {0, 1} of every lane entry of the
+// 16-row blocks it covers -- 8 bytes per entry -- plus each entry's scale and
+// zero, into registers.  The dequantisation runs when the registers are
+// written to LDS, after the multiplies of the current stage have been issued.
 // ---------------------------------------------------------------------------
-template <int ROWS, int THREADS>
+template <class Cfg, int ROWS>
 struct W4Loader {
+  static constexpr bool kDMA = false;
   static constexpr int ENTRIES = ROWS / 16 * 64;
-  static constexpr int P = ENTRIES / THREADS;
-  static_assert(ENTRIES % THREADS == 0, "rows must cover whole lane-entry passes");
+  static constexpr int P = ENTRIES / Cfg::THREADS;
+  static_assert(Cfg::BK == 64, "the uint4 loader moves half a 128-k block per k-tile");
+  static_assert(ENTRIES % Cfg::THREADS == 0, "rows must cover whole lane-entry passes");
   struct Regs {
     u32x2 w[P];
-    uint32_t sz[P];  // scale bits | zero << 16
+    uint32_t s[P], z[P];
   };
-  W4Geom g;
-  int n0;
+  rsrc_t rw, rsc, rz;
+  uint32_t kblocks, N, group, block0;
 
-  __device__ __forceinline__ void init(const W4Geom& g_, int n0_) {
-    g = g_;
-    n0 = n0_;
+  __device__ __forceinline__ void init(const W4Geom& g, int n0) {
+    rw = make_rsrc(g.w, (uint32_t)((int64_t)g.N * g.K / 2));
+    rsc = make_rsrc(g.scales, (uint32_t)((int64_t)g.N * (g.K / g.group) * 2));
+    rz = make_rsrc(g.zeros, (uint32_t)((int64_t)g.N / 2 * (g.K / g.group)));
+    kblocks = g.K / 128;
+    N = g.N;
+    group = g.group;
+    block0 = n0 / 16;
   }
 
   __device__ __forceinline__ void load(int kt, Regs& rg) const {
-    const int kblocks = g.K / 128;
-    const int grp = (kt * BK) / g.group;
+    const uint32_t grp = (uint32_t)(kt * Cfg::BK) / group;
 #pragma unroll
     for (int i = 0; i < P; ++i) {
-      const int e = threadIdx.x + i * THREADS;
-      const int nb = e / 64, L = e % 64;
-      const int n = n0 + nb * 16 + (L % 16);
-      if (n < g.N) {
-        const uint8_t* src = g.w + ((int64_t)((n0 / 16 + nb) * kblocks + kt / 2) * 1024 + L * 16 + (kt & 1) * 8);
-        rg.w[i] = *(const u32x2*)src;
-        const uint32_t s = g.scales[(int64_t)grp * g.N + n];
-        const uint32_t z = (g.zeros[(int64_t)grp * (g.N / 2) + n / 2] >> ((n & 1) * 4)) & 15u;
-        rg.sz[i] = s | (z << 16);
-      } else {
-        rg.w[i] = u32x2{0, 0};
-        rg.sz[i] = 0;  // scale 0, zero 0: the row dequantises to zeros
-      }
+      const int e = threadIdx.x + i * Cfg::THREADS;
+      const uint32_t nb = e / 64, L = e % 64;
+      const uint32_t n = (block0 + nb) * 16 + (L % 16);
+      const bool ok = n < N;
+      rg.w[i] = buf_load8(rw, ok ? ((block0 + nb) * kblocks + kt / 2) * 1024u + L * 16u + (kt & 1) * 8u : OOB);
+      rg.s[i] = buf_load2(rsc, ok ? (grp * N + n) * 2u : OOB);
+      rg.z[i] = buf_load1(rz, ok ? grp * (N / 2) + n / 2 : OOB);
     }
   }
 
   __device__ __forceinline__ void store(char* lds, const Regs& rg) const {
 #pragma unroll
     for (int i = 0; i < P; ++i) {
-      const int e = threadIdx.x + i * THREADS;
+      const int e = threadIdx.x + i * Cfg::THREADS;
       const int nb = e / 64, L = e % 64;
       const int row = nb * 16 + (L % 16), h = L / 16;
-      const f16x2 ss = scale_pair(rg.sz[i] & 0xffffu), zz = zero_pair((rg.sz[i] >> 16) & 15u);
+      const uint32_t n = (block0 + nb) * 16 + (L % 16);
+      const f16x2 ss = scale_pair(rg.s[i] & 0xffffu), zz = zero_pair((rg.z[i] >> ((n & 1) * 4)) & 15u);
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) *(u32x4*)(lds + lds_off(row, 4 * jj + h)) = dequant8(rg.w[i][jj], zz, ss);
+      for (int jj = 0; jj < 2; ++jj) *(u32x4*)(lds + Cfg::off(row, 4 * jj + h)) = dequant8(rg.w[i][jj], zz, ss);
     }
   }
 };
 
-// ---------------------------------------------------------------------------
-// Mainloop: acc[tm][tn] += B-fragment x A-fragment over all k-tiles.
-// The MFMA's first operand is the B tile (rows n), its second the A tile
-// (rows m), so each lane's four consecutive result registers are four
-// consecutive n of one output row m: the epilogue writes 8-byte runs.
-// Two LDS stages: while the waves multiply stage s, the next k-tile is loaded
-// into registers and written into stage s ^ 1; one barrier per k-tile.
-// ---------------------------------------------------------------------------
-template <class Cfg, int DT, class ALd, class BLd>
-__device__ __forceinline__ void mainloop(char* lds, const ALd& al, const BLd& bl, int nk,
-                                         f32x16 (&acc)[Cfg::TM][Cfg::TN]) {
-#pragma unroll
-  for (int i = 0; i < Cfg::TM; ++i)
-#pragma unroll
-    for (int j = 0; j < Cfg::TN; ++j) acc[i][j] = f32x16{};
-  if (nk <= 0) return;
+template <class Ld>
+constexpr int dma_count() {
+  if constexpr (Ld::kDMA)
+    return Ld::P;
+  else
+    return 0;
+}
 
+struct NoRegs {};
+template <class Ld, bool = Ld::kDMA>
+struct RegsOf {
+  using type = NoRegs;
+};
+template <class Ld>
+struct RegsOf<Ld, false> {
+  using type = typename Ld::Regs;
+};
+struct NoPrep {};
+template <class Ld, bool = Ld::kDMA>
+struct PrepOf {
+  using type = typename Ld::Prep;
+};
+template <class Ld>
+struct PrepOf<Ld, false> {
+  using type = NoPrep;
+};
+
+// ---------------------------------------------------------------------------
+// Multiply one stage: acc[i][j] += B-fragment j x A-fragment i for every 16-k
+// step.  The MFMA's first operand is the B tile (rows n), its second the A
+// tile (rows m), so each lane's four consecutive result registers are four
+// consecutive n of one output row m.  On entry fa[0] / fb[0] hold this
+// stage's first-step fragments; during step kk the fragments of step kk + 1
+// are read, and during the last step those of the first step of stage `nxs`
+// (the next k-tile, already visible when CROSS is set) -- so no step starts
+// by waiting on LDS.  The instruction order is fixed slot by slot (each slot
+// closed by a scheduling barrier): one MFMA, then one fragment read, then the
+// direct-to-LDS copies of k-tile kt_dma that fall in this slot, spread evenly
+// over the stage so the memory pipeline is fed at its own rate instead of
+// receiving a burst that would stall the wave (and the matrix core) at issue.
+// ---------------------------------------------------------------------------
+template <class Cfg>
+__device__ __forceinline__ void read_frags(const char* st, int kk, u32x4 (&fa)[Cfg::TM], u32x4 (&fb)[Cfg::TN]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = (wave / Cfg::WAVES_N) * Cfg::WTM, wn = (wave % Cfg::WAVES_N) * Cfg::WTN;
   const int frow = lane & 31, fchunk = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i) fa[i] = *(const u32x4*)(st + Cfg::off(wm + i * 32 + frow, kk * 2 + fchunk));
+#pragma unroll
+  for (int j = 0; j < Cfg::TN; ++j)
+    fb[j] = *(const u32x4*)(st + Cfg::A_BYTES + Cfg::off(wn + j * 32 + frow, kk * 2 + fchunk));
+}
 
-  typename ALd::Regs ra;
-  typename BLd::Regs rb;
-  al.load(0, ra);
-  bl.load(0, rb);
-  al.store(lds, ra);
-  bl.store(lds + Cfg::A_BYTES, rb);
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    char* sa = lds + (kt & 1) * Cfg::STAGE_BYTES;
-    char* sb = sa + Cfg::A_BYTES;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      al.load(kt + 1, ra);
-      bl.load(kt + 1, rb);
+template <class Cfg, int DT, bool CROSS, class ALd, class BLd>
+__device__ __forceinline__ void multiply_stage(const char* st, const char* nxs, f32x16 (&acc)[Cfg::TM][Cfg::TN],
+                                               u32x4 (&fa)[2][Cfg::TM], u32x4 (&fb)[2][Cfg::TN], const ALd& al,
+                                               const BLd& bl, int kt_dma, char* dma_st) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = (wave / Cfg::WAVES_N) * Cfg::WTM, wn = (wave % Cfg::WAVES_N) * Cfg::WTN;
+  const int frow = lane & 31, fchunk = lane >> 5;
+  constexpr int KK = Cfg::BK / 16;
+  static_assert(KK % 2 == 0, "fragment double buffer flips once per step");
+  constexpr int NMFMA = Cfg::TM * Cfg::TN, NDS = Cfg::TM + Cfg::TN;
+  constexpr int PA = dma_count<ALd>(), PB = dma_count<BLd>(), T = PA + PB;
+  constexpr int SPAN = KK * NMFMA;  // copy slots
+  typename PrepOf<ALd>::type pa{};
+  typename PrepOf<BLd>::type pb{};
+  if constexpr (PA > 0) pa = al.prep(kt_dma);
+  if constexpr (PB > 0) pb = bl.prep(kt_dma);
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const int cur = kk & 1, nx = cur ^ 1;
+    const bool rd = CROSS || kk + 1 < KK;  // fragments to read during this step
+    const char* src = (kk + 1 < KK) ? st : nxs;
+    const int rk = (kk + 1 < KK) ? kk + 1 : 0;
+#pragma unroll
+    for (int m = 0; m < NMFMA; ++m) {
+      const int i = m / Cfg::TN, j = m % Cfg::TN;
+      acc[i][j] = mfma32<DT>(fb[cur][j], fa[cur][i], acc[i][j]);
+      if (rd) {
+        if (m < Cfg::TM)
+          fa[nx][m] = *(const u32x4*)(src + Cfg::off(wm + m * 32 + frow, rk * 2 + fchunk));
+        else if (m < NDS)
+          fb[nx][m - Cfg::TM] =
+              *(const u32x4*)(src + Cfg::A_BYTES + Cfg::off(wn + (m - Cfg::TM) * 32 + frow, rk * 2 + fchunk));
+      }
+      const int slot = kk * NMFMA + m;
+      const int v0 = (slot * T + SPAN - 1) / SPAN, v1 = ((slot + 1) * T + SPAN - 1) / SPAN;
+#pragma unroll
+      for (int v = v0; v < v1; ++v) {
+        if constexpr (PA > 0) {
+          if (v < PA) al.issue_one(v, pa, dma_st);
+        }
+        if constexpr (PB > 0) {
+          if (v >= PA) bl.issue_one(v - PA, pb, dma_st + Cfg::A_BYTES);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (NMFMA < NDS) {  // more fragments than MFMA slots
+      if (rd) {
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      u32x4 fa[Cfg::TM], fb[Cfg::TN];
-#pragma unroll
-      for (int i = 0; i < Cfg::TM; ++i) fa[i] = *(const u32x4*)(sa + lds_off(wm + i * 32 + frow, kk * 2 + fchunk));
-#pragma unroll
-      for (int j = 0; j < Cfg::TN; ++j) fb[j] = *(const u32x4*)(sb + lds_off(wn + j * 32 + frow, kk * 2 + fchunk));
-#pragma unroll
-      for (int i = 0; i < Cfg::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < Cfg::TN; ++j) acc[i][j] = mfma32<DT>(fb[j], fa[i], acc[i][j]);
+        for (int m = NMFMA; m < NDS; ++m) {
+          if (m < Cfg::TM)
+            fa[nx][m] = *(const u32x4*)(src + Cfg::off(wm + m * 32 + frow, rk * 2 + fchunk));
+          else
+            fb[nx][m - Cfg::TM] =
+                *(const u32x4*)(src + Cfg::A_BYTES + Cfg::off(wn + (m - Cfg::TM) * 32 + frow, rk * 2 + fchunk));
+        }
+      }
     }
-    if (more) {
-      char* na = lds + ((kt + 1) & 1) * Cfg::STAGE_BYTES;
-      al.store(na, ra);
-      bl.store(na + Cfg::A_BYTES, rb);
-    }
-    __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------------------
-// Epilogue: D[m][n] = RN(alpha * acc + beta * C[m][n]); C is read only when
-// beta != 0.  Lane l of block (i, j), register group q holds
-// m = wm + 32 i + l % 32, n = wn + 32 j + 8 q + 4 (l / 32) + {0..3}.
+// Mainloop over a ring of STAGES LDS stages.  Direct-to-LDS operands (EARLY
+// scheme, STAGES >= 3, prefetch distance D = STAGES - 1): while the waves
+// multiply k-tile kt, the copies of k-tile kt + D stream into the stage freed
+// by k-tile kt - 1.  At the end of k-tile kt each wave waits until its own
+// copies of k-tile kt + 2 have landed (vmcnt counts down in issue order, so
+// the younger k-tiles stay in flight) and a barrier publishes them; k-tile
+// kt + 1, published one step earlier, is already being read -- its first
+// fragments come in during the last step of kt.  Copies past the last k-tile
+// are issued anyway (they land as zeros), keeping counts uniform and the
+// multiply free of branches.  Register-staged operands (uint4 weights, two
+// stages): the loads of k-tile kt + 1 are written to LDS after the multiply
+// of kt and the wait is for everything.
 // ---------------------------------------------------------------------------
+template <class Cfg, int DT, class ALd, class BLd>
+__device__ __forceinline__ void mainloop(char* lds, const ALd& al, const BLd& bl, int nk,
+                                         f32x16 (&acc)[Cfg::TM][Cfg::TN]) {
+  constexpr int S = Cfg::STAGES, D = S - 1;
+  constexpr int PT = dma_count<ALd>() + dma_count<BLd>();
+  constexpr bool REG = !ALd::kDMA || !BLd::kDMA;
+  static_assert(REG ? S == 2 : S >= 3, "register-staged operands use two stages, direct-to-LDS at least three");
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::TN; ++j) acc[i][j] = f32x16{};
+  // the previous tile's epilogue may still be reading the stages
+  __builtin_amdgcn_s_barrier();
+  if (nk <= 0) return;
+  u32x4 fa[2][Cfg::TM], fb[2][Cfg::TN];
+
+  if constexpr (!REG) {
+    // prologue: k-tiles 0 .. D - 1; k-tiles 0 and 1 landed and published
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      char* st = lds + s * Cfg::STAGE_BYTES;
+      al.issue(s, st);
+      bl.issue(s, st + Cfg::A_BYTES);
+    }
+    constexpr bool FIX = ALd::kFIX || BLd::kFIX;
+    wait_vm_le<(D - 2) * PT>();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      al.fix_tail(s, lds + s * Cfg::STAGE_BYTES);
+      bl.fix_tail(s, lds + s * Cfg::STAGE_BYTES + Cfg::A_BYTES);
+    }
+    if constexpr (FIX) wait_lgkm();
+    __builtin_amdgcn_s_barrier();
+    read_frags<Cfg>(lds, 0, fa[0], fb[0]);
+    int cs = 0;  // stage of k-tile kt
+    // one loop body (a second copy makes the register allocator shuttle the
+    // accumulators between AGPRs and VGPRs); stages are picked per k-tile
+    for (int kt = 0; kt < nk; ++kt) {
+      const int n1 = (cs + 1) % S, n2 = (cs + 2) % S, nd = (cs + D) % S;
+      char* cur = lds + cs * Cfg::STAGE_BYTES;
+      multiply_stage<Cfg, DT, true>(cur, lds + n1 * Cfg::STAGE_BYTES, acc, fa, fb, al, bl, kt + D,
+                                    lds + nd * Cfg::STAGE_BYTES);
+      wait_vm_le<(D - 2) * PT>();
+      al.fix_tail(kt + 2, lds + n2 * Cfg::STAGE_BYTES);
+      bl.fix_tail(kt + 2, lds + n2 * Cfg::STAGE_BYTES + Cfg::A_BYTES);
+      if constexpr (FIX) wait_lgkm();  // the masked chunks are in LDS before the barrier
+      __builtin_amdgcn_s_barrier();
+      cs = n1;
+    }
+  } else {
+    typename RegsOf<ALd>::type ra;
+    typename RegsOf<BLd>::type rb;
+    if constexpr (ALd::kDMA) al.issue(0, lds); else al.load(0, ra);
+    if constexpr (BLd::kDMA) bl.issue(0, lds + Cfg::A_BYTES); else bl.load(0, rb);
+    wait_vm_le<0>();
+    if constexpr (ALd::kDMA) al.fix_tail(0, lds); else al.store(lds, ra);
+    if constexpr (BLd::kDMA) bl.fix_tail(0, lds + Cfg::A_BYTES); else bl.store(lds + Cfg::A_BYTES, rb);
+    wait_lgkm();
+    __builtin_amdgcn_s_barrier();
+    int cs = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+      char* cur = lds + cs * Cfg::STAGE_BYTES;
+      char* nxt = lds + (cs ^ 1) * Cfg::STAGE_BYTES;
+      const bool more = kt + 1 < nk;
+      if constexpr (!ALd::kDMA) {
+        if (more) al.load(kt + 1, ra);
+      }
+      if constexpr (!BLd::kDMA) {
+        if (more) bl.load(kt + 1, rb);
+      }
+      read_frags<Cfg>(cur, 0, fa[0], fb[0]);
+      multiply_stage<Cfg, DT, false>(cur, cur, acc, fa, fb, al, bl, kt + 1, nxt);
+      wait_vm_le<0>();
+      if (more) {
+        if constexpr (ALd::kDMA) al.fix_tail(kt + 1, nxt); else al.store(nxt, ra);
+        if constexpr (BLd::kDMA) bl.fix_tail(kt + 1, nxt + Cfg::A_BYTES); else bl.store(nxt + Cfg::A_BYTES, rb);
+        wait_lgkm();
+      }
+      __builtin_amdgcn_s_barrier();
+      cs ^= 1;
+    }
+  }
+  // copies past the last k-tile are still landing (as zeros): drain them
+  // before anyone reuses the stages
+  wait_vm_le<0>();
+  __builtin_amdgcn_s_barrier();
+}
+
+// ---------------------------------------------------------------------------
+// Epilogue: D[m][n] = RN(alpha * acc + beta * C[m][n]) in fp32, C read only
+// when beta != 0.  Lane l of accumulator block (i, j), register group q holds
+// row 32 i + l % 32 and columns 32 j + 8 q + 4 (l / 32) + {0..3} of its wave
+// tile; written straight to memory those would be 8-byte runs scattered over
+// 32 rows.  Instead each wave stages its fp32 accumulators in its own LDS
+// region (the stages are free after the last k-tile), PASS blocks of 32 rows
+// at a time, and reads them back row-major, 8 floats per lane: every store
+// instruction writes whole row segments, 16 bytes per lane.  Region row r
+// holds WTN floats in 16-byte chunks, chunk x in slot x ^ (r % 16) ^ bit 4 of
+// x: 16 lanes writing one chunk of 16 rows, or reading the even (odd) chunks
+// of one row, touch all 64 banks once.  Rows past M are dropped by the
+// store's buffer range; a tile that crosses N stores element by element.
+// ---------------------------------------------------------------------------
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return to_bits<DT>(a) | (to_bits<DT>(b) << 16);
+}
+
 template <class Cfg, int DT>
-__device__ __forceinline__ void epilogue(const Tile& t, const f32x16 (&acc)[Cfg::TM][Cfg::TN], float alpha,
-                                         float beta) {
+__device__ __forceinline__ void store_tile(const Tile& t, const f32x16 (&acc)[Cfg::TM][Cfg::TN], float alpha,
+                                           float beta, char* lds) {
+  constexpr int ROWB = Cfg::WTN * 4;  // fp32 row of the wave tile
+  constexpr int PASS = (4 * 2 * 32 * ROWB <= Cfg::LDS_BYTES) ? 2 : 1;  // 32-row blocks per pass
+  constexpr int REGION = PASS * 32 * ROWB;
+  static_assert(4 * REGION <= Cfg::LDS_BYTES && Cfg::TM % PASS == 0, "four wave regions must fit the stages");
+  constexpr int LPR = Cfg::WTN / 8;  // lanes per row on read-back (8 floats each)
+  constexpr int RPI = 64 / LPR;      // rows per read-back instruction
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = (wave / Cfg::WAVES_N) * Cfg::WTM, wn = (wave % Cfg::WAVES_N) * Cfg::WTN;
+  char* reg = lds + wave * REGION;
+  auto slot = [](int r, int x) { return (x ^ (r & 15) ^ ((x >> 4) & 1)) << 4; };
+
+  int rows = t.M - t.m0;
+  if (rows > Cfg::BM) rows = Cfg::BM;
   const bool use_c = beta != 0.0f;
+  const bool full_n = t.n0 + Cfg::BN <= t.N;
+  const rsrc_t rd = make_rsrc(t.D + (int64_t)t.m0 * t.ldd, (uint32_t)rows * (uint32_t)t.ldd * 2u);
+  const rsrc_t rc = use_c ? make_rsrc(t.C + (int64_t)t.m0 * t.ldc, (uint32_t)rows * (uint32_t)t.ldc * 2u) : rd;
+  const uint32_t ldd2 = (uint32_t)t.ldd * 2u, ldc2 = (uint32_t)t.ldc * 2u;
+
 #pragma unroll
-  for (int i = 0; i < Cfg::TM; ++i) {
-    const int m = t.m0 + wm + i * 32 + (lane & 31);
-    if (m >= t.M) continue;
-    uint16_t* drow = t.D + (int64_t)m * t.ldd;
-    const uint16_t* crow = use_c ? t.C + (int64_t)m * t.ldc : nullptr;
+  for (int p0 = 0; p0 < Cfg::TM; p0 += PASS) {
 #pragma unroll
-    for (int j = 0; j < Cfg::TN; ++j) {
+    for (int ii = 0; ii < PASS; ++ii) {
+      const int r = ii * 32 + (lane & 31);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = t.n0 + wn + j * 32 + q * 8 + (lane >> 5) * 4;
-        float v[4];
+      for (int j = 0; j < Cfg::TN; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = alpha * acc[i][j][q * 4 + e];
-        if (n + 4 <= t.N) {
-          if (use_c) {
-            u32x2 c2 = *(const u32x2*)(crow + n);
-            v[0] += beta * from_bits<DT>(c2[0] & 0xffffu);
-            v[1] += beta * from_bits<DT>(c2[0] >> 16);
-            v[2] += beta * from_bits<DT>(c2[1] & 0xffffu);
-            v[3] += beta * from_bits<DT>(c2[1] >> 16);
-          }
-          *(u32x2*)(drow + n) =
-              u32x2{to_bits<DT>(v[0]) | (to_bits<DT>(v[1]) << 16), to_bits<DT>(v[2]) | (to_bits<DT>(v[3]) << 16)};
-        } else {
+        for (int q = 0; q < 4; ++q) {
+          const int x = 8 * j + 2 * q + (lane >> 5);  // 16-byte chunk: columns 4x .. 4x + 3
+          const f32x4 v{acc[p0 + ii][j][4 * q], acc[p0 + ii][j][4 * q + 1], acc[p0 + ii][j][4 * q + 2],
+                        acc[p0 + ii][j][4 * q + 3]};
+          *(f32x4*)(reg + r * ROWB + slot(r, x)) = v;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < PASS * 32 / RPI; ++k) {
+      const int r = k * RPI + lane / LPR, c = lane % LPR;  // lane stores columns 8c .. 8c + 7
+      const f32x4 a0 = *(const f32x4*)(reg + r * ROWB + slot(r, 2 * c));
+      const f32x4 a1 = *(const f32x4*)(reg + r * ROWB + slot(r, 2 * c + 1));
+      float v[8] = {alpha * a0[0], alpha * a0[1], alpha * a0[2], alpha * a0[3],
+                    alpha * a1[0], alpha * a1[1], alpha * a1[2], alpha * a1[3]};
+      const uint32_t row = (uint32_t)(wm + p0 * 32 + r);
+      const int col = t.n0 + wn + 8 * c;
+      if (full_n || col + 8 <= t.N) {
+        if (use_c) {
+          const u32x4 c4 = buf_load16(rc, row * ldc2 + (uint32_t)col * 2u);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            if (n + e < t.N) {
-              float r = v[e];
-              if (use_c) r += beta * from_bits<DT>(crow[n + e]);
-              drow[n + e] = (uint16_t)to_bits<DT>(r);
-            }
+            v[2 * e] += beta * from_bits<DT>(c4[e] & 0xffffu);
+            v[2 * e + 1] += beta * from_bits<DT>(c4[e] >> 16);
+          }
+        }
+        buf_store16(rd, row * ldd2 + (uint32_t)col * 2u,
+                    u32x4{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3]), pack2<DT>(v[4], v[5]), pack2<DT>(v[6], v[7])});
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (col + e < t.N) {
+            float x = v[e];
+            if (use_c) x += beta * from_bits<DT>(buf_load2(rc, row * ldc2 + (uint32_t)(col + e) * 2u));
+            buf_store2(rd, row * ldd2 + (uint32_t)(col + e) * 2u, to_bits<DT>(x));
           }
         }
       }

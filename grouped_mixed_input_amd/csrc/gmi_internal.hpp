@@ -24,7 +24,7 @@ constexpr size_t kWorkspaceHeader = 256;
 enum TileShape { TILE_256x256 = 0, TILE_128x128 = 1, TILE_256x128 = 2 };
 inline int tile_bm(int s) { return s == TILE_128x128 ? 128 : 256; }
 inline int tile_bn(int s) { return s == TILE_256x256 ? 256 : 128; }
-inline int tile_wgs_per_cu(int s) { return s == TILE_128x128 ? 2 : 1; }
+inline int tile_wgs_per_cu(int s) { return s == TILE_256x256 ? 1 : 2; }  // matches TileCfg::WGS_PER_CU
 
 struct PtrArrayLaunch {
   const uint16_t* const* A;
@@ -56,8 +56,8 @@ struct W4Launch {
 
 int device_cu_count();  // cached per device
 
-hipError_t launch_grouped(const GroupDesc* desc_dev, int count, int total_tiles, int shape, int dtype, float alpha,
-                          float beta, hipStream_t stream);
+hipError_t launch_grouped(const GroupDesc* desc_dev, int count, int total_tiles, int shape, int dtype, bool ktail,
+                          float alpha, float beta, hipStream_t stream);
 hipError_t launch_ptr_array(const PtrArrayLaunch& a, int shape, int dtype, float alpha, float beta,
                             hipStream_t stream);
 hipError_t launch_conv_fprop(const ConvLaunch& a, int shape, int dtype, float alpha, float beta, hipStream_t stream);

@@ -24,7 +24,7 @@ struct ConvArgs {
 // Tile ids run n-tile fastest: the few n-tiles of a pixel block are
 // consecutive, so one XCD gathers each activation panel once into its L2.
 template <class Cfg, int DT>
-__global__ __launch_bounds__(Cfg::THREADS) void k_conv_fprop(ConvArgs a) {
+__global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_conv_fprop(ConvArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
   const int G = gridDim.x;
   for (int base = 0; base < a.total_tiles; base += G) {
@@ -40,24 +40,24 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_conv_fprop(ConvArgs a) {
     t.ldc = a.Nk;
     t.D = a.y;
     t.ldd = a.Nk;
-    ConvLoader<Cfg::BM, Cfg::THREADS> al;
-    DenseLoader<Cfg::BN, Cfg::THREADS> bl;
+    ConvLoader<Cfg, Cfg::BM> al;
+    DenseLoader<Cfg, Cfg::BN> bl;
     al.init(a.g, t.m0, t.M);
     bl.init(a.w, a.g.Kg, t.n0, t.N, t.K);
     f32x16 acc[Cfg::TM][Cfg::TN];
-    mainloop<Cfg, DT>(lds, al, bl, (t.K + BK - 1) / BK, acc);
-    epilogue<Cfg, DT>(t, acc, a.alpha, a.beta);
+    mainloop<Cfg, DT>(lds, al, bl, (t.K + Cfg::BK - 1) / Cfg::BK, acc);
+    store_tile<Cfg, DT>(t, acc, a.alpha, a.beta, lds);
   }
 }
 
-using ConvCfg256 = TileCfg<256, 256, 2, 2>;
-using ConvCfg128 = TileCfg<128, 128, 2, 2>;
-using ConvCfg256x128 = TileCfg<256, 128, 2, 2>;
+using ConvCfg256 = TileCfg<256, 256, 2, 2, 32, 4>;
+using ConvCfg256x128 = TileCfg<256, 128, 2, 2, 32, 3>;
+using ConvCfg128 = TileCfg<128, 128, 2, 2, 32, 4>;
 
 hipError_t launch_conv_fprop(const ConvLaunch& p, int shape, int dtype, float alpha, float beta,
                              hipStream_t stream) {
   ConvArgs a;
-  a.g = ConvGeom{p.x, p.H, p.W, p.C, p.S, p.P, p.Q, p.ph, p.pw, p.sh, p.sw, p.dh, p.dw, p.R * p.S * p.C};
+  a.g = ConvGeom{p.x, (uint32_t)((int64_t)p.N * p.H * p.W * p.C * 2), p.H, p.W, p.C, p.S, p.P, p.Q, p.ph, p.pw, p.sh, p.sw, p.dh, p.dw, p.R * p.S * p.C};
   a.w = p.w;
   a.c = p.c;
   a.y = p.y;

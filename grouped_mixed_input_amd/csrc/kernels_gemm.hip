@@ -11,15 +11,15 @@
 
 namespace gmi {
 
-template <class Cfg, int DT>
+template <class Cfg, int DT, bool KTAIL>
 __device__ __forceinline__ void run_tile(char* lds, const Tile& t, float alpha, float beta) {
-  DenseLoader<Cfg::BM, Cfg::THREADS> al;
-  DenseLoader<Cfg::BN, Cfg::THREADS> bl;
+  DenseLoader<Cfg, Cfg::BM, KTAIL> al;
+  DenseLoader<Cfg, Cfg::BN, KTAIL> bl;
   al.init(t.A, t.lda, t.m0, t.M, t.K);
   bl.init(t.B, t.ldb, t.n0, t.N, t.K);
   f32x16 acc[Cfg::TM][Cfg::TN];
-  mainloop<Cfg, DT>(lds, al, bl, (t.K + BK - 1) / BK, acc);
-  epilogue<Cfg, DT>(t, acc, alpha, beta);
+  mainloop<Cfg, DT>(lds, al, bl, (t.K + Cfg::BK - 1) / Cfg::BK, acc);
+  store_tile<Cfg, DT>(t, acc, alpha, beta, lds);
 }
 
 struct GroupedArgs {
@@ -31,8 +31,8 @@ struct GroupedArgs {
 // Tile ids are laid out problem after problem; inside a problem the m-tile
 // index runs fastest, so consecutive tiles (one XCD's share of a round) reuse
 // the same B panel -- the expert weight in a mixture-of-experts layer.
-template <class Cfg, int DT>
-__global__ __launch_bounds__(Cfg::THREADS) void k_gemm_grouped(GroupedArgs a) {
+template <class Cfg, int DT, bool KTAIL>
+__global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_gemm_grouped(GroupedArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
   const int G = gridDim.x;
   int g = 0;
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_grouped(GroupedArgs a) {
     t.ldc = d.ldc;
     t.D = d.D;
     t.ldd = d.ldd;
-    run_tile<Cfg, DT>(lds, t, a.alpha, a.beta);
+    run_tile<Cfg, DT, KTAIL>(lds, t, a.alpha, a.beta);
   }
 }
 
@@ -67,8 +67,8 @@ struct PtrArrayArgs {
   float alpha, beta;
 };
 
-template <class Cfg, int DT>
-__global__ __launch_bounds__(Cfg::THREADS) void k_gemm_ptr_array(PtrArrayArgs a) {
+template <class Cfg, int DT, bool KTAIL>
+__global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_gemm_ptr_array(PtrArrayArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
   const int G = gridDim.x;
   for (int base = 0; base < a.total_tiles; base += G) {
@@ -89,13 +89,15 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_gemm_ptr_array(PtrArrayArgs a)
     t.ldc = a.p.ldc;
     t.D = a.p.D[l];
     t.ldd = a.p.ldd;
-    run_tile<Cfg, DT>(lds, t, a.alpha, a.beta);
+    run_tile<Cfg, DT, KTAIL>(lds, t, a.alpha, a.beta);
   }
 }
 
-using Cfg256 = TileCfg<256, 256, 2, 2>;
-using Cfg128 = TileCfg<128, 128, 2, 2>;
-using Cfg256x128 = TileCfg<256, 128, 2, 2>;
+// 32-k stages: 4 x 32 KB (one workgroup per CU), 3 x 24 KB and 4 x 16 KB
+// (two per CU)
+using Cfg256 = TileCfg<256, 256, 2, 2, 32, 4>;
+using Cfg256x128 = TileCfg<256, 128, 2, 2, 32, 3>;
+using Cfg128 = TileCfg<128, 128, 2, 2, 32, 4>;
 
 // Persistent grid: a whole number of XCD rounds, no more workgroups than can
 // be resident at once and no more than the tiles need.
@@ -106,32 +108,32 @@ static int persistent_grid(int total_tiles, int shape) {
   return g < XCDS ? XCDS : g;
 }
 
-// Instantiate and launch KER for the tile shape and element type.
-#define GMI_DISPATCH(KER, shape, dtype, grid, args, stream)                                                   \
-  do {                                                                                                      \
-    if ((shape) == TILE_256x256) {                                                                          \
-      if ((dtype) == DT_F16)                                                                                \
-        hipLaunchKernelGGL((KER<Cfg256, DT_F16>), dim3(grid), dim3(Cfg256::THREADS), 0, stream, args);      \
-      else                                                                                                  \
-        hipLaunchKernelGGL((KER<Cfg256, DT_BF16>), dim3(grid), dim3(Cfg256::THREADS), 0, stream, args);     \
-    } else if ((shape) == TILE_256x128) {                                                                   \
-      if ((dtype) == DT_F16)                                                                                \
-        hipLaunchKernelGGL((KER<Cfg256x128, DT_F16>), dim3(grid), dim3(Cfg256x128::THREADS), 0, stream, args);  \
-      else                                                                                                  \
-        hipLaunchKernelGGL((KER<Cfg256x128, DT_BF16>), dim3(grid), dim3(Cfg256x128::THREADS), 0, stream, args); \
-    } else {                                                                                                \
-      if ((dtype) == DT_F16)                                                                                \
-        hipLaunchKernelGGL((KER<Cfg128, DT_F16>), dim3(grid), dim3(Cfg128::THREADS), 0, stream, args);      \
-      else                                                                                                  \
-        hipLaunchKernelGGL((KER<Cfg128, DT_BF16>), dim3(grid), dim3(Cfg128::THREADS), 0, stream, args);     \
-    }                                                                                                       \
+// Instantiate and launch KER for the tile shape, element type and K-tail mode
+// (KT: some K is not a multiple of 8, so a chunk can straddle K).
+#define GMI_LAUNCH1(KER, CFG, DT, KT, grid, args, stream) \
+  hipLaunchKernelGGL((KER<CFG, DT, KT>), dim3(grid), dim3(CFG::THREADS), 0, stream, args)
+#define GMI_LAUNCH_DT(KER, CFG, dtype, kt, grid, args, stream)                                 \
+  do {                                                                                       \
+    if ((dtype) == DT_F16) {                                                                 \
+      if (kt) GMI_LAUNCH1(KER, CFG, DT_F16, true, grid, args, stream);                       \
+      else GMI_LAUNCH1(KER, CFG, DT_F16, false, grid, args, stream);                         \
+    } else {                                                                                 \
+      if (kt) GMI_LAUNCH1(KER, CFG, DT_BF16, true, grid, args, stream);                      \
+      else GMI_LAUNCH1(KER, CFG, DT_BF16, false, grid, args, stream);                        \
+    }                                                                                        \
+  } while (0)
+#define GMI_DISPATCH(KER, shape, dtype, kt, grid, args, stream)                                                \
+  do {                                                                                                       \
+    if ((shape) == TILE_256x256) GMI_LAUNCH_DT(KER, Cfg256, dtype, kt, grid, args, stream);                 \
+    else if ((shape) == TILE_256x128) GMI_LAUNCH_DT(KER, Cfg256x128, dtype, kt, grid, args, stream);        \
+    else GMI_LAUNCH_DT(KER, Cfg128, dtype, kt, grid, args, stream);                                         \
   } while (0)
 
-hipError_t launch_grouped(const GroupDesc* desc_dev, int count, int total_tiles, int shape, int dtype, float alpha,
-                          float beta, hipStream_t stream) {
+hipError_t launch_grouped(const GroupDesc* desc_dev, int count, int total_tiles, int shape, int dtype, bool ktail,
+                          float alpha, float beta, hipStream_t stream) {
   GroupedArgs a{desc_dev, count, total_tiles, alpha, beta};
   const int grid = persistent_grid(total_tiles, shape);
-  GMI_DISPATCH(k_gemm_grouped, shape, dtype, grid, a, stream);
+  GMI_DISPATCH(k_gemm_grouped, shape, dtype, ktail, grid, a, stream);
   return hipGetLastError();
 }
 
@@ -145,7 +147,7 @@ hipError_t launch_ptr_array(const PtrArrayLaunch& p, int shape, int dtype, float
   a.alpha = alpha;
   a.beta = beta;
   const int grid = persistent_grid(a.total_tiles, shape);
-  GMI_DISPATCH(k_gemm_ptr_array, shape, dtype, grid, a, stream);
+  GMI_DISPATCH(k_gemm_ptr_array, shape, dtype, (p.K % 8) != 0, grid, a, stream);
   return hipGetLastError();
 }
 

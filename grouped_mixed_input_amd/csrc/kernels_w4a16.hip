@@ -68,34 +68,32 @@ struct SkinnyStage {
   u32x4 x[MT][4];
 };
 
+struct SkinnyRes {
+  rsrc_t w, x, s, z;
+  uint32_t kblocks;
+};
+
 template <int NB, int MT>
-__device__ __forceinline__ void skinny_load(SkinnyStage<NB, MT>& st, const W4Launch& a, int n_base, int kb,
-                                            int kblocks, int lane) {
-  const int r = lane & 15, h = lane >> 4;
-  const int grp = (kb * 128) / a.group;
+__device__ __forceinline__ void skinny_load(SkinnyStage<NB, MT>& st, const W4Launch& a, const SkinnyRes& rs,
+                                            int n_base, int kb, int lane) {
+  const uint32_t r = lane & 15, h = lane >> 4;
+  const uint32_t grp = (uint32_t)(kb * 128) / (uint32_t)a.group;
+  const uint32_t N = a.N;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int n = n_base + nb * 16 + r;
-    if (n_base + nb * 16 < a.N) {
-      st.w[nb] = *(const u32x4*)(a.w + ((int64_t)((n_base / 16 + nb) * kblocks + kb) * 1024 + lane * 16));
-      const uint32_t s = a.scales[(int64_t)grp * a.N + n];
-      const uint32_t z = (a.zeros[(int64_t)grp * (a.N / 2) + n / 2] >> ((n & 1) * 4)) & 15u;
-      st.sz[nb] = s | (z << 16);
-    } else {
-      st.w[nb] = u32x4{0, 0, 0, 0};
-      st.sz[nb] = 0;
-    }
+    const uint32_t blk = n_base / 16 + nb, n = blk * 16 + r;
+    const bool ok = n < N;
+    st.w[nb] = buf_load16(rs.w, ok ? (blk * rs.kblocks + kb) * 1024u + lane * 16u : OOB);
+    const uint32_t s = buf_load2(rs.s, ok ? (grp * N + n) * 2u : OOB);
+    const uint32_t z = (buf_load1(rs.z, ok ? grp * (N / 2) + n / 2 : OOB) >> ((n & 1) * 4)) & 15u;
+    st.sz[nb] = s | (z << 16);
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int tok = mt * 16 + r;
+    const uint32_t tok = mt * 16 + r;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (tok < a.M)
-        st.x[mt][j] = *(const u32x4*)(a.X + (int64_t)tok * a.ldx + kb * 128 + j * 32 + h * 8);
-      else
-        st.x[mt][j] = u32x4{0, 0, 0, 0};
-    }
+    for (int j = 0; j < 4; ++j)
+      st.x[mt][j] = buf_load16(rs.x, (int)tok < a.M ? (tok * (uint32_t)a.ldx + kb * 128 + j * 32 + h * 8) * 2u : OOB);
   }
 }
 
@@ -129,11 +127,17 @@ __global__ __launch_bounds__(64 * KW) void k_w4a16_skinny(W4Launch a) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = f32x4{0, 0, 0, 0};
 
+  SkinnyRes rs;
+  rs.w = make_rsrc(a.w, (uint32_t)((int64_t)a.N * a.K / 2));
+  rs.x = make_rsrc(a.X, (uint32_t)((int64_t)a.M * a.ldx * 2));
+  rs.s = make_rsrc(a.scales, (uint32_t)((int64_t)a.N * (a.K / a.group) * 2));
+  rs.z = make_rsrc(a.zeros, (uint32_t)((int64_t)a.N / 2 * (a.K / a.group)));
+  rs.kblocks = kblocks;
   if (kb0 < kb1) {
     SkinnyStage<NB, MT> cur, nxt;
-    skinny_load<NB, MT>(cur, a, n_base, kb0, kblocks, lane);
+    skinny_load<NB, MT>(cur, a, rs, n_base, kb0, lane);
     for (int kb = kb0; kb < kb1; ++kb) {
-      if (kb + 1 < kb1) skinny_load<NB, MT>(nxt, a, n_base, kb + 1, kblocks, lane);
+      if (kb + 1 < kb1) skinny_load<NB, MT>(nxt, a, rs, n_base, kb + 1, lane);
       skinny_mma<NB, MT>(cur, acc);
       cur = nxt;
     }
@@ -153,7 +157,7 @@ __global__ __launch_bounds__(64 * KW) void k_w4a16_skinny(W4Launch a) {
     const int nb = idx / (MT * 64), mt = (idx / 64) % MT, q = idx % 64;
     const int n = n_base + nb * 16 + 4 * (q / 16), tok = mt * 16 + (q % 16);
     if (tok < a.M && n < a.N) {
-      *(u32x2*)(a.Y + (int64_t)tok * a.ldy + n) = u32x2{to_bits<DT_F16>(s[0]) | (to_bits<DT_F16>(s[1]) << 16),
+      *(gu32x2*)(a.Y + (int64_t)tok * a.ldy + n) = u32x2{to_bits<DT_F16>(s[0]) | (to_bits<DT_F16>(s[1]) << 16),
                                                         to_bits<DT_F16>(s[2]) | (to_bits<DT_F16>(s[3]) << 16)};
     }
   }
@@ -164,7 +168,7 @@ __global__ __launch_bounds__(64 * KW) void k_w4a16_skinny(W4Launch a) {
 // weight (dequantised on its way into LDS) as the column-major B operand.
 // ---------------------------------------------------------------------------
 template <class Cfg>
-__global__ __launch_bounds__(Cfg::THREADS) void k_w4a16_tiled(W4Launch a, int tiles_m, int total_tiles) {
+__global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_w4a16_tiled(W4Launch a, int tiles_m, int total_tiles) {
   __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
   const int G = gridDim.x;
   const W4Geom g{a.w, a.scales, a.zeros, a.N, a.K, a.group};
@@ -181,18 +185,18 @@ __global__ __launch_bounds__(Cfg::THREADS) void k_w4a16_tiled(W4Launch a, int ti
     t.ldc = 0;
     t.D = a.Y;
     t.ldd = a.ldy;
-    DenseLoader<Cfg::BM, Cfg::THREADS> al;
-    W4Loader<Cfg::BN, Cfg::THREADS> bl;
+    DenseLoader<Cfg, Cfg::BM> al;
+    W4Loader<Cfg, Cfg::BN> bl;
     al.init(a.X, a.ldx, t.m0, t.M, t.K);
     bl.init(g, t.n0);
     f32x16 acc[Cfg::TM][Cfg::TN];
-    mainloop<Cfg, DT_F16>(lds, al, bl, t.K / BK, acc);
-    epilogue<Cfg, DT_F16>(t, acc, 1.0f, 0.0f);
+    mainloop<Cfg, DT_F16>(lds, al, bl, t.K / Cfg::BK, acc);
+    store_tile<Cfg, DT_F16>(t, acc, 1.0f, 0.0f, lds);
   }
 }
 
-using W4Cfg256 = TileCfg<256, 256, 2, 2>;
-using W4Cfg128 = TileCfg<128, 128, 2, 2>;
+using W4Cfg256 = TileCfg<256, 256, 2, 2, 64, 2>;
+using W4Cfg128 = TileCfg<128, 128, 2, 2, 64, 2>;
 
 hipError_t launch_w4a16(const W4Launch& a, hipStream_t stream) {
   if (a.M <= 64) {
