@@ -185,6 +185,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--headline-only", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-ref", action="store_true",
+                    help="after the timed region, run one plain 256 MiB device copy (a known-size kernel that "
+                         "calibrates hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library's kernels run on a single device and there is no "
@@ -227,8 +230,14 @@ def main():
                    "cache": f"cold: {R} rotating copies of the {ws / 2**20:.0f} MiB working set"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_16, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_MFMA_16, 4), "traffic": None,
-                     "kernel": "k_gemm_ptr_array<TileCfg<256,256,2,2,32,4>, bf16, false>"},
+                     "kernel": "k_gemm_ptr_array<TileCfg<256,256,4,2,64,2,5>, bf16, false>"},
     }
+    if args.copy_ref:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.headline_only:
         result["workloads"] = bench_workloads(torch, gmi, gi, dev, args)
     if not args.no_cpu_baseline:

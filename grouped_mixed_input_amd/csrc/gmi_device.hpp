@@ -113,14 +113,19 @@ __device__ __forceinline__ uint32_t buf_load2(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ uint32_t buf_load1(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
 }
+// Output stores are streaming (nt): each result is written once and not read
+// back by the kernel, so the L2 sends it on toward memory instead of holding it
+// dirty until the end-of-kernel writeback, which would serialize the whole
+// output write after the last tile.
+constexpr int CPOL_NT = 2;
 __device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, u32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, CPOL_NT);
 }
 __device__ __forceinline__ void buf_store8(rsrc_t r, uint32_t off, u32x2 v) {
-  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, CPOL_NT);
 }
 __device__ __forceinline__ void buf_store2(rsrc_t r, uint32_t off, uint32_t v) {
-  __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, (int)off, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, (int)off, 0, CPOL_NT);
 }
 
 // s_waitcnt: gfx9 encoding, vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8
@@ -154,33 +159,39 @@ __device__ __forceinline__ u32x4 mask_tail(u32x4 v, int n) {
 // slot c ^ ((r / RPL) % CPR): the rows sharing a bank position within their
 // lines get distinct slots.
 // ---------------------------------------------------------------------------
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int STAGES_>
+// SLOTS_ = 0: a ring of STAGES stages, each holding one k-tile of A and of B.
+// SLOTS_ > 0 (BM == BN): a ring of SLOTS_ single-operand slots, A of k-tile
+// kt in slot 2 kt and B in slot 2 kt + 1 (mod SLOTS_); STAGES is then unused.
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int STAGES_, int SLOTS_ = 0>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, SLOTS = SLOTS_;
+  static constexpr int RING_BYTES = SLOTS_ > 0 ? SLOTS_ * BM_ * BK_ * 2 : STAGES_ * (BM_ + BN_) * BK_ * 2;
   // workgroups one CU holds: LDS-bound (160 KB); the kernels' launch bounds
-  // hold the registers to match (waves per SIMD = workgroups per CU)
-  static constexpr int WGS_PER_CU = (160 * 1024) / (STAGES_ * (BM_ + BN_) * BK_ * 2) >= 2 ? 2 : 1;
+  // hold the registers to match (waves per SIMD = workgroups per CU x NW / 4)
+  static constexpr int WGS_PER_CU = (160 * 1024) / RING_BYTES >= 2 ? 2 : 1;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
-  static constexpr int THREADS = 64 * WAVES_M * WAVES_N;
+  static constexpr int NW = WAVES_M * WAVES_N, THREADS = 64 * NW;
   static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;  // wave tile
   static constexpr int TM = WTM / 32, TN = WTN / 32;            // 32x32 blocks per wave
   static constexpr int ROWB = BK * 2, CPR = ROWB / 16, RPL = 256 / ROWB;
   static constexpr int RPI = 1024 / ROWB;  // rows moved by one 1 KB wave copy
   static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
-  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static constexpr int SLOT_BYTES = A_BYTES;
+  static constexpr int LDS_BYTES = RING_BYTES;
+  static_assert(SLOTS == 0 || (BM == BN && SLOTS >= 5), "split ring: square tile, at least five slots");
   static_assert(BK == 32 || BK == 64, "k-tile of 32 or 64");
-  static_assert(THREADS == 256, "4 waves");
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
   static_assert(STAGES >= 2 && LDS_BYTES <= 160 * 1024, "LDS budget");
   __device__ static __forceinline__ int swz(int row) { return (row / RPL) % CPR; }
   __device__ static __forceinline__ int off(int row, int chunk) { return row * ROWB + ((chunk ^ swz(row)) << 4); }
-  // direct-to-LDS copies: instruction i of wave w fills rows RPI (4 i + w) + l / CPR;
+  // direct-to-LDS copies: instruction i of wave w fills rows RPI (NW i + w) + l / CPR;
   // lane l writes slot l % CPR of its row, i.e. k-chunk (l % CPR) ^ swz(row)
-  __device__ static __forceinline__ int dma_row(int i, int lane) { return RPI * (4 * i + wave_id()) + lane / CPR; }
+  __device__ static __forceinline__ int dma_row(int i, int lane) { return RPI * (NW * i + wave_id()) + lane / CPR; }
   __device__ static __forceinline__ int dma_chunk(int lane) { return (lane % CPR) ^ swz(dma_row(0, lane)); }
   // wave-uniform (scalar) LDS destination of copy i
-  __device__ static __forceinline__ char* dma_dst(char* tile, int i) { return tile + (4 * i + wave_id()) * 1024; }
+  __device__ static __forceinline__ char* dma_dst(char* tile, int i) { return tile + (NW * i + wave_id()) * 1024; }
 };
 
 // One output tile of one GEMM problem, as the persistent walk hands it out.
@@ -208,8 +219,8 @@ template <class Cfg, int ROWS, bool KTAIL = false>
 struct DenseLoader {
   static constexpr bool kDMA = true;
   static constexpr bool kFIX = KTAIL;  // fix_tail may write LDS
-  static constexpr int P = ROWS * Cfg::ROWB / 4096;  // 1 KB copies per wave per k-tile
-  static_assert(P >= 1 && ROWS % (4 * Cfg::RPI) == 0, "rows must fill whole copy passes");
+  static constexpr int P = ROWS * Cfg::ROWB / (1024 * Cfg::NW);  // 1 KB copies per wave per k-tile
+  static_assert(P >= 1 && ROWS % (Cfg::NW * Cfg::RPI) == 0, "rows must fill whole copy passes");
   rsrc_t rs;
   uint32_t voff[P];  // lane offset of copy i within k-tile 0, bytes
   int K, nk;
@@ -228,7 +239,7 @@ struct DenseLoader {
     rs = make_rsrc(base + (int64_t)row0 * ld, (uint32_t)left * (uint32_t)ld * 2u);
     const int lane = threadIdx.x & 63;
     const uint32_t v0 = (uint32_t)Cfg::dma_row(0, lane) * (uint32_t)ld * 2u + (uint32_t)Cfg::dma_chunk(lane) * 16u;
-    const uint32_t step = 4u * Cfg::RPI * (uint32_t)ld * 2u;
+    const uint32_t step = (uint32_t)(Cfg::NW * Cfg::RPI) * (uint32_t)ld * 2u;
 #pragma unroll
     for (int i = 0; i < P; ++i) voff[i] = v0 + i * step;
     K = K_;
@@ -339,8 +350,8 @@ template <class Cfg, int ROWS>
 struct ConvLoader {
   static constexpr bool kDMA = true;
   static constexpr bool kFIX = false;
-  static constexpr int P = ROWS * Cfg::ROWB / 4096;
-  static_assert(P >= 1 && ROWS % (4 * Cfg::RPI) == 0, "rows must fill whole copy passes");
+  static constexpr int P = ROWS * Cfg::ROWB / (1024 * Cfg::NW);
+  static_assert(P >= 1 && ROWS % (Cfg::NW * Cfg::RPI) == 0, "rows must fill whole copy passes");
   rsrc_t rs;
   int H, W, C, S, dh, dw, Kg;
   int pix[P];        // first pixel of the row's image: n * H * W
@@ -446,6 +457,7 @@ struct W4Geom {
 template <class Cfg, int ROWS>
 struct W4Loader {
   static constexpr bool kDMA = false;
+  static constexpr bool kFIX = false;
   static constexpr int ENTRIES = ROWS / 16 * 64;
   static constexpr int P = ENTRIES / Cfg::THREADS;
   static_assert(Cfg::BK == 64, "the uint4 loader moves half a 128-k block per k-tile");
@@ -524,51 +536,75 @@ struct PrepOf<Ld, false> {
 
 // ---------------------------------------------------------------------------
 // Multiply one stage: acc[i][j] += B-fragment j x A-fragment i for every 16-k
-// step.  The MFMA's first operand is the B tile (rows n), its second the A
-// tile (rows m), so each lane's four consecutive result registers are four
-// consecutive n of one output row m.  On entry fa[0] / fb[0] hold this
-// stage's first-step fragments; during step kk the fragments of step kk + 1
-// are read, and during the last step those of the first step of stage `nxs`
-// (the next k-tile, already visible when CROSS is set) -- so no step starts
-// by waiting on LDS.  The instruction order is fixed slot by slot (each slot
-// closed by a scheduling barrier): one MFMA, then one fragment read, then the
-// direct-to-LDS copies of k-tile kt_dma that fall in this slot, spread evenly
-// over the stage so the memory pipeline is fed at its own rate instead of
-// receiving a burst that would stall the wave (and the matrix core) at issue.
+// step, the A tile at `sa` and the B tile at `sb`.  The MFMA's first operand
+// is the B tile (rows n), its second the A tile (rows m), so each lane's four
+// consecutive result registers are four consecutive n of one output row m.
+// On entry fa[0] / fb[0] hold this stage's first-step fragments; during step
+// kk the fragments of step kk + 1 are read, and during the last step those of
+// the first step of the next k-tile at `na` / `nb` (already visible when
+// CROSS is set) -- so no step starts by waiting on LDS.  The instruction order
+// is fixed slot by slot (each slot closed by a scheduling barrier): one MFMA,
+// then one fragment read, then the direct-to-LDS copies that fall in this
+// slot -- first those of loader l1 (k-tile k1 into d1), then those of l2 (k2
+// into d2) -- spread evenly over the first 1 / SPAN_DIV of the stage so the
+// memory pipeline is fed at its own rate instead of receiving a burst that
+// would stall the wave (and the matrix core) at issue.
 // ---------------------------------------------------------------------------
+// Per-lane LDS byte offsets of this wave's fragments, one per 16-k step and
+// operand: the row of fragment i (j) is 32 i (32 j) past the first and the
+// swizzle repeats every RPL * CPR rows, which divides 32, so fragment i sits a
+// constant 32 i rows past fragment 0 of the same step.
 template <class Cfg>
-__device__ __forceinline__ void read_frags(const char* st, int kk, u32x4 (&fa)[Cfg::TM], u32x4 (&fb)[Cfg::TN]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = (wave / Cfg::WAVES_N) * Cfg::WTM, wn = (wave % Cfg::WAVES_N) * Cfg::WTN;
-  const int frow = lane & 31, fchunk = lane >> 5;
+struct FragAddr {
+  static constexpr int KK = Cfg::BK / 16;
+  static_assert(32 % (Cfg::RPL * Cfg::CPR) == 0, "swizzle period must divide the fragment row step");
+  uint32_t a[KK], b[KK];
+  __device__ __forceinline__ void init() {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = (wave / Cfg::WAVES_N) * Cfg::WTM, wn = (wave % Cfg::WAVES_N) * Cfg::WTN;
+    const int frow = lane & 31, fchunk = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < Cfg::TM; ++i) fa[i] = *(const u32x4*)(st + Cfg::off(wm + i * 32 + frow, kk * 2 + fchunk));
-#pragma unroll
-  for (int j = 0; j < Cfg::TN; ++j)
-    fb[j] = *(const u32x4*)(st + Cfg::A_BYTES + Cfg::off(wn + j * 32 + frow, kk * 2 + fchunk));
+    for (int kk = 0; kk < KK; ++kk) {
+      a[kk] = (uint32_t)Cfg::off(wm + frow, kk * 2 + fchunk);
+      b[kk] = (uint32_t)Cfg::off(wn + frow, kk * 2 + fchunk);
+    }
+  }
+};
+
+template <class Cfg>
+__device__ __forceinline__ u32x4 frag_at(const char* st, uint32_t base, int blk) {
+  return *(const u32x4*)(st + base + blk * 32 * Cfg::ROWB);
 }
 
-template <class Cfg, int DT, bool CROSS, class ALd, class BLd>
-__device__ __forceinline__ void multiply_stage(const char* st, const char* nxs, f32x16 (&acc)[Cfg::TM][Cfg::TN],
-                                               u32x4 (&fa)[2][Cfg::TM], u32x4 (&fb)[2][Cfg::TN], const ALd& al,
-                                               const BLd& bl, int kt_dma, char* dma_st) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = (wave / Cfg::WAVES_N) * Cfg::WTM, wn = (wave % Cfg::WAVES_N) * Cfg::WTN;
-  const int frow = lane & 31, fchunk = lane >> 5;
+template <class Cfg>
+__device__ __forceinline__ void read_frags(const FragAddr<Cfg>& fa_, const char* sa, const char* sb, int kk,
+                                           u32x4 (&fa)[Cfg::TM], u32x4 (&fb)[Cfg::TN]) {
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i) fa[i] = frag_at<Cfg>(sa, fa_.a[kk], i);
+#pragma unroll
+  for (int j = 0; j < Cfg::TN; ++j) fb[j] = frag_at<Cfg>(sb, fa_.b[kk], j);
+}
+
+template <class Cfg, int DT, bool CROSS, int SPAN_DIV, class L1, class L2>
+__device__ __forceinline__ void multiply_stage(const FragAddr<Cfg>& ad, const char* sa, const char* sb,
+                                               const char* na, const char* nb, f32x16 (&acc)[Cfg::TM][Cfg::TN],
+                                               u32x4 (&fa)[2][Cfg::TM], u32x4 (&fb)[2][Cfg::TN], const L1& l1,
+                                               int k1, char* d1, const L2& l2, int k2, char* d2) {
   constexpr int KK = Cfg::BK / 16;
   static_assert(KK % 2 == 0, "fragment double buffer flips once per step");
   constexpr int NMFMA = Cfg::TM * Cfg::TN, NDS = Cfg::TM + Cfg::TN;
-  constexpr int PA = dma_count<ALd>(), PB = dma_count<BLd>(), T = PA + PB;
-  constexpr int SPAN = KK * NMFMA;  // copy slots
-  typename PrepOf<ALd>::type pa{};
-  typename PrepOf<BLd>::type pb{};
-  if constexpr (PA > 0) pa = al.prep(kt_dma);
-  if constexpr (PB > 0) pb = bl.prep(kt_dma);
+  constexpr int P1 = dma_count<L1>(), P2 = dma_count<L2>(), T = P1 + P2;
+  constexpr int SPAN = (KK * NMFMA + SPAN_DIV - 1) / SPAN_DIV;  // copy slots
+  typename PrepOf<L1>::type p1{};
+  typename PrepOf<L2>::type p2{};
+  if constexpr (P1 > 0) p1 = l1.prep(k1);
+  if constexpr (P2 > 0) p2 = l2.prep(k2);
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
     const int cur = kk & 1, nx = cur ^ 1;
     const bool rd = CROSS || kk + 1 < KK;  // fragments to read during this step
-    const char* src = (kk + 1 < KK) ? st : nxs;
+    const char* ra = (kk + 1 < KK) ? sa : na;
+    const char* rb = (kk + 1 < KK) ? sb : nb;
     const int rk = (kk + 1 < KK) ? kk + 1 : 0;
 #pragma unroll
     for (int m = 0; m < NMFMA; ++m) {
@@ -576,20 +612,20 @@ __device__ __forceinline__ void multiply_stage(const char* st, const char* nxs, 
       acc[i][j] = mfma32<DT>(fb[cur][j], fa[cur][i], acc[i][j]);
       if (rd) {
         if (m < Cfg::TM)
-          fa[nx][m] = *(const u32x4*)(src + Cfg::off(wm + m * 32 + frow, rk * 2 + fchunk));
+          fa[nx][m] = frag_at<Cfg>(ra, ad.a[rk], m);
         else if (m < NDS)
-          fb[nx][m - Cfg::TM] =
-              *(const u32x4*)(src + Cfg::A_BYTES + Cfg::off(wn + (m - Cfg::TM) * 32 + frow, rk * 2 + fchunk));
+          fb[nx][m - Cfg::TM] = frag_at<Cfg>(rb, ad.b[rk], m - Cfg::TM);
       }
       const int slot = kk * NMFMA + m;
-      const int v0 = (slot * T + SPAN - 1) / SPAN, v1 = ((slot + 1) * T + SPAN - 1) / SPAN;
+      const int v0 = slot < SPAN ? (slot * T + SPAN - 1) / SPAN : T;
+      const int v1 = slot < SPAN ? ((slot + 1) * T + SPAN - 1) / SPAN : T;
 #pragma unroll
       for (int v = v0; v < v1; ++v) {
-        if constexpr (PA > 0) {
-          if (v < PA) al.issue_one(v, pa, dma_st);
+        if constexpr (P1 > 0) {
+          if (v < P1) l1.issue_one(v, p1, d1);
         }
-        if constexpr (PB > 0) {
-          if (v >= PA) bl.issue_one(v - PA, pb, dma_st + Cfg::A_BYTES);
+        if constexpr (P2 > 0) {
+          if (v >= P1) l2.issue_one(v - P1, p2, d2);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -599,10 +635,9 @@ __device__ __forceinline__ void multiply_stage(const char* st, const char* nxs, 
 #pragma unroll
         for (int m = NMFMA; m < NDS; ++m) {
           if (m < Cfg::TM)
-            fa[nx][m] = *(const u32x4*)(src + Cfg::off(wm + m * 32 + frow, rk * 2 + fchunk));
+            fa[nx][m] = frag_at<Cfg>(ra, ad.a[rk], m);
           else
-            fb[nx][m - Cfg::TM] =
-                *(const u32x4*)(src + Cfg::A_BYTES + Cfg::off(wn + (m - Cfg::TM) * 32 + frow, rk * 2 + fchunk));
+            fb[nx][m - Cfg::TM] = frag_at<Cfg>(rb, ad.b[rk], m - Cfg::TM);
         }
       }
     }
@@ -610,26 +645,43 @@ __device__ __forceinline__ void multiply_stage(const char* st, const char* nxs, 
 }
 
 // ---------------------------------------------------------------------------
-// Mainloop over a ring of STAGES LDS stages.  Direct-to-LDS operands (EARLY
-// scheme, STAGES >= 3, prefetch distance D = STAGES - 1): while the waves
-// multiply k-tile kt, the copies of k-tile kt + D stream into the stage freed
-// by k-tile kt - 1.  At the end of k-tile kt each wave waits until its own
-// copies of k-tile kt + 2 have landed (vmcnt counts down in issue order, so
-// the younger k-tiles stay in flight) and a barrier publishes them; k-tile
-// kt + 1, published one step earlier, is already being read -- its first
-// fragments come in during the last step of kt.  Copies past the last k-tile
-// are issued anyway (they land as zeros), keeping counts uniform and the
-// multiply free of branches.  Register-staged operands (uint4 weights, two
-// stages): the loads of k-tile kt + 1 are written to LDS after the multiply
-// of kt and the wait is for everything.
+// Mainloop.  Three schemes, picked by the tile configuration:
+//
+// Split ring (SLOTS > 0, direct-to-LDS operands): single-operand slots, A of
+// k-tile kt in slot 2 kt, B in slot 2 kt + 1 (mod SLOTS).  While the waves
+// multiply k-tile kt (two slots), the other three or more slots take the
+// copies of B of kt + 1 (early in the stage) and A of kt + 2 (late in the
+// stage), so the copy stream never drains; at the end of kt each wave waits
+// for its copies of B of kt + 1 only (vmcnt counts down in issue order, A of
+// kt + 2 stays in flight) and a barrier publishes k-tile kt + 1.
+//
+// Stage ring (EARLY, STAGES >= 3, direct-to-LDS operands, prefetch distance
+// D = STAGES - 1): while the waves multiply k-tile kt, the copies of k-tile
+// kt + D stream into the stage freed by k-tile kt - 1; at the end of kt each
+// wave waits until its copies of k-tile kt + 2 have landed and a barrier
+// publishes them; k-tile kt + 1, published one step earlier, is already
+// being read -- its first fragments come in during the last step of kt.
+//
+// Two stages (register-staged operands such as the uint4 weights, or two
+// direct-to-LDS stages): the loads of k-tile kt + 1 are issued during the
+// multiply of kt (copies in its first half), written to the other stage and
+// waited for in full at the end of kt.
+//
+// Copies past the last k-tile are issued anyway (they re-read the last
+// k-tile or land as zeros), keeping counts uniform and the multiply free of
+// branches.
 // ---------------------------------------------------------------------------
 template <class Cfg, int DT, class ALd, class BLd>
 __device__ __forceinline__ void mainloop(char* lds, const ALd& al, const BLd& bl, int nk,
                                          f32x16 (&acc)[Cfg::TM][Cfg::TN]) {
   constexpr int S = Cfg::STAGES, D = S - 1;
-  constexpr int PT = dma_count<ALd>() + dma_count<BLd>();
-  constexpr bool REG = !ALd::kDMA || !BLd::kDMA;
-  static_assert(REG ? S == 2 : S >= 3, "register-staged operands use two stages, direct-to-LDS at least three");
+  constexpr int PA = dma_count<ALd>(), PB = dma_count<BLd>(), PT = PA + PB;
+  constexpr bool DMA = ALd::kDMA && BLd::kDMA;
+  constexpr bool SPLIT = Cfg::SLOTS > 0;
+  constexpr bool REG = !SPLIT && (!DMA || S == 2);
+  constexpr bool FIX = ALd::kFIX || BLd::kFIX;
+  static_assert(!SPLIT || DMA, "the split ring takes direct-to-LDS operands");
+  static_assert(SPLIT || (REG ? S == 2 : S >= 3), "register-staged operands use two stages");
 #pragma unroll
   for (int i = 0; i < Cfg::TM; ++i)
 #pragma unroll
@@ -638,8 +690,36 @@ __device__ __forceinline__ void mainloop(char* lds, const ALd& al, const BLd& bl
   __builtin_amdgcn_s_barrier();
   if (nk <= 0) return;
   u32x4 fa[2][Cfg::TM], fb[2][Cfg::TN];
+  FragAddr<Cfg> ad;
+  ad.init();
 
-  if constexpr (!REG) {
+  if constexpr (SPLIT) {
+    constexpr int NS = Cfg::SLOTS;
+    // prologue: A0 -> slot 0, B0 -> 1, A1 -> 2; A0 and B0 landed and published
+    al.issue(0, lds);
+    bl.issue(0, lds + Cfg::SLOT_BYTES);
+    al.issue(1, lds + 2 * Cfg::SLOT_BYTES);
+    wait_vm_le<PA>();
+    al.fix_tail(0, lds);
+    bl.fix_tail(0, lds + Cfg::SLOT_BYTES);
+    if constexpr (FIX) wait_lgkm();
+    __builtin_amdgcn_s_barrier();
+    int sa = 0;  // slot of A of k-tile kt; B follows
+    for (int kt = 0; kt < nk; ++kt) {
+      const int sb = (sa + 1) % NS, a1 = (sa + 2) % NS, b1 = (sa + 3) % NS, a2 = (sa + 4) % NS;
+      const char* pa = lds + sa * Cfg::SLOT_BYTES;
+      const char* pb = lds + sb * Cfg::SLOT_BYTES;
+      read_frags<Cfg>(ad, pa, pb, 0, fa[0], fb[0]);
+      multiply_stage<Cfg, DT, false, 1>(ad, pa, pb, pa, pb, acc, fa, fb, bl, kt + 1, lds + b1 * Cfg::SLOT_BYTES, al,
+                                        kt + 2, lds + a2 * Cfg::SLOT_BYTES);
+      wait_vm_le<PA>();
+      al.fix_tail(kt + 1, lds + a1 * Cfg::SLOT_BYTES);
+      bl.fix_tail(kt + 1, lds + b1 * Cfg::SLOT_BYTES);
+      if constexpr (FIX) wait_lgkm();  // the masked chunks are in LDS before the barrier
+      __builtin_amdgcn_s_barrier();
+      sa = a1;
+    }
+  } else if constexpr (!REG) {
     // prologue: k-tiles 0 .. D - 1; k-tiles 0 and 1 landed and published
 #pragma unroll
     for (int s = 0; s < D; ++s) {
@@ -647,7 +727,6 @@ __device__ __forceinline__ void mainloop(char* lds, const ALd& al, const BLd& bl
       al.issue(s, st);
       bl.issue(s, st + Cfg::A_BYTES);
     }
-    constexpr bool FIX = ALd::kFIX || BLd::kFIX;
     wait_vm_le<(D - 2) * PT>();
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -656,15 +735,17 @@ __device__ __forceinline__ void mainloop(char* lds, const ALd& al, const BLd& bl
     }
     if constexpr (FIX) wait_lgkm();
     __builtin_amdgcn_s_barrier();
-    read_frags<Cfg>(lds, 0, fa[0], fb[0]);
+    read_frags<Cfg>(ad, lds, lds + Cfg::A_BYTES, 0, fa[0], fb[0]);
     int cs = 0;  // stage of k-tile kt
     // one loop body (a second copy makes the register allocator shuttle the
     // accumulators between AGPRs and VGPRs); stages are picked per k-tile
     for (int kt = 0; kt < nk; ++kt) {
       const int n1 = (cs + 1) % S, n2 = (cs + 2) % S, nd = (cs + D) % S;
-      char* cur = lds + cs * Cfg::STAGE_BYTES;
-      multiply_stage<Cfg, DT, true>(cur, lds + n1 * Cfg::STAGE_BYTES, acc, fa, fb, al, bl, kt + D,
-                                    lds + nd * Cfg::STAGE_BYTES);
+      const char* cur = lds + cs * Cfg::STAGE_BYTES;
+      const char* nxs = lds + n1 * Cfg::STAGE_BYTES;
+      char* dst = lds + nd * Cfg::STAGE_BYTES;
+      multiply_stage<Cfg, DT, true, 1>(ad, cur, cur + Cfg::A_BYTES, nxs, nxs + Cfg::A_BYTES, acc, fa, fb, al, kt + D,
+                                       dst, bl, kt + D, dst + Cfg::A_BYTES);
       wait_vm_le<(D - 2) * PT>();
       al.fix_tail(kt + 2, lds + n2 * Cfg::STAGE_BYTES);
       bl.fix_tail(kt + 2, lds + n2 * Cfg::STAGE_BYTES + Cfg::A_BYTES);
@@ -684,7 +765,7 @@ __device__ __forceinline__ void mainloop(char* lds, const ALd& al, const BLd& bl
     __builtin_amdgcn_s_barrier();
     int cs = 0;
     for (int kt = 0; kt < nk; ++kt) {
-      char* cur = lds + cs * Cfg::STAGE_BYTES;
+      const char* cur = lds + cs * Cfg::STAGE_BYTES;
       char* nxt = lds + (cs ^ 1) * Cfg::STAGE_BYTES;
       const bool more = kt + 1 < nk;
       if constexpr (!ALd::kDMA) {
@@ -693,8 +774,9 @@ __device__ __forceinline__ void mainloop(char* lds, const ALd& al, const BLd& bl
       if constexpr (!BLd::kDMA) {
         if (more) bl.load(kt + 1, rb);
       }
-      read_frags<Cfg>(cur, 0, fa[0], fb[0]);
-      multiply_stage<Cfg, DT, false>(cur, cur, acc, fa, fb, al, bl, kt + 1, nxt);
+      read_frags<Cfg>(ad, cur, cur + Cfg::A_BYTES, 0, fa[0], fb[0]);
+      multiply_stage<Cfg, DT, false, 2>(ad, cur, cur + Cfg::A_BYTES, cur, cur + Cfg::A_BYTES, acc, fa, fb, al, kt + 1,
+                                        nxt, bl, kt + 1, nxt + Cfg::A_BYTES);
       wait_vm_le<0>();
       if (more) {
         if constexpr (ALd::kDMA) al.fix_tail(kt + 1, nxt); else al.store(nxt, ra);
@@ -705,8 +787,8 @@ __device__ __forceinline__ void mainloop(char* lds, const ALd& al, const BLd& bl
       cs ^= 1;
     }
   }
-  // copies past the last k-tile are still landing (as zeros): drain them
-  // before anyone reuses the stages
+  // copies past the last k-tile are still landing: drain them before anyone
+  // reuses the ring
   wait_vm_le<0>();
   __builtin_amdgcn_s_barrier();
 }
@@ -734,12 +816,17 @@ template <class Cfg, int DT>
 __device__ __forceinline__ void store_tile(const Tile& t, const f32x16 (&acc)[Cfg::TM][Cfg::TN], float alpha,
                                            float beta, char* lds) {
   constexpr int ROWB = Cfg::WTN * 4;  // fp32 row of the wave tile
-  constexpr int PASS = (4 * 2 * 32 * ROWB <= Cfg::LDS_BYTES) ? 2 : 1;  // 32-row blocks per pass
+  constexpr int PASS = (Cfg::NW * 2 * 32 * ROWB <= Cfg::LDS_BYTES) ? 2 : 1;  // 32-row blocks per pass
   constexpr int REGION = PASS * 32 * ROWB;
-  static_assert(4 * REGION <= Cfg::LDS_BYTES && Cfg::TM % PASS == 0, "four wave regions must fit the stages");
+  static_assert(Cfg::NW * REGION <= Cfg::LDS_BYTES && Cfg::TM % PASS == 0, "the wave regions must fit the stages");
   constexpr int LPR = Cfg::WTN / 8;  // lanes per row on read-back (8 floats each)
   constexpr int RPI = 64 / LPR;      // rows per read-back instruction
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the staging addresses depend only on the lane; kept opaque here so they
+  // are formed per tile instead of being hoisted out of the tile loop and
+  // held in registers through the mainloop
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wave = tid >> 6;
   const int wm = (wave / Cfg::WAVES_N) * Cfg::WTM, wn = (wave % Cfg::WAVES_N) * Cfg::WTN;
   char* reg = lds + wave * REGION;
   auto slot = [](int r, int x) { return (x ^ (r & 15) ^ ((x >> 4) & 1)) << 4; };
@@ -809,5 +896,19 @@ __device__ __forceinline__ void store_tile(const Tile& t, const f32x16 (&acc)[Cf
 // ---------------------------------------------------------------------------
 constexpr int XCDS = 8;
 __device__ __forceinline__ int remap_slot(int w, int G) { return (w % XCDS) * (G / XCDS) + w / XCDS; }
+
+// Tile order inside one problem of tm x tn tiles: bands of up to RASTER_M
+// m-tiles, the m index fastest inside a band.  An XCD's run of consecutive
+// tiles then covers a block of at most RASTER_M m-tiles by a few n-tiles, so
+// at every k-step its CUs fetch few distinct A and B panel slices into its L2.
+constexpr int RASTER_M = 8;
+__device__ __forceinline__ void raster(int local, int tm, int tn, int& mi, int& ni) {
+  const int band = local / (RASTER_M * tn);
+  const int r = local - band * RASTER_M * tn;
+  const int left = tm - band * RASTER_M;
+  const int rows = left < RASTER_M ? left : RASTER_M;
+  mi = band * RASTER_M + r % rows;
+  ni = r / rows;
+}
 
 }  // namespace gmi

@@ -50,7 +50,7 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_conv_fprop(Co
   }
 }
 
-using ConvCfg256 = TileCfg<256, 256, 2, 2, 32, 4>;
+using ConvCfg256 = TileCfg<256, 256, 4, 2, 64, 2, 5>;
 using ConvCfg256x128 = TileCfg<256, 128, 2, 2, 32, 3>;
 using ConvCfg128 = TileCfg<128, 128, 2, 2, 32, 4>;
 
@@ -74,19 +74,19 @@ hipError_t launch_conv_fprop(const ConvLaunch& p, int shape, int dtype, float al
   if (grid < XCDS) grid = XCDS;
   if (shape == TILE_256x256) {
     if (dtype == DT_F16)
-      hipLaunchKernelGGL((k_conv_fprop<ConvCfg256, DT_F16>), dim3(grid), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((k_conv_fprop<ConvCfg256, DT_F16>), dim3(grid), dim3(ConvCfg256::THREADS), 0, stream, a);
     else
-      hipLaunchKernelGGL((k_conv_fprop<ConvCfg256, DT_BF16>), dim3(grid), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((k_conv_fprop<ConvCfg256, DT_BF16>), dim3(grid), dim3(ConvCfg256::THREADS), 0, stream, a);
   } else if (shape == TILE_256x128) {
     if (dtype == DT_F16)
-      hipLaunchKernelGGL((k_conv_fprop<ConvCfg256x128, DT_F16>), dim3(grid), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((k_conv_fprop<ConvCfg256x128, DT_F16>), dim3(grid), dim3(ConvCfg256x128::THREADS), 0, stream, a);
     else
-      hipLaunchKernelGGL((k_conv_fprop<ConvCfg256x128, DT_BF16>), dim3(grid), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((k_conv_fprop<ConvCfg256x128, DT_BF16>), dim3(grid), dim3(ConvCfg256x128::THREADS), 0, stream, a);
   } else {
     if (dtype == DT_F16)
-      hipLaunchKernelGGL((k_conv_fprop<ConvCfg128, DT_F16>), dim3(grid), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((k_conv_fprop<ConvCfg128, DT_F16>), dim3(grid), dim3(ConvCfg128::THREADS), 0, stream, a);
     else
-      hipLaunchKernelGGL((k_conv_fprop<ConvCfg128, DT_BF16>), dim3(grid), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL((k_conv_fprop<ConvCfg128, DT_BF16>), dim3(grid), dim3(ConvCfg128::THREADS), 0, stream, a);
   }
   return hipGetLastError();
 }

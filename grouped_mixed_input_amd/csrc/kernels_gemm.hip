@@ -28,9 +28,10 @@ struct GroupedArgs {
   float alpha, beta;
 };
 
-// Tile ids are laid out problem after problem; inside a problem the m-tile
-// index runs fastest, so consecutive tiles (one XCD's share of a round) reuse
-// the same B panel -- the expert weight in a mixture-of-experts layer.
+// Tile ids are laid out problem after problem, and inside a problem in bands
+// of m-tiles (raster), so one XCD's share of a round -- consecutive tiles --
+// reuses a few A and B panels, e.g. one expert weight in a mixture-of-experts
+// layer.
 template <class Cfg, int DT, bool KTAIL>
 __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_gemm_grouped(GroupedArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
@@ -42,13 +43,14 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_gemm_grouped(
     while (g + 1 < a.count && a.desc[g + 1].tile_start <= tile) ++g;
     const GroupDesc& d = a.desc[g];
     const int local = tile - d.tile_start;
-    const int tiles_m = (d.M + Cfg::BM - 1) / Cfg::BM;
+    int mi, ni;
+    raster(local, (d.M + Cfg::BM - 1) / Cfg::BM, (d.N + Cfg::BN - 1) / Cfg::BN, mi, ni);
     Tile t;
     t.M = d.M;
     t.N = d.N;
     t.K = d.K;
-    t.m0 = (local % tiles_m) * Cfg::BM;
-    t.n0 = (local / tiles_m) * Cfg::BN;
+    t.m0 = mi * Cfg::BM;
+    t.n0 = ni * Cfg::BN;
     t.A = d.A;
     t.lda = d.lda;
     t.B = d.B;
@@ -75,12 +77,14 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_gemm_ptr_arra
     const int tile = base + remap_slot(blockIdx.x, G);
     if (tile >= a.total_tiles) break;
     const int l = tile / a.tiles_per_batch, local = tile - l * a.tiles_per_batch;
+    int mi, ni;
+    raster(local, a.tiles_m, a.tiles_per_batch / a.tiles_m, mi, ni);
     Tile t;
     t.M = a.p.M;
     t.N = a.p.N;
     t.K = a.p.K;
-    t.m0 = (local % a.tiles_m) * Cfg::BM;
-    t.n0 = (local / a.tiles_m) * Cfg::BN;
+    t.m0 = mi * Cfg::BM;
+    t.n0 = ni * Cfg::BN;
     t.A = a.p.A[l];
     t.lda = a.p.lda;
     t.B = a.p.B[l];
@@ -93,9 +97,9 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_gemm_ptr_arra
   }
 }
 
-// 32-k stages: 4 x 32 KB (one workgroup per CU), 3 x 24 KB and 4 x 16 KB
-// (two per CU)
-using Cfg256 = TileCfg<256, 256, 2, 2, 32, 4>;
+// 32-k stages: 4 x 32 KB (one workgroup of 8 waves per CU), 3 x 24 KB and
+// 4 x 16 KB (two workgroups of 4 waves per CU)
+using Cfg256 = TileCfg<256, 256, 4, 2, 64, 2, 5>;
 using Cfg256x128 = TileCfg<256, 128, 2, 2, 32, 3>;
 using Cfg128 = TileCfg<128, 128, 2, 2, 32, 4>;
 
