@@ -27,6 +27,12 @@ sys.path.insert(0, ROOT)
 
 PEAK_MFMA_16 = 2516.6  # TFLOP/s, dense fp16 / bf16: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_HBM = 8000.0  # GB/s
+# HBM bytes per launch of the headline kernel: rocprofv3 FETCH_SIZE and WRITE_SIZE of the headline command,
+# each scaled by what the same counter reads for a plain 256 MiB device copy (FETCH x 1.9997, WRITE x 1.0);
+# summary and commands in profiles/k_gemm_ptr_array_256x256_bf16_ptr_array_L16_1024.md.  Valid for the
+# kernel named here only.
+HEADLINE_KERNEL = "k_gemm_ptr_array<TileCfg<256,256,4,2,64,2,5>, bf16, false>"
+HEADLINE_TRAFFIC_BYTES = 100978322
 MALL_BYTES = 256 << 20
 ROTATE_TARGET = 512 << 20
 METRIC = "TFLOP/s and % of MFMA peak: grouped bf16 GEMM, w4a16 GEMM, conv fprop"
@@ -229,8 +235,9 @@ def main():
                                "beta=0, fp32 accumulate, bf16 D", "L": 16, "M": 1024, "N": 1024, "K": 1024,
                    "cache": f"cold: {R} rotating copies of the {ws / 2**20:.0f} MiB working set"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_16, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_MFMA_16, 4), "traffic": None,
-                     "kernel": "k_gemm_ptr_array<TileCfg<256,256,4,2,64,2,5>, bf16, false>"},
+                     "frac": round(tflops / PEAK_MFMA_16, 4), "traffic": HEADLINE_TRAFFIC_BYTES,
+                     "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": 3 * 16 * 1024 * 1024 * 2,
+                     "kernel": HEADLINE_KERNEL},
     }
     if args.copy_ref:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
