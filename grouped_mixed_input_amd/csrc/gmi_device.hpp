@@ -100,6 +100,10 @@ __device__ __forceinline__ void dma16(rsrc_t r, uint32_t off, char* dst) {
 __device__ __forceinline__ void dma16s(rsrc_t r, uint32_t off, uint32_t soff, char* dst) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, (int)off, (int)soff, 0, 0);
 }
+// as dma16 with 4 bytes per lane (lane l's dword lands at dst + 4 l)
+__device__ __forceinline__ void dma4(rsrc_t r, uint32_t off, char* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 4, (int)off, 0, 0, 0);
+}
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
@@ -133,6 +137,19 @@ template <int N>
 __device__ __forceinline__ void wait_vm_le() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+// wait_vm_le<n> for an n known only after unrolling (n <= N): folds to one
+// s_waitcnt when n is a constant
+template <int N>
+__device__ __forceinline__ void wait_vm_le_n(int n) {
+  if constexpr (N == 0) {
+    wait_vm_le<0>();
+  } else {
+    if (n >= N)
+      wait_vm_le<N>();
+    else
+      wait_vm_le_n<N - 1>(n);
+  }
 }
 __device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07F); }  // lgkmcnt(0)
 
@@ -424,6 +441,19 @@ __device__ __forceinline__ f16x2 zero_pair(uint32_t z) {
   return __builtin_bit_cast(f16x2, (0x6400u | z) * 0x00010001u);
 }
 __device__ __forceinline__ f16x2 scale_pair(uint32_t s_bits) { return __builtin_bit_cast(f16x2, s_bits * 0x00010001u); }
+
+// The integer part only: q - z for the 8 nibbles of w, exact in fp16, for
+// kernels that apply the group scale to the fp32 partial sums instead.  The
+// OR constant is passed in a VGPR so that mask-and-OR is one v_and_or_b32.
+__device__ __forceinline__ u32x4 unpack8_minus_zero(uint32_t w, f16x2 zz, uint32_t magic) {
+  u32x4 out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f16x2 h = __builtin_bit_cast(f16x2, ((w >> (4 * i)) & 0x000F000Fu) | magic);
+    out[i] = __builtin_bit_cast(uint32_t, h - zz);
+  }
+  return out;
+}
 
 __device__ __forceinline__ u32x4 dequant8(uint32_t w, f16x2 zz, f16x2 ss) {
   u32x4 out;

@@ -164,6 +164,141 @@ __global__ __launch_bounds__(64 * KW) void k_w4a16_skinny(W4Launch a) {
 }
 
 // ---------------------------------------------------------------------------
+// Decode kernel (M <= 16): the weight stream is the whole cost (N K / 2 bytes
+// against 2 M (N + K) for X and Y), so it is put in flight as early and as
+// deep as the LDS allows.  Workgroup = KW waves over NB 16-row weight blocks;
+// wave w owns a contiguous range of 128-wide k-blocks, taken R at a time
+// (one round), and works alone until the final reduction.  Per round a wave
+// issues, without waiting:
+//   * two direct-to-LDS copies of the round's scale and zero-point rows
+//     (32 rows x R groups);
+//   * per k-block, its NB weight blocks of 1 KB each (one block of the
+//     prepacked layout per copy) into the wave's own LDS ring, then its X
+//     fragments into registers (token L % 16, k-group L / 16 of each 32-k
+//     step; L2-resident, shared by every workgroup).
+// It then multiplies the k-blocks in order, each after a wait that leaves the
+// younger weight copies in flight.  Per k-block (one 128-k scale group) the
+// MFMA takes the exact integers q - z as fp16 (the 0x6400 construction of
+// transform_A_kblock's conversion without the scale) into a fresh fp32
+// partial sum, and each output row's scale multiplies that partial sum:
+// sum_k (q - z) s x = sum over groups of s * sum_k (q - z) x, with the scale
+// applied in fp32 instead of rounding every weight to fp16 first.  All loads of a round are issued in
+// straight-line code before their first use, slot by slot (weight blocks,
+// then X fragments), so the weight stream starts at once and each wait --
+// ours or the compiler's for the X registers -- leaves the younger slots in
+// flight.  Slots past the wave's
+// range are pointed out of bounds (they land as zeros) so every wait counts a
+// fixed number of younger copies.
+// ---------------------------------------------------------------------------
+template <int NB, int R>
+struct DecodeLds {
+  static constexpr int WSLOT = NB * 1024;  // one k-block of the wave's weight rows
+  static constexpr int WRING = R * WSLOT;
+  static constexpr int SZ = 2048;           // scales (1 KB) then zero points (1 KB)
+  static constexpr int WAVE = WRING + SZ;
+  static_assert(NB == 2, "scale rows are 32 weight rows (64 bytes), zero rows 16 bytes");
+  static_assert(R * 4 <= 64, "one copy instruction carries a round's scale rows");
+};
+
+template <int NB, int KW, int R>
+__global__ __launch_bounds__(64 * KW) void k_w4a16_decode(W4Launch a) {
+  using L = DecodeLds<NB, R>;
+  __shared__ __attribute__((aligned(16))) char lds[KW * L::WAVE];
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  char* wring = lds + wave * L::WAVE;
+  char* szb = wring + L::WRING;
+  const int n_base = blockIdx.x * NB * 16;
+  const uint32_t N = a.N;
+  const int kblocks = a.K / 128;
+  const int per = (kblocks + KW - 1) / KW;
+  const int kb0 = wave * per;
+  const int kb1 = kb0 + per < kblocks ? kb0 + per : kblocks;
+  const int rounds = (per + R - 1) / R;
+
+  const rsrc_t rw = make_rsrc(a.w, (uint32_t)((int64_t)a.N * a.K / 2));
+  const rsrc_t rx = make_rsrc(a.X, (uint32_t)((int64_t)a.M * a.ldx * 2));
+  const rsrc_t rs = make_rsrc(a.scales, (uint32_t)((int64_t)a.N * (a.K / a.group) * 2));
+  const rsrc_t rz = make_rsrc(a.zeros, (uint32_t)((int64_t)a.N / 2 * (a.K / a.group)));
+  const uint32_t r = lane & 15, h = lane >> 4;
+  const bool tok_ok = (int)r < a.M;
+  uint32_t magic = 0x64006400u;  // fp16 pair (1024, 1024): 1024 + q for a nibble q in the low mantissa bits
+  asm volatile("" : "+v"(magic));
+
+  f32x4 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0, 0, 0, 0};
+
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int base = kb0 + rd * R;
+    u32x4 x[R][4];
+    {
+      // scales: lane -> slot lane / 4, 8-row chunk lane % 4 (16 bytes);
+      // zero points: the same slot and chunk, 4 bytes
+      const int s = lane >> 2, c = lane & 3, ks = base + s;
+      const uint32_t gs = (uint32_t)(ks * 128) / (uint32_t)a.group;
+      const bool ok = s < R && ks < kb1 && n_base + 8 * c < (int)N;
+      dma16(rs, ok ? (gs * N + n_base + 8 * c) * 2u : OOB, szb);
+      dma4(rz, ok ? gs * (N / 2) + n_base / 2 + 4 * c : OOB, szb + 1024);
+    }
+#pragma unroll
+    for (int s = 0; s < R; ++s) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const uint32_t blk = n_base / 16 + nb;
+        dma16(rw, base + s < kb1 && blk * 16 < N ? (blk * (uint32_t)kblocks + base + s) * 1024u + lane * 16u : OOB,
+              wring + s * L::WSLOT + nb * 1024);
+      }
+      const bool ok = base + s < kb1 && tok_ok;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        x[s][j] = buf_load16(rx, ok ? (r * (uint32_t)a.ldx + (base + s) * 128 + j * 32 + h * 8) * 2u : OOB);
+    }
+#pragma unroll
+    for (int s = 0; s < R; ++s) {
+      // weight blocks and X fragments of slot s (and everything older)
+      wait_vm_le_n<(R - 1) * (NB + 4)>((R - 1 - s) * (NB + 4));
+      if (base + s < kb1) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          // the MFMA takes the exact integers q - z of weight row `row`; the
+          // group scale of each output row multiplies the fp32 partial sum
+          const u32x4 wq = *(const u32x4*)(wring + s * L::WSLOT + nb * 1024 + lane * 16);
+          const int row = nb * 16 + r;
+          const uint32_t zbits = (*(const uint8_t*)(szb + 1024 + s * 16 + row / 2) >> ((row & 1) * 4)) & 15u;
+          const f16x2 zz = zero_pair(zbits);
+          f32x4 part = {0, 0, 0, 0};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) part = mfma16<DT_F16>(unpack8_minus_zero(wq[j], zz, magic), x[s][j], part);
+          // output rows of this lane: nb * 16 + 4 h + {0..3}
+          const u32x2 sc = *(const u32x2*)(szb + s * 64 + (nb * 16 + 4 * h) * 2);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[nb][i] = __builtin_fmaf(from_bits<DT_F16>((sc[i / 2] >> (16 * (i % 2))) & 0xffffu), part[i],
+                                        acc[nb][i]);
+        }
+      }
+    }
+  }
+  __syncthreads();  // every wave is done with its ring: reuse it for the reduction
+
+  f32x4* red = (f32x4*)lds;  // [KW][NB][64]
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) red[(wave * NB + nb) * 64 + lane] = acc[nb];
+  __syncthreads();
+  // lane quad q of block nb: rows n_base + 16 nb + 4 (q / 16) + {0..3}, token q % 16
+  for (int idx = threadIdx.x; idx < NB * 64; idx += 64 * KW) {
+    f32x4 t = red[idx];
+#pragma unroll
+    for (int w = 1; w < KW; ++w) t += red[w * NB * 64 + idx];
+    const int nb = idx / 64, q = idx % 64;
+    const int n = n_base + nb * 16 + 4 * (q / 16), tok = q % 16;
+    if (tok < a.M && n < a.N)
+      *(gu32x2*)(a.Y + (int64_t)tok * a.ldy + n) = u32x2{to_bits<DT_F16>(t[0]) | (to_bits<DT_F16>(t[1]) << 16),
+                                                        to_bits<DT_F16>(t[2]) | (to_bits<DT_F16>(t[3]) << 16)};
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Large-M kernel: the dense mainloop, X as the A operand, the prepacked
 // weight (dequantised on its way into LDS) as the column-major B operand.
 // ---------------------------------------------------------------------------
@@ -199,12 +334,15 @@ using W4Cfg256 = TileCfg<256, 256, 2, 2, 64, 2>;
 using W4Cfg128 = TileCfg<128, 128, 2, 2, 64, 2>;
 
 hipError_t launch_w4a16(const W4Launch& a, hipStream_t stream) {
+  if (a.M <= 16) {
+    constexpr int NB = 2, KW = 8, R = 8;
+    hipLaunchKernelGGL((k_w4a16_decode<NB, KW, R>), dim3((a.N + NB * 16 - 1) / (NB * 16)), dim3(64 * KW), 0, stream, a);
+    return hipGetLastError();
+  }
   if (a.M <= 64) {
     constexpr int NB = 2, KW = 8;
     const dim3 grid((a.N + NB * 16 - 1) / (NB * 16)), block(64 * KW);
-    if (a.M <= 16)
-      hipLaunchKernelGGL((k_w4a16_skinny<NB, KW, 1>), grid, block, 0, stream, a);
-    else if (a.M <= 32)
+    if (a.M <= 32)
       hipLaunchKernelGGL((k_w4a16_skinny<NB, KW, 2>), grid, block, 0, stream, a);
     else
       hipLaunchKernelGGL((k_w4a16_skinny<NB, KW, 4>), grid, block, 0, stream, a);
