@@ -159,9 +159,11 @@ def bench_workloads(torch, gmi, gi, dev, args):
         sets = [(base_pp.clone(), S.clone(), Z.clone(), X.clone(), torch.empty((M, 8192), dtype=torch.float16,
                                                                                 device=dev)) for _ in range(R)]
 
-        def fn(i, sets=sets):
+        wsp = torch.empty(gmi.w4a16_workspace_bytes(M, 8192, 8192), dtype=torch.uint8, device=dev)
+
+        def fn(i, sets=sets, wsp=wsp):
             pp, s, z, x, y = sets[i]
-            gmi.gemm_w4a16(x, pp, s, z, 128, 8192, Y=y)
+            gmi.gemm_w4a16(x, pp, s, z, 128, 8192, Y=y, workspace=wsp)
 
         ms = time_launches(torch, fn, R, 5, max(20, R * 2))
         bound = "hbm" if M <= 64 else "mfma"

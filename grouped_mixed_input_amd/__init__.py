@@ -65,7 +65,9 @@ def lib() -> ctypes.CDLL:
     L.gmi_prepack_w4.restype = ctypes.c_int
     L.gmi_prepack_w4.argtypes = [_p, _i32, _i32, _p, _p]
     L.gmi_gemm_w4a16.restype = ctypes.c_int
-    L.gmi_gemm_w4a16.argtypes = [_i32, _i32, _i32, _p, _i64, _p, _p, _p, _i32, _p, _i64, _p]
+    L.gmi_gemm_w4a16.argtypes = [_i32, _i32, _i32, _p, _i64, _p, _p, _p, _i32, _p, _i64, _p, _sz, _p]
+    L.gmi_w4a16_workspace_bytes.restype = _sz
+    L.gmi_w4a16_workspace_bytes.argtypes = [_i32, _i32, _i32]
     L.gmi_conv2d_fprop_implicit.restype = ctypes.c_int
     L.gmi_conv2d_fprop_implicit.argtypes = [_i32] * 13 + [_p, _p, _p, _p, ctypes.c_int, _f32, _f32, _p]
     _lib = L
@@ -151,14 +153,26 @@ def prepack_w4(w_u4: torch.Tensor, N: int, K: int, out: torch.Tensor | None = No
     return out
 
 
+def w4a16_workspace_bytes(M: int, N: int, K: int) -> int:
+    return lib().gmi_w4a16_workspace_bytes(M, N, K)
+
+
 def gemm_w4a16(X: torch.Tensor, w_prepacked: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
-               group_size: int, N: int, Y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Y = X W^T with X fp16 [M][K], scales fp16 [K/g][N], zeros uint8 [K/g][N/2]."""
+               group_size: int, N: int, Y: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+               stream=None) -> torch.Tensor:
+    """Y = X W^T with X fp16 [M][K], scales fp16 [K/g][N], zeros uint8 [K/g][N/2].  `workspace` (a device
+    byte tensor of at least w4a16_workspace_bytes(M, N, K)) enables the split-K path; pass an empty tensor
+    (numel 0) to run unsplit.  With None, one is allocated for this call."""
     M, K = X.shape
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float16, device=X.device)
+    if workspace is None:
+        need = w4a16_workspace_bytes(M, N, K)
+        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
     _check(lib().gmi_gemm_w4a16(M, N, K, X.data_ptr(), _ld(X), w_prepacked.data_ptr(), scales.data_ptr(),
-                                zeros.data_ptr(), group_size, Y.data_ptr(), _ld(Y), _stream(stream)))
+                                zeros.data_ptr(), group_size, Y.data_ptr(), _ld(Y),
+                                workspace.data_ptr() if workspace.numel() else None, workspace.numel(),
+                                _stream(stream)))
     return Y
 
 

@@ -227,9 +227,15 @@ gmi_status gmi_prepack_w4(const uint8_t* w_u4, int32_t N, int32_t K, uint8_t* w_
   return hip_status(launch_prepack_w4(w_u4, N, K, w_prepacked, (hipStream_t)stream), "prepack_w4: launch");
 }
 
+size_t gmi_w4a16_workspace_bytes(int32_t M, int32_t N, int32_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || N % 16 || K % 128) return 0;
+  const int split = w4a16_split(M, N, K);
+  return split > 1 ? (size_t)split * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
 gmi_status gmi_gemm_w4a16(int32_t M, int32_t N, int32_t K, const void* X, int64_t ldx, const uint8_t* w_prepacked,
                           const void* scales, const uint8_t* zeros, int32_t group_size, void* Y, int64_t ldy,
-                          void* stream) {
+                          void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   if (M < 0 || N < 0 || K < 0) return fail(GMI_ERR_INVALID_ARG, "gemm_w4a16: negative size (%d, %d, %d)", M, N, K);
   if (N % 16 || K % 128)
@@ -260,6 +266,14 @@ gmi_status gmi_gemm_w4a16(int32_t M, int32_t N, int32_t K, const void* X, int64_
   a.zeros = zeros;
   a.Y = (uint16_t*)Y;
   a.ldy = ldy;
+  a.split = 1;
+  a.partial = nullptr;
+  const size_t need = gmi_w4a16_workspace_bytes(M, N, K);
+  if (need > 0 && workspace && workspace_bytes >= need) {
+    if (!aligned16(workspace)) return fail(GMI_ERR_MISALIGNED, "gemm_w4a16: workspace must be 16-byte aligned");
+    a.split = w4a16_split(M, N, K);
+    a.partial = (float*)workspace;
+  }
   return hip_status(launch_w4a16(a, (hipStream_t)stream), "gemm_w4a16: launch");
 }
 

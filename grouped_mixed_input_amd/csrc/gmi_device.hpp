@@ -497,9 +497,10 @@ struct W4Loader {
     uint32_t s[P], z[P];
   };
   rsrc_t rw, rsc, rz;
-  uint32_t kblocks, N, group, block0;
+  uint32_t kblocks, N, group, block0, kt0;
 
-  __device__ __forceinline__ void init(const W4Geom& g, int n0) {
+  // rows n0 .., k-tiles from kt_first on (kt_first even: whole 128-k blocks)
+  __device__ __forceinline__ void init(const W4Geom& g, int n0, int kt_first = 0) {
     rw = make_rsrc(g.w, (uint32_t)((int64_t)g.N * g.K / 2));
     rsc = make_rsrc(g.scales, (uint32_t)((int64_t)g.N * (g.K / g.group) * 2));
     rz = make_rsrc(g.zeros, (uint32_t)((int64_t)g.N / 2 * (g.K / g.group)));
@@ -507,10 +508,12 @@ struct W4Loader {
     N = g.N;
     group = g.group;
     block0 = n0 / 16;
+    kt0 = kt_first;
   }
 
-  __device__ __forceinline__ void load(int kt, Regs& rg) const {
-    const uint32_t grp = (uint32_t)(kt * Cfg::BK) / group;
+  __device__ __forceinline__ void load(int kt_local, Regs& rg) const {
+    const uint32_t kt = kt_local + kt0;
+    const uint32_t grp = (kt * Cfg::BK) / group;
 #pragma unroll
     for (int i = 0; i < P; ++i) {
       const int e = threadIdx.x + i * Cfg::THREADS;

@@ -302,18 +302,51 @@ __global__ __launch_bounds__(64 * KW) void k_w4a16_decode(W4Launch a) {
 // Large-M kernel: the dense mainloop, X as the A operand, the prepacked
 // weight (dequantised on its way into LDS) as the column-major B operand.
 // ---------------------------------------------------------------------------
+// fp32 partial tile: each lane's accumulator runs (4 consecutive n of one
+// row m) stored as they are, rows past M dropped by the buffer range,
+// columns past N skipped
 template <class Cfg>
-__global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_w4a16_tiled(W4Launch a, int tiles_m, int total_tiles) {
+__device__ __forceinline__ void store_partial(const Tile& t, const f32x16 (&acc)[Cfg::TM][Cfg::TN], float* P) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = (wave / Cfg::WAVES_N) * Cfg::WTM, wn = (wave % Cfg::WAVES_N) * Cfg::WTN;
+  int rows = t.M - t.m0;
+  if (rows > Cfg::BM) rows = Cfg::BM;
+  const rsrc_t rp = make_rsrc(P + (int64_t)t.m0 * t.N, (uint32_t)rows * (uint32_t)t.N * 4u);
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t row = wm + 32 * i + (lane & 31);
+        const int col = t.n0 + wn + 32 * j + 8 * q + 4 * (lane >> 5);
+        if (col < t.N)
+          buf_store16(rp, (row * (uint32_t)t.N + col) * 4u,
+                      __builtin_bit_cast(u32x4, f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                                      acc[i][j][4 * q + 3]}));
+      }
+}
+
+// Work item w = tile * split + s: output tile `tile`, k-range s of `split`
+// equal ranges (whole 128-k blocks).  Unsplit, the epilogue rounds to fp16
+// into Y; split, the fp32 partial goes to partial[s] and k_w4a16_sum adds
+// the ranges afterwards.  The ranges of a tile are consecutive work items,
+// so they run in one XCD round and share the tile's X panel in its L2.
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_w4a16_tiled(W4Launch a, int tiles_m, int total_work) {
   __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
   const int G = gridDim.x;
   const W4Geom g{a.w, a.scales, a.zeros, a.N, a.K, a.group};
-  for (int base = 0; base < total_tiles; base += G) {
-    const int tile = base + remap_slot(blockIdx.x, G);
-    if (tile >= total_tiles) break;
+  const int Ks = a.K / a.split;
+  for (int base = 0; base < total_work; base += G) {
+    const int work = base + remap_slot(blockIdx.x, G);
+    if (work >= total_work) break;
+    const int tile = work / a.split, sidx = work - tile * a.split;
+    const int k0 = sidx * Ks;
     Tile t;
     t.M = a.M;
     t.N = a.N;
-    t.K = a.K;
+    t.K = Ks;
     t.m0 = (tile % tiles_m) * Cfg::BM;
     t.n0 = (tile / tiles_m) * Cfg::BN;
     t.C = nullptr;
@@ -322,16 +355,55 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_w4a16_tiled(W
     t.ldd = a.ldy;
     DenseLoader<Cfg, Cfg::BM> al;
     W4Loader<Cfg, Cfg::BN> bl;
-    al.init(a.X, a.ldx, t.m0, t.M, t.K);
-    bl.init(g, t.n0);
+    al.init(a.X + k0, a.ldx, t.m0, t.M, Ks);
+    bl.init(g, t.n0, k0 / Cfg::BK);
     f32x16 acc[Cfg::TM][Cfg::TN];
-    mainloop<Cfg, DT_F16>(lds, al, bl, t.K / Cfg::BK, acc);
-    store_tile<Cfg, DT_F16>(t, acc, 1.0f, 0.0f, lds);
+    mainloop<Cfg, DT_F16>(lds, al, bl, Ks / Cfg::BK, acc);
+    if (a.split == 1)
+      store_tile<Cfg, DT_F16>(t, acc, 1.0f, 0.0f, lds);
+    else
+      store_partial<Cfg>(t, acc, a.partial + (int64_t)sidx * a.M * a.N);
+  }
+}
+
+// Y = RN16(sum over s of partial[s]) in s order: 8 consecutive n per thread
+__global__ __launch_bounds__(256) void k_w4a16_sum(const float* __restrict__ P, int split, int M, int N,
+                                                   uint16_t* __restrict__ Y, int64_t ldy) {
+  const int64_t groups = (int64_t)M * N / 8;
+  const int64_t plane = (int64_t)M * N;
+  for (int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; id < groups;
+       id += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = id * 8;
+    const int m = (int)(e / N), n = (int)(e - (int64_t)m * N);
+    f32x4 lo = *(const f32x4*)(P + e), hi = *(const f32x4*)(P + e + 4);
+    for (int s = 1; s < split; ++s) {
+      lo += *(const f32x4*)(P + s * plane + e);
+      hi += *(const f32x4*)(P + s * plane + e + 4);
+    }
+    *(u32x4*)(Y + (int64_t)m * ldy + n) =
+        u32x4{to_bits<DT_F16>(lo[0]) | (to_bits<DT_F16>(lo[1]) << 16), to_bits<DT_F16>(lo[2]) | (to_bits<DT_F16>(lo[3]) << 16),
+              to_bits<DT_F16>(hi[0]) | (to_bits<DT_F16>(hi[1]) << 16), to_bits<DT_F16>(hi[2]) | (to_bits<DT_F16>(hi[3]) << 16)};
   }
 }
 
 using W4Cfg256 = TileCfg<256, 256, 2, 2, 64, 2>;
 using W4Cfg128 = TileCfg<128, 128, 2, 2, 64, 2>;
+
+// Tile shape of the tiled path: 256 x 256 when those tiles alone fill the
+// device, else 128 x 128 (two workgroups per CU).
+static bool w4_big_tiles(int M, int N, int cus) { return ((M + 255) / 256) * ((N + 255) / 256) >= cus; }
+
+int w4a16_split(int M, int N, int K) {
+  if (M <= 64) return 1;  // decode / skinny kernels
+  const int cus = device_cu_count();
+  if (w4_big_tiles(M, N, cus)) return 1;
+  const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  int split = 1;
+  // up to four k-ranges of whole 128-k blocks, at least 8 k-tiles each, until
+  // the work items cover every CU once
+  while (split < 4 && tiles * split < cus && K % (128 * split * 2) == 0 && K / (split * 2) >= 512) split *= 2;
+  return split;
+}
 
 hipError_t launch_w4a16(const W4Launch& a, hipStream_t stream) {
   if (a.M <= 16) {
@@ -349,11 +421,10 @@ hipError_t launch_w4a16(const W4Launch& a, hipStream_t stream) {
     return hipGetLastError();
   }
   const int cus = device_cu_count();
-  const int t256 = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-  const bool big = t256 >= cus;
+  const bool big = w4_big_tiles(a.M, a.N, cus);
   const int bm = big ? 256 : 128, bn = big ? 256 : 128;
   const int tiles_m = (a.M + bm - 1) / bm;
-  const int total = tiles_m * ((a.N + bn - 1) / bn);
+  const int total = tiles_m * ((a.N + bn - 1) / bn) * a.split;
   const int resident = cus * (big ? 1 : 2);
   int grid = (total + XCDS - 1) / XCDS * XCDS;
   if (grid > resident) grid = resident / XCDS * XCDS;
@@ -361,6 +432,15 @@ hipError_t launch_w4a16(const W4Launch& a, hipStream_t stream) {
     hipLaunchKernelGGL((k_w4a16_tiled<W4Cfg256>), dim3(grid), dim3(W4Cfg256::THREADS), 0, stream, a, tiles_m, total);
   else
     hipLaunchKernelGGL((k_w4a16_tiled<W4Cfg128>), dim3(grid), dim3(W4Cfg128::THREADS), 0, stream, a, tiles_m, total);
+  if (a.split > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t groups = (int64_t)a.M * a.N / 8;
+    int64_t blocks = (groups + 255) / 256;
+    if (blocks > 4 * cus) blocks = 4 * cus;
+    hipLaunchKernelGGL(k_w4a16_sum, dim3((unsigned)blocks), dim3(256), 0, stream, a.partial, a.split, a.M, a.N, a.Y,
+                       a.ldy);
+  }
   return hipGetLastError();
 }
 

@@ -120,14 +120,28 @@ size_t gmi_prepack_w4_bytes(int32_t N, int32_t K);
  * A bijection on the N*K/2 bytes; `w_u4` and `w_prepacked` must not overlap. */
 gmi_status gmi_prepack_w4(const uint8_t* w_u4, int32_t N, int32_t K, uint8_t* w_prepacked, void* stream);
 
+/* Bytes of the optional workspace that lets gmi_gemm_w4a16 split K across
+ * workgroups for this shape on the current device (fp32 partial products of
+ * the k-ranges, summed by a second launch); 0 when no split is used. */
+size_t gmi_w4a16_workspace_bytes(int32_t M, int32_t N, int32_t K);
+
 /* Mixed-input GEMM Y = X W^T, 4-bit weights with per-group scales and zero
  * points: w[n][k] = (q[n][k] - z[k/g][n]) * s[k/g][n], the conversion mode
  * "convert, scale, add zero" of machete_mainloop.cuh (ConversionMode
  * ConvertAndScaleWithZero; scale_k = ceil(K / group_size) from
  * to_underlying_arguments; transform_A_kblock).  The zero point is read here
- * as an unsigned 4-bit offset subtracted before scaling.  Each weight is
- * dequantised to fp16 as RN16((q - z) * s), then multiplied with X in fp16
- * with fp32 accumulation; Y is rounded to fp16.
+ * as an unsigned 4-bit offset subtracted before scaling.  For M <= 16 the
+ * matrix instruction takes the exact integers q - z (fp16) and each group's
+ * scale multiplies the fp32 partial sum over that group; otherwise each
+ * weight is dequantised to fp16 as RN16((q - z) * s) and multiplied in fp16.
+ * Accumulation is fp32 either way; Y is rounded to fp16.
+ *   workspace    optional device memory of at least
+ *                gmi_w4a16_workspace_bytes(M, N, K) bytes, 16-byte aligned,
+ *                no initialisation needed: with it, shapes whose output tiles
+ *                cannot fill the device split K (partials then a summing
+ *                launch, both on `stream`); NULL or smaller runs unsplit.
+ *                Contents are scratch; calls sharing one workspace must be
+ *                ordered (same stream).
  *   X            fp16 [M][ldx], ldx >= K.
  *   w_prepacked  gmi_prepack_w4 output for the [N][K] weight.
  *   scales       fp16 [K/group_size][N] (n contiguous).
@@ -139,7 +153,7 @@ gmi_status gmi_prepack_w4(const uint8_t* w_u4, int32_t N, int32_t K, uint8_t* w_
  * Requires N % 16 == 0, K % 128 == 0, scales and zeros 16-byte aligned. */
 gmi_status gmi_gemm_w4a16(int32_t M, int32_t N, int32_t K, const void* X, int64_t ldx, const uint8_t* w_prepacked,
                           const void* scales, const uint8_t* zeros, int32_t group_size, void* Y, int64_t ldy,
-                          void* stream);
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Implicit-GEMM conv2d forward (cross-correlation, groups == 1):
  *   y[n][p][q][k] = alpha * sum_{r,s,c} x[n][p*sh - ph + r*dh][q*sw - pw + s*dw][c] * w[k][r][s][c]

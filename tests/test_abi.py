@@ -117,8 +117,9 @@ def test_prepack_validation(gmi):
     assert L.gmi_prepack_w4(None, 0, 128, None, None) == gmi.GMI_OK
 
 
-def _w4(gmi, M=16, N=64, K=256, X=A16, ldx=256, W=A16 * 2, S=A16 * 3, Z=A16 * 4, g=128, Y=A16 * 5, ldy=64):
-    return gmi.lib().gmi_gemm_w4a16(M, N, K, X, ldx, W, S, Z, g, Y, ldy, None)
+def _w4(gmi, M=16, N=64, K=256, X=A16, ldx=256, W=A16 * 2, S=A16 * 3, Z=A16 * 4, g=128, Y=A16 * 5, ldy=64, ws=None,
+        ws_bytes=0):
+    return gmi.lib().gmi_gemm_w4a16(M, N, K, X, ldx, W, S, Z, g, Y, ldy, ws, ws_bytes, None)
 
 
 def test_w4a16_validation(gmi):
@@ -135,6 +136,21 @@ def test_w4a16_validation(gmi):
     assert _w4(gmi, ldy=68) == gmi.GMI_ERR_MISALIGNED
     assert _w4(gmi, S=A16 + 2) == gmi.GMI_ERR_MISALIGNED
     assert _w4(gmi, M=0, X=None, W=None, S=None, Z=None, Y=None) == gmi.GMI_OK
+    # a workspace that would enable the split must be 16-byte aligned
+    need = gmi.lib().gmi_w4a16_workspace_bytes(128, 8192, 8192)
+    assert _w4(gmi, M=128, N=8192, K=8192, ldx=8192, ldy=8192, ws=A16 + 4, ws_bytes=need) == gmi.GMI_ERR_MISALIGNED
+
+
+def test_w4a16_workspace_bytes(gmi):
+    # without a device the library assumes 256 CUs, as on MI355X: 128 x 8192 has 64 output tiles of
+    # 128 x 128, so four k-ranges of fp32 partials; decode shapes and shapes that fill the device use none
+    L = gmi.lib()
+    assert L.gmi_w4a16_workspace_bytes(128, 8192, 8192) == 4 * 128 * 8192 * 4
+    assert L.gmi_w4a16_workspace_bytes(16, 8192, 8192) == 0
+    assert L.gmi_w4a16_workspace_bytes(4096, 8192, 8192) == 0
+    assert L.gmi_w4a16_workspace_bytes(128, 8192, 1024) == 2 * 128 * 8192 * 4  # k-ranges keep >= 512 k each
+    assert L.gmi_w4a16_workspace_bytes(-1, 16, 128) == 0
+    assert L.gmi_w4a16_workspace_bytes(128, 24, 128) == 0
 
 
 def _conv(gmi, N=2, H=8, W=8, C=16, K=16, R=3, S=3, ph=1, pw=1, sh=1, sw=1, dh=1, dw=1, x=A16, w=A16 * 2,

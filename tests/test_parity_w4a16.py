@@ -90,3 +90,21 @@ def test_w4a16_prepack_layout_matters(gmi):
     ref = oracle.w4a16(d["X"], d["W"], d["scales"], d["zeros"], 64, 256, 128)
     got = oracle.decode(host_bits(Y), "f16")
     assert not np.all(np.abs(got - ref) <= 1e-2 * np.abs(ref) + 1e-2)
+
+
+def test_w4a16_split_and_unsplit_agree(gmi):
+    # M = 160, N = 256, K = 2048: four output tiles, so with a workspace K is split into four k-ranges whose
+    # fp32 partials a second launch sums; without one the same tiles run unsplit.  Both meet the oracle.
+    M, N, K = 160, 256, 2048
+    assert gmi.w4a16_workspace_bytes(M, N, K) == 4 * M * N * 4
+    d = gi.w4a16(seed=11, M=M, N=N, K=K, group=128)
+    ref = oracle.w4a16(d["X"], d["W"], d["scales"], d["zeros"], N, K, 128)
+    wpp = gmi.prepack_w4(bytes_to_dev(d["W"]), N, K)
+    args = (to_dev(d["X"], "f16"), wpp, to_dev(d["scales"], "f16"), bytes_to_dev(d["zeros"]), 128, N)
+    for ws in (torch.zeros(gmi.w4a16_workspace_bytes(M, N, K), dtype=torch.uint8, device=dev()),
+               torch.empty(0, dtype=torch.uint8, device=dev())):
+        out = Guarded(M, N, N + 8, "f16")
+        gmi.gemm_w4a16(*args, Y=out.view, workspace=ws)
+        torch.cuda.synchronize()
+        out.check_guards(f"w4a16 split workspace {ws.numel()} bytes")
+        check_close(out.bits(), ref, "f16", f"w4a16 workspace {ws.numel()} bytes")
