@@ -8,6 +8,7 @@
 // (machete_mainloop.cuh), and the convolution rules -- channel-innermost
 // tensors, traversal stride 1..8, cross-correlation, groups == 1
 // (sm100_implicit_gemm_umma_warpspecialized.hpp).
+#include <algorithm>
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
@@ -131,14 +132,27 @@ gmi_status gmi_gemm_grouped(const gmi_problem* problems, int32_t count, gmi_dtyp
       if (problems[g].M > 0 && problems[g].N > 0) t += cdiv(problems[g].M, bm) * cdiv(problems[g].N, bn);
     return t;
   });
-  const int bm = tile_bm(shape), bn = tile_bn(shape);
+  const int bn = tile_bn(shape);
+  // Problems are laid out in decreasing order of work per tile (rows of the
+  // tile actually used x K; ties keep the caller's order), so the persistent
+  // walk hands out the long tiles first and the short ones fill the tail.
+  // The order changes nothing in the results: every problem has its own D.
+  std::vector<int32_t> order;
+  order.reserve(live);
+  for (int32_t g = 0; g < count; ++g)
+    if (problems[g].M > 0 && problems[g].N > 0) order.push_back(g);
+  auto tile_work = [&](int32_t g) {
+    const gmi_problem& p = problems[g];
+    const int rows = grouped_tile_rows(shape, p.M);
+    return (int64_t)std::min<int64_t>(p.M, rows) * (int64_t)std::max(p.K, 1);
+  };
+  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return tile_work(x) > tile_work(y); });
   std::vector<GroupDesc> desc;
   desc.reserve(live);
   int64_t tiles = 0;
   bool ktail = false;
-  for (int32_t g = 0; g < count; ++g) {
+  for (const int32_t g : order) {
     const gmi_problem& p = problems[g];
-    if (p.M == 0 || p.N == 0) continue;
     ktail = ktail || (p.K % 8) != 0;
     GroupDesc d;
     d.A = (const uint16_t*)p.A;
@@ -153,7 +167,7 @@ gmi_status gmi_gemm_grouped(const gmi_problem* problems, int32_t count, gmi_dtyp
     d.N = p.N;
     d.K = p.K;
     d.tile_start = (int32_t)tiles;
-    tiles += cdiv(p.M, bm) * cdiv(p.N, bn);
+    tiles += cdiv(p.M, grouped_tile_rows(shape, p.M)) * cdiv(p.N, bn);
     if (tiles > INT32_MAX) return fail(GMI_ERR_INVALID_ARG, "gemm_grouped: more than 2^31 - 1 output tiles");
     desc.push_back(d);
   }

@@ -862,7 +862,11 @@ __device__ __forceinline__ void store_tile(const Tile& t, const f32x16 (&acc)[Cf
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = (wave / Cfg::WAVES_N) * Cfg::WTM, wn = (wave % Cfg::WAVES_N) * Cfg::WTN;
   char* reg = lds + wave * REGION;
-  auto slot = [](int r, int x) { return (x ^ (r & 15) ^ ((x >> 4) & 1)) << 4; };
+  // 16-byte slot of chunk x in row r: XOR with up to 4 row bits (as many as
+  // the row has chunks), plus bit 4 for rows of 32 or more chunks
+  constexpr int CH = Cfg::WTN / 4;
+  constexpr int XM = CH >= 16 ? 15 : CH - 1;
+  auto slot = [](int r, int x) { return (x ^ (r & XM) ^ (CH >= 32 ? (x >> 4) & 1 : 0)) << 4; };
 
   int rows = t.M - t.m0;
   if (rows > Cfg::BM) rows = Cfg::BM;

@@ -25,6 +25,14 @@ enum TileShape { TILE_256x256 = 0, TILE_128x128 = 1, TILE_256x128 = 2 };
 inline int tile_bm(int s) { return s == TILE_128x128 ? 128 : 256; }
 inline int tile_bn(int s) { return s == TILE_256x256 ? 256 : 128; }
 inline int tile_wgs_per_cu(int s) { return s == TILE_256x256 ? 1 : 2; }  // matches TileCfg::WGS_PER_CU
+// Grouped GEMM with 256x256 tiles: a problem of at most SMALL_M rows takes
+// SMALL_M x 256 tiles instead (same kernel, its own tile configuration), so
+// short groups -- the rare experts of a mixture-of-experts layer -- do not pay
+// for 256 rows of matrix work.  Host tile counting and the kernel use this rule.
+constexpr int SMALL_M = 64;
+inline int grouped_tile_rows(int shape, int M) {
+  return (shape == TILE_256x256 && M <= SMALL_M) ? SMALL_M : tile_bm(shape);
+}
 
 struct PtrArrayLaunch {
   const uint16_t* const* A;

@@ -6,6 +6,8 @@
 // problem shape of its group / batch before running the k-loop and the
 // epilogue).  Grouped problems carry their own shape and strides; the array
 // mode shares one shape and one stride per operand over L batches.
+#include <type_traits>
+
 #include "gmi_device.hpp"
 #include "gmi_internal.hpp"
 
@@ -22,6 +24,14 @@ __device__ __forceinline__ void run_tile(char* lds, const Tile& t, float alpha, 
   store_tile<Cfg, DT>(t, acc, alpha, beta, lds);
 }
 
+template <class Cfg>
+constexpr int lds_of() {
+  if constexpr (std::is_void<Cfg>::value)
+    return 0;
+  else
+    return Cfg::LDS_BYTES;
+}
+
 struct GroupedArgs {
   const GroupDesc* desc;
   int count, total_tiles;
@@ -32,9 +42,39 @@ struct GroupedArgs {
 // of m-tiles (raster), so one XCD's share of a round -- consecutive tiles --
 // reuses a few A and B panels, e.g. one expert weight in a mixture-of-experts
 // layer.
+// Tile configuration a grouped 256x256 launch uses for problems of at most
+// SMALL_M rows: SMALL_M x 256 over the same 8 waves (one wave row, eight wave
+// columns), a four-stage ring of 40 KB.
+template <class Cfg>
+struct SmallOf {
+  using type = void;
+};
+template <int DT, bool KTAIL, class Cfg>
+__device__ __forceinline__ void grouped_tile(char* lds, const GroupDesc& d, int local, float alpha, float beta) {
+  int mi, ni;
+  raster(local, (d.M + Cfg::BM - 1) / Cfg::BM, (d.N + Cfg::BN - 1) / Cfg::BN, mi, ni);
+  Tile t;
+  t.M = d.M;
+  t.N = d.N;
+  t.K = d.K;
+  t.m0 = mi * Cfg::BM;
+  t.n0 = ni * Cfg::BN;
+  t.A = d.A;
+  t.lda = d.lda;
+  t.B = d.B;
+  t.ldb = d.ldb;
+  t.C = d.C;
+  t.ldc = d.ldc;
+  t.D = d.D;
+  t.ldd = d.ldd;
+  run_tile<Cfg, DT, KTAIL>(lds, t, alpha, beta);
+}
+
 template <class Cfg, int DT, bool KTAIL>
 __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_gemm_grouped(GroupedArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
+  using Small = typename SmallOf<Cfg>::type;
+  constexpr int LDS = Cfg::LDS_BYTES > lds_of<Small>() ? Cfg::LDS_BYTES : lds_of<Small>();
+  __shared__ __attribute__((aligned(16))) char lds[LDS];
   const int G = gridDim.x;
   int g = 0;
   for (int base = 0; base < a.total_tiles; base += G) {
@@ -43,23 +83,13 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_gemm_grouped(
     while (g + 1 < a.count && a.desc[g + 1].tile_start <= tile) ++g;
     const GroupDesc& d = a.desc[g];
     const int local = tile - d.tile_start;
-    int mi, ni;
-    raster(local, (d.M + Cfg::BM - 1) / Cfg::BM, (d.N + Cfg::BN - 1) / Cfg::BN, mi, ni);
-    Tile t;
-    t.M = d.M;
-    t.N = d.N;
-    t.K = d.K;
-    t.m0 = mi * Cfg::BM;
-    t.n0 = ni * Cfg::BN;
-    t.A = d.A;
-    t.lda = d.lda;
-    t.B = d.B;
-    t.ldb = d.ldb;
-    t.C = d.C;
-    t.ldc = d.ldc;
-    t.D = d.D;
-    t.ldd = d.ldd;
-    run_tile<Cfg, DT, KTAIL>(lds, t, a.alpha, a.beta);
+    if constexpr (!std::is_void<Small>::value) {
+      if (d.M <= SMALL_M) {
+        grouped_tile<DT, KTAIL, Small>(lds, d, local, a.alpha, a.beta);
+        continue;
+      }
+    }
+    grouped_tile<DT, KTAIL, Cfg>(lds, d, local, a.alpha, a.beta);
   }
 }
 
@@ -102,6 +132,12 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_gemm_ptr_arra
 using Cfg256 = TileCfg<256, 256, 4, 2, 64, 2, 5>;
 using Cfg256x128 = TileCfg<256, 128, 2, 2, 32, 3>;
 using Cfg128 = TileCfg<128, 128, 2, 2, 32, 4>;
+using CfgSmall256 = TileCfg<SMALL_M, 256, 1, 8, 64, 4>;
+template <>
+struct SmallOf<Cfg256> {
+  using type = CfgSmall256;
+};
+static_assert(CfgSmall256::THREADS == Cfg256::THREADS, "both tile shapes run on the same workgroup");
 
 // Persistent grid: a whole number of XCD rounds, no more workgroups than can
 // be resident at once and no more than the tiles need.
