@@ -48,11 +48,35 @@ def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     return (rounded >> np.uint32(16)).astype(np.uint16)
 
 
+def f32_to_e4m3_bits(a: np.ndarray) -> np.ndarray:
+    """float32 -> OCP fp8 E4M3 codes (uint8), round to nearest even, saturating
+    at +-448 (the format has no infinities); NaN -> 0x7F.  Written from the
+    format: 3 mantissa bits, exponent bias 7, subnormal quantum 2^-9."""
+    x = np.asarray(a, dtype=np.float32).astype(np.float64)
+    sign = np.signbit(x).astype(np.uint8) << np.uint8(7)
+    mag = np.minimum(np.abs(x), 448.0)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(mag > 0, mag, 1.0)))
+    e = np.maximum(e, -6.0)  # below 2^-6 the quantum stays 2^-9 (subnormals)
+    q = np.ldexp(1.0, (e - 3).astype(np.int64))
+    r = np.minimum(np.round(mag / q) * q, 448.0)  # np.round: ties to even
+    normal = r >= 2.0 ** -6
+    with np.errstate(divide="ignore"):
+        er = np.floor(np.log2(np.where(normal, r, 1.0)))
+    mant_n = np.where(normal, r / np.ldexp(1.0, er.astype(np.int64)) * 8 - 8, 0).astype(np.uint8)
+    code_n = ((er + 7).astype(np.int64).clip(0, 15).astype(np.uint8) << np.uint8(3)) | mant_n
+    code_s = np.where(normal, 0, r / 2.0 ** -9).astype(np.uint8)
+    code = np.where(normal, code_n, code_s).astype(np.uint8) | sign
+    return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
+
+
 def to_bits(a: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "f16":
         return f32_to_f16_bits(a)
     if dtype == "bf16":
         return f32_to_bf16_bits(a)
+    if dtype == "f8e4m3":
+        return f32_to_e4m3_bits(a)
     raise ValueError(dtype)
 
 
@@ -168,3 +192,24 @@ def conv_fprop_bf16(seed: int = DEFAULT_SEED, N: int = 32, H: int = 56, W: int =
     x = to_bits(normal(rng(seed, 5, 0), (N, H, W, C), 1.0), "bf16")
     w = to_bits(normal(rng(seed, 5, 1), (K, R, S, C), 1.0 / np.sqrt(R * S * C)), "bf16")
     return x, w
+
+
+# ----------------------------------------------------------------------------
+# workload 6: fp8 E4M3 GEMMs (bf16 results) -- the headline pointer-array shape
+# and the MoE layer with fp8 operands.  Values are drawn N(0, 1), the range an
+# fp8 tensor holds after its per-tensor scaling; the stored codes are the
+# inputs.
+# ----------------------------------------------------------------------------
+def ptr_array_f8(seed: int = DEFAULT_SEED, L: int = 16, M: int = 1024, N: int = 1024, K: int = 1024):
+    """Returns (A_list, B_list) of uint8 E4M3 codes: A_l [M][K], B_l column-major as [N][K]."""
+    A = [to_bits(normal(rng(seed, 6, 100 + l), (M, K), 1.0), "f8e4m3") for l in range(L)]
+    B = [to_bits(normal(rng(seed, 6, 200 + l), (N, K), 1.0), "f8e4m3") for l in range(L)]
+    return A, B
+
+
+def moe_activations_f8(seed: int = DEFAULT_SEED, tokens: int = 16384, K: int = 4096) -> np.ndarray:
+    return to_bits(normal(rng(seed, 6, 0), (tokens, K), 1.0), "f8e4m3")
+
+
+def moe_expert_weight_f8(group: int, seed: int = DEFAULT_SEED, N: int = 2048, K: int = 4096) -> np.ndarray:
+    return to_bits(normal(rng(seed, 6, 1000 + group), (N, K), 1.0), "f8e4m3")

@@ -20,8 +20,8 @@ LIB_PATH = _PKG / "libgmi.so"
 GMI_OK, GMI_ERR_INVALID_ARG, GMI_ERR_UNSUPPORTED, GMI_ERR_MISALIGNED, GMI_ERR_WORKSPACE, GMI_ERR_HIP = range(6)
 STATUS_NAMES = ["GMI_OK", "GMI_ERR_INVALID_ARG", "GMI_ERR_UNSUPPORTED", "GMI_ERR_MISALIGNED", "GMI_ERR_WORKSPACE",
                 "GMI_ERR_HIP"]
-GMI_F16, GMI_BF16 = 0, 1
-_DT = {torch.float16: GMI_F16, torch.bfloat16: GMI_BF16}
+GMI_F16, GMI_BF16, GMI_F8E4M3 = 0, 1, 2
+_DT = {torch.float16: GMI_F16, torch.bfloat16: GMI_BF16, torch.float8_e4m3fn: GMI_F8E4M3}
 
 
 class GmiError(RuntimeError):
@@ -113,8 +113,9 @@ def make_problems(As, Bs, Cs, Ds) -> "ctypes.Array":
 
 
 def gemm_grouped(As, Bs, Cs, Ds, alpha=1.0, beta=0.0, workspace=None, stream=None):
-    """D_g = alpha A_g B_g + beta C_g for every g, in one launch."""
-    dt = _DT[Ds[0].dtype]
+    """D_g = alpha A_g B_g + beta C_g for every g, in one launch.  The element type is that of A
+    (float8_e4m3fn A and B give bfloat16 C and D)."""
+    dt = _DT[As[0].dtype]
     probs = make_problems(As, Bs, Cs if Cs is not None else [None] * len(As), Ds)
     need = workspace_bytes(len(As))
     if workspace is None:

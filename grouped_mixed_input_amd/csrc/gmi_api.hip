@@ -58,6 +58,12 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // 256-row tile of any operand must span less than 2^32 bytes.
 constexpr int64_t kMaxLd = int64_t(1) << 22;
 static bool dtype_ok(gmi_dtype d) { return d == GMI_F16 || d == GMI_BF16; }
+static bool gemm_dtype_ok(gmi_dtype d) { return dtype_ok(d) || d == GMI_F8E4M3; }
+// fp8 A and B: 16 elements per 16-byte chunk, so K and their leading
+// dimensions must be multiples of 16 (chunks never straddle K)
+static bool f8_shape_ok(gmi_dtype d, int64_t K, int64_t lda, int64_t ldb) {
+  return d != GMI_F8E4M3 || K == 0 || (K % 16 == 0 && lda % 16 == 0 && ldb % 16 == 0);
+}
 
 // Tile shape for a list of problems: 256x256 when it alone fills every CU,
 // then 256x128, else 128x128 (two resident workgroups per CU).
@@ -100,7 +106,7 @@ gmi_status gmi_gemm_grouped(const gmi_problem* problems, int32_t count, gmi_dtyp
   g_last_error.clear();
   if (count < 0) return fail(GMI_ERR_INVALID_ARG, "gemm_grouped: count %d < 0", count);
   if (count > 0 && !problems) return fail(GMI_ERR_INVALID_ARG, "gemm_grouped: problems is NULL");
-  if (!dtype_ok(dtype)) return fail(GMI_ERR_UNSUPPORTED, "gemm_grouped: dtype %d not supported", (int)dtype);
+  if (!gemm_dtype_ok(dtype)) return fail(GMI_ERR_UNSUPPORTED, "gemm_grouped: dtype %d not supported", (int)dtype);
   const bool use_c = beta != 0.0f;
   int live = 0;
   for (int32_t g = 0; g < count; ++g) {
@@ -115,6 +121,8 @@ gmi_status gmi_gemm_grouped(const gmi_problem* problems, int32_t count, gmi_dtyp
       return fail(GMI_ERR_INVALID_ARG, "gemm_grouped: problem %d has a leading dimension below its row width", g);
     if (p.lda > kMaxLd || p.ldb > kMaxLd || p.ldd > kMaxLd || (use_c && p.ldc > kMaxLd))
       return fail(GMI_ERR_UNSUPPORTED, "gemm_grouped: problem %d: a leading dimension above 2^22 elements", g);
+    if (!f8_shape_ok(dtype, p.K, p.lda, p.ldb))
+      return fail(GMI_ERR_UNSUPPORTED, "gemm_grouped: problem %d: fp8 needs K, lda and ldb multiples of 16", g);
     if ((p.K > 0 && (!aligned16(p.A) || !aligned16(p.B) || p.lda % 8 || p.ldb % 8)) || !aligned16(p.D) ||
         p.ldd % 8 || (use_c && (!aligned16(p.C) || p.ldc % 8)))
       return fail(GMI_ERR_MISALIGNED, "gemm_grouped: problem %d: pointers must be 16-byte aligned, ld multiples of 8",
@@ -189,7 +197,7 @@ gmi_status gmi_gemm_ptr_array(int32_t L, int32_t M, int32_t N, int32_t K, const 
   g_last_error.clear();
   if (L < 0 || M < 0 || N < 0 || K < 0)
     return fail(GMI_ERR_INVALID_ARG, "gemm_ptr_array: negative size (L %d, M %d, N %d, K %d)", L, M, N, K);
-  if (!dtype_ok(dtype)) return fail(GMI_ERR_UNSUPPORTED, "gemm_ptr_array: dtype %d not supported", (int)dtype);
+  if (!gemm_dtype_ok(dtype)) return fail(GMI_ERR_UNSUPPORTED, "gemm_ptr_array: dtype %d not supported", (int)dtype);
   if (L == 0 || M == 0 || N == 0) return GMI_OK;
   const bool use_c = beta != 0.0f;
   if (!D || (K > 0 && (!A || !B)) || (use_c && !C))
@@ -200,6 +208,8 @@ gmi_status gmi_gemm_ptr_array(int32_t L, int32_t M, int32_t N, int32_t K, const 
     return fail(GMI_ERR_MISALIGNED, "gemm_ptr_array: leading dimensions must be multiples of 8");
   if (lda > kMaxLd || ldb > kMaxLd || ldd > kMaxLd || (use_c && ldc > kMaxLd))
     return fail(GMI_ERR_UNSUPPORTED, "gemm_ptr_array: a leading dimension above 2^22 elements");
+  if (!f8_shape_ok(dtype, K, lda, ldb))
+    return fail(GMI_ERR_UNSUPPORTED, "gemm_ptr_array: fp8 needs K, lda and ldb multiples of 16");
   if (((uintptr_t)A | (uintptr_t)B | (uintptr_t)D | (uintptr_t)(use_c ? C : nullptr)) & 7u)
     return fail(GMI_ERR_MISALIGNED, "gemm_ptr_array: pointer arrays must be 8-byte aligned");
   const int shape = choose_shape([&](int bm, int bn) { return (int64_t)L * cdiv(M, bm) * cdiv(N, bn); });

@@ -16,6 +16,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace gmi {
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -25,8 +27,16 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-enum { DT_F16 = 0, DT_BF16 = 1 };
+// Element types of A and B.  fp16 and bf16 results are stored in the input
+// type; OCP fp8 E4M3 inputs give a bf16 result.
+enum { DT_F16 = 0, DT_BF16 = 1, DT_F8 = 2 };
+template <int DT>
+constexpr int out_dt() {
+  return DT == DT_F8 ? DT_BF16 : DT;
+}
 
 // ---------------------------------------------------------------------------
 // MFMA.  Operand fragments: lane l holds row (l % 32) and the 8 consecutive k
@@ -42,6 +52,15 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   else
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                    0, 0, 0);
+}
+
+// v_mfma_scale_f32_32x32x64_f8f6f4 with both operands OCP fp8 E4M3 (format
+// 0) and unit E8M0 block scales (127 = 2^0): a plain fp8 product, fp32
+// accumulation.  Lane l holds 32 consecutive-slot bytes of row l % 32, k-half
+// l / 32 of the 64-k step.
+__device__ __forceinline__ f32x16 mfma32_f8(u32x8 a, u32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(i32x8, a), __builtin_bit_cast(i32x8, b), c,
+                                                         0, 0, 0, 127, 0, 127);
 }
 
 template <int DT>
@@ -179,10 +198,13 @@ __device__ __forceinline__ u32x4 mask_tail(u32x4 v, int n) {
 // SLOTS_ = 0: a ring of STAGES stages, each holding one k-tile of A and of B.
 // SLOTS_ > 0 (BM == BN): a ring of SLOTS_ single-operand slots, A of k-tile
 // kt in slot 2 kt and B in slot 2 kt + 1 (mod SLOTS_); STAGES is then unused.
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int STAGES_, int SLOTS_ = 0>
+// EB_: bytes per element of A and B (2: fp16 / bf16, 1: fp8); BK counts
+// elements, so a k-tile row is BK * EB bytes.
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int BK_, int STAGES_, int SLOTS_ = 0, int EB_ = 2>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, SLOTS = SLOTS_;
-  static constexpr int RING_BYTES = SLOTS_ > 0 ? SLOTS_ * BM_ * BK_ * 2 : STAGES_ * (BM_ + BN_) * BK_ * 2;
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, SLOTS = SLOTS_, EB = EB_;
+  static constexpr int RING_BYTES =
+      SLOTS_ > 0 ? SLOTS_ * BM_ * BK_ * EB_ : STAGES_ * (BM_ + BN_) * BK_ * EB_;
   // workgroups one CU holds: LDS-bound (160 KB); the kernels' launch bounds
   // hold the registers to match (waves per SIMD = workgroups per CU x NW / 4)
   static constexpr int WGS_PER_CU = (160 * 1024) / RING_BYTES >= 2 ? 2 : 1;
@@ -190,14 +212,24 @@ struct TileCfg {
   static constexpr int NW = WAVES_M * WAVES_N, THREADS = 64 * NW;
   static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;  // wave tile
   static constexpr int TM = WTM / 32, TN = WTN / 32;            // 32x32 blocks per wave
-  static constexpr int ROWB = BK * 2, CPR = ROWB / 16, RPL = 256 / ROWB;
+  static constexpr int ROWB = BK * EB, CPR = ROWB / 16, RPL = 256 / ROWB;
+  static constexpr int CE = 16 / EB;  // elements per 16-byte chunk
+  // matrix-instruction step: 16 k (one chunk per lane) for 16-bit inputs,
+  // 64 k (two chunks per lane) for fp8
+  static constexpr int KSTEP = EB == 2 ? 16 : 64, FC = EB == 2 ? 1 : 2, KK = BK / KSTEP;
+  // chunk t of the fragment of step kk for lanes l / 32 == h
+  __device__ static __forceinline__ int frag_chunk(int kk, int h, int t) {
+    return EB == 2 ? 2 * kk + h : 4 * kk + 2 * h + t;
+  }
   static constexpr int RPI = 1024 / ROWB;  // rows moved by one 1 KB wave copy
   static constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   static constexpr int SLOT_BYTES = A_BYTES;
   static constexpr int LDS_BYTES = RING_BYTES;
   static_assert(SLOTS == 0 || (BM == BN && SLOTS >= 5), "split ring: square tile, at least five slots");
-  static_assert(BK == 32 || BK == 64, "k-tile of 32 or 64");
+  static_assert(EB == 2 || EB == 1, "16-bit or 8-bit elements");
+  static_assert(ROWB == 64 || ROWB == 128, "k-tile rows of 64 or 128 bytes");
+  static_assert(KK >= 2 && KK % 2 == 0, "an even number of matrix steps per k-tile");
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
   static_assert(STAGES >= 2 && LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -249,14 +281,17 @@ struct DenseLoader {
     uint32_t vo[P];  // lane offset of copy i, or OOB for a chunk past K
   };
 
-  __device__ __forceinline__ void init(const uint16_t* base, int64_t ld, int row0, int rows, int K_) {
+  static_assert(!KTAIL || Cfg::EB == 2, "K tails are masked for 16-bit elements only");
+  // base: the operand's first element; ld and K in elements
+  __device__ __forceinline__ void init(const void* base, int64_t ld, int row0, int rows, int K_) {
     int left = rows - row0;
     if (left > ROWS) left = ROWS;
     if (left < 0) left = 0;
-    rs = make_rsrc(base + (int64_t)row0 * ld, (uint32_t)left * (uint32_t)ld * 2u);
+    const uint32_t ldb = (uint32_t)ld * Cfg::EB;  // row pitch, bytes
+    rs = make_rsrc((const char*)base + (int64_t)row0 * ld * Cfg::EB, (uint32_t)left * ldb);
     const int lane = threadIdx.x & 63;
-    const uint32_t v0 = (uint32_t)Cfg::dma_row(0, lane) * (uint32_t)ld * 2u + (uint32_t)Cfg::dma_chunk(lane) * 16u;
-    const uint32_t step = (uint32_t)(Cfg::NW * Cfg::RPI) * (uint32_t)ld * 2u;
+    const uint32_t v0 = (uint32_t)Cfg::dma_row(0, lane) * ldb + (uint32_t)Cfg::dma_chunk(lane) * 16u;
+    const uint32_t step = (uint32_t)(Cfg::NW * Cfg::RPI) * ldb;
 #pragma unroll
     for (int i = 0; i < P; ++i) voff[i] = v0 + i * step;
     K = K_;
@@ -267,7 +302,7 @@ struct DenseLoader {
     const int ke = kt < nk ? kt : nk - 1;
     Prep p;
     p.soff = (uint32_t)ke * Cfg::ROWB;
-    const bool in = (ke * Cfg::BK + Cfg::dma_chunk(threadIdx.x & 63) * 8) < K;
+    const bool in = (ke * Cfg::BK + Cfg::dma_chunk(threadIdx.x & 63) * Cfg::CE) < K;
 #pragma unroll
     for (int i = 0; i < P; ++i) p.vo[i] = in ? voff[i] : OOB;
     return p;
@@ -299,51 +334,6 @@ struct DenseLoader {
 };
 
 // ---------------------------------------------------------------------------
-// Dense K-contiguous operand, register-staged: the same rows and chunks as
-// DenseLoader, moved with buffer_load_dwordx4 into VGPRs and ds_write_b128
-// into the swizzled LDS tile after the current stage's multiplies.  Thread t
-// moves chunk t % CPR of rows t / CPR + i * (256 / CPR).
-// ---------------------------------------------------------------------------
-template <class Cfg, int ROWS, bool KTAIL = false>
-struct DenseRegLoader {
-  static constexpr bool kDMA = false;
-  static constexpr bool kFIX = false;
-  static constexpr int RPP = Cfg::THREADS / Cfg::CPR;  // rows per pass
-  static constexpr int P = ROWS / RPP;
-  static_assert(ROWS % RPP == 0, "rows must fill whole passes");
-  struct Regs {
-    u32x4 v[P];
-  };
-  rsrc_t rs;
-  uint32_t voff, step;
-  int K;
-
-  __device__ __forceinline__ void init(const uint16_t* base, int64_t ld, int row0, int rows, int K_) {
-    int left = rows - row0;
-    if (left > ROWS) left = ROWS;
-    if (left < 0) left = 0;
-    rs = make_rsrc(base + (int64_t)row0 * ld, (uint32_t)left * (uint32_t)ld * 2u);
-    voff = (uint32_t)(threadIdx.x / Cfg::CPR) * (uint32_t)ld * 2u + (threadIdx.x % Cfg::CPR) * 16u;
-    step = (uint32_t)RPP * (uint32_t)ld * 2u;
-    K = K_;
-  }
-  __device__ __forceinline__ void load(int kt, Regs& rg) const {
-    const int kc = kt * Cfg::BK + (int)(threadIdx.x % Cfg::CPR) * 8;
-    const int n = K - kc;
-#pragma unroll
-    for (int i = 0; i < P; ++i) {
-      const u32x4 v = buf_load16(rs, n > 0 ? voff + i * step + (uint32_t)kt * Cfg::ROWB : OOB);
-      rg.v[i] = (!KTAIL || n >= 8) ? v : mask_tail(v, n);
-    }
-  }
-  __device__ __forceinline__ void store(char* tile, const Regs& rg) const {
-#pragma unroll
-    for (int i = 0; i < P; ++i)
-      *(u32x4*)(tile + Cfg::off(threadIdx.x / Cfg::CPR + i * RPP, threadIdx.x % Cfg::CPR)) = rg.v[i];
-  }
-};
-
-// ---------------------------------------------------------------------------
 // Implicit-GEMM convolution A operand (fprop, direct to LDS).  GEMM row m is
 // output pixel (n, p, q), m = (n P + p) Q + q; GEMM column k is filter tap
 // (r, s, c), k = (r S + s) C + c.  Element (m, k) is
@@ -367,6 +357,7 @@ template <class Cfg, int ROWS>
 struct ConvLoader {
   static constexpr bool kDMA = true;
   static constexpr bool kFIX = false;
+  static_assert(Cfg::EB == 2, "16-bit activations");
   static constexpr int P = ROWS * Cfg::ROWB / (1024 * Cfg::NW);
   static_assert(P >= 1 && ROWS % (Cfg::NW * Cfg::RPI) == 0, "rows must fill whole copy passes");
   rsrc_t rs;
@@ -583,35 +574,57 @@ struct PrepOf<Ld, false> {
 // memory pipeline is fed at its own rate instead of receiving a burst that
 // would stall the wave (and the matrix core) at issue.
 // ---------------------------------------------------------------------------
-// Per-lane LDS byte offsets of this wave's fragments, one per 16-k step and
-// operand: the row of fragment i (j) is 32 i (32 j) past the first and the
-// swizzle repeats every RPL * CPR rows, which divides 32, so fragment i sits a
+// Per-lane LDS byte offsets of this wave's fragments, per matrix step and
+// operand (one 16-byte chunk per fragment for 16-bit inputs, two for fp8):
+// the row of fragment i (j) is 32 i (32 j) past the first and the swizzle
+// repeats every RPL * CPR rows, which divides 32, so fragment i sits a
 // constant 32 i rows past fragment 0 of the same step.
 template <class Cfg>
 struct FragAddr {
-  static constexpr int KK = Cfg::BK / 16;
+  static constexpr int KK = Cfg::KK, FC = Cfg::FC;
   static_assert(32 % (Cfg::RPL * Cfg::CPR) == 0, "swizzle period must divide the fragment row step");
-  uint32_t a[KK], b[KK];
+  uint32_t a[KK][FC], b[KK][FC];
   __device__ __forceinline__ void init() {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = (wave / Cfg::WAVES_N) * Cfg::WTM, wn = (wave % Cfg::WAVES_N) * Cfg::WTN;
-    const int frow = lane & 31, fchunk = lane >> 5;
+    const int frow = lane & 31, h = lane >> 5;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      a[kk] = (uint32_t)Cfg::off(wm + frow, kk * 2 + fchunk);
-      b[kk] = (uint32_t)Cfg::off(wn + frow, kk * 2 + fchunk);
-    }
+    for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+      for (int t = 0; t < FC; ++t) {
+        a[kk][t] = (uint32_t)Cfg::off(wm + frow, Cfg::frag_chunk(kk, h, t));
+        b[kk][t] = (uint32_t)Cfg::off(wn + frow, Cfg::frag_chunk(kk, h, t));
+      }
   }
 };
 
+// the fragment a lane holds for one matrix instruction
 template <class Cfg>
-__device__ __forceinline__ u32x4 frag_at(const char* st, uint32_t base, int blk) {
-  return *(const u32x4*)(st + base + blk * 32 * Cfg::ROWB);
+using frag_t = typename std::conditional<Cfg::FC == 1, u32x4, u32x8>::type;
+
+template <class Cfg>
+__device__ __forceinline__ frag_t<Cfg> frag_at(const char* st, const uint32_t (&base)[Cfg::FC], int blk) {
+  if constexpr (Cfg::FC == 1) {
+    return *(const u32x4*)(st + base[0] + blk * 32 * Cfg::ROWB);
+  } else {
+    const u32x4 lo = *(const u32x4*)(st + base[0] + blk * 32 * Cfg::ROWB);
+    const u32x4 hi = *(const u32x4*)(st + base[1] + blk * 32 * Cfg::ROWB);
+    return u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+}
+
+// one accumulator block: acc += B fragment x A fragment
+template <class Cfg, int DT>
+__device__ __forceinline__ f32x16 mma_block(const frag_t<Cfg>& fb, const frag_t<Cfg>& fa, f32x16 acc) {
+  if constexpr (DT == DT_F8)
+    return mfma32_f8(fb, fa, acc);
+  else
+    return mfma32<DT>(fb, fa, acc);
 }
 
 template <class Cfg>
 __device__ __forceinline__ void read_frags(const FragAddr<Cfg>& fa_, const char* sa, const char* sb, int kk,
-                                           u32x4 (&fa)[Cfg::TM], u32x4 (&fb)[Cfg::TN]) {
+                                           frag_t<Cfg> (&fa)[Cfg::TM], frag_t<Cfg> (&fb)[Cfg::TN]) {
 #pragma unroll
   for (int i = 0; i < Cfg::TM; ++i) fa[i] = frag_at<Cfg>(sa, fa_.a[kk], i);
 #pragma unroll
@@ -621,9 +634,9 @@ __device__ __forceinline__ void read_frags(const FragAddr<Cfg>& fa_, const char*
 template <class Cfg, int DT, bool CROSS, int SPAN_DIV, class L1, class L2>
 __device__ __forceinline__ void multiply_stage(const FragAddr<Cfg>& ad, const char* sa, const char* sb,
                                                const char* na, const char* nb, f32x16 (&acc)[Cfg::TM][Cfg::TN],
-                                               u32x4 (&fa)[2][Cfg::TM], u32x4 (&fb)[2][Cfg::TN], const L1& l1,
-                                               int k1, char* d1, const L2& l2, int k2, char* d2) {
-  constexpr int KK = Cfg::BK / 16;
+                                               frag_t<Cfg> (&fa)[2][Cfg::TM], frag_t<Cfg> (&fb)[2][Cfg::TN],
+                                               const L1& l1, int k1, char* d1, const L2& l2, int k2, char* d2) {
+  constexpr int KK = Cfg::KK;
   static_assert(KK % 2 == 0, "fragment double buffer flips once per step");
   constexpr int NMFMA = Cfg::TM * Cfg::TN, NDS = Cfg::TM + Cfg::TN;
   constexpr int P1 = dma_count<L1>(), P2 = dma_count<L2>(), T = P1 + P2;
@@ -642,7 +655,7 @@ __device__ __forceinline__ void multiply_stage(const FragAddr<Cfg>& ad, const ch
 #pragma unroll
     for (int m = 0; m < NMFMA; ++m) {
       const int i = m / Cfg::TN, j = m % Cfg::TN;
-      acc[i][j] = mfma32<DT>(fb[cur][j], fa[cur][i], acc[i][j]);
+      acc[i][j] = mma_block<Cfg, DT>(fb[cur][j], fa[cur][i], acc[i][j]);
       if (rd) {
         if (m < Cfg::TM)
           fa[nx][m] = frag_at<Cfg>(ra, ad.a[rk], m);
@@ -722,7 +735,7 @@ __device__ __forceinline__ void mainloop(char* lds, const ALd& al, const BLd& bl
   // the previous tile's epilogue may still be reading the stages
   __builtin_amdgcn_s_barrier();
   if (nk <= 0) return;
-  u32x4 fa[2][Cfg::TM], fb[2][Cfg::TN];
+  frag_t<Cfg> fa[2][Cfg::TM], fb[2][Cfg::TN];
   FragAddr<Cfg> ad;
   ad.init();
 

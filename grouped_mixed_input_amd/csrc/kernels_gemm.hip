@@ -21,7 +21,7 @@ __device__ __forceinline__ void run_tile(char* lds, const Tile& t, float alpha, 
   bl.init(t.B, t.ldb, t.n0, t.N, t.K);
   f32x16 acc[Cfg::TM][Cfg::TN];
   mainloop<Cfg, DT>(lds, al, bl, (t.K + Cfg::BK - 1) / Cfg::BK, acc);
-  store_tile<Cfg, DT>(t, acc, alpha, beta, lds);
+  store_tile<Cfg, out_dt<DT>()>(t, acc, alpha, beta, lds);
 }
 
 template <class Cfg>
@@ -127,53 +127,69 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_gemm_ptr_arra
   }
 }
 
-// 32-k stages: 4 x 32 KB (one workgroup of 8 waves per CU), 3 x 24 KB and
-// 4 x 16 KB (two workgroups of 4 waves per CU)
+// 16-bit inputs: 256x256 on a five-slot ring of 64-k single-operand slots
+// (one workgroup of 8 waves per CU); 256x128 and 128x128 on rings of three
+// 24 KB and four 16 KB 32-k stages (two workgroups of 4 waves per CU).
 using Cfg256 = TileCfg<256, 256, 4, 2, 64, 2, 5>;
 using Cfg256x128 = TileCfg<256, 128, 2, 2, 32, 3>;
 using Cfg128 = TileCfg<128, 128, 2, 2, 32, 4>;
 using CfgSmall256 = TileCfg<SMALL_M, 256, 1, 8, 64, 4>;
+// fp8 inputs: the same row bytes (128 k per 128-byte row), so the same rings
+// where they fit; 256x128 and 128x128 on two stages of 48 KB and 32 KB.
+using Cfg256F8 = TileCfg<256, 256, 4, 2, 128, 2, 5, 1>;
+using Cfg256x128F8 = TileCfg<256, 128, 2, 2, 128, 2, 0, 1>;
+using Cfg128F8 = TileCfg<128, 128, 2, 2, 128, 2, 0, 1>;
+using CfgSmall256F8 = TileCfg<SMALL_M, 256, 1, 8, 128, 4, 0, 1>;
 template <>
 struct SmallOf<Cfg256> {
   using type = CfgSmall256;
 };
-static_assert(CfgSmall256::THREADS == Cfg256::THREADS, "both tile shapes run on the same workgroup");
+template <>
+struct SmallOf<Cfg256F8> {
+  using type = CfgSmall256F8;
+};
+static_assert(CfgSmall256::THREADS == Cfg256::THREADS && CfgSmall256F8::THREADS == Cfg256F8::THREADS,
+              "both tile shapes run on the same workgroup");
 
 // Persistent grid: a whole number of XCD rounds, no more workgroups than can
 // be resident at once and no more than the tiles need.
-static int persistent_grid(int total_tiles, int shape) {
-  const int resident = device_cu_count() * tile_wgs_per_cu(shape);
+static int persistent_grid(int total_tiles, int wgs_per_cu) {
+  const int resident = device_cu_count() * wgs_per_cu;
   int g = (total_tiles + XCDS - 1) / XCDS * XCDS;
   if (g > resident) g = resident / XCDS * XCDS;
   return g < XCDS ? XCDS : g;
 }
 
 // Instantiate and launch KER for the tile shape, element type and K-tail mode
-// (KT: some K is not a multiple of 8, so a chunk can straddle K).
-#define GMI_LAUNCH1(KER, CFG, DT, KT, grid, args, stream) \
-  hipLaunchKernelGGL((KER<CFG, DT, KT>), dim3(grid), dim3(CFG::THREADS), 0, stream, args)
-#define GMI_LAUNCH_DT(KER, CFG, dtype, kt, grid, args, stream)                                 \
+// (KT: some K is not a multiple of 8, so a chunk can straddle K; fp8 requires
+// K % 16 == 0 and has no tail mode).
+#define GMI_LAUNCH1(KER, CFG, DT, KT, tiles, args, stream)                                              \
+  hipLaunchKernelGGL((KER<CFG, DT, KT>), dim3(persistent_grid(tiles, CFG::WGS_PER_CU)), dim3(CFG::THREADS), 0, \
+                     stream, args)
+#define GMI_LAUNCH_DT(KER, CFG, CFG8, dtype, kt, tiles, args, stream)                         \
   do {                                                                                       \
     if ((dtype) == DT_F16) {                                                                 \
-      if (kt) GMI_LAUNCH1(KER, CFG, DT_F16, true, grid, args, stream);                       \
-      else GMI_LAUNCH1(KER, CFG, DT_F16, false, grid, args, stream);                         \
+      if (kt) GMI_LAUNCH1(KER, CFG, DT_F16, true, tiles, args, stream);                      \
+      else GMI_LAUNCH1(KER, CFG, DT_F16, false, tiles, args, stream);                        \
+    } else if ((dtype) == DT_BF16) {                                                         \
+      if (kt) GMI_LAUNCH1(KER, CFG, DT_BF16, true, tiles, args, stream);                     \
+      else GMI_LAUNCH1(KER, CFG, DT_BF16, false, tiles, args, stream);                       \
     } else {                                                                                 \
-      if (kt) GMI_LAUNCH1(KER, CFG, DT_BF16, true, grid, args, stream);                      \
-      else GMI_LAUNCH1(KER, CFG, DT_BF16, false, grid, args, stream);                        \
+      GMI_LAUNCH1(KER, CFG8, DT_F8, false, tiles, args, stream);                             \
     }                                                                                        \
   } while (0)
-#define GMI_DISPATCH(KER, shape, dtype, kt, grid, args, stream)                                                \
+#define GMI_DISPATCH(KER, shape, dtype, kt, tiles, args, stream)                                               \
   do {                                                                                                       \
-    if ((shape) == TILE_256x256) GMI_LAUNCH_DT(KER, Cfg256, dtype, kt, grid, args, stream);                 \
-    else if ((shape) == TILE_256x128) GMI_LAUNCH_DT(KER, Cfg256x128, dtype, kt, grid, args, stream);        \
-    else GMI_LAUNCH_DT(KER, Cfg128, dtype, kt, grid, args, stream);                                         \
+    if ((shape) == TILE_256x256) GMI_LAUNCH_DT(KER, Cfg256, Cfg256F8, dtype, kt, tiles, args, stream);      \
+    else if ((shape) == TILE_256x128)                                                                        \
+      GMI_LAUNCH_DT(KER, Cfg256x128, Cfg256x128F8, dtype, kt, tiles, args, stream);                          \
+    else GMI_LAUNCH_DT(KER, Cfg128, Cfg128F8, dtype, kt, tiles, args, stream);                               \
   } while (0)
 
 hipError_t launch_grouped(const GroupDesc* desc_dev, int count, int total_tiles, int shape, int dtype, bool ktail,
                           float alpha, float beta, hipStream_t stream) {
   GroupedArgs a{desc_dev, count, total_tiles, alpha, beta};
-  const int grid = persistent_grid(total_tiles, shape);
-  GMI_DISPATCH(k_gemm_grouped, shape, dtype, ktail, grid, a, stream);
+  GMI_DISPATCH(k_gemm_grouped, shape, dtype, ktail, total_tiles, a, stream);
   return hipGetLastError();
 }
 
@@ -186,8 +202,7 @@ hipError_t launch_ptr_array(const PtrArrayLaunch& p, int shape, int dtype, float
   a.total_tiles = a.tiles_per_batch * p.L;
   a.alpha = alpha;
   a.beta = beta;
-  const int grid = persistent_grid(a.total_tiles, shape);
-  GMI_DISPATCH(k_gemm_ptr_array, shape, dtype, (p.K % 8) != 0, grid, a, stream);
+  GMI_DISPATCH(k_gemm_ptr_array, shape, dtype, (p.K % 8) != 0, a.total_tiles, a, stream);
   return hipGetLastError();
 }
 

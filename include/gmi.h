@@ -51,7 +51,14 @@ typedef enum {
   GMI_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed   */
 } gmi_status;
 
-typedef enum { GMI_F16 = 0, GMI_BF16 = 1 } gmi_dtype;
+/* Element types.  GMI_F8E4M3 (GEMM calls only): A and B are OCP fp8 E4M3
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits, no infinities,
+ * S.1111.111 is NaN, largest finite 448), C and D are bf16; the product of
+ * two fp8 values and their sum are formed exactly in fp32 by the matrix
+ * instruction, then accumulated in fp32.  This is the fp8 grouped GEMM the
+ * element-type aliases of the grouped kernel page admit, on gfx950's
+ * v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales. */
+typedef enum { GMI_F16 = 0, GMI_BF16 = 1, GMI_F8E4M3 = 2 } gmi_dtype;
 
 /* One problem of a grouped GEMM (host memory; the pointers are device
  * pointers).  Mirrors the per-group problem shape (M, N, K) and the per-group
@@ -81,7 +88,10 @@ size_t gmi_workspace_bytes(int32_t problem_count);
  * refresh; can_implement).
  *   problems   host array of `count` descriptors; it may be reused as soon as
  *              the call returns (the table is staged into `workspace`).
- *   dtype      element type of A, B, C and D (fp16 or bf16); fp32 accumulate.
+ *   dtype      element type of A, B, C and D (fp16 or bf16), or GMI_F8E4M3
+ *              (A and B fp8, C and D bf16; K, lda and ldb multiples of 16,
+ *              else GMI_ERR_UNSUPPORTED); fp32 accumulate.  Leading dimensions
+ *              count elements of their own operand.
  *   workspace  device buffer of at least gmi_workspace_bytes(count) bytes,
  *              16-byte aligned; overwritten by the call and read by the kernel
  *              until it completes on `stream`.
@@ -96,6 +106,7 @@ gmi_status gmi_gemm_grouped(const gmi_problem* problems, int32_t count, gmi_dtyp
  * operand shared by all batches) of
  * sm90_gemm_array_tma_warpspecialized_cooperative.hpp.
  *   C        may be NULL iff beta == 0; otherwise L valid pointers.
+ *   dtype    as for gmi_gemm_grouped (fp8 A and B give bf16 C and D).
  * No workspace is needed. */
 gmi_status gmi_gemm_ptr_array(int32_t L, int32_t M, int32_t N, int32_t K, const void* const* A, int64_t lda,
                               const void* const* B, int64_t ldb, const void* const* C, int64_t ldc,

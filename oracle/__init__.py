@@ -7,7 +7,8 @@ C, fp64, OpenMP over output rows); this module builds it with gcc and marshals
 numpy arrays into it.
 
 Inputs are the stored element bytes: fp16 / bf16 bit patterns as ``uint16``
-arrays, uint4 tensors packed two per byte (even index in the low nibble).
+arrays, OCP fp8 E4M3 codes as ``uint8`` arrays ("f8e4m3", A and B of the fp8
+GEMM only), uint4 tensors packed two per byte (even index in the low nibble).
 Results are unrounded ``float64`` arrays; ``round_to`` rounds them (RNE) only
 for bit-exact comparisons.
 """
@@ -25,7 +26,7 @@ _SRC = _HERE / "oracle.c"
 _LIB_PATH = _HERE / "liboracle.so"
 _lib = None
 
-DTYPES = {"f16": 0, "bf16": 1}
+DTYPES = {"f16": 0, "bf16": 1, "f8e4m3": 2}
 
 _d = ctypes.c_double
 _i32 = ctypes.c_int32
@@ -79,7 +80,7 @@ def _c(a, dtype):
 
 
 def decode(bits: np.ndarray, dtype: str) -> np.ndarray:
-    """fp16 / bf16 bit patterns -> exact float64 values."""
+    """fp16 / bf16 bit patterns or fp8 E4M3 codes -> exact float64 values."""
     b = _c(bits, np.uint16)
     out = np.empty(b.shape, np.float64)
     _load().ora_decode(_ptr(b), b.size, DTYPES[dtype], _ptr(out))
@@ -99,7 +100,10 @@ def gemm(A, B, C=None, *, K=None, alpha=1.0, beta=0.0, dtype="f16", dtype_c=None
 
     A: uint16 [M][lda] (row-major, K leading entries used), B: uint16 [N][ldb]
     (column-major B: row n of the array is column n of B), C: uint16 [M][ldc] or
-    None.  Returns float64 [M][N]."""
+    None.  For dtype "f8e4m3", A and B are uint8 codes and C is dtype_c
+    (bf16 by default).  Returns float64 [M][N]."""
+    if dtype == "f8e4m3" and dtype_c is None:
+        dtype_c = "bf16"
     A = _c(A, np.uint16)
     B = _c(B, np.uint16)
     M, lda = A.shape

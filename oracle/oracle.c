@@ -35,6 +35,7 @@
 
 #define ORA_F16 0
 #define ORA_BF16 1
+#define ORA_F8 2 /* OCP fp8 E4M3: A and B of the fp8 GEMM, one byte per element */
 
 /* ------------------------------------------------------------------------
  * Element decoding: IEEE-754 binary16 and bfloat16 (the upper half of
@@ -64,7 +65,25 @@ double ora_bf16_to_f64(uint16_t b) {
   return s ? -v : v;
 }
 
-static double dec(uint16_t v, int dt) { return dt == ORA_BF16 ? ora_bf16_to_f64(v) : ora_f16_to_f64(v); }
+/* OCP 8-bit floating point E4M3 ("fn": finite, no infinities): sign 1,
+ * exponent 4 with bias 7, mantissa 3; exponent 0 holds the subnormals
+ * m * 2^-9; S.1111.111 is NaN, so the largest finite value is 1.75 * 2^8. */
+double ora_e4m3_to_f64(uint8_t b) {
+  int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
+  double v;
+  if (e == 15 && m == 7)
+    v = NAN;
+  else if (e == 0)
+    v = ldexp((double)m, -9); /* subnormal: (m / 8) * 2^(1-7) */
+  else
+    v = ldexp((double)(8 + m), e - 10); /* (1 + m/8) * 2^(e-7) */
+  return s ? -v : v;
+}
+
+static double dec(uint16_t v, int dt) {
+  if (dt == ORA_F8) return ora_e4m3_to_f64((uint8_t)(v & 0xFFu));
+  return dt == ORA_BF16 ? ora_bf16_to_f64(v) : ora_f16_to_f64(v);
+}
 
 void ora_decode(const uint16_t* in, int64_t n, int32_t dt, double* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = dec(in[i], dt);
@@ -108,6 +127,8 @@ void ora_round(const double* in, int64_t n, int32_t dt, uint16_t* out) {
 /* ------------------------------------------------------------------------
  * GEMM [p1]: one problem of a grouped or pointer-array list.
  *   out[m*ldo + n] = alpha * sum_{k<K} A[m][k] * B[k][n] + beta * C[m][n]
+ * A and B elements arrive as uint16 codes: fp16 / bf16 bit patterns, or an
+ * fp8 E4M3 byte zero-extended (dt_ab == ORA_F8); C is of type dt_c.
  * A row-major (A[m][k] at A[m*lda + k]); B column-major (B[k][n] at
  * B[n*ldb + k]); C row-major (C[m][n] at C[m*ldc + n]); the C term is
  * omitted when beta == 0 (C may then be NULL).

@@ -19,6 +19,8 @@ def dev():
 
 
 def to_dev(bits: np.ndarray, dtype: str) -> torch.Tensor:
+    if dtype == "f8e4m3":
+        return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint8)).view(torch.float8_e4m3fn).to(dev())
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(TORCH_DT[dtype]).to(dev())
 
 

@@ -74,6 +74,7 @@ def test_grouped_validation(gmi):
     assert _grouped(gmi, [P(gmi, lda=68)])[0] == gmi.GMI_ERR_MISALIGNED
     assert _grouped(gmi, [P(gmi, ldc=60, C=A16 * 3)], beta=0.5)[0] == gmi.GMI_ERR_INVALID_ARG
     assert _grouped(gmi, [P(gmi)], dtype=7)[0] == gmi.GMI_ERR_UNSUPPORTED
+    assert _grouped(gmi, [P(gmi, K=40, lda=64, ldb=64)], dtype=2)[0] == gmi.GMI_ERR_UNSUPPORTED
     st, msg = _grouped(gmi, [P(gmi), P(gmi)], ws_bytes=100)
     assert st == gmi.GMI_ERR_WORKSPACE and "workspace" in msg
     assert _grouped(gmi, [P(gmi)], ws=0, ws_bytes=ok_ws)[0] == gmi.GMI_ERR_WORKSPACE
@@ -103,6 +104,9 @@ def test_ptr_array_validation(gmi):
     assert _ptr(gmi, ldb=56) == gmi.GMI_ERR_INVALID_ARG
     assert _ptr(gmi, ldd=72 + 4) == gmi.GMI_ERR_MISALIGNED
     assert _ptr(gmi, A=A16 + 4) == gmi.GMI_ERR_MISALIGNED
+    # fp8: K and the A / B leading dimensions must be multiples of 16
+    assert _ptr(gmi, dt=2, K=72, lda=80, ldb=80) == gmi.GMI_ERR_UNSUPPORTED
+    assert _ptr(gmi, dt=2, K=64, lda=72, ldb=64) == gmi.GMI_ERR_UNSUPPORTED
     assert _ptr(gmi, L=0, A=None, B=None, D=None) == gmi.GMI_OK
 
 

@@ -64,3 +64,26 @@ def test_moe_counts_recipe():
 def test_bf16_cast_is_round_to_nearest_even():
     f = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -20, -2.5], np.float32)
     assert gi.f32_to_bf16_bits(f).tolist() == [0x3F80, 0x3F82, 0x3F81, 0xC020]
+
+
+def test_e4m3_encoder_matches_torch_and_saturates():
+    import torch
+
+    r = np.random.default_rng(3)
+    x = np.concatenate([r.standard_normal(50000) * 10.0 ** r.uniform(-4, 2.6, 50000), np.linspace(-448, 448, 4001)])
+    x = np.clip(x, -448, 448).astype(np.float32)
+    # exact halfway points between neighbouring positive codes (ties go to the even code)
+    codes = np.arange(126, dtype=np.uint8)
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    x = np.concatenate([x, ((vals[:-1] + vals[1:]) / 2).astype(np.float32)])
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(gi.to_bits(x, "f8e4m3"), want)
+    # beyond the largest finite value (1.75 * 2^8) the encoder saturates
+    assert list(gi.to_bits(np.array([1e4, -500.0, 449.0], np.float32), "f8e4m3")) == [0x7E, 0xFE, 0x7E]
+
+
+def test_fp8_workloads():
+    A, B = gi.ptr_array_f8(L=2, M=8, N=16, K=32)
+    assert A[0].dtype == np.uint8 and A[0].shape == (8, 32) and B[1].shape == (16, 32)
+    assert _h(*A) == _h(*gi.ptr_array_f8(L=2, M=8, N=16, K=32)[0])
+    assert gi.moe_expert_weight_f8(3, N=16, K=32).shape == (16, 32)

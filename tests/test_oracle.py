@@ -38,6 +38,8 @@ def test_golden_encodings():
         want = eval(expr, {"__builtins__": {}}, {"float": float})
         got = oracle.decode(np.array([int(bits, 16)], np.uint16), fmt)[0]
         assert got == want and np.signbit(got) == np.signbit(want), (fmt, bits)
+        if fmt == "f8e4m3":  # fp8 is an input type only: the oracle never rounds to it
+            continue
         back = oracle.round_to(np.array([want]), fmt)[0]
         assert back == int(bits, 16), (fmt, bits, hex(back))
 
@@ -50,6 +52,31 @@ def test_decode_all_patterns_match_library(dtype):
     nan = np.isnan(want)
     assert np.array_equal(np.isnan(got), nan)
     assert np.array_equal(got[~nan], want[~nan])
+
+
+def test_decode_all_e4m3_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    got = oracle.decode(codes, "f8e4m3")
+    want = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(want)
+    assert nan.sum() == 2  # S.1111.111 only: the format has no infinities
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def test_gemm_fp8_brute_force_numpy():
+    # fp8 A and B (codes), bf16 C: the oracle against numpy over torch-decoded values
+    for M, N, K in [(1, 1, 16), (5, 7, 32), (13, 8, 48)]:
+        a = RNG.integers(0, 256, (M, K + 16), dtype=np.uint8)
+        b = RNG.integers(0, 256, (N, K + 16), dtype=np.uint8)
+        a[(a & 0x7F) == 0x7F] = 0x38  # no NaN codes
+        b[(b & 0x7F) == 0x7F] = 0x38
+        c = bf16_bits(RNG.standard_normal((M, N)))
+        dec = lambda x: torch.from_numpy(x.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+        want = 0.5 * dec(a)[:, :K] @ dec(b)[:, :K].T - 2.0 * lib_decode(c, "bf16")
+        got = oracle.gemm(a, b, c, K=K, alpha=0.5, beta=-2.0, dtype="f8e4m3")
+        assert np.allclose(got, want, rtol=1e-13, atol=1e-13), (M, N, K)
 
 
 def test_round_f16_matches_numpy_direct_double_to_half():
