@@ -26,6 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_MFMA_16 = 2516.6  # TFLOP/s, dense fp16 / bf16: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_MFMA_8 = 5033.2  # TFLOP/s, dense fp8: twice the 16-bit rate
 PEAK_HBM = 8000.0  # GB/s
 # HBM bytes per launch of the headline kernel: rocprofv3 FETCH_SIZE and WRITE_SIZE of the headline command,
 # each scaled by what the same counter reads for a plain 256 MiB device copy (FETCH x 1.9997, WRITE x 1.0);
@@ -61,13 +62,13 @@ def time_launches(torch, fn, n_copies, warmup, iters):
     return s.elapsed_time(e) / iters
 
 
-def roof(flops, bytes_, ms):
+def roof(flops, bytes_, ms, peak=PEAK_MFMA_16):
     t = ms * 1e-3
     tf = flops / t / 1e12
     gbs = bytes_ / t / 1e9
-    return dict(us=round(ms * 1e3, 3), tflops=round(tf, 2), frac_mfma=round(tf / PEAK_MFMA_16, 4),
+    return dict(us=round(ms * 1e3, 3), tflops=round(tf, 2), frac_mfma=round(tf / peak, 4),
                 gbps=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM, 4),
-                roofline_frac=round(max(flops / (PEAK_MFMA_16 * 1e12), bytes_ / (PEAK_HBM * 1e9)) / t, 4))
+                roofline_frac=round(max(flops / (peak * 1e12), bytes_ / (PEAK_HBM * 1e9)) / t, 4))
 
 
 def t16(torch, bits, dtype, dev):
@@ -183,6 +184,39 @@ def bench_workloads(torch, gmi, gi, dev, args):
                        max(20, 2 * R))
     out["conv_fprop_bf16"] = dict(roof(2.0 * 100352 * 256 * 2304, ws, ms), bound="mfma")
     log("bench: conv done")
+    del sets
+    torch.cuda.empty_cache()
+
+    # 6. fp8 (E4M3) inputs, bf16 results: the pointer-array headline shape and the MoE layer
+    A8, B8 = gi.ptr_array_f8(L=16)
+    ws = 16 * (2 * 1024 * 1024 + 2 * 1024 * 1024 * 2)
+    R = copies_for(ws)
+    f8 = torch.float8_e4m3fn
+    sets = []
+    for r in range(R):
+        Ad = [torch.from_numpy(a).view(f8).to(dev) for a in A8]
+        Bd = [torch.from_numpy(b).view(f8).to(dev) for b in B8]
+        Dd = [torch.empty((1024, 1024), dtype=torch.bfloat16, device=dev) for _ in range(16)]
+        sets.append([gmi.pointer_array(x, dev) for x in (Ad, Bd, Dd)] + [Ad, Bd, Dd])
+    ms = time_launches(torch, lambda i: gmi.gemm_ptr_array(16, 1024, 1024, 1024, sets[i][0], 1024, sets[i][1], 1024,
+                                                           None, 1024, sets[i][2], 1024, gmi.GMI_F8E4M3, 1.0, 0.0),
+                       R, 10, max(50, 2 * R))
+    out["ptr_array_fp8"] = dict(roof(2.0 * 16 * 1024 ** 3, ws, ms, PEAK_MFMA_8), bound="hbm")
+    del sets, A8, B8
+    N, K = 2048, 4096
+    A = torch.from_numpy(gi.moe_activations_f8()).view(f8).to(dev)
+    D = torch.empty((int(counts.sum()), N), dtype=torch.bfloat16, device=dev)
+    Bw = [torch.from_numpy(gi.moe_expert_weight_f8(g)).view(f8).to(dev) for g in range(len(counts))]
+    table = gmi.make_problems([A[off[g]:off[g + 1]] for g in range(128)], Bw, [None] * 128,
+                              [D[off[g]:off[g + 1]] for g in range(128)])
+    wsb = torch.empty(gmi.workspace_bytes(128), dtype=torch.uint8, device=dev)
+    fl = 2.0 * counts.sum() * N * K
+    by = counts.sum() * K + int((counts > 0).sum()) * N * K + 2 * counts.sum() * N
+    ms = time_launches(torch, lambda i: gmi.gemm_grouped_raw(table, 128, gmi.GMI_F8E4M3, 1.0, 0.0, wsb), 1, 3, 10)
+    out["moe_grouped_fp8"] = dict(roof(fl, by, ms, PEAK_MFMA_8), bound="hbm")
+    del Bw, A, D
+    torch.cuda.empty_cache()
+    log("bench: fp8 done")
     return out
 
 
