@@ -143,7 +143,14 @@ def bench_workloads(torch, gmi, gi, dev, args):
     by = 2 * (counts.sum() * K + int((counts > 0).sum()) * N * K + counts.sum() * N)
     ms = time_launches(torch, lambda i: gmi.gemm_grouped_raw(table, 128, gmi.GMI_BF16, 1.0, 0.0, wsb), 1, 3, 10)
     out["moe_grouped_bf16"] = dict(roof(fl, by, ms), bound="hbm")
-    del Bw, A, D
+    # the same layer with the group sizes held on the device (row offsets; a
+    # table-building launch, then the GEMM): no host round trip
+    B3 = torch.stack(Bw)
+    del Bw
+    offs = torch.tensor(off.astype(np.int32), device=dev)
+    ms = time_launches(torch, lambda i: gmi.gemm_grouped_offsets(offs, A, B3, D, workspace=wsb), 1, 3, 10)
+    out["moe_grouped_offsets_bf16"] = dict(roof(fl, by, ms), bound="hbm")
+    del B3, A, D
     torch.cuda.empty_cache()
     log("bench: MoE grouped done")
 

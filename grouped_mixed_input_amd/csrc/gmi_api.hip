@@ -191,6 +191,66 @@ gmi_status gmi_gemm_grouped(const gmi_problem* problems, int32_t count, gmi_dtyp
                     "gemm_grouped: launch");
 }
 
+gmi_status gmi_gemm_grouped_offsets(int32_t count, const int32_t* offsets, int32_t rows, int32_t N, int32_t K,
+                                    const void* A, int64_t lda, const void* B, int64_t ldb, int64_t stride_b,
+                                    const void* C, int64_t ldc, void* D, int64_t ldd, gmi_dtype dtype,
+                                    float alpha, float beta, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  g_last_error.clear();
+  if (count < 0 || rows < 0 || N < 0 || K < 0)
+    return fail(GMI_ERR_INVALID_ARG, "gemm_grouped_offsets: negative size (count %d, rows %d, N %d, K %d)", count,
+                rows, N, K);
+  if (count > kMaxOffsetGroupCount)
+    return fail(GMI_ERR_UNSUPPORTED, "gemm_grouped_offsets: %d groups, at most %d", count, kMaxOffsetGroupCount);
+  if (!gemm_dtype_ok(dtype))
+    return fail(GMI_ERR_UNSUPPORTED, "gemm_grouped_offsets: dtype %d not supported", (int)dtype);
+  if (count == 0 || rows == 0 || N == 0) return GMI_OK;
+  const bool use_c = beta != 0.0f;
+  if (!offsets || !D || (K > 0 && (!A || !B)) || (use_c && !C))
+    return fail(GMI_ERR_INVALID_ARG, "gemm_grouped_offsets: a NULL operand");
+  if ((K > 0 && (lda < K || ldb < K)) || ldd < N || (use_c && ldc < N))
+    return fail(GMI_ERR_INVALID_ARG, "gemm_grouped_offsets: a leading dimension below its row width");
+  if (stride_b < 0) return fail(GMI_ERR_INVALID_ARG, "gemm_grouped_offsets: stride_b %lld < 0", (long long)stride_b);
+  if (lda > kMaxLd || ldb > kMaxLd || ldd > kMaxLd || (use_c && ldc > kMaxLd))
+    return fail(GMI_ERR_UNSUPPORTED, "gemm_grouped_offsets: a leading dimension above 2^22 elements");
+  if (!f8_shape_ok(dtype, K, lda, ldb) || (dtype == GMI_F8E4M3 && stride_b % 16))
+    return fail(GMI_ERR_UNSUPPORTED, "gemm_grouped_offsets: fp8 needs K, lda, ldb and stride_b multiples of 16");
+  if ((K > 0 && (!aligned16(A) || !aligned16(B) || lda % 8 || ldb % 8 || stride_b % 8)) || !aligned16(D) ||
+      ldd % 8 || (use_c && (!aligned16(C) || ldc % 8)) || ((uintptr_t)offsets & 3u))
+    return fail(GMI_ERR_MISALIGNED,
+                "gemm_grouped_offsets: pointers must be 16-byte aligned (offsets 4-byte), ld and stride_b multiples "
+                "of 8");
+  if (!workspace || workspace_bytes < gmi_workspace_bytes(count))
+    return fail(GMI_ERR_WORKSPACE, "gemm_grouped_offsets: workspace of %zu bytes, %zu needed", workspace_bytes,
+                gmi_workspace_bytes(count));
+  if (!aligned16(workspace)) return fail(GMI_ERR_MISALIGNED, "gemm_grouped_offsets: workspace must be 16-byte aligned");
+  // The group sizes are unknown here: the shape is chosen from the fewest
+  // tiles the rows can make (all rows in one group), and the tile total is
+  // bounded by every group adding at most one partial tile row.
+  const int shape = choose_shape([&](int bm, int bn) { return cdiv(rows, bm) * cdiv(N, bn); });
+  const int64_t bound = (cdiv(rows, SMALL_M) + count) * cdiv(N, tile_bn(shape));
+  if (bound > INT32_MAX) return fail(GMI_ERR_INVALID_ARG, "gemm_grouped_offsets: more than 2^31 - 1 output tiles");
+  OffsetsLaunch p;
+  p.offsets = offsets;
+  p.count = count;
+  p.rows = rows;
+  p.N = N;
+  p.K = K;
+  p.A = A;
+  p.B = B;
+  p.C = use_c ? C : nullptr;
+  p.D = D;
+  p.lda = lda;
+  p.ldb = ldb;
+  p.stride_b = stride_b;
+  p.ldc = ldc;
+  p.ldd = ldd;
+  p.total = (int32_t*)workspace;
+  p.desc = (GroupDesc*)((char*)workspace + kWorkspaceHeader);
+  return hip_status(launch_grouped_offsets(p, shape, (int)dtype, alpha, beta, (hipStream_t)stream),
+                    "gemm_grouped_offsets: launch");
+}
+
 gmi_status gmi_gemm_ptr_array(int32_t L, int32_t M, int32_t N, int32_t K, const void* const* A, int64_t lda,
                               const void* const* B, int64_t ldb, const void* const* C, int64_t ldc, void* const* D,
                               int64_t ldd, gmi_dtype dtype, float alpha, float beta, void* stream) {

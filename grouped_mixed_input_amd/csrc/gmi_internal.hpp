@@ -34,6 +34,21 @@ inline int grouped_tile_rows(int shape, int M) {
   return (shape == TILE_256x256 && M <= SMALL_M) ? SMALL_M : tile_bm(shape);
 }
 
+// Grouped launch whose group sizes are device-held row offsets; `desc` and
+// `total` point into the caller's workspace.
+struct OffsetsLaunch {
+  const int32_t* offsets;
+  int count, rows, N, K;
+  const void* A;
+  const void* B;
+  const void* C;  // NULL when beta == 0
+  void* D;
+  int64_t lda, ldb, stride_b, ldc, ldd;
+  GroupDesc* desc;
+  int32_t* total;
+};
+constexpr int kMaxOffsetGroupCount = 1024;
+
 struct PtrArrayLaunch {
   const uint16_t* const* A;
   const uint16_t* const* B;
@@ -71,6 +86,8 @@ int w4a16_split(int M, int N, int K);
 
 hipError_t launch_grouped(const GroupDesc* desc_dev, int count, int total_tiles, int shape, int dtype, bool ktail,
                           float alpha, float beta, hipStream_t stream);
+hipError_t launch_grouped_offsets(const OffsetsLaunch& p, int shape, int dtype, float alpha, float beta,
+                                  hipStream_t stream);
 hipError_t launch_ptr_array(const PtrArrayLaunch& a, int shape, int dtype, float alpha, float beta,
                             hipStream_t stream);
 hipError_t launch_conv_fprop(const ConvLaunch& a, int shape, int dtype, float alpha, float beta, hipStream_t stream);

@@ -34,7 +34,8 @@ constexpr int lds_of() {
 
 struct GroupedArgs {
   const GroupDesc* desc;
-  int count, total_tiles;
+  int count, total_tiles;  // total_tiles < 0: read the total from *total_dev
+  const int32_t* total_dev;
   float alpha, beta;
 };
 
@@ -76,10 +77,13 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_gemm_grouped(
   constexpr int LDS = Cfg::LDS_BYTES > lds_of<Small>() ? Cfg::LDS_BYTES : lds_of<Small>();
   __shared__ __attribute__((aligned(16))) char lds[LDS];
   const int G = gridDim.x;
+  // with device-held group sizes the grid is sized for the device, not the
+  // tiles: workgroups past the total find no tile and return
+  const int total = a.total_tiles >= 0 ? a.total_tiles : *a.total_dev;
   int g = 0;
-  for (int base = 0; base < a.total_tiles; base += G) {
+  for (int base = 0; base < total; base += G) {
     const int tile = base + remap_slot(blockIdx.x, G);
-    if (tile >= a.total_tiles) break;
+    if (tile >= total) break;
     while (g + 1 < a.count && a.desc[g + 1].tile_start <= tile) ++g;
     const GroupDesc& d = a.desc[g];
     const int local = tile - d.tile_start;
@@ -91,6 +95,82 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_gemm_grouped(
     }
     grouped_tile<DT, KTAIL, Cfg>(lds, d, local, a.alpha, a.beta);
   }
+}
+
+// Group table from device-held row offsets (one workgroup, one thread per
+// group): group g owns rows [offsets[g], offsets[g + 1]) clipped to
+// [0, rows); it gets the tile rows of the grouped rule, and the groups are
+// ranked by work per tile (rows a tile actually uses; K is shared), largest
+// first, ties in group order -- the same order the host-built table uses.
+// The tile prefix sums follow the ranking; the total goes to *total.
+struct OffsetsTableArgs {
+  const int32_t* offsets;
+  int count, rows, N, K;
+  const char* A;  // byte pointers; A and B elements are `eb` bytes, C and D two
+  const char* B;
+  const char* C;
+  char* D;
+  int64_t lda, ldb, stride_b, ldc, ldd;
+  int eb, bm, bn, small_class;
+  GroupDesc* desc;
+  int32_t* total;
+};
+
+
+__global__ __launch_bounds__(kMaxOffsetGroupCount) void k_group_table(OffsetsTableArgs a) {
+  __shared__ int32_t key[kMaxOffsetGroupCount];
+  __shared__ int32_t scan[2][kMaxOffsetGroupCount];
+  const int g = threadIdx.x;
+  const bool live = g < a.count;
+  int lo = 0, m = 0, work = -1, tiles = 0;
+  if (live) {
+    lo = min(max(a.offsets[g], 0), a.rows);
+    const int hi = min(max(a.offsets[g + 1], 0), a.rows);
+    m = hi > lo ? hi - lo : 0;
+    if (m > 0 && a.N > 0) {
+      const int tr = (a.small_class && m <= SMALL_M) ? SMALL_M : a.bm;
+      tiles = (m + tr - 1) / tr * ((a.N + a.bn - 1) / a.bn);
+      work = min(m, tr);
+    }
+  }
+  key[g] = work;
+  __syncthreads();
+  int rank = g;
+  if (live) {
+    rank = 0;
+    for (int h = 0; h < a.count; ++h) {
+      const int kh = key[h];
+      rank += (kh > work) || (kh == work && h < g);
+    }
+  }
+  scan[0][g] = 0;
+  __syncthreads();
+  if (live) scan[0][rank] = tiles;
+  __syncthreads();
+  int cur = 0;
+  for (int d = 1; d < kMaxOffsetGroupCount; d <<= 1) {  // inclusive scan over ranks
+    const int v = scan[cur][g] + (g >= d ? scan[cur][g - d] : 0);
+    scan[cur ^ 1][g] = v;
+    cur ^= 1;
+    __syncthreads();
+  }
+  if (live) {
+    GroupDesc d;
+    d.A = (const uint16_t*)(a.A + (int64_t)lo * a.lda * a.eb);
+    d.B = (const uint16_t*)(a.B + (int64_t)g * a.stride_b * a.eb);
+    d.C = a.C ? (const uint16_t*)(a.C + (int64_t)lo * a.ldc * 2) : nullptr;
+    d.D = (uint16_t*)(a.D + (int64_t)lo * a.ldd * 2);
+    d.lda = a.lda;
+    d.ldb = a.ldb;
+    d.ldc = a.ldc;
+    d.ldd = a.ldd;
+    d.M = m;
+    d.N = a.N;
+    d.K = a.K;
+    d.tile_start = scan[cur][rank] - tiles;
+    a.desc[rank] = d;
+  }
+  if (g == 0) *a.total = a.count > 0 ? scan[cur][a.count - 1] : 0;
 }
 
 struct PtrArrayArgs {
@@ -188,8 +268,42 @@ static int persistent_grid(int total_tiles, int wgs_per_cu) {
 
 hipError_t launch_grouped(const GroupDesc* desc_dev, int count, int total_tiles, int shape, int dtype, bool ktail,
                           float alpha, float beta, hipStream_t stream) {
-  GroupedArgs a{desc_dev, count, total_tiles, alpha, beta};
+  GroupedArgs a{desc_dev, count, total_tiles, nullptr, alpha, beta};
   GMI_DISPATCH(k_gemm_grouped, shape, dtype, ktail, total_tiles, a, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_offsets(const OffsetsLaunch& p, int shape, int dtype, float alpha, float beta,
+                                  hipStream_t stream) {
+  OffsetsTableArgs t;
+  t.offsets = p.offsets;
+  t.count = p.count;
+  t.rows = p.rows;
+  t.N = p.N;
+  t.K = p.K;
+  t.A = (const char*)p.A;
+  t.B = (const char*)p.B;
+  t.C = (const char*)p.C;
+  t.D = (char*)p.D;
+  t.lda = p.lda;
+  t.ldb = p.ldb;
+  t.stride_b = p.stride_b;
+  t.ldc = p.ldc;
+  t.ldd = p.ldd;
+  t.eb = dtype == DT_F8 ? 1 : 2;
+  t.bm = tile_bm(shape);
+  t.bn = tile_bn(shape);
+  t.small_class = shape == TILE_256x256;
+  t.desc = p.desc;
+  t.total = p.total;
+  hipLaunchKernelGGL(k_group_table, dim3(1), dim3(kMaxOffsetGroupCount), 0, stream, t);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // the tile total is known on the device only: size the grid for the
+  // device (every resident workgroup), idle ones return at once
+  GroupedArgs a{p.desc, p.count, -1, p.total, alpha, beta};
+  const int fill = 1 << 20;
+  GMI_DISPATCH(k_gemm_grouped, shape, dtype, (p.K % 8) != 0, fill, a, stream);
   return hipGetLastError();
 }
 

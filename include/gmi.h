@@ -99,6 +99,38 @@ size_t gmi_workspace_bytes(int32_t problem_count);
 gmi_status gmi_gemm_grouped(const gmi_problem* problems, int32_t count, gmi_dtype dtype, float alpha,
                             float beta, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Grouped GEMM whose group sizes exist only on the device -- the
+ * mixture-of-experts layout, where a routing kernel writes how many rows
+ * each expert received and the host never reads them back.  The grouped
+ * kernel page allows problem shapes that only the device holds (its grid may
+ * then be larger than the tiles, and a workgroup that finds no work returns);
+ * here the device-held shapes take the form of row offsets:
+ *   group g < count owns rows [offsets[g], offsets[g + 1]) of A (row-major,
+ *   [rows][lda], K contiguous) and of D (and C), and multiplies them by its
+ *   own B_g = B + g * stride_b elements (column-major as for
+ *   gmi_gemm_grouped: column n at B_g + n * ldb); N and K are shared.
+ *   offsets    device array of count + 1 int32, non-decreasing, offsets[0] >= 0,
+ *              offsets[count] <= rows.  Read on the device only, when the
+ *              work runs on `stream`.  A group whose range is empty, reversed
+ *              or outside [0, rows) is clipped to the part inside (or skipped),
+ *              so no access leaves the buffers; its rows of D are then
+ *              unspecified.
+ *   rows       host: number of rows A, C and D hold (the capacity, e.g. tokens
+ *              x experts per token); sizes the tile shape and bounds the grid.
+ *   count      1 .. 1024 groups, else GMI_ERR_UNSUPPORTED (0 is a no-op).
+ *   stride_b   elements between consecutive B_g; a multiple of 8 (16 for fp8).
+ *   dtype      as for gmi_gemm_grouped.
+ *   workspace  at least gmi_workspace_bytes(count) bytes, 16-byte aligned; a
+ *              first launch writes the group table there (groups in decreasing
+ *              order of work per tile, tile prefix sums, the tile total), the
+ *              GEMM launch reads it.
+ * Rows of D outside every group are not written. */
+gmi_status gmi_gemm_grouped_offsets(int32_t count, const int32_t* offsets, int32_t rows, int32_t N, int32_t K,
+                                    const void* A, int64_t lda, const void* B, int64_t ldb, int64_t stride_b,
+                                    const void* C, int64_t ldc, void* D, int64_t ldd, gmi_dtype dtype,
+                                    float alpha, float beta, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
 /* Pointer-array batched GEMM: L problems of one shape (M, N, K) and shared
  * leading dimensions, each operand a separate device buffer.  The pointer
  * arrays themselves are device arrays of L device pointers.  Follows the

@@ -31,7 +31,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ["gmi_gemm_grouped", "gmi_gemm_ptr_array", "gmi_prepack_w4", "gmi_gemm_w4a16",
-                 "gmi_conv2d_fprop_implicit", "gmi_workspace_bytes", "gmi_prepack_w4_bytes", "gmi_last_error"]:
+                 "gmi_conv2d_fprop_implicit", "gmi_workspace_bytes", "gmi_prepack_w4_bytes", "gmi_last_error",
+                 "gmi_gemm_grouped_offsets", "gmi_w4a16_workspace_bytes"]:
         assert want in names
 
 
@@ -89,6 +90,34 @@ def test_grouped_empty_requests_launch_nothing(gmi):
     assert gmi.lib().gmi_gemm_grouped(None, 0, 0, 1.0, 0.0, None, 0, None) == gmi.GMI_OK
     empty = [P(gmi, M=0, A=None, B=None, C=None, D=None), P(gmi, N=0, A=None, B=None, C=None, D=None)]
     assert _grouped(gmi, empty, ws=0, ws_bytes=0)[0] == gmi.GMI_OK
+
+
+def _offs(gmi, count=4, offsets=A16 * 5, rows=256, N=64, K=64, A=A16, lda=64, B=A16 * 2, ldb=64, stride_b=64 * 64,
+          C=None, ldc=64, D=A16 * 4, ldd=64, dt=1, beta=0.0, ws=A16 * 64, ws_bytes=1 << 20):
+    st = gmi.lib().gmi_gemm_grouped_offsets(count, offsets, rows, N, K, A, lda, B, ldb, stride_b, C, ldc, D, ldd, dt,
+                                            1.0, beta, ws, ws_bytes, None)
+    return st, gmi.lib().gmi_last_error().decode()
+
+
+def test_grouped_offsets_validation(gmi):
+    bad = gmi.GMI_ERR_INVALID_ARG
+    for kw in (dict(count=-1), dict(rows=-2), dict(N=-1), dict(K=-5), dict(offsets=None), dict(A=None),
+               dict(D=None), dict(beta=0.5), dict(lda=32), dict(ldd=56), dict(stride_b=-64)):
+        assert _offs(gmi, **kw)[0] == bad, kw
+    st, msg = _offs(gmi, count=1025)
+    assert st == gmi.GMI_ERR_UNSUPPORTED and "1024" in msg
+    assert _offs(gmi, dt=9)[0] == gmi.GMI_ERR_UNSUPPORTED
+    assert _offs(gmi, dt=2, stride_b=64 * 64 + 8)[0] == gmi.GMI_ERR_UNSUPPORTED  # fp8 expert stride
+    assert _offs(gmi, dt=2, K=40, lda=48, ldb=48)[0] == gmi.GMI_ERR_UNSUPPORTED
+    for kw in (dict(offsets=A16 + 2), dict(A=A16 + 8), dict(stride_b=64 * 64 + 4), dict(lda=68),
+               dict(ws=A16 + 4)):
+        assert _offs(gmi, **kw)[0] == gmi.GMI_ERR_MISALIGNED, kw
+    st, msg = _offs(gmi, ws_bytes=256 + 80 * 4 - 1)
+    assert st == gmi.GMI_ERR_WORKSPACE and "workspace" in msg
+    assert _offs(gmi, ws=0)[0] == gmi.GMI_ERR_WORKSPACE
+    # nothing to do: no groups, no rows or no columns -- OK without a GPU call
+    for kw in (dict(count=0), dict(rows=0), dict(N=0)):
+        assert _offs(gmi, offsets=None, A=None, B=None, D=None, ws=0, ws_bytes=0, **kw)[0] == gmi.GMI_OK, kw
 
 
 def _ptr(gmi, L=2, M=64, N=64, K=64, A=A16, lda=64, B=A16, ldb=64, C=None, ldc=64, D=A16, ldd=64, dt=1, beta=0.0):
