@@ -61,6 +61,10 @@ def _load():
     lib.ora_dequant_w4.restype = ctypes.c_int
     lib.ora_w4a16.argtypes = [_i32, _i32, _i32, _p, _i64, _p, _p, _p, _i32, _p]
     lib.ora_w4a16.restype = ctypes.c_int
+    lib.ora_dequant_mixed.argtypes = [_i32, _i32, _p, _i32, _p, _i32, _p, _i32, _p]
+    lib.ora_dequant_mixed.restype = ctypes.c_int
+    lib.ora_mixed.argtypes = [_i32, _i32, _i32, _p, _i64, _i32, _p, _i32, _p, _p, _i32, _p]
+    lib.ora_mixed.restype = ctypes.c_int
     lib.ora_conv2d_fprop.argtypes = [_i32] * 13 + [_p, _p, _p, _i32, _d, _d, _p]
     lib.ora_conv2d_fprop.restype = ctypes.c_int
     lib.ora_prepack_w4.argtypes = [_i32, _i32, _p, _p]
@@ -142,6 +146,37 @@ def w4a16(X, W, scales, zeros, N, K, group) -> np.ndarray:
     out = np.empty((M, N), np.float64)
     if _load().ora_w4a16(M, N, K, _ptr(X), ldx, _ptr(W), _ptr(s), _ptr(z), group, _ptr(out)):
         raise ValueError("ora_w4a16 rejected its arguments")
+    return out
+
+
+W4_SIGNED = {"uint4": 0, "int4": 1}
+
+
+def dequant_mixed(W, scales, zeros, N, K, group, w_type="uint4", dtype="f16") -> np.ndarray:
+    """Dequantised weights in the conversion mode the arguments select: scales None -> v(q); zeros None ->
+    v(q) s; both -> (v(q) - v(z)) s, where v() reads a nibble as `w_type` ("uint4" or "int4", two's
+    complement) and the scales are `dtype` ("f16" or "bf16") bit patterns.  float64 [N][K]."""
+    W = _c(W, np.uint8)
+    s = None if scales is None else _c(scales, np.uint16)
+    z = None if zeros is None else _c(zeros, np.uint8)
+    out = np.empty((N, K), np.float64)
+    if _load().ora_dequant_mixed(N, K, _ptr(W), W4_SIGNED[w_type], _ptr(s), DTYPES[dtype], _ptr(z), group,
+                                 _ptr(out)):
+        raise ValueError("ora_dequant_mixed rejected its arguments")
+    return out
+
+
+def mixed(X, W, scales, zeros, N, K, group, w_type="uint4", dtype="f16") -> np.ndarray:
+    """Y = X W^T with the weights of dequant_mixed; X [M][ldx] `dtype` bit patterns.  float64 [M][N]."""
+    X = _c(X, np.uint16)
+    M, ldx = X.shape
+    W = _c(W, np.uint8)
+    s = None if scales is None else _c(scales, np.uint16)
+    z = None if zeros is None else _c(zeros, np.uint8)
+    out = np.empty((M, N), np.float64)
+    if _load().ora_mixed(M, N, K, _ptr(X), ldx, DTYPES[dtype], _ptr(W), W4_SIGNED[w_type], _ptr(s), _ptr(z), group,
+                         _ptr(out)):
+        raise ValueError("ora_mixed rejected its arguments")
     return out
 
 

@@ -220,6 +220,60 @@ int ora_w4a16(int32_t M, int32_t N, int32_t K, const uint16_t* X, int64_t ldx, c
 }
 
 /* ------------------------------------------------------------------------
+ * The three conversion modes of [p2] (ConversionMode, chosen by which of the
+ * scale and zero types is void) over a 4-bit weight of either signedness:
+ *   DirectConvert            (scales == NULL, zeros == NULL): w = v(q)
+ *   ConvertAndScale          (zeros == NULL):                 w = v(q) s
+ *   ConvertAndScaleWithZero  (both):                          w = (v(q) - v(z)) s
+ * v() is the value of a nibble: itself for uint4, two's complement for int4
+ * (nibbles 8..15 are -8..-1).  Scales are stored in `sdt` (fp16 or bf16),
+ * [ceil(K/g)][N]; zeros have the weight's type, [ceil(K/g)][N/2] packed.
+ * ------------------------------------------------------------------------ */
+static int nib_value(int q, int is_signed) { return (is_signed && q >= 8) ? q - 16 : q; }
+
+int ora_dequant_mixed(int32_t N, int32_t K, const uint8_t* w_u4, int32_t is_signed, const uint16_t* scales,
+                      int32_t sdt, const uint8_t* zeros, int32_t g, double* wout) {
+  if (N < 0 || K < 0 || g <= 0 || (K & 1) || (zeros && !scales)) return -1;
+  if (scales && sdt != ORA_F16 && sdt != ORA_BF16) return -1;
+  int64_t kh = K / 2, nz = (N + 1) / 2;
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t k = 0; k < K; ++k) {
+      int64_t grp = k / g;
+      int v = nib_value(nib(w_u4 + n * kh, k), is_signed);
+      if (zeros) v -= nib_value(nib(zeros + grp * nz, n), is_signed);
+      double s = scales ? dec(scales[grp * N + n], sdt) : 1.0;
+      wout[n * K + k] = (double)v * s;
+    }
+  return 0;
+}
+
+/* Y = X W^T with the weights of ora_dequant_mixed; X [M][ldx] and the scales
+ * of type `xdt`, out [M][N] unrounded. */
+int ora_mixed(int32_t M, int32_t N, int32_t K, const uint16_t* X, int64_t ldx, int32_t xdt, const uint8_t* w_u4,
+              int32_t is_signed, const uint16_t* scales, const uint8_t* zeros, int32_t g, double* out) {
+  if (M < 0 || N < 0 || K < 0 || g <= 0 || (K & 1) || (xdt != ORA_F16 && xdt != ORA_BF16)) return -1;
+  double* w = (double*)malloc(sizeof(double) * (size_t)(N ? N : 1) * (size_t)(K ? K : 1));
+  double* x = (double*)malloc(sizeof(double) * (size_t)(M ? M : 1) * (size_t)(K ? K : 1));
+  if (!w || !x || ora_dequant_mixed(N, K, w_u4, is_signed, scales, xdt, zeros, g, w)) {
+    free(w);
+    free(x);
+    return -1;
+  }
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t k = 0; k < K; ++k) x[m * K + k] = dec(X[m * ldx + k], xdt);
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t m = 0; m < M; ++m) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < K; ++k) acc += x[m * K + k] * w[n * K + k];
+      out[m * N + n] = acc;
+    }
+  free(w);
+  free(x);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------
  * Convolution forward [p3], direct form (no im2col), cross-correlation:
  *   out[n][p][q][k] = alpha * sum_{r,s,c} x[n][p*sh - ph + r*dh][q*sw - pw + s*dw][c]
  *                                         * w[k][r][s][c]   + beta * C[n][p][q][k]

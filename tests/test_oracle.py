@@ -267,6 +267,73 @@ def test_w4_group_equals_k_is_per_channel():
     assert np.array_equal(w, (q.astype(np.int64) - zz[:, None]) * lib_decode(s, "f16")[0][:, None])
 
 
+# ------------------------------------------------ conversion modes, int4, bf16
+def _nibbles(packed, signed):
+    """numpy nibble extraction; int4 by arithmetic-shift sign extension of the nibble placed in a byte's top."""
+    n = np.empty((packed.shape[0], packed.shape[1] * 2), np.uint8)
+    n[:, 0::2] = packed & 15
+    n[:, 1::2] = packed >> 4
+    if signed:
+        return ((n << 4).astype(np.uint8).view(np.int8) >> 4).astype(np.int64)
+    return n.astype(np.int64)
+
+
+def test_mixed_direct_convert_reads_each_nibble():
+    W = np.arange(256, dtype=np.uint8).reshape(1, 256)  # every byte, so every nibble in both positions
+    got_u = oracle.dequant_mixed(W, None, None, 1, 512, 512, "uint4")
+    got_s = oracle.dequant_mixed(W, None, None, 1, 512, 512, "int4")
+    assert np.array_equal(got_u, _nibbles(W, False).astype(np.float64))
+    assert np.array_equal(got_s, _nibbles(W, True).astype(np.float64))
+    # two's complement: nibble 8 is -8, 15 is -1, 7 is 7
+    assert got_s[0, 0x08 * 2] == -8 and got_s[0, 0x0F * 2] == -1 and got_s[0, 0x07 * 2] == 7
+
+
+def test_mixed_uint4_modes_reduce_to_the_zero_mode():
+    N, K, grp = 6, 256, 128
+    q, z, s, X, Wp, Zp = _w4_case(2, N, K, grp, seed=11)
+    zero_z = np.zeros_like(Zp)
+    ones = f16_bits(np.ones((K // grp, N)))
+    assert np.array_equal(oracle.dequant_mixed(Wp, s, None, N, K, grp), oracle.dequant_w4(Wp, s, zero_z, N, K, grp))
+    assert np.array_equal(oracle.dequant_mixed(Wp, None, None, N, K, grp),
+                          oracle.dequant_w4(Wp, ones, zero_z, N, K, grp))
+    assert np.array_equal(oracle.dequant_mixed(Wp, s, Zp, N, K, grp), oracle.dequant_w4(Wp, s, Zp, N, K, grp))
+    assert np.array_equal(oracle.mixed(X, Wp, s, Zp, N, K, grp), oracle.w4a16(X, Wp, s, Zp, N, K, grp))
+
+
+def test_mixed_int4_with_zeros_is_offset_binary_uint4():
+    # v(q) - v(z) with two's complement nibbles equals (q ^ 8) - (z ^ 8) as unsigned nibbles
+    N, K, grp = 8, 256, 64
+    q, z, s, X, Wp, Zp = _w4_case(1, N, K, grp, seed=13)
+    got = oracle.dequant_mixed(Wp, s, Zp, N, K, grp, "int4")
+    assert np.array_equal(got, oracle.dequant_w4(Wp ^ 0x88, s, Zp ^ 0x88, N, K, grp))
+    # and without zero points int4 is offset binary with the constant zero 8
+    eights = np.full_like(Zp, 0x88)
+    assert np.array_equal(oracle.dequant_mixed(Wp, s, None, N, K, grp, "int4"),
+                          oracle.dequant_w4(Wp ^ 0x88, s, eights, N, K, grp))
+
+
+@pytest.mark.parametrize("w_type,mode", [("int4", "zero"), ("int4", "scale"), ("uint4", "direct"),
+                                         ("uint4", "zero")])
+def test_mixed_bf16_against_numpy(w_type, mode):
+    M, N, K, grp = 4, 10, 256, 128
+    r = np.random.default_rng(17)
+    Wp = r.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    Zp = r.integers(0, 256, (K // grp, N // 2), dtype=np.uint8)
+    s = bf16_bits(r.uniform(0.001, 0.01, (K // grp, N)))
+    X = bf16_bits(r.standard_normal((M, K)))
+    signed = w_type == "int4"
+    v = _nibbles(Wp, signed)
+    if mode == "zero":
+        v = v - np.repeat(_nibbles(Zp, signed).T, grp, axis=1)
+    w = v * (np.repeat(lib_decode(s, "bf16").T, grp, axis=1) if mode != "direct" else 1.0)
+    want = lib_decode(X, "bf16") @ w.T
+    got = oracle.mixed(X, Wp, s if mode != "direct" else None, Zp if mode == "zero" else None, N, K, grp, w_type,
+                       "bf16")
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+    with pytest.raises(ValueError):
+        oracle.dequant_mixed(Wp, None, Zp, N, K, grp)  # zero points without scales: no such mode
+
+
 # ---------------------------------------------------------------- conv
 def _conv_scipy(x, w, pad, stride, dil, dtype="bf16"):
     xd, wd = lib_decode(x, dtype), lib_decode(w, dtype)
