@@ -69,6 +69,9 @@ def lib() -> ctypes.CDLL:
     L.gmi_prepack_w4.argtypes = [_p, _i32, _i32, _p, _p]
     L.gmi_gemm_w4a16.restype = ctypes.c_int
     L.gmi_gemm_w4a16.argtypes = [_i32, _i32, _i32, _p, _i64, _p, _p, _p, _i32, _p, _i64, _p, _sz, _p]
+    L.gmi_gemm_mixed.restype = ctypes.c_int
+    L.gmi_gemm_mixed.argtypes = [_i32, _i32, _i32, ctypes.c_int, _p, _i64, _p, ctypes.c_int, _p, _p, _i32, _p, _i64,
+                                 _p, _sz, _p]
     L.gmi_w4a16_workspace_bytes.restype = _sz
     L.gmi_w4a16_workspace_bytes.argtypes = [_i32, _i32, _i32]
     L.gmi_conv2d_fprop_implicit.restype = ctypes.c_int
@@ -200,6 +203,27 @@ def gemm_w4a16(X: torch.Tensor, w_prepacked: torch.Tensor, scales: torch.Tensor,
         workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
     _check(lib().gmi_gemm_w4a16(M, N, K, X.data_ptr(), _ld(X), w_prepacked.data_ptr(), scales.data_ptr(),
                                 zeros.data_ptr(), group_size, Y.data_ptr(), _ld(Y),
+                                workspace.data_ptr() if workspace.numel() else None, workspace.numel(),
+                                _stream(stream)))
+    return Y
+
+
+W4_TYPES = {"uint4": 0, "int4": 1}
+
+
+def gemm_mixed(X: torch.Tensor, w_prepacked: torch.Tensor, scales: torch.Tensor | None, zeros: torch.Tensor | None,
+               group_size: int, N: int, w_type: str = "uint4", Y: torch.Tensor | None = None,
+               workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Y = X W^T in any conversion mode: scales None is the direct conversion, zeros None the conversion
+    without zero point.  X, scales and Y share one type (float16 or bfloat16); `w_type` is "uint4" or
+    "int4" (zero points, if any, have the same type).  Workspace as for gemm_w4a16."""
+    M, K = X.shape
+    if Y is None:
+        Y = torch.empty((M, N), dtype=X.dtype, device=X.device)
+    if workspace is None:
+        workspace = torch.empty(w4a16_workspace_bytes(M, N, K), dtype=torch.uint8, device=X.device)
+    _check(lib().gmi_gemm_mixed(M, N, K, _DT[X.dtype], X.data_ptr(), _ld(X), w_prepacked.data_ptr(),
+                                W4_TYPES[w_type], _ptr(scales), _ptr(zeros), group_size, Y.data_ptr(), _ld(Y),
                                 workspace.data_ptr() if workspace.numel() else None, workspace.numel(),
                                 _stream(stream)))
     return Y

@@ -317,48 +317,85 @@ size_t gmi_w4a16_workspace_bytes(int32_t M, int32_t N, int32_t K) {
   return split > 1 ? (size_t)split * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
-gmi_status gmi_gemm_w4a16(int32_t M, int32_t N, int32_t K, const void* X, int64_t ldx, const uint8_t* w_prepacked,
-                          const void* scales, const uint8_t* zeros, int32_t group_size, void* Y, int64_t ldy,
-                          void* workspace, size_t workspace_bytes, void* stream) {
-  g_last_error.clear();
-  if (M < 0 || N < 0 || K < 0) return fail(GMI_ERR_INVALID_ARG, "gemm_w4a16: negative size (%d, %d, %d)", M, N, K);
+// Shared by the two mixed-input entry points: every rule checked, then one
+// launch.  `scales` NULL is the direct conversion (no scale), `zeros` NULL the
+// conversion without zero point.
+static gmi_status mixed_gemm(const char* who, int32_t M, int32_t N, int32_t K, gmi_dtype x_dtype, const void* X,
+                             int64_t ldx, const uint8_t* w_prepacked, gmi_w4_type w_type, const void* scales,
+                             const uint8_t* zeros, int32_t group_size, void* Y, int64_t ldy, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return fail(GMI_ERR_INVALID_ARG, "%s: negative size (%d, %d, %d)", who, M, N, K);
+  if (!dtype_ok(x_dtype)) return fail(GMI_ERR_UNSUPPORTED, "%s: activation type %d not supported", who, (int)x_dtype);
+  if (w_type != GMI_W4_UINT4 && w_type != GMI_W4_INT4)
+    return fail(GMI_ERR_UNSUPPORTED, "%s: weight type %d not supported", who, (int)w_type);
+  if (zeros && !scales)
+    return fail(GMI_ERR_UNSUPPORTED, "%s: zero points without scales is not a conversion mode", who);
+  if (!scales) group_size = K > 0 ? K : 128;  // unused without scales
   if (N % 16 || K % 128)
-    return fail(GMI_ERR_UNSUPPORTED, "gemm_w4a16: needs N %% 16 == 0 and K %% 128 == 0 (prepack blocks)");
-  if (group_size <= 0) return fail(GMI_ERR_INVALID_ARG, "gemm_w4a16: group_size %d <= 0", group_size);
+    return fail(GMI_ERR_UNSUPPORTED, "%s: needs N %% 16 == 0 and K %% 128 == 0 (prepack blocks)", who);
+  if (group_size <= 0) return fail(GMI_ERR_INVALID_ARG, "%s: group_size %d <= 0", who, group_size);
   if (K > 0 && K % group_size)
-    return fail(GMI_ERR_INVALID_ARG, "gemm_w4a16: K %d is not a multiple of group_size %d", K, group_size);
+    return fail(GMI_ERR_INVALID_ARG, "%s: K %d is not a multiple of group_size %d", who, K, group_size);
   if (group_size != K && group_size % 128)
-    return fail(GMI_ERR_UNSUPPORTED, "gemm_w4a16: group_size must equal K or be a multiple of 128");
+    return fail(GMI_ERR_UNSUPPORTED, "%s: group_size must equal K or be a multiple of 128", who);
   if ((int64_t)N * K / 2 > INT32_MAX || (int64_t)M * ldx * 2 > INT32_MAX || ldy > kMaxLd)
-    return fail(GMI_ERR_UNSUPPORTED, "gemm_w4a16: W (N*K/2 bytes) and X (M*ldx*2 bytes) must stay below 2^31 bytes");
+    return fail(GMI_ERR_UNSUPPORTED, "%s: W (N*K/2 bytes) and X (M*ldx*2 bytes) must stay below 2^31 bytes", who);
   if (M == 0 || N == 0) return GMI_OK;
-  if (!Y || (K > 0 && (!X || !w_prepacked || !scales || !zeros)))
-    return fail(GMI_ERR_INVALID_ARG, "gemm_w4a16: NULL pointer");
-  if ((K > 0 && ldx < K) || ldy < N) return fail(GMI_ERR_INVALID_ARG, "gemm_w4a16: ldx < K or ldy < N");
+  if (!Y || (K > 0 && (!X || !w_prepacked))) return fail(GMI_ERR_INVALID_ARG, "%s: NULL pointer", who);
+  if ((K > 0 && ldx < K) || ldy < N) return fail(GMI_ERR_INVALID_ARG, "%s: ldx < K or ldy < N", who);
   if (!aligned16(Y) || ldy % 8 ||
-      (K > 0 && (!aligned16(X) || !aligned16(w_prepacked) || !aligned16(scales) || !aligned16(zeros) || ldx % 8)))
-    return fail(GMI_ERR_MISALIGNED, "gemm_w4a16: pointers must be 16-byte aligned, ld multiples of 8");
+      (K > 0 && (!aligned16(X) || !aligned16(w_prepacked) || (scales && !aligned16(scales)) ||
+                 (zeros && !aligned16(zeros)) || ldx % 8)))
+    return fail(GMI_ERR_MISALIGNED, "%s: pointers must be 16-byte aligned, ld multiples of 8", who);
   W4Launch a;
   a.M = M;
   a.N = N;
   a.K = K;
   a.group = group_size;
+  a.dt = (int)x_dtype;  // the kernels number the element types as gmi_dtype does
   a.X = (const uint16_t*)X;
   a.ldx = ldx;
   a.w = w_prepacked;
   a.scales = (const uint16_t*)scales;
   a.zeros = zeros;
+  const int64_t groups = K > 0 ? K / group_size : 0;
+  a.s_bytes = scales ? (uint32_t)(groups * N * 2) : 0u;
+  a.z_bytes = zeros ? (uint32_t)(groups * N / 2) : 0u;
+  a.sor = scales ? 0u : (x_dtype == GMI_BF16 ? 0x3F80u : 0x3C00u);  // 1.0
+  // int4 (two's complement) read as offset binary: v = (q ^ 8) - 8, and
+  // v_q - v_z = (q ^ 8) - (z ^ 8); without zero points z reads as 0, so the
+  // zero becomes the constant 8
+  a.wxor = w_type == GMI_W4_INT4 ? 0x88888888u : 0u;
+  a.zxor = w_type == GMI_W4_INT4 ? 8u : 0u;
   a.Y = (uint16_t*)Y;
   a.ldy = ldy;
   a.split = 1;
   a.partial = nullptr;
   const size_t need = gmi_w4a16_workspace_bytes(M, N, K);
   if (need > 0 && workspace && workspace_bytes >= need) {
-    if (!aligned16(workspace)) return fail(GMI_ERR_MISALIGNED, "gemm_w4a16: workspace must be 16-byte aligned");
+    if (!aligned16(workspace)) return fail(GMI_ERR_MISALIGNED, "%s: workspace must be 16-byte aligned", who);
     a.split = w4a16_split(M, N, K);
     a.partial = (float*)workspace;
   }
-  return hip_status(launch_w4a16(a, (hipStream_t)stream), "gemm_w4a16: launch");
+  return hip_status(launch_w4a16(a, (hipStream_t)stream), who);
+}
+
+gmi_status gmi_gemm_w4a16(int32_t M, int32_t N, int32_t K, const void* X, int64_t ldx, const uint8_t* w_prepacked,
+                          const void* scales, const uint8_t* zeros, int32_t group_size, void* Y, int64_t ldy,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (M > 0 && N > 0 && K > 0 && (!scales || !zeros)) return fail(GMI_ERR_INVALID_ARG, "gemm_w4a16: NULL pointer");
+  return mixed_gemm("gemm_w4a16", M, N, K, GMI_F16, X, ldx, w_prepacked, GMI_W4_UINT4, scales, zeros, group_size,
+                    Y, ldy, workspace, workspace_bytes, stream);
+}
+
+gmi_status gmi_gemm_mixed(int32_t M, int32_t N, int32_t K, gmi_dtype x_dtype, const void* X, int64_t ldx,
+                          const uint8_t* w_prepacked, gmi_w4_type w_type, const void* scales, const uint8_t* zeros,
+                          int32_t group_size, void* Y, int64_t ldy, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  g_last_error.clear();
+  return mixed_gemm("gemm_mixed", M, N, K, x_dtype, X, ldx, w_prepacked, w_type, scales, zeros, group_size, Y, ldy,
+                    workspace, workspace_bytes, stream);
 }
 
 gmi_status gmi_conv2d_fprop_implicit(int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int32_t R, int32_t S,

@@ -82,6 +82,19 @@ __device__ __forceinline__ uint32_t to_bits(float f) {
     return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
+// two fp32 -> one 32-bit word of 16-bit patterns (a low, b high), round to
+// nearest even; one v_cvt_pk_{f16,bf16}_f32
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  if constexpr (DT == DT_F16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), h2));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), b2));
+}
+
 template <int DT>
 __device__ __forceinline__ float from_bits(uint32_t b) {
   if constexpr (DT == DT_F16)
@@ -457,15 +470,66 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t w, f16x2 zz, f16x2 ss) {
   return out;
 }
 
+// bfloat16 counterparts.  bfloat16 has too few mantissa bits for the OR
+// construction to stay cheap, so the nibbles go through fp32: spread into
+// bytes (even nibbles, odd nibbles), each byte converted by one
+// v_cvt_f32_ubyte.  The bytes of w & 0x0F0F0F0F are elements 0, 4, 1, 5 of
+// the word, those of (w >> 4) & 0x0F0F0F0F elements 2, 6, 3, 7.
+__device__ __forceinline__ float ubyte_f32(uint32_t v, int i) { return (float)((v >> (8 * i)) & 0xFFu); }
+
+// upper halves of two fp32 values: their bfloat16 patterns when exact
+__device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
+  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo), 0x07060302u);
+}
+
+// q - z for the 8 nibbles of w as exact bfloat16 integers (|q - z| <= 15
+// needs 4 significant bits; fp32 subtraction is exact, truncation too)
+__device__ __forceinline__ u32x4 unpack8_minus_zero_bf16(uint32_t w, float zf) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  u32x4 out;
+  out[0] = pack_hi16(ubyte_f32(lo, 0) - zf, ubyte_f32(lo, 2) - zf);
+  out[1] = pack_hi16(ubyte_f32(hi, 0) - zf, ubyte_f32(hi, 2) - zf);
+  out[2] = pack_hi16(ubyte_f32(lo, 1) - zf, ubyte_f32(lo, 3) - zf);
+  out[3] = pack_hi16(ubyte_f32(hi, 1) - zf, ubyte_f32(hi, 3) - zf);
+  return out;
+}
+
+// RN_bf16((q - z) s) for the 8 nibbles of w: q s - z s is formed exactly by
+// one fma (a 4-bit integer times an 8-bit significand fits fp32; nzs = -z s
+// is exact too), then rounded to nearest even by the conversion.
+__device__ __forceinline__ u32x4 dequant8_bf16(uint32_t w, float s, float nzs) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  auto d = [&](uint32_t v, int i) { return __builtin_fmaf(ubyte_f32(v, i), s, nzs); };
+  u32x4 out;
+  out[0] = pack2<DT_BF16>(d(lo, 0), d(lo, 2));
+  out[1] = pack2<DT_BF16>(d(hi, 0), d(hi, 2));
+  out[2] = pack2<DT_BF16>(d(lo, 1), d(lo, 3));
+  out[3] = pack2<DT_BF16>(d(hi, 1), d(hi, 3));
+  return out;
+}
+
+// dequantised 16-bit weights of one word in the activation type: s_bits is
+// the scale's storage pattern, z the zero point (both after the mode fix-ups)
+template <int DT>
+__device__ __forceinline__ u32x4 dequant8_dt(uint32_t w, uint32_t s_bits, uint32_t z) {
+  if constexpr (DT == DT_F16) {
+    return dequant8(w, zero_pair(z), scale_pair(s_bits));
+  } else {
+    const float s = from_bits<DT_BF16>(s_bits);
+    return dequant8_bf16(w, s, -(float)z * s);
+  }
+}
+
 // Prepacked weight geometry: 16 rows x 128 k per 1024-byte block, block
 // (n / 16, k / 128) at ((n / 16) * (K / 128) + k / 128) * 1024; lane L of a
 // block owns bytes [16 L, 16 L + 16): row L % 16, word j covering
 // k = 32 j + 8 (L / 16) + {0..7}.
 struct W4Geom {
   const uint8_t* w;        // prepacked weight
-  const uint16_t* scales;  // [K / g][N] fp16
-  const uint8_t* zeros;    // [K / g][N / 2] uint4
+  const uint16_t* scales;  // [K / g][N], the activation type
+  const uint8_t* zeros;    // [K / g][N / 2] 4-bit
   int N, K, group;
+  uint32_t s_bytes, z_bytes, sor, wxor, zxor;  // conversion mode (see W4Launch)
 };
 
 // ---------------------------------------------------------------------------
@@ -475,7 +539,7 @@ struct W4Geom {
 // zero, into registers.  The dequantisation runs when the registers are
 // written to LDS, after the multiplies of the current stage have been issued.
 // ---------------------------------------------------------------------------
-template <class Cfg, int ROWS>
+template <class Cfg, int ROWS, int DT = DT_F16>
 struct W4Loader {
   static constexpr bool kDMA = false;
   static constexpr bool kFIX = false;
@@ -488,18 +552,21 @@ struct W4Loader {
     uint32_t s[P], z[P];
   };
   rsrc_t rw, rsc, rz;
-  uint32_t kblocks, N, group, block0, kt0;
+  uint32_t kblocks, N, group, block0, kt0, sor, wxor, zxor;
 
   // rows n0 .., k-tiles from kt_first on (kt_first even: whole 128-k blocks)
   __device__ __forceinline__ void init(const W4Geom& g, int n0, int kt_first = 0) {
     rw = make_rsrc(g.w, (uint32_t)((int64_t)g.N * g.K / 2));
-    rsc = make_rsrc(g.scales, (uint32_t)((int64_t)g.N * (g.K / g.group) * 2));
-    rz = make_rsrc(g.zeros, (uint32_t)((int64_t)g.N / 2 * (g.K / g.group)));
+    rsc = make_rsrc(g.scales, g.s_bytes);
+    rz = make_rsrc(g.zeros, g.z_bytes);
     kblocks = g.K / 128;
     N = g.N;
     group = g.group;
     block0 = n0 / 16;
     kt0 = kt_first;
+    sor = g.sor;
+    wxor = g.wxor;
+    zxor = g.zxor;
   }
 
   __device__ __forceinline__ void load(int kt_local, Regs& rg) const {
@@ -524,9 +591,10 @@ struct W4Loader {
       const int nb = e / 64, L = e % 64;
       const int row = nb * 16 + (L % 16), h = L / 16;
       const uint32_t n = (block0 + nb) * 16 + (L % 16);
-      const f16x2 ss = scale_pair(rg.s[i] & 0xffffu), zz = zero_pair((rg.z[i] >> ((n & 1) * 4)) & 15u);
+      const uint32_t sb = (rg.s[i] & 0xffffu) | sor, z = ((rg.z[i] >> ((n & 1) * 4)) & 15u) ^ zxor;
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) *(u32x4*)(lds + Cfg::off(row, 4 * jj + h)) = dequant8(rg.w[i][jj], zz, ss);
+      for (int jj = 0; jj < 2; ++jj)
+        *(u32x4*)(lds + Cfg::off(row, 4 * jj + h)) = dequant8_dt<DT>(rg.w[i][jj] ^ wxor, sb, z);
     }
   }
 };
@@ -853,10 +921,6 @@ __device__ __forceinline__ void mainloop(char* lds, const ALd& al, const BLd& bl
 // of one row, touch all 64 banks once.  Rows past M are dropped by the
 // store's buffer range; a tile that crosses N stores element by element.
 // ---------------------------------------------------------------------------
-template <int DT>
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-  return to_bits<DT>(a) | (to_bits<DT>(b) << 16);
-}
 
 template <class Cfg, int DT>
 __device__ __forceinline__ void store_tile(const Tile& t, const f32x16 (&acc)[Cfg::TM][Cfg::TN], float alpha,

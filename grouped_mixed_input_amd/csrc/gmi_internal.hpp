@@ -68,11 +68,18 @@ struct ConvLaunch {
 
 struct W4Launch {
   int M, N, K, group;
+  int dt;  // DT_F16 or DT_BF16: X, the scales and Y
   const uint16_t* X;
   int64_t ldx;
   const uint8_t* w;
   const uint16_t* scales;
   const uint8_t* zeros;
+  // Conversion mode, applied as the values are read: missing scales or zero
+  // points get a zero-sized buffer range (every read returns 0).
+  uint32_t s_bytes, z_bytes;  // buffer ranges of scales and zeros
+  uint32_t sor;               // OR-ed into every scale: the type's 1.0 without scales, else 0
+  uint32_t wxor;              // XOR on every weight word: 0x88888888 for int4 (to offset binary), else 0
+  uint32_t zxor;              // XOR on every zero point: 8 for int4 (the constant 8 without zeros), else 0
   uint16_t* Y;
   int64_t ldy;
   int split;       // k-ranges per output tile (1: no split)

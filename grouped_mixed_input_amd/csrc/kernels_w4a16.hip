@@ -84,8 +84,8 @@ __device__ __forceinline__ void skinny_load(SkinnyStage<NB, MT>& st, const W4Lau
     const uint32_t blk = n_base / 16 + nb, n = blk * 16 + r;
     const bool ok = n < N;
     st.w[nb] = buf_load16(rs.w, ok ? (blk * rs.kblocks + kb) * 1024u + lane * 16u : OOB);
-    const uint32_t s = buf_load2(rs.s, ok ? (grp * N + n) * 2u : OOB);
-    const uint32_t z = (buf_load1(rs.z, ok ? grp * (N / 2) + n / 2 : OOB) >> ((n & 1) * 4)) & 15u;
+    const uint32_t s = buf_load2(rs.s, ok ? (grp * N + n) * 2u : OOB) | a.sor;
+    const uint32_t z = ((buf_load1(rs.z, ok ? grp * (N / 2) + n / 2 : OOB) >> ((n & 1) * 4)) & 15u) ^ a.zxor;
     st.sz[nb] = s | (z << 16);
   }
 #pragma unroll
@@ -97,21 +97,20 @@ __device__ __forceinline__ void skinny_load(SkinnyStage<NB, MT>& st, const W4Lau
   }
 }
 
-template <int NB, int MT>
-__device__ __forceinline__ void skinny_mma(const SkinnyStage<NB, MT>& st, f32x4 (&acc)[NB][MT]) {
+template <int DT, int NB, int MT>
+__device__ __forceinline__ void skinny_mma(const SkinnyStage<NB, MT>& st, uint32_t wxor, f32x4 (&acc)[NB][MT]) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const f16x2 ss = scale_pair(st.sz[nb] & 0xffffu), zz = zero_pair(st.sz[nb] >> 16);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const u32x4 wf = dequant8(st.w[nb][j], zz, ss);
+      const u32x4 wf = dequant8_dt<DT>(st.w[nb][j] ^ wxor, st.sz[nb] & 0xffffu, st.sz[nb] >> 16);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = mfma16<DT_F16>(wf, st.x[mt][j], acc[nb][mt]);
+      for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = mfma16<DT>(wf, st.x[mt][j], acc[nb][mt]);
     }
   }
 }
 
-template <int NB, int KW, int MT>
+template <int DT, int NB, int KW, int MT>
 __global__ __launch_bounds__(64 * KW) void k_w4a16_skinny(W4Launch a) {
   __shared__ f32x4 red[KW][NB * MT * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -130,15 +129,15 @@ __global__ __launch_bounds__(64 * KW) void k_w4a16_skinny(W4Launch a) {
   SkinnyRes rs;
   rs.w = make_rsrc(a.w, (uint32_t)((int64_t)a.N * a.K / 2));
   rs.x = make_rsrc(a.X, (uint32_t)((int64_t)a.M * a.ldx * 2));
-  rs.s = make_rsrc(a.scales, (uint32_t)((int64_t)a.N * (a.K / a.group) * 2));
-  rs.z = make_rsrc(a.zeros, (uint32_t)((int64_t)a.N / 2 * (a.K / a.group)));
+  rs.s = make_rsrc(a.scales, a.s_bytes);
+  rs.z = make_rsrc(a.zeros, a.z_bytes);
   rs.kblocks = kblocks;
   if (kb0 < kb1) {
     SkinnyStage<NB, MT> cur, nxt;
     skinny_load<NB, MT>(cur, a, rs, n_base, kb0, lane);
     for (int kb = kb0; kb < kb1; ++kb) {
       if (kb + 1 < kb1) skinny_load<NB, MT>(nxt, a, rs, n_base, kb + 1, lane);
-      skinny_mma<NB, MT>(cur, acc);
+      skinny_mma<DT, NB, MT>(cur, a.wxor, acc);
       cur = nxt;
     }
   }
@@ -157,8 +156,7 @@ __global__ __launch_bounds__(64 * KW) void k_w4a16_skinny(W4Launch a) {
     const int nb = idx / (MT * 64), mt = (idx / 64) % MT, q = idx % 64;
     const int n = n_base + nb * 16 + 4 * (q / 16), tok = mt * 16 + (q % 16);
     if (tok < a.M && n < a.N) {
-      *(gu32x2*)(a.Y + (int64_t)tok * a.ldy + n) = u32x2{to_bits<DT_F16>(s[0]) | (to_bits<DT_F16>(s[1]) << 16),
-                                                        to_bits<DT_F16>(s[2]) | (to_bits<DT_F16>(s[3]) << 16)};
+      *(gu32x2*)(a.Y + (int64_t)tok * a.ldy + n) = u32x2{pack2<DT>(s[0], s[1]), pack2<DT>(s[2], s[3])};
     }
   }
 }
@@ -200,7 +198,7 @@ struct DecodeLds {
   static_assert(R * 4 <= 64, "one copy instruction carries a round's scale rows");
 };
 
-template <int NB, int KW, int R>
+template <int DT, int NB, int KW, int R>
 __global__ __launch_bounds__(64 * KW) void k_w4a16_decode(W4Launch a) {
   using L = DecodeLds<NB, R>;
   __shared__ __attribute__((aligned(16))) char lds[KW * L::WAVE];
@@ -217,8 +215,9 @@ __global__ __launch_bounds__(64 * KW) void k_w4a16_decode(W4Launch a) {
 
   const rsrc_t rw = make_rsrc(a.w, (uint32_t)((int64_t)a.N * a.K / 2));
   const rsrc_t rx = make_rsrc(a.X, (uint32_t)((int64_t)a.M * a.ldx * 2));
-  const rsrc_t rs = make_rsrc(a.scales, (uint32_t)((int64_t)a.N * (a.K / a.group) * 2));
-  const rsrc_t rz = make_rsrc(a.zeros, (uint32_t)((int64_t)a.N / 2 * (a.K / a.group)));
+  const rsrc_t rs = make_rsrc(a.scales, a.s_bytes);
+  const rsrc_t rz = make_rsrc(a.zeros, a.z_bytes);
+  const uint32_t sor2 = a.sor * 0x00010001u;
   const uint32_t r = lane & 15, h = lane >> 4;
   const bool tok_ok = (int)r < a.M;
   uint32_t magic = 0x64006400u;  // fp16 pair (1024, 1024): 1024 + q for a nibble q in the low mantissa bits
@@ -262,18 +261,25 @@ __global__ __launch_bounds__(64 * KW) void k_w4a16_decode(W4Launch a) {
         for (int nb = 0; nb < NB; ++nb) {
           // the MFMA takes the exact integers q - z of weight row `row`; the
           // group scale of each output row multiplies the fp32 partial sum
-          const u32x4 wq = *(const u32x4*)(wring + s * L::WSLOT + nb * 1024 + lane * 16);
+          const u32x4 wq = *(const u32x4*)(wring + s * L::WSLOT + nb * 1024 + lane * 16) ^ a.wxor;
           const int row = nb * 16 + r;
-          const uint32_t zbits = (*(const uint8_t*)(szb + 1024 + s * 16 + row / 2) >> ((row & 1) * 4)) & 15u;
-          const f16x2 zz = zero_pair(zbits);
+          const uint32_t zbits =
+              ((*(const uint8_t*)(szb + 1024 + s * 16 + row / 2) >> ((row & 1) * 4)) & 15u) ^ a.zxor;
           f32x4 part = {0, 0, 0, 0};
+          if constexpr (DT == DT_F16) {
+            const f16x2 zz = zero_pair(zbits);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) part = mfma16<DT_F16>(unpack8_minus_zero(wq[j], zz, magic), x[s][j], part);
+            for (int j = 0; j < 4; ++j) part = mfma16<DT>(unpack8_minus_zero(wq[j], zz, magic), x[s][j], part);
+          } else {
+            const float zf = (float)zbits;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) part = mfma16<DT>(unpack8_minus_zero_bf16(wq[j], zf), x[s][j], part);
+          }
           // output rows of this lane: nb * 16 + 4 h + {0..3}
-          const u32x2 sc = *(const u32x2*)(szb + s * 64 + (nb * 16 + 4 * h) * 2);
+          const u32x2 sc = *(const u32x2*)(szb + s * 64 + (nb * 16 + 4 * h) * 2) | sor2;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            acc[nb][i] = __builtin_fmaf(from_bits<DT_F16>((sc[i / 2] >> (16 * (i % 2))) & 0xffffu), part[i],
+            acc[nb][i] = __builtin_fmaf(from_bits<DT>((sc[i / 2] >> (16 * (i % 2))) & 0xffffu), part[i],
                                         acc[nb][i]);
         }
       }
@@ -293,8 +299,7 @@ __global__ __launch_bounds__(64 * KW) void k_w4a16_decode(W4Launch a) {
     const int nb = idx / 64, q = idx % 64;
     const int n = n_base + nb * 16 + 4 * (q / 16), tok = q % 16;
     if (tok < a.M && n < a.N)
-      *(gu32x2*)(a.Y + (int64_t)tok * a.ldy + n) = u32x2{to_bits<DT_F16>(t[0]) | (to_bits<DT_F16>(t[1]) << 16),
-                                                        to_bits<DT_F16>(t[2]) | (to_bits<DT_F16>(t[3]) << 16)};
+      *(gu32x2*)(a.Y + (int64_t)tok * a.ldy + n) = u32x2{pack2<DT>(t[0], t[1]), pack2<DT>(t[2], t[3])};
   }
 }
 
@@ -332,11 +337,11 @@ __device__ __forceinline__ void store_partial(const Tile& t, const f32x16 (&acc)
 // into Y; split, the fp32 partial goes to partial[s] and k_w4a16_sum adds
 // the ranges afterwards.  The ranges of a tile are consecutive work items,
 // so they run in one XCD round and share the tile's X panel in its L2.
-template <class Cfg>
+template <class Cfg, int DT>
 __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_w4a16_tiled(W4Launch a, int tiles_m, int total_work) {
   __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
   const int G = gridDim.x;
-  const W4Geom g{a.w, a.scales, a.zeros, a.N, a.K, a.group};
+  const W4Geom g{a.w, a.scales, a.zeros, a.N, a.K, a.group, a.s_bytes, a.z_bytes, a.sor, a.wxor, a.zxor};
   const int Ks = a.K / a.split;
   for (int base = 0; base < total_work; base += G) {
     const int work = base + remap_slot(blockIdx.x, G);
@@ -354,19 +359,20 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_w4a16_tiled(W
     t.D = a.Y;
     t.ldd = a.ldy;
     DenseLoader<Cfg, Cfg::BM> al;
-    W4Loader<Cfg, Cfg::BN> bl;
+    W4Loader<Cfg, Cfg::BN, DT> bl;
     al.init(a.X + k0, a.ldx, t.m0, t.M, Ks);
     bl.init(g, t.n0, k0 / Cfg::BK);
     f32x16 acc[Cfg::TM][Cfg::TN];
-    mainloop<Cfg, DT_F16>(lds, al, bl, Ks / Cfg::BK, acc);
+    mainloop<Cfg, DT>(lds, al, bl, Ks / Cfg::BK, acc);
     if (a.split == 1)
-      store_tile<Cfg, DT_F16>(t, acc, 1.0f, 0.0f, lds);
+      store_tile<Cfg, DT>(t, acc, 1.0f, 0.0f, lds);
     else
       store_partial<Cfg>(t, acc, a.partial + (int64_t)sidx * a.M * a.N);
   }
 }
 
-// Y = RN16(sum over s of partial[s]) in s order: 8 consecutive n per thread
+// Y = RN(sum over s of partial[s]) in s order: 8 consecutive n per thread
+template <int DT>
 __global__ __launch_bounds__(256) void k_w4a16_sum(const float* __restrict__ P, int split, int M, int N,
                                                    uint16_t* __restrict__ Y, int64_t ldy) {
   const int64_t groups = (int64_t)M * N / 8;
@@ -381,8 +387,7 @@ __global__ __launch_bounds__(256) void k_w4a16_sum(const float* __restrict__ P, 
       hi += *(const f32x4*)(P + s * plane + e + 4);
     }
     *(u32x4*)(Y + (int64_t)m * ldy + n) =
-        u32x4{to_bits<DT_F16>(lo[0]) | (to_bits<DT_F16>(lo[1]) << 16), to_bits<DT_F16>(lo[2]) | (to_bits<DT_F16>(lo[3]) << 16),
-              to_bits<DT_F16>(hi[0]) | (to_bits<DT_F16>(hi[1]) << 16), to_bits<DT_F16>(hi[2]) | (to_bits<DT_F16>(hi[3]) << 16)};
+        u32x4{pack2<DT>(lo[0], lo[1]), pack2<DT>(lo[2], lo[3]), pack2<DT>(hi[0], hi[1]), pack2<DT>(hi[2], hi[3])};
   }
 }
 
@@ -405,19 +410,21 @@ int w4a16_split(int M, int N, int K) {
   return split;
 }
 
-hipError_t launch_w4a16(const W4Launch& a, hipStream_t stream) {
+template <int DT>
+static hipError_t launch_w4a16_dt(const W4Launch& a, hipStream_t stream) {
   if (a.M <= 16) {
     constexpr int NB = 2, KW = 8, R = 8;
-    hipLaunchKernelGGL((k_w4a16_decode<NB, KW, R>), dim3((a.N + NB * 16 - 1) / (NB * 16)), dim3(64 * KW), 0, stream, a);
+    hipLaunchKernelGGL((k_w4a16_decode<DT, NB, KW, R>), dim3((a.N + NB * 16 - 1) / (NB * 16)), dim3(64 * KW), 0,
+                       stream, a);
     return hipGetLastError();
   }
   if (a.M <= 64) {
     constexpr int NB = 2, KW = 8;
     const dim3 grid((a.N + NB * 16 - 1) / (NB * 16)), block(64 * KW);
     if (a.M <= 32)
-      hipLaunchKernelGGL((k_w4a16_skinny<NB, KW, 2>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((k_w4a16_skinny<DT, NB, KW, 2>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((k_w4a16_skinny<NB, KW, 4>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((k_w4a16_skinny<DT, NB, KW, 4>), grid, block, 0, stream, a);
     return hipGetLastError();
   }
   const int cus = device_cu_count();
@@ -429,19 +436,25 @@ hipError_t launch_w4a16(const W4Launch& a, hipStream_t stream) {
   int grid = (total + XCDS - 1) / XCDS * XCDS;
   if (grid > resident) grid = resident / XCDS * XCDS;
   if (big)
-    hipLaunchKernelGGL((k_w4a16_tiled<W4Cfg256>), dim3(grid), dim3(W4Cfg256::THREADS), 0, stream, a, tiles_m, total);
+    hipLaunchKernelGGL((k_w4a16_tiled<W4Cfg256, DT>), dim3(grid), dim3(W4Cfg256::THREADS), 0, stream, a, tiles_m,
+                       total);
   else
-    hipLaunchKernelGGL((k_w4a16_tiled<W4Cfg128>), dim3(grid), dim3(W4Cfg128::THREADS), 0, stream, a, tiles_m, total);
+    hipLaunchKernelGGL((k_w4a16_tiled<W4Cfg128, DT>), dim3(grid), dim3(W4Cfg128::THREADS), 0, stream, a, tiles_m,
+                       total);
   if (a.split > 1) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t groups = (int64_t)a.M * a.N / 8;
     int64_t blocks = (groups + 255) / 256;
     if (blocks > 4 * cus) blocks = 4 * cus;
-    hipLaunchKernelGGL(k_w4a16_sum, dim3((unsigned)blocks), dim3(256), 0, stream, a.partial, a.split, a.M, a.N, a.Y,
-                       a.ldy);
+    hipLaunchKernelGGL(k_w4a16_sum<DT>, dim3((unsigned)blocks), dim3(256), 0, stream, a.partial, a.split, a.M, a.N,
+                       a.Y, a.ldy);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_w4a16(const W4Launch& a, hipStream_t stream) {
+  return a.dt == DT_BF16 ? launch_w4a16_dt<DT_BF16>(a, stream) : launch_w4a16_dt<DT_F16>(a, stream);
 }
 
 }  // namespace gmi

@@ -198,6 +198,34 @@ gmi_status gmi_gemm_w4a16(int32_t M, int32_t N, int32_t K, const void* X, int64_
                           const void* scales, const uint8_t* zeros, int32_t group_size, void* Y, int64_t ldy,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* 4-bit weight element types: GMI_W4_UINT4 holds 0..15, GMI_W4_INT4 holds
+ * -8..7 in two's complement (nibble 8 is -8).  Both are stored and prepacked
+ * alike (gmi_prepack_w4 moves nibbles and never reads their values). */
+typedef enum { GMI_W4_UINT4 = 0, GMI_W4_INT4 = 1 } gmi_w4_type;
+
+/* Mixed-input GEMM Y = X W^T in each conversion mode of machete_mainloop.cuh
+ * (ConversionMode, chosen there by which of scale and zero types is void):
+ *   DirectConvert            scales == NULL, zeros == NULL: w = v(q)
+ *   ConvertAndScale          zeros == NULL:                 w = v(q) * s[k/g][n]
+ *   ConvertAndScaleWithZero  both given:                    w = (v(q) - v(z[k/g][n])) * s[k/g][n]
+ * where v() is the value of a 4-bit element of type `w_type`; the zero
+ * points have the weight's type and are subtracted before the scale, as in
+ * gmi_gemm_w4a16 (which is this call with fp16, uint4 and both arrays).
+ * Zero points without scales are GMI_ERR_UNSUPPORTED (no such mode).
+ *   x_dtype      GMI_F16 or GMI_BF16: the type of X, of the scales and of Y
+ *                (the page's fp16 and bf16 activation / scale types).
+ *   group_size   as for gmi_gemm_w4a16; ignored when scales == NULL.
+ *   other arguments, layouts, workspace and errors as for gmi_gemm_w4a16.
+ * Numerics: for M <= 16 the matrix instruction takes the exact integers
+ * v(q) - v(z) in the activation type and the scale multiplies each group's
+ * fp32 partial sum; otherwise every weight is first rounded to the
+ * activation type, RN((v(q) - v(z)) * s).  fp32 accumulation; Y is rounded to
+ * nearest even. */
+gmi_status gmi_gemm_mixed(int32_t M, int32_t N, int32_t K, gmi_dtype x_dtype, const void* X, int64_t ldx,
+                          const uint8_t* w_prepacked, gmi_w4_type w_type, const void* scales, const uint8_t* zeros,
+                          int32_t group_size, void* Y, int64_t ldy, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* Implicit-GEMM conv2d forward (cross-correlation, groups == 1):
  *   y[n][p][q][k] = alpha * sum_{r,s,c} x[n][p*sh - ph + r*dh][q*sw - pw + s*dw][c] * w[k][r][s][c]
  *                   + beta * c_in[n][p][q][k]

@@ -32,7 +32,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ["gmi_gemm_grouped", "gmi_gemm_ptr_array", "gmi_prepack_w4", "gmi_gemm_w4a16",
                  "gmi_conv2d_fprop_implicit", "gmi_workspace_bytes", "gmi_prepack_w4_bytes", "gmi_last_error",
-                 "gmi_gemm_grouped_offsets", "gmi_w4a16_workspace_bytes"]:
+                 "gmi_gemm_grouped_offsets", "gmi_w4a16_workspace_bytes", "gmi_gemm_mixed"]:
         assert want in names
 
 
@@ -172,6 +172,23 @@ def test_w4a16_validation(gmi):
     # a workspace that would enable the split must be 16-byte aligned
     need = gmi.lib().gmi_w4a16_workspace_bytes(128, 8192, 8192)
     assert _w4(gmi, M=128, N=8192, K=8192, ldx=8192, ldy=8192, ws=A16 + 4, ws_bytes=need) == gmi.GMI_ERR_MISALIGNED
+
+
+def _mixed(gmi, M=16, N=64, K=256, xdt=1, X=A16, ldx=256, W=A16 * 2, wt=1, S=A16 * 3, Z=A16 * 4, g=128, Y=A16 * 5,
+           ldy=64):
+    return gmi.lib().gmi_gemm_mixed(M, N, K, xdt, X, ldx, W, wt, S, Z, g, Y, ldy, None, 0, None)
+
+
+def test_mixed_validation(gmi):
+    assert _mixed(gmi, xdt=2) == gmi.GMI_ERR_UNSUPPORTED  # fp8 activations: not a mixed-input type here
+    assert _mixed(gmi, wt=2) == gmi.GMI_ERR_UNSUPPORTED
+    assert _mixed(gmi, S=None) == gmi.GMI_ERR_UNSUPPORTED  # zero points without scales
+    assert _mixed(gmi, g=96) == gmi.GMI_ERR_INVALID_ARG
+    assert _mixed(gmi, N=24) == gmi.GMI_ERR_UNSUPPORTED
+    assert _mixed(gmi, W=None) == gmi.GMI_ERR_INVALID_ARG
+    assert _mixed(gmi, Z=A16 + 4) == gmi.GMI_ERR_MISALIGNED
+    assert _mixed(gmi, S=None, Z=None, ldy=60) == gmi.GMI_ERR_INVALID_ARG  # reaches the shape checks
+    assert _mixed(gmi, M=0, S=None, Z=None, g=0) == gmi.GMI_OK  # group size unused without scales
 
 
 def test_w4a16_workspace_bytes(gmi):

@@ -198,3 +198,23 @@ def test_grouped_mixed_tile_classes(gmi, K):
     assert sum((M + 255) // 256 * 4 for M, _, _ in shapes) >= 256
     for got, ref, shp in run_grouped(gmi, shapes, "bf16", 1.5, 0.5, seed=K, ld_pad=8):
         check_close(got, ref, "bf16", f"grouped tile classes {shp}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_output_rounding_is_nearest_even(gmi, dtype):
+    # D = A B with A rows [1, t, 0 ...] and B columns [1, 1, 0 ...]: 1 + t exactly in the fp32 accumulator, on,
+    # above and below the midpoint of two representable values; the stored bits must be the oracle's RNE
+    ties = {"f16": [3 * 2.0**-11, 2.0**-11, 2.0**-11 + 2.0**-16, 3 * 2.0**-11 - 2.0**-16],
+            "bf16": [3 * 2.0**-8, 2.0**-8, 2.0**-8 + 2.0**-14, 3 * 2.0**-8 - 2.0**-14]}[dtype]
+    M, N, K = 64, 64, 8
+    a = np.zeros((M, K), np.float32)
+    a[:, 0], a[:, 1] = 1.0, np.resize(np.array(ties, np.float32), M)
+    b = np.zeros((N, K), np.float32)
+    b[:, :2] = 1.0
+    A, B = gi.to_bits(a, dtype), gi.to_bits(b, dtype)
+    G = Guarded(M, N, N, dtype)
+    gmi.gemm_grouped([to_dev(A, dtype)], [to_dev(B, dtype)], None, [G.view])
+    torch.cuda.synchronize()
+    ref = oracle.gemm(A, B, dtype=dtype)
+    assert np.array_equal(ref, np.repeat(1.0 + a[:, 1:2].astype(np.float64), N, axis=1))
+    assert np.array_equal(G.bits(), oracle.round_to(ref, dtype))
