@@ -72,6 +72,9 @@ def lib() -> ctypes.CDLL:
     L.gmi_gemm_mixed.restype = ctypes.c_int
     L.gmi_gemm_mixed.argtypes = [_i32, _i32, _i32, ctypes.c_int, _p, _i64, _p, ctypes.c_int, _p, _p, _i32, _p, _i64,
                                  _p, _sz, _p]
+    L.gmi_gemm_mixed_grouped.restype = ctypes.c_int
+    L.gmi_gemm_mixed_grouped.argtypes = [_i32, _p, _i32, _i32, _i32, ctypes.c_int, _p, _i64, _p, _i64, ctypes.c_int,
+                                         _p, _i64, _p, _i64, _i32, _p, _i64, _p]
     L.gmi_w4a16_workspace_bytes.restype = _sz
     L.gmi_w4a16_workspace_bytes.argtypes = [_i32, _i32, _i32]
     L.gmi_conv2d_fprop_implicit.restype = ctypes.c_int
@@ -226,6 +229,26 @@ def gemm_mixed(X: torch.Tensor, w_prepacked: torch.Tensor, scales: torch.Tensor 
                                 W4_TYPES[w_type], _ptr(scales), _ptr(zeros), group_size, Y.data_ptr(), _ld(Y),
                                 workspace.data_ptr() if workspace.numel() else None, workspace.numel(),
                                 _stream(stream)))
+    return Y
+
+
+def gemm_mixed_grouped(offsets: torch.Tensor, X: torch.Tensor, w_prepacked: torch.Tensor,
+                       scales: torch.Tensor | None, zeros: torch.Tensor | None, group_size: int, N: int,
+                       w_type: str = "uint4", Y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Per-group Y_g = X_g W_g^T (mixture of experts): rows offsets[g] .. offsets[g+1] of X [rows][K] and Y
+    [rows][N]; w_prepacked [groups][N*K/2] (each row a gmi_prepack_w4 output), scales [groups][K/g][N] or
+    None, zeros [groups][K/g][N/2] or None.  `offsets` is a device int32 tensor of groups + 1 entries."""
+    rows, K = X.shape
+    count = w_prepacked.shape[0]
+    if offsets.dtype != torch.int32 or offsets.numel() != count + 1 or not offsets.is_contiguous():
+        raise ValueError("offsets must be a contiguous int32 vector of groups + 1 entries")
+    if Y is None:
+        Y = torch.empty((rows, N), dtype=X.dtype, device=X.device)
+    _check(lib().gmi_gemm_mixed_grouped(count, offsets.data_ptr(), rows, N, K, _DT[X.dtype], X.data_ptr(), _ld(X),
+                                        w_prepacked.data_ptr(), w_prepacked.stride(0), W4_TYPES[w_type],
+                                        _ptr(scales), scales.stride(0) if scales is not None else 0, _ptr(zeros),
+                                        zeros.stride(0) if zeros is not None else 0, group_size, Y.data_ptr(),
+                                        _ld(Y), _stream(stream)))
     return Y
 
 

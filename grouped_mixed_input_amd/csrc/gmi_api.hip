@@ -320,10 +320,15 @@ size_t gmi_w4a16_workspace_bytes(int32_t M, int32_t N, int32_t K) {
 // Shared by the two mixed-input entry points: every rule checked, then one
 // launch.  `scales` NULL is the direct conversion (no scale), `zeros` NULL the
 // conversion without zero point.
-static gmi_status mixed_gemm(const char* who, int32_t M, int32_t N, int32_t K, gmi_dtype x_dtype, const void* X,
-                             int64_t ldx, const uint8_t* w_prepacked, gmi_w4_type w_type, const void* scales,
-                             const uint8_t* zeros, int32_t group_size, void* Y, int64_t ldy, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+// Checks shared by the mixed-input entry points and the launch record they
+// fill (M, split and partial are the caller's).  `M` is the row count, or
+// for the grouped call the row capacity.  Returns GMI_OK with `nothing` set
+// when there is no work.
+static gmi_status mixed_prepare(const char* who, int32_t M, int32_t N, int32_t K, gmi_dtype x_dtype, const void* X,
+                                int64_t ldx, const uint8_t* w_prepacked, gmi_w4_type w_type, const void* scales,
+                                const uint8_t* zeros, int32_t group_size, void* Y, int64_t ldy, W4Launch& a,
+                                bool& nothing) {
+  nothing = false;
   if (M < 0 || N < 0 || K < 0) return fail(GMI_ERR_INVALID_ARG, "%s: negative size (%d, %d, %d)", who, M, N, K);
   if (!dtype_ok(x_dtype)) return fail(GMI_ERR_UNSUPPORTED, "%s: activation type %d not supported", who, (int)x_dtype);
   if (w_type != GMI_W4_UINT4 && w_type != GMI_W4_INT4)
@@ -340,14 +345,16 @@ static gmi_status mixed_gemm(const char* who, int32_t M, int32_t N, int32_t K, g
     return fail(GMI_ERR_UNSUPPORTED, "%s: group_size must equal K or be a multiple of 128", who);
   if ((int64_t)N * K / 2 > INT32_MAX || (int64_t)M * ldx * 2 > INT32_MAX || ldy > kMaxLd)
     return fail(GMI_ERR_UNSUPPORTED, "%s: W (N*K/2 bytes) and X (M*ldx*2 bytes) must stay below 2^31 bytes", who);
-  if (M == 0 || N == 0) return GMI_OK;
+  if (M == 0 || N == 0) {
+    nothing = true;
+    return GMI_OK;
+  }
   if (!Y || (K > 0 && (!X || !w_prepacked))) return fail(GMI_ERR_INVALID_ARG, "%s: NULL pointer", who);
   if ((K > 0 && ldx < K) || ldy < N) return fail(GMI_ERR_INVALID_ARG, "%s: ldx < K or ldy < N", who);
   if (!aligned16(Y) || ldy % 8 ||
       (K > 0 && (!aligned16(X) || !aligned16(w_prepacked) || (scales && !aligned16(scales)) ||
                  (zeros && !aligned16(zeros)) || ldx % 8)))
     return fail(GMI_ERR_MISALIGNED, "%s: pointers must be 16-byte aligned, ld multiples of 8", who);
-  W4Launch a;
   a.M = M;
   a.N = N;
   a.K = K;
@@ -371,6 +378,18 @@ static gmi_status mixed_gemm(const char* who, int32_t M, int32_t N, int32_t K, g
   a.ldy = ldy;
   a.split = 1;
   a.partial = nullptr;
+  return GMI_OK;
+}
+
+static gmi_status mixed_gemm(const char* who, int32_t M, int32_t N, int32_t K, gmi_dtype x_dtype, const void* X,
+                             int64_t ldx, const uint8_t* w_prepacked, gmi_w4_type w_type, const void* scales,
+                             const uint8_t* zeros, int32_t group_size, void* Y, int64_t ldy, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  W4Launch a;
+  bool nothing;
+  const gmi_status st = mixed_prepare(who, M, N, K, x_dtype, X, ldx, w_prepacked, w_type, scales, zeros, group_size,
+                                      Y, ldy, a, nothing);
+  if (st != GMI_OK || nothing) return st;
   const size_t need = gmi_w4a16_workspace_bytes(M, N, K);
   if (need > 0 && workspace && workspace_bytes >= need) {
     if (!aligned16(workspace)) return fail(GMI_ERR_MISALIGNED, "%s: workspace must be 16-byte aligned", who);
@@ -387,6 +406,43 @@ gmi_status gmi_gemm_w4a16(int32_t M, int32_t N, int32_t K, const void* X, int64_
   if (M > 0 && N > 0 && K > 0 && (!scales || !zeros)) return fail(GMI_ERR_INVALID_ARG, "gemm_w4a16: NULL pointer");
   return mixed_gemm("gemm_w4a16", M, N, K, GMI_F16, X, ldx, w_prepacked, GMI_W4_UINT4, scales, zeros, group_size,
                     Y, ldy, workspace, workspace_bytes, stream);
+}
+
+gmi_status gmi_gemm_mixed_grouped(int32_t count, const int32_t* offsets, int32_t rows, int32_t N, int32_t K,
+                                  gmi_dtype x_dtype, const void* X, int64_t ldx, const uint8_t* w_prepacked,
+                                  int64_t w_stride, gmi_w4_type w_type, const void* scales, int64_t s_stride,
+                                  const uint8_t* zeros, int64_t z_stride, int32_t group_size, void* Y, int64_t ldy,
+                                  void* stream) {
+  g_last_error.clear();
+  const char* who = "gemm_mixed_grouped";
+  if (count < 0) return fail(GMI_ERR_INVALID_ARG, "%s: count %d < 0", who, count);
+  if (count > 65535) return fail(GMI_ERR_UNSUPPORTED, "%s: %d groups, at most 65535", who, count);
+  if (count == 0) return GMI_OK;
+  W4Launch a;
+  bool nothing;
+  gmi_status st = mixed_prepare(who, rows, N, K, x_dtype, X, ldx, w_prepacked, w_type, scales, zeros, group_size, Y,
+                                ldy, a, nothing);
+  if (st != GMI_OK) return st;
+  if (nothing) return GMI_OK;
+  if (!offsets) return fail(GMI_ERR_INVALID_ARG, "%s: offsets is NULL", who);
+  if ((uintptr_t)offsets & 3u) return fail(GMI_ERR_MISALIGNED, "%s: offsets must be 4-byte aligned", who);
+  const int64_t w_bytes = (int64_t)N * K / 2;
+  if (w_stride < 0 || s_stride < 0 || z_stride < 0)
+    return fail(GMI_ERR_INVALID_ARG, "%s: negative group stride", who);
+  if (count > 1 && (w_stride < w_bytes || (scales && s_stride < (int64_t)a.s_bytes / 2) ||
+                    (zeros && z_stride < (int64_t)a.z_bytes)))
+    return fail(GMI_ERR_INVALID_ARG, "%s: a group stride is smaller than one group's data", who);
+  if (w_stride % 16 || (s_stride * 2) % 16 || z_stride % 16)
+    return fail(GMI_ERR_MISALIGNED, "%s: group strides must keep every group's data 16-byte aligned", who);
+  W4Grouped gq;
+  gq.base = a;
+  gq.offsets = offsets;
+  gq.count = count;
+  gq.rows = rows;
+  gq.w_stride = w_stride;
+  gq.s_stride = scales ? s_stride : 0;
+  gq.z_stride = zeros ? z_stride : 0;
+  return hip_status(launch_w4a16_grouped(gq, (hipStream_t)stream), who);
 }
 
 gmi_status gmi_gemm_mixed(int32_t M, int32_t N, int32_t K, gmi_dtype x_dtype, const void* X, int64_t ldx,

@@ -86,6 +86,18 @@ struct W4Launch {
   float* partial;  // split > 1: fp32 [split][M][N] partial products
 };
 
+// Grouped (mixture-of-experts) mixed-input launch: group g owns rows
+// [offsets[g], offsets[g + 1]) of X and Y (clipped to [0, rows)) and its own
+// weight, scales and zero points at base + g * stride (bytes for the weight
+// and the zeros, elements for the scales).  `base` carries every shared field;
+// its M is unused.
+struct W4Grouped {
+  W4Launch base;
+  const int32_t* offsets;
+  int count, rows;
+  int64_t w_stride, s_stride, z_stride;
+};
+
 int device_cu_count();  // cached per device
 // k-ranges per output tile the W4A16 GEMM uses for this shape on the current
 // device (1 when the tiles alone fill the device or the path is skinny)
@@ -100,5 +112,6 @@ hipError_t launch_ptr_array(const PtrArrayLaunch& a, int shape, int dtype, float
 hipError_t launch_conv_fprop(const ConvLaunch& a, int shape, int dtype, float alpha, float beta, hipStream_t stream);
 hipError_t launch_prepack_w4(const uint8_t* w, int N, int K, uint8_t* out, hipStream_t stream);
 hipError_t launch_w4a16(const W4Launch& a, hipStream_t stream);
+hipError_t launch_w4a16_grouped(const W4Grouped& a, hipStream_t stream);
 
 }  // namespace gmi

@@ -110,11 +110,17 @@ __device__ __forceinline__ void skinny_mma(const SkinnyStage<NB, MT>& st, uint32
   }
 }
 
+template <int NB, int KW, int MT>
+constexpr int skinny_lds_bytes() {
+  return KW * NB * MT * 64 * (int)sizeof(f32x4);
+}
+
+// weight rows n_base .. n_base + 16 NB of Y = X W^T for the a.M <= 16 MT
+// tokens of X; `lds` holds skinny_lds_bytes<NB, KW, MT>() bytes
 template <int DT, int NB, int KW, int MT>
-__global__ __launch_bounds__(64 * KW) void k_w4a16_skinny(W4Launch a) {
-  __shared__ f32x4 red[KW][NB * MT * 64];
+__device__ __forceinline__ void skinny_body(const W4Launch& a, int n_base, char* lds) {
+  f32x4(*red)[NB * MT * 64] = (f32x4(*)[NB * MT * 64])lds;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n_base = blockIdx.x * NB * 16;
   const int kblocks = a.K / 128;
   const int per = (kblocks + KW - 1) / KW;
   const int kb0 = wave * per;
@@ -161,6 +167,12 @@ __global__ __launch_bounds__(64 * KW) void k_w4a16_skinny(W4Launch a) {
   }
 }
 
+template <int DT, int NB, int KW, int MT>
+__global__ __launch_bounds__(64 * KW) void k_w4a16_skinny(W4Launch a) {
+  __shared__ __attribute__((aligned(16))) char lds[skinny_lds_bytes<NB, KW, MT>()];
+  skinny_body<DT, NB, KW, MT>(a, blockIdx.x * NB * 16, lds);
+}
+
 // ---------------------------------------------------------------------------
 // Decode kernel (M <= 16): the weight stream is the whole cost (N K / 2 bytes
 // against 2 M (N + K) for X and Y), so it is put in flight as early and as
@@ -198,14 +210,14 @@ struct DecodeLds {
   static_assert(R * 4 <= 64, "one copy instruction carries a round's scale rows");
 };
 
+// weight rows n_base .. n_base + 16 NB of Y = X W^T for the a.M <= 16
+// tokens of X; `lds` holds KW * DecodeLds<NB, R>::WAVE bytes
 template <int DT, int NB, int KW, int R>
-__global__ __launch_bounds__(64 * KW) void k_w4a16_decode(W4Launch a) {
+__device__ __forceinline__ void decode_body(const W4Launch& a, int n_base, char* lds) {
   using L = DecodeLds<NB, R>;
-  __shared__ __attribute__((aligned(16))) char lds[KW * L::WAVE];
   const int lane = threadIdx.x & 63, wave = wave_id();
   char* wring = lds + wave * L::WAVE;
   char* szb = wring + L::WRING;
-  const int n_base = blockIdx.x * NB * 16;
   const uint32_t N = a.N;
   const int kblocks = a.K / 128;
   const int per = (kblocks + KW - 1) / KW;
@@ -301,6 +313,12 @@ __global__ __launch_bounds__(64 * KW) void k_w4a16_decode(W4Launch a) {
     if (tok < a.M && n < a.N)
       *(gu32x2*)(a.Y + (int64_t)tok * a.ldy + n) = u32x2{pack2<DT>(t[0], t[1]), pack2<DT>(t[2], t[3])};
   }
+}
+
+template <int DT, int NB, int KW, int R>
+__global__ __launch_bounds__(64 * KW) void k_w4a16_decode(W4Launch a) {
+  __shared__ __attribute__((aligned(16))) char lds[KW * DecodeLds<NB, R>::WAVE];
+  decode_body<DT, NB, KW, R>(a, blockIdx.x * NB * 16, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -450,6 +468,49 @@ static hipError_t launch_w4a16_dt(const W4Launch& a, hipStream_t stream) {
     hipLaunchKernelGGL(k_w4a16_sum<DT>, dim3((unsigned)blocks), dim3(256), 0, stream, a.partial, a.split, a.M, a.N,
                        a.Y, a.ldy);
   }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Grouped (mixture-of-experts) kernel: workgroup (x, g) takes weight rows
+// 32 x .. 32 x + 31 of group g over that group's rows, whose count only the
+// device knows -- the decode body for at most 16 rows, else the skinny body
+// 64 rows at a time.  A group with no rows returns at once.
+// ---------------------------------------------------------------------------
+constexpr int kGroupedLds = 8 * DecodeLds<2, 8>::WAVE;
+static_assert(skinny_lds_bytes<2, 8, 4>() <= kGroupedLds, "one LDS block serves both bodies");
+
+template <int DT>
+__global__ __launch_bounds__(512) void k_w4a16_grouped(W4Grouped a) {
+  __shared__ __attribute__((aligned(16))) char lds[kGroupedLds];
+  const int g = blockIdx.y;
+  const int lo = min(max(a.offsets[g], 0), a.rows);
+  const int hi = min(max(a.offsets[g + 1], 0), a.rows);
+  if (hi <= lo) return;
+  W4Launch p = a.base;
+  p.w = a.base.w + g * a.w_stride;
+  p.scales = a.base.scales + g * a.s_stride;
+  p.zeros = a.base.zeros + g * a.z_stride;
+  const int n_base = blockIdx.x * 32;
+  const int chunk = hi - lo <= 16 ? 16 : 64;
+  for (int r0 = lo; r0 < hi; r0 += chunk) {
+    p.M = min(chunk, hi - r0);
+    p.X = a.base.X + (int64_t)r0 * a.base.ldx;
+    p.Y = a.base.Y + (int64_t)r0 * a.base.ldy;
+    if (chunk == 16)
+      decode_body<DT, 2, 8, 8>(p, n_base, lds);
+    else
+      skinny_body<DT, 2, 8, 4>(p, n_base, lds);
+    __syncthreads();  // the next chunk reuses the LDS the reduction just read
+  }
+}
+
+hipError_t launch_w4a16_grouped(const W4Grouped& a, hipStream_t stream) {
+  const dim3 grid((a.base.N + 31) / 32, a.count);
+  if (a.base.dt == DT_BF16)
+    hipLaunchKernelGGL(k_w4a16_grouped<DT_BF16>, grid, dim3(512), 0, stream, a);
+  else
+    hipLaunchKernelGGL(k_w4a16_grouped<DT_F16>, grid, dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 

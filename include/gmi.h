@@ -226,6 +226,34 @@ gmi_status gmi_gemm_mixed(int32_t M, int32_t N, int32_t K, gmi_dtype x_dtype, co
                           int32_t group_size, void* Y, int64_t ldy, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* Grouped mixed-input GEMM, the mixture-of-experts form that combines the
+ * grouped problem list of sm90_gemm_array_tma_warpspecialized_cooperative.hpp
+ * (group sizes held on the device, as for gmi_gemm_grouped_offsets) with the
+ * conversion of machete_mainloop.cuh: group g < count owns rows
+ * [offsets[g], offsets[g + 1]) of X and Y and computes
+ * Y_g = X_g W_g^T with its own weight, scales and zero points:
+ *   W_g = w_prepacked + g * w_stride      (bytes; a gmi_prepack_w4 output of [N][K])
+ *   s_g = scales      + g * s_stride      (elements of x_dtype; [K/group][N])
+ *   z_g = zeros       + g * z_stride      (bytes; [K/group][N/2])
+ *   offsets  device int32 [count + 1], read on the device; ranges are
+ *            clipped to [0, rows) and an empty or reversed one is skipped, so
+ *            no access leaves the buffers; rows outside every group are not
+ *            written.
+ *   rows     host: rows X and Y hold.
+ *   count    0 .. 65535 groups.
+ *   strides  at least one group's data when count > 1 (N*K/2 bytes,
+ *            (K/group)*N scales, (K/group)*N/2 zero bytes) and keeping every
+ *            group's data 16-byte aligned; ignored for a NULL array.
+ * Modes, types, layouts and numerics as for gmi_gemm_mixed; a group of at
+ * most 16 rows takes the M <= 16 kernel body, a larger one is processed 64
+ * rows at a time by the skinny body (weights rounded to the activation type).
+ * No workspace. */
+gmi_status gmi_gemm_mixed_grouped(int32_t count, const int32_t* offsets, int32_t rows, int32_t N, int32_t K,
+                                  gmi_dtype x_dtype, const void* X, int64_t ldx, const uint8_t* w_prepacked,
+                                  int64_t w_stride, gmi_w4_type w_type, const void* scales, int64_t s_stride,
+                                  const uint8_t* zeros, int64_t z_stride, int32_t group_size, void* Y, int64_t ldy,
+                                  void* stream);
+
 /* Implicit-GEMM conv2d forward (cross-correlation, groups == 1):
  *   y[n][p][q][k] = alpha * sum_{r,s,c} x[n][p*sh - ph + r*dh][q*sw - pw + s*dw][c] * w[k][r][s][c]
  *                   + beta * c_in[n][p][q][k]

@@ -32,7 +32,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ["gmi_gemm_grouped", "gmi_gemm_ptr_array", "gmi_prepack_w4", "gmi_gemm_w4a16",
                  "gmi_conv2d_fprop_implicit", "gmi_workspace_bytes", "gmi_prepack_w4_bytes", "gmi_last_error",
-                 "gmi_gemm_grouped_offsets", "gmi_w4a16_workspace_bytes", "gmi_gemm_mixed"]:
+                 "gmi_gemm_grouped_offsets", "gmi_w4a16_workspace_bytes", "gmi_gemm_mixed",
+                 "gmi_gemm_mixed_grouped"]:
         assert want in names
 
 
@@ -189,6 +190,31 @@ def test_mixed_validation(gmi):
     assert _mixed(gmi, Z=A16 + 4) == gmi.GMI_ERR_MISALIGNED
     assert _mixed(gmi, S=None, Z=None, ldy=60) == gmi.GMI_ERR_INVALID_ARG  # reaches the shape checks
     assert _mixed(gmi, M=0, S=None, Z=None, g=0) == gmi.GMI_OK  # group size unused without scales
+
+
+def _mg(gmi, count=4, offsets=A16 * 6, rows=64, N=64, K=256, xdt=0, X=A16, ldx=256, W=A16 * 2, ws=64 * 128, wt=0,
+        S=A16 * 3, ss=128, Z=A16 * 4, zs=64, g=128, Y=A16 * 5, ldy=64):
+    return gmi.lib().gmi_gemm_mixed_grouped(count, offsets, rows, N, K, xdt, X, ldx, W, ws, wt, S, ss, Z, zs, g, Y,
+                                            ldy, None)
+
+
+def test_mixed_grouped_validation(gmi):
+    assert _mg(gmi, count=-1) == gmi.GMI_ERR_INVALID_ARG
+    assert _mg(gmi, count=65536) == gmi.GMI_ERR_UNSUPPORTED
+    assert _mg(gmi, offsets=None) == gmi.GMI_ERR_INVALID_ARG
+    assert _mg(gmi, offsets=A16 + 2) == gmi.GMI_ERR_MISALIGNED
+    assert _mg(gmi, ws=64 * 128 - 16) == gmi.GMI_ERR_INVALID_ARG  # weight stride below one expert
+    assert _mg(gmi, ss=120) == gmi.GMI_ERR_INVALID_ARG  # scale stride below one expert's scales
+    assert _mg(gmi, zs=48) == gmi.GMI_ERR_INVALID_ARG
+    assert _mg(gmi, ws=64 * 128 + 8) == gmi.GMI_ERR_MISALIGNED
+    assert _mg(gmi, ss=132) == gmi.GMI_ERR_MISALIGNED
+    assert _mg(gmi, S=None) == gmi.GMI_ERR_UNSUPPORTED  # zero points without scales
+    assert _mg(gmi, xdt=2) == gmi.GMI_ERR_UNSUPPORTED
+    assert _mg(gmi, N=24) == gmi.GMI_ERR_UNSUPPORTED
+    assert _mg(gmi, ldx=128) == gmi.GMI_ERR_INVALID_ARG
+    # nothing to do: no groups, no rows or no columns
+    for kw in (dict(count=0), dict(rows=0), dict(N=0)):
+        assert _mg(gmi, offsets=None, X=None, W=None, S=None, Z=None, Y=None, **kw) == gmi.GMI_OK, kw
 
 
 def test_w4a16_workspace_bytes(gmi):

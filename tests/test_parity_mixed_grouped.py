@@ -1,0 +1,129 @@
+"""GPU parity of the grouped (mixture-of-experts) mixed-input GEMM: group sizes
+as device row offsets, one prepacked 4-bit weight with its scales and zero
+points per group.  Each group is checked against the fp64 oracle on its own
+rows and weights (same tolerance as the ungrouped call), and groups of at most
+64 rows also bit for bit against the ungrouped call on the same rows."""
+import numpy as np
+import pytest
+import torch
+
+import gmi_inputs as gi
+import oracle
+from helpers import SENTINEL, bytes_to_dev, check_close, dev, host_bits, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def gmi():
+    import grouped_mixed_input_amd as g
+
+    g.lib()
+    return g
+
+
+def _experts(G, N, K, group, dtype, seed):
+    r = np.random.default_rng(seed)
+    W = r.integers(0, 256, (G, N, K // 2), dtype=np.uint8)
+    Z = r.integers(0, 256, (G, K // group, N // 2), dtype=np.uint8)
+    S = gi.to_bits(r.uniform(0.001, 0.01, (G, K // group, N)).astype(np.float32), dtype)
+    return W, S, Z
+
+
+def _bf16_bound(ref, X, W, S, Z, N, K, group, w_type):
+    w = oracle.dequant_mixed(W, S, Z, N, K, group, w_type, "bf16")
+    return 1e-2 * np.abs(ref) + 1e-2 + 2.0**-8 * (np.abs(oracle.decode(X, "bf16")) @ np.abs(w).T)
+
+
+def _run(gmi, offsets, rows, X, W, S, Z, N, K, group, dtype, w_type, mode):
+    G = W.shape[0]
+    wpp = torch.stack([gmi.prepack_w4(bytes_to_dev(W[g]), N, K) for g in range(G)])
+    s_dev = to_dev(S.reshape(G, -1), dtype).view(G, K // group, N) if mode != "direct" else None
+    z_dev = bytes_to_dev(Z) if mode == "zero" else None
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    Yfull = torch.full((rows, N + 8), SENTINEL, dtype=torch.int16, device=dev()).view(tdt)
+    off = torch.tensor(np.asarray(offsets, np.int32), device=dev())
+    gmi.gemm_mixed_grouped(off, to_dev(X, dtype), wpp, s_dev, z_dev, group, N, w_type=w_type, Y=Yfull[:, :N])
+    torch.cuda.synchronize()
+    got = host_bits(Yfull)
+    assert np.all(got[:, N:] == SENTINEL), "padding columns of Y written"
+    return got[:, :N], wpp, s_dev, z_dev
+
+
+def _check_groups(got, offsets, rows, X, W, S, Z, N, K, group, dtype, w_type, mode):
+    covered = np.zeros(rows, bool)
+    for g in range(len(offsets) - 1):
+        lo, hi = min(max(offsets[g], 0), rows), min(max(offsets[g + 1], 0), rows)
+        if hi <= lo:
+            continue
+        covered[lo:hi] = True
+        s = S[g] if mode != "direct" else None
+        z = Z[g] if mode == "zero" else None
+        ref = oracle.mixed(X[lo:hi], W[g], s, z, N, K, group, w_type, dtype)
+        what = f"group {g} rows {lo}:{hi} {dtype} {w_type} {mode}"
+        if dtype == "f16":
+            check_close(got[lo:hi], ref, dtype, what)
+        else:
+            d = oracle.decode(got[lo:hi], dtype)
+            bound = _bf16_bound(ref, X[lo:hi], W[g], s, z, N, K, group, w_type)
+            assert np.all(np.abs(d - ref) <= bound), what
+    assert np.all(got[~covered] == SENTINEL), "rows outside every group written"
+
+
+@pytest.mark.parametrize("dtype,w_type,mode", [("f16", "uint4", "zero"), ("bf16", "int4", "zero"),
+                                               ("f16", "int4", "scale"), ("bf16", "uint4", "direct")])
+def test_mixed_grouped_moe_decode(gmi, dtype, w_type, mode):
+    # 24 experts, a few routed rows each (0 .. 40: the decode body up to 16 rows, the skinny body above)
+    r = np.random.default_rng(3)
+    counts = r.integers(0, 41, 24)
+    counts[[2, 7, 11]] = 0
+    counts[5], counts[6] = 16, 17
+    N, K, group = 256, 512, 128
+    rows = int(counts.sum()) + 24
+    X = gi.to_bits(r.standard_normal((rows, K)).astype(np.float32), dtype)
+    W, S, Z = _experts(len(counts), N, K, group, dtype, seed=4)
+    off = np.concatenate([[0], np.cumsum(counts)])
+    got, *_ = _run(gmi, off, rows, X, W, S, Z, N, K, group, dtype, w_type, mode)
+    _check_groups(got, off, rows, X, W, S, Z, N, K, group, dtype, w_type, mode)
+
+
+def test_mixed_grouped_large_groups_in_chunks(gmi):
+    # groups of 150 and 64 rows: 64-row chunks of the skinny body, the last one partial
+    counts = np.array([150, 0, 64, 3])
+    N, K, group = 128, 1024, 256
+    rows = int(counts.sum())
+    r = np.random.default_rng(5)
+    X = gi.to_bits(r.standard_normal((rows, K)).astype(np.float32), "f16")
+    W, S, Z = _experts(len(counts), N, K, group, "f16", seed=6)
+    off = np.concatenate([[0], np.cumsum(counts)])
+    got, *_ = _run(gmi, off, rows, X, W, S, Z, N, K, group, "f16", "int4", "zero")
+    _check_groups(got, off, rows, X, W, S, Z, N, K, group, "f16", "int4", "zero")
+
+
+@pytest.mark.parametrize("offsets", [[-10, 5, 30, 500], [0, 20, 40, 12], [40, 40, 40, 40]])
+def test_mixed_grouped_offsets_are_clipped(gmi, offsets):
+    N, K, group, rows = 64, 256, 128, 40
+    r = np.random.default_rng(7)
+    X = gi.to_bits(r.standard_normal((rows, K)).astype(np.float32), "bf16")
+    W, S, Z = _experts(3, N, K, group, "bf16", seed=8)
+    got, *_ = _run(gmi, offsets, rows, X, W, S, Z, N, K, group, "bf16", "uint4", "zero")
+    _check_groups(got, offsets, rows, X, W, S, Z, N, K, group, "bf16", "uint4", "zero")
+
+
+def test_mixed_grouped_matches_ungrouped_bit_for_bit(gmi):
+    # groups of at most 64 rows run the same kernel bodies as the ungrouped call on those rows
+    counts = np.array([1, 9, 16, 17, 33, 64, 0, 5])
+    N, K, group = 256, 1024, 128
+    rows = int(counts.sum())
+    r = np.random.default_rng(9)
+    X = gi.to_bits(r.standard_normal((rows, K)).astype(np.float32), "bf16")
+    W, S, Z = _experts(len(counts), N, K, group, "bf16", seed=10)
+    off = np.concatenate([[0], np.cumsum(counts)])
+    got, wpp, s_dev, z_dev = _run(gmi, off, rows, X, W, S, Z, N, K, group, "bf16", "int4", "zero")
+    Xd = to_dev(X, "bf16")
+    for g in range(len(counts)):
+        if counts[g] == 0:
+            continue
+        Yg = gmi.gemm_mixed(Xd[off[g]:off[g + 1]], wpp[g], s_dev[g], z_dev[g], group, N, w_type="int4")
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(Yg), got[off[g]:off[g + 1]]), g
