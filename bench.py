@@ -178,7 +178,51 @@ def bench_workloads(torch, gmi, gi, dev, args):
         out[f"w4a16_M{M}"] = dict(roof(2.0 * M * 8192 * 8192, ws, ms), bound=bound)
         del sets
     del rx
+    # the same shapes with bf16 activations and scales, int4 weights with zero points
+    Sb = S.float().to(torch.bfloat16)
+    for M in (16, 1024):
+        X = t16(torch, gi.w4a16(M=M, N=16, K=8192)["X"], torch.float16, dev).float().to(torch.bfloat16)
+        ws = 8192 * 8192 // 2 + Sb.numel() * 2 + Z.numel() + 2 * M * 8192 * 2
+        R = copies_for(ws)
+        sets = [(base_pp.clone(), Sb.clone(), Z.clone(), X.clone(), torch.empty((M, 8192), dtype=torch.bfloat16,
+                                                                                 device=dev)) for _ in range(R)]
+        wsp = torch.empty(gmi.w4a16_workspace_bytes(M, 8192, 8192), dtype=torch.uint8, device=dev)
+
+        def fn(i, sets=sets, wsp=wsp):
+            pp, s, z, x, y = sets[i]
+            gmi.gemm_mixed(x, pp, s, z, 128, 8192, w_type="int4", Y=y, workspace=wsp)
+
+        ms = time_launches(torch, fn, R, 5, max(20, R * 2))
+        out[f"mixed_bf16_int4_M{M}"] = dict(roof(2.0 * M * 8192 * 8192, ws, ms), bound="hbm" if M <= 64 else "mfma")
+        del sets
     log("bench: W4A16 done")
+
+    # 4b. MoE decode step with 4-bit experts: 128 routed rows over 128 experts
+    # (N 2048, K 4096, g 128), bf16, int4 with zero points, sizes on the device
+    counts = gi.moe_w4_counts()
+    E, N, K = len(counts), 2048, 4096
+    experts = [gi.moe_w4_expert(e) for e in range(E)]
+    wpp = torch.stack([gmi.prepack_w4(torch.from_numpy(w).to(dev), N, K) for w, _, _ in experts])
+    Sx = torch.stack([t16(torch, s, torch.bfloat16, dev) for _, s, _ in experts])
+    Zx = torch.stack([torch.from_numpy(z).to(dev) for _, _, z in experts])
+    del experts
+    Xm = t16(torch, gi.moe_w4_activations(rows=int(counts.sum())), torch.bfloat16, dev)
+    Ym = torch.empty((Xm.shape[0], N), dtype=torch.bfloat16, device=dev)
+    offs = torch.tensor(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32), device=dev)
+    live = int((counts > 0).sum())
+    by = live * (N * K // 2 + (K // 128) * N * 2 + (K // 128) * N // 2) + 2 * int(counts.sum()) * (K + N)
+    R = copies_for(by)
+    sets = [(wpp, Sx, Zx)] + [(wpp.clone(), Sx.clone(), Zx.clone()) for _ in range(R - 1)]
+
+    def fn(i, sets=sets):
+        w, s, z = sets[i]
+        gmi.gemm_mixed_grouped(offs, Xm, w, s, z, 128, N, w_type="int4", Y=Ym)
+
+    ms = time_launches(torch, fn, R, 5, max(50, 2 * R))
+    out["moe_w4_decode_bf16"] = dict(roof(2.0 * int(counts.sum()) * N * K, by, ms), bound="hbm", experts_live=live)
+    del sets, wpp, Sx, Zx, Xm, Ym
+    torch.cuda.empty_cache()
+    log("bench: MoE W4 decode done")
 
     # 5. conv fprop bf16 32x56x56x256, 3x3x256 -> 256, pad 1
     x, wf = gi.conv_fprop_bf16()

@@ -213,3 +213,26 @@ def moe_activations_f8(seed: int = DEFAULT_SEED, tokens: int = 16384, K: int = 4
 
 def moe_expert_weight_f8(group: int, seed: int = DEFAULT_SEED, N: int = 2048, K: int = 4096) -> np.ndarray:
     return to_bits(normal(rng(seed, 6, 1000 + group), (N, K), 1.0), "f8e4m3")
+
+
+# ----------------------------------------------------------------------------
+# workload 7: mixture-of-experts decode step with 4-bit expert weights -- 16
+# tokens routed to 8 experts each (128 rows) over 128 experts with the MoE
+# layer's expert shape (N 2048, K 4096), bf16 activations and scales, int4
+# weights with int4 zero points per 128-k group.
+# ----------------------------------------------------------------------------
+def moe_w4_counts(seed: int = DEFAULT_SEED, rows: int = 128, groups: int = 128) -> np.ndarray:
+    """Rows per expert, Zipf(1.1)-skewed like the MoE layer's token counts."""
+    return moe_counts(seed, tokens=rows, groups=groups, empty=8)
+
+
+def moe_w4_expert(group: int, seed: int = DEFAULT_SEED, N: int = 2048, K: int = 4096, g: int = 128):
+    """One expert: packed weight [N][K/2], bf16 scales [K/g][N], packed zero points [K/g][N/2]."""
+    w = uint4(rng(seed, 7, 1000 + group), N, K)
+    s = to_bits(uniform(rng(seed, 7, 3000 + group), (K // g, N), 0.001, 0.01), "bf16")
+    z = uint4(rng(seed, 7, 5000 + group), K // g, N)
+    return pack_u4(w), s, pack_u4(z)
+
+
+def moe_w4_activations(seed: int = DEFAULT_SEED, rows: int = 128, K: int = 4096) -> np.ndarray:
+    return to_bits(normal(rng(seed, 7, 0), (rows, K), 1.0), "bf16")

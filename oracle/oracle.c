@@ -328,6 +328,64 @@ int ora_conv2d_fprop(int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int3
 }
 
 /* ------------------------------------------------------------------------
+ * Convolution data gradient [p3] (the dgrad operator): the adjoint of the
+ * forward map above in its first argument.  Every product the forward pass
+ * forms, x[n][ih][iw][c] * w[k][r][s][c] feeding y[n][p][q][k], sends
+ * dy[n][p][q][k] * w[k][r][s][c] back to dx[n][ih][iw][c]:
+ *   dx[n][h][w][c] = alpha * sum over (p, q, k, r, s) with
+ *                    p*sh - ph + r*dh = h and q*sw - pw + s*dw = w
+ *                    of dy[n][p][q][k] * w[k][r][s][c]   + beta * C[n][h][w][c]
+ * dy NPQK with P, Q as for the forward pass; dx, C NHWC.
+ * ------------------------------------------------------------------------ */
+int ora_conv2d_dgrad(int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int32_t R, int32_t S, int32_t ph,
+                     int32_t pw, int32_t sh, int32_t sw, int32_t dh, int32_t dw, const uint16_t* dy,
+                     const uint16_t* w, const uint16_t* cin, int32_t dt, double alpha, double beta, double* out) {
+  if (N < 0 || H <= 0 || W <= 0 || C <= 0 || K <= 0 || R <= 0 || S <= 0) return -1;
+  if (ph < 0 || pw < 0 || sh <= 0 || sw <= 0 || dh <= 0 || dw <= 0) return -1;
+  if (beta != 0.0 && !cin) return -1;
+  int64_t P = (H + 2 * (int64_t)ph - (int64_t)dh * (R - 1) - 1) / sh + 1;
+  int64_t Q = (W + 2 * (int64_t)pw - (int64_t)dw * (S - 1) - 1) / sw + 1;
+  if (P <= 0 || Q <= 0) return -1;
+  int64_t nx = (int64_t)N * H * W * C, nw = (int64_t)K * R * S * C;
+  double* wd = (double*)malloc(sizeof(double) * (size_t)nw);
+  double* acc = (double*)calloc((size_t)(nx ? nx : 1), sizeof(double));
+  if (!wd || !acc) {
+    free(wd);
+    free(acc);
+    return -1;
+  }
+  for (int64_t i = 0; i < nw; ++i) wd[i] = dec(w[i], dt);
+  /* one image per thread: the scatter of image n touches only dx of image n */
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t p = 0; p < P; ++p)
+      for (int64_t q = 0; q < Q; ++q)
+        for (int64_t k = 0; k < K; ++k) {
+          double g = dec(dy[((n * P + p) * Q + q) * K + k], dt);
+          if (g == 0.0) continue;
+          for (int64_t r = 0; r < R; ++r) {
+            int64_t ih = p * sh - ph + r * dh;
+            if (ih < 0 || ih >= H) continue;
+            for (int64_t s = 0; s < S; ++s) {
+              int64_t iw = q * sw - pw + s * dw;
+              if (iw < 0 || iw >= W) continue;
+              double* xp = acc + ((n * H + ih) * W + iw) * C;
+              const double* wp = wd + ((k * R + r) * S + s) * C;
+              for (int64_t c = 0; c < C; ++c) xp[c] += g * wp[c];
+            }
+          }
+        }
+  for (int64_t i = 0; i < nx; ++i) {
+    double v = alpha * acc[i];
+    if (beta != 0.0) v += beta * dec(cin[i], dt);
+    out[i] = v;
+  }
+  free(wd);
+  free(acc);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------
  * Weight prepack [p2 design note: the narrow weight is reordered once so that
  * each lane's operand values for several consecutive matrix instructions sit
  * in one 128-bit word].  This library's permutation pi, over N x K uint4

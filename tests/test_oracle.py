@@ -447,6 +447,52 @@ def test_conv_beta_term():
     np.testing.assert_allclose(got, 2.0 * base - 0.5 * lib_decode(c, "bf16"), rtol=1e-14, atol=1e-14)
 
 
+# ---------------------------------------------------------------- conv dgrad
+def _int_bits(shape, lo=-3, hi=4):
+    return bf16_bits(RNG.integers(lo, hi, shape).astype(np.float64))
+
+
+@pytest.mark.parametrize("H,R,pad,stride,dil", [(7, 3, 1, 1, 1), (8, 3, 0, 2, 1), (9, 3, 2, 1, 2), (10, 5, 2, 3, 1),
+                                                (6, 1, 0, 1, 1)])
+def test_dgrad_is_the_adjoint_of_fprop(H, R, pad, stride, dil):
+    # <fprop(x, w), dy> == <x, dgrad(dy, w)> for every x, dy: integer-valued operands make both sides exact
+    N, C, K = 2, 5, 3
+    x = _int_bits((N, H, H + 1, C))
+    w = _int_bits((K, R, R, C))
+    P = oracle.conv_out_size(H, R, pad, stride, dil)
+    Q = oracle.conv_out_size(H + 1, R, pad, stride, dil)
+    dy = _int_bits((N, P, Q, K))
+    y = oracle.conv2d_fprop(x, w, pad=(pad, pad), stride=(stride, stride), dil=(dil, dil))
+    dx = oracle.conv2d_dgrad(dy, w, H, H + 1, pad=(pad, pad), stride=(stride, stride), dil=(dil, dil))
+    assert np.sum(y * lib_decode(dy, "bf16")) == np.sum(lib_decode(x, "bf16") * dx)
+
+
+@pytest.mark.parametrize("R,pad,dil", [(3, 1, 1), (3, 0, 2), (5, 2, 1), (2, 1, 3)])
+def test_dgrad_stride_one_is_fprop_with_flipped_filter(R, pad, dil):
+    # textbook identity: the transposed stride-1 convolution is a convolution of dy with the filter rotated by
+    # 180 degrees, its in / out channels swapped, and padding dil * (R - 1) - pad
+    N, H, C, K = 2, 9, 4, 6
+    w = bf16_bits(RNG.standard_normal((K, R, R, C))).reshape(K, R, R, C)
+    P = oracle.conv_out_size(H, R, pad, 1, dil)
+    dy = bf16_bits(RNG.standard_normal((N, P, P, K))).reshape(N, P, P, K)
+    wf = np.ascontiguousarray(w[:, ::-1, ::-1, :].transpose(3, 1, 2, 0))  # [C][R][S][K], flipped taps
+    pad2 = dil * (R - 1) - pad
+    want = oracle.conv2d_fprop(dy, wf, pad=(pad2, pad2), dil=(dil, dil))
+    got = oracle.conv2d_dgrad(dy, w, H, H, pad=(pad, pad), dil=(dil, dil))
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_dgrad_beta_term_and_shape_checks():
+    dy = bf16_bits(RNG.standard_normal(1 * 4 * 4 * 3)).reshape(1, 4, 4, 3)
+    w = bf16_bits(RNG.standard_normal(3 * 3 * 3 * 8)).reshape(3, 3, 3, 8)
+    c = bf16_bits(RNG.standard_normal(1 * 4 * 4 * 8)).reshape(1, 4, 4, 8)
+    base = oracle.conv2d_dgrad(dy, w, 4, 4, pad=(1, 1))
+    got = oracle.conv2d_dgrad(dy, w, 4, 4, pad=(1, 1), C_in=c, alpha=2.0, beta=-0.5)
+    np.testing.assert_allclose(got, 2.0 * base - 0.5 * lib_decode(c, "bf16"), rtol=1e-14, atol=1e-14)
+    with pytest.raises(AssertionError):
+        oracle.conv2d_dgrad(dy, w, 5, 4, pad=(1, 1))  # dy does not have the forward output's size
+
+
 # ---------------------------------------------------------------- prepack
 def test_golden_prepack_positions():
     N, K = 32, 256
