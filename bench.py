@@ -199,18 +199,18 @@ def bench_workloads(torch, gmi, gi, dev, args):
 
     # 4b. MoE decode step with 4-bit experts: 128 routed rows over 128 experts
     # (N 2048, K 4096, g 128), bf16, int4 with zero points, sizes on the device
-    counts = gi.moe_w4_counts()
-    E, N, K = len(counts), 2048, 4096
+    w4_counts = gi.moe_w4_counts()
+    E, N, K = len(w4_counts), 2048, 4096
     experts = [gi.moe_w4_expert(e) for e in range(E)]
     wpp = torch.stack([gmi.prepack_w4(torch.from_numpy(w).to(dev), N, K) for w, _, _ in experts])
     Sx = torch.stack([t16(torch, s, torch.bfloat16, dev) for _, s, _ in experts])
     Zx = torch.stack([torch.from_numpy(z).to(dev) for _, _, z in experts])
     del experts
-    Xm = t16(torch, gi.moe_w4_activations(rows=int(counts.sum())), torch.bfloat16, dev)
+    Xm = t16(torch, gi.moe_w4_activations(rows=int(w4_counts.sum())), torch.bfloat16, dev)
     Ym = torch.empty((Xm.shape[0], N), dtype=torch.bfloat16, device=dev)
-    offs = torch.tensor(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32), device=dev)
-    live = int((counts > 0).sum())
-    by = live * (N * K // 2 + (K // 128) * N * 2 + (K // 128) * N // 2) + 2 * int(counts.sum()) * (K + N)
+    offs = torch.tensor(np.concatenate([[0], np.cumsum(w4_counts)]).astype(np.int32), device=dev)
+    live = int((w4_counts > 0).sum())
+    by = live * (N * K // 2 + (K // 128) * N * 2 + (K // 128) * N // 2) + 2 * int(w4_counts.sum()) * (K + N)
     R = copies_for(by)
     sets = [(wpp, Sx, Zx)] + [(wpp.clone(), Sx.clone(), Zx.clone()) for _ in range(R - 1)]
 
@@ -219,7 +219,7 @@ def bench_workloads(torch, gmi, gi, dev, args):
         gmi.gemm_mixed_grouped(offs, Xm, w, s, z, 128, N, w_type="int4", Y=Ym)
 
     ms = time_launches(torch, fn, R, 5, max(50, 2 * R))
-    out["moe_w4_decode_bf16"] = dict(roof(2.0 * int(counts.sum()) * N * K, by, ms), bound="hbm", experts_live=live)
+    out["moe_w4_decode_bf16"] = dict(roof(2.0 * int(w4_counts.sum()) * N * K, by, ms), bound="hbm", experts_live=live)
     del sets, wpp, Sx, Zx, Xm, Ym
     torch.cuda.empty_cache()
     log("bench: MoE W4 decode done")

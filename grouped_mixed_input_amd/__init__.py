@@ -75,6 +75,10 @@ def lib() -> ctypes.CDLL:
     L.gmi_gemm_mixed_grouped.restype = ctypes.c_int
     L.gmi_gemm_mixed_grouped.argtypes = [_i32, _p, _i32, _i32, _i32, ctypes.c_int, _p, _i64, _p, _i64, ctypes.c_int,
                                          _p, _i64, _p, _i64, _i32, _p, _i64, _p]
+    L.gmi_conv2d_dgrad_workspace_bytes.restype = _sz
+    L.gmi_conv2d_dgrad_workspace_bytes.argtypes = [_i32] * 4
+    L.gmi_conv2d_dgrad_implicit.restype = ctypes.c_int
+    L.gmi_conv2d_dgrad_implicit.argtypes = [_i32] * 13 + [_p, _p, _p, _p, ctypes.c_int, _f32, _f32, _p, _sz, _p]
     L.gmi_w4a16_workspace_bytes.restype = _sz
     L.gmi_w4a16_workspace_bytes.argtypes = [_i32, _i32, _i32]
     L.gmi_conv2d_fprop_implicit.restype = ctypes.c_int
@@ -270,3 +274,22 @@ def conv2d_fprop(x: torch.Tensor, w: torch.Tensor, pad=(0, 0), stride=(1, 1), di
                                            x.data_ptr(), w.data_ptr(), _ptr(c_in), y.data_ptr(), _DT[x.dtype], alpha,
                                            beta, _stream(stream)))
     return y
+
+
+def conv2d_dgrad(dy: torch.Tensor, w: torch.Tensor, H: int, W: int, pad=(0, 0), dil=(1, 1), c_in=None, alpha=1.0,
+                 beta=0.0, dx: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                 stream=None) -> torch.Tensor:
+    """Data gradient of conv2d_fprop (stride 1): dy NPQK, w KRSC, the forward input's H, W -> dx NHWC."""
+    N, P, Q, K = dy.shape
+    K2, R, S, C = w.shape
+    if K2 != K:
+        raise ValueError("dy and w disagree on K")
+    if dx is None:
+        dx = torch.empty((N, H, W, C), dtype=dy.dtype, device=dy.device)
+    if workspace is None:
+        workspace = torch.empty(lib().gmi_conv2d_dgrad_workspace_bytes(C, K, R, S), dtype=torch.uint8,
+                                device=dy.device)
+    _check(lib().gmi_conv2d_dgrad_implicit(N, H, W, C, K, R, S, pad[0], pad[1], 1, 1, dil[0], dil[1],
+                                           dy.data_ptr(), w.data_ptr(), _ptr(c_in), dx.data_ptr(), _DT[dy.dtype],
+                                           alpha, beta, workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return dx

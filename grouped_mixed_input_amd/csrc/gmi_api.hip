@@ -454,6 +454,67 @@ gmi_status gmi_gemm_mixed(int32_t M, int32_t N, int32_t K, gmi_dtype x_dtype, co
                     workspace, workspace_bytes, stream);
 }
 
+size_t gmi_conv2d_dgrad_workspace_bytes(int32_t C, int32_t K, int32_t R, int32_t S) {
+  if (C < 1 || K < 1 || R < 1 || S < 1) return 0;
+  return ((size_t)C * K * R * S * 2 + 255) / 256 * 256;
+}
+
+gmi_status gmi_conv2d_dgrad_implicit(int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int32_t R, int32_t S,
+                                     int32_t pad_h, int32_t pad_w, int32_t stride_h, int32_t stride_w, int32_t dil_h,
+                                     int32_t dil_w, const void* dy, const void* w, const void* c_in, void* dx,
+                                     gmi_dtype dtype, float alpha, float beta, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  const char* who = "conv2d_dgrad";
+  if (N < 0 || H < 1 || W < 1 || C < 1 || K < 1 || R < 1 || S < 1)
+    return fail(GMI_ERR_INVALID_ARG, "%s: sizes must be positive (N >= 0)", who);
+  if (pad_h < 0 || pad_w < 0 || stride_h < 1 || stride_w < 1 || dil_h < 1 || dil_w < 1)
+    return fail(GMI_ERR_INVALID_ARG, "%s: padding >= 0, stride >= 1 and dilation >= 1 required", who);
+  if (stride_h != 1 || stride_w != 1)
+    return fail(GMI_ERR_UNSUPPORTED, "%s: only traversal stride 1 (the non-strided dgrad of the page)", who);
+  if (!dtype_ok(dtype)) return fail(GMI_ERR_UNSUPPORTED, "%s: dtype %d not supported", who, (int)dtype);
+  if (C % 8 || K % 8) return fail(GMI_ERR_MISALIGNED, "%s: C and K must be multiples of 8", who);
+  const int64_t P = (int64_t)H + 2 * (int64_t)pad_h - (int64_t)dil_h * (R - 1);
+  const int64_t Q = (int64_t)W + 2 * (int64_t)pad_w - (int64_t)dil_w * (S - 1);
+  if (P < 1 || Q < 1) return fail(GMI_ERR_INVALID_ARG, "%s: the filter does not fit the padded image", who);
+  if ((int64_t)N * H * W > INT32_MAX || (int64_t)N * P * Q > INT32_MAX || (int64_t)R * S * K > kMaxLd ||
+      (int64_t)N * P * Q * K * 2 > INT32_MAX || C > kMaxLd)
+    return fail(GMI_ERR_UNSUPPORTED, "%s: dy above 2^31 bytes, R*S*K above 2^22 or too many pixels", who);
+  if (N == 0) return GMI_OK;
+  const bool use_c = beta != 0.0f;
+  if (!dy || !w || !dx || (use_c && !c_in)) return fail(GMI_ERR_INVALID_ARG, "%s: NULL pointer", who);
+  if (!aligned16(dy) || !aligned16(w) || !aligned16(dx) || (use_c && !aligned16(c_in)))
+    return fail(GMI_ERR_MISALIGNED, "%s: pointers must be 16-byte aligned", who);
+  if (!workspace || workspace_bytes < gmi_conv2d_dgrad_workspace_bytes(C, K, R, S))
+    return fail(GMI_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", who, workspace_bytes,
+                gmi_conv2d_dgrad_workspace_bytes(C, K, R, S));
+  if (!aligned16(workspace)) return fail(GMI_ERR_MISALIGNED, "%s: workspace must be 16-byte aligned", who);
+  ConvLaunch a;  // the forward problem; x is dy and y is dx here
+  a.x = (const uint16_t*)dy;
+  a.w = (const uint16_t*)w;
+  a.c = use_c ? (const uint16_t*)c_in : nullptr;
+  a.y = (uint16_t*)dx;
+  a.N = N;
+  a.H = H;
+  a.W = W;
+  a.C = C;
+  a.K = K;
+  a.R = R;
+  a.S = S;
+  a.P = (int)P;
+  a.Q = (int)Q;
+  a.ph = pad_h;
+  a.pw = pad_w;
+  a.sh = 1;
+  a.sw = 1;
+  a.dh = dil_h;
+  a.dw = dil_w;
+  const int64_t Mg = (int64_t)N * H * W;
+  const int shape = choose_shape([&](int bm, int bn) { return cdiv(Mg, bm) * cdiv(C, bn); });
+  return hip_status(launch_conv_dgrad(a, (uint16_t*)workspace, shape, (int)dtype, alpha, beta, (hipStream_t)stream),
+                    who);
+}
+
 gmi_status gmi_conv2d_fprop_implicit(int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int32_t R, int32_t S,
                                      int32_t pad_h, int32_t pad_w, int32_t stride_h, int32_t stride_w, int32_t dil_h,
                                      int32_t dil_w, const void* x, const void* w, const void* c_in, void* y,

@@ -110,6 +110,8 @@ hipError_t launch_grouped_offsets(const OffsetsLaunch& p, int shape, int dtype, 
 hipError_t launch_ptr_array(const PtrArrayLaunch& a, int shape, int dtype, float alpha, float beta,
                             hipStream_t stream);
 hipError_t launch_conv_fprop(const ConvLaunch& a, int shape, int dtype, float alpha, float beta, hipStream_t stream);
+hipError_t launch_conv_dgrad(const ConvLaunch& a, uint16_t* wt, int shape, int dtype, float alpha, float beta,
+                             hipStream_t stream);
 hipError_t launch_prepack_w4(const uint8_t* w, int N, int K, uint8_t* out, hipStream_t stream);
 hipError_t launch_w4a16(const W4Launch& a, hipStream_t stream);
 hipError_t launch_w4a16_grouped(const W4Grouped& a, hipStream_t stream);

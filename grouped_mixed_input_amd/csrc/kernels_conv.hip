@@ -91,4 +91,59 @@ hipError_t launch_conv_fprop(const ConvLaunch& p, int shape, int dtype, float al
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Data gradient, stride 1.  The page runs dgrad through the same im2col
+// operand with the filter-tap strides negated: dx[n][h][w][c] sums
+// dy[n][h + ph - r dh][w + pw - s dw][k] w[k][r][s][c], which is the forward
+// gather over dy with padding -ph and dilation -dh.  The GEMM's B operand is
+// then the filter with its reduction (r, s, k) contiguous per column c, i.e.
+// w transposed to [C][R][S][K]: one 64 x 64 (k, c) block of one tap per
+// workgroup, through LDS so reads run along c and writes along k.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_filter_transpose(const uint16_t* __restrict__ w, uint16_t* __restrict__ wt,
+                                                          int K, int RS, int C) {
+  __shared__ uint16_t t[64][65];
+  const int rs = blockIdx.z, k0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int kk = i / 64, cc = i % 64, k = k0 + kk, c = c0 + cc;
+    t[kk][cc] = (k < K && c < C) ? w[((int64_t)k * RS + rs) * C + c] : 0;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int cc = i / 64, kk = i % 64, k = k0 + kk, c = c0 + cc;
+    if (k < K && c < C) wt[((int64_t)c * RS + rs) * K + k] = t[kk][cc];
+  }
+}
+
+hipError_t launch_conv_dgrad(const ConvLaunch& p, uint16_t* wt, int shape, int dtype, float alpha, float beta,
+                             hipStream_t stream) {
+  // p describes the forward problem (x: N x H x W x C, y: N x P x Q x K);
+  // here p.x is dy, p.y is dx
+  const dim3 tgrid((p.C + 63) / 64, (p.K + 63) / 64, p.R * p.S);
+  hipLaunchKernelGGL(k_filter_transpose, tgrid, dim3(256), 0, stream, p.w, wt, p.K, p.R * p.S, p.C);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  ConvLaunch f;  // the forward view: gather over dy, filter [C][R][S][K]
+  f.x = p.x;
+  f.w = wt;
+  f.c = p.c;
+  f.y = p.y;
+  f.N = p.N;
+  f.H = p.P;
+  f.W = p.Q;
+  f.C = p.K;
+  f.K = p.C;
+  f.R = p.R;
+  f.S = p.S;
+  f.P = p.H;
+  f.Q = p.W;
+  f.ph = -p.ph;
+  f.pw = -p.pw;
+  f.sh = 1;
+  f.sw = 1;
+  f.dh = -p.dh;
+  f.dw = -p.dw;
+  return launch_conv_fprop(f, shape, dtype, alpha, beta, stream);
+}
+
 }  // namespace gmi

@@ -474,14 +474,18 @@ static hipError_t launch_w4a16_dt(const W4Launch& a, hipStream_t stream) {
 // ---------------------------------------------------------------------------
 // Grouped (mixture-of-experts) kernel: workgroup (x, g) takes weight rows
 // 32 x .. 32 x + 31 of group g over that group's rows, whose count only the
-// device knows -- the decode body for at most 16 rows, else the skinny body
-// 64 rows at a time.  A group with no rows returns at once.
+// device knows, 16 rows at a time through the decode body (a decode step
+// routes a few rows to each expert; a larger group re-reads its weight slice,
+// from L2, once per 16 rows).  A group with no rows returns at once.  Each
+// workgroup moves only 32 weight rows, so the body runs on 4 waves with a
+// 4-slot ring (40 KB of LDS, at most 128 VGPRs): four workgroups share a CU
+// and keep its weight stream busy while others reduce and store.
 // ---------------------------------------------------------------------------
-constexpr int kGroupedLds = 8 * DecodeLds<2, 8>::WAVE;
-static_assert(skinny_lds_bytes<2, 8, 4>() <= kGroupedLds, "one LDS block serves both bodies");
+constexpr int kGroupedWaves = 4, kGroupedRing = 4;
+constexpr int kGroupedLds = kGroupedWaves * DecodeLds<2, kGroupedRing>::WAVE;
 
 template <int DT>
-__global__ __launch_bounds__(512) void k_w4a16_grouped(W4Grouped a) {
+__global__ __launch_bounds__(64 * kGroupedWaves, 4) void k_w4a16_grouped(W4Grouped a) {
   __shared__ __attribute__((aligned(16))) char lds[kGroupedLds];
   const int g = blockIdx.y;
   const int lo = min(max(a.offsets[g], 0), a.rows);
@@ -492,15 +496,11 @@ __global__ __launch_bounds__(512) void k_w4a16_grouped(W4Grouped a) {
   p.scales = a.base.scales + g * a.s_stride;
   p.zeros = a.base.zeros + g * a.z_stride;
   const int n_base = blockIdx.x * 32;
-  const int chunk = hi - lo <= 16 ? 16 : 64;
-  for (int r0 = lo; r0 < hi; r0 += chunk) {
-    p.M = min(chunk, hi - r0);
+  for (int r0 = lo; r0 < hi; r0 += 16) {
+    p.M = min(16, hi - r0);
     p.X = a.base.X + (int64_t)r0 * a.base.ldx;
     p.Y = a.base.Y + (int64_t)r0 * a.base.ldy;
-    if (chunk == 16)
-      decode_body<DT, 2, 8, 8>(p, n_base, lds);
-    else
-      skinny_body<DT, 2, 8, 4>(p, n_base, lds);
+    decode_body<DT, 2, kGroupedWaves, kGroupedRing>(p, n_base, lds);
     __syncthreads();  // the next chunk reuses the LDS the reduction just read
   }
 }
@@ -508,9 +508,9 @@ __global__ __launch_bounds__(512) void k_w4a16_grouped(W4Grouped a) {
 hipError_t launch_w4a16_grouped(const W4Grouped& a, hipStream_t stream) {
   const dim3 grid((a.base.N + 31) / 32, a.count);
   if (a.base.dt == DT_BF16)
-    hipLaunchKernelGGL(k_w4a16_grouped<DT_BF16>, grid, dim3(512), 0, stream, a);
+    hipLaunchKernelGGL(k_w4a16_grouped<DT_BF16>, grid, dim3(64 * kGroupedWaves), 0, stream, a);
   else
-    hipLaunchKernelGGL(k_w4a16_grouped<DT_F16>, grid, dim3(512), 0, stream, a);
+    hipLaunchKernelGGL(k_w4a16_grouped<DT_F16>, grid, dim3(64 * kGroupedWaves), 0, stream, a);
   return hipGetLastError();
 }
 

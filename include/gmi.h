@@ -244,10 +244,11 @@ gmi_status gmi_gemm_mixed(int32_t M, int32_t N, int32_t K, gmi_dtype x_dtype, co
  *   strides  at least one group's data when count > 1 (N*K/2 bytes,
  *            (K/group)*N scales, (K/group)*N/2 zero bytes) and keeping every
  *            group's data 16-byte aligned; ignored for a NULL array.
- * Modes, types, layouts and numerics as for gmi_gemm_mixed; a group of at
- * most 16 rows takes the M <= 16 kernel body, a larger one is processed 64
- * rows at a time by the skinny body (weights rounded to the activation type).
- * No workspace. */
+ * Modes, types and layouts as for gmi_gemm_mixed.  Every group runs 16 rows
+ * at a time through the M <= 16 kernel body (exact integers v(q) - v(z) into
+ * the matrix instruction, each group's scale on the fp32 partial sums); it
+ * suits decode-size groups, and a larger group re-reads its weight once per
+ * 16 rows.  No workspace. */
 gmi_status gmi_gemm_mixed_grouped(int32_t count, const int32_t* offsets, int32_t rows, int32_t N, int32_t K,
                                   gmi_dtype x_dtype, const void* X, int64_t ldx, const uint8_t* w_prepacked,
                                   int64_t w_stride, gmi_w4_type w_type, const void* scales, int64_t s_stride,
@@ -275,6 +276,33 @@ gmi_status gmi_conv2d_fprop_implicit(int32_t N, int32_t H, int32_t W, int32_t C,
                                      int32_t pad_h, int32_t pad_w, int32_t stride_h, int32_t stride_w,
                                      int32_t dil_h, int32_t dil_w, const void* x, const void* w, const void* c_in,
                                      void* y, gmi_dtype dtype, float alpha, float beta, void* stream);
+
+/* Bytes of the workspace gmi_conv2d_dgrad_implicit needs: the filter
+ * rearranged to [C][R][S][K] (C*K*R*S*2, rounded up to 256); 0 for a
+ * non-positive size. */
+size_t gmi_conv2d_dgrad_workspace_bytes(int32_t C, int32_t K, int32_t R, int32_t S);
+
+/* Implicit-GEMM conv2d data gradient (the page's non-strided dgrad operator),
+ * the adjoint of gmi_conv2d_fprop_implicit in its activation:
+ *   dx[n][h][w][c] = alpha * sum over (p, q, k, r, s) with p - ph + r*dh = h,
+ *                    q - pw + s*dw = w of dy[n][p][q][k] * w[k][r][s][c]
+ *                    + beta * c_in[n][h][w][c]
+ * Arguments describe the forward problem: x was N x H x W x C, the filter is
+ * w KRSC, dy is N x P x Q x K with P = H + 2 ph - dh (R-1), Q likewise; dx
+ * and c_in are NHWC.  As on the page, dgrad gathers dy through the im2col
+ * addressing with the filter-tap strides negated (here padding -ph and
+ * dilation -dh over dy); the GEMM view is M = N*H*W, N = C, K = R*S*K.
+ *   workspace  at least gmi_conv2d_dgrad_workspace_bytes(C, K, R, S) bytes,
+ *              16-byte aligned: a first launch writes the filter there as
+ *              [C][R][S][K], the GEMM launch reads it.
+ * Traversal stride must be 1 (the page's strided dgrad is a separate
+ * operator), else GMI_ERR_UNSUPPORTED.  Other rules as for the forward pass:
+ * C % 8 == 0 and K % 8 == 0, 16-byte aligned pointers, c_in NULL iff beta == 0. */
+gmi_status gmi_conv2d_dgrad_implicit(int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int32_t R, int32_t S,
+                                     int32_t pad_h, int32_t pad_w, int32_t stride_h, int32_t stride_w,
+                                     int32_t dil_h, int32_t dil_w, const void* dy, const void* w, const void* c_in,
+                                     void* dx, gmi_dtype dtype, float alpha, float beta, void* workspace,
+                                     size_t workspace_bytes, void* stream);
 
 /* Text of the last failed check or HIP error on the calling thread ("" if
  * none).  The pointer stays valid until the next gmi_* call on that thread. */

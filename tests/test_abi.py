@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
     for want in ["gmi_gemm_grouped", "gmi_gemm_ptr_array", "gmi_prepack_w4", "gmi_gemm_w4a16",
                  "gmi_conv2d_fprop_implicit", "gmi_workspace_bytes", "gmi_prepack_w4_bytes", "gmi_last_error",
                  "gmi_gemm_grouped_offsets", "gmi_w4a16_workspace_bytes", "gmi_gemm_mixed",
-                 "gmi_gemm_mixed_grouped"]:
+                 "gmi_gemm_mixed_grouped", "gmi_conv2d_dgrad_implicit", "gmi_conv2d_dgrad_workspace_bytes"]:
         assert want in names
 
 
@@ -215,6 +215,31 @@ def test_mixed_grouped_validation(gmi):
     # nothing to do: no groups, no rows or no columns
     for kw in (dict(count=0), dict(rows=0), dict(N=0)):
         assert _mg(gmi, offsets=None, X=None, W=None, S=None, Z=None, Y=None, **kw) == gmi.GMI_OK, kw
+
+
+def _dg(gmi, N=2, H=8, W=8, C=16, K=8, R=3, S=3, ph=1, pw=1, sh=1, sw=1, dh=1, dw=1, dy=A16, w=A16 * 2, c=None,
+        dx=A16 * 3, dt=1, beta=0.0, ws=A16 * 4, ws_bytes=1 << 20):
+    return gmi.lib().gmi_conv2d_dgrad_implicit(N, H, W, C, K, R, S, ph, pw, sh, sw, dh, dw, dy, w, c, dx, dt, 1.0,
+                                               beta, ws, ws_bytes, None)
+
+
+def test_conv_dgrad_validation(gmi):
+    L = gmi.lib()
+    assert L.gmi_conv2d_dgrad_workspace_bytes(16, 8, 3, 3) == 16 * 8 * 9 * 2  # already a multiple of 256
+    assert L.gmi_conv2d_dgrad_workspace_bytes(8, 8, 1, 3) == 512  # 384 rounded up
+    assert L.gmi_conv2d_dgrad_workspace_bytes(0, 8, 3, 3) == 0
+    assert _dg(gmi, H=0) == gmi.GMI_ERR_INVALID_ARG
+    assert _dg(gmi, ph=-1) == gmi.GMI_ERR_INVALID_ARG
+    assert _dg(gmi, sh=2) == gmi.GMI_ERR_UNSUPPORTED  # strided dgrad is not built
+    assert _dg(gmi, dt=2) == gmi.GMI_ERR_UNSUPPORTED
+    assert _dg(gmi, C=12) == gmi.GMI_ERR_MISALIGNED
+    assert _dg(gmi, H=1, ph=0) == gmi.GMI_ERR_INVALID_ARG  # a 3x3 filter does not fit a 1-row image
+    assert _dg(gmi, beta=1.0) == gmi.GMI_ERR_INVALID_ARG  # c_in required
+    assert _dg(gmi, dy=A16 + 2) == gmi.GMI_ERR_MISALIGNED
+    assert _dg(gmi, ws_bytes=100) == gmi.GMI_ERR_WORKSPACE
+    assert _dg(gmi, ws=None) == gmi.GMI_ERR_WORKSPACE
+    assert _dg(gmi, ws=A16 + 8) == gmi.GMI_ERR_MISALIGNED
+    assert _dg(gmi, N=0, dy=None, w=None, dx=None, ws=None) == gmi.GMI_OK
 
 
 def test_w4a16_workspace_bytes(gmi):
