@@ -180,6 +180,9 @@ gmi_status gmi_gemm_grouped(const gmi_problem* problems, int32_t count, gmi_dtyp
     desc.push_back(d);
   }
   hipStream_t s = (hipStream_t)stream;
+  if (live <= kInlineGroups)
+    return hip_status(launch_grouped_inline(desc.data(), live, (int)tiles, shape, (int)dtype, ktail, alpha, beta, s),
+                      "gemm_grouped: launch");
   GroupDesc* dev_desc = (GroupDesc*)((char*)workspace + kWorkspaceHeader);
   // pageable source: the copy completes before the call returns, so the
   // host table may be reused immediately

@@ -105,6 +105,11 @@ int w4a16_split(int M, int N, int K);
 
 hipError_t launch_grouped(const GroupDesc* desc_dev, int count, int total_tiles, int shape, int dtype, bool ktail,
                           float alpha, float beta, hipStream_t stream);
+// up to kInlineGroups problems: the table (host memory) is passed in the
+// kernel arguments instead of being staged into the workspace
+constexpr int kInlineGroups = 32;
+hipError_t launch_grouped_inline(const GroupDesc* desc_host, int count, int total_tiles, int shape, int dtype,
+                                 bool ktail, float alpha, float beta, hipStream_t stream);
 hipError_t launch_grouped_offsets(const OffsetsLaunch& p, int shape, int dtype, float alpha, float beta,
                                   hipStream_t stream);
 hipError_t launch_ptr_array(const PtrArrayLaunch& a, int shape, int dtype, float alpha, float beta,

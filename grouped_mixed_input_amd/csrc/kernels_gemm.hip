@@ -71,30 +71,58 @@ __device__ __forceinline__ void grouped_tile(char* lds, const GroupDesc& d, int 
   run_tile<Cfg, DT, KTAIL>(lds, t, alpha, beta);
 }
 
-template <class Cfg, int DT, bool KTAIL>
-__global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_gemm_grouped(GroupedArgs a) {
+// The persistent walk over a problem table `desc` (global memory, or the
+// kernel's own arguments for short lists).
+template <class Cfg, int DT, bool KTAIL, class Table>
+__device__ __forceinline__ void grouped_walk(char* lds, const Table& desc, int count, int total, float alpha,
+                                             float beta) {
   using Small = typename SmallOf<Cfg>::type;
-  constexpr int LDS = Cfg::LDS_BYTES > lds_of<Small>() ? Cfg::LDS_BYTES : lds_of<Small>();
-  __shared__ __attribute__((aligned(16))) char lds[LDS];
   const int G = gridDim.x;
-  // with device-held group sizes the grid is sized for the device, not the
-  // tiles: workgroups past the total find no tile and return
-  const int total = a.total_tiles >= 0 ? a.total_tiles : *a.total_dev;
   int g = 0;
   for (int base = 0; base < total; base += G) {
     const int tile = base + remap_slot(blockIdx.x, G);
     if (tile >= total) break;
-    while (g + 1 < a.count && a.desc[g + 1].tile_start <= tile) ++g;
-    const GroupDesc& d = a.desc[g];
+    while (g + 1 < count && desc[g + 1].tile_start <= tile) ++g;
+    const GroupDesc& d = desc[g];
     const int local = tile - d.tile_start;
     if constexpr (!std::is_void<Small>::value) {
       if (d.M <= SMALL_M) {
-        grouped_tile<DT, KTAIL, Small>(lds, d, local, a.alpha, a.beta);
+        grouped_tile<DT, KTAIL, Small>(lds, d, local, alpha, beta);
         continue;
       }
     }
-    grouped_tile<DT, KTAIL, Cfg>(lds, d, local, a.alpha, a.beta);
+    grouped_tile<DT, KTAIL, Cfg>(lds, d, local, alpha, beta);
   }
+}
+
+template <class Cfg>
+constexpr int grouped_lds() {
+  using Small = typename SmallOf<Cfg>::type;
+  return Cfg::LDS_BYTES > lds_of<Small>() ? Cfg::LDS_BYTES : lds_of<Small>();
+}
+
+template <class Cfg, int DT, bool KTAIL>
+__global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_gemm_grouped(GroupedArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[grouped_lds<Cfg>()];
+  // with device-held group sizes the grid is sized for the device, not the
+  // tiles: workgroups past the total find no tile and return
+  const int total = a.total_tiles >= 0 ? a.total_tiles : *a.total_dev;
+  grouped_walk<Cfg, DT, KTAIL>(lds, a.desc, a.count, total, a.alpha, a.beta);
+}
+
+// Short problem lists travel in the kernel arguments: no staging copy before
+// the launch, which is most of the cost of a call on a few small problems.
+struct GroupedInlineArgs {
+  GroupDesc desc[kInlineGroups];
+  int count, total_tiles;
+  float alpha, beta;
+};
+static_assert(sizeof(GroupedInlineArgs) <= 4096, "kernel arguments are limited to 4 KB");
+
+template <class Cfg, int DT, bool KTAIL>
+__global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_gemm_grouped_inline(GroupedInlineArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[grouped_lds<Cfg>()];
+  grouped_walk<Cfg, DT, KTAIL>(lds, a.desc, a.count, a.total_tiles, a.alpha, a.beta);
 }
 
 // Group table from device-held row offsets (one workgroup, one thread per
@@ -270,6 +298,18 @@ hipError_t launch_grouped(const GroupDesc* desc_dev, int count, int total_tiles,
                           float alpha, float beta, hipStream_t stream) {
   GroupedArgs a{desc_dev, count, total_tiles, nullptr, alpha, beta};
   GMI_DISPATCH(k_gemm_grouped, shape, dtype, ktail, total_tiles, a, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_inline(const GroupDesc* desc, int count, int total_tiles, int shape, int dtype,
+                                 bool ktail, float alpha, float beta, hipStream_t stream) {
+  GroupedInlineArgs a;
+  for (int g = 0; g < count; ++g) a.desc[g] = desc[g];
+  a.count = count;
+  a.total_tiles = total_tiles;
+  a.alpha = alpha;
+  a.beta = beta;
+  GMI_DISPATCH(k_gemm_grouped_inline, shape, dtype, ktail, total_tiles, a, stream);
   return hipGetLastError();
 }
 

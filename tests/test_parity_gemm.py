@@ -218,3 +218,16 @@ def test_output_rounding_is_nearest_even(gmi, dtype):
     ref = oracle.gemm(A, B, dtype=dtype)
     assert np.array_equal(ref, np.repeat(1.0 + a[:, 1:2].astype(np.float64), N, axis=1))
     assert np.array_equal(G.bits(), oracle.round_to(ref, dtype))
+
+
+def test_grouped_inline_and_staged_tables_agree(gmi):
+    # up to 32 problems travel in the kernel arguments, more are staged into the workspace: the same 32 problems
+    # with and without a 33rd give identical bits, and both match the oracle
+    r = np.random.default_rng(33)
+    shapes = [(int(r.integers(1, 300)), int(r.integers(1, 300)), int(r.integers(1, 200))) for _ in range(33)]
+    inline = run_grouped(gmi, shapes[:32], "bf16", 1.0, 0.25, seed=12, ld_pad=8)
+    staged = run_grouped(gmi, shapes, "bf16", 1.0, 0.25, seed=12, ld_pad=8)
+    assert len(inline) == 32 and len(staged) == 33
+    for (a, ref, shp), (b, _, _) in zip(inline, staged):
+        assert np.array_equal(a, b), shp
+        check_close(a, ref, "bf16", f"grouped {shp}")
