@@ -184,11 +184,9 @@ gmi_status gmi_gemm_grouped(const gmi_problem* problems, int32_t count, gmi_dtyp
     return hip_status(launch_grouped_inline(desc.data(), live, (int)tiles, shape, (int)dtype, ktail, alpha, beta, s),
                       "gemm_grouped: launch");
   GroupDesc* dev_desc = (GroupDesc*)((char*)workspace + kWorkspaceHeader);
-  // pageable source: the copy completes before the call returns, so the
-  // host table may be reused immediately
-  gmi_status st = hip_status(
-      hipMemcpyAsync(dev_desc, desc.data(), sizeof(GroupDesc) * desc.size(), hipMemcpyHostToDevice, s),
-      "gemm_grouped: staging the problem table");
+  // the table travels in launch arguments (copied at enqueue), so the host
+  // table may be reused immediately and the host does not wait for the stream
+  gmi_status st = hip_status(stage_table(desc.data(), live, dev_desc, s), "gemm_grouped: staging the problem table");
   if (st != GMI_OK) return st;
   return hip_status(launch_grouped(dev_desc, live, (int)tiles, shape, (int)dtype, ktail, alpha, beta, s),
                     "gemm_grouped: launch");

@@ -108,6 +108,9 @@ hipError_t launch_grouped(const GroupDesc* desc_dev, int count, int total_tiles,
 // up to kInlineGroups problems: the table (host memory) is passed in the
 // kernel arguments instead of being staged into the workspace
 constexpr int kInlineGroups = 32;
+// write a host table into device memory through kernel arguments (no copy
+// from pageable memory, which would wait for the stream)
+hipError_t stage_table(const GroupDesc* desc_host, int count, GroupDesc* dst, hipStream_t stream);
 hipError_t launch_grouped_inline(const GroupDesc* desc_host, int count, int total_tiles, int shape, int dtype,
                                  bool ktail, float alpha, float beta, hipStream_t stream);
 hipError_t launch_grouped_offsets(const OffsetsLaunch& p, int shape, int dtype, float alpha, float beta,

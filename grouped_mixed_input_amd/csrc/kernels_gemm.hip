@@ -301,6 +301,33 @@ hipError_t launch_grouped(const GroupDesc* desc_dev, int count, int total_tiles,
   return hipGetLastError();
 }
 
+// A host problem table written into the workspace by launches whose
+// arguments carry it, kInlineGroups descriptors each: unlike a copy from
+// pageable host memory, a launch does not wait for the work already queued
+// on the stream, so the host goes on while the previous GEMM runs.
+struct TableChunk {
+  GroupDesc desc[kInlineGroups];
+  GroupDesc* dst;
+  int n;
+};
+
+__global__ __launch_bounds__(64) void k_write_table(TableChunk c) {
+  if ((int)threadIdx.x < c.n) c.dst[threadIdx.x] = c.desc[threadIdx.x];
+}
+
+hipError_t stage_table(const GroupDesc* desc, int count, GroupDesc* dst, hipStream_t stream) {
+  for (int g0 = 0; g0 < count; g0 += kInlineGroups) {
+    TableChunk c;
+    c.n = count - g0 < kInlineGroups ? count - g0 : kInlineGroups;
+    for (int i = 0; i < c.n; ++i) c.desc[i] = desc[g0 + i];
+    c.dst = dst + g0;
+    hipLaunchKernelGGL(k_write_table, dim3(1), dim3(64), 0, stream, c);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_grouped_inline(const GroupDesc* desc, int count, int total_tiles, int shape, int dtype,
                                  bool ktail, float alpha, float beta, hipStream_t stream) {
   GroupedInlineArgs a;
