@@ -277,9 +277,10 @@ def conv2d_fprop(x: torch.Tensor, w: torch.Tensor, pad=(0, 0), stride=(1, 1), di
 
 
 def conv2d_dgrad(dy: torch.Tensor, w: torch.Tensor, H: int, W: int, pad=(0, 0), dil=(1, 1), c_in=None, alpha=1.0,
-                 beta=0.0, dx: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                 beta=0.0, dx: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stride=(1, 1),
                  stream=None) -> torch.Tensor:
-    """Data gradient of conv2d_fprop (stride 1): dy NPQK, w KRSC, the forward input's H, W -> dx NHWC."""
+    """Data gradient of conv2d_fprop: dy NPQK, w KRSC, the forward input's H, W -> dx NHWC (stride 1, 2, 4 or
+    8, the same in both dimensions)."""
     N, P, Q, K = dy.shape
     K2, R, S, C = w.shape
     if K2 != K:
@@ -289,7 +290,7 @@ def conv2d_dgrad(dy: torch.Tensor, w: torch.Tensor, H: int, W: int, pad=(0, 0), 
     if workspace is None:
         workspace = torch.empty(lib().gmi_conv2d_dgrad_workspace_bytes(C, K, R, S), dtype=torch.uint8,
                                 device=dy.device)
-    _check(lib().gmi_conv2d_dgrad_implicit(N, H, W, C, K, R, S, pad[0], pad[1], 1, 1, dil[0], dil[1],
+    _check(lib().gmi_conv2d_dgrad_implicit(N, H, W, C, K, R, S, pad[0], pad[1], stride[0], stride[1], dil[0], dil[1],
                                            dy.data_ptr(), w.data_ptr(), _ptr(c_in), dx.data_ptr(), _DT[dy.dtype],
                                            alpha, beta, workspace.data_ptr(), workspace.numel(), _stream(stream)))
     return dx

@@ -471,13 +471,14 @@ gmi_status gmi_conv2d_dgrad_implicit(int32_t N, int32_t H, int32_t W, int32_t C,
     return fail(GMI_ERR_INVALID_ARG, "%s: sizes must be positive (N >= 0)", who);
   if (pad_h < 0 || pad_w < 0 || stride_h < 1 || stride_w < 1 || dil_h < 1 || dil_w < 1)
     return fail(GMI_ERR_INVALID_ARG, "%s: padding >= 0, stride >= 1 and dilation >= 1 required", who);
-  if (stride_h != 1 || stride_w != 1)
-    return fail(GMI_ERR_UNSUPPORTED, "%s: only traversal stride 1 (the non-strided dgrad of the page)", who);
+  if (stride_h != stride_w || (stride_h != 1 && stride_h != 2 && stride_h != 4 && stride_h != 8))
+    return fail(GMI_ERR_UNSUPPORTED, "%s: the traversal stride must be 1, 2, 4 or 8 in both dimensions", who);
   if (!dtype_ok(dtype)) return fail(GMI_ERR_UNSUPPORTED, "%s: dtype %d not supported", who, (int)dtype);
   if (C % 8 || K % 8) return fail(GMI_ERR_MISALIGNED, "%s: C and K must be multiples of 8", who);
-  const int64_t P = (int64_t)H + 2 * (int64_t)pad_h - (int64_t)dil_h * (R - 1);
-  const int64_t Q = (int64_t)W + 2 * (int64_t)pad_w - (int64_t)dil_w * (S - 1);
-  if (P < 1 || Q < 1) return fail(GMI_ERR_INVALID_ARG, "%s: the filter does not fit the padded image", who);
+  const int64_t Ph = (int64_t)H + 2 * (int64_t)pad_h - (int64_t)dil_h * (R - 1) - 1;
+  const int64_t Qw = (int64_t)W + 2 * (int64_t)pad_w - (int64_t)dil_w * (S - 1) - 1;
+  if (Ph < 0 || Qw < 0) return fail(GMI_ERR_INVALID_ARG, "%s: the filter does not fit the padded image", who);
+  const int64_t P = Ph / stride_h + 1, Q = Qw / stride_w + 1;
   if ((int64_t)N * H * W > INT32_MAX || (int64_t)N * P * Q > INT32_MAX || (int64_t)R * S * K > kMaxLd ||
       (int64_t)N * P * Q * K * 2 > INT32_MAX || C > kMaxLd)
     return fail(GMI_ERR_UNSUPPORTED, "%s: dy above 2^31 bytes, R*S*K above 2^22 or too many pixels", who);
@@ -506,8 +507,8 @@ gmi_status gmi_conv2d_dgrad_implicit(int32_t N, int32_t H, int32_t W, int32_t C,
   a.Q = (int)Q;
   a.ph = pad_h;
   a.pw = pad_w;
-  a.sh = 1;
-  a.sw = 1;
+  a.sh = stride_h;
+  a.sw = stride_w;
   a.dh = dil_h;
   a.dw = dil_w;
   const int64_t Mg = (int64_t)N * H * W;

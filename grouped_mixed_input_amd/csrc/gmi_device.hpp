@@ -364,6 +364,11 @@ struct ConvGeom {
   int P, Q;
   int ph, pw, sh, sw, dh, dw;
   int Kg;  // R * S * C
+  // Zero insertion (the strided data gradient): the gather addresses a
+  // virtual input of Hv x Wv pixels in which only coordinates divisible by
+  // 2^ush hold data, pixel (h, w) of x at (h << ush, w << ush).  ush = 0,
+  // Hv = H, Wv = W for the forward pass.
+  int Hv, Wv, ush;
 };
 
 template <class Cfg, int ROWS>
@@ -374,14 +379,18 @@ struct ConvLoader {
   static constexpr int P = ROWS * Cfg::ROWB / (1024 * Cfg::NW);
   static_assert(P >= 1 && ROWS % (Cfg::NW * Cfg::RPI) == 0, "rows must fill whole copy passes");
   rsrc_t rs;
-  int H, W, C, S, dh, dw, Kg;
+  int H, W, C, S, dh, dw, Kg, Hv, Wv, ush, umask;
   int pix[P];        // first pixel of the row's image: n * H * W
-  int h0[P], w0[P];  // input coordinates of tap (0, 0); far negative for rows past M
+  int h0[P], w0[P];  // (virtual) input coordinates of tap (0, 0); far negative for rows past M
 
   __device__ __forceinline__ void init(const ConvGeom& g, int m0, int M) {
     rs = make_rsrc(g.x, g.x_bytes);
     H = g.H;
     W = g.W;
+    Hv = g.Hv;
+    Wv = g.Wv;
+    ush = g.ush;
+    umask = (1 << g.ush) - 1;
     C = g.C;
     S = g.S;
     dh = g.dh;
@@ -420,8 +429,9 @@ struct ConvLoader {
   }
   __device__ __forceinline__ void issue_one(int i, const Prep& p, char* tile) const {
     const int ih = h0[i] + p.dr, iw = w0[i] + p.ds;
-    const bool in = p.kin && (unsigned)ih < (unsigned)H && (unsigned)iw < (unsigned)W;
-    dma16(rs, in ? (uint32_t)((pix[i] + ih * W + iw) * C + p.c) * 2u : OOB, Cfg::dma_dst(tile, i));
+    const bool in = p.kin && (unsigned)ih < (unsigned)Hv && (unsigned)iw < (unsigned)Wv && ((ih | iw) & umask) == 0;
+    dma16(rs, in ? (uint32_t)((pix[i] + (ih >> ush) * W + (iw >> ush)) * C + p.c) * 2u : OOB,
+          Cfg::dma_dst(tile, i));
   }
   __device__ __forceinline__ void issue(int kt, char* tile) const {
     const Prep p = prep(kt);

@@ -64,6 +64,7 @@ struct ConvLaunch {
   const uint16_t* c;
   uint16_t* y;
   int N, H, W, C, K, R, S, P, Q, ph, pw, sh, sw, dh, dw;
+  int ush = 0;  // log2 of the zero insertion of the gathered input (data gradient of a strided pass)
 };
 
 struct W4Launch {

@@ -57,7 +57,16 @@ using ConvCfg128 = TileCfg<128, 128, 2, 2, 32, 4>;
 hipError_t launch_conv_fprop(const ConvLaunch& p, int shape, int dtype, float alpha, float beta,
                              hipStream_t stream) {
   ConvArgs a;
-  a.g = ConvGeom{p.x, (uint32_t)((int64_t)p.N * p.H * p.W * p.C * 2), p.H, p.W, p.C, p.S, p.P, p.Q, p.ph, p.pw, p.sh, p.sw, p.dh, p.dw, p.R * p.S * p.C};
+  a.g = ConvGeom{p.x,   (uint32_t)((int64_t)p.N * p.H * p.W * p.C * 2),
+                 p.H,   p.W,
+                 p.C,   p.S,
+                 p.P,   p.Q,
+                 p.ph,  p.pw,
+                 p.sh,  p.sw,
+                 p.dh,  p.dw,
+                 p.R * p.S * p.C,
+                 ((p.H - 1) << p.ush) + 1, ((p.W - 1) << p.ush) + 1,
+                 p.ush};
   a.w = p.w;
   a.c = p.c;
   a.y = p.y;
@@ -92,12 +101,16 @@ hipError_t launch_conv_fprop(const ConvLaunch& p, int shape, int dtype, float al
 }
 
 // ---------------------------------------------------------------------------
-// Data gradient, stride 1.  The page runs dgrad through the same im2col
-// operand with the filter-tap strides negated: dx[n][h][w][c] sums
+// Data gradient.  The page runs the non-strided dgrad through the same
+// im2col operand with the filter-tap strides negated: dx[n][h][w][c] sums
 // dy[n][h + ph - r dh][w + pw - s dw][k] w[k][r][s][c], which is the forward
-// gather over dy with padding -ph and dilation -dh.  The GEMM's B operand is
-// then the filter with its reduction (r, s, k) contiguous per column c, i.e.
-// w transposed to [C][R][S][K]: one 64 x 64 (k, c) block of one tap per
+// gather over dy with padding -ph and dilation -dh.  A forward stride s
+// (a power of two here) puts dy on every s-th coordinate of a virtual
+// zero-inserted image, dy[n][p][q] at (s p, s q): the same gather, which
+// reads only coordinates divisible by s (the others are zeros, and their
+// products are wasted matrix work, a factor s^2).  The GEMM's B operand is
+// the filter with its reduction (r, s, k) contiguous per column c, i.e. w
+// transposed to [C][R][S][K]: one 64 x 64 (k, c) block of one tap per
 // workgroup, through LDS so reads run along c and writes along k.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_filter_transpose(const uint16_t* __restrict__ w, uint16_t* __restrict__ wt,
@@ -143,6 +156,7 @@ hipError_t launch_conv_dgrad(const ConvLaunch& p, uint16_t* wt, int shape, int d
   f.sw = 1;
   f.dh = -p.dh;
   f.dw = -p.dw;
+  f.ush = p.sh == 1 ? 0 : p.sh == 2 ? 1 : p.sh == 4 ? 2 : 3;  // sh == sw, a power of two
   return launch_conv_fprop(f, shape, dtype, alpha, beta, stream);
 }
 

@@ -1,5 +1,5 @@
-"""GPU parity of the implicit-GEMM conv2d data gradient (stride 1) against the
-fp64 oracle, which computes it as the adjoint of the forward convolution."""
+"""GPU parity of the implicit-GEMM conv2d data gradient against the fp64
+oracle, which computes it as the adjoint of the forward convolution."""
 import numpy as np
 import pytest
 import torch
@@ -19,10 +19,10 @@ def gmi():
     return g
 
 
-def _case(N, H, W, C, K, R, S, pad, dil, dtype, seed):
+def _case(N, H, W, C, K, R, S, pad, dil, dtype, seed, stride=1):
     r = np.random.default_rng(seed)
-    P = oracle.conv_out_size(H, R, pad, 1, dil)
-    Q = oracle.conv_out_size(W, S, pad, 1, dil)
+    P = oracle.conv_out_size(H, R, pad, stride, dil)
+    Q = oracle.conv_out_size(W, S, pad, stride, dil)
     dy = gi.to_bits(r.standard_normal((N, P, Q, K)).astype(np.float32), dtype)
     w = gi.to_bits((r.standard_normal((K, R, S, C)) / np.sqrt(R * S * K)).astype(np.float32), dtype)
     return dy, w
@@ -86,3 +86,21 @@ def test_dgrad_full_size_sampled(gmi):
     pick = [0, 9, 22, 31]
     ref = oracle.conv2d_dgrad(dy[pick], w, H, W, pad=(1, 1))
     check_close(host_bits(dx)[pick], ref, "bf16", f"dgrad full size images {pick}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("N,H,W,C,K,R,S,pad,stride,dil", [
+    (2, 9, 9, 16, 24, 3, 3, 1, 2, 1),     # odd size: the last input row takes fewer taps
+    (1, 16, 12, 32, 16, 3, 3, 1, 2, 1),
+    (2, 13, 11, 8, 40, 3, 3, 2, 2, 2),
+    (1, 17, 17, 24, 8, 5, 5, 2, 4, 1),
+    (1, 8, 8, 8, 16, 1, 1, 0, 2, 1),      # 1x1, stride 2: every other input pixel gets no gradient
+    (1, 30, 20, 16, 16, 3, 3, 0, 8, 1),
+])
+def test_dgrad_strided(gmi, dtype, N, H, W, C, K, R, S, pad, stride, dil):
+    dy, w = _case(N, H, W, C, K, R, S, pad, dil, dtype, seed=N * H + C + stride, stride=stride)
+    dx = gmi.conv2d_dgrad(to_dev(dy, dtype), to_dev(w, dtype), H, W, pad=(pad, pad), dil=(dil, dil),
+                          stride=(stride, stride))
+    torch.cuda.synchronize()
+    ref = oracle.conv2d_dgrad(dy, w, H, W, pad=(pad, pad), stride=(stride, stride), dil=(dil, dil), dtype=dtype)
+    check_close(host_bits(dx), ref, dtype, f"dgrad {N},{H},{W},{C},{K},{R},{S} p{pad} s{stride} d{dil}")
