@@ -328,6 +328,64 @@ int ora_conv2d_fprop(int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int3
 }
 
 /* ------------------------------------------------------------------------
+ * Convolution weight gradient [p3] (the wgrad operator): the adjoint of the
+ * forward map in its filter argument.  Every product the forward pass forms,
+ * x[n][ih][iw][c] * w[k][r][s][c] feeding y[n][p][q][k], sends
+ * dy[n][p][q][k] * x[n][ih][iw][c] back to dw[k][r][s][c]:
+ *   dw[k][r][s][c] = alpha * sum over (n, p, q) with ih = p*sh - ph + r*dh,
+ *                    iw = q*sw - pw + s*dw inside the image
+ *                    of dy[n][p][q][k] * x[n][ih][iw][c]   + beta * C[k][r][s][c]
+ * x NHWC, dy NPQK, dw and C KRSC.
+ * ------------------------------------------------------------------------ */
+int ora_conv2d_wgrad(int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int32_t R, int32_t S, int32_t ph,
+                     int32_t pw, int32_t sh, int32_t sw, int32_t dh, int32_t dw, const uint16_t* x,
+                     const uint16_t* dy, const uint16_t* cin, int32_t dt, double alpha, double beta, double* out) {
+  if (N < 0 || H <= 0 || W <= 0 || C <= 0 || K <= 0 || R <= 0 || S <= 0) return -1;
+  if (ph < 0 || pw < 0 || sh <= 0 || sw <= 0 || dh <= 0 || dw <= 0) return -1;
+  if (beta != 0.0 && !cin) return -1;
+  int64_t P = (H + 2 * (int64_t)ph - (int64_t)dh * (R - 1) - 1) / sh + 1;
+  int64_t Q = (W + 2 * (int64_t)pw - (int64_t)dw * (S - 1) - 1) / sw + 1;
+  if (P <= 0 || Q <= 0) return -1;
+  int64_t nx = (int64_t)N * H * W * C, ny = (int64_t)N * P * Q * K;
+  double* xd = (double*)malloc(sizeof(double) * (size_t)(nx ? nx : 1));
+  double* gd = (double*)malloc(sizeof(double) * (size_t)(ny ? ny : 1));
+  if (!xd || !gd) {
+    free(xd);
+    free(gd);
+    return -1;
+  }
+  for (int64_t i = 0; i < nx; ++i) xd[i] = dec(x[i], dt);
+  for (int64_t i = 0; i < ny; ++i) gd[i] = dec(dy[i], dt);
+  /* one filter tap (k, r, s) per iteration: a plain sum over images and output pixels */
+#pragma omp parallel for schedule(static)
+  for (int64_t krs = 0; krs < (int64_t)K * R * S; ++krs) {
+    int64_t k = krs / (R * S), r = (krs / S) % R, s = krs % S;
+    double* acc = out + krs * C;
+    for (int64_t c = 0; c < C; ++c) acc[c] = 0.0;
+    for (int64_t n = 0; n < N; ++n)
+      for (int64_t p = 0; p < P; ++p) {
+        int64_t ih = p * sh - ph + r * dh;
+        if (ih < 0 || ih >= H) continue;
+        for (int64_t q = 0; q < Q; ++q) {
+          int64_t iw = q * sw - pw + s * dw;
+          if (iw < 0 || iw >= W) continue;
+          double g = gd[((n * P + p) * Q + q) * K + k];
+          const double* xp = xd + ((n * H + ih) * W + iw) * C;
+          for (int64_t c = 0; c < C; ++c) acc[c] += g * xp[c];
+        }
+      }
+    for (int64_t c = 0; c < C; ++c) {
+      double v = alpha * acc[c];
+      if (beta != 0.0) v += beta * dec(cin[krs * C + c], dt);
+      acc[c] = v;
+    }
+  }
+  free(xd);
+  free(gd);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------
  * Convolution data gradient [p3] (the dgrad operator): the adjoint of the
  * forward map above in its first argument.  Every product the forward pass
  * forms, x[n][ih][iw][c] * w[k][r][s][c] feeding y[n][p][q][k], sends

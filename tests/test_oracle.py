@@ -493,6 +493,41 @@ def test_dgrad_beta_term_and_shape_checks():
         oracle.conv2d_dgrad(dy, w, 5, 4, pad=(1, 1))  # dy does not have the forward output's size
 
 
+# ---------------------------------------------------------------- conv wgrad
+@pytest.mark.parametrize("H,R,pad,stride,dil", [(7, 3, 1, 1, 1), (8, 3, 0, 2, 1), (9, 3, 2, 1, 2), (10, 5, 2, 3, 1),
+                                                (6, 1, 0, 1, 1)])
+def test_wgrad_is_the_adjoint_of_fprop_in_the_filter(H, R, pad, stride, dil):
+    # <fprop(x, w), dy> == <w, wgrad(x, dy)> for every w, dy: integer-valued operands make both sides exact
+    N, C, K = 2, 5, 3
+    x = _int_bits((N, H, H + 1, C))
+    w = _int_bits((K, R, R, C))
+    P = oracle.conv_out_size(H, R, pad, stride, dil)
+    Q = oracle.conv_out_size(H + 1, R, pad, stride, dil)
+    dy = _int_bits((N, P, Q, K))
+    y = oracle.conv2d_fprop(x, w, pad=(pad, pad), stride=(stride, stride), dil=(dil, dil))
+    dw = oracle.conv2d_wgrad(x, dy, R, R, pad=(pad, pad), stride=(stride, stride), dil=(dil, dil))
+    assert np.sum(y * lib_decode(dy, "bf16")) == np.sum(lib_decode(w, "bf16") * dw)
+
+
+def test_wgrad_1x1_is_a_gemm_over_pixels():
+    # a 1x1 filter with stride 1 and no padding: dw[k][c] = sum over pixels of dy[.., k] x[.., c], i.e. dy^T x
+    N, H, W, C, K = 2, 5, 6, 7, 4
+    x = bf16_bits(RNG.standard_normal((N, H, W, C)))
+    dy = bf16_bits(RNG.standard_normal((N, H, W, K)))
+    got = oracle.conv2d_wgrad(x, dy, 1, 1)
+    want = lib_decode(dy, "bf16").reshape(-1, K).T @ lib_decode(x, "bf16").reshape(-1, C)
+    np.testing.assert_allclose(got.reshape(K, C), want, rtol=1e-12, atol=1e-12)
+
+
+def test_wgrad_beta_term():
+    x = bf16_bits(RNG.standard_normal((1, 4, 4, 8)))
+    dy = bf16_bits(RNG.standard_normal((1, 4, 4, 3)))
+    c = bf16_bits(RNG.standard_normal((3, 3, 3, 8)))
+    base = oracle.conv2d_wgrad(x, dy, 3, 3, pad=(1, 1))
+    got = oracle.conv2d_wgrad(x, dy, 3, 3, pad=(1, 1), C_in=c, alpha=2.0, beta=-0.5)
+    np.testing.assert_allclose(got, 2.0 * base - 0.5 * lib_decode(c, "bf16"), rtol=1e-14, atol=1e-14)
+
+
 # ---------------------------------------------------------------- prepack
 def test_golden_prepack_positions():
     N, K = 32, 256
