@@ -379,12 +379,14 @@ struct ConvLoader {
   static constexpr int P = ROWS * Cfg::ROWB / (1024 * Cfg::NW);
   static_assert(P >= 1 && ROWS % (Cfg::NW * Cfg::RPI) == 0, "rows must fill whole copy passes");
   rsrc_t rs;
-  int H, W, C, S, dh, dw, Kg, Hv, Wv, ush, umask;
+  int H, W, C, S, dh, dw, Kg, Hv, Wv, ush, umask, kt0;
   int pix[P];        // first pixel of the row's image: n * H * W
   int h0[P], w0[P];  // (virtual) input coordinates of tap (0, 0); far negative for rows past M
 
-  __device__ __forceinline__ void init(const ConvGeom& g, int m0, int M) {
+  // rows m0 .., k-tiles from kt_first on
+  __device__ __forceinline__ void init(const ConvGeom& g, int m0, int M, int kt_first = 0) {
     rs = make_rsrc(g.x, g.x_bytes);
+    kt0 = kt_first;
     H = g.H;
     W = g.W;
     Hv = g.Hv;
@@ -422,7 +424,7 @@ struct ConvLoader {
     bool kin;
   };
   __device__ __forceinline__ Prep prep(int kt) const {
-    const int kc = kt * Cfg::BK + Cfg::dma_chunk(threadIdx.x & 63) * 8;
+    const int kc = (kt + kt0) * Cfg::BK + Cfg::dma_chunk(threadIdx.x & 63) * 8;
     const int rsx = kc / C, c = kc - rsx * C;
     const int r = rsx / S, s = rsx - r * S;
     return Prep{r * dh, s * dw, c, kc < Kg};
@@ -931,6 +933,31 @@ __device__ __forceinline__ void mainloop(char* lds, const ALd& al, const BLd& bl
 // of one row, touch all 64 banks once.  Rows past M are dropped by the
 // store's buffer range; a tile that crosses N stores element by element.
 // ---------------------------------------------------------------------------
+
+// fp32 partial tile: each lane's accumulator runs (4 consecutive n of one
+// row m) stored as they are, rows past M dropped by the buffer range,
+// columns past N skipped
+template <class Cfg>
+__device__ __forceinline__ void store_partial(const Tile& t, const f32x16 (&acc)[Cfg::TM][Cfg::TN], float* P) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = (wave / Cfg::WAVES_N) * Cfg::WTM, wn = (wave % Cfg::WAVES_N) * Cfg::WTN;
+  int rows = t.M - t.m0;
+  if (rows > Cfg::BM) rows = Cfg::BM;
+  const rsrc_t rp = make_rsrc(P + (int64_t)t.m0 * t.N, (uint32_t)rows * (uint32_t)t.N * 4u);
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t row = wm + 32 * i + (lane & 31);
+        const int col = t.n0 + wn + 32 * j + 8 * q + 4 * (lane >> 5);
+        if (col < t.N)
+          buf_store16(rp, (row * (uint32_t)t.N + col) * 4u,
+                      __builtin_bit_cast(u32x4, f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                                      acc[i][j][4 * q + 3]}));
+      }
+}
 
 template <class Cfg, int DT>
 __device__ __forceinline__ void store_tile(const Tile& t, const f32x16 (&acc)[Cfg::TM][Cfg::TN], float alpha,

@@ -65,6 +65,9 @@ struct ConvLaunch {
   uint16_t* y;
   int N, H, W, C, K, R, S, P, Q, ph, pw, sh, sw, dh, dw;
   int ush = 0;  // log2 of the zero insertion of the gathered input (data gradient of a strided pass)
+  // split over the taps into fp32 partials (see k_conv_fprop); 1 / NULL: none
+  int split = 1, kt_split = 1 << 30;
+  float* partial = nullptr;
 };
 
 struct W4Launch {
@@ -121,6 +124,20 @@ hipError_t launch_ptr_array(const PtrArrayLaunch& a, int shape, int dtype, float
 hipError_t launch_conv_fprop(const ConvLaunch& a, int shape, int dtype, float alpha, float beta, hipStream_t stream);
 hipError_t launch_conv_dgrad(const ConvLaunch& a, uint16_t* wt, int shape, int dtype, float alpha, float beta,
                              hipStream_t stream);
+
+// Weight gradient as a forward pass over transposed operands (see
+// kernels_conv.hip): the plan fixes the view, the split over taps and the
+// workspace layout; the workspace size and the launch both use it.
+struct WgradPlan {
+  int N, H, W, C, K, R, S, P, Q, ph, pw, sh, sw, dh, dw;  // the forward problem
+  int N8, Rp, Sp;        // batch rounded up to 8; the view's output taps (>= R, S)
+  int split, kt_split;   // the view's split over its P*Q*N8 taps (64 per k-tile)
+  size_t x_off, dy_off, part_off, bytes;  // workspace layout
+};
+bool plan_wgrad(int N, int H, int W, int C, int K, int R, int S, int ph, int pw, int sh, int sw, int dh, int dw,
+                WgradPlan& p);
+hipError_t launch_conv_wgrad(const WgradPlan& p, const uint16_t* x, const uint16_t* dy, const uint16_t* c_in,
+                             uint16_t* dwt, char* workspace, int dtype, float alpha, float beta, hipStream_t stream);
 hipError_t launch_prepack_w4(const uint8_t* w, int N, int K, uint8_t* out, hipStream_t stream);
 hipError_t launch_w4a16(const W4Launch& a, hipStream_t stream);
 hipError_t launch_w4a16_grouped(const W4Grouped& a, hipStream_t stream);

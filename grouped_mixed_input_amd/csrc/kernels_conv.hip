@@ -19,6 +19,11 @@ struct ConvArgs {
   int M, Nk;  // GEMM M and N
   int tiles_n, total_tiles;
   float alpha, beta;
+  // split over the taps: work item w is tile w / split, k-tiles
+  // (w % split) * kt_split .. + kt_split; with `partial` set, every item
+  // stores its fp32 sum to partial[w % split] ([M][Nk]) instead of y
+  int split, kt_split;
+  float* partial;
 };
 
 // Tile ids run n-tile fastest: the few n-tiles of a pixel block are
@@ -27,13 +32,19 @@ template <class Cfg, int DT>
 __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_conv_fprop(ConvArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
   const int G = gridDim.x;
-  for (int base = 0; base < a.total_tiles; base += G) {
-    const int tile = base + remap_slot(blockIdx.x, G);
-    if (tile >= a.total_tiles) break;
+  const int total = a.total_tiles * a.split;
+  const int nkt = (a.g.Kg + Cfg::BK - 1) / Cfg::BK;
+  for (int base = 0; base < total; base += G) {
+    const int work = base + remap_slot(blockIdx.x, G);
+    if (work >= total) break;
+    const int tile = work / a.split, sidx = work - tile * a.split;
+    const int kt0 = sidx * a.kt_split;
+    const int nk = min(a.kt_split, nkt - kt0);
+    const int k0 = kt0 * Cfg::BK;
     Tile t;
     t.M = a.M;
     t.N = a.Nk;
-    t.K = a.g.Kg;
+    t.K = min(nk * Cfg::BK, a.g.Kg - k0);
     t.m0 = (tile / a.tiles_n) * Cfg::BM;
     t.n0 = (tile % a.tiles_n) * Cfg::BN;
     t.C = a.c;
@@ -42,11 +53,14 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_conv_fprop(Co
     t.ldd = a.Nk;
     ConvLoader<Cfg, Cfg::BM> al;
     DenseLoader<Cfg, Cfg::BN> bl;
-    al.init(a.g, t.m0, t.M);
-    bl.init(a.w, a.g.Kg, t.n0, t.N, t.K);
+    al.init(a.g, t.m0, t.M, kt0);
+    bl.init(a.w + k0, a.g.Kg, t.n0, t.N, t.K);
     f32x16 acc[Cfg::TM][Cfg::TN];
-    mainloop<Cfg, DT>(lds, al, bl, (t.K + Cfg::BK - 1) / Cfg::BK, acc);
-    store_tile<Cfg, DT>(t, acc, a.alpha, a.beta, lds);
+    mainloop<Cfg, DT>(lds, al, bl, nk, acc);
+    if (a.partial)
+      store_partial<Cfg>(t, acc, a.partial + (int64_t)sidx * a.M * a.Nk);
+    else
+      store_tile<Cfg, DT>(t, acc, a.alpha, a.beta, lds);
   }
 }
 
@@ -77,8 +91,11 @@ hipError_t launch_conv_fprop(const ConvLaunch& p, int shape, int dtype, float al
   a.total_tiles = ((a.M + bm - 1) / bm) * a.tiles_n;
   a.alpha = alpha;
   a.beta = beta;
+  a.split = p.split;
+  a.kt_split = p.kt_split;
+  a.partial = p.partial;
   const int resident = device_cu_count() * tile_wgs_per_cu(shape);
-  int grid = (a.total_tiles + XCDS - 1) / XCDS * XCDS;
+  int grid = (a.total_tiles * a.split + XCDS - 1) / XCDS * XCDS;
   if (grid > resident) grid = resident / XCDS * XCDS;
   if (grid < XCDS) grid = XCDS;
   if (shape == TILE_256x256) {
@@ -110,31 +127,40 @@ hipError_t launch_conv_fprop(const ConvLaunch& p, int shape, int dtype, float al
 // reads only coordinates divisible by s (the others are zeros, and their
 // products are wasted matrix work, a factor s^2).  The GEMM's B operand is
 // the filter with its reduction (r, s, k) contiguous per column c, i.e. w
-// transposed to [C][R][S][K]: one 64 x 64 (k, c) block of one tap per
-// workgroup, through LDS so reads run along c and writes along k.
+// transposed to [C][R][S][K].
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_filter_transpose(const uint16_t* __restrict__ w, uint16_t* __restrict__ wt,
-                                                          int K, int RS, int C) {
+// out[c][b][a] = in[a][b][c] for a < A, 0 for A <= a < Ap: one 64 x 64 (a, c)
+// block of one b per workgroup (b in grid z, looping past 65535).
+__global__ __launch_bounds__(256) void k_transpose_outer(const uint16_t* __restrict__ in, uint16_t* __restrict__ out,
+                                                         int A, int B, int C, int Ap) {
   __shared__ uint16_t t[64][65];
-  const int rs = blockIdx.z, k0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int kk = i / 64, cc = i % 64, k = k0 + kk, c = c0 + cc;
-    t[kk][cc] = (k < K && c < C) ? w[((int64_t)k * RS + rs) * C + c] : 0;
+  const int a0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  for (int b = blockIdx.z; b < B; b += gridDim.z) {
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+      const int aa = i / 64, cc = i % 64, a = a0 + aa, c = c0 + cc;
+      t[aa][cc] = (a < A && c < C) ? in[((int64_t)a * B + b) * C + c] : 0;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+      const int cc = i / 64, aa = i % 64, a = a0 + aa, c = c0 + cc;
+      if (a < Ap && c < C) out[((int64_t)c * B + b) * Ap + a] = t[aa][cc];
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int cc = i / 64, kk = i % 64, k = k0 + kk, c = c0 + cc;
-    if (k < K && c < C) wt[((int64_t)c * RS + rs) * K + k] = t[kk][cc];
-  }
+}
+
+static hipError_t transpose_outer(const uint16_t* in, uint16_t* out, int A, int B, int C, int Ap,
+                                  hipStream_t stream) {
+  const dim3 grid((C + 63) / 64, (Ap + 63) / 64, B < 65535 ? B : 65535);
+  hipLaunchKernelGGL(k_transpose_outer, grid, dim3(256), 0, stream, in, out, A, B, C, Ap);
+  return hipGetLastError();
 }
 
 hipError_t launch_conv_dgrad(const ConvLaunch& p, uint16_t* wt, int shape, int dtype, float alpha, float beta,
                              hipStream_t stream) {
   // p describes the forward problem (x: N x H x W x C, y: N x P x Q x K);
   // here p.x is dy, p.y is dx
-  const dim3 tgrid((p.C + 63) / 64, (p.K + 63) / 64, p.R * p.S);
-  hipLaunchKernelGGL(k_filter_transpose, tgrid, dim3(256), 0, stream, p.w, wt, p.K, p.R * p.S, p.C);
-  const hipError_t e = hipGetLastError();
+  const hipError_t e = transpose_outer(p.w, wt, p.K, p.R * p.S, p.C, p.K, stream);
   if (e != hipSuccess) return e;
   ConvLaunch f;  // the forward view: gather over dy, filter [C][R][S][K]
   f.x = p.x;
@@ -158,6 +184,140 @@ hipError_t launch_conv_dgrad(const ConvLaunch& p, uint16_t* wt, int shape, int d
   f.dw = -p.dw;
   f.ush = p.sh == 1 ? 0 : p.sh == 2 ? 1 : p.sh == 4 ? 2 : 3;  // sh == sw, a power of two
   return launch_conv_fprop(f, shape, dtype, alpha, beta, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Weight gradient.  dw[k][r][s][c] sums dy[n][p][q][k] x[n][p sh - ph + r dh]
+// [q sw - pw + s dw][c] over images and output pixels.  Read with the images
+// as channels, this is itself a forward convolution: each input channel c is
+// an "image" of H x W pixels with N channels, each k a "filter" of P x Q taps
+// over those N channels, and the forward pass's dilation and stride trade
+// places:
+//   out[c][r][s][k] = sum_{p,q,n} X[c][r dh - ph + p sh][s dw - pw + q sw][n] F[k][p][q][n]
+// with X[c][h][w][n] = x[n][h][w][c] and F[k][p][q][n] = dy[n][p][q][k].  The
+// page runs wgrad with the activation as the im2col operand and dy tiled;
+// here the two transposes put both in the channel-innermost layout the
+// forward kernel gathers, with the batch padded to a multiple of 8 by zeros.
+// The view's reduction (P*Q*N taps) is long and its output (C*R*S x K) small,
+// so it is split over taps into fp32 partials, which a last launch sums in a
+// fixed order, scales, adds beta * C, rounds and transposes to KRSC.
+// ---------------------------------------------------------------------------
+using WgradCfg = ConvCfg256;
+
+bool plan_wgrad(int N, int H, int W, int C, int K, int R, int S, int ph, int pw, int sh, int sw, int dh, int dw,
+                WgradPlan& p) {
+  p.N = N;
+  p.H = H;
+  p.W = W;
+  p.C = C;
+  p.K = K;
+  p.R = R;
+  p.S = S;
+  p.ph = ph;
+  p.pw = pw;
+  p.sh = sh;
+  p.sw = sw;
+  p.dh = dh;
+  p.dw = dw;
+  const int64_t ph2 = (int64_t)H + 2 * ph - (int64_t)dh * (R - 1) - 1, pw2 = (int64_t)W + 2 * pw - (int64_t)dw * (S - 1) - 1;
+  if (ph2 < 0 || pw2 < 0) return false;
+  p.P = (int)(ph2 / sh + 1);
+  p.Q = (int)(pw2 / sw + 1);
+  p.N8 = (N + 7) / 8 * 8;
+  // the view's output size: (H + 2 ph - sh (P - 1) - 1) / dh + 1 >= R
+  p.Rp = (int)(((int64_t)H + 2 * ph - (int64_t)sh * (p.P - 1) - 1) / dh + 1);
+  p.Sp = (int)(((int64_t)W + 2 * pw - (int64_t)sw * (p.Q - 1) - 1) / dw + 1);
+  if (p.Rp < R || p.Sp < S) return false;
+  const int64_t Mv = (int64_t)C * p.Rp * p.Sp, Kg = (int64_t)p.P * p.Q * p.N8;
+  const int64_t tiles = (Mv + WgradCfg::BM - 1) / WgradCfg::BM * ((K + WgradCfg::BN - 1) / WgradCfg::BN);
+  const int64_t nkt = (Kg + WgradCfg::BK - 1) / WgradCfg::BK;
+  int64_t split = (device_cu_count() + tiles - 1) / tiles;  // one work item per CU at least
+  if (split > nkt / 8) split = nkt / 8;                     // at least 8 k-tiles per item
+  if (split < 1) split = 1;
+  p.kt_split = (int)((nkt + split - 1) / split);
+  p.split = (int)((nkt + p.kt_split - 1) / p.kt_split);
+  auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+  p.x_off = 0;
+  p.dy_off = up((size_t)C * H * W * p.N8 * 2);
+  p.part_off = p.dy_off + up((size_t)K * p.P * p.Q * p.N8 * 2);
+  p.bytes = p.part_off + up((size_t)p.split * Mv * K * 4);
+  return true;
+}
+
+// dw[k][r][s][c] = RN(alpha * sum over splits of part[.][(c Rp + r) Sp + s][k]
+// + beta * c_in[k][r][s][c]): one 64 x 64 (c, k) block of one tap per
+// workgroup, read along k, written along c.
+template <int DT>
+__global__ __launch_bounds__(256) void k_wgrad_finish(const float* __restrict__ part, int split, int C, int K, int R,
+                                                      int S, int Rp, int Sp, const uint16_t* __restrict__ cin,
+                                                      float alpha, float beta, uint16_t* __restrict__ dw) {
+  __shared__ float t[64][65];
+  const int rs = blockIdx.z, r = rs / S, s = rs % S;
+  const int c0 = blockIdx.x * 64, k0 = blockIdx.y * 64;
+  const int64_t plane = (int64_t)C * Rp * Sp * K;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int cc = i / 64, kk = i % 64, c = c0 + cc, k = k0 + kk;
+    float v = 0.0f;
+    if (c < C && k < K) {
+      const float* src = part + ((int64_t)(c * Rp + r) * Sp + s) * K + k;
+      for (int sp = 0; sp < split; ++sp) v += src[sp * plane];
+    }
+    t[cc][kk] = v;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int kk = i / 64, cc = i % 64, c = c0 + cc, k = k0 + kk;
+    if (c < C && k < K) {
+      const int64_t o = ((int64_t)(k * R + r) * S + s) * C + c;
+      float v = alpha * t[cc][kk];
+      if (cin) v += beta * from_bits<DT>(cin[o]);
+      dw[o] = (uint16_t)to_bits<DT>(v);
+    }
+  }
+}
+
+hipError_t launch_conv_wgrad(const WgradPlan& p, const uint16_t* x, const uint16_t* dy, const uint16_t* c_in,
+                             uint16_t* dwt, char* workspace, int dtype, float alpha, float beta, hipStream_t stream) {
+  uint16_t* xt = (uint16_t*)(workspace + p.x_off);
+  uint16_t* gt = (uint16_t*)(workspace + p.dy_off);
+  float* part = (float*)(workspace + p.part_off);
+  hipError_t e = transpose_outer(x, xt, p.N, p.H * p.W, p.C, p.N8, stream);
+  if (e != hipSuccess) return e;
+  e = transpose_outer(dy, gt, p.N, p.P * p.Q, p.K, p.N8, stream);
+  if (e != hipSuccess) return e;
+  ConvLaunch f;  // the forward view
+  f.x = xt;
+  f.w = gt;
+  f.c = nullptr;
+  f.y = nullptr;
+  f.N = p.C;
+  f.H = p.H;
+  f.W = p.W;
+  f.C = p.N8;
+  f.K = p.K;
+  f.R = p.P;
+  f.S = p.Q;
+  f.P = p.Rp;
+  f.Q = p.Sp;
+  f.ph = p.ph;
+  f.pw = p.pw;
+  f.sh = p.dh;
+  f.sw = p.dw;
+  f.dh = p.sh;
+  f.dw = p.sw;
+  f.split = p.split;
+  f.kt_split = p.kt_split;
+  f.partial = part;
+  e = launch_conv_fprop(f, TILE_256x256, dtype, 1.0f, 0.0f, stream);
+  if (e != hipSuccess) return e;
+  const dim3 grid((p.C + 63) / 64, (p.K + 63) / 64, p.R * p.S);
+  if (dtype == DT_F16)
+    hipLaunchKernelGGL(k_wgrad_finish<DT_F16>, grid, dim3(256), 0, stream, part, p.split, p.C, p.K, p.R, p.S, p.Rp,
+                       p.Sp, c_in, alpha, beta, dwt);
+  else
+    hipLaunchKernelGGL(k_wgrad_finish<DT_BF16>, grid, dim3(256), 0, stream, part, p.split, p.C, p.K, p.R, p.S, p.Rp,
+                       p.Sp, c_in, alpha, beta, dwt);
+  return hipGetLastError();
 }
 
 }  // namespace gmi

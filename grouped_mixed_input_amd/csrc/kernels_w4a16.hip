@@ -325,31 +325,6 @@ __global__ __launch_bounds__(64 * KW) void k_w4a16_decode(W4Launch a) {
 // Large-M kernel: the dense mainloop, X as the A operand, the prepacked
 // weight (dequantised on its way into LDS) as the column-major B operand.
 // ---------------------------------------------------------------------------
-// fp32 partial tile: each lane's accumulator runs (4 consecutive n of one
-// row m) stored as they are, rows past M dropped by the buffer range,
-// columns past N skipped
-template <class Cfg>
-__device__ __forceinline__ void store_partial(const Tile& t, const f32x16 (&acc)[Cfg::TM][Cfg::TN], float* P) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = (wave / Cfg::WAVES_N) * Cfg::WTM, wn = (wave % Cfg::WAVES_N) * Cfg::WTN;
-  int rows = t.M - t.m0;
-  if (rows > Cfg::BM) rows = Cfg::BM;
-  const rsrc_t rp = make_rsrc(P + (int64_t)t.m0 * t.N, (uint32_t)rows * (uint32_t)t.N * 4u);
-#pragma unroll
-  for (int i = 0; i < Cfg::TM; ++i)
-#pragma unroll
-    for (int j = 0; j < Cfg::TN; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t row = wm + 32 * i + (lane & 31);
-        const int col = t.n0 + wn + 32 * j + 8 * q + 4 * (lane >> 5);
-        if (col < t.N)
-          buf_store16(rp, (row * (uint32_t)t.N + col) * 4u,
-                      __builtin_bit_cast(u32x4, f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                                      acc[i][j][4 * q + 3]}));
-      }
-}
-
 // Work item w = tile * split + s: output tile `tile`, k-range s of `split`
 // equal ranges (whole 128-k blocks).  Unsplit, the epilogue rounds to fp16
 // into Y; split, the fp32 partial goes to partial[s] and k_w4a16_sum adds

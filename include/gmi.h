@@ -301,6 +301,37 @@ size_t gmi_conv2d_dgrad_workspace_bytes(int32_t C, int32_t K, int32_t R, int32_t
  * The traversal stride must be 1, 2, 4 or 8 and equal in both dimensions,
  * else GMI_ERR_UNSUPPORTED.  Other rules as for the forward pass: C % 8 == 0
  * and K % 8 == 0, 16-byte aligned pointers, c_in NULL iff beta == 0. */
+/* Bytes of the workspace gmi_conv2d_wgrad_implicit needs for this problem
+ * on the current device (the transposed operands and fp32 partial sums of
+ * the split over taps); 0 if the problem is rejected. */
+size_t gmi_conv2d_wgrad_workspace_bytes(int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int32_t R, int32_t S,
+                                        int32_t pad_h, int32_t pad_w, int32_t stride_h, int32_t stride_w,
+                                        int32_t dil_h, int32_t dil_w);
+
+/* Implicit-GEMM conv2d weight gradient (the page's wgrad operator), the
+ * adjoint of gmi_conv2d_fprop_implicit in its filter:
+ *   dw[k][r][s][c] = alpha * sum over (n, p, q) of dy[n][p][q][k] *
+ *                    x[n][p*sh - ph + r*dh][q*sw - pw + s*dw][c]   (taps inside the image)
+ *                    + beta * c_in[k][r][s][c]
+ * Arguments describe the forward problem: x NHWC (N x H x W x C), dy NPQK
+ * with P, Q as for the forward pass, dw and c_in KRSC.  The page gathers the
+ * activation as the im2col operand with dy tiled; here the sum is computed
+ * as a forward convolution of the channel-major activation (each channel an
+ * image whose channels are the batch) with dy as the filter, stride and
+ * dilation exchanged, after two transposes into `workspace`; it is split over
+ * taps into fp32 partials that a last launch sums in a fixed order, scales,
+ * rounds to nearest even and writes as KRSC.
+ *   workspace  at least gmi_conv2d_wgrad_workspace_bytes(...) bytes, 16-byte
+ *              aligned, scratch for the call.
+ * Requires N >= 1, C % 8 == 0 and K % 8 == 0 (else GMI_ERR_MISALIGNED),
+ * stride and dilation in [1, 8], 16-byte aligned pointers, c_in NULL iff
+ * beta == 0. */
+gmi_status gmi_conv2d_wgrad_implicit(int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int32_t R, int32_t S,
+                                     int32_t pad_h, int32_t pad_w, int32_t stride_h, int32_t stride_w,
+                                     int32_t dil_h, int32_t dil_w, const void* x, const void* dy, const void* c_in,
+                                     void* dw, gmi_dtype dtype, float alpha, float beta, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
 gmi_status gmi_conv2d_dgrad_implicit(int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int32_t R, int32_t S,
                                      int32_t pad_h, int32_t pad_w, int32_t stride_h, int32_t stride_w,
                                      int32_t dil_h, int32_t dil_w, const void* dy, const void* w, const void* c_in,

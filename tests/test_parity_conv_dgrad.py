@@ -62,7 +62,7 @@ def test_dgrad_alpha_beta_and_guarded_output(gmi):
 
 
 def test_dgrad_integer_inputs_bit_exact(gmi):
-    # small integers: every product and partial sum is exact in fp32, so the result must equal the oracle exactly
+    # small integers: every product and partial sum is exact in fp32, so the result is the RNE of the exact value
     N, H, W, C, K = 2, 12, 9, 24, 16
     r = np.random.default_rng(5)
     P, Q = H, W  # 3x3, pad 1
@@ -71,7 +71,7 @@ def test_dgrad_integer_inputs_bit_exact(gmi):
     dx = gmi.conv2d_dgrad(to_dev(dy, "bf16"), to_dev(w, "bf16"), H, W, pad=(1, 1))
     torch.cuda.synchronize()
     ref = oracle.conv2d_dgrad(dy, w, H, W, pad=(1, 1))
-    assert np.array_equal(oracle.decode(host_bits(dx), "bf16"), ref)
+    assert np.array_equal(host_bits(dx), oracle.round_to(ref, "bf16"))
 
 
 def test_dgrad_full_size_sampled(gmi):
