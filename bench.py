@@ -239,6 +239,13 @@ def bench_workloads(torch, gmi, gi, dev, args):
     ms = time_launches(torch, lambda i: gmi.conv2d_dgrad(sets[i][2], sets[i][1], 56, 56, pad=(1, 1), dx=sets[i][0],
                                                          workspace=wsd), R, 5, max(20, 2 * R))
     out["conv_dgrad_bf16"] = dict(roof(2.0 * 100352 * 256 * 2304, ws, ms), bound="mfma")
+    # and its weight gradient (x and dy of the same shapes; transposes and the split sum included)
+    dws = torch.empty((256, 3, 3, 256), dtype=torch.bfloat16, device=dev)
+    wsw = torch.empty(gmi.conv2d_wgrad_workspace_bytes((32, 56, 56, 256), (32, 56, 56, 256), 3, 3, (1, 1)),
+                      dtype=torch.uint8, device=dev)
+    ms = time_launches(torch, lambda i: gmi.conv2d_wgrad(sets[i][0], sets[i][2], 3, 3, pad=(1, 1), dw=dws,
+                                                         workspace=wsw), R, 3, max(10, 2 * R))
+    out["conv_wgrad_bf16"] = dict(roof(2.0 * 100352 * 256 * 2304, ws, ms), bound="mfma")
     log("bench: conv done")
     del sets
     torch.cuda.empty_cache()
