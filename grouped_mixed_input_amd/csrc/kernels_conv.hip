@@ -19,9 +19,11 @@ struct ConvArgs {
   int M, Nk;  // GEMM M and N
   int tiles_n, total_tiles;
   float alpha, beta;
-  // split over the taps: work item w is tile w / split, k-tiles
-  // (w % split) * kt_split .. + kt_split; with `partial` set, every item
-  // stores its fp32 sum to partial[w % split] ([M][Nk]) instead of y
+  // split over the taps: work item w is tile w % total_tiles, k-tiles
+  // (w / total_tiles) * kt_split .. + kt_split -- the tiles of one tap range
+  // run together and share its filter slice in L2; with `partial` set,
+  // every item stores its fp32 sum to partial[w / total_tiles] ([M][Nk])
+  // instead of y
   int split, kt_split;
   float* partial;
 };
@@ -37,7 +39,7 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_conv_fprop(Co
   for (int base = 0; base < total; base += G) {
     const int work = base + remap_slot(blockIdx.x, G);
     if (work >= total) break;
-    const int tile = work / a.split, sidx = work - tile * a.split;
+    const int sidx = work / a.total_tiles, tile = work - sidx * a.total_tiles;
     const int kt0 = sidx * a.kt_split;
     const int nk = min(a.kt_split, nkt - kt0);
     const int k0 = kt0 * Cfg::BK;
@@ -130,20 +132,36 @@ hipError_t launch_conv_fprop(const ConvLaunch& p, int shape, int dtype, float al
 // transposed to [C][R][S][K].
 // ---------------------------------------------------------------------------
 // out[c][b][a] = in[a][b][c] for a < A, 0 for A <= a < Ap: one 64 x 64 (a, c)
-// block of one b per workgroup (b in grid z, looping past 65535).
+// block of one b per workgroup (b in grid z, looping past 65535), moved in
+// 16-byte runs: 8 consecutive c on the way in, 8 consecutive a on the way out
+// (C % 8 == 0 and Ap % 8 == 0).
 __global__ __launch_bounds__(256) void k_transpose_outer(const uint16_t* __restrict__ in, uint16_t* __restrict__ out,
                                                          int A, int B, int C, int Ap) {
-  __shared__ uint16_t t[64][65];
+  __shared__ uint16_t t[64][72];
   const int a0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int row = threadIdx.x / 8, vec = threadIdx.x % 8;
   for (int b = blockIdx.z; b < B; b += gridDim.z) {
-    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-      const int aa = i / 64, cc = i % 64, a = a0 + aa, c = c0 + cc;
-      t[aa][cc] = (a < A && c < C) ? in[((int64_t)a * B + b) * C + c] : 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int aa = row + 32 * j, a = a0 + aa, c = c0 + vec * 8;
+      u32x4 v = {0, 0, 0, 0};
+      if (a < A && c < C) v = *(const u32x4*)(in + ((int64_t)a * B + b) * C + c);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        t[aa][vec * 8 + 2 * e] = (uint16_t)(v[e] & 0xffffu);
+        t[aa][vec * 8 + 2 * e + 1] = (uint16_t)(v[e] >> 16);
+      }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-      const int cc = i / 64, aa = i % 64, a = a0 + aa, c = c0 + cc;
-      if (a < Ap && c < C) out[((int64_t)c * B + b) * Ap + a] = t[aa][cc];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int cc = row + 32 * j, c = c0 + cc, a = a0 + vec * 8;
+      if (c < C && a < Ap) {
+        u32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (uint32_t)t[vec * 8 + 2 * e][cc] | ((uint32_t)t[vec * 8 + 2 * e + 1][cc] << 16);
+        *(u32x4*)(out + ((int64_t)c * B + b) * Ap + a) = v;
+      }
     }
     __syncthreads();
   }
@@ -245,33 +263,55 @@ bool plan_wgrad(int N, int H, int W, int C, int K, int R, int S, int ph, int pw,
 }
 
 // dw[k][r][s][c] = RN(alpha * sum over splits of part[.][(c Rp + r) Sp + s][k]
-// + beta * c_in[k][r][s][c]): one 64 x 64 (c, k) block of one tap per
-// workgroup, read along k, written along c.
+// + beta * c_in[k][r][s][c]): one 32 x 64 (c, k) block of one tap per
+// workgroup, read along k (eight independent sums per thread, so the loads
+// of a split are in flight together), written along c.
 template <int DT>
 __global__ __launch_bounds__(256) void k_wgrad_finish(const float* __restrict__ part, int split, int C, int K, int R,
                                                       int S, int Rp, int Sp, const uint16_t* __restrict__ cin,
                                                       float alpha, float beta, uint16_t* __restrict__ dw) {
-  __shared__ float t[64][65];
+  __shared__ float t[32][65];
   const int rs = blockIdx.z, r = rs / S, s = rs % S;
-  const int c0 = blockIdx.x * 64, k0 = blockIdx.y * 64;
+  const int c0 = blockIdx.x * 32, k0 = blockIdx.y * 64;
   const int64_t plane = (int64_t)C * Rp * Sp * K;
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int cc = i / 64, kk = i % 64, c = c0 + cc, k = k0 + kk;
-    float v = 0.0f;
-    if (c < C && k < K) {
-      const float* src = part + ((int64_t)(c * Rp + r) * Sp + s) * K + k;
-      for (int sp = 0; sp < split; ++sp) v += src[sp * plane];
-    }
-    t[cc][kk] = v;
+  const int kk = threadIdx.x % 64, cb = threadIdx.x / 64;  // this thread: k0 + kk, rows c0 + cb + 4 j
+  const int k = k0 + kk;
+  float v[8];
+  const float* src[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int c = c0 + cb + 4 * j;
+    v[j] = 0.0f;
+    src[j] = (c < C && k < K) ? part + ((int64_t)(c * Rp + r) * Sp + s) * K + k : nullptr;
   }
+  // four splits per round trip (32 loads in flight per thread), in order
+  int sp = 0;
+  for (; sp + 4 <= split; sp += 4) {
+    float u[4][8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) u[q][j] = src[j] ? src[j][(sp + q) * plane] : 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] += u[q][j];
+  }
+  for (; sp < split; ++sp) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (src[j]) v[j] += src[j][sp * plane];
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) t[cb + 4 * j][kk] = v[j];
   __syncthreads();
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int kk = i / 64, cc = i % 64, c = c0 + cc, k = k0 + kk;
-    if (c < C && k < K) {
-      const int64_t o = ((int64_t)(k * R + r) * S + s) * C + c;
-      float v = alpha * t[cc][kk];
-      if (cin) v += beta * from_bits<DT>(cin[o]);
-      dw[o] = (uint16_t)to_bits<DT>(v);
+  for (int i = threadIdx.x; i < 32 * 64; i += 256) {
+    const int ko = i / 32, cc = i % 32, c = c0 + cc, kx = k0 + ko;
+    if (c < C && kx < K) {
+      const int64_t o = ((int64_t)(kx * R + r) * S + s) * C + c;
+      float x = alpha * t[cc][ko];
+      if (cin) x += beta * from_bits<DT>(cin[o]);
+      dw[o] = (uint16_t)to_bits<DT>(x);
     }
   }
 }
@@ -310,7 +350,7 @@ hipError_t launch_conv_wgrad(const WgradPlan& p, const uint16_t* x, const uint16
   f.partial = part;
   e = launch_conv_fprop(f, TILE_256x256, dtype, 1.0f, 0.0f, stream);
   if (e != hipSuccess) return e;
-  const dim3 grid((p.C + 63) / 64, (p.K + 63) / 64, p.R * p.S);
+  const dim3 grid((p.C + 31) / 32, (p.K + 63) / 64, p.R * p.S);
   if (dtype == DT_F16)
     hipLaunchKernelGGL(k_wgrad_finish<DT_F16>, grid, dim3(256), 0, stream, part, p.split, p.C, p.K, p.R, p.S, p.Rp,
                        p.Sp, c_in, alpha, beta, dwt);
