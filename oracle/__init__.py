@@ -70,6 +70,8 @@ def _load():
     lib.ora_conv2d_dgrad.argtypes = [_i32] * 13 + [_p, _p, _p, _i32, _d, _d, _p]
     lib.ora_conv2d_wgrad.argtypes = [_i32] * 13 + [_p, _p, _p, _i32, _d, _d, _p]
     lib.ora_conv2d_wgrad.restype = ctypes.c_int
+    lib.ora_conv2d_wgrad_grouped.argtypes = [_i32] * 14 + [_p, _p, _p, _i32, _d, _d, _p]
+    lib.ora_conv2d_wgrad_grouped.restype = ctypes.c_int
     lib.ora_conv2d_dgrad.restype = ctypes.c_int
     lib.ora_prepack_w4.argtypes = [_i32, _i32, _p, _p]
     lib.ora_prepack_w4.restype = ctypes.c_int
@@ -231,9 +233,10 @@ def conv2d_dgrad(dy, w, H, W, *, pad=(0, 0), stride=(1, 1), dil=(1, 1), C_in=Non
 
 
 def conv2d_wgrad(x, dy, R, S, *, pad=(0, 0), stride=(1, 1), dil=(1, 1), C_in=None, alpha=1.0, beta=0.0,
-                 dtype="bf16") -> np.ndarray:
+                 dtype="bf16", groups=1) -> np.ndarray:
     """Filter gradient of conv2d_fprop: x uint16 [N][H][W][C], dy uint16 [N][P][Q][K], the filter size R, S;
-    C_in uint16 [K][R][S][C] or None.  Returns float64 [K][R][S][C]."""
+    C_in uint16 [K][R][S][C/groups] or None.  With groups, output channel k sees only the input channels of its
+    group.  Returns float64 [K][R][S][C/groups]."""
     x = _c(x, np.uint16)
     dy = _c(dy, np.uint16)
     N, H, W, C = x.shape
@@ -241,10 +244,10 @@ def conv2d_wgrad(x, dy, R, S, *, pad=(0, 0), stride=(1, 1), dil=(1, 1), C_in=Non
     assert N == N2
     assert P == conv_out_size(H, R, pad[0], stride[0], dil[0]) and Q == conv_out_size(W, S, pad[1], stride[1], dil[1])
     ci = None if C_in is None else _c(C_in, np.uint16)
-    out = np.empty((K, R, S, C), np.float64)
-    rc = _load().ora_conv2d_wgrad(N, H, W, C, K, R, S, pad[0], pad[1], stride[0], stride[1], dil[0], dil[1],
-                                  _ptr(x), _ptr(dy), _ptr(ci), DTYPES[dtype], float(alpha), float(beta),
-                                  _ptr(out))
+    out = np.empty((K, R, S, C // groups), np.float64)
+    rc = _load().ora_conv2d_wgrad_grouped(N, H, W, C, K, R, S, pad[0], pad[1], stride[0], stride[1], dil[0],
+                                          dil[1], groups, _ptr(x), _ptr(dy), _ptr(ci), DTYPES[dtype], float(alpha),
+                                          float(beta), _ptr(out))
     if rc:
         raise ValueError("ora_conv2d_wgrad rejected its arguments")
     return out

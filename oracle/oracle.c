@@ -337,10 +337,26 @@ int ora_conv2d_fprop(int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int3
  *                    of dy[n][p][q][k] * x[n][ih][iw][c]   + beta * C[k][r][s][c]
  * x NHWC, dy NPQK, dw and C KRSC.
  * ------------------------------------------------------------------------ */
+/* With channel groups (the grouped wgrad): output channel k belongs to group
+ * g = k / (K/G) and sees only input channels g*(C/G) + c, c < C/G; dw and C
+ * are [K][R][S][C/G].  G = 1 is the plain weight gradient. */
+int ora_conv2d_wgrad_grouped(int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int32_t R, int32_t S, int32_t ph,
+                             int32_t pw, int32_t sh, int32_t sw, int32_t dh, int32_t dw, int32_t G,
+                             const uint16_t* x, const uint16_t* dy, const uint16_t* cin, int32_t dt, double alpha,
+                             double beta, double* out);
+
 int ora_conv2d_wgrad(int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int32_t R, int32_t S, int32_t ph,
                      int32_t pw, int32_t sh, int32_t sw, int32_t dh, int32_t dw, const uint16_t* x,
                      const uint16_t* dy, const uint16_t* cin, int32_t dt, double alpha, double beta, double* out) {
+  return ora_conv2d_wgrad_grouped(N, H, W, C, K, R, S, ph, pw, sh, sw, dh, dw, 1, x, dy, cin, dt, alpha, beta, out);
+}
+
+int ora_conv2d_wgrad_grouped(int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int32_t R, int32_t S, int32_t ph,
+                             int32_t pw, int32_t sh, int32_t sw, int32_t dh, int32_t dw, int32_t G,
+                             const uint16_t* x, const uint16_t* dy, const uint16_t* cin, int32_t dt, double alpha,
+                             double beta, double* out) {
   if (N < 0 || H <= 0 || W <= 0 || C <= 0 || K <= 0 || R <= 0 || S <= 0) return -1;
+  if (G <= 0 || C % G || K % G) return -1;
   if (ph < 0 || pw < 0 || sh <= 0 || sw <= 0 || dh <= 0 || dw <= 0) return -1;
   if (beta != 0.0 && !cin) return -1;
   int64_t P = (H + 2 * (int64_t)ph - (int64_t)dh * (R - 1) - 1) / sh + 1;
@@ -356,12 +372,14 @@ int ora_conv2d_wgrad(int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int3
   }
   for (int64_t i = 0; i < nx; ++i) xd[i] = dec(x[i], dt);
   for (int64_t i = 0; i < ny; ++i) gd[i] = dec(dy[i], dt);
+  const int64_t Cg = C / G, Kg = K / G;
   /* one filter tap (k, r, s) per iteration: a plain sum over images and output pixels */
 #pragma omp parallel for schedule(static)
   for (int64_t krs = 0; krs < (int64_t)K * R * S; ++krs) {
     int64_t k = krs / (R * S), r = (krs / S) % R, s = krs % S;
-    double* acc = out + krs * C;
-    for (int64_t c = 0; c < C; ++c) acc[c] = 0.0;
+    int64_t c0 = (k / Kg) * Cg; /* the group's first input channel */
+    double* acc = out + krs * Cg;
+    for (int64_t c = 0; c < Cg; ++c) acc[c] = 0.0;
     for (int64_t n = 0; n < N; ++n)
       for (int64_t p = 0; p < P; ++p) {
         int64_t ih = p * sh - ph + r * dh;
@@ -370,13 +388,13 @@ int ora_conv2d_wgrad(int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int3
           int64_t iw = q * sw - pw + s * dw;
           if (iw < 0 || iw >= W) continue;
           double g = gd[((n * P + p) * Q + q) * K + k];
-          const double* xp = xd + ((n * H + ih) * W + iw) * C;
-          for (int64_t c = 0; c < C; ++c) acc[c] += g * xp[c];
+          const double* xp = xd + ((n * H + ih) * W + iw) * C + c0;
+          for (int64_t c = 0; c < Cg; ++c) acc[c] += g * xp[c];
         }
       }
-    for (int64_t c = 0; c < C; ++c) {
+    for (int64_t c = 0; c < Cg; ++c) {
       double v = alpha * acc[c];
-      if (beta != 0.0) v += beta * dec(cin[krs * C + c], dt);
+      if (beta != 0.0) v += beta * dec(cin[krs * Cg + c], dt);
       acc[c] = v;
     }
   }

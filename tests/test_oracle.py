@@ -519,6 +519,22 @@ def test_wgrad_1x1_is_a_gemm_over_pixels():
     np.testing.assert_allclose(got.reshape(K, C), want, rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("G", [2, 4])
+def test_grouped_wgrad_is_the_wgrad_of_each_channel_slice(G):
+    # output channels of group g see only input channels g*C/G ..: the grouped result equals the plain weight
+    # gradient of each group's channel slices
+    N, H, C, K, R = 2, 7, 8, 12, 3
+    x = bf16_bits(RNG.standard_normal((N, H, H, C)))
+    dy = bf16_bits(RNG.standard_normal((N, H, H, K)))
+    got = oracle.conv2d_wgrad(x, dy, R, R, pad=(1, 1), groups=G)
+    assert got.shape == (K, R, R, C // G)
+    cg, kg = C // G, K // G
+    for g in range(G):
+        part = oracle.conv2d_wgrad(np.ascontiguousarray(x[..., g * cg:(g + 1) * cg]),
+                                   np.ascontiguousarray(dy[..., g * kg:(g + 1) * kg]), R, R, pad=(1, 1))
+        assert np.array_equal(got[g * kg:(g + 1) * kg], part)
+
+
 def test_wgrad_beta_term():
     x = bf16_bits(RNG.standard_normal((1, 4, 4, 8)))
     dy = bf16_bits(RNG.standard_normal((1, 4, 4, 3)))
