@@ -80,9 +80,9 @@ def lib() -> ctypes.CDLL:
     L.gmi_conv2d_dgrad_implicit.restype = ctypes.c_int
     L.gmi_conv2d_dgrad_implicit.argtypes = [_i32] * 13 + [_p, _p, _p, _p, ctypes.c_int, _f32, _f32, _p, _sz, _p]
     L.gmi_conv2d_wgrad_workspace_bytes.restype = _sz
-    L.gmi_conv2d_wgrad_workspace_bytes.argtypes = [_i32] * 13
+    L.gmi_conv2d_wgrad_workspace_bytes.argtypes = [_i32] * 14
     L.gmi_conv2d_wgrad_implicit.restype = ctypes.c_int
-    L.gmi_conv2d_wgrad_implicit.argtypes = [_i32] * 13 + [_p, _p, _p, _p, ctypes.c_int, _f32, _f32, _p, _sz, _p]
+    L.gmi_conv2d_wgrad_implicit.argtypes = [_i32] * 14 + [_p, _p, _p, _p, ctypes.c_int, _f32, _f32, _p, _sz, _p]
     L.gmi_w4a16_workspace_bytes.restype = _sz
     L.gmi_w4a16_workspace_bytes.argtypes = [_i32, _i32, _i32]
     L.gmi_conv2d_fprop_implicit.restype = ctypes.c_int
@@ -300,25 +300,26 @@ def conv2d_dgrad(dy: torch.Tensor, w: torch.Tensor, H: int, W: int, pad=(0, 0), 
     return dx
 
 
-def conv2d_wgrad_workspace_bytes(x_shape, dy_shape, R, S, pad=(0, 0), stride=(1, 1), dil=(1, 1)) -> int:
+def conv2d_wgrad_workspace_bytes(x_shape, dy_shape, R, S, pad=(0, 0), stride=(1, 1), dil=(1, 1), groups=1) -> int:
     N, H, W, C = x_shape
     K = dy_shape[3]
     return lib().gmi_conv2d_wgrad_workspace_bytes(N, H, W, C, K, R, S, pad[0], pad[1], stride[0], stride[1], dil[0],
-                                                  dil[1])
+                                                  dil[1], groups)
 
 
 def conv2d_wgrad(x: torch.Tensor, dy: torch.Tensor, R: int, S: int, pad=(0, 0), stride=(1, 1), dil=(1, 1),
                  c_in=None, alpha=1.0, beta=0.0, dw: torch.Tensor | None = None,
-                 workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Filter gradient of conv2d_fprop: x NHWC, dy NPQK, the filter size R, S -> dw KRSC."""
+                 workspace: torch.Tensor | None = None, groups: int = 1, stream=None) -> torch.Tensor:
+    """Filter gradient of conv2d_fprop: x NHWC, dy NPQK, the filter size R, S -> dw K x R x S x C/groups."""
     N, H, W, C = x.shape
     K = dy.shape[3]
     if dw is None:
-        dw = torch.empty((K, R, S, C), dtype=x.dtype, device=x.device)
+        dw = torch.empty((K, R, S, C // groups), dtype=x.dtype, device=x.device)
     if workspace is None:
-        workspace = torch.empty(conv2d_wgrad_workspace_bytes(x.shape, dy.shape, R, S, pad, stride, dil),
+        workspace = torch.empty(conv2d_wgrad_workspace_bytes(x.shape, dy.shape, R, S, pad, stride, dil, groups),
                                 dtype=torch.uint8, device=x.device)
     _check(lib().gmi_conv2d_wgrad_implicit(N, H, W, C, K, R, S, pad[0], pad[1], stride[0], stride[1], dil[0], dil[1],
-                                           x.data_ptr(), dy.data_ptr(), _ptr(c_in), dw.data_ptr(), _DT[x.dtype],
+                                           groups, x.data_ptr(), dy.data_ptr(), _ptr(c_in), dw.data_ptr(),
+                                           _DT[x.dtype],
                                            alpha, beta, workspace.data_ptr(), workspace.numel(), _stream(stream)))
     return dw

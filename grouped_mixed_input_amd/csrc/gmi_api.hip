@@ -458,7 +458,7 @@ gmi_status gmi_gemm_mixed(int32_t M, int32_t N, int32_t K, gmi_dtype x_dtype, co
 // Checks shared by the weight-gradient calls; fills the plan.
 static gmi_status wgrad_check(const char* who, int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int32_t R,
                               int32_t S, int32_t pad_h, int32_t pad_w, int32_t stride_h, int32_t stride_w,
-                              int32_t dil_h, int32_t dil_w, WgradPlan& plan) {
+                              int32_t dil_h, int32_t dil_w, int32_t groups, WgradPlan& plan) {
   if (N < 1 || H < 1 || W < 1 || C < 1 || K < 1 || R < 1 || S < 1)
     return fail(GMI_ERR_INVALID_ARG, "%s: sizes must be positive", who);
   if (pad_h < 0 || pad_w < 0 || stride_h < 1 || stride_w < 1 || dil_h < 1 || dil_w < 1)
@@ -466,7 +466,11 @@ static gmi_status wgrad_check(const char* who, int32_t N, int32_t H, int32_t W, 
   if (dil_h > 8 || dil_w > 8 || stride_h > 8 || stride_w > 8)
     return fail(GMI_ERR_UNSUPPORTED, "%s: stride and dilation must be in [1, 8]", who);
   if (C % 8 || K % 8) return fail(GMI_ERR_MISALIGNED, "%s: C and K must be multiples of 8", who);
-  if (!plan_wgrad(N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w, plan))
+  if (groups < 1 || C % groups || K % groups)
+    return fail(GMI_ERR_INVALID_ARG, "%s: groups %d must divide C %d and K %d", who, groups, C, K);
+  if ((K / groups) % 8)
+    return fail(GMI_ERR_UNSUPPORTED, "%s: output channels per group must be a multiple of 8", who);
+  if (!plan_wgrad(N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w, groups, plan))
     return fail(GMI_ERR_INVALID_ARG, "%s: the filter does not fit the padded image", who);
   const int64_t n8 = plan.N8;
   if ((int64_t)C * H * W * n8 * 2 > INT32_MAX || (int64_t)plan.P * plan.Q * n8 > kMaxLd ||
@@ -479,25 +483,27 @@ static gmi_status wgrad_check(const char* who, int32_t N, int32_t H, int32_t W, 
 
 size_t gmi_conv2d_wgrad_workspace_bytes(int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int32_t R, int32_t S,
                                         int32_t pad_h, int32_t pad_w, int32_t stride_h, int32_t stride_w,
-                                        int32_t dil_h, int32_t dil_w) {
+                                        int32_t dil_h, int32_t dil_w, int32_t groups) {
   WgradPlan plan;
   const std::string saved = g_last_error;
   const gmi_status st = wgrad_check("conv2d_wgrad_workspace_bytes", N, H, W, C, K, R, S, pad_h, pad_w, stride_h,
-                                    stride_w, dil_h, dil_w, plan);
+                                    stride_w, dil_h, dil_w, groups, plan);
   g_last_error = saved;
   return st == GMI_OK ? plan.bytes : 0;
 }
 
 gmi_status gmi_conv2d_wgrad_implicit(int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int32_t R, int32_t S,
                                      int32_t pad_h, int32_t pad_w, int32_t stride_h, int32_t stride_w, int32_t dil_h,
-                                     int32_t dil_w, const void* x, const void* dy, const void* c_in, void* dw,
+                                     int32_t dil_w, int32_t groups, const void* x, const void* dy, const void* c_in,
+                                     void* dw,
                                      gmi_dtype dtype, float alpha, float beta, void* workspace,
                                      size_t workspace_bytes, void* stream) {
   g_last_error.clear();
   const char* who = "conv2d_wgrad";
   if (!dtype_ok(dtype)) return fail(GMI_ERR_UNSUPPORTED, "%s: dtype %d not supported", who, (int)dtype);
   WgradPlan plan;
-  const gmi_status st = wgrad_check(who, N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w, plan);
+  const gmi_status st =
+      wgrad_check(who, N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w, groups, plan);
   if (st != GMI_OK) return st;
   const bool use_c = beta != 0.0f;
   if (!x || !dy || !dw || (use_c && !c_in)) return fail(GMI_ERR_INVALID_ARG, "%s: NULL pointer", who);

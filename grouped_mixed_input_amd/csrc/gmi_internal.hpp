@@ -68,6 +68,9 @@ struct ConvLaunch {
   // split over the taps into fp32 partials (see k_conv_fprop); 1 / NULL: none
   int split = 1, kt_split = 1 << 30;
   float* partial = nullptr;
+  // independent groups (see k_conv_fprop): offsets per group in elements
+  int groups = 1;
+  int64_t x_group = 0, w_group = 0, part_group = 0;
 };
 
 struct W4Launch {
@@ -130,12 +133,13 @@ hipError_t launch_conv_dgrad(const ConvLaunch& a, uint16_t* wt, int shape, int d
 // workspace layout; the workspace size and the launch both use it.
 struct WgradPlan {
   int N, H, W, C, K, R, S, P, Q, ph, pw, sh, sw, dh, dw;  // the forward problem
+  int groups, cg, kg;    // channel groups; input and output channels per group
   int N8, Rp, Sp;        // batch rounded up to 8; the view's output taps (>= R, S)
   int split, kt_split;   // the view's split over its P*Q*N8 taps (64 per k-tile)
   size_t x_off, dy_off, part_off, bytes;  // workspace layout
 };
 bool plan_wgrad(int N, int H, int W, int C, int K, int R, int S, int ph, int pw, int sh, int sw, int dh, int dw,
-                WgradPlan& p);
+                int groups, WgradPlan& p);
 hipError_t launch_conv_wgrad(const WgradPlan& p, const uint16_t* x, const uint16_t* dy, const uint16_t* c_in,
                              uint16_t* dwt, char* workspace, int dtype, float alpha, float beta, hipStream_t stream);
 hipError_t launch_prepack_w4(const uint8_t* w, int N, int K, uint8_t* out, hipStream_t stream);

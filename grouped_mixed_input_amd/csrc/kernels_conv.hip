@@ -26,6 +26,11 @@ struct ConvArgs {
   // instead of y
   int split, kt_split;
   float* partial;
+  // independent groups (the grouped weight gradient): group j gathers from
+  // g.x + j * x_group, reads filters w + j * w_group and writes partials
+  // partial + j * part_group; work items run group-major
+  int groups;
+  int64_t x_group, w_group, part_group;
 };
 
 // Tile ids run n-tile fastest: the few n-tiles of a pixel block are
@@ -34,12 +39,14 @@ template <class Cfg, int DT>
 __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_conv_fprop(ConvArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
   const int G = gridDim.x;
-  const int total = a.total_tiles * a.split;
+  const int per_group = a.total_tiles * a.split;
+  const int total = per_group * a.groups;
   const int nkt = (a.g.Kg + Cfg::BK - 1) / Cfg::BK;
   for (int base = 0; base < total; base += G) {
     const int work = base + remap_slot(blockIdx.x, G);
     if (work >= total) break;
-    const int sidx = work / a.total_tiles, tile = work - sidx * a.total_tiles;
+    const int grp = work / per_group, rest = work - grp * per_group;
+    const int sidx = rest / a.total_tiles, tile = rest - sidx * a.total_tiles;
     const int kt0 = sidx * a.kt_split;
     const int nk = min(a.kt_split, nkt - kt0);
     const int k0 = kt0 * Cfg::BK;
@@ -53,14 +60,16 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_conv_fprop(Co
     t.ldc = a.Nk;
     t.D = a.y;
     t.ldd = a.Nk;
+    ConvGeom gg = a.g;
+    gg.x += grp * a.x_group;
     ConvLoader<Cfg, Cfg::BM> al;
     DenseLoader<Cfg, Cfg::BN> bl;
-    al.init(a.g, t.m0, t.M, kt0);
-    bl.init(a.w + k0, a.g.Kg, t.n0, t.N, t.K);
+    al.init(gg, t.m0, t.M, kt0);
+    bl.init(a.w + grp * a.w_group + k0, a.g.Kg, t.n0, t.N, t.K);
     f32x16 acc[Cfg::TM][Cfg::TN];
     mainloop<Cfg, DT>(lds, al, bl, nk, acc);
     if (a.partial)
-      store_partial<Cfg>(t, acc, a.partial + (int64_t)sidx * a.M * a.Nk);
+      store_partial<Cfg>(t, acc, a.partial + grp * a.part_group + (int64_t)sidx * a.M * a.Nk);
     else
       store_tile<Cfg, DT>(t, acc, a.alpha, a.beta, lds);
   }
@@ -96,8 +105,12 @@ hipError_t launch_conv_fprop(const ConvLaunch& p, int shape, int dtype, float al
   a.split = p.split;
   a.kt_split = p.kt_split;
   a.partial = p.partial;
+  a.groups = p.groups;
+  a.x_group = p.x_group;
+  a.w_group = p.w_group;
+  a.part_group = p.part_group;
   const int resident = device_cu_count() * tile_wgs_per_cu(shape);
-  int grid = (a.total_tiles * a.split + XCDS - 1) / XCDS * XCDS;
+  int grid = (a.total_tiles * a.split * a.groups + XCDS - 1) / XCDS * XCDS;
   if (grid > resident) grid = resident / XCDS * XCDS;
   if (grid < XCDS) grid = XCDS;
   if (shape == TILE_256x256) {
@@ -223,7 +236,11 @@ hipError_t launch_conv_dgrad(const ConvLaunch& p, uint16_t* wt, int shape, int d
 using WgradCfg = ConvCfg256;
 
 bool plan_wgrad(int N, int H, int W, int C, int K, int R, int S, int ph, int pw, int sh, int sw, int dh, int dw,
-                WgradPlan& p) {
+                int groups, WgradPlan& p) {
+  if (groups < 1 || C % groups || K % groups) return false;
+  p.groups = groups;
+  p.cg = C / groups;
+  p.kg = K / groups;
   p.N = N;
   p.H = H;
   p.W = W;
@@ -246,8 +263,10 @@ bool plan_wgrad(int N, int H, int W, int C, int K, int R, int S, int ph, int pw,
   p.Rp = (int)(((int64_t)H + 2 * ph - (int64_t)sh * (p.P - 1) - 1) / dh + 1);
   p.Sp = (int)(((int64_t)W + 2 * pw - (int64_t)sw * (p.Q - 1) - 1) / dw + 1);
   if (p.Rp < R || p.Sp < S) return false;
-  const int64_t Mv = (int64_t)C * p.Rp * p.Sp, Kg = (int64_t)p.P * p.Q * p.N8;
-  const int64_t tiles = (Mv + WgradCfg::BM - 1) / WgradCfg::BM * ((K + WgradCfg::BN - 1) / WgradCfg::BN);
+  // per group: M = cg * Rp * Sp view pixels, N = kg filters
+  const int64_t Mv = (int64_t)p.cg * p.Rp * p.Sp, Kg = (int64_t)p.P * p.Q * p.N8;
+  const int64_t tiles =
+      groups * ((Mv + WgradCfg::BM - 1) / WgradCfg::BM * ((p.kg + WgradCfg::BN - 1) / WgradCfg::BN));
   const int64_t nkt = (Kg + WgradCfg::BK - 1) / WgradCfg::BK;
   int64_t split = (device_cu_count() + tiles - 1) / tiles;  // one work item per CU at least
   if (split > nkt / 8) split = nkt / 8;                     // at least 8 k-tiles per item
@@ -258,7 +277,7 @@ bool plan_wgrad(int N, int H, int W, int C, int K, int R, int S, int ph, int pw,
   p.x_off = 0;
   p.dy_off = up((size_t)C * H * W * p.N8 * 2);
   p.part_off = p.dy_off + up((size_t)K * p.P * p.Q * p.N8 * 2);
-  p.bytes = p.part_off + up((size_t)p.split * Mv * K * 4);
+  p.bytes = p.part_off + up((size_t)groups * p.split * Mv * p.kg * 4);
   return true;
 }
 
@@ -266,23 +285,26 @@ bool plan_wgrad(int N, int H, int W, int C, int K, int R, int S, int ph, int pw,
 // + beta * c_in[k][r][s][c]): one 32 x 64 (c, k) block of one tap per
 // workgroup, read along k (eight independent sums per thread, so the loads
 // of a split are in flight together), written along c.
+// With groups, C is the channels per group and output channel k belongs to
+// group k / kg, whose partials start at part + (k / kg) * split * plane.
 template <int DT>
-__global__ __launch_bounds__(256) void k_wgrad_finish(const float* __restrict__ part, int split, int C, int K, int R,
-                                                      int S, int Rp, int Sp, const uint16_t* __restrict__ cin,
+__global__ __launch_bounds__(256) void k_wgrad_finish(const float* __restrict__ part, int split, int C, int K, int kg,
+                                                      int R, int S, int Rp, int Sp, const uint16_t* __restrict__ cin,
                                                       float alpha, float beta, uint16_t* __restrict__ dw) {
   __shared__ float t[32][65];
   const int rs = blockIdx.z, r = rs / S, s = rs % S;
   const int c0 = blockIdx.x * 32, k0 = blockIdx.y * 64;
-  const int64_t plane = (int64_t)C * Rp * Sp * K;
+  const int64_t plane = (int64_t)C * Rp * Sp * kg;
   const int kk = threadIdx.x % 64, cb = threadIdx.x / 64;  // this thread: k0 + kk, rows c0 + cb + 4 j
-  const int k = k0 + kk;
+  const int k = k0 + kk, grp = k / kg, kl = k - grp * kg;
+  const float* gpart = part + grp * split * plane;
   float v[8];
   const float* src[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int c = c0 + cb + 4 * j;
     v[j] = 0.0f;
-    src[j] = (c < C && k < K) ? part + ((int64_t)(c * Rp + r) * Sp + s) * K + k : nullptr;
+    src[j] = (c < C && k < K) ? gpart + ((int64_t)(c * Rp + r) * Sp + s) * kg + kl : nullptr;
   }
   // four splits per round trip (32 loads in flight per thread), in order
   int sp = 0;
@@ -325,16 +347,16 @@ hipError_t launch_conv_wgrad(const WgradPlan& p, const uint16_t* x, const uint16
   if (e != hipSuccess) return e;
   e = transpose_outer(dy, gt, p.N, p.P * p.Q, p.K, p.N8, stream);
   if (e != hipSuccess) return e;
-  ConvLaunch f;  // the forward view
+  ConvLaunch f;  // the forward view, one problem per channel group
   f.x = xt;
   f.w = gt;
   f.c = nullptr;
   f.y = nullptr;
-  f.N = p.C;
+  f.N = p.cg;
   f.H = p.H;
   f.W = p.W;
   f.C = p.N8;
-  f.K = p.K;
+  f.K = p.kg;
   f.R = p.P;
   f.S = p.Q;
   f.P = p.Rp;
@@ -348,15 +370,19 @@ hipError_t launch_conv_wgrad(const WgradPlan& p, const uint16_t* x, const uint16
   f.split = p.split;
   f.kt_split = p.kt_split;
   f.partial = part;
+  f.groups = p.groups;
+  f.x_group = (int64_t)p.cg * p.H * p.W * p.N8;
+  f.w_group = (int64_t)p.kg * p.P * p.Q * p.N8;
+  f.part_group = (int64_t)p.split * p.cg * p.Rp * p.Sp * p.kg;
   e = launch_conv_fprop(f, TILE_256x256, dtype, 1.0f, 0.0f, stream);
   if (e != hipSuccess) return e;
-  const dim3 grid((p.C + 31) / 32, (p.K + 63) / 64, p.R * p.S);
+  const dim3 grid((p.cg + 31) / 32, (p.K + 63) / 64, p.R * p.S);
   if (dtype == DT_F16)
-    hipLaunchKernelGGL(k_wgrad_finish<DT_F16>, grid, dim3(256), 0, stream, part, p.split, p.C, p.K, p.R, p.S, p.Rp,
-                       p.Sp, c_in, alpha, beta, dwt);
+    hipLaunchKernelGGL(k_wgrad_finish<DT_F16>, grid, dim3(256), 0, stream, part, p.split, p.cg, p.K, p.kg, p.R, p.S,
+                       p.Rp, p.Sp, c_in, alpha, beta, dwt);
   else
-    hipLaunchKernelGGL(k_wgrad_finish<DT_BF16>, grid, dim3(256), 0, stream, part, p.split, p.C, p.K, p.R, p.S, p.Rp,
-                       p.Sp, c_in, alpha, beta, dwt);
+    hipLaunchKernelGGL(k_wgrad_finish<DT_BF16>, grid, dim3(256), 0, stream, part, p.split, p.cg, p.K, p.kg, p.R, p.S,
+                       p.Rp, p.Sp, c_in, alpha, beta, dwt);
   return hipGetLastError();
 }
 

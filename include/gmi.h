@@ -306,15 +306,18 @@ size_t gmi_conv2d_dgrad_workspace_bytes(int32_t C, int32_t K, int32_t R, int32_t
  * the split over taps); 0 if the problem is rejected. */
 size_t gmi_conv2d_wgrad_workspace_bytes(int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int32_t R, int32_t S,
                                         int32_t pad_h, int32_t pad_w, int32_t stride_h, int32_t stride_w,
-                                        int32_t dil_h, int32_t dil_w);
+                                        int32_t dil_h, int32_t dil_w, int32_t groups);
 
-/* Implicit-GEMM conv2d weight gradient (the page's wgrad operator), the
- * adjoint of gmi_conv2d_fprop_implicit in its filter:
+/* Implicit-GEMM conv2d weight gradient (the page's wgrad operator, and its
+ * grouped wgrad), the adjoint of the forward convolution in its filter:
  *   dw[k][r][s][c] = alpha * sum over (n, p, q) of dy[n][p][q][k] *
- *                    x[n][p*sh - ph + r*dh][q*sw - pw + s*dw][c]   (taps inside the image)
- *                    + beta * c_in[k][r][s][c]
+ *                    x[n][p*sh - ph + r*dh][q*sw - pw + s*dw][g(k) * C/groups + c]
+ *                    (taps inside the image) + beta * c_in[k][r][s][c],
+ *   c < C/groups, g(k) = k / (K/groups): output channel k of group g sees
+ *   only input channels g*C/groups .. (g+1)*C/groups - 1 (groups == 1 is the
+ *   plain weight gradient of gmi_conv2d_fprop_implicit).
  * Arguments describe the forward problem: x NHWC (N x H x W x C), dy NPQK
- * with P, Q as for the forward pass, dw and c_in KRSC.  The page gathers the
+ * with P, Q as for the forward pass, dw and c_in K x R x S x C/groups.  The page gathers the
  * activation as the im2col operand with dy tiled; here the sum is computed
  * as a forward convolution of the channel-major activation (each channel an
  * image whose channels are the batch) with dy as the filter, stride and
@@ -324,11 +327,12 @@ size_t gmi_conv2d_wgrad_workspace_bytes(int32_t N, int32_t H, int32_t W, int32_t
  *   workspace  at least gmi_conv2d_wgrad_workspace_bytes(...) bytes, 16-byte
  *              aligned, scratch for the call.
  * Requires N >= 1, C % 8 == 0 and K % 8 == 0 (else GMI_ERR_MISALIGNED),
- * stride and dilation in [1, 8], 16-byte aligned pointers, c_in NULL iff
- * beta == 0. */
+ * groups dividing C and K with K/groups % 8 == 0, stride and dilation in
+ * [1, 8], 16-byte aligned pointers, c_in NULL iff beta == 0. */
 gmi_status gmi_conv2d_wgrad_implicit(int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int32_t R, int32_t S,
                                      int32_t pad_h, int32_t pad_w, int32_t stride_h, int32_t stride_w,
-                                     int32_t dil_h, int32_t dil_w, const void* x, const void* dy, const void* c_in,
+                                     int32_t dil_h, int32_t dil_w, int32_t groups, const void* x, const void* dy,
+                                     const void* c_in,
                                      void* dw, gmi_dtype dtype, float alpha, float beta, void* workspace,
                                      size_t workspace_bytes, void* stream);
 

@@ -245,18 +245,20 @@ def test_conv_dgrad_validation(gmi):
     assert _dg(gmi, N=0, dy=None, w=None, dx=None, ws=None) == gmi.GMI_OK
 
 
-def _wg(gmi, N=2, H=8, W=8, C=16, K=8, R=3, S=3, ph=1, pw=1, sh=1, sw=1, dh=1, dw=1, x=A16, dy=A16 * 2, c=None,
-        out=A16 * 3, dt=1, beta=0.0, ws=A16 * 4, ws_bytes=1 << 26):
-    return gmi.lib().gmi_conv2d_wgrad_implicit(N, H, W, C, K, R, S, ph, pw, sh, sw, dh, dw, x, dy, c, out, dt, 1.0,
-                                               beta, ws, ws_bytes, None)
+def _wg(gmi, N=2, H=8, W=8, C=16, K=8, R=3, S=3, ph=1, pw=1, sh=1, sw=1, dh=1, dw=1, groups=1, x=A16, dy=A16 * 2,
+        c=None, out=A16 * 3, dt=1, beta=0.0, ws=A16 * 4, ws_bytes=1 << 26):
+    return gmi.lib().gmi_conv2d_wgrad_implicit(N, H, W, C, K, R, S, ph, pw, sh, sw, dh, dw, groups, x, dy, c, out, dt,
+                                               1.0, beta, ws, ws_bytes, None)
 
 
 def test_conv_wgrad_validation(gmi):
     L = gmi.lib()
-    need = L.gmi_conv2d_wgrad_workspace_bytes(2, 8, 8, 16, 8, 3, 3, 1, 1, 1, 1, 1, 1)
+    need = L.gmi_conv2d_wgrad_workspace_bytes(2, 8, 8, 16, 8, 3, 3, 1, 1, 1, 1, 1, 1, 1)
     # at least the two transposed operands (batch padded to 8) and one fp32 partial of the 16 x 3 x 3 x 8 output
     assert need >= 16 * 8 * 8 * 8 * 2 + 8 * 8 * 8 * 8 * 2 + 16 * 9 * 8 * 4
-    assert L.gmi_conv2d_wgrad_workspace_bytes(2, 8, 8, 12, 8, 3, 3, 1, 1, 1, 1, 1, 1) == 0  # rejected problem
+    assert L.gmi_conv2d_wgrad_workspace_bytes(2, 8, 8, 12, 8, 3, 3, 1, 1, 1, 1, 1, 1, 1) == 0  # rejected problem
+    assert _wg(gmi, groups=3) == gmi.GMI_ERR_INVALID_ARG  # does not divide C and K
+    assert _wg(gmi, C=32, K=32, groups=8) == gmi.GMI_ERR_UNSUPPORTED  # 4 output channels per group
     assert _wg(gmi, N=0) == gmi.GMI_ERR_INVALID_ARG
     assert _wg(gmi, ph=-1) == gmi.GMI_ERR_INVALID_ARG
     assert _wg(gmi, dh=9) == gmi.GMI_ERR_UNSUPPORTED

@@ -87,3 +87,20 @@ def test_wgrad_full_size_sampled(gmi):
     ks = [0, 37, 100, 128, 200, 201, 254, 255]
     ref = oracle.conv2d_wgrad(x, np.ascontiguousarray(dy[..., ks]), 3, 3, pad=(1, 1))
     check_close(host_bits(dw)[ks], ref, "bf16", f"wgrad full size filters {ks}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("N,H,W,C,K,R,pad,stride,groups", [
+    (4, 12, 10, 32, 32, 3, 1, 1, 4),     # 8 channels per group in and out (the page's depthwise-like case)
+    (2, 9, 9, 64, 64, 3, 1, 2, 2),
+    (3, 8, 12, 16, 48, 1, 0, 1, 2),      # 8 in, 24 out per group
+    (2, 14, 14, 128, 128, 3, 1, 1, 16),
+])
+def test_grouped_wgrad(gmi, dtype, N, H, W, C, K, R, pad, stride, groups):
+    x, dy = _case(N, H, W, C, K, R, R, pad, stride, 1, dtype, seed=C + groups)
+    dw = gmi.conv2d_wgrad(to_dev(x, dtype), to_dev(dy, dtype), R, R, pad=(pad, pad), stride=(stride, stride),
+                          groups=groups)
+    torch.cuda.synchronize()
+    assert dw.shape == (K, R, R, C // groups)
+    ref = oracle.conv2d_wgrad(x, dy, R, R, pad=(pad, pad), stride=(stride, stride), dtype=dtype, groups=groups)
+    check_close(host_bits(dw), ref, dtype, f"grouped wgrad {N},{H},{W},{C},{K},{R} g{groups}")
