@@ -87,3 +87,15 @@ def test_fp8_workloads():
     assert A[0].dtype == np.uint8 and A[0].shape == (8, 32) and B[1].shape == (16, 32)
     assert _h(*A) == _h(*gi.ptr_array_f8(L=2, M=8, N=16, K=32)[0])
     assert gi.moe_expert_weight_f8(3, N=16, K=32).shape == (16, 32)
+
+
+def test_moe_w4_decode_workload():
+    c = gi.moe_w4_counts()
+    assert c.sum() == 128 and len(c) == 128 and (c == 0).sum() >= 8
+    w, s, z = gi.moe_w4_expert(5, N=32, K=256)
+    assert w.shape == (32, 128) and w.dtype == np.uint8
+    assert s.shape == (2, 32) and s.dtype == np.uint16 and z.shape == (2, 16)
+    sv = (s.astype(np.uint32) << 16).view(np.float32)  # bf16 scales in [0.001, 0.01]
+    assert np.all((sv >= 0.000999) & (sv <= 0.0101))
+    assert _h(w) == _h(gi.moe_w4_expert(5, N=32, K=256)[0]) and _h(w) != _h(gi.moe_w4_expert(6, N=32, K=256)[0])
+    assert gi.moe_w4_activations(rows=7, K=64).shape == (7, 64)
