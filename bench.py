@@ -283,6 +283,31 @@ def bench_workloads(torch, gmi, gi, dev, args):
     return out
 
 
+def decode_only(torch, gmi, gi, dev, args):
+    """The W4A16 M = 16 line of the workloads alone: rotating copies, HIP events over the timed launches."""
+    M, N, K, g = 16, 8192, 8192, 128
+    w = gi.w4a16(M=M, N=N, K=K, group=g)
+    pp = gmi.prepack_w4(torch.from_numpy(w["W"]).to(dev), N, K)
+    S = t16(torch, w["scales"], torch.float16, dev)
+    Z = torch.from_numpy(w["zeros"]).to(dev)
+    X = t16(torch, w["X"], torch.float16, dev)
+    ws = N * K // 2 + S.numel() * 2 + Z.numel() + 2 * M * (N + K)
+    R = copies_for(ws)
+    sets = [(pp.clone(), S.clone(), Z.clone(), X.clone(), torch.empty((M, N), dtype=torch.float16, device=dev))
+            for _ in range(R)]
+    wsp = torch.empty(gmi.w4a16_workspace_bytes(M, N, K), dtype=torch.uint8, device=dev)
+    fn = lambda i: gmi.gemm_w4a16(sets[i][3], sets[i][0], sets[i][1], sets[i][2], g, N, Y=sets[i][4], workspace=wsp)
+    ms = time_launches(torch, fn, R, args.warmup, args.steps)
+    if args.copy_ref:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+    line = dict(workload=f"w4a16 decode M={M} N={N} K={K} g={g}", steps=args.steps, warmup=args.warmup,
+                us=round(ms * 1e3, 3), algorithmic_bytes=ws, gbps=round(ws / (ms * 1e-3) / 1e9, 1),
+                frac_hbm=round(ws / (ms * 1e-3) / (PEAK_HBM * 1e9), 4), copies=R)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -290,6 +315,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--headline-only", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only the W4A16 decode workload (M = 16, N = K = 8192, g = 128) and print one line "
+                         "for it (for the decode kernel's profiles)")
     ap.add_argument("--copy-ref", action="store_true",
                     help="after the timed region, run one plain 256 MiB device copy (a known-size kernel that "
                          "calibrates hardware byte counters)")
@@ -310,6 +338,9 @@ def main():
         build()
     gmi.lib()
     dev = torch.device("cuda:0")
+    if args.decode_only:
+        decode_only(torch, gmi, gi, dev, args)
+        return
     log("bench: building inputs")
     fn, R, flops, ws, keep = setup_ptr_array(torch, gmi, gi, dev)
     log(f"bench: headline rotates {R} copies of {ws / 2**20:.0f} MiB")
