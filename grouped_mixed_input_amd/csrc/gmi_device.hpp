@@ -369,7 +369,20 @@ struct ConvGeom {
   // 2^ush hold data, pixel (h, w) of x at (h << ush, w << ush).  ush = 0,
   // Hv = H, Wv = W for the forward pass.
   int Hv, Wv, ush;
+  // k-tile order.  prs = 0: the GEMM's own order, taps (r, s) outer and
+  // channels inner.  prs = R * S (only when C is a whole number pcb of
+  // k-tiles): loop step t takes channel block t / prs of tap t % prs, so the
+  // R * S taps of one channel block run back to back and re-read input rows
+  // that the previous taps just brought into L2.  The k-tiles partition the
+  // same sum either way; only the fp32 accumulation order differs.
+  int prs, pcb;
 };
+
+// GEMM k-tile of loop step lt under the order above (steps past the last
+// k-tile map to themselves)
+__device__ __forceinline__ int conv_ktile(int lt, int prs, int pcb) {
+  return (prs && lt < prs * pcb) ? (lt % prs) * pcb + lt / prs : lt;
+}
 
 template <class Cfg, int ROWS>
 struct ConvLoader {
@@ -379,7 +392,7 @@ struct ConvLoader {
   static constexpr int P = ROWS * Cfg::ROWB / (1024 * Cfg::NW);
   static_assert(P >= 1 && ROWS % (Cfg::NW * Cfg::RPI) == 0, "rows must fill whole copy passes");
   rsrc_t rs;
-  int H, W, C, S, dh, dw, Kg, Hv, Wv, ush, umask, kt0;
+  int H, W, C, S, dh, dw, Kg, Hv, Wv, ush, umask, kt0, prs, pcb;
   int pix[P];        // first pixel of the row's image: n * H * W
   int h0[P], w0[P];  // (virtual) input coordinates of tap (0, 0); far negative for rows past M
 
@@ -398,6 +411,8 @@ struct ConvLoader {
     dh = g.dh;
     dw = g.dw;
     Kg = g.Kg;
+    prs = g.prs;
+    pcb = g.pcb;
     const int PQ = g.P * g.Q;
     const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -424,7 +439,7 @@ struct ConvLoader {
     bool kin;
   };
   __device__ __forceinline__ Prep prep(int kt) const {
-    const int kc = (kt + kt0) * Cfg::BK + Cfg::dma_chunk(threadIdx.x & 63) * 8;
+    const int kc = conv_ktile(kt + kt0, prs, pcb) * Cfg::BK + Cfg::dma_chunk(threadIdx.x & 63) * 8;
     const int rsx = kc / C, c = kc - rsx * C;
     const int r = rsx / S, s = rsx - r * S;
     return Prep{r * dh, s * dw, c, kc < Kg};
@@ -441,6 +456,29 @@ struct ConvLoader {
     for (int i = 0; i < P; ++i) issue_one(i, p, tile);
   }
   __device__ __forceinline__ void fix_tail(int, char*) const {}  // C % 8 == 0: chunks never straddle K
+};
+
+// The KRSC filter as the column-major B operand (leading dimension R * S * C),
+// its k-tiles taken in the gather's order.
+template <class Cfg, int ROWS>
+struct FilterLoader : DenseLoader<Cfg, ROWS> {
+  using Base = DenseLoader<Cfg, ROWS>;
+  using typename Base::Prep;
+  int kt0, prs, pcb;
+  __device__ __forceinline__ void init(const uint16_t* w, const ConvGeom& g, int row0, int rows, int kt_first) {
+    Base::init(w, g.Kg, row0, rows, g.Kg);
+    kt0 = kt_first;
+    prs = g.prs;
+    pcb = g.pcb;
+  }
+  __device__ __forceinline__ Prep prep(int kt) const {
+    return Base::prep(conv_ktile(kt + kt0, prs, pcb));
+  }
+  __device__ __forceinline__ void issue(int kt, char* tile) const {
+    const Prep p = prep(kt);
+#pragma unroll
+    for (int i = 0; i < Base::P; ++i) Base::issue_one(i, p, tile);
+  }
 };
 
 // ---------------------------------------------------------------------------

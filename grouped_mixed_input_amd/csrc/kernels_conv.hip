@@ -63,9 +63,9 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_conv_fprop(Co
     ConvGeom gg = a.g;
     gg.x += grp * a.x_group;
     ConvLoader<Cfg, Cfg::BM> al;
-    DenseLoader<Cfg, Cfg::BN> bl;
+    FilterLoader<Cfg, Cfg::BN> bl;
     al.init(gg, t.m0, t.M, kt0);
-    bl.init(a.w + grp * a.w_group + k0, a.g.Kg, t.n0, t.N, t.K);
+    bl.init(a.w + grp * a.w_group, gg, t.n0, t.N, kt0);
     f32x16 acc[Cfg::TM][Cfg::TN];
     mainloop<Cfg, DT>(lds, al, bl, nk, acc);
     if (a.partial)
@@ -79,6 +79,10 @@ using ConvCfg256 = TileCfg<256, 256, 4, 2, 64, 2, 5>;
 using ConvCfg256x128 = TileCfg<256, 128, 2, 2, 32, 3>;
 using ConvCfg128 = TileCfg<128, 128, 2, 2, 32, 4>;
 
+static int conv_bk(int shape) {
+  return shape == TILE_256x256 ? ConvCfg256::BK : shape == TILE_256x128 ? ConvCfg256x128::BK : ConvCfg128::BK;
+}
+
 hipError_t launch_conv_fprop(const ConvLaunch& p, int shape, int dtype, float alpha, float beta,
                              hipStream_t stream) {
   ConvArgs a;
@@ -91,7 +95,15 @@ hipError_t launch_conv_fprop(const ConvLaunch& p, int shape, int dtype, float al
                  p.dh,  p.dw,
                  p.R * p.S * p.C,
                  ((p.H - 1) << p.ush) + 1, ((p.W - 1) << p.ush) + 1,
-                 p.ush};
+                 p.ush,
+                 0,     0};
+  // channel-block-major k order when the channels fill whole k-tiles and the
+  // launch is not split over k (a split keeps each range's taps together)
+  const int bk = conv_bk(shape);
+  if (p.R * p.S > 1 && p.C % bk == 0 && p.split == 1) {
+    a.g.prs = p.R * p.S;
+    a.g.pcb = p.C / bk;
+  }
   a.w = p.w;
   a.c = p.c;
   a.y = p.y;

@@ -35,6 +35,8 @@ def _run(gmi, x, w, pad, stride, dil, dtype="bf16", c=None, alpha=1.0, beta=0.0)
     (1, 30, 30, 8, 136, 5, 5, 2, 3, 1),
     (2, 11, 13, 24, 40, 2, 3, 0, 1, 1),
     (1, 6, 6, 8, 8, 3, 3, 0, 8, 1),
+    (2, 10, 9, 128, 24, 3, 3, 1, 1, 1),   # several whole channel blocks per tap: channel-block-major k order
+    (1, 12, 12, 96, 40, 3, 3, 1, 1, 2),
 ])
 def test_conv_shapes(gmi, dtype, N, H, W, C, K, R, S, pad, stride, dil):
     r = np.random.default_rng(N * H + C)

@@ -37,6 +37,7 @@ def _case(N, H, W, C, K, R, S, pad, dil, dtype, seed, stride=1):
     (1, 30, 30, 136, 8, 5, 5, 2, 1),
     (2, 11, 13, 40, 24, 2, 3, 0, 1),
     (1, 6, 6, 8, 8, 3, 3, 0, 1),
+    (2, 10, 9, 24, 128, 3, 3, 1, 1),     # the gather runs over dy's 128 channels: several channel blocks per tap
 ])
 def test_dgrad_shapes(gmi, dtype, N, H, W, C, K, R, S, pad, dil):
     dy, w = _case(N, H, W, C, K, R, S, pad, dil, dtype, seed=N * H + C)
