@@ -62,6 +62,17 @@ def time_launches(torch, fn, n_copies, warmup, iters):
     return s.elapsed_time(e) / iters
 
 
+def copy_ref(torch, dev, args):
+    """With --copy-ref, one plain 256 MiB device-to-device copy: a kernel of known traffic that calibrates
+    the hardware byte counters."""
+    if args.copy_ref:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+
 def roof(flops, bytes_, ms, peak=PEAK_MFMA_16):
     t = ms * 1e-3
     tf = flops / t / 1e12
@@ -113,22 +124,8 @@ def cpu_baseline(gi, A, B, budget_s=12.0):
                       f"{sec:.1f} s"}
 
 
-def bench_workloads(torch, gmi, gi, dev, args):
-    out = {}
-    # 1. grouped fp16, 4 groups, beta 0.5 (launch-latency bound)
-    probs = gi.grouped_f16()
-    As = [t16(torch, p["A"], torch.float16, dev) for p in probs]
-    Bs = [t16(torch, p["B"], torch.float16, dev) for p in probs]
-    Cs = [t16(torch, p["C"], torch.float16, dev) for p in probs]
-    Ds = [torch.empty((p["M"], p["N"]), dtype=torch.float16, device=dev) for p in probs]
-    table = gmi.make_problems(As, Bs, Cs, Ds)
-    wsb = torch.empty(gmi.workspace_bytes(4), dtype=torch.uint8, device=dev)
-    fl = sum(2.0 * p["M"] * p["N"] * p["K"] for p in probs)
-    by = sum(2 * (p["M"] * p["K"] + p["N"] * p["K"] + 2 * p["M"] * p["N"]) for p in probs)
-    ms = time_launches(torch, lambda i: gmi.gemm_grouped_raw(table, 4, gmi.GMI_F16, 1.0, 0.5, wsb), 1, 20, 500)
-    out["grouped_f16_4groups"] = dict(roof(fl, by, ms), bound="launch")
-    log("bench: grouped fp16 done")
-
+def bench_moe(torch, gmi, gi, dev, out):
+    """The MoE grouped bf16 layer, host table and device-held group sizes."""
     # 3. MoE grouped bf16, 16384 tokens over 128 experts, N 2048, K 4096
     counts = gi.moe_counts()
     N, K = 2048, 4096
@@ -153,6 +150,55 @@ def bench_workloads(torch, gmi, gi, dev, args):
     del B3, A, D
     torch.cuda.empty_cache()
     log("bench: MoE grouped done")
+    return counts, off
+
+
+def bench_conv(torch, gmi, gi, dev, out):
+    """Conv fprop, dgrad and wgrad of one 3x3 layer."""
+    # 5. conv fprop bf16 32x56x56x256, 3x3x256 -> 256, pad 1
+    x, wf = gi.conv_fprop_bf16()
+    xd, wd = t16(torch, x, torch.bfloat16, dev), t16(torch, wf, torch.bfloat16, dev)
+    ws = 2 * (x.size + wf.size + 32 * 56 * 56 * 256)
+    R = copies_for(ws)
+    sets = [(xd.clone(), wd.clone(), torch.empty((32, 56, 56, 256), dtype=torch.bfloat16, device=dev))
+            for _ in range(R)]
+    ms = time_launches(torch, lambda i: gmi.conv2d_fprop(sets[i][0], sets[i][1], pad=(1, 1), y=sets[i][2]), R, 5,
+                       max(20, 2 * R))
+    out["conv_fprop_bf16"] = dict(roof(2.0 * 100352 * 256 * 2304, ws, ms), bound="mfma")
+    # the data gradient of the same layer (dy of the forward output's shape; the filter rearranged each call)
+    wsd = torch.empty(gmi.lib().gmi_conv2d_dgrad_workspace_bytes(256, 256, 3, 3), dtype=torch.uint8, device=dev)
+    ms = time_launches(torch, lambda i: gmi.conv2d_dgrad(sets[i][2], sets[i][1], 56, 56, pad=(1, 1), dx=sets[i][0],
+                                                         workspace=wsd), R, 5, max(20, 2 * R))
+    out["conv_dgrad_bf16"] = dict(roof(2.0 * 100352 * 256 * 2304, ws, ms), bound="mfma")
+    # and its weight gradient (x and dy of the same shapes; transposes and the split sum included)
+    dws = torch.empty((256, 3, 3, 256), dtype=torch.bfloat16, device=dev)
+    wsw = torch.empty(gmi.conv2d_wgrad_workspace_bytes((32, 56, 56, 256), (32, 56, 56, 256), 3, 3, (1, 1)),
+                      dtype=torch.uint8, device=dev)
+    ms = time_launches(torch, lambda i: gmi.conv2d_wgrad(sets[i][0], sets[i][2], 3, 3, pad=(1, 1), dw=dws,
+                                                         workspace=wsw), R, 3, max(10, 2 * R))
+    out["conv_wgrad_bf16"] = dict(roof(2.0 * 100352 * 256 * 2304, ws, ms), bound="mfma")
+    log("bench: conv done")
+    del sets
+    torch.cuda.empty_cache()
+
+
+def bench_workloads(torch, gmi, gi, dev, args):
+    out = {}
+    # 1. grouped fp16, 4 groups, beta 0.5 (launch-latency bound)
+    probs = gi.grouped_f16()
+    As = [t16(torch, p["A"], torch.float16, dev) for p in probs]
+    Bs = [t16(torch, p["B"], torch.float16, dev) for p in probs]
+    Cs = [t16(torch, p["C"], torch.float16, dev) for p in probs]
+    Ds = [torch.empty((p["M"], p["N"]), dtype=torch.float16, device=dev) for p in probs]
+    table = gmi.make_problems(As, Bs, Cs, Ds)
+    wsb = torch.empty(gmi.workspace_bytes(4), dtype=torch.uint8, device=dev)
+    fl = sum(2.0 * p["M"] * p["N"] * p["K"] for p in probs)
+    by = sum(2 * (p["M"] * p["K"] + p["N"] * p["K"] + 2 * p["M"] * p["N"]) for p in probs)
+    ms = time_launches(torch, lambda i: gmi.gemm_grouped_raw(table, 4, gmi.GMI_F16, 1.0, 0.5, wsb), 1, 20, 500)
+    out["grouped_f16_4groups"] = dict(roof(fl, by, ms), bound="launch")
+    log("bench: grouped fp16 done")
+
+    counts, off = bench_moe(torch, gmi, gi, dev, out)
 
     # 4. W4A16, N = K = 8192, g = 128
     w = gi.w4a16(M=16)
@@ -224,31 +270,7 @@ def bench_workloads(torch, gmi, gi, dev, args):
     torch.cuda.empty_cache()
     log("bench: MoE W4 decode done")
 
-    # 5. conv fprop bf16 32x56x56x256, 3x3x256 -> 256, pad 1
-    x, wf = gi.conv_fprop_bf16()
-    xd, wd = t16(torch, x, torch.bfloat16, dev), t16(torch, wf, torch.bfloat16, dev)
-    ws = 2 * (x.size + wf.size + 32 * 56 * 56 * 256)
-    R = copies_for(ws)
-    sets = [(xd.clone(), wd.clone(), torch.empty((32, 56, 56, 256), dtype=torch.bfloat16, device=dev))
-            for _ in range(R)]
-    ms = time_launches(torch, lambda i: gmi.conv2d_fprop(sets[i][0], sets[i][1], pad=(1, 1), y=sets[i][2]), R, 5,
-                       max(20, 2 * R))
-    out["conv_fprop_bf16"] = dict(roof(2.0 * 100352 * 256 * 2304, ws, ms), bound="mfma")
-    # the data gradient of the same layer (dy of the forward output's shape; the filter rearranged each call)
-    wsd = torch.empty(gmi.lib().gmi_conv2d_dgrad_workspace_bytes(256, 256, 3, 3), dtype=torch.uint8, device=dev)
-    ms = time_launches(torch, lambda i: gmi.conv2d_dgrad(sets[i][2], sets[i][1], 56, 56, pad=(1, 1), dx=sets[i][0],
-                                                         workspace=wsd), R, 5, max(20, 2 * R))
-    out["conv_dgrad_bf16"] = dict(roof(2.0 * 100352 * 256 * 2304, ws, ms), bound="mfma")
-    # and its weight gradient (x and dy of the same shapes; transposes and the split sum included)
-    dws = torch.empty((256, 3, 3, 256), dtype=torch.bfloat16, device=dev)
-    wsw = torch.empty(gmi.conv2d_wgrad_workspace_bytes((32, 56, 56, 256), (32, 56, 56, 256), 3, 3, (1, 1)),
-                      dtype=torch.uint8, device=dev)
-    ms = time_launches(torch, lambda i: gmi.conv2d_wgrad(sets[i][0], sets[i][2], 3, 3, pad=(1, 1), dw=dws,
-                                                         workspace=wsw), R, 3, max(10, 2 * R))
-    out["conv_wgrad_bf16"] = dict(roof(2.0 * 100352 * 256 * 2304, ws, ms), bound="mfma")
-    log("bench: conv done")
-    del sets
-    torch.cuda.empty_cache()
+    bench_conv(torch, gmi, gi, dev, out)
 
     # 6. fp8 (E4M3) inputs, bf16 results: the pointer-array headline shape and the MoE layer
     A8, B8 = gi.ptr_array_f8(L=16)
@@ -298,10 +320,7 @@ def decode_only(torch, gmi, gi, dev, args):
     wsp = torch.empty(gmi.w4a16_workspace_bytes(M, N, K), dtype=torch.uint8, device=dev)
     fn = lambda i: gmi.gemm_w4a16(sets[i][3], sets[i][0], sets[i][1], sets[i][2], g, N, Y=sets[i][4], workspace=wsp)
     ms = time_launches(torch, fn, R, args.warmup, args.steps)
-    if args.copy_ref:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
-        torch.empty_like(src).copy_(src)
-        torch.cuda.synchronize()
+    copy_ref(torch, dev, args)
     line = dict(workload=f"w4a16 decode M={M} N={N} K={K} g={g}", steps=args.steps, warmup=args.warmup,
                 us=round(ms * 1e3, 3), algorithmic_bytes=ws, gbps=round(ws / (ms * 1e-3) / 1e9, 1),
                 frac_hbm=round(ws / (ms * 1e-3) / (PEAK_HBM * 1e9), 4), copies=R)
@@ -318,6 +337,9 @@ def main():
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the W4A16 decode workload (M = 16, N = K = 8192, g = 128) and print one line "
                          "for it (for the decode kernel's profiles)")
+    ap.add_argument("--only", choices=["moe", "conv"],
+                    help="time only the MoE layers or only the conv layers and print their lines (for those "
+                         "kernels' profiles)")
     ap.add_argument("--copy-ref", action="store_true",
                     help="after the timed region, run one plain 256 MiB device copy (a known-size kernel that "
                          "calibrates hardware byte counters)")
@@ -340,6 +362,12 @@ def main():
     dev = torch.device("cuda:0")
     if args.decode_only:
         decode_only(torch, gmi, gi, dev, args)
+        return
+    if args.only:
+        out = {}
+        (bench_moe if args.only == "moe" else bench_conv)(torch, gmi, gi, dev, out)
+        copy_ref(torch, dev, args)
+        print(json.dumps(out), flush=True)
         return
     log("bench: building inputs")
     fn, R, flops, ws, keep = setup_ptr_array(torch, gmi, gi, dev)
@@ -369,12 +397,7 @@ def main():
                      "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": 3 * 16 * 1024 * 1024 * 2,
                      "kernel": HEADLINE_KERNEL},
     }
-    if args.copy_ref:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    copy_ref(torch, dev, args)
     if not args.headline_only:
         result["workloads"] = bench_workloads(torch, gmi, gi, dev, args)
     if not args.no_cpu_baseline:
