@@ -322,8 +322,89 @@ __global__ __launch_bounds__(64 * KW) void k_w4a16_decode(W4Launch a) {
 }
 
 // ---------------------------------------------------------------------------
-// Large-M kernel: the dense mainloop, X as the A operand, the prepacked
-// weight (dequantised on its way into LDS) as the column-major B operand.
+// Large-M kernel: the dense tiles' fragments, multiply stage and epilogue,
+// X as the A operand, the prepacked weight (dequantised on its way into LDS)
+// as the column-major B operand.
+//
+// Mainloop of the tiled kernel: three X stages (direct-to-LDS copies) and two
+// weight stages (dequantised from registers into LDS), with the weight
+// registers double-buffered.  While k-tile kt is multiplied, the X copies and
+// weight loads of kt + 2 are issued and those of kt + 1 are still landing, so
+// every load has two stage times to arrive; the end of step kt waits for
+// k-tile kt + 1 only (the loads of kt + 2 are the younger ones), dequantises
+// its weights into the free weight stage and publishes both.  Every step
+// issues the same loads (past the last k-tile they re-read valid data or land
+// as zeros and are never multiplied), so the wait counts are fixed.
+// ---------------------------------------------------------------------------
+template <class Cfg>
+struct W4Ring {
+  static constexpr int A_STAGES = 3, B_STAGES = 2;
+  static constexpr int BYTES = A_STAGES * Cfg::A_BYTES + B_STAGES * Cfg::B_BYTES;
+  static_assert(BYTES <= 160 * 1024 && BYTES * Cfg::WGS_PER_CU <= 160 * 1024, "LDS budget");
+  __device__ static __forceinline__ char* a(char* lds, int s) { return lds + s * Cfg::A_BYTES; }
+  __device__ static __forceinline__ char* b(char* lds, int s) {
+    return lds + A_STAGES * Cfg::A_BYTES + s * Cfg::B_BYTES;
+  }
+};
+
+// one k-tile: weights of kt + 2 into `rl`, multiply kt, then publish kt + 1
+// (X already copied, weights from `rs`)
+template <class Cfg, int DT, class ALd, class BLd>
+__device__ __forceinline__ void w4_step(char* lds, const ALd& al, const BLd& bl, int kt, int nk,
+                                        typename BLd::Regs& rl, const typename BLd::Regs& rs, const FragAddr<Cfg>& ad,
+                                        f32x16 (&acc)[Cfg::TM][Cfg::TN], frag_t<Cfg> (&fa)[2][Cfg::TM],
+                                        frag_t<Cfg> (&fb)[2][Cfg::TN]) {
+  using Ring = W4Ring<Cfg>;
+  constexpr int YOUNG = ALd::P + 3 * BLd::P;  // one k-tile's copies and loads
+  bl.load(kt + 2, rl);
+  const char* ca = Ring::a(lds, kt % 3);
+  const char* cb = Ring::b(lds, kt & 1);
+  read_frags<Cfg>(ad, ca, cb, 0, fa[0], fb[0]);
+  multiply_stage<Cfg, DT, false, 2>(ad, ca, cb, ca, cb, acc, fa, fb, al, kt + 2, Ring::a(lds, (kt + 2) % 3), bl, 0,
+                                    nullptr);
+  wait_vm_le<YOUNG>();
+  if (kt + 1 < nk) bl.store(Ring::b(lds, (kt + 1) & 1), rs);
+  wait_lgkm();
+  __builtin_amdgcn_s_barrier();
+}
+
+template <class Cfg, int DT, class ALd, class BLd>
+__device__ __forceinline__ void mainloop_w4(char* lds, const ALd& al, const BLd& bl, int nk,
+                                            f32x16 (&acc)[Cfg::TM][Cfg::TN]) {
+  using Ring = W4Ring<Cfg>;
+  static_assert(ALd::kDMA && !BLd::kDMA, "X by direct copies, weights through registers");
+  constexpr int YOUNG = ALd::P + 3 * BLd::P;
+#pragma unroll
+  for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::TN; ++j) acc[i][j] = f32x16{};
+  // the previous tile's epilogue may still be reading the stages
+  __builtin_amdgcn_s_barrier();
+  if (nk <= 0) return;
+  frag_t<Cfg> fa[2][Cfg::TM], fb[2][Cfg::TN];
+  FragAddr<Cfg> ad;
+  ad.init();
+  typename BLd::Regs r0, r1;
+  // prologue: k-tiles 0 and 1 in flight; 0 landed and published
+  bl.load(0, r0);
+  al.issue(0, Ring::a(lds, 0));
+  bl.load(1, r1);
+  al.issue(1, Ring::a(lds, 1));
+  wait_vm_le<YOUNG>();
+  bl.store(Ring::b(lds, 0), r0);
+  wait_lgkm();
+  __builtin_amdgcn_s_barrier();
+  // two k-tiles per trip so each register set keeps a fixed name
+  for (int kt = 0; kt < nk; kt += 2) {
+    w4_step<Cfg, DT>(lds, al, bl, kt, nk, r0, r1, ad, acc, fa, fb);
+    if (kt + 1 < nk) w4_step<Cfg, DT>(lds, al, bl, kt + 1, nk, r1, r0, ad, acc, fa, fb);
+  }
+  // copies and loads past the last k-tile are still landing: drain them
+  // before anyone reuses the stages
+  wait_vm_le<0>();
+  __builtin_amdgcn_s_barrier();
+}
+
 // ---------------------------------------------------------------------------
 // Work item w = tile * split + s: output tile `tile`, k-range s of `split`
 // equal ranges (whole 128-k blocks).  Unsplit, the epilogue rounds to fp16
@@ -332,7 +413,7 @@ __global__ __launch_bounds__(64 * KW) void k_w4a16_decode(W4Launch a) {
 // so they run in one XCD round and share the tile's X panel in its L2.
 template <class Cfg, int DT>
 __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_w4a16_tiled(W4Launch a, int tiles_m, int total_work) {
-  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char lds[W4Ring<Cfg>::BYTES];
   const int G = gridDim.x;
   const W4Geom g{a.w, a.scales, a.zeros, a.N, a.K, a.group, a.s_bytes, a.z_bytes, a.sor, a.wxor, a.zxor};
   const int Ks = a.K / a.split;
@@ -356,7 +437,7 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_w4a16_tiled(W
     al.init(a.X + k0, a.ldx, t.m0, t.M, Ks);
     bl.init(g, t.n0, k0 / Cfg::BK);
     f32x16 acc[Cfg::TM][Cfg::TN];
-    mainloop<Cfg, DT>(lds, al, bl, Ks / Cfg::BK, acc);
+    mainloop_w4<Cfg, DT>(lds, al, bl, Ks / Cfg::BK, acc);
     if (a.split == 1)
       store_tile<Cfg, DT>(t, acc, 1.0f, 0.0f, lds);
     else
@@ -384,7 +465,7 @@ __global__ __launch_bounds__(256) void k_w4a16_sum(const float* __restrict__ P, 
   }
 }
 
-using W4Cfg256 = TileCfg<256, 256, 2, 2, 64, 2>;
+using W4Cfg256 = TileCfg<256, 256, 4, 2, 64, 2>;
 using W4Cfg128 = TileCfg<128, 128, 2, 2, 64, 2>;
 
 // Tile shape of the tiled path: 256 x 256 when those tiles alone fill the
