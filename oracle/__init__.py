@@ -191,10 +191,15 @@ def conv_out_size(H, R, pad, stride, dil):
 
 
 def conv2d_fprop(x, w, *, pad=(0, 0), stride=(1, 1), dil=(1, 1), C_in=None, alpha=1.0, beta=0.0,
-                 dtype="bf16") -> np.ndarray:
+                 dtype="bf16", bias=None, act=None) -> np.ndarray:
     """Direct cross-correlation.  x uint16 [N][H][W][C] (NHWC), w uint16
     [K][R][S][C] (KRSC), C_in uint16 [N][P][Q][K] or None.  Returns float64
-    [N][P][Q][K]."""
+    [N][P][Q][K].
+
+    Fused epilogue (the conv page's collective epilogue is only a template
+    parameter; the reading here): bias uint16 [K] in the output type is added
+    per output channel after alpha * acc + beta * C, then act = "relu" takes
+    max(v, 0).  Both are applied to the unrounded fp64 value."""
     x = _c(x, np.uint16)
     w = _c(w, np.uint16)
     N, H, Wd, C = x.shape
@@ -209,6 +214,14 @@ def conv2d_fprop(x, w, *, pad=(0, 0), stride=(1, 1), dil=(1, 1), C_in=None, alph
                                   _ptr(out))
     if rc:
         raise ValueError("ora_conv2d_fprop rejected its arguments")
+    if bias is not None:
+        b = decode(_c(bias, np.uint16), dtype)
+        assert b.shape == (K,)
+        out += b[None, None, None, :]
+    if act == "relu":
+        np.maximum(out, 0.0, out=out)
+    elif act is not None:
+        raise ValueError(f"unknown activation {act!r}")
     return out
 
 

@@ -447,6 +447,53 @@ def test_conv_beta_term():
     np.testing.assert_allclose(got, 2.0 * base - 0.5 * lib_decode(c, "bf16"), rtol=1e-14, atol=1e-14)
 
 
+# ---------------------------------------------------------------- conv fused bias / ReLU epilogue
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_conv_bias_relu_zero_input_is_the_bias(dtype):
+    # x = 0: every output pixel of channel k is bias[k], then max(bias[k], 0) with ReLU (W != K and C != K, so
+    # a bias indexed by column q or by input channel would fail)
+    N, H, W, C, K = 2, 4, 5, 8, 6
+    enc = bf16_bits if dtype == "bf16" else f16_bits
+    x = enc(np.zeros(N * H * W * C)).reshape(N, H, W, C)
+    w = enc(RNG.standard_normal(K * 3 * 3 * C)).reshape(K, 3, 3, C)
+    b = enc([-2.5, 0.75, 0.0, 3.0, -0.125, 1.5])
+    bd = lib_decode(b, dtype)
+    got = oracle.conv2d_fprop(x, w, pad=(1, 1), bias=b, dtype=dtype)
+    assert np.array_equal(got, np.broadcast_to(bd, (N, H, W, K)))
+    got = oracle.conv2d_fprop(x, w, pad=(1, 1), bias=b, act="relu", dtype=dtype)
+    assert np.array_equal(got, np.broadcast_to(np.maximum(bd, 0.0), (N, H, W, K)))
+
+
+def test_conv_bias_relu_delta_filter():
+    # identity filter on the first K input channels: y = max(x[..., k] + bias[k], 0), exactly (integer values)
+    N, H, W, C, K = 2, 5, 4, 8, 4
+    x = _int_bits((N, H, W, C), -6, 7)
+    w = np.zeros((K, 3, 3, C))
+    for k in range(K):
+        w[k, 1, 1, k] = 1.0
+    b = bf16_bits([-2.0, 3.0, 0.0, -5.0])
+    want = np.maximum(lib_decode(x, "bf16")[..., :K] + lib_decode(b, "bf16"), 0.0)
+    got = oracle.conv2d_fprop(x, bf16_bits(w.ravel()).reshape(K, 3, 3, C), pad=(1, 1), bias=b, act="relu")
+    assert np.array_equal(got, want)
+    assert (got == 0).any() and (got > 0).any()
+
+
+def test_conv_bias_after_alpha_beta():
+    # bias is added after alpha * acc + beta * C (not scaled by alpha), ReLU after the bias
+    x = bf16_bits(RNG.standard_normal(1 * 4 * 4 * 8)).reshape(1, 4, 4, 8)
+    w = bf16_bits(RNG.standard_normal(3 * 3 * 3 * 8)).reshape(3, 3, 3, 8)
+    c = bf16_bits(RNG.standard_normal(1 * 4 * 4 * 3)).reshape(1, 4, 4, 3)
+    b = bf16_bits([0.5, -1.0, 2.0])
+    base = oracle.conv2d_fprop(x, w, pad=(1, 1))
+    want = 2.0 * base - 0.5 * lib_decode(c, "bf16") + lib_decode(b, "bf16")
+    got = oracle.conv2d_fprop(x, w, pad=(1, 1), C_in=c, alpha=2.0, beta=-0.5, bias=b)
+    np.testing.assert_allclose(got, want, rtol=1e-14, atol=1e-14)
+    got = oracle.conv2d_fprop(x, w, pad=(1, 1), C_in=c, alpha=2.0, beta=-0.5, bias=b, act="relu")
+    np.testing.assert_allclose(got, np.where(want > 0, want, 0.0), rtol=1e-14, atol=1e-14)
+    with pytest.raises(ValueError):
+        oracle.conv2d_fprop(x, w, pad=(1, 1), act="gelu")
+
+
 # ---------------------------------------------------------------- conv dgrad
 def _int_bits(shape, lo=-3, hi=4):
     return bf16_bits(RNG.integers(lo, hi, shape).astype(np.float64))
