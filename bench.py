@@ -165,6 +165,11 @@ def bench_conv(torch, gmi, gi, dev, out):
     ms = time_launches(torch, lambda i: gmi.conv2d_fprop(sets[i][0], sets[i][1], pad=(1, 1), y=sets[i][2]), R, 5,
                        max(20, 2 * R))
     out["conv_fprop_bf16"] = dict(roof(2.0 * 100352 * 256 * 2304, ws, ms), bound="mfma")
+    # the same layer with its bias and ReLU fused into the epilogue
+    bd = t16(torch, gi.conv_bias(), torch.bfloat16, dev)
+    ms = time_launches(torch, lambda i: gmi.conv2d_fprop(sets[i][0], sets[i][1], pad=(1, 1), y=sets[i][2], bias=bd,
+                                                         act="relu"), R, 5, max(20, 2 * R))
+    out["conv_fprop_bias_relu_bf16"] = dict(roof(2.0 * 100352 * 256 * 2304, ws + 512, ms), bound="mfma")
     # the data gradient of the same layer (dy of the forward output's shape; the filter rearranged each call)
     wsd = torch.empty(gmi.lib().gmi_conv2d_dgrad_workspace_bytes(256, 256, 3, 3), dtype=torch.uint8, device=dev)
     ms = time_launches(torch, lambda i: gmi.conv2d_dgrad(sets[i][2], sets[i][1], 56, 56, pad=(1, 1), dx=sets[i][0],

@@ -194,6 +194,12 @@ def conv_fprop_bf16(seed: int = DEFAULT_SEED, N: int = 32, H: int = 56, W: int =
     return x, w
 
 
+def conv_bias(seed: int = DEFAULT_SEED, K: int = 256, dtype: str = "bf16"):
+    """Per-output-channel bias of the fused conv epilogue: N(0, 1), the spread of the conv outputs above, so a
+    ReLU after it zeroes about half of them."""
+    return to_bits(normal(rng(seed, 5, 2), (K,), 1.0), dtype)
+
+
 # ----------------------------------------------------------------------------
 # workload 6: fp8 E4M3 GEMMs (bf16 results) -- the headline pointer-array shape
 # and the MoE layer with fp8 operands.  Values are drawn N(0, 1), the range an

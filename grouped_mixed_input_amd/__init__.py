@@ -75,6 +75,9 @@ def lib() -> ctypes.CDLL:
     L.gmi_gemm_mixed_grouped.restype = ctypes.c_int
     L.gmi_gemm_mixed_grouped.argtypes = [_i32, _p, _i32, _i32, _i32, ctypes.c_int, _p, _i64, _p, _i64, ctypes.c_int,
                                          _p, _i64, _p, _i64, _i32, _p, _i64, _p]
+    L.gmi_conv2d_fprop_implicit_fused.restype = ctypes.c_int
+    L.gmi_conv2d_fprop_implicit_fused.argtypes = [_i32] * 13 + [_p, _p, _p, _p, _p, ctypes.c_int, _f32, _f32,
+                                                               ctypes.c_int, _p]
     L.gmi_conv2d_dgrad_workspace_bytes.restype = _sz
     L.gmi_conv2d_dgrad_workspace_bytes.argtypes = [_i32] * 4
     L.gmi_conv2d_dgrad_implicit.restype = ctypes.c_int
@@ -265,18 +268,32 @@ def conv_out_size(H, R, pad, stride, dil):
     return (H + 2 * pad - dil * (R - 1) - 1) // stride + 1
 
 
+ACTIVATIONS = {None: 0, "none": 0, "relu": 1}
+
+
 def conv2d_fprop(x: torch.Tensor, w: torch.Tensor, pad=(0, 0), stride=(1, 1), dil=(1, 1), c_in=None, alpha=1.0,
-                 beta=0.0, y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Implicit-GEMM cross-correlation: x NHWC, w KRSC -> y NPQK."""
+                 beta=0.0, y: torch.Tensor | None = None, stream=None, bias: torch.Tensor | None = None,
+                 act: str | None = None) -> torch.Tensor:
+    """Implicit-GEMM cross-correlation: x NHWC, w KRSC -> y NPQK.  With `bias` (K elements of x's type) or
+    `act` ("relu"), the fused entry point adds the bias per output channel and applies the activation before
+    the output is rounded."""
     N, H, W, C = x.shape
     K, R, S, _ = w.shape
     if y is None:
         P = conv_out_size(H, R, pad[0], stride[0], dil[0])
         Q = conv_out_size(W, S, pad[1], stride[1], dil[1])
         y = torch.empty((N, max(P, 0), max(Q, 0), K), dtype=x.dtype, device=x.device)
-    _check(lib().gmi_conv2d_fprop_implicit(N, H, W, C, K, R, S, pad[0], pad[1], stride[0], stride[1], dil[0], dil[1],
-                                           x.data_ptr(), w.data_ptr(), _ptr(c_in), y.data_ptr(), _DT[x.dtype], alpha,
-                                           beta, _stream(stream)))
+    if bias is None and act in (None, "none"):
+        _check(lib().gmi_conv2d_fprop_implicit(N, H, W, C, K, R, S, pad[0], pad[1], stride[0], stride[1], dil[0],
+                                               dil[1], x.data_ptr(), w.data_ptr(), _ptr(c_in), y.data_ptr(),
+                                               _DT[x.dtype], alpha, beta, _stream(stream)))
+    else:
+        if bias is not None and (bias.numel() != K or bias.dtype != x.dtype):
+            raise ValueError("bias must hold K elements of the activation's type")
+        _check(lib().gmi_conv2d_fprop_implicit_fused(N, H, W, C, K, R, S, pad[0], pad[1], stride[0], stride[1],
+                                                     dil[0], dil[1], x.data_ptr(), w.data_ptr(), _ptr(c_in),
+                                                     _ptr(bias), y.data_ptr(), _DT[x.dtype], alpha, beta,
+                                                     ACTIVATIONS[act], _stream(stream)))
     return y
 
 

@@ -580,11 +580,14 @@ gmi_status gmi_conv2d_dgrad_implicit(int32_t N, int32_t H, int32_t W, int32_t C,
                     who);
 }
 
-gmi_status gmi_conv2d_fprop_implicit(int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int32_t R, int32_t S,
-                                     int32_t pad_h, int32_t pad_w, int32_t stride_h, int32_t stride_w, int32_t dil_h,
-                                     int32_t dil_w, const void* x, const void* w, const void* c_in, void* y,
-                                     gmi_dtype dtype, float alpha, float beta, void* stream) {
-  g_last_error.clear();
+// the forward pass, with or without the fused epilogue (bias NULL and act 0)
+static gmi_status conv_fprop(int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int32_t R, int32_t S,
+                             int32_t pad_h, int32_t pad_w, int32_t stride_h, int32_t stride_w, int32_t dil_h,
+                             int32_t dil_w, const void* x, const void* w, const void* c_in, const void* bias, void* y,
+                             gmi_dtype dtype, float alpha, float beta, int act, void* stream) {
+  if (act != GMI_ACT_NONE && act != GMI_ACT_RELU)
+    return fail(GMI_ERR_INVALID_ARG, "conv2d_fprop: activation %d is not one of GMI_ACT_NONE, GMI_ACT_RELU", act);
+  if (bias && !aligned16(bias)) return fail(GMI_ERR_MISALIGNED, "conv2d_fprop: bias must be 16-byte aligned");
   if (N < 0 || H < 1 || W < 1 || C < 1 || K < 1 || R < 1 || S < 1)
     return fail(GMI_ERR_INVALID_ARG, "conv2d_fprop: sizes must be positive (N >= 0)");
   if (pad_h < 0 || pad_w < 0 || stride_h < 1 || stride_w < 1 || dil_h < 1 || dil_w < 1)
@@ -628,10 +631,32 @@ gmi_status gmi_conv2d_fprop_implicit(int32_t N, int32_t H, int32_t W, int32_t C,
   a.sw = stride_w;
   a.dh = dil_h;
   a.dw = dil_w;
+  a.bias = (const uint16_t*)bias;
+  a.act = act;
   const int64_t Mg = (int64_t)N * P * Q;
   const int shape = choose_shape([&](int bm, int bn) { return cdiv(Mg, bm) * cdiv(K, bn); });
   return hip_status(launch_conv_fprop(a, shape, (int)dtype, alpha, beta, (hipStream_t)stream),
                     "conv2d_fprop: launch");
+}
+
+gmi_status gmi_conv2d_fprop_implicit(int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int32_t R, int32_t S,
+                                     int32_t pad_h, int32_t pad_w, int32_t stride_h, int32_t stride_w, int32_t dil_h,
+                                     int32_t dil_w, const void* x, const void* w, const void* c_in, void* y,
+                                     gmi_dtype dtype, float alpha, float beta, void* stream) {
+  g_last_error.clear();
+  return conv_fprop(N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w, x, w, c_in, nullptr, y,
+                    dtype, alpha, beta, GMI_ACT_NONE, stream);
+}
+
+gmi_status gmi_conv2d_fprop_implicit_fused(int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int32_t R,
+                                           int32_t S, int32_t pad_h, int32_t pad_w, int32_t stride_h,
+                                           int32_t stride_w, int32_t dil_h, int32_t dil_w, const void* x,
+                                           const void* w, const void* c_in, const void* bias, void* y,
+                                           gmi_dtype dtype, float alpha, float beta, gmi_activation act,
+                                           void* stream) {
+  g_last_error.clear();
+  return conv_fprop(N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w, x, w, c_in, bias, y, dtype,
+                    alpha, beta, (int)act, stream);
 }
 
 }  // extern "C"

@@ -268,7 +268,12 @@ struct Tile {
   int64_t ldc;
   uint16_t* D;
   int64_t ldd;
+  // fused epilogue: per-column bias (output type, NULL: none) added after
+  // alpha * acc + beta * C, then the activation (ACT_NONE / ACT_RELU)
+  const uint16_t* bias = nullptr;
+  int act = 0;
 };
+constexpr int ACT_NONE = 0, ACT_RELU = 1;
 
 // ---------------------------------------------------------------------------
 // Dense K-contiguous operand (direct to LDS): ROWS rows x BK k per k-tile
@@ -1027,6 +1032,8 @@ __device__ __forceinline__ void store_tile(const Tile& t, const f32x16 (&acc)[Cf
   const rsrc_t rd = make_rsrc(t.D + (int64_t)t.m0 * t.ldd, (uint32_t)rows * (uint32_t)t.ldd * 2u);
   const rsrc_t rc = use_c ? make_rsrc(t.C + (int64_t)t.m0 * t.ldc, (uint32_t)rows * (uint32_t)t.ldc * 2u) : rd;
   const uint32_t ldd2 = (uint32_t)t.ldd * 2u, ldc2 = (uint32_t)t.ldc * 2u;
+  const bool use_bias = t.bias != nullptr, relu = t.act == ACT_RELU;
+  const rsrc_t rbias = use_bias ? make_rsrc(t.bias, (uint32_t)t.N * 2u) : rd;
 
 #pragma unroll
   for (int p0 = 0; p0 < Cfg::TM; p0 += PASS) {
@@ -1061,6 +1068,18 @@ __device__ __forceinline__ void store_tile(const Tile& t, const f32x16 (&acc)[Cf
             v[2 * e + 1] += beta * from_bits<DT>(c4[e] >> 16);
           }
         }
+        if (use_bias) {
+          const u32x4 b4 = buf_load16(rbias, (uint32_t)col * 2u);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[2 * e] += from_bits<DT>(b4[e] & 0xffffu);
+            v[2 * e + 1] += from_bits<DT>(b4[e] >> 16);
+          }
+        }
+        if (relu) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = v[e] > 0.0f ? v[e] : 0.0f;
+        }
         buf_store16(rd, row * ldd2 + (uint32_t)col * 2u,
                     u32x4{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3]), pack2<DT>(v[4], v[5]), pack2<DT>(v[6], v[7])});
       } else {
@@ -1069,6 +1088,8 @@ __device__ __forceinline__ void store_tile(const Tile& t, const f32x16 (&acc)[Cf
           if (col + e < t.N) {
             float x = v[e];
             if (use_c) x += beta * from_bits<DT>(buf_load2(rc, row * ldc2 + (uint32_t)(col + e) * 2u));
+            if (use_bias) x += from_bits<DT>(buf_load2(rbias, (uint32_t)(col + e) * 2u));
+            if (relu) x = x > 0.0f ? x : 0.0f;
             buf_store2(rd, row * ldd2 + (uint32_t)(col + e) * 2u, to_bits<DT>(x));
           }
         }

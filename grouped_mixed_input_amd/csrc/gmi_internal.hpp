@@ -71,6 +71,10 @@ struct ConvLaunch {
   // independent groups (see k_conv_fprop): offsets per group in elements
   int groups = 1;
   int64_t x_group = 0, w_group = 0, part_group = 0;
+  // fused epilogue of the forward pass: per-output-channel bias (NULL: none)
+  // and activation (0: none, 1: ReLU); unsplit launches only
+  const uint16_t* bias = nullptr;
+  int act = 0;
 };
 
 struct W4Launch {

@@ -31,6 +31,9 @@ struct ConvArgs {
   // partial + j * part_group; work items run group-major
   int groups;
   int64_t x_group, w_group, part_group;
+  // fused epilogue (see Tile): per-output-channel bias, activation
+  const uint16_t* bias;
+  int act;
 };
 
 // Tile ids run n-tile fastest: the few n-tiles of a pixel block are
@@ -60,6 +63,8 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_conv_fprop(Co
     t.ldc = a.Nk;
     t.D = a.y;
     t.ldd = a.Nk;
+    t.bias = a.bias;
+    t.act = a.act;
     ConvGeom gg = a.g;
     gg.x += grp * a.x_group;
     ConvLoader<Cfg, Cfg::BM> al;
@@ -121,6 +126,8 @@ hipError_t launch_conv_fprop(const ConvLaunch& p, int shape, int dtype, float al
   a.x_group = p.x_group;
   a.w_group = p.w_group;
   a.part_group = p.part_group;
+  a.bias = p.bias;
+  a.act = p.act;
   const int resident = device_cu_count() * tile_wgs_per_cu(shape);
   int grid = (a.total_tiles * a.split * a.groups + XCDS - 1) / XCDS * XCDS;
   if (grid > resident) grid = resident / XCDS * XCDS;

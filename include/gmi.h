@@ -277,6 +277,28 @@ gmi_status gmi_conv2d_fprop_implicit(int32_t N, int32_t H, int32_t W, int32_t C,
                                      int32_t dil_h, int32_t dil_w, const void* x, const void* w, const void* c_in,
                                      void* y, gmi_dtype dtype, float alpha, float beta, void* stream);
 
+/* Activation of the fused conv epilogue. */
+typedef enum { GMI_ACT_NONE = 0, GMI_ACT_RELU = 1 } gmi_activation;
+
+/* gmi_conv2d_fprop_implicit with a fused epilogue:
+ *   v = alpha * sum(...) + beta * c_in[n][p][q][k] + bias[k]
+ *   y[n][p][q][k] = RN(act(v)),   act: identity (GMI_ACT_NONE) or max(v, 0) (GMI_ACT_RELU)
+ * The conv page leaves its collective epilogue a template parameter (the
+ * kernel only hands it the accumulator tile); this is the common bias +
+ * activation instance of it, evaluated in fp32 on the accumulator before the
+ * single rounding to the output type.
+ *   bias   K elements of `dtype` (one per output channel), 16-byte aligned, or
+ *          NULL for none.
+ *   act    GMI_ACT_NONE or GMI_ACT_RELU; any other value gives
+ *          GMI_ERR_INVALID_ARG.
+ * All other arguments, layouts and errors as for gmi_conv2d_fprop_implicit. */
+gmi_status gmi_conv2d_fprop_implicit_fused(int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int32_t R,
+                                           int32_t S, int32_t pad_h, int32_t pad_w, int32_t stride_h,
+                                           int32_t stride_w, int32_t dil_h, int32_t dil_w, const void* x,
+                                           const void* w, const void* c_in, const void* bias, void* y,
+                                           gmi_dtype dtype, float alpha, float beta, gmi_activation act,
+                                           void* stream);
+
 /* Bytes of the workspace gmi_conv2d_dgrad_implicit needs: the filter
  * rearranged to [C][R][S][K] (C*K*R*S*2, rounded up to 256); 0 for a
  * non-positive size. */

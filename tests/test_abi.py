@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
                  "gmi_conv2d_fprop_implicit", "gmi_workspace_bytes", "gmi_prepack_w4_bytes", "gmi_last_error",
                  "gmi_gemm_grouped_offsets", "gmi_w4a16_workspace_bytes", "gmi_gemm_mixed",
                  "gmi_gemm_mixed_grouped", "gmi_conv2d_dgrad_implicit", "gmi_conv2d_dgrad_workspace_bytes",
-                 "gmi_conv2d_wgrad_implicit", "gmi_conv2d_wgrad_workspace_bytes"]:
+                 "gmi_conv2d_wgrad_implicit", "gmi_conv2d_wgrad_workspace_bytes", "gmi_conv2d_fprop_implicit_fused"]:
         assert want in names
 
 
@@ -313,3 +313,19 @@ def test_errors_raise_through_the_binding(gmi):
         gmi.gemm_w4a16(torch.empty((16, 256), dtype=torch.float16), torch.empty(16384, dtype=torch.uint8),
                        torch.empty((2, 64), dtype=torch.float16), torch.empty((2, 32), dtype=torch.uint8), 128, 64,
                        Y=torch.empty((16, 68), dtype=torch.float16)[:, 2:66], stream=0)
+
+
+def _conv_fused(gmi, bias=A16 * 5, act=1, N=2, C=16, K=16, dt=1, x=A16, y=A16 * 3):
+    return gmi.lib().gmi_conv2d_fprop_implicit_fused(N, 8, 8, C, K, 3, 3, 1, 1, 1, 1, 1, 1, x, A16 * 2, None, bias,
+                                                     y, dt, 1.0, 0.0, act, None)
+
+
+def test_conv_fused_validation(gmi):
+    # rejected before any launch: an unknown activation, a misaligned bias, and every rule of the plain call
+    assert _conv_fused(gmi, act=2) == gmi.GMI_ERR_INVALID_ARG
+    assert _conv_fused(gmi, act=-1) == gmi.GMI_ERR_INVALID_ARG
+    assert _conv_fused(gmi, bias=A16 + 2) == gmi.GMI_ERR_MISALIGNED
+    assert _conv_fused(gmi, C=12) == gmi.GMI_ERR_MISALIGNED
+    assert _conv_fused(gmi, dt=3) == gmi.GMI_ERR_UNSUPPORTED
+    assert _conv_fused(gmi, x=None) == gmi.GMI_ERR_INVALID_ARG
+    assert _conv_fused(gmi, N=0) == gmi.GMI_OK  # no images: nothing to do, nothing launched
