@@ -271,9 +271,25 @@ def bench_workloads(torch, gmi, gi, dev, args):
 
     ms = time_launches(torch, fn, R, 5, max(50, 2 * R))
     out["moe_w4_decode_bf16"] = dict(roof(2.0 * int(w4_counts.sum()) * N * K, by, ms), bound="hbm", experts_live=live)
-    del sets, wpp, Sx, Zx, Xm, Ym
+    del Xm, Ym
+    # 4c. the same experts on a prefill batch: 16384 rows routed like the bf16 MoE layer (groups above 64 rows
+    # take the tiled launch, the rest the decode launch)
+    p_counts = gi.moe_w4_counts(rows=16384)
+    Xp = t16(torch, gi.moe_w4_activations(rows=16384), torch.bfloat16, dev)
+    Yp = torch.empty((16384, N), dtype=torch.bfloat16, device=dev)
+    p_offs = torch.tensor(np.concatenate([[0], np.cumsum(p_counts)]).astype(np.int32), device=dev)
+    p_live = int((p_counts > 0).sum())
+    p_by = p_live * (N * K // 2 + (K // 128) * N * 2 + (K // 128) * N // 2) + 2 * 16384 * (K + N)
+
+    def fnp(i, sets=sets):
+        w, s, z = sets[i]
+        gmi.gemm_mixed_grouped(p_offs, Xp, w, s, z, 128, N, w_type="int4", Y=Yp)
+
+    ms = time_launches(torch, fnp, R, 3, max(10, 2 * R))
+    out["moe_w4_prefill_bf16"] = dict(roof(2.0 * 16384 * N * K, p_by, ms), bound="mfma", experts_live=p_live)
+    del sets, wpp, Sx, Zx, Xp, Yp
     torch.cuda.empty_cache()
-    log("bench: MoE W4 decode done")
+    log("bench: MoE W4 decode and prefill done")
 
     bench_conv(torch, gmi, gi, dev, out)
 

@@ -13,6 +13,8 @@
 //     The waves of a workgroup split K and reduce through LDS.
 //   * k_w4a16_tiled (M > 64) is the dense mainloop with the weight loader
 //     (W4Loader) dequantising into the LDS B tile.
+#include <climits>
+
 #include "gmi_device.hpp"
 #include "gmi_internal.hpp"
 
@@ -541,12 +543,12 @@ constexpr int kGroupedWaves = 4, kGroupedRing = 4;
 constexpr int kGroupedLds = kGroupedWaves * DecodeLds<2, kGroupedRing>::WAVE;
 
 template <int DT>
-__global__ __launch_bounds__(64 * kGroupedWaves, 4) void k_w4a16_grouped(W4Grouped a) {
+__global__ __launch_bounds__(64 * kGroupedWaves, 4) void k_w4a16_grouped(W4Grouped a, int max_rows) {
   __shared__ __attribute__((aligned(16))) char lds[kGroupedLds];
   const int g = blockIdx.y;
   const int lo = min(max(a.offsets[g], 0), a.rows);
   const int hi = min(max(a.offsets[g + 1], 0), a.rows);
-  if (hi <= lo) return;
+  if (hi <= lo || hi - lo > max_rows) return;  // empty, or taken by the tiled launch
   W4Launch p = a.base;
   p.w = a.base.w + g * a.w_stride;
   p.scales = a.base.scales + g * a.s_stride;
@@ -561,12 +563,125 @@ __global__ __launch_bounds__(64 * kGroupedWaves, 4) void k_w4a16_grouped(W4Group
   }
 }
 
+// ---------------------------------------------------------------------------
+// Tiled path of the grouped call, for groups of more than kGroupedDecodeRows
+// rows (a prefill-size batch routed to an expert): a persistent walk over the
+// 128 x 128 output tiles of those groups through the tiled mainloop (X tiles
+// by direct copies, the group's weight dequantised into LDS), so each weight
+// panel is read once per 128 rows instead of once per 16.  Group sizes are
+// only on the device, so every wave turns the offsets into a tile prefix held
+// in its own registers (count <= kMaxOffsetGroupCount: lane l holds the first
+// tile of groups 16 l .. 16 l + 15), and finds the group of tile t as the
+// number of groups whose first tile is <= t, minus one (first tiles never
+// decrease, and an empty group shares its successor's).  No LDS beyond the
+// mainloop's, so two workgroups share a CU.  Inside a group the tiles run
+// m-fastest, so the workgroups that share a weight panel run together and
+// find it in L2.
+// ---------------------------------------------------------------------------
+constexpr int kGroupedDecodeRows = 64;
+constexpr int kGroupsPerLane = kMaxOffsetGroupCount / 64;
+
+// wave-wide sum of v (every lane gets it)
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) v += __shfl_xor(v, d, 64);
+  return v;
+}
+
+template <class Cfg, int DT>
+__global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_w4a16_grouped_tiled(W4Grouped a) {
+  __shared__ __attribute__((aligned(16))) char lds[W4Ring<Cfg>::BYTES];
+  const int lane = threadIdx.x & 63;
+  const int tn = (a.base.N + Cfg::BN - 1) / Cfg::BN;
+  auto clip = [&](int v) { return min(max(v, 0), a.rows); };
+
+  // tiles of groups 16 lane .. + 15 (0 for those the decode launch takes),
+  // then their first tiles: an exclusive scan over the lanes
+  int first[kGroupsPerLane];
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < kGroupsPerLane; ++i) {
+    const int g = lane * kGroupsPerLane + i;
+    int c = 0;
+    if (g < a.count) {
+      const int rows = clip(a.offsets[g + 1]) - clip(a.offsets[g]);
+      if (rows > kGroupedDecodeRows) c = ((rows + Cfg::BM - 1) / Cfg::BM) * tn;
+    }
+    first[i] = c;  // the count for now
+    sum += c;
+  }
+  int incl = sum;  // inclusive scan of the lane sums
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += v;
+  }
+  const int total = __shfl(incl, 63, 64);
+  int run = incl - sum;
+#pragma unroll
+  for (int i = 0; i < kGroupsPerLane; ++i) {
+    const int c = first[i];
+    first[i] = run;
+    run += c;
+  }
+
+  const int G = gridDim.x;
+  for (int base = 0; base < total; base += G) {
+    const int t = base + remap_slot(blockIdx.x, G);
+    if (t >= total) break;
+    int below = 0;  // groups of this lane whose first tile is <= t
+#pragma unroll
+    for (int i = 0; i < kGroupsPerLane; ++i) below += first[i] <= t && lane * kGroupsPerLane + i < a.count;
+    const int g = __builtin_amdgcn_readfirstlane(wave_sum(below) - 1);
+    int mine = 0;  // first tile of group g, from the lane that holds it
+#pragma unroll
+    for (int i = 0; i < kGroupsPerLane; ++i) mine = (i == g % kGroupsPerLane) ? first[i] : mine;
+    const int g_first = __builtin_amdgcn_readfirstlane(__shfl(mine, g / kGroupsPerLane, 64));
+    const int row0 = clip(a.offsets[g]), rows = clip(a.offsets[g + 1]) - row0;
+    const int tm = (rows + Cfg::BM - 1) / Cfg::BM;
+    const int local = t - g_first;
+    Tile tt;
+    tt.M = rows;
+    tt.N = a.base.N;
+    tt.K = a.base.K;
+    tt.m0 = (local % tm) * Cfg::BM;
+    tt.n0 = (local / tm) * Cfg::BN;
+    tt.C = nullptr;
+    tt.ldc = 0;
+    tt.D = a.base.Y + (int64_t)row0 * a.base.ldy;
+    tt.ldd = a.base.ldy;
+    const W4Launch& b = a.base;
+    const W4Geom geo{b.w + g * a.w_stride, b.scales + g * a.s_stride, b.zeros + g * a.z_stride, b.N, b.K, b.group,
+                     b.s_bytes, b.z_bytes, b.sor, b.wxor, b.zxor};
+    DenseLoader<Cfg, Cfg::BM> al;
+    W4Loader<Cfg, Cfg::BN, DT> bl;
+    al.init(b.X + (int64_t)row0 * b.ldx, b.ldx, tt.m0, rows, b.K);
+    bl.init(geo, tt.n0, 0);
+    f32x16 acc[Cfg::TM][Cfg::TN];
+    mainloop_w4<Cfg, DT>(lds, al, bl, b.K / Cfg::BK, acc);
+    store_tile<Cfg, DT>(tt, acc, 1.0f, 0.0f, lds);
+  }
+}
+
 hipError_t launch_w4a16_grouped(const W4Grouped& a, hipStream_t stream) {
+  // groups of more than kGroupedDecodeRows rows go to the tiled launch when
+  // the group count fits its table (and some group can be that large)
+  const bool tiled = a.count <= kMaxOffsetGroupCount && a.rows > kGroupedDecodeRows;
+  const int max_rows = tiled ? kGroupedDecodeRows : INT_MAX;
   const dim3 grid((a.base.N + 31) / 32, a.count);
   if (a.base.dt == DT_BF16)
-    hipLaunchKernelGGL(k_w4a16_grouped<DT_BF16>, grid, dim3(64 * kGroupedWaves), 0, stream, a);
+    hipLaunchKernelGGL(k_w4a16_grouped<DT_BF16>, grid, dim3(64 * kGroupedWaves), 0, stream, a, max_rows);
   else
-    hipLaunchKernelGGL(k_w4a16_grouped<DT_F16>, grid, dim3(64 * kGroupedWaves), 0, stream, a);
+    hipLaunchKernelGGL(k_w4a16_grouped<DT_F16>, grid, dim3(64 * kGroupedWaves), 0, stream, a, max_rows);
+  if (!tiled) return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  int g1 = device_cu_count() * W4Cfg128::WGS_PER_CU / XCDS * XCDS;
+  if (g1 < XCDS) g1 = XCDS;
+  if (a.base.dt == DT_BF16)
+    hipLaunchKernelGGL((k_w4a16_grouped_tiled<W4Cfg128, DT_BF16>), dim3(g1), dim3(W4Cfg128::THREADS), 0, stream, a);
+  else
+    hipLaunchKernelGGL((k_w4a16_grouped_tiled<W4Cfg128, DT_F16>), dim3(g1), dim3(W4Cfg128::THREADS), 0, stream, a);
   return hipGetLastError();
 }
 
