@@ -579,6 +579,9 @@ __global__ __launch_bounds__(64 * kGroupedWaves, 4) void k_w4a16_grouped(W4Group
 // find it in L2.
 // ---------------------------------------------------------------------------
 constexpr int kGroupedDecodeRows = 64;
+// calls of at most this many rows run every group through the decode body:
+// the tiled launch would cost more than a group of that size saves
+constexpr int kGroupedTiledMinRows = 256;
 constexpr int kGroupsPerLane = kMaxOffsetGroupCount / 64;
 
 // wave-wide sum of v (every lane gets it)
@@ -665,8 +668,9 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_w4a16_grouped
 
 hipError_t launch_w4a16_grouped(const W4Grouped& a, hipStream_t stream) {
   // groups of more than kGroupedDecodeRows rows go to the tiled launch when
-  // the group count fits its table (and some group can be that large)
-  const bool tiled = a.count <= kMaxOffsetGroupCount && a.rows > kGroupedDecodeRows;
+  // the group count fits its table and the call has more than
+  // kGroupedTiledMinRows rows
+  const bool tiled = a.count <= kMaxOffsetGroupCount && a.rows > kGroupedTiledMinRows;
   const int max_rows = tiled ? kGroupedDecodeRows : INT_MAX;
   const dim3 grid((a.base.N + 31) / 32, a.count);
   if (a.base.dt == DT_BF16)

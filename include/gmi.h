@@ -247,10 +247,10 @@ gmi_status gmi_gemm_mixed(int32_t M, int32_t N, int32_t K, gmi_dtype x_dtype, co
  * Modes, types and layouts as for gmi_gemm_mixed.  A group of at most 64
  * rows runs 16 rows at a time through the M <= 16 kernel body (exact integers
  * v(q) - v(z) into the matrix instruction, each group's scale on the fp32
- * partial sums).  When count <= 1024, larger groups run a second launch over
- * their 128 x 128 output tiles through the tiled mainloop (each weight
- * dequantised once to the activation type, as gmi_gemm_mixed does for
- * M > 64); with more groups they too take the 16-row body.  Both launches
+ * partial sums).  When count <= 1024 and rows > 256, larger groups run a
+ * second launch over their 128 x 128 output tiles through the tiled mainloop
+ * (each weight dequantised once to the activation type, as gmi_gemm_mixed
+ * does for M > 64); otherwise they too take the 16-row body.  Both launches
  * are enqueued on `stream` and write disjoint rows.  No workspace. */
 gmi_status gmi_gemm_mixed_grouped(int32_t count, const int32_t* offsets, int32_t rows, int32_t N, int32_t K,
                                   gmi_dtype x_dtype, const void* X, int64_t ldx, const uint8_t* w_prepacked,

@@ -3,11 +3,12 @@ as device row offsets, one prepacked 4-bit weight with its scales and zero
 points per group.  Each group is checked against the fp64 oracle on its own
 rows and weights, and against the same group launched alone, bit for bit.
 
-Tolerance: |d - ref| <= 1e-2 |ref| + 1e-2 for groups of up to 64 rows (the
-exact-integer-weight decode body, 16 rows at a time) and for fp16.  A larger
-group runs the tiled kernel, which with bf16 activations rounds every
-dequantised weight to bf16 (up to 2^-9 |w| each), so its bar adds
-2^-8 sum_k |x_k w_k|, as for the plain tiled call."""
+Tolerance: |d - ref| <= 1e-2 |ref| + 1e-2 for groups that run the
+exact-integer-weight decode body (16 rows at a time) and for fp16.  A group of
+more than 64 rows in a call of more than 256 rows runs the tiled kernel,
+which with bf16 activations rounds every dequantised weight to bf16 (up to
+2^-9 |w| each), so its bar adds 2^-8 sum_k |x_k w_k|, as for the plain tiled
+call."""
 import numpy as np
 import pytest
 import torch
@@ -18,7 +19,8 @@ from helpers import SENTINEL, bytes_to_dev, check_close, dev, host_bits, to_dev
 
 pytestmark = pytest.mark.gpu
 
-TILED_ROWS = 64  # groups above this many rows run the tiled kernel
+TILED_ROWS = 64  # groups above this many rows run the tiled kernel ...
+TILED_CALL_ROWS = 256  # ... in calls of more than this many rows
 
 
 @pytest.fixture(scope="module")
@@ -63,7 +65,7 @@ def _check_groups(got, offsets, rows, X, W, S, Z, N, K, group, dtype, w_type, mo
         z = Z[g] if mode == "zero" else None
         ref = oracle.mixed(X[lo:hi], W[g], s, z, N, K, group, w_type, dtype)
         what = f"group {g} rows {lo}:{hi} {dtype} {w_type} {mode}"
-        if dtype == "bf16" and hi - lo > TILED_ROWS:
+        if dtype == "bf16" and hi - lo > TILED_ROWS and rows > TILED_CALL_ROWS:
             w = oracle.dequant_mixed(W[g], s, z, N, K, group, w_type, dtype)
             mag = np.abs(oracle.decode(X[lo:hi], dtype)) @ np.abs(w).T
             d = oracle.decode(got[lo:hi], dtype)
@@ -92,7 +94,8 @@ def test_mixed_grouped_moe_decode(gmi, dtype, w_type, mode):
 
 
 def test_mixed_grouped_large_groups_in_chunks(gmi):
-    # groups of 150 and 64 rows: 16-row chunks, the last one partial
+    # groups of 150 and 64 rows in a call of 217 rows: all through the decode body, 16-row chunks, the last
+    # one partial
     counts = np.array([150, 0, 64, 3])
     N, K, group = 128, 1024, 256
     rows = int(counts.sum())
@@ -184,3 +187,40 @@ def test_mixed_grouped_many_groups_all_decode(gmi):
     off = np.concatenate([[0], np.cumsum(counts)])
     got, *_ = _run(gmi, off, rows, X, W, S, Z, N, K, group, "f16", "uint4", "zero")
     _check_groups(got, off, rows, X, W, S, Z, N, K, group, "f16", "uint4", "zero")
+
+
+def test_moe_w4_prefill_full_size_sampled(gmi):
+    # the bench's 4-bit MoE prefill layer: 16384 rows routed over 128 experts (N 2048, K 4096, g 128, bf16,
+    # int4 with zero points); 8 sampled rows of the four largest experts (tiled launch), of a mid-size one
+    # and of every row of one decode-size expert, against the oracle
+    N, K, group = 2048, 4096, 128
+    counts = gi.moe_w4_counts(rows=16384)
+    order = np.argsort(-counts)
+    mid = int(order[np.searchsorted(-counts[order], -100)])           # about 100 rows: tiled
+    small = int([g for g in order if 0 < counts[g] <= 64][0])         # the largest decode-size group
+    picks = [int(g) for g in order[:4]] + [mid, small]
+    experts = {g: gi.moe_w4_expert(g) for g in range(len(counts))}
+    wpp = torch.stack([gmi.prepack_w4(bytes_to_dev(experts[g][0]), N, K) for g in range(len(counts))])
+    Sx = torch.stack([to_dev(experts[g][1], "bf16") for g in range(len(counts))])
+    Zx = torch.stack([bytes_to_dev(experts[g][2]) for g in range(len(counts))])
+    X = gi.moe_w4_activations(rows=16384)
+    off = np.concatenate([[0], np.cumsum(counts)])
+    Y = gmi.gemm_mixed_grouped(torch.tensor(off.astype(np.int32), device=dev()), to_dev(X, "bf16"), wpp, Sx, Zx,
+                               group, N, w_type="int4")
+    torch.cuda.synchronize()
+    got = host_bits(Y)
+    r = np.random.default_rng(17)
+    for g in picks:
+        lo, hi = int(off[g]), int(off[g + 1])
+        rows = np.arange(lo, hi) if hi - lo <= 64 else np.sort(r.choice(np.arange(lo, hi), 8, replace=False))
+        w, s, z = experts[g]
+        ref = oracle.mixed(X[rows], w, s, z, N, K, group, "int4", "bf16")
+        what = f"prefill expert {g} ({hi - lo} rows)"
+        if hi - lo > TILED_ROWS:
+            wd = oracle.dequant_mixed(w, s, z, N, K, group, "int4", "bf16")
+            mag = np.abs(oracle.decode(X[rows], "bf16")) @ np.abs(wd).T
+            d = oracle.decode(got[rows], "bf16")
+            bad = ~(np.abs(d - ref) <= 1e-2 * np.abs(ref) + 1e-2 + 2.0**-8 * mag)
+            assert not bad.any(), f"{what}: {int(bad.sum())} of {bad.size} outside tolerance"
+        else:
+            check_close(got[rows], ref, "bf16", what)
