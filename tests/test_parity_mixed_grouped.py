@@ -224,3 +224,19 @@ def test_moe_w4_prefill_full_size_sampled(gmi):
             assert not bad.any(), f"{what}: {int(bad.sum())} of {bad.size} outside tolerance"
         else:
             check_close(got[rows], ref, "bf16", what)
+
+
+def test_mixed_grouped_tiled_is_deterministic_and_covers_every_row(gmi):
+    # three calls over Zipf-routed groups (several tiles per workgroup, partial row tiles, both launches):
+    # every output element written, the same bits each time
+    N, K, group = 512, 1024, 128
+    counts = gi.moe_w4_counts(rows=6000, groups=64)
+    rows = int(counts.sum())
+    r = np.random.default_rng(19)
+    X = gi.to_bits(r.standard_normal((rows, K)).astype(np.float32), "bf16")
+    W, S, Z = _experts(len(counts), N, K, group, "bf16", seed=20)
+    off = np.concatenate([[0], np.cumsum(counts)])
+    outs = [_run(gmi, off, rows, X, W, S, Z, N, K, group, "bf16", "int4", "zero")[0] for _ in range(3)]
+    assert not np.any(outs[0] == SENTINEL), "output elements left unwritten"
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+    assert (counts > TILED_ROWS).sum() >= 10 and ((counts > 0) & (counts <= TILED_ROWS)).sum() >= 5
