@@ -265,10 +265,15 @@ __device__ __forceinline__ void decode_body(const W4Launch& a, int n_base, char*
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         x[s][j] = buf_load16(rx, ok ? (r * (uint32_t)a.ldx + (base + s) * 128 + j * 32 + h * 8) * 2u : OOB);
+      // the waits below count in issue order: no load of a later slot (a
+      // plain load the compiler could hoist) may go out before this slot's
+      // weight copies (which it does not track)
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int s = 0; s < R; ++s) {
       // weight blocks and X fragments of slot s (and everything older)
+      __builtin_amdgcn_sched_barrier(0);
       wait_vm_le_n<(R - 1) * (NB + 4)>((R - 1 - s) * (NB + 4));
       if (base + s < kb1) {
 #pragma unroll
@@ -358,12 +363,17 @@ __device__ __forceinline__ void w4_step(char* lds, const ALd& al, const BLd& bl,
                                         frag_t<Cfg> (&fb)[2][Cfg::TN]) {
   using Ring = W4Ring<Cfg>;
   constexpr int YOUNG = ALd::P + 3 * BLd::P;  // one k-tile's copies and loads
+  // The wait below counts outstanding loads in issue order, and the compiler
+  // does not track the direct-to-LDS copies: the fences keep every load and
+  // copy of k-tile kt + 2 between the previous step's wait and this one's.
+  __builtin_amdgcn_sched_barrier(0);
   bl.load(kt + 2, rl);
   const char* ca = Ring::a(lds, kt % 3);
   const char* cb = Ring::b(lds, kt & 1);
   read_frags<Cfg>(ad, ca, cb, 0, fa[0], fb[0]);
   multiply_stage<Cfg, DT, false, 2>(ad, ca, cb, ca, cb, acc, fa, fb, al, kt + 2, Ring::a(lds, (kt + 2) % 3), bl, 0,
                                     nullptr);
+  __builtin_amdgcn_sched_barrier(0);
   wait_vm_le<YOUNG>();
   if (kt + 1 < nk) bl.store(Ring::b(lds, (kt + 1) & 1), rs);
   wait_lgkm();
@@ -387,11 +397,18 @@ __device__ __forceinline__ void mainloop_w4(char* lds, const ALd& al, const BLd&
   FragAddr<Cfg> ad;
   ad.init();
   typename BLd::Regs r0, r1;
-  // prologue: k-tiles 0 and 1 in flight; 0 landed and published
+  // prologue: k-tiles 0 and 1 in flight; 0 landed and published.  The wait
+  // leaves k-tile 1's loads and copies in flight, so all of k-tile 0's must
+  // be issued before any of them: the compiler may otherwise hoist a weight
+  // load of k-tile 1 (a plain load into registers) above a copy of k-tile 0
+  // (which it does not track), and the wait would then release before that
+  // copy has landed.
   bl.load(0, r0);
   al.issue(0, Ring::a(lds, 0));
+  __builtin_amdgcn_sched_barrier(0);
   bl.load(1, r1);
   al.issue(1, Ring::a(lds, 1));
+  __builtin_amdgcn_sched_barrier(0);
   wait_vm_le<YOUNG>();
   bl.store(Ring::b(lds, 0), r0);
   wait_lgkm();
