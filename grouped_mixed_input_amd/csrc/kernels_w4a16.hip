@@ -595,7 +595,7 @@ __global__ __launch_bounds__(64 * kGroupedWaves, 4) void k_w4a16_grouped(W4Group
 // m-fastest, so the workgroups that share a weight panel run together and
 // find it in L2.
 // ---------------------------------------------------------------------------
-constexpr int kGroupedDecodeRows = 64;
+constexpr int kGroupedDecodeRows = 32;
 // calls of at most this many rows run every group through the decode body:
 // the tiled launch would cost more than a group of that size saves
 constexpr int kGroupedTiledMinRows = 256;

@@ -244,7 +244,7 @@ gmi_status gmi_gemm_mixed(int32_t M, int32_t N, int32_t K, gmi_dtype x_dtype, co
  *   strides  at least one group's data when count > 1 (N*K/2 bytes,
  *            (K/group)*N scales, (K/group)*N/2 zero bytes) and keeping every
  *            group's data 16-byte aligned; ignored for a NULL array.
- * Modes, types and layouts as for gmi_gemm_mixed.  A group of at most 64
+ * Modes, types and layouts as for gmi_gemm_mixed.  A group of at most 32
  * rows runs 16 rows at a time through the M <= 16 kernel body (exact integers
  * v(q) - v(z) into the matrix instruction, each group's scale on the fp32
  * partial sums).  When count <= 1024 and rows > 256, larger groups run a

@@ -5,7 +5,7 @@ rows and weights, and against the same group launched alone, bit for bit.
 
 Tolerance: |d - ref| <= 1e-2 |ref| + 1e-2 for groups that run the
 exact-integer-weight decode body (16 rows at a time) and for fp16.  A group of
-more than 64 rows in a call of more than 256 rows runs the tiled kernel,
+more than 32 rows in a call of more than 256 rows runs the tiled kernel,
 which with bf16 activations rounds every dequantised weight to bf16 (up to
 2^-9 |w| each), so its bar adds 2^-8 sum_k |x_k w_k|, as for the plain tiled
 call."""
@@ -19,7 +19,7 @@ from helpers import SENTINEL, bytes_to_dev, check_close, dev, host_bits, to_dev
 
 pytestmark = pytest.mark.gpu
 
-TILED_ROWS = 64  # groups above this many rows run the tiled kernel ...
+TILED_ROWS = 32  # groups above this many rows run the tiled kernel ...
 TILED_CALL_ROWS = 256  # ... in calls of more than this many rows
 
 
@@ -141,9 +141,9 @@ def test_mixed_grouped_groups_are_independent(gmi):
 @pytest.mark.parametrize("dtype,w_type,mode", [("f16", "uint4", "zero"), ("bf16", "int4", "zero"),
                                                ("bf16", "uint4", "scale"), ("f16", "int4", "direct")])
 def test_mixed_grouped_prefill_groups_tiled(gmi, dtype, w_type, mode):
-    # groups above 64 rows run the tiled launch (128 x 128 tiles, ragged in rows and in N), the others the
+    # groups above 32 rows run the tiled launch (128 x 128 tiles, ragged in rows and in N), the others the
     # decode launch, in one call; empty groups between them
-    counts = np.array([0, 3, 64, 65, 0, 300, 129, 1, 513, 16])
+    counts = np.array([0, 3, 32, 33, 0, 300, 129, 1, 513, 16, 64])
     N, K, group = 320, 512, 128
     rows = int(counts.sum()) + 7
     r = np.random.default_rng(11)
