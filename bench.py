@@ -153,6 +153,51 @@ def bench_moe(torch, gmi, gi, dev, out):
     return counts, off
 
 
+def bench_moe_w4(torch, gmi, gi, dev, out):
+    # 4b. MoE decode step with 4-bit experts: 128 routed rows over 128 experts
+    # (N 2048, K 4096, g 128), bf16, int4 with zero points, sizes on the device
+    w4_counts = gi.moe_w4_counts()
+    E, N, K = len(w4_counts), 2048, 4096
+    experts = [gi.moe_w4_expert(e) for e in range(E)]
+    wpp = torch.stack([gmi.prepack_w4(torch.from_numpy(w).to(dev), N, K) for w, _, _ in experts])
+    Sx = torch.stack([t16(torch, s, torch.bfloat16, dev) for _, s, _ in experts])
+    Zx = torch.stack([torch.from_numpy(z).to(dev) for _, _, z in experts])
+    del experts
+    Xm = t16(torch, gi.moe_w4_activations(rows=int(w4_counts.sum())), torch.bfloat16, dev)
+    Ym = torch.empty((Xm.shape[0], N), dtype=torch.bfloat16, device=dev)
+    offs = torch.tensor(np.concatenate([[0], np.cumsum(w4_counts)]).astype(np.int32), device=dev)
+    live = int((w4_counts > 0).sum())
+    by = live * (N * K // 2 + (K // 128) * N * 2 + (K // 128) * N // 2) + 2 * int(w4_counts.sum()) * (K + N)
+    R = copies_for(by)
+    sets = [(wpp, Sx, Zx)] + [(wpp.clone(), Sx.clone(), Zx.clone()) for _ in range(R - 1)]
+
+    def fn(i, sets=sets):
+        w, s, z = sets[i]
+        gmi.gemm_mixed_grouped(offs, Xm, w, s, z, 128, N, w_type="int4", Y=Ym)
+
+    ms = time_launches(torch, fn, R, 5, max(50, 2 * R))
+    out["moe_w4_decode_bf16"] = dict(roof(2.0 * int(w4_counts.sum()) * N * K, by, ms), bound="hbm", experts_live=live)
+    del Xm, Ym
+    # 4c. the same experts on a prefill batch: 16384 rows routed like the bf16 MoE layer (groups above 32 rows
+    # take the tiled launch, the rest the decode launch)
+    p_counts = gi.moe_w4_counts(rows=16384)
+    Xp = t16(torch, gi.moe_w4_activations(rows=16384), torch.bfloat16, dev)
+    Yp = torch.empty((16384, N), dtype=torch.bfloat16, device=dev)
+    p_offs = torch.tensor(np.concatenate([[0], np.cumsum(p_counts)]).astype(np.int32), device=dev)
+    p_live = int((p_counts > 0).sum())
+    p_by = p_live * (N * K // 2 + (K // 128) * N * 2 + (K // 128) * N // 2) + 2 * 16384 * (K + N)
+
+    def fnp(i, sets=sets):
+        w, s, z = sets[i]
+        gmi.gemm_mixed_grouped(p_offs, Xp, w, s, z, 128, N, w_type="int4", Y=Yp)
+
+    ms = time_launches(torch, fnp, R, 3, max(10, 2 * R))
+    out["moe_w4_prefill_bf16"] = dict(roof(2.0 * 16384 * N * K, p_by, ms), bound="mfma", experts_live=p_live)
+    del sets, wpp, Sx, Zx, Xp, Yp
+    torch.cuda.empty_cache()
+    log("bench: MoE W4 decode and prefill done")
+
+
 def bench_conv(torch, gmi, gi, dev, out):
     """Conv fprop, dgrad and wgrad of one 3x3 layer."""
     # 5. conv fprop bf16 32x56x56x256, 3x3x256 -> 256, pad 1
@@ -248,48 +293,7 @@ def bench_workloads(torch, gmi, gi, dev, args):
         del sets
     log("bench: W4A16 done")
 
-    # 4b. MoE decode step with 4-bit experts: 128 routed rows over 128 experts
-    # (N 2048, K 4096, g 128), bf16, int4 with zero points, sizes on the device
-    w4_counts = gi.moe_w4_counts()
-    E, N, K = len(w4_counts), 2048, 4096
-    experts = [gi.moe_w4_expert(e) for e in range(E)]
-    wpp = torch.stack([gmi.prepack_w4(torch.from_numpy(w).to(dev), N, K) for w, _, _ in experts])
-    Sx = torch.stack([t16(torch, s, torch.bfloat16, dev) for _, s, _ in experts])
-    Zx = torch.stack([torch.from_numpy(z).to(dev) for _, _, z in experts])
-    del experts
-    Xm = t16(torch, gi.moe_w4_activations(rows=int(w4_counts.sum())), torch.bfloat16, dev)
-    Ym = torch.empty((Xm.shape[0], N), dtype=torch.bfloat16, device=dev)
-    offs = torch.tensor(np.concatenate([[0], np.cumsum(w4_counts)]).astype(np.int32), device=dev)
-    live = int((w4_counts > 0).sum())
-    by = live * (N * K // 2 + (K // 128) * N * 2 + (K // 128) * N // 2) + 2 * int(w4_counts.sum()) * (K + N)
-    R = copies_for(by)
-    sets = [(wpp, Sx, Zx)] + [(wpp.clone(), Sx.clone(), Zx.clone()) for _ in range(R - 1)]
-
-    def fn(i, sets=sets):
-        w, s, z = sets[i]
-        gmi.gemm_mixed_grouped(offs, Xm, w, s, z, 128, N, w_type="int4", Y=Ym)
-
-    ms = time_launches(torch, fn, R, 5, max(50, 2 * R))
-    out["moe_w4_decode_bf16"] = dict(roof(2.0 * int(w4_counts.sum()) * N * K, by, ms), bound="hbm", experts_live=live)
-    del Xm, Ym
-    # 4c. the same experts on a prefill batch: 16384 rows routed like the bf16 MoE layer (groups above 64 rows
-    # take the tiled launch, the rest the decode launch)
-    p_counts = gi.moe_w4_counts(rows=16384)
-    Xp = t16(torch, gi.moe_w4_activations(rows=16384), torch.bfloat16, dev)
-    Yp = torch.empty((16384, N), dtype=torch.bfloat16, device=dev)
-    p_offs = torch.tensor(np.concatenate([[0], np.cumsum(p_counts)]).astype(np.int32), device=dev)
-    p_live = int((p_counts > 0).sum())
-    p_by = p_live * (N * K // 2 + (K // 128) * N * 2 + (K // 128) * N // 2) + 2 * 16384 * (K + N)
-
-    def fnp(i, sets=sets):
-        w, s, z = sets[i]
-        gmi.gemm_mixed_grouped(p_offs, Xp, w, s, z, 128, N, w_type="int4", Y=Yp)
-
-    ms = time_launches(torch, fnp, R, 3, max(10, 2 * R))
-    out["moe_w4_prefill_bf16"] = dict(roof(2.0 * 16384 * N * K, p_by, ms), bound="mfma", experts_live=p_live)
-    del sets, wpp, Sx, Zx, Xp, Yp
-    torch.cuda.empty_cache()
-    log("bench: MoE W4 decode and prefill done")
+    bench_moe_w4(torch, gmi, gi, dev, out)
 
     bench_conv(torch, gmi, gi, dev, out)
 
@@ -358,8 +362,8 @@ def main():
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the W4A16 decode workload (M = 16, N = K = 8192, g = 128) and print one line "
                          "for it (for the decode kernel's profiles)")
-    ap.add_argument("--only", choices=["moe", "conv"],
-                    help="time only the MoE layers or only the conv layers and print their lines (for those "
+    ap.add_argument("--only", choices=["moe", "moe_w4", "conv"],
+                    help="time only the bf16 MoE layers, the 4-bit MoE layers or the conv layers and print their lines (for those "
                          "kernels' profiles)")
     ap.add_argument("--copy-ref", action="store_true",
                     help="after the timed region, run one plain 256 MiB device copy (a known-size kernel that "
@@ -386,7 +390,7 @@ def main():
         return
     if args.only:
         out = {}
-        (bench_moe if args.only == "moe" else bench_conv)(torch, gmi, gi, dev, out)
+        {"moe": bench_moe, "moe_w4": bench_moe_w4, "conv": bench_conv}[args.only](torch, gmi, gi, dev, out)
         copy_ref(torch, dev, args)
         print(json.dumps(out), flush=True)
         return

@@ -212,10 +212,12 @@ struct DecodeLds {
   static_assert(R * 4 <= 64, "one copy instruction carries a round's scale rows");
 };
 
-// weight rows n_base .. n_base + 16 NB of Y = X W^T for the a.M <= 16
-// tokens of X; `lds` holds KW * DecodeLds<NB, R>::WAVE bytes
-template <int DT, int NB, int KW, int R>
+// weight rows n_base .. n_base + 16 NB of Y = X W^T for the a.M <= 16 MT
+// tokens of X (MT 16-token tiles share each k-block's weights); `lds` holds
+// KW * DecodeLds<NB, R>::WAVE bytes
+template <int DT, int NB, int KW, int R, int MT = 1>
 __device__ __forceinline__ void decode_body(const W4Launch& a, int n_base, char* lds) {
+  static_assert(KW * NB * MT * 64 * 16 <= KW * DecodeLds<NB, R>::WAVE, "the reduction reuses the rings");
   using L = DecodeLds<NB, R>;
   const int lane = threadIdx.x & 63, wave = wave_id();
   char* wring = lds + wave * L::WAVE;
@@ -233,17 +235,18 @@ __device__ __forceinline__ void decode_body(const W4Launch& a, int n_base, char*
   const rsrc_t rz = make_rsrc(a.zeros, a.z_bytes);
   const uint32_t sor2 = a.sor * 0x00010001u;
   const uint32_t r = lane & 15, h = lane >> 4;
-  const bool tok_ok = (int)r < a.M;
   uint32_t magic = 0x64006400u;  // fp16 pair (1024, 1024): 1024 + q for a nibble q in the low mantissa bits
   asm volatile("" : "+v"(magic));
 
-  f32x4 acc[NB];
+  f32x4 acc[NB][MT];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0, 0, 0, 0};
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = f32x4{0, 0, 0, 0};
 
   for (int rd = 0; rd < rounds; ++rd) {
     const int base = kb0 + rd * R;
-    u32x4 x[R][4];
+    u32x4 x[R][MT][4];
     {
       // scales: lane -> slot lane / 4, 8-row chunk lane % 4 (16 bytes);
       // zero points: the same slot and chunk, 4 bytes
@@ -261,10 +264,14 @@ __device__ __forceinline__ void decode_body(const W4Launch& a, int n_base, char*
         dma16(rw, base + s < kb1 && blk * 16 < N ? (blk * (uint32_t)kblocks + base + s) * 1024u + lane * 16u : OOB,
               wring + s * L::WSLOT + nb * 1024);
       }
-      const bool ok = base + s < kb1 && tok_ok;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        x[s][j] = buf_load16(rx, ok ? (r * (uint32_t)a.ldx + (base + s) * 128 + j * 32 + h * 8) * 2u : OOB);
+      for (int mt = 0; mt < MT; ++mt) {
+        const uint32_t tok = mt * 16 + r;
+        const bool ok = base + s < kb1 && (int)tok < a.M;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          x[s][mt][j] = buf_load16(rx, ok ? (tok * (uint32_t)a.ldx + (base + s) * 128 + j * 32 + h * 8) * 2u : OOB);
+      }
       // the waits below count in issue order: no load of a later slot (a
       // plain load the compiler could hoist) may go out before this slot's
       // weight copies (which it does not track)
@@ -274,7 +281,7 @@ __device__ __forceinline__ void decode_body(const W4Launch& a, int n_base, char*
     for (int s = 0; s < R; ++s) {
       // weight blocks and X fragments of slot s (and everything older)
       __builtin_amdgcn_sched_barrier(0);
-      wait_vm_le_n<(R - 1) * (NB + 4)>((R - 1 - s) * (NB + 4));
+      wait_vm_le_n<(R - 1) * (NB + 4 * MT)>((R - 1 - s) * (NB + 4 * MT));
       if (base + s < kb1) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
@@ -284,39 +291,53 @@ __device__ __forceinline__ void decode_body(const W4Launch& a, int n_base, char*
           const int row = nb * 16 + r;
           const uint32_t zbits =
               ((*(const uint8_t*)(szb + 1024 + s * 16 + row / 2) >> ((row & 1) * 4)) & 15u) ^ a.zxor;
-          f32x4 part = {0, 0, 0, 0};
+          f32x4 part[MT];
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) part[mt] = f32x4{0, 0, 0, 0};
           if constexpr (DT == DT_F16) {
             const f16x2 zz = zero_pair(zbits);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) part = mfma16<DT>(unpack8_minus_zero(wq[j], zz, magic), x[s][j], part);
+            for (int j = 0; j < 4; ++j) {
+              const u32x4 wf = unpack8_minus_zero(wq[j], zz, magic);
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt) part[mt] = mfma16<DT>(wf, x[s][mt][j], part[mt]);
+            }
           } else {
             const float zf = (float)zbits;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) part = mfma16<DT>(unpack8_minus_zero_bf16(wq[j], zf), x[s][j], part);
+            for (int j = 0; j < 4; ++j) {
+              const u32x4 wf = unpack8_minus_zero_bf16(wq[j], zf);
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt) part[mt] = mfma16<DT>(wf, x[s][mt][j], part[mt]);
+            }
           }
           // output rows of this lane: nb * 16 + 4 h + {0..3}
           const u32x2 sc = *(const u32x2*)(szb + s * 64 + (nb * 16 + 4 * h) * 2) | sor2;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[nb][i] = __builtin_fmaf(from_bits<DT>((sc[i / 2] >> (16 * (i % 2))) & 0xffffu), part[i],
-                                        acc[nb][i]);
+          for (int i = 0; i < 4; ++i) {
+            const float si = from_bits<DT>((sc[i / 2] >> (16 * (i % 2))) & 0xffffu);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[nb][mt][i] = __builtin_fmaf(si, part[mt][i], acc[nb][mt][i]);
+          }
         }
       }
     }
   }
   __syncthreads();  // every wave is done with its ring: reuse it for the reduction
 
-  f32x4* red = (f32x4*)lds;  // [KW][NB][64]
+  f32x4* red = (f32x4*)lds;  // [KW][NB][MT][64]
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) red[(wave * NB + nb) * 64 + lane] = acc[nb];
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) red[((wave * NB + nb) * MT + mt) * 64 + lane] = acc[nb][mt];
   __syncthreads();
-  // lane quad q of block nb: rows n_base + 16 nb + 4 (q / 16) + {0..3}, token q % 16
-  for (int idx = threadIdx.x; idx < NB * 64; idx += 64 * KW) {
+  // lane quad q of block nb, tile mt: rows n_base + 16 nb + 4 (q / 16) + {0..3}, token 16 mt + q % 16
+  for (int idx = threadIdx.x; idx < NB * MT * 64; idx += 64 * KW) {
     f32x4 t = red[idx];
 #pragma unroll
-    for (int w = 1; w < KW; ++w) t += red[w * NB * 64 + idx];
-    const int nb = idx / 64, q = idx % 64;
-    const int n = n_base + nb * 16 + 4 * (q / 16), tok = q % 16;
+    for (int w = 1; w < KW; ++w) t += red[w * NB * MT * 64 + idx];
+    const int nb = idx / (MT * 64), mt = (idx / 64) % MT, q = idx % 64;
+    const int n = n_base + nb * 16 + 4 * (q / 16), tok = mt * 16 + q % 16;
     if (tok < a.M && n < a.N)
       *(gu32x2*)(a.Y + (int64_t)tok * a.ldy + n) = u32x2{pack2<DT>(t[0], t[1]), pack2<DT>(t[2], t[3])};
   }
@@ -683,12 +704,42 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_w4a16_grouped
   }
 }
 
+// Groups of kGroupedPairRows + 1 .. kGroupedDecodeRows rows in a call that
+// takes the tiled launch: the decode body over both 16-row tiles of the
+// group at once (each k-block's weights unpacked once for the two tiles), so
+// the weight is streamed once instead of once per 16 rows, with the same
+// exact-integer arithmetic.  Workgroup (x, g) as in k_w4a16_grouped; every
+// other group returns at once.  The second tile's X fragments double the
+// registers a slot holds, so two workgroups share a CU instead of four.
+// ---------------------------------------------------------------------------
+constexpr int kGroupedPairRows = 16;
+constexpr int kPairRing = 4, kPairWgsPerCu = 2;
+constexpr int kPairLds = kGroupedWaves * DecodeLds<2, kPairRing>::WAVE;
+
+template <int DT>
+__global__ __launch_bounds__(64 * kGroupedWaves, kPairWgsPerCu) void k_w4a16_grouped_pair(W4Grouped a) {
+  __shared__ __attribute__((aligned(16))) char lds[kPairLds];
+  const int g = blockIdx.y;
+  const int lo = min(max(a.offsets[g], 0), a.rows);
+  const int hi = min(max(a.offsets[g + 1], 0), a.rows);
+  if (hi - lo <= kGroupedPairRows || hi - lo > kGroupedDecodeRows) return;
+  W4Launch p = a.base;
+  p.w = a.base.w + g * a.w_stride;
+  p.scales = a.base.scales + g * a.s_stride;
+  p.zeros = a.base.zeros + g * a.z_stride;
+  p.M = hi - lo;
+  p.X = a.base.X + (int64_t)lo * a.base.ldx;
+  p.Y = a.base.Y + (int64_t)lo * a.base.ldy;
+  decode_body<DT, 2, kGroupedWaves, kPairRing, 2>(p, blockIdx.x * 32, lds);
+}
+
 hipError_t launch_w4a16_grouped(const W4Grouped& a, hipStream_t stream) {
-  // groups of more than kGroupedDecodeRows rows go to the tiled launch when
-  // the group count fits its table and the call has more than
-  // kGroupedTiledMinRows rows
+  // when the group count fits the tiled launch's table and the call has more
+  // than kGroupedTiledMinRows rows, groups of more than kGroupedDecodeRows
+  // rows go to the tiled launch and those of more than kGroupedPairRows to
+  // the two-tile decode launch; otherwise the decode launch takes every group
   const bool tiled = a.count <= kMaxOffsetGroupCount && a.rows > kGroupedTiledMinRows;
-  const int max_rows = tiled ? kGroupedDecodeRows : INT_MAX;
+  const int max_rows = tiled ? kGroupedPairRows : INT_MAX;
   const dim3 grid((a.base.N + 31) / 32, a.count);
   if (a.base.dt == DT_BF16)
     hipLaunchKernelGGL(k_w4a16_grouped<DT_BF16>, grid, dim3(64 * kGroupedWaves), 0, stream, a, max_rows);
@@ -697,6 +748,12 @@ hipError_t launch_w4a16_grouped(const W4Grouped& a, hipStream_t stream) {
   if (!tiled) return hipGetLastError();
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.base.dt == DT_BF16)
+    hipLaunchKernelGGL(k_w4a16_grouped_pair<DT_BF16>, grid, dim3(64 * kGroupedWaves), 0, stream, a);
+  else
+    hipLaunchKernelGGL(k_w4a16_grouped_pair<DT_F16>, grid, dim3(64 * kGroupedWaves), 0, stream, a);
+  const hipError_t e2 = hipGetLastError();
+  if (e2 != hipSuccess) return e2;
   int g1 = device_cu_count() * W4Cfg128::WGS_PER_CU / XCDS * XCDS;
   if (g1 < XCDS) g1 = XCDS;
   if (a.base.dt == DT_BF16)
