@@ -208,8 +208,11 @@ struct DecodeLds {
   static constexpr int WRING = R * WSLOT;
   static constexpr int SZ = 2048;           // scales (1 KB) then zero points (1 KB)
   static constexpr int WAVE = WRING + SZ;
-  static_assert(NB == 2, "scale rows are 32 weight rows (64 bytes), zero rows 16 bytes");
-  static_assert(R * 4 <= 64, "one copy instruction carries a round's scale rows");
+  static constexpr int CHUNKS = 2 * NB;     // 8-row chunks per slot: 16 bytes of scales, 4 of zero points
+  static constexpr int SROW = NB * 32;      // scale bytes per slot
+  static constexpr int ZROW = NB * 8;       // zero-point bytes per slot
+  static_assert(R * CHUNKS <= 64, "one copy instruction carries a round's scale rows");
+  static_assert(R * SROW <= 1024 && R * ZROW <= 1024, "a round's scale and zero rows fit their 1 KB");
 };
 
 // weight rows n_base .. n_base + 16 NB of Y = X W^T for the a.M <= 16 MT
@@ -248,9 +251,9 @@ __device__ __forceinline__ void decode_body(const W4Launch& a, int n_base, char*
     const int base = kb0 + rd * R;
     u32x4 x[R][MT][4];
     {
-      // scales: lane -> slot lane / 4, 8-row chunk lane % 4 (16 bytes);
-      // zero points: the same slot and chunk, 4 bytes
-      const int s = lane >> 2, c = lane & 3, ks = base + s;
+      // scales: lane -> slot lane / CHUNKS, 8-row chunk lane % CHUNKS (16
+      // bytes); zero points: the same slot and chunk, 4 bytes
+      const int s = lane / L::CHUNKS, c = lane % L::CHUNKS, ks = base + s;
       const uint32_t gs = (uint32_t)(ks * 128) / (uint32_t)a.group;
       const bool ok = s < R && ks < kb1 && n_base + 8 * c < (int)N;
       dma16(rs, ok ? (gs * N + n_base + 8 * c) * 2u : OOB, szb);
@@ -290,7 +293,7 @@ __device__ __forceinline__ void decode_body(const W4Launch& a, int n_base, char*
           const u32x4 wq = *(const u32x4*)(wring + s * L::WSLOT + nb * 1024 + lane * 16) ^ a.wxor;
           const int row = nb * 16 + r;
           const uint32_t zbits =
-              ((*(const uint8_t*)(szb + 1024 + s * 16 + row / 2) >> ((row & 1) * 4)) & 15u) ^ a.zxor;
+              ((*(const uint8_t*)(szb + 1024 + s * L::ZROW + row / 2) >> ((row & 1) * 4)) & 15u) ^ a.zxor;
           f32x4 part[MT];
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) part[mt] = f32x4{0, 0, 0, 0};
@@ -312,7 +315,7 @@ __device__ __forceinline__ void decode_body(const W4Launch& a, int n_base, char*
             }
           }
           // output rows of this lane: nb * 16 + 4 h + {0..3}
-          const u32x2 sc = *(const u32x2*)(szb + s * 64 + (nb * 16 + 4 * h) * 2) | sor2;
+          const u32x2 sc = *(const u32x2*)(szb + s * L::SROW + (nb * 16 + 4 * h) * 2) | sor2;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float si = from_bits<DT>((sc[i / 2] >> (16 * (i % 2))) & 0xffffu);
@@ -708,13 +711,15 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_w4a16_grouped
 // takes the tiled launch: the decode body over both 16-row tiles of the
 // group at once (each k-block's weights unpacked once for the two tiles), so
 // the weight is streamed once instead of once per 16 rows, with the same
-// exact-integer arithmetic.  Workgroup (x, g) as in k_w4a16_grouped; every
+// exact-integer arithmetic.  Workgroup (x, g) takes weight rows 64 x ..
+// 64 x + 63 of group g (every workgroup of a group reads all of its X, twice
+// the bytes of its weight slice, so wider slices halve that traffic); every
 // other group returns at once.  The second tile's X fragments double the
 // registers a slot holds, so two workgroups share a CU instead of four.
 // ---------------------------------------------------------------------------
 constexpr int kGroupedPairRows = 16;
-constexpr int kPairRing = 4, kPairWgsPerCu = 2;
-constexpr int kPairLds = kGroupedWaves * DecodeLds<2, kPairRing>::WAVE;
+constexpr int kPairBlocks = 4, kPairRing = 4, kPairWgsPerCu = 2;
+constexpr int kPairLds = kGroupedWaves * DecodeLds<kPairBlocks, kPairRing>::WAVE;
 
 template <int DT>
 __global__ __launch_bounds__(64 * kGroupedWaves, kPairWgsPerCu) void k_w4a16_grouped_pair(W4Grouped a) {
@@ -730,7 +735,7 @@ __global__ __launch_bounds__(64 * kGroupedWaves, kPairWgsPerCu) void k_w4a16_gro
   p.M = hi - lo;
   p.X = a.base.X + (int64_t)lo * a.base.ldx;
   p.Y = a.base.Y + (int64_t)lo * a.base.ldy;
-  decode_body<DT, 2, kGroupedWaves, kPairRing, 2>(p, blockIdx.x * 32, lds);
+  decode_body<DT, kPairBlocks, kGroupedWaves, kPairRing, 2>(p, blockIdx.x * kPairBlocks * 16, lds);
 }
 
 hipError_t launch_w4a16_grouped(const W4Grouped& a, hipStream_t stream) {
@@ -748,10 +753,11 @@ hipError_t launch_w4a16_grouped(const W4Grouped& a, hipStream_t stream) {
   if (!tiled) return hipGetLastError();
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const dim3 pgrid((a.base.N + kPairBlocks * 16 - 1) / (kPairBlocks * 16), a.count);
   if (a.base.dt == DT_BF16)
-    hipLaunchKernelGGL(k_w4a16_grouped_pair<DT_BF16>, grid, dim3(64 * kGroupedWaves), 0, stream, a);
+    hipLaunchKernelGGL(k_w4a16_grouped_pair<DT_BF16>, pgrid, dim3(64 * kGroupedWaves), 0, stream, a);
   else
-    hipLaunchKernelGGL(k_w4a16_grouped_pair<DT_F16>, grid, dim3(64 * kGroupedWaves), 0, stream, a);
+    hipLaunchKernelGGL(k_w4a16_grouped_pair<DT_F16>, pgrid, dim3(64 * kGroupedWaves), 0, stream, a);
   const hipError_t e2 = hipGetLastError();
   if (e2 != hipSuccess) return e2;
   int g1 = device_cu_count() * W4Cfg128::WGS_PER_CU / XCDS * XCDS;

@@ -177,7 +177,7 @@ def test_mixed_grouped_tiled_matches_the_plain_call(gmi):
 def test_mixed_grouped_pairs_match_the_decode_body(gmi, dtype, mode):
     # in a call that takes the tiled launch, groups of 17 to 32 rows run both 16-row tiles at once; they give the
     # bits of a small call (at most 256 rows: every group 16 rows at a time through the decode body)
-    N, K, group = 320, 1024, 128
+    N, K, group = 336, 1024, 128  # 64-row weight slices, the last one a single 16-row block
     off = [0, 24, 56, 60, 400]  # 24 and 32 rows (two tiles at once), 4 (decode), 340 (tiled)
     rows = 400
     r = np.random.default_rng(21)
