@@ -13,7 +13,6 @@
 //     The waves of a workgroup split K and reduce through LDS.
 //   * k_w4a16_tiled (M > 64) is the dense mainloop with the weight loader
 //     (W4Loader) dequantising into the LDS B tile.
-#include <climits>
 
 #include "gmi_device.hpp"
 #include "gmi_internal.hpp"
@@ -584,12 +583,12 @@ constexpr int kGroupedWaves = 4, kGroupedRing = 4;
 constexpr int kGroupedLds = kGroupedWaves * DecodeLds<2, kGroupedRing>::WAVE;
 
 template <int DT>
-__global__ __launch_bounds__(64 * kGroupedWaves, 4) void k_w4a16_grouped(W4Grouped a, int max_rows) {
+__global__ __launch_bounds__(64 * kGroupedWaves, 4) void k_w4a16_grouped(W4Grouped a) {
   __shared__ __attribute__((aligned(16))) char lds[kGroupedLds];
   const int g = blockIdx.y;
   const int lo = min(max(a.offsets[g], 0), a.rows);
   const int hi = min(max(a.offsets[g + 1], 0), a.rows);
-  if (hi <= lo || hi - lo > max_rows) return;  // empty, or taken by the tiled launch
+  if (hi <= lo) return;
   W4Launch p = a.base;
   p.w = a.base.w + g * a.w_stride;
   p.scales = a.base.scales + g * a.s_stride;
@@ -707,17 +706,18 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_w4a16_grouped
   }
 }
 
-// Groups of kGroupedPairRows + 1 .. kGroupedDecodeRows rows in a call that
-// takes the tiled launch: the decode body over both 16-row tiles of the
-// group at once (each k-block's weights unpacked once for the two tiles), so
-// the weight is streamed once instead of once per 16 rows, with the same
-// exact-integer arithmetic.  Workgroup (x, g) takes weight rows 64 x ..
+// Groups of 1 .. kGroupedDecodeRows rows in a call that takes the tiled
+// launch: the decode body over both 16-row tiles of the group at once (each
+// k-block's weights unpacked once for the two tiles; a group of at most 16
+// rows leaves the second tile empty), so the weight is streamed once instead
+// of once per 16 rows, with the same exact-integer arithmetic and the same
+// bits as the 16-row passes.  Workgroup (x, g) takes weight rows 64 x ..
 // 64 x + 63 of group g (every workgroup of a group reads all of its X, twice
 // the bytes of its weight slice, so wider slices halve that traffic); every
-// other group returns at once.  The second tile's X fragments double the
-// registers a slot holds, so two workgroups share a CU instead of four.
+// larger or empty group returns at once.  The second tile's X fragments
+// double the registers a slot holds, so two workgroups share a CU instead of
+// four.
 // ---------------------------------------------------------------------------
-constexpr int kGroupedPairRows = 16;
 constexpr int kPairBlocks = 4, kPairRing = 4, kPairWgsPerCu = 2;
 constexpr int kPairLds = kGroupedWaves * DecodeLds<kPairBlocks, kPairRing>::WAVE;
 
@@ -727,7 +727,7 @@ __global__ __launch_bounds__(64 * kGroupedWaves, kPairWgsPerCu) void k_w4a16_gro
   const int g = blockIdx.y;
   const int lo = min(max(a.offsets[g], 0), a.rows);
   const int hi = min(max(a.offsets[g + 1], 0), a.rows);
-  if (hi - lo <= kGroupedPairRows || hi - lo > kGroupedDecodeRows) return;
+  if (hi <= lo || hi - lo > kGroupedDecodeRows) return;
   W4Launch p = a.base;
   p.w = a.base.w + g * a.w_stride;
   p.scales = a.base.scales + g * a.s_stride;
@@ -739,27 +739,25 @@ __global__ __launch_bounds__(64 * kGroupedWaves, kPairWgsPerCu) void k_w4a16_gro
 }
 
 hipError_t launch_w4a16_grouped(const W4Grouped& a, hipStream_t stream) {
-  // when the group count fits the tiled launch's table and the call has more
-  // than kGroupedTiledMinRows rows, groups of more than kGroupedDecodeRows
-  // rows go to the tiled launch and those of more than kGroupedPairRows to
-  // the two-tile decode launch; otherwise the decode launch takes every group
-  const bool tiled = a.count <= kMaxOffsetGroupCount && a.rows > kGroupedTiledMinRows;
-  const int max_rows = tiled ? kGroupedPairRows : INT_MAX;
-  const dim3 grid((a.base.N + 31) / 32, a.count);
-  if (a.base.dt == DT_BF16)
-    hipLaunchKernelGGL(k_w4a16_grouped<DT_BF16>, grid, dim3(64 * kGroupedWaves), 0, stream, a, max_rows);
-  else
-    hipLaunchKernelGGL(k_w4a16_grouped<DT_F16>, grid, dim3(64 * kGroupedWaves), 0, stream, a, max_rows);
-  if (!tiled) return hipGetLastError();
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // a call of at most kGroupedTiledMinRows rows, or with more groups than the
+  // tiled launch's table holds, runs every group through the decode launch;
+  // otherwise groups of at most kGroupedDecodeRows rows take the two-tile
+  // launch and larger ones the tiled launch
+  if (a.count > kMaxOffsetGroupCount || a.rows <= kGroupedTiledMinRows) {
+    const dim3 grid((a.base.N + 31) / 32, a.count);
+    if (a.base.dt == DT_BF16)
+      hipLaunchKernelGGL(k_w4a16_grouped<DT_BF16>, grid, dim3(64 * kGroupedWaves), 0, stream, a);
+    else
+      hipLaunchKernelGGL(k_w4a16_grouped<DT_F16>, grid, dim3(64 * kGroupedWaves), 0, stream, a);
+    return hipGetLastError();
+  }
   const dim3 pgrid((a.base.N + kPairBlocks * 16 - 1) / (kPairBlocks * 16), a.count);
   if (a.base.dt == DT_BF16)
     hipLaunchKernelGGL(k_w4a16_grouped_pair<DT_BF16>, pgrid, dim3(64 * kGroupedWaves), 0, stream, a);
   else
     hipLaunchKernelGGL(k_w4a16_grouped_pair<DT_F16>, pgrid, dim3(64 * kGroupedWaves), 0, stream, a);
-  const hipError_t e2 = hipGetLastError();
-  if (e2 != hipSuccess) return e2;
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   int g1 = device_cu_count() * W4Cfg128::WGS_PER_CU / XCDS * XCDS;
   if (g1 < XCDS) g1 = XCDS;
   if (a.base.dt == DT_BF16)

@@ -247,12 +247,12 @@ gmi_status gmi_gemm_mixed(int32_t M, int32_t N, int32_t K, gmi_dtype x_dtype, co
  * Modes, types and layouts as for gmi_gemm_mixed.  By default a group runs
  * 16 rows at a time through the M <= 16 kernel body (exact integers
  * v(q) - v(z) into the matrix instruction, each group's scale on the fp32
- * partial sums).  When count <= 1024 and rows > 256, groups of 17 to 32 rows
- * run a second launch of the same body over both 16-row tiles at once (each
- * weight streamed once; the same bits), and larger groups a third launch over
+ * partial sums).  When count <= 1024 and rows > 256, groups of at most 32
+ * rows instead run the same body over both 16-row tiles at once (each weight
+ * streamed once; the same bits), and larger groups a second launch over
  * their 128 x 128 output tiles through the tiled mainloop (each weight
  * dequantised once to the activation type, as gmi_gemm_mixed does for
- * M > 64).  The launches are enqueued on `stream` and write disjoint rows.
+ * M > 64).  Both launches are enqueued on `stream` and write disjoint rows.
  * No workspace. */
 gmi_status gmi_gemm_mixed_grouped(int32_t count, const int32_t* offsets, int32_t rows, int32_t N, int32_t K,
                                   gmi_dtype x_dtype, const void* X, int64_t ldx, const uint8_t* w_prepacked,

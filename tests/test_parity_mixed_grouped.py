@@ -19,8 +19,7 @@ from helpers import SENTINEL, bytes_to_dev, check_close, dev, host_bits, to_dev
 
 pytestmark = pytest.mark.gpu
 
-PAIR_ROWS = 16  # groups above this many rows run the two-tile decode kernel ...
-TILED_ROWS = 32  # ... and above this many the tiled kernel ...
+TILED_ROWS = 32  # groups above this many rows run the tiled kernel, the others the two-tile decode kernel ...
 TILED_CALL_ROWS = 256  # ... in calls of more than this many rows
 
 
@@ -142,8 +141,8 @@ def test_mixed_grouped_groups_are_independent(gmi):
 @pytest.mark.parametrize("dtype,w_type,mode", [("f16", "uint4", "zero"), ("bf16", "int4", "zero"),
                                                ("bf16", "uint4", "scale"), ("f16", "int4", "direct")])
 def test_mixed_grouped_prefill_groups_tiled(gmi, dtype, w_type, mode):
-    # groups above 32 rows run the tiled launch (128 x 128 tiles, ragged in rows and in N), those of 17 to 32
-    # the two-tile decode launch, the others the decode launch, in one call; empty groups between them
+    # groups above 32 rows run the tiled launch (128 x 128 tiles, ragged in rows and in N), the others the
+    # two-tile decode launch, in one call; empty groups between them
     counts = np.array([0, 3, 32, 33, 0, 300, 129, 1, 513, 16, 17, 64])
     N, K, group = 320, 512, 128
     rows = int(counts.sum()) + 7
@@ -175,18 +174,19 @@ def test_mixed_grouped_tiled_matches_the_plain_call(gmi):
 
 @pytest.mark.parametrize("dtype,mode", [("bf16", "zero"), ("f16", "zero"), ("bf16", "scale")])
 def test_mixed_grouped_pairs_match_the_decode_body(gmi, dtype, mode):
-    # in a call that takes the tiled launch, groups of 17 to 32 rows run both 16-row tiles at once; they give the
-    # bits of a small call (at most 256 rows: every group 16 rows at a time through the decode body)
+    # in a call that takes the tiled launch, groups of at most 32 rows run both 16-row tiles at once (the second
+    # one empty for a group of at most 16 rows); they give the bits of a small call (at most 256 rows: every
+    # group 16 rows at a time through the decode body)
     N, K, group = 336, 1024, 128  # 64-row weight slices, the last one a single 16-row block
-    off = [0, 24, 56, 60, 400]  # 24 and 32 rows (two tiles at once), 4 (decode), 340 (tiled)
+    off = [0, 24, 56, 60, 400]  # 24, 32 and 4 rows (two tiles at once), 340 (tiled)
     rows = 400
     r = np.random.default_rng(21)
     X = gi.to_bits(r.standard_normal((rows, K)).astype(np.float32), dtype)
     W, S, Z = _experts(4, N, K, group, dtype, seed=22)
     got = _run(gmi, off, rows, X, W, S, Z, N, K, group, dtype, "uint4", mode)[0]
     _check_groups(got, off, rows, X, W, S, Z, N, K, group, dtype, "uint4", mode)
-    small = _run(gmi, off[:3], 56, X[:56], W[:2], S[:2], Z[:2], N, K, group, dtype, "uint4", mode)[0]
-    assert np.array_equal(small, got[:56])
+    small = _run(gmi, off[:4], 60, X[:60], W[:3], S[:3], Z[:3], N, K, group, dtype, "uint4", mode)[0]
+    assert np.array_equal(small, got[:60])
 
 
 def test_mixed_grouped_many_groups_all_decode(gmi):
