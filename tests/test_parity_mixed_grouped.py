@@ -190,10 +190,11 @@ def test_mixed_grouped_pairs_match_the_decode_body(gmi, dtype, mode):
 
 
 def test_mixed_grouped_many_groups_all_decode(gmi):
-    # more groups than the tiled launch's table holds: every group, large ones too, runs the decode launch
+    # more groups than the tiled launch's table holds, in a call of more than 256 rows: every group, large ones
+    # too, runs the decode launch
     G = 1100
     counts = np.zeros(G, np.int64)
-    counts[[0, 5, 700, 1099]] = [2, 90, 17, 70]
+    counts[[0, 5, 700, 1099]] = [2, 90, 17, 170]
     N, K, group = 64, 256, 128
     rows = int(counts.sum())
     r = np.random.default_rng(15)
@@ -202,6 +203,7 @@ def test_mixed_grouped_many_groups_all_decode(gmi):
     Z = r.integers(0, 256, (G, K // group, N // 2), dtype=np.uint8)
     S = gi.to_bits(r.uniform(0.001, 0.01, (G, K // group, N)).astype(np.float32), "f16")
     off = np.concatenate([[0], np.cumsum(counts)])
+    assert rows > TILED_CALL_ROWS
     got, *_ = _run(gmi, off, rows, X, W, S, Z, N, K, group, "f16", "uint4", "zero")
     _check_groups(got, off, rows, X, W, S, Z, N, K, group, "f16", "uint4", "zero")
 
