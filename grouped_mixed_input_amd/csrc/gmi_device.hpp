@@ -514,6 +514,16 @@ __device__ __forceinline__ u32x4 unpack8_minus_zero(uint32_t w, f16x2 zz, uint32
   return out;
 }
 
+// 128 + q for the 8 nibbles of w as exact bfloat16 values, in the order of
+// unpack8_minus_zero: with magic = 0x43004300 each half is 128 (exponent 7)
+// whose 7-bit mantissa holds q in its low 4 bits
+__device__ __forceinline__ u32x4 unpack8_biased_bf16(uint32_t w, uint32_t magic) {
+  u32x4 out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = ((w >> (4 * i)) & 0x000F000Fu) | magic;
+  return out;
+}
+
 __device__ __forceinline__ u32x4 dequant8(uint32_t w, f16x2 zz, f16x2 ss) {
   u32x4 out;
 #pragma unroll
@@ -531,23 +541,6 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t w, f16x2 zz, f16x2 ss) {
 // v_cvt_f32_ubyte.  The bytes of w & 0x0F0F0F0F are elements 0, 4, 1, 5 of
 // the word, those of (w >> 4) & 0x0F0F0F0F elements 2, 6, 3, 7.
 __device__ __forceinline__ float ubyte_f32(uint32_t v, int i) { return (float)((v >> (8 * i)) & 0xFFu); }
-
-// upper halves of two fp32 values: their bfloat16 patterns when exact
-__device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
-  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo), 0x07060302u);
-}
-
-// q - z for the 8 nibbles of w as exact bfloat16 integers (|q - z| <= 15
-// needs 4 significant bits; fp32 subtraction is exact, truncation too)
-__device__ __forceinline__ u32x4 unpack8_minus_zero_bf16(uint32_t w, float zf) {
-  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-  u32x4 out;
-  out[0] = pack_hi16(ubyte_f32(lo, 0) - zf, ubyte_f32(lo, 2) - zf);
-  out[1] = pack_hi16(ubyte_f32(hi, 0) - zf, ubyte_f32(hi, 2) - zf);
-  out[2] = pack_hi16(ubyte_f32(lo, 1) - zf, ubyte_f32(lo, 3) - zf);
-  out[3] = pack_hi16(ubyte_f32(hi, 1) - zf, ubyte_f32(hi, 3) - zf);
-  return out;
-}
 
 // RN_bf16((q - z) s) for the 8 nibbles of w: q s - z s is formed exactly by
 // one fma (a 4-bit integer times an 8-bit significand fits fp32; nzs = -z s

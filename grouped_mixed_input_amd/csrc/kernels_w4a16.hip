@@ -193,7 +193,11 @@ __global__ __launch_bounds__(64 * KW) void k_w4a16_skinny(W4Launch a) {
 // transform_A_kblock's conversion without the scale) into a fresh fp32
 // partial sum, and each output row's scale multiplies that partial sum:
 // sum_k (q - z) s x = sum over groups of s * sum_k (q - z) x, with the scale
-// applied in fp32 instead of rounding every weight to fp16 first.  All loads of a round are issued in
+// applied in fp32 instead of rounding every weight to fp16 first.  With bf16
+// activations the MFMA takes 128 + q (bf16 0x4300 | q, exact) and
+// (128 + z) sum_k x, the k-block's activation sum from one more MFMA against
+// ones, comes off each output row's partial sum in fp32: a third of the
+// unpacking work of forming q - z in bf16.  All loads of a round are issued in
 // straight-line code before their first use, slot by slot (weight blocks,
 // then X fragments), so the weight stream starts at once and each wait --
 // ours or the compiler's for the X registers -- leaves the younger slots in
@@ -237,7 +241,9 @@ __device__ __forceinline__ void decode_body(const W4Launch& a, int n_base, char*
   const rsrc_t rz = make_rsrc(a.zeros, a.z_bytes);
   const uint32_t sor2 = a.sor * 0x00010001u;
   const uint32_t r = lane & 15, h = lane >> 4;
-  uint32_t magic = 0x64006400u;  // fp16 pair (1024, 1024): 1024 + q for a nibble q in the low mantissa bits
+  // fp16 pair (1024, 1024): 1024 + q for a nibble q in the low mantissa
+  // bits; bf16 pair (128, 128): 128 + q
+  uint32_t magic = DT == DT_F16 ? 0x64006400u : 0x43004300u;
   asm volatile("" : "+v"(magic));
 
   f32x4 acc[NB][MT];
@@ -285,18 +291,30 @@ __device__ __forceinline__ void decode_body(const W4Launch& a, int n_base, char*
       __builtin_amdgcn_sched_barrier(0);
       wait_vm_le_n<(R - 1) * (NB + 4 * MT)>((R - 1 - s) * (NB + 4 * MT));
       if (base + s < kb1) {
+        // bf16: the k-block's activation sum of each token, by the matrix
+        // instruction against a fragment of ones (every output row the same)
+        f32x4 sx[MT];
+        if constexpr (DT == DT_BF16) {
+          const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            sx[mt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sx[mt] = mfma16<DT>(ones, x[s][mt][j], sx[mt]);
+          }
+        }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           // the MFMA takes the exact integers q - z of weight row `row`; the
           // group scale of each output row multiplies the fp32 partial sum
           const u32x4 wq = *(const u32x4*)(wring + s * L::WSLOT + nb * 1024 + lane * 16) ^ a.wxor;
-          const int row = nb * 16 + r;
-          const uint32_t zbits =
-              ((*(const uint8_t*)(szb + 1024 + s * L::ZROW + row / 2) >> ((row & 1) * 4)) & 15u) ^ a.zxor;
           f32x4 part[MT];
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) part[mt] = f32x4{0, 0, 0, 0};
           if constexpr (DT == DT_F16) {
+            const int row = nb * 16 + r;
+            const uint32_t zbits =
+                ((*(const uint8_t*)(szb + 1024 + s * L::ZROW + row / 2) >> ((row & 1) * 4)) & 15u) ^ a.zxor;
             const f16x2 zz = zero_pair(zbits);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -305,12 +323,21 @@ __device__ __forceinline__ void decode_body(const W4Launch& a, int n_base, char*
               for (int mt = 0; mt < MT; ++mt) part[mt] = mfma16<DT>(wf, x[s][mt][j], part[mt]);
             }
           } else {
-            const float zf = (float)zbits;
+            // sum_k (q - z) x = sum_k (128 + q) x - (128 + z) sum_k x: the
+            // biased integers go in exactly, the bias comes off each output
+            // row (rows nb * 16 + 4 h + {0..3} of this lane) in fp32
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const u32x4 wf = unpack8_minus_zero_bf16(wq[j], zf);
+              const u32x4 wf = unpack8_biased_bf16(wq[j], magic);
 #pragma unroll
               for (int mt = 0; mt < MT; ++mt) part[mt] = mfma16<DT>(wf, x[s][mt][j], part[mt]);
+            }
+            const uint32_t z4 = *(const uint16_t*)(szb + 1024 + s * L::ZROW + (nb * 16 + 4 * h) / 2);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float zb = (float)(128u + (((z4 >> (4 * i)) & 15u) ^ a.zxor));
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt) part[mt][i] = __builtin_fmaf(-zb, sx[mt][i], part[mt][i]);
             }
           }
           // output rows of this lane: nb * 16 + 4 h + {0..3}

@@ -216,11 +216,12 @@ typedef enum { GMI_W4_UINT4 = 0, GMI_W4_INT4 = 1 } gmi_w4_type;
  *                (the page's fp16 and bf16 activation / scale types).
  *   group_size   as for gmi_gemm_w4a16; ignored when scales == NULL.
  *   other arguments, layouts, workspace and errors as for gmi_gemm_w4a16.
- * Numerics: for M <= 16 the matrix instruction takes the exact integers
- * v(q) - v(z) in the activation type and the scale multiplies each group's
- * fp32 partial sum; otherwise every weight is first rounded to the
- * activation type, RN((v(q) - v(z)) * s).  fp32 accumulation; Y is rounded to
- * nearest even. */
+ * Numerics: for M <= 16 the matrix instruction takes exact integer weights
+ * and the scale multiplies each group's fp32 partial sum: v(q) - v(z) for
+ * fp16; for bf16 the offset-binary nibble plus 128, with (128 + zero point)
+ * times the group's activation sum taken off that partial sum.  Otherwise
+ * every weight is first rounded to the activation type,
+ * RN((v(q) - v(z)) * s).  fp32 accumulation; Y is rounded to nearest even. */
 gmi_status gmi_gemm_mixed(int32_t M, int32_t N, int32_t K, gmi_dtype x_dtype, const void* X, int64_t ldx,
                           const uint8_t* w_prepacked, gmi_w4_type w_type, const void* scales, const uint8_t* zeros,
                           int32_t group_size, void* Y, int64_t ldy, void* workspace, size_t workspace_bytes,
@@ -245,9 +246,9 @@ gmi_status gmi_gemm_mixed(int32_t M, int32_t N, int32_t K, gmi_dtype x_dtype, co
  *            (K/group)*N scales, (K/group)*N/2 zero bytes) and keeping every
  *            group's data 16-byte aligned; ignored for a NULL array.
  * Modes, types and layouts as for gmi_gemm_mixed.  By default a group runs
- * 16 rows at a time through the M <= 16 kernel body (exact integers
- * v(q) - v(z) into the matrix instruction, each group's scale on the fp32
- * partial sums).  When count <= 1024 and rows > 256, groups of at most 32
+ * 16 rows at a time through the M <= 16 kernel body (exact integer weights
+ * into the matrix instruction, each group's scale on the fp32 partial sums,
+ * as gmi_gemm_mixed does for M <= 16).  When count <= 1024 and rows > 256, groups of at most 32
  * rows instead run the same body over both 16-row tiles at once (each weight
  * streamed once; the same bits), and larger groups a second launch over
  * their 128 x 128 output tiles through the tiled mainloop (each weight
