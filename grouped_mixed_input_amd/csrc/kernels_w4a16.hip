@@ -175,7 +175,8 @@ __global__ __launch_bounds__(64 * KW) void k_w4a16_skinny(W4Launch a) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode kernel (M <= 16): the weight stream is the whole cost (N K / 2 bytes
+// Decode kernel (M <= 16, or M <= 32 as two 16-row tiles): the weight
+// stream is the whole cost (N K / 2 bytes
 // against 2 M (N + K) for X and Y), so it is put in flight as early and as
 // deep as the LDS allows.  Workgroup = KW waves over NB 16-row weight blocks;
 // wave w owns a contiguous range of 128-wide k-blocks, taken R at a time
@@ -372,10 +373,10 @@ __device__ __forceinline__ void decode_body(const W4Launch& a, int n_base, char*
   }
 }
 
-template <int DT, int NB, int KW, int R>
+template <int DT, int NB, int KW, int R, int MT = 1>
 __global__ __launch_bounds__(64 * KW) void k_w4a16_decode(W4Launch a) {
   __shared__ __attribute__((aligned(16))) char lds[KW * DecodeLds<NB, R>::WAVE];
-  decode_body<DT, NB, KW, R>(a, blockIdx.x * NB * 16, lds);
+  decode_body<DT, NB, KW, R, MT>(a, blockIdx.x * NB * 16, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -561,13 +562,18 @@ static hipError_t launch_w4a16_dt(const W4Launch& a, hipStream_t stream) {
                        stream, a);
     return hipGetLastError();
   }
+  if (a.M <= 32) {
+    // both 16-row tiles through the decode body (exact integer weights);
+    // the second tile's X registers leave room for a four-slot ring
+    constexpr int NB = 2, KW = 8, R = 4;
+    hipLaunchKernelGGL((k_w4a16_decode<DT, NB, KW, R, 2>), dim3((a.N + NB * 16 - 1) / (NB * 16)), dim3(64 * KW), 0,
+                       stream, a);
+    return hipGetLastError();
+  }
   if (a.M <= 64) {
     constexpr int NB = 2, KW = 8;
     const dim3 grid((a.N + NB * 16 - 1) / (NB * 16)), block(64 * KW);
-    if (a.M <= 32)
-      hipLaunchKernelGGL((k_w4a16_skinny<DT, NB, KW, 2>), grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL((k_w4a16_skinny<DT, NB, KW, 4>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((k_w4a16_skinny<DT, NB, KW, 4>), grid, block, 0, stream, a);
     return hipGetLastError();
   }
   const int cus = device_cu_count();
