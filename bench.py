@@ -34,6 +34,8 @@ PEAK_HBM = 8000.0  # GB/s
 # kernel named here only.
 HEADLINE_KERNEL = "k_gemm_ptr_array<TileCfg<256,256,4,2,64,2,5>, bf16, false>"
 HEADLINE_TRAFFIC_BYTES = 101441928
+HEADLINE_PROFILE = "k_gemm_ptr_array_256x256_bf16_ptr_array_L16_1024.md"
+HEADLINE_PMC_CLOCK_MHZ = None  # GRBM_GUI_ACTIVE cycles / kernel ns of the headline kernel, from that profile
 MALL_BYTES = 256 << 20
 ROTATE_TARGET = 512 << 20
 METRIC = "TFLOP/s and % of MFMA peak: grouped bf16 GEMM, w4a16 GEMM, conv fprop"
@@ -47,19 +49,35 @@ def copies_for(ws_bytes: int) -> int:
     return 1 if ws_bytes >= ROTATE_TARGET else int(math.ceil(ROTATE_TARGET / ws_bytes))
 
 
-def time_launches(torch, fn, n_copies, warmup, iters):
-    """Average ms per launch over `iters` back-to-back launches (cycling over
-    the rotating copies), HIP events on the launch stream."""
-    for i in range(warmup):
+def time_launches(torch, fn, n_copies, warmup, group=1, min_window_ms=2.0, windows=7):
+    """Per-launch time of fn (cycling over the rotating copies), HIP events on the launch stream.
+
+    After `warmup` untimed launches and one untimed calibration window of `group` launches, the loop times
+    `windows` windows; each is a whole number of `group`-launch runs, enough to last at least min_window_ms.
+    Returns the median per-launch time over the windows (ms) with the spread and the window size."""
+    i = 0
+    for _ in range(warmup):
         fn(i % n_copies)
+        i += 1
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    for i in range(iters):
-        fn(i % n_copies)
-    e.record()
-    torch.cuda.synchronize()
-    return s.elapsed_time(e) / iters
+
+    def window(n):
+        nonlocal i
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(n):
+            fn(i % n_copies)
+            i += 1
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e)
+
+    reps = max(1, int(math.ceil(min_window_ms / max(window(group), 1e-3))))
+    n = group * reps
+    per = sorted(window(n) / n for _ in range(windows))
+    return {"ms": per[len(per) // 2], "min_ms": per[0], "max_ms": per[-1], "windows": windows,
+            "launches_per_window": n}
 
 
 def copy_ref(torch, dev, args):
@@ -73,17 +91,97 @@ def copy_ref(torch, dev, args):
         del src, dst
 
 
-def roof(flops, bytes_, ms, peak=PEAK_MFMA_16):
-    t = ms * 1e-3
-    tf = flops / t / 1e12
-    gbs = bytes_ / t / 1e9
-    return dict(us=round(ms * 1e3, 3), tflops=round(tf, 2), frac_mfma=round(tf / peak, 4),
-                gbps=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM, 4),
-                roofline_frac=round(max(flops / (peak * 1e12), bytes_ / (PEAK_HBM * 1e9)) / t, 4))
+def roof(flops, bytes_, t, peak=PEAK_MFMA_16, bound=None):
+    """Rates and roofline fractions of one workload from its time_launches record; `bound` is the roof
+    that is closer (the larger of the two fractions) unless given ("launch" for latency-bound calls)."""
+    ms = t["ms"]
+    sec = ms * 1e-3
+    tf = flops / sec / 1e12
+    gbs = bytes_ / sec / 1e9
+    f_mfma, f_hbm = tf / peak, gbs / PEAK_HBM
+    return dict(us=round(ms * 1e3, 3), us_min=round(t["min_ms"] * 1e3, 3), us_max=round(t["max_ms"] * 1e3, 3),
+                launches_per_window=t["launches_per_window"], tflops=round(tf, 2), frac_mfma=round(f_mfma, 4),
+                gbps=round(gbs, 1), frac_hbm=round(f_hbm, 4), roofline_frac=round(max(f_mfma, f_hbm), 4),
+                bound=bound or ("mfma" if f_mfma >= f_hbm else "hbm"))
 
 
 def t16(torch, bits, dtype, dev):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(dtype).to(dev)
+
+
+def shader_clock(torch, fn, n_copies, seconds=1.5):
+    """Shader clock under the headline load, for context next to the fixed 2.4 GHz of the peak: the headline
+    launches run back to back for about `seconds` while `amd-smi metric -c` samples the graphics clock from
+    another process (median of the samples, MHz).  The clock that rocprofv3 derives for the same kernel
+    (GRBM_GUI_ACTIVE cycles over the kernel time) is recorded beside it."""
+    import subprocess
+    import threading
+
+    samples, errors = [], []
+
+    def gfx_mhz(obj):
+        # every "gfx_<i>" entry's current clock, in MHz, wherever it sits in the JSON
+        out = []
+        if isinstance(obj, dict):
+            for k, v in obj.items():
+                if str(k).lower().startswith("gfx") and isinstance(v, dict) and "clk" in v:
+                    c = v["clk"]
+                    c = c.get("value") if isinstance(c, dict) else c
+                    try:
+                        out.append(float(str(c).split()[0]))
+                    except ValueError:
+                        pass
+                else:
+                    out += gfx_mhz(v)
+        elif isinstance(obj, list):
+            for v in obj:
+                out += gfx_mhz(v)
+        return out
+
+    stop = threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "--json"], capture_output=True, text=True,
+                                   timeout=10)
+                v = gfx_mhz(json.loads(r.stdout)) if r.returncode == 0 else []
+                if v:
+                    samples.append(max(v))
+                else:
+                    errors.append((r.stderr or r.stdout).strip()[:200])
+            except Exception as exc:  # a missing or failing tool leaves the clock unreported
+                errors.append(repr(exc)[:200])
+            stop.wait(0.2)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t0, i = time.perf_counter(), 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(50):
+            fn(i % n_copies)
+            i += 1
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=15)
+    pmc = {"mhz": HEADLINE_PMC_CLOCK_MHZ, "source": "rocprofv3 GRBM_GUI_ACTIVE / kernel duration of the headline "
+                                                    "kernel, profiles/" + HEADLINE_PROFILE}
+    if not samples:
+        return {"amd_smi_mhz": None, "amd_smi_error": errors[-1] if errors else "no sample", "pmc": pmc}
+    samples.sort()
+    return {"amd_smi_mhz": samples[len(samples) // 2], "amd_smi_samples": len(samples), "pmc": pmc}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
 
 
 # --------------------------------------------------------------------------
@@ -119,7 +217,8 @@ def cpu_baseline(gi, A, B, budget_s=12.0):
         if time.perf_counter() - t0 > budget_s:
             break
     sec = time.perf_counter() - t0
-    return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "cpu": cpu_model(),
+            "logical_cpus": os.cpu_count(), "kind": "oracle",
             "sample": f"{done} batch products of 1024^3 bf16 inputs in fp64 (cycling over the 16 batches), "
                       f"{sec:.1f} s"}
 
@@ -138,15 +237,15 @@ def bench_moe(torch, gmi, gi, dev, out):
     wsb = torch.empty(gmi.workspace_bytes(128), dtype=torch.uint8, device=dev)
     fl = 2.0 * counts.sum() * N * K
     by = 2 * (counts.sum() * K + int((counts > 0).sum()) * N * K + counts.sum() * N)
-    ms = time_launches(torch, lambda i: gmi.gemm_grouped_raw(table, 128, gmi.GMI_BF16, 1.0, 0.0, wsb), 1, 3, 10)
-    out["moe_grouped_bf16"] = dict(roof(fl, by, ms), bound="hbm")
+    tm = time_launches(torch, lambda i: gmi.gemm_grouped_raw(table, 128, gmi.GMI_BF16, 1.0, 0.0, wsb), 1, 3)
+    out["moe_grouped_bf16"] = roof(fl, by, tm)
     # the same layer with the group sizes held on the device (row offsets; a
     # table-building launch, then the GEMM): no host round trip
     B3 = torch.stack(Bw)
     del Bw
     offs = torch.tensor(off.astype(np.int32), device=dev)
-    ms = time_launches(torch, lambda i: gmi.gemm_grouped_offsets(offs, A, B3, D, workspace=wsb), 1, 3, 10)
-    out["moe_grouped_offsets_bf16"] = dict(roof(fl, by, ms), bound="hbm")
+    tm = time_launches(torch, lambda i: gmi.gemm_grouped_offsets(offs, A, B3, D, workspace=wsb), 1, 3)
+    out["moe_grouped_offsets_bf16"] = roof(fl, by, tm)
     del B3, A, D
     torch.cuda.empty_cache()
     log("bench: MoE grouped done")
@@ -175,8 +274,8 @@ def bench_moe_w4(torch, gmi, gi, dev, out):
         w, s, z = sets[i]
         gmi.gemm_mixed_grouped(offs, Xm, w, s, z, 128, N, w_type="int4", Y=Ym)
 
-    ms = time_launches(torch, fn, R, 5, max(50, 2 * R))
-    out["moe_w4_decode_bf16"] = dict(roof(2.0 * int(w4_counts.sum()) * N * K, by, ms), bound="hbm", experts_live=live)
+    tm = time_launches(torch, fn, R, 5)
+    out["moe_w4_decode_bf16"] = dict(roof(2.0 * int(w4_counts.sum()) * N * K, by, tm), experts_live=live)
     del Xm, Ym
     # 4c. the same experts on a prefill batch: 16384 rows routed like the bf16 MoE layer (groups above 32 rows
     # take the tiled launch, the rest the decode launch)
@@ -191,8 +290,8 @@ def bench_moe_w4(torch, gmi, gi, dev, out):
         w, s, z = sets[i]
         gmi.gemm_mixed_grouped(p_offs, Xp, w, s, z, 128, N, w_type="int4", Y=Yp)
 
-    ms = time_launches(torch, fnp, R, 3, max(10, 2 * R))
-    out["moe_w4_prefill_bf16"] = dict(roof(2.0 * 16384 * N * K, p_by, ms), bound="mfma", experts_live=p_live)
+    tm = time_launches(torch, fnp, R, 3)
+    out["moe_w4_prefill_bf16"] = dict(roof(2.0 * 16384 * N * K, p_by, tm), experts_live=p_live)
     del sets, wpp, Sx, Zx, Xp, Yp
     torch.cuda.empty_cache()
     log("bench: MoE W4 decode and prefill done")
@@ -207,26 +306,25 @@ def bench_conv(torch, gmi, gi, dev, out):
     R = copies_for(ws)
     sets = [(xd.clone(), wd.clone(), torch.empty((32, 56, 56, 256), dtype=torch.bfloat16, device=dev))
             for _ in range(R)]
-    ms = time_launches(torch, lambda i: gmi.conv2d_fprop(sets[i][0], sets[i][1], pad=(1, 1), y=sets[i][2]), R, 5,
-                       max(20, 2 * R))
-    out["conv_fprop_bf16"] = dict(roof(2.0 * 100352 * 256 * 2304, ws, ms), bound="mfma")
+    tm = time_launches(torch, lambda i: gmi.conv2d_fprop(sets[i][0], sets[i][1], pad=(1, 1), y=sets[i][2]), R, 5)
+    out["conv_fprop_bf16"] = roof(2.0 * 100352 * 256 * 2304, ws, tm)
     # the same layer with its bias and ReLU fused into the epilogue
     bd = t16(torch, gi.conv_bias(), torch.bfloat16, dev)
-    ms = time_launches(torch, lambda i: gmi.conv2d_fprop(sets[i][0], sets[i][1], pad=(1, 1), y=sets[i][2], bias=bd,
-                                                         act="relu"), R, 5, max(20, 2 * R))
-    out["conv_fprop_bias_relu_bf16"] = dict(roof(2.0 * 100352 * 256 * 2304, ws + 512, ms), bound="mfma")
+    tm = time_launches(torch, lambda i: gmi.conv2d_fprop(sets[i][0], sets[i][1], pad=(1, 1), y=sets[i][2], bias=bd,
+                                                         act="relu"), R, 5)
+    out["conv_fprop_bias_relu_bf16"] = roof(2.0 * 100352 * 256 * 2304, ws + 512, tm)
     # the data gradient of the same layer (dy of the forward output's shape; the filter rearranged each call)
     wsd = torch.empty(gmi.lib().gmi_conv2d_dgrad_workspace_bytes(256, 256, 3, 3), dtype=torch.uint8, device=dev)
-    ms = time_launches(torch, lambda i: gmi.conv2d_dgrad(sets[i][2], sets[i][1], 56, 56, pad=(1, 1), dx=sets[i][0],
-                                                         workspace=wsd), R, 5, max(20, 2 * R))
-    out["conv_dgrad_bf16"] = dict(roof(2.0 * 100352 * 256 * 2304, ws, ms), bound="mfma")
+    tm = time_launches(torch, lambda i: gmi.conv2d_dgrad(sets[i][2], sets[i][1], 56, 56, pad=(1, 1), dx=sets[i][0],
+                                                         workspace=wsd), R, 5)
+    out["conv_dgrad_bf16"] = roof(2.0 * 100352 * 256 * 2304, ws, tm)
     # and its weight gradient (x and dy of the same shapes; transposes and the split sum included)
     dws = torch.empty((256, 3, 3, 256), dtype=torch.bfloat16, device=dev)
     wsw = torch.empty(gmi.conv2d_wgrad_workspace_bytes((32, 56, 56, 256), (32, 56, 56, 256), 3, 3, (1, 1)),
                       dtype=torch.uint8, device=dev)
-    ms = time_launches(torch, lambda i: gmi.conv2d_wgrad(sets[i][0], sets[i][2], 3, 3, pad=(1, 1), dw=dws,
-                                                         workspace=wsw), R, 3, max(10, 2 * R))
-    out["conv_wgrad_bf16"] = dict(roof(2.0 * 100352 * 256 * 2304, ws, ms), bound="mfma")
+    tm = time_launches(torch, lambda i: gmi.conv2d_wgrad(sets[i][0], sets[i][2], 3, 3, pad=(1, 1), dw=dws,
+                                                         workspace=wsw), R, 3)
+    out["conv_wgrad_bf16"] = roof(2.0 * 100352 * 256 * 2304, ws, tm)
     log("bench: conv done")
     del sets
     torch.cuda.empty_cache()
@@ -244,8 +342,8 @@ def bench_workloads(torch, gmi, gi, dev, args):
     wsb = torch.empty(gmi.workspace_bytes(4), dtype=torch.uint8, device=dev)
     fl = sum(2.0 * p["M"] * p["N"] * p["K"] for p in probs)
     by = sum(2 * (p["M"] * p["K"] + p["N"] * p["K"] + 2 * p["M"] * p["N"]) for p in probs)
-    ms = time_launches(torch, lambda i: gmi.gemm_grouped_raw(table, 4, gmi.GMI_F16, 1.0, 0.5, wsb), 1, 20, 500)
-    out["grouped_f16_4groups"] = dict(roof(fl, by, ms), bound="launch")
+    tm = time_launches(torch, lambda i: gmi.gemm_grouped_raw(table, 4, gmi.GMI_F16, 1.0, 0.5, wsb), 1, 20)
+    out["grouped_f16_4groups"] = roof(fl, by, tm, bound="launch")
     log("bench: grouped fp16 done")
 
     counts, off = bench_moe(torch, gmi, gi, dev, out)
@@ -269,9 +367,8 @@ def bench_workloads(torch, gmi, gi, dev, args):
             pp, s, z, x, y = sets[i]
             gmi.gemm_w4a16(x, pp, s, z, 128, 8192, Y=y, workspace=wsp)
 
-        ms = time_launches(torch, fn, R, 5, max(20, R * 2))
-        bound = "hbm" if M <= 64 else "mfma"
-        out[f"w4a16_M{M}"] = dict(roof(2.0 * M * 8192 * 8192, ws, ms), bound=bound)
+        tm = time_launches(torch, fn, R, 5)
+        out[f"w4a16_M{M}"] = roof(2.0 * M * 8192 * 8192, ws, tm)
         del sets
     del rx
     # the same shapes with bf16 activations and scales, int4 weights with zero points
@@ -288,8 +385,8 @@ def bench_workloads(torch, gmi, gi, dev, args):
             pp, s, z, x, y = sets[i]
             gmi.gemm_mixed(x, pp, s, z, 128, 8192, w_type="int4", Y=y, workspace=wsp)
 
-        ms = time_launches(torch, fn, R, 5, max(20, R * 2))
-        out[f"mixed_bf16_int4_M{M}"] = dict(roof(2.0 * M * 8192 * 8192, ws, ms), bound="hbm" if M <= 64 else "mfma")
+        tm = time_launches(torch, fn, R, 5)
+        out[f"mixed_bf16_int4_M{M}"] = roof(2.0 * M * 8192 * 8192, ws, tm)
         del sets
     log("bench: W4A16 done")
 
@@ -299,7 +396,7 @@ def bench_workloads(torch, gmi, gi, dev, args):
 
     # 6. fp8 (E4M3) inputs, bf16 results: the pointer-array headline shape and the MoE layer
     A8, B8 = gi.ptr_array_f8(L=16)
-    ws = 16 * (2 * 1024 * 1024 + 2 * 1024 * 1024 * 2)
+    ws = 16 * (1024 * 1024 + 1024 * 1024 + 1024 * 1024 * 2)  # A, B fp8 read once; D bf16 written once
     R = copies_for(ws)
     f8 = torch.float8_e4m3fn
     sets = []
@@ -308,10 +405,10 @@ def bench_workloads(torch, gmi, gi, dev, args):
         Bd = [torch.from_numpy(b).view(f8).to(dev) for b in B8]
         Dd = [torch.empty((1024, 1024), dtype=torch.bfloat16, device=dev) for _ in range(16)]
         sets.append([gmi.pointer_array(x, dev) for x in (Ad, Bd, Dd)] + [Ad, Bd, Dd])
-    ms = time_launches(torch, lambda i: gmi.gemm_ptr_array(16, 1024, 1024, 1024, sets[i][0], 1024, sets[i][1], 1024,
+    tm = time_launches(torch, lambda i: gmi.gemm_ptr_array(16, 1024, 1024, 1024, sets[i][0], 1024, sets[i][1], 1024,
                                                            None, 1024, sets[i][2], 1024, gmi.GMI_F8E4M3, 1.0, 0.0),
-                       R, 10, max(50, 2 * R))
-    out["ptr_array_fp8"] = dict(roof(2.0 * 16 * 1024 ** 3, ws, ms, PEAK_MFMA_8), bound="hbm")
+                       R, 10)
+    out["ptr_array_fp8"] = roof(2.0 * 16 * 1024 ** 3, ws, tm, PEAK_MFMA_8)
     del sets, A8, B8
     N, K = 2048, 4096
     A = torch.from_numpy(gi.moe_activations_f8()).view(f8).to(dev)
@@ -322,8 +419,8 @@ def bench_workloads(torch, gmi, gi, dev, args):
     wsb = torch.empty(gmi.workspace_bytes(128), dtype=torch.uint8, device=dev)
     fl = 2.0 * counts.sum() * N * K
     by = counts.sum() * K + int((counts > 0).sum()) * N * K + 2 * counts.sum() * N
-    ms = time_launches(torch, lambda i: gmi.gemm_grouped_raw(table, 128, gmi.GMI_F8E4M3, 1.0, 0.0, wsb), 1, 3, 10)
-    out["moe_grouped_fp8"] = dict(roof(fl, by, ms, PEAK_MFMA_8), bound="hbm")
+    tm = time_launches(torch, lambda i: gmi.gemm_grouped_raw(table, 128, gmi.GMI_F8E4M3, 1.0, 0.0, wsb), 1, 3)
+    out["moe_grouped_fp8"] = roof(fl, by, tm, PEAK_MFMA_8)
     del Bw, A, D
     torch.cuda.empty_cache()
     log("bench: fp8 done")
@@ -344,11 +441,10 @@ def decode_only(torch, gmi, gi, dev, args):
             for _ in range(R)]
     wsp = torch.empty(gmi.w4a16_workspace_bytes(M, N, K), dtype=torch.uint8, device=dev)
     fn = lambda i: gmi.gemm_w4a16(sets[i][3], sets[i][0], sets[i][1], sets[i][2], g, N, Y=sets[i][4], workspace=wsp)
-    ms = time_launches(torch, fn, R, args.warmup, args.steps)
+    tm = time_launches(torch, fn, R, args.warmup, group=args.steps)
     copy_ref(torch, dev, args)
     line = dict(workload=f"w4a16 decode M={M} N={N} K={K} g={g}", steps=args.steps, warmup=args.warmup,
-                us=round(ms * 1e3, 3), algorithmic_bytes=ws, gbps=round(ws / (ms * 1e-3) / 1e9, 1),
-                frac_hbm=round(ws / (ms * 1e-3) / (PEAK_HBM * 1e9), 4), copies=R)
+                algorithmic_bytes=ws, copies=R, **roof(2.0 * M * N * K, ws, tm))
     print(json.dumps(line), flush=True)
 
 
@@ -397,18 +493,15 @@ def main():
     log("bench: building inputs")
     fn, R, flops, ws, keep = setup_ptr_array(torch, gmi, gi, dev)
     log(f"bench: headline rotates {R} copies of {ws / 2**20:.0f} MiB")
-    for i in range(args.warmup):
-        fn(i % R)
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(args.steps):
-        fn(i % R)
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    # W untimed warm-up steps, then windows of whole K-step runs (each window at least 2 ms, bracketed by
+    # synchronizations); the step time is the median over the windows
+    tm = time_launches(torch, fn, R, args.warmup, group=args.steps)
+    ms = tm["ms"]
     tflops = flops / (ms * 1e-3) / 1e12
-    log(f"bench: headline {ms * 1e3:.1f} us/step, {tflops:.1f} TFLOP/s")
+    log(f"bench: headline {ms * 1e3:.1f} us/step (median of {tm['windows']} windows of {tm['launches_per_window']} "
+        f"steps; {tm['min_ms'] * 1e3:.1f} to {tm['max_ms'] * 1e3:.1f}), {tflops:.1f} TFLOP/s")
+    clock = shader_clock(torch, fn, R)
+    log(f"bench: shader clock under the headline load {clock}")
 
     result = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -417,10 +510,13 @@ def main():
         "config": {"workload": "pointer-array bf16 GEMM, L=16 separately allocated M=N=K=1024 problems, "
                                "beta=0, fp32 accumulate, bf16 D", "L": 16, "M": 1024, "N": 1024, "K": 1024,
                    "cache": f"cold: {R} rotating copies of the {ws / 2**20:.0f} MiB working set"},
+        "timing": {"windows": tm["windows"], "steps_per_window": tm["launches_per_window"],
+                   "us_per_step_median": round(ms * 1e3, 3), "us_per_step_min": round(tm["min_ms"] * 1e3, 3),
+                   "us_per_step_max": round(tm["max_ms"] * 1e3, 3)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_16, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_MFMA_16, 4), "traffic": HEADLINE_TRAFFIC_BYTES,
                      "traffic_unit": "HBM bytes per launch", "algorithmic_bytes": 3 * 16 * 1024 * 1024 * 2,
-                     "kernel": HEADLINE_KERNEL},
+                     "kernel": HEADLINE_KERNEL, "clock": clock},
     }
     copy_ref(torch, dev, args)
     if not args.headline_only:

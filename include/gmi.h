@@ -310,25 +310,6 @@ gmi_status gmi_conv2d_fprop_implicit_fused(int32_t N, int32_t H, int32_t W, int3
  * non-positive size. */
 size_t gmi_conv2d_dgrad_workspace_bytes(int32_t C, int32_t K, int32_t R, int32_t S);
 
-/* Implicit-GEMM conv2d data gradient (the page's dgrad operator), the
- * adjoint of gmi_conv2d_fprop_implicit in its activation:
- *   dx[n][h][w][c] = alpha * sum over (p, q, k, r, s) with p*sh - ph + r*dh = h,
- *                    q*sw - pw + s*dw = w of dy[n][p][q][k] * w[k][r][s][c]
- *                    + beta * c_in[n][h][w][c]
- * Arguments describe the forward problem: x was N x H x W x C, the filter is
- * w KRSC, dy is N x P x Q x K with P, Q as for the forward pass; dx and c_in
- * are NHWC.  As on the page, dgrad gathers dy through the im2col addressing
- * with the filter-tap strides negated (padding -ph and dilation -dh over
- * dy); the GEMM view is M = N*H*W, N = C, K = R*S*K.  A forward stride s
- * places dy on every s-th coordinate of a zero-inserted image that the same
- * gather reads; the skipped coordinates cost matrix work (a factor s^2 over
- * the stride-1 cost), unlike the page's separate strided-dgrad operator.
- *   workspace  at least gmi_conv2d_dgrad_workspace_bytes(C, K, R, S) bytes,
- *              16-byte aligned: a first launch writes the filter there as
- *              [C][R][S][K], the GEMM launch reads it.
- * The traversal stride must be 1, 2, 4 or 8 and equal in both dimensions,
- * else GMI_ERR_UNSUPPORTED.  Other rules as for the forward pass: C % 8 == 0
- * and K % 8 == 0, 16-byte aligned pointers, c_in NULL iff beta == 0. */
 /* Bytes of the workspace gmi_conv2d_wgrad_implicit needs for this problem
  * on the current device (the transposed operands and fp32 partial sums of
  * the split over taps); 0 if the problem is rejected. */
@@ -364,6 +345,25 @@ gmi_status gmi_conv2d_wgrad_implicit(int32_t N, int32_t H, int32_t W, int32_t C,
                                      void* dw, gmi_dtype dtype, float alpha, float beta, void* workspace,
                                      size_t workspace_bytes, void* stream);
 
+/* Implicit-GEMM conv2d data gradient (the page's dgrad operator), the
+ * adjoint of gmi_conv2d_fprop_implicit in its activation:
+ *   dx[n][h][w][c] = alpha * sum over (p, q, k, r, s) with p*sh - ph + r*dh = h,
+ *                    q*sw - pw + s*dw = w of dy[n][p][q][k] * w[k][r][s][c]
+ *                    + beta * c_in[n][h][w][c]
+ * Arguments describe the forward problem: x was N x H x W x C, the filter is
+ * w KRSC, dy is N x P x Q x K with P, Q as for the forward pass; dx and c_in
+ * are NHWC.  As on the page, dgrad gathers dy through the im2col addressing
+ * with the filter-tap strides negated (padding -ph and dilation -dh over
+ * dy); the GEMM view is M = N*H*W, N = C, K = R*S*K.  A forward stride s
+ * places dy on every s-th coordinate of a zero-inserted image that the same
+ * gather reads; the skipped coordinates cost matrix work (a factor s^2 over
+ * the stride-1 cost), unlike the page's separate strided-dgrad operator.
+ *   workspace  at least gmi_conv2d_dgrad_workspace_bytes(C, K, R, S) bytes,
+ *              16-byte aligned: a first launch writes the filter there as
+ *              [C][R][S][K], the GEMM launch reads it.
+ * The traversal stride must be 1, 2, 4 or 8 and equal in both dimensions,
+ * else GMI_ERR_UNSUPPORTED.  Other rules as for the forward pass: C % 8 == 0
+ * and K % 8 == 0, 16-byte aligned pointers, c_in NULL iff beta == 0. */
 gmi_status gmi_conv2d_dgrad_implicit(int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int32_t R, int32_t S,
                                      int32_t pad_h, int32_t pad_w, int32_t stride_h, int32_t stride_w,
                                      int32_t dil_h, int32_t dil_w, const void* dy, const void* w, const void* c_in,
