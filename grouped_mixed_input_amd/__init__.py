@@ -60,6 +60,9 @@ def lib() -> ctypes.CDLL:
     L.gmi_gemm_grouped_offsets.restype = ctypes.c_int
     L.gmi_gemm_grouped_offsets.argtypes = [_i32, _p, _i32, _i32, _i32, _p, _i64, _p, _i64, _i64, _p, _i64, _p, _i64,
                                            ctypes.c_int, _f32, _f32, _p, _sz, _p]
+    L.gmi_gemm_grouped_offsets_noalloc.restype = ctypes.c_int
+    L.gmi_gemm_grouped_offsets_noalloc.argtypes = [_i32, _p, _i32, _i32, _i32, _p, _i64, _p, _i64, _i64, _p, _i64, _p,
+                                                   _i64, ctypes.c_int, _f32, _f32, _p]
     L.gmi_gemm_ptr_array.restype = ctypes.c_int
     L.gmi_gemm_ptr_array.argtypes = [_i32, _i32, _i32, _i32, _p, _i64, _p, _i64, _p, _i64, _p, _i64, ctypes.c_int,
                                      _f32, _f32, _p]
@@ -151,11 +154,7 @@ def gemm_grouped_raw(problems, count, dtype, alpha, beta, workspace, stream=None
                                   _stream(stream)))
 
 
-def gemm_grouped_offsets(offsets: torch.Tensor, A: torch.Tensor, B: torch.Tensor, D: torch.Tensor,
-                         C: torch.Tensor | None = None, alpha=1.0, beta=0.0, workspace=None, stream=None):
-    """Grouped GEMM with device-held group sizes: group g owns rows offsets[g] .. offsets[g+1] of A [rows][K]
-    and D [rows][N] (and C) and multiplies them by B[g] (B is [groups][N][K], each B[g] column-major K x N).
-    `offsets` is a device int32 tensor of groups + 1 entries; nothing is read back to the host."""
+def _offsets_args(offsets, A, B, D):
     if B.dim() != 3 or B.stride(2) != 1 or B.stride(1) < B.shape[2]:
         raise ValueError("B must be [groups][N][K] with unit stride along K")
     if offsets.dtype != torch.int32 or offsets.dim() != 1 or not offsets.is_contiguous():
@@ -167,12 +166,33 @@ def gemm_grouped_offsets(offsets: torch.Tensor, A: torch.Tensor, B: torch.Tensor
     K = A.shape[1]
     if A.shape[0] != rows or B.shape[1] != N or B.shape[2] != K:
         raise ValueError("A [rows][K], B [groups][N][K] and D [rows][N] disagree")
+    return count, rows, N, K
+
+
+def gemm_grouped_offsets(offsets: torch.Tensor, A: torch.Tensor, B: torch.Tensor, D: torch.Tensor,
+                         C: torch.Tensor | None = None, alpha=1.0, beta=0.0, workspace=None, stream=None):
+    """Grouped GEMM with device-held group sizes: group g owns rows offsets[g] .. offsets[g+1] of A [rows][K]
+    and D [rows][N] (and C) and multiplies them by B[g] (B is [groups][N][K], each B[g] column-major K x N).
+    `offsets` is a device int32 tensor of groups + 1 entries; nothing is read back to the host."""
+    count, rows, N, K = _offsets_args(offsets, A, B, D)
     if workspace is None:
         workspace = torch.empty(workspace_bytes(count), dtype=torch.uint8, device=D.device)
     _check(lib().gmi_gemm_grouped_offsets(count, offsets.data_ptr(), rows, N, K, A.data_ptr(), _ld(A),
                                           B.data_ptr(), B.stride(1), B.stride(0), _ptr(C),
                                           _ld(C) if C is not None else 0, D.data_ptr(), _ld(D), _DT[A.dtype],
                                           alpha, beta, workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return D
+
+
+def gemm_grouped_offsets_noalloc(offsets: torch.Tensor, A: torch.Tensor, B: torch.Tensor, D: torch.Tensor,
+                                 C: torch.Tensor | None = None, alpha=1.0, beta=0.0, stream=None):
+    """gemm_grouped_offsets without a workspace: the library keeps the group table in its own static device
+    array (at most 1024 groups); calls that overlap on one device race on that array."""
+    count, rows, N, K = _offsets_args(offsets, A, B, D)
+    _check(lib().gmi_gemm_grouped_offsets_noalloc(count, offsets.data_ptr(), rows, N, K, A.data_ptr(), _ld(A),
+                                                  B.data_ptr(), B.stride(1), B.stride(0), _ptr(C),
+                                                  _ld(C) if C is not None else 0, D.data_ptr(), _ld(D), _DT[A.dtype],
+                                                  alpha, beta, _stream(stream)))
     return D
 
 

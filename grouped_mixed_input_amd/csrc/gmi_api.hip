@@ -13,6 +13,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -87,6 +88,43 @@ static int choose_shape(F tiles_at) {
 }
 
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Scratch of the allocation-free grouped call (gmi_gemm_grouped_offsets_noalloc):
+// what gmi_gemm_grouped_offsets keeps in the caller's workspace -- the tile
+// total in the header, then one descriptor per group -- for the largest
+// group count the call takes.  Each device the library runs on holds its own
+// copy from the library's load until the process ends.  Host code never uses
+// the array's name as an address: the device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kScratchBytes = kWorkspaceHeader + sizeof(GroupDesc) * kMaxOffsetGroupCount;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::atomic<void*> g_scratch_addr[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+// the current device's address of `scratch`, looked up on its first use
+static gmi_status scratch_address(const char* who, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(GMI_ERR_HIP, "%s: hipGetDevice: %s", who, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(GMI_ERR_UNSUPPORTED, "%s: device %d, the scratch table is kept for devices 0..%d", who, dev,
+                kMaxDevices - 1);
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p)
+        return fail(GMI_ERR_HIP, "%s: hipGetSymbolAddress of the scratch table: %s", who, hipGetErrorString(e));
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return GMI_OK;
+}
 
 }  // namespace gmi
 
@@ -192,45 +230,55 @@ gmi_status gmi_gemm_grouped(const gmi_problem* problems, int32_t count, gmi_dtyp
                     "gemm_grouped: launch");
 }
 
-gmi_status gmi_gemm_grouped_offsets(int32_t count, const int32_t* offsets, int32_t rows, int32_t N, int32_t K,
-                                    const void* A, int64_t lda, const void* B, int64_t ldb, int64_t stride_b,
-                                    const void* C, int64_t ldc, void* D, int64_t ldd, gmi_dtype dtype,
-                                    float alpha, float beta, void* workspace, size_t workspace_bytes,
-                                    void* stream) {
-  g_last_error.clear();
+}  // extern "C"
+
+// The grouped GEMM with device-held group sizes: every check, then the
+// table-building launch and the GEMM launch.  `own_scratch` selects the
+// library's static per-device table instead of the caller's workspace (the
+// allocation-free call); it is looked up only after every check has passed.
+static gmi_status grouped_offsets(const char* who, int32_t count, const int32_t* offsets, int32_t rows, int32_t N,
+                                  int32_t K, const void* A, int64_t lda, const void* B, int64_t ldb, int64_t stride_b,
+                                  const void* C, int64_t ldc, void* D, int64_t ldd, gmi_dtype dtype, float alpha,
+                                  float beta, void* workspace, size_t workspace_bytes, bool own_scratch,
+                                  void* stream) {
   if (count < 0 || rows < 0 || N < 0 || K < 0)
-    return fail(GMI_ERR_INVALID_ARG, "gemm_grouped_offsets: negative size (count %d, rows %d, N %d, K %d)", count,
+    return fail(GMI_ERR_INVALID_ARG, "%s: negative size (count %d, rows %d, N %d, K %d)", who, count,
                 rows, N, K);
   if (count > kMaxOffsetGroupCount)
-    return fail(GMI_ERR_UNSUPPORTED, "gemm_grouped_offsets: %d groups, at most %d", count, kMaxOffsetGroupCount);
+    return fail(GMI_ERR_UNSUPPORTED, "%s: %d groups, at most %d", who, count, kMaxOffsetGroupCount);
   if (!gemm_dtype_ok(dtype))
-    return fail(GMI_ERR_UNSUPPORTED, "gemm_grouped_offsets: dtype %d not supported", (int)dtype);
+    return fail(GMI_ERR_UNSUPPORTED, "%s: dtype %d not supported", who, (int)dtype);
   if (count == 0 || rows == 0 || N == 0) return GMI_OK;
   const bool use_c = beta != 0.0f;
   if (!offsets || !D || (K > 0 && (!A || !B)) || (use_c && !C))
-    return fail(GMI_ERR_INVALID_ARG, "gemm_grouped_offsets: a NULL operand");
+    return fail(GMI_ERR_INVALID_ARG, "%s: a NULL operand", who);
   if ((K > 0 && (lda < K || ldb < K)) || ldd < N || (use_c && ldc < N))
-    return fail(GMI_ERR_INVALID_ARG, "gemm_grouped_offsets: a leading dimension below its row width");
-  if (stride_b < 0) return fail(GMI_ERR_INVALID_ARG, "gemm_grouped_offsets: stride_b %lld < 0", (long long)stride_b);
+    return fail(GMI_ERR_INVALID_ARG, "%s: a leading dimension below its row width", who);
+  if (stride_b < 0) return fail(GMI_ERR_INVALID_ARG, "%s: stride_b %lld < 0", who, (long long)stride_b);
   if (lda > kMaxLd || ldb > kMaxLd || ldd > kMaxLd || (use_c && ldc > kMaxLd))
-    return fail(GMI_ERR_UNSUPPORTED, "gemm_grouped_offsets: a leading dimension above 2^22 elements");
+    return fail(GMI_ERR_UNSUPPORTED, "%s: a leading dimension above 2^22 elements", who);
   if (!f8_shape_ok(dtype, K, lda, ldb) || (dtype == GMI_F8E4M3 && stride_b % 16))
-    return fail(GMI_ERR_UNSUPPORTED, "gemm_grouped_offsets: fp8 needs K, lda, ldb and stride_b multiples of 16");
+    return fail(GMI_ERR_UNSUPPORTED, "%s: fp8 needs K, lda, ldb and stride_b multiples of 16", who);
   if ((K > 0 && (!aligned16(A) || !aligned16(B) || lda % 8 || ldb % 8 || stride_b % 8)) || !aligned16(D) ||
       ldd % 8 || (use_c && (!aligned16(C) || ldc % 8)) || ((uintptr_t)offsets & 3u))
     return fail(GMI_ERR_MISALIGNED,
-                "gemm_grouped_offsets: pointers must be 16-byte aligned (offsets 4-byte), ld and stride_b multiples "
-                "of 8");
+                "%s: pointers must be 16-byte aligned (offsets 4-byte), ld and stride_b multiples "
+                "of 8", who);
+  if (own_scratch) {
+    const gmi_status st = scratch_address(who, &workspace);
+    if (st != GMI_OK) return st;
+    workspace_bytes = kScratchBytes;
+  }
   if (!workspace || workspace_bytes < gmi_workspace_bytes(count))
-    return fail(GMI_ERR_WORKSPACE, "gemm_grouped_offsets: workspace of %zu bytes, %zu needed", workspace_bytes,
+    return fail(GMI_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", who, workspace_bytes,
                 gmi_workspace_bytes(count));
-  if (!aligned16(workspace)) return fail(GMI_ERR_MISALIGNED, "gemm_grouped_offsets: workspace must be 16-byte aligned");
+  if (!aligned16(workspace)) return fail(GMI_ERR_MISALIGNED, "%s: workspace must be 16-byte aligned", who);
   // The group sizes are unknown here: the shape is chosen from the fewest
   // tiles the rows can make (all rows in one group), and the tile total is
   // bounded by every group adding at most one partial tile row.
   const int shape = choose_shape([&](int bm, int bn) { return cdiv(rows, bm) * cdiv(N, bn); });
   const int64_t bound = (cdiv(rows, SMALL_M) + count) * cdiv(N, tile_bn(shape));
-  if (bound > INT32_MAX) return fail(GMI_ERR_INVALID_ARG, "gemm_grouped_offsets: more than 2^31 - 1 output tiles");
+  if (bound > INT32_MAX) return fail(GMI_ERR_INVALID_ARG, "%s: more than 2^31 - 1 output tiles", who);
   OffsetsLaunch p;
   p.offsets = offsets;
   p.count = count;
@@ -248,8 +296,28 @@ gmi_status gmi_gemm_grouped_offsets(int32_t count, const int32_t* offsets, int32
   p.ldd = ldd;
   p.total = (int32_t*)workspace;
   p.desc = (GroupDesc*)((char*)workspace + kWorkspaceHeader);
-  return hip_status(launch_grouped_offsets(p, shape, (int)dtype, alpha, beta, (hipStream_t)stream),
-                    "gemm_grouped_offsets: launch");
+  return hip_status(launch_grouped_offsets(p, shape, (int)dtype, alpha, beta, (hipStream_t)stream), who);
+}
+
+extern "C" {
+
+gmi_status gmi_gemm_grouped_offsets(int32_t count, const int32_t* offsets, int32_t rows, int32_t N, int32_t K,
+                                    const void* A, int64_t lda, const void* B, int64_t ldb, int64_t stride_b,
+                                    const void* C, int64_t ldc, void* D, int64_t ldd, gmi_dtype dtype,
+                                    float alpha, float beta, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  g_last_error.clear();
+  return grouped_offsets("gemm_grouped_offsets", count, offsets, rows, N, K, A, lda, B, ldb, stride_b, C, ldc, D, ldd,
+                         dtype, alpha, beta, workspace, workspace_bytes, false, stream);
+}
+
+gmi_status gmi_gemm_grouped_offsets_noalloc(int32_t count, const int32_t* offsets, int32_t rows, int32_t N,
+                                            int32_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                                            int64_t stride_b, const void* C, int64_t ldc, void* D, int64_t ldd,
+                                            gmi_dtype dtype, float alpha, float beta, void* stream) {
+  g_last_error.clear();
+  return grouped_offsets("gemm_grouped_offsets_noalloc", count, offsets, rows, N, K, A, lda, B, ldb, stride_b, C, ldc,
+                         D, ldd, dtype, alpha, beta, nullptr, 0, true, stream);
 }
 
 gmi_status gmi_gemm_ptr_array(int32_t L, int32_t M, int32_t N, int32_t K, const void* const* A, int64_t lda,

@@ -131,6 +131,26 @@ gmi_status gmi_gemm_grouped_offsets(int32_t count, const int32_t* offsets, int32
                                     float alpha, float beta, void* workspace, size_t workspace_bytes,
                                     void* stream);
 
+/* For callers that cannot allocate device memory -- work captured into a HIP
+ * graph, tight serving loops, harnesses that forbid hipMalloc -- the same call
+ * as gmi_gemm_grouped_offsets without a workspace argument: the group table
+ * and tile total live in a static device array of the library, 82,176 bytes
+ * (256 + 80 * 1024), one per device, which each device holds from the
+ * library's load until the process ends.  The call allocates nothing; on a
+ * device's first call it looks up that device's address of the array.
+ *   count  1 .. 1024 (the table's capacity), else GMI_ERR_UNSUPPORTED.
+ * Every call on one device shares that device's array and leaves the last
+ * call's table in it (each call rewrites every entry it reads, so nothing
+ * needs clearing): two calls that overlap on one device, on different
+ * streams or from different threads, race on the array and give undefined
+ * results; order them on one stream.  A failed address lookup returns
+ * GMI_ERR_HIP.  Every other argument, layout and rule as for
+ * gmi_gemm_grouped_offsets. */
+gmi_status gmi_gemm_grouped_offsets_noalloc(int32_t count, const int32_t* offsets, int32_t rows, int32_t N,
+                                            int32_t K, const void* A, int64_t lda, const void* B, int64_t ldb,
+                                            int64_t stride_b, const void* C, int64_t ldc, void* D, int64_t ldd,
+                                            gmi_dtype dtype, float alpha, float beta, void* stream);
+
 /* Pointer-array batched GEMM: L problems of one shape (M, N, K) and shared
  * leading dimensions, each operand a separate device buffer.  The pointer
  * arrays themselves are device arrays of L device pointers.  Follows the

@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
                  "gmi_conv2d_fprop_implicit", "gmi_workspace_bytes", "gmi_prepack_w4_bytes", "gmi_last_error",
                  "gmi_gemm_grouped_offsets", "gmi_w4a16_workspace_bytes", "gmi_gemm_mixed",
                  "gmi_gemm_mixed_grouped", "gmi_conv2d_dgrad_implicit", "gmi_conv2d_dgrad_workspace_bytes",
-                 "gmi_conv2d_wgrad_implicit", "gmi_conv2d_wgrad_workspace_bytes", "gmi_conv2d_fprop_implicit_fused"]:
+                 "gmi_conv2d_wgrad_implicit", "gmi_conv2d_wgrad_workspace_bytes", "gmi_conv2d_fprop_implicit_fused",
+                 "gmi_gemm_grouped_offsets_noalloc"]:
         assert want in names
 
 
@@ -120,6 +121,26 @@ def test_grouped_offsets_validation(gmi):
     # nothing to do: no groups, no rows or no columns -- OK without a GPU call
     for kw in (dict(count=0), dict(rows=0), dict(N=0)):
         assert _offs(gmi, offsets=None, A=None, B=None, D=None, ws=0, ws_bytes=0, **kw)[0] == gmi.GMI_OK, kw
+
+
+def test_grouped_offsets_noalloc_validation(gmi):
+    # the allocation-free call runs the same checks before it looks anything up on a device; its table holds
+    # at most 1024 groups
+    L = gmi.lib()
+
+    def noalloc(count=4, offsets=A16 * 5, A=A16, lda=64, dt=1):
+        st = L.gmi_gemm_grouped_offsets_noalloc(count, offsets, 256, 64, 64, A, lda, A16 * 2, 64, 64 * 64, None, 64,
+                                                A16 * 4, 64, dt, 1.0, 0.0, None)
+        return st, L.gmi_last_error().decode()
+
+    st, msg = noalloc(count=1025)
+    assert st == gmi.GMI_ERR_UNSUPPORTED and "1024" in msg and "noalloc" in msg
+    assert noalloc(count=-1)[0] == gmi.GMI_ERR_INVALID_ARG
+    assert noalloc(offsets=None)[0] == gmi.GMI_ERR_INVALID_ARG
+    assert noalloc(A=A16 + 8)[0] == gmi.GMI_ERR_MISALIGNED
+    assert noalloc(lda=32)[0] == gmi.GMI_ERR_INVALID_ARG
+    assert noalloc(dt=9)[0] == gmi.GMI_ERR_UNSUPPORTED
+    assert noalloc(count=0, offsets=None, A=None)[0] == gmi.GMI_OK
 
 
 def _ptr(gmi, L=2, M=64, N=64, K=64, A=A16, lda=64, B=A16, ldb=64, C=None, ldc=64, D=A16, ldd=64, dt=1, beta=0.0):
