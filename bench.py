@@ -330,6 +330,49 @@ def bench_conv(torch, gmi, gi, dev, out):
     torch.cuda.empty_cache()
 
 
+def bench_w4(torch, gmi, gi, dev, out):
+    """W4A16 at M = 16 / 128 / 1024 / 4096 (fp16, uint4 with zero points) and the bf16 / int4 mixed-input lines."""
+    # 4. W4A16, N = K = 8192, g = 128
+    w = gi.w4a16(M=16)
+    base_pp = gmi.prepack_w4(torch.from_numpy(w["W"]).to(dev), 8192, 8192)
+    S = t16(torch, w["scales"], torch.float16, dev)
+    Z = torch.from_numpy(w["zeros"]).to(dev)
+    for M in (16, 128, 1024, 4096):
+        X = t16(torch, gi.w4a16(M=M, N=16, K=8192)["X"], torch.float16, dev)
+        ws = 8192 * 8192 // 2 + S.numel() * 2 + Z.numel() + 2 * M * 8192 * 2
+        R = copies_for(ws)
+        sets = [(base_pp.clone(), S.clone(), Z.clone(), X.clone(), torch.empty((M, 8192), dtype=torch.float16,
+                                                                                device=dev)) for _ in range(R)]
+
+        wsp = torch.empty(gmi.w4a16_workspace_bytes(M, 8192, 8192), dtype=torch.uint8, device=dev)
+
+        def fn(i, sets=sets, wsp=wsp):
+            pp, s, z, x, y = sets[i]
+            gmi.gemm_w4a16(x, pp, s, z, 128, 8192, Y=y, workspace=wsp)
+
+        tm = time_launches(torch, fn, R, 5)
+        out[f"w4a16_M{M}"] = roof(2.0 * M * 8192 * 8192, ws, tm)
+        del sets
+    # the same shapes with bf16 activations and scales, int4 weights with zero points
+    Sb = S.float().to(torch.bfloat16)
+    for M in (16, 48, 128, 1024):
+        X = t16(torch, gi.w4a16(M=M, N=16, K=8192)["X"], torch.float16, dev).float().to(torch.bfloat16)
+        ws = 8192 * 8192 // 2 + Sb.numel() * 2 + Z.numel() + 2 * M * 8192 * 2
+        R = copies_for(ws)
+        sets = [(base_pp.clone(), Sb.clone(), Z.clone(), X.clone(), torch.empty((M, 8192), dtype=torch.bfloat16,
+                                                                                 device=dev)) for _ in range(R)]
+        wsp = torch.empty(gmi.w4a16_workspace_bytes(M, 8192, 8192), dtype=torch.uint8, device=dev)
+
+        def fn(i, sets=sets, wsp=wsp):
+            pp, s, z, x, y = sets[i]
+            gmi.gemm_mixed(x, pp, s, z, 128, 8192, w_type="int4", Y=y, workspace=wsp)
+
+        tm = time_launches(torch, fn, R, 5)
+        out[f"mixed_bf16_int4_M{M}"] = roof(2.0 * M * 8192 * 8192, ws, tm)
+        del sets
+    log("bench: W4A16 done")
+
+
 def bench_workloads(torch, gmi, gi, dev, args):
     out = {}
     # 1. grouped fp16, 4 groups, beta 0.5 (launch-latency bound)
@@ -348,47 +391,7 @@ def bench_workloads(torch, gmi, gi, dev, args):
 
     counts, off = bench_moe(torch, gmi, gi, dev, out)
 
-    # 4. W4A16, N = K = 8192, g = 128
-    w = gi.w4a16(M=16)
-    base_pp = gmi.prepack_w4(torch.from_numpy(w["W"]).to(dev), 8192, 8192)
-    S = t16(torch, w["scales"], torch.float16, dev)
-    Z = torch.from_numpy(w["zeros"]).to(dev)
-    rx = np.random.default_rng(0)
-    for M in (16, 128, 1024, 4096):
-        X = t16(torch, gi.w4a16(M=M, N=16, K=8192)["X"], torch.float16, dev)
-        ws = 8192 * 8192 // 2 + S.numel() * 2 + Z.numel() + 2 * M * 8192 * 2
-        R = copies_for(ws)
-        sets = [(base_pp.clone(), S.clone(), Z.clone(), X.clone(), torch.empty((M, 8192), dtype=torch.float16,
-                                                                                device=dev)) for _ in range(R)]
-
-        wsp = torch.empty(gmi.w4a16_workspace_bytes(M, 8192, 8192), dtype=torch.uint8, device=dev)
-
-        def fn(i, sets=sets, wsp=wsp):
-            pp, s, z, x, y = sets[i]
-            gmi.gemm_w4a16(x, pp, s, z, 128, 8192, Y=y, workspace=wsp)
-
-        tm = time_launches(torch, fn, R, 5)
-        out[f"w4a16_M{M}"] = roof(2.0 * M * 8192 * 8192, ws, tm)
-        del sets
-    del rx
-    # the same shapes with bf16 activations and scales, int4 weights with zero points
-    Sb = S.float().to(torch.bfloat16)
-    for M in (16, 1024):
-        X = t16(torch, gi.w4a16(M=M, N=16, K=8192)["X"], torch.float16, dev).float().to(torch.bfloat16)
-        ws = 8192 * 8192 // 2 + Sb.numel() * 2 + Z.numel() + 2 * M * 8192 * 2
-        R = copies_for(ws)
-        sets = [(base_pp.clone(), Sb.clone(), Z.clone(), X.clone(), torch.empty((M, 8192), dtype=torch.bfloat16,
-                                                                                 device=dev)) for _ in range(R)]
-        wsp = torch.empty(gmi.w4a16_workspace_bytes(M, 8192, 8192), dtype=torch.uint8, device=dev)
-
-        def fn(i, sets=sets, wsp=wsp):
-            pp, s, z, x, y = sets[i]
-            gmi.gemm_mixed(x, pp, s, z, 128, 8192, w_type="int4", Y=y, workspace=wsp)
-
-        tm = time_launches(torch, fn, R, 5)
-        out[f"mixed_bf16_int4_M{M}"] = roof(2.0 * M * 8192 * 8192, ws, tm)
-        del sets
-    log("bench: W4A16 done")
+    bench_w4(torch, gmi, gi, dev, out)
 
     bench_moe_w4(torch, gmi, gi, dev, out)
 
@@ -458,9 +461,9 @@ def main():
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the W4A16 decode workload (M = 16, N = K = 8192, g = 128) and print one line "
                          "for it (for the decode kernel's profiles)")
-    ap.add_argument("--only", choices=["moe", "moe_w4", "conv"],
-                    help="time only the bf16 MoE layers, the 4-bit MoE layers or the conv layers and print their lines (for those "
-                         "kernels' profiles)")
+    ap.add_argument("--only", choices=["moe", "moe_w4", "conv", "w4"],
+                    help="time only the bf16 MoE layers, the 4-bit MoE layers, the conv layers or the W4A16 / mixed-input "
+                         "lines and print their lines (for those kernels' profiles)")
     ap.add_argument("--copy-ref", action="store_true",
                     help="after the timed region, run one plain 256 MiB device copy (a known-size kernel that "
                          "calibrates hardware byte counters)")
@@ -486,7 +489,7 @@ def main():
         return
     if args.only:
         out = {}
-        {"moe": bench_moe, "moe_w4": bench_moe_w4, "conv": bench_conv}[args.only](torch, gmi, gi, dev, out)
+        {"moe": bench_moe, "moe_w4": bench_moe_w4, "conv": bench_conv, "w4": bench_w4}[args.only](torch, gmi, gi, dev, out)
         copy_ref(torch, dev, args)
         print(json.dumps(out), flush=True)
         return

@@ -556,6 +556,20 @@ __device__ __forceinline__ u32x4 dequant8_bf16(uint32_t w, float s, float nzs) {
   return out;
 }
 
+// q - z for the 8 nibbles of w as exact bfloat16 values (|q - z| <= 15 has
+// at most 4 significant bits), in the order of dequant8_bf16: the integer
+// part only, for kernels that apply the group scale to fp32 partial sums.
+__device__ __forceinline__ u32x4 exact8_bf16(uint32_t w, float zf) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  auto d = [&](uint32_t v, int i) { return ubyte_f32(v, i) - zf; };
+  u32x4 out;
+  out[0] = pack2<DT_BF16>(d(lo, 0), d(lo, 2));
+  out[1] = pack2<DT_BF16>(d(hi, 0), d(hi, 2));
+  out[2] = pack2<DT_BF16>(d(lo, 1), d(lo, 3));
+  out[3] = pack2<DT_BF16>(d(hi, 1), d(hi, 3));
+  return out;
+}
+
 // dequantised 16-bit weights of one word in the activation type: s_bits is
 // the scale's storage pattern, z the zero point (both after the mode fix-ups)
 template <int DT>
@@ -586,13 +600,28 @@ struct W4Geom {
 // 16-row blocks it covers -- 8 bytes per entry -- plus each entry's scale and
 // zero, into registers.  The dequantisation runs when the registers are
 // written to LDS, after the multiplies of the current stage have been issued.
+//
+// fp16: the LDS tile holds RN16((q - z) s), the page's conversion in the
+// activation type (its 11-bit significand keeps that rounding far inside the
+// parity bar).  bf16 (EXACT): an 8-bit significand would round each weight by
+// up to 2^-9 |w|, which over K = 8192 terms reaches the bar, so the tile holds
+// the exact integers q - z instead and the mainloop multiplies into fp32
+// partial sums that each 128-k-multiple scale group folds into the
+// accumulators with its own scale: sum_k x (q - z) s = sum over groups of
+// s * sum_k x (q - z), with every product exact and only fp32 sums rounding.
+// The scale of each accumulator column is then loaded once per group
+// (fold_scales) instead of once per weight entry.
 // ---------------------------------------------------------------------------
 template <class Cfg, int ROWS, int DT = DT_F16>
 struct W4Loader {
   static constexpr bool kDMA = false;
   static constexpr bool kFIX = false;
+  static constexpr bool EXACT = DT == DT_BF16;
   static constexpr int ENTRIES = ROWS / 16 * 64;
   static constexpr int P = ENTRIES / Cfg::THREADS;
+  // loads one k-tile issues per lane entry: weight bytes, zero point and, for
+  // the rounded form, the scale
+  static constexpr int LOADS = P * (EXACT ? 2 : 3);
   static_assert(Cfg::BK == 64, "the uint4 loader moves half a 128-k block per k-tile");
   static_assert(ENTRIES % Cfg::THREADS == 0, "rows must cover whole lane-entry passes");
   struct Regs {
@@ -627,7 +656,7 @@ struct W4Loader {
       const uint32_t n = (block0 + nb) * 16 + (L % 16);
       const bool ok = n < N;
       rg.w[i] = buf_load8(rw, ok ? ((block0 + nb) * kblocks + kt / 2) * 1024u + L * 16u + (kt & 1) * 8u : OOB);
-      rg.s[i] = buf_load2(rsc, ok ? (grp * N + n) * 2u : OOB);
+      if constexpr (!EXACT) rg.s[i] = buf_load2(rsc, ok ? (grp * N + n) * 2u : OOB);
       rg.z[i] = buf_load1(rz, ok ? grp * (N / 2) + n / 2 : OOB);
     }
   }
@@ -639,11 +668,59 @@ struct W4Loader {
       const int nb = e / 64, L = e % 64;
       const int row = nb * 16 + (L % 16), h = L / 16;
       const uint32_t n = (block0 + nb) * 16 + (L % 16);
-      const uint32_t sb = (rg.s[i] & 0xffffu) | sor, z = ((rg.z[i] >> ((n & 1) * 4)) & 15u) ^ zxor;
+      const uint32_t z = ((rg.z[i] >> ((n & 1) * 4)) & 15u) ^ zxor;
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-        *(u32x4*)(lds + Cfg::off(row, 4 * jj + h)) = dequant8_dt<DT>(rg.w[i][jj] ^ wxor, sb, z);
+      for (int jj = 0; jj < 2; ++jj) {
+        u32x4 v;
+        if constexpr (EXACT)
+          v = exact8_bf16(rg.w[i][jj] ^ wxor, (float)z);
+        else
+          v = dequant8_dt<DT>(rg.w[i][jj] ^ wxor, (rg.s[i] & 0xffffu) | sor, z);
+        *(u32x4*)(lds + Cfg::off(row, 4 * jj + h)) = v;
+      }
     }
+  }
+
+  // EXACT: the group scales of this lane's accumulator columns for the group
+  // holding k-tile kt_local, as bf16 pairs: block j of the wave tile, register
+  // group q covers columns n0 + wn + 32 j + 8 q + 4 (lane / 32) + {0..3}
+  // (the MFMA result layout with the weight fragment as first operand)
+  __device__ __forceinline__ void fold_scales(int kt_local, u32x2 (&sc)[Cfg::TN][4]) const {
+    const uint32_t grp = ((kt_local + kt0) * Cfg::BK) / group;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t wn = (wave % Cfg::WAVES_N) * Cfg::WTN;
+#pragma unroll
+    for (int j = 0; j < Cfg::TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t n = block0 * 16 + wn + 32 * j + 8 * q + 4 * (lane >> 5);
+        sc[j][q] = buf_load8(rsc, n < N ? (grp * N + n) * 2u : OOB);
+      }
+  }
+  // acc += s * part over the accumulators, then part = 0.  The mode's OR
+  // (1.0 without scales) is applied here, where the scale registers are first
+  // read: that is after the k-tile's wait, so the compiler's own wait for
+  // them holds back nothing younger.
+  __device__ __forceinline__ void fold(f32x16 (&acc)[Cfg::TM][Cfg::TN], f32x16 (&part)[Cfg::TM][Cfg::TN],
+                                       const u32x2 (&sc)[Cfg::TN][4]) const {
+#pragma unroll
+    for (int j = 0; j < Cfg::TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float s = from_bits<DT_BF16>(((sc[j][q][e / 2] >> (16 * (e % 2))) & 0xffffu) | sor);
+#pragma unroll
+          for (int i = 0; i < Cfg::TM; ++i) acc[i][j][4 * q + e] = __builtin_fmaf(s, part[i][j][4 * q + e], acc[i][j][4 * q + e]);
+        }
+#pragma unroll
+    for (int i = 0; i < Cfg::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < Cfg::TN; ++j) part[i][j] = f32x16{};
+  }
+  // EXACT: does the group of k-tile kt_local end with it (or does the k-range)?
+  __device__ __forceinline__ bool group_ends(int kt_local, int nk) const {
+    return kt_local + 1 == nk || (((kt_local + kt0 + 1) * Cfg::BK) % group) == 0;
   }
 };
 
@@ -747,6 +824,23 @@ __device__ __forceinline__ void read_frags(const FragAddr<Cfg>& fa_, const char*
   for (int j = 0; j < Cfg::TN; ++j) fb[j] = frag_at<Cfg>(sb, fa_.b[kk], j);
 }
 
+// Copies spread over the first SPAN matrix slots of a stage: slot i issues
+// copies [ceil(i T / SPAN), ceil((i + 1) T / SPAN)).  The ranges tile [0, T)
+// in order, so every copy is issued exactly once and those of the first
+// loader (indices below P1) all go out before any of the second's -- the
+// order the end-of-stage waits count on.
+constexpr int slot_first_copy(int slot, int T, int SPAN) { return slot < SPAN ? (slot * T + SPAN - 1) / SPAN : T; }
+constexpr bool copy_slots_tile(int T, int SPAN, int SLOTS) {
+  if (SPAN < 1 || SPAN > SLOTS) return false;
+  int next = 0;
+  for (int i = 0; i < SLOTS; ++i) {
+    const int v0 = slot_first_copy(i, T, SPAN), v1 = slot_first_copy(i + 1, T, SPAN);
+    if (v0 != next || v1 < v0) return false;
+    next = v1;
+  }
+  return next == T;
+}
+
 template <class Cfg, int DT, bool CROSS, int SPAN_DIV, class L1, class L2>
 __device__ __forceinline__ void multiply_stage(const FragAddr<Cfg>& ad, const char* sa, const char* sb,
                                                const char* na, const char* nb, f32x16 (&acc)[Cfg::TM][Cfg::TN],
@@ -757,6 +851,7 @@ __device__ __forceinline__ void multiply_stage(const FragAddr<Cfg>& ad, const ch
   constexpr int NMFMA = Cfg::TM * Cfg::TN, NDS = Cfg::TM + Cfg::TN;
   constexpr int P1 = dma_count<L1>(), P2 = dma_count<L2>(), T = P1 + P2;
   constexpr int SPAN = (KK * NMFMA + SPAN_DIV - 1) / SPAN_DIV;  // copy slots
+  static_assert(copy_slots_tile(T, SPAN, KK * NMFMA), "each copy of the stage is issued once, in loader order");
   typename PrepOf<L1>::type p1{};
   typename PrepOf<L2>::type p2{};
   if constexpr (P1 > 0) p1 = l1.prep(k1);
@@ -779,14 +874,16 @@ __device__ __forceinline__ void multiply_stage(const FragAddr<Cfg>& ad, const ch
           fb[nx][m - Cfg::TM] = frag_at<Cfg>(rb, ad.b[rk], m - Cfg::TM);
       }
       const int slot = kk * NMFMA + m;
-      const int v0 = slot < SPAN ? (slot * T + SPAN - 1) / SPAN : T;
-      const int v1 = slot < SPAN ? ((slot + 1) * T + SPAN - 1) / SPAN : T;
+      const int v0 = slot_first_copy(slot, T, SPAN), v1 = slot_first_copy(slot + 1, T, SPAN);
 #pragma unroll
       for (int v = v0; v < v1; ++v) {
         if constexpr (P1 > 0) {
           if (v < P1) l1.issue_one(v, p1, d1);
         }
         if constexpr (P2 > 0) {
+          // the second loader's first copy: fenced so that no copy of the
+          // first loader can be scheduled after it
+          if (v == P1 && P1 > 0) __builtin_amdgcn_sched_barrier(0);
           if (v >= P1) l2.issue_one(v - P1, p2, d2);
         }
       }
@@ -855,6 +952,18 @@ __device__ __forceinline__ void mainloop(char* lds, const ALd& al, const BLd& bl
   FragAddr<Cfg> ad;
   ad.init();
 
+  // The waits below count outstanding vector-memory operations in issue
+  // order (the compiler does not track direct-to-LDS copies), and each leaves
+  // in flight exactly the copies issued after the ones it waits for:
+  //   split ring: a stage issues B of kt + 1 (multiply_stage's first loader,
+  //     PB copies), then A of kt + 2 (its second, PA); waiting down to PA
+  //     lands B of kt + 1.  The prologue issues A0, B0, A1: down to PA lands
+  //     A0 and B0.
+  //   stage ring: a stage issues the PT copies of k-tile kt + D; k-tiles
+  //     kt + 3 .. kt + D stay in flight, (D - 2) PT copies.
+  //   two stages: everything is waited for (0).
+  static_assert(!SPLIT || (PA > 0 && PB > 0), "the split ring waits on the A copies of the next k-tile");
+  static_assert(SPLIT || REG || (D - 2) * PT < 64, "the stages in flight fit the vmcnt counter");
   if constexpr (SPLIT) {
     constexpr int NS = Cfg::SLOTS;
     // prologue: A0 -> slot 0, B0 -> 1, A1 -> 2; A0 and B0 landed and published

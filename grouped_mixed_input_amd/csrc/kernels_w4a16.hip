@@ -62,10 +62,14 @@ hipError_t launch_prepack_w4(const uint8_t* w, int N, int K, uint8_t* out, hipSt
 // matching four 16-byte X fragments (token L % 16, same k-groups).  The next
 // k-block's loads are issued before the current one is multiplied.
 // ---------------------------------------------------------------------------
+// bf16 activations take the exact integers q - z into an fp32 partial sum per
+// k-block, which the scales of the lane's output rows then fold into the
+// accumulators (see W4Loader): `so` holds those four scales per weight block.
 template <int NB, int MT>
 struct SkinnyStage {
   u32x4 w[NB];
   uint32_t sz[NB];
+  u32x2 so[NB];
   u32x4 x[MT][4];
 };
 
@@ -74,9 +78,10 @@ struct SkinnyRes {
   uint32_t kblocks;
 };
 
-template <int NB, int MT>
+template <int DT, int NB, int MT>
 __device__ __forceinline__ void skinny_load(SkinnyStage<NB, MT>& st, const W4Launch& a, const SkinnyRes& rs,
                                             int n_base, int kb, int lane) {
+  constexpr bool EXACT = DT == DT_BF16;
   const uint32_t r = lane & 15, h = lane >> 4;
   const uint32_t grp = (uint32_t)(kb * 128) / (uint32_t)a.group;
   const uint32_t N = a.N;
@@ -85,9 +90,12 @@ __device__ __forceinline__ void skinny_load(SkinnyStage<NB, MT>& st, const W4Lau
     const uint32_t blk = n_base / 16 + nb, n = blk * 16 + r;
     const bool ok = n < N;
     st.w[nb] = buf_load16(rs.w, ok ? (blk * rs.kblocks + kb) * 1024u + lane * 16u : OOB);
-    const uint32_t s = buf_load2(rs.s, ok ? (grp * N + n) * 2u : OOB) | a.sor;
+    const uint32_t s = EXACT ? 0u : buf_load2(rs.s, ok ? (grp * N + n) * 2u : OOB) | a.sor;
     const uint32_t z = ((buf_load1(rs.z, ok ? grp * (N / 2) + n / 2 : OOB) >> ((n & 1) * 4)) & 15u) ^ a.zxor;
     st.sz[nb] = s | (z << 16);
+    // output rows blk * 16 + 4 h + {0..3} of this lane (N is a multiple of 16)
+    if constexpr (EXACT)
+      st.so[nb] = buf_load8(rs.s, blk * 16 < N ? (grp * N + blk * 16 + 4 * h) * 2u : OOB) | (a.sor * 0x00010001u);
   }
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -102,11 +110,30 @@ template <int DT, int NB, int MT>
 __device__ __forceinline__ void skinny_mma(const SkinnyStage<NB, MT>& st, uint32_t wxor, f32x4 (&acc)[NB][MT]) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
+    if constexpr (DT == DT_BF16) {
+      f32x4 part[MT];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const u32x4 wf = dequant8_dt<DT>(st.w[nb][j] ^ wxor, st.sz[nb] & 0xffffu, st.sz[nb] >> 16);
+      for (int mt = 0; mt < MT; ++mt) part[mt] = f32x4{0, 0, 0, 0};
+      const float zf = (float)(st.sz[nb] >> 16);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = mfma16<DT>(wf, st.x[mt][j], acc[nb][mt]);
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 wf = exact8_bf16(st.w[nb][j] ^ wxor, zf);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) part[mt] = mfma16<DT>(wf, st.x[mt][j], part[mt]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float si = from_bits<DT_BF16>((st.so[nb][i / 2] >> (16 * (i % 2))) & 0xffffu);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[nb][mt][i] = __builtin_fmaf(si, part[mt][i], acc[nb][mt][i]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 wf = dequant8_dt<DT>(st.w[nb][j] ^ wxor, st.sz[nb] & 0xffffu, st.sz[nb] >> 16);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = mfma16<DT>(wf, st.x[mt][j], acc[nb][mt]);
+      }
     }
   }
 }
@@ -141,9 +168,9 @@ __device__ __forceinline__ void skinny_body(const W4Launch& a, int n_base, char*
   rs.kblocks = kblocks;
   if (kb0 < kb1) {
     SkinnyStage<NB, MT> cur, nxt;
-    skinny_load<NB, MT>(cur, a, rs, n_base, kb0, lane);
+    skinny_load<DT, NB, MT>(cur, a, rs, n_base, kb0, lane);
     for (int kb = kb0; kb < kb1; ++kb) {
-      if (kb + 1 < kb1) skinny_load<NB, MT>(nxt, a, rs, n_base, kb + 1, lane);
+      if (kb + 1 < kb1) skinny_load<DT, NB, MT>(nxt, a, rs, n_base, kb + 1, lane);
       skinny_mma<DT, NB, MT>(cur, a.wxor, acc);
       cur = nxt;
     }
@@ -226,6 +253,12 @@ template <int DT, int NB, int KW, int R, int MT = 1>
 __device__ __forceinline__ void decode_body(const W4Launch& a, int n_base, char* lds) {
   static_assert(KW * NB * MT * 64 * 16 <= KW * DecodeLds<NB, R>::WAVE, "the reduction reuses the rings");
   using L = DecodeLds<NB, R>;
+  // vector-memory operations one ring slot issues, in this order: NB weight
+  // copies (direct to LDS, not tracked by the compiler), then 4 MT X loads.
+  // The wait before slot s leaves exactly the younger slots' operations in
+  // flight, so every slot must issue exactly this many, whatever its range.
+  constexpr int SLOT_VM = NB + 4 * MT;
+  static_assert((R - 1) * SLOT_VM < 64, "the younger slots fit the vmcnt counter");
   const int lane = threadIdx.x & 63, wave = wave_id();
   char* wring = lds + wave * L::WAVE;
   char* szb = wring + L::WRING;
@@ -290,7 +323,7 @@ __device__ __forceinline__ void decode_body(const W4Launch& a, int n_base, char*
     for (int s = 0; s < R; ++s) {
       // weight blocks and X fragments of slot s (and everything older)
       __builtin_amdgcn_sched_barrier(0);
-      wait_vm_le_n<(R - 1) * (NB + 4 * MT)>((R - 1 - s) * (NB + 4 * MT));
+      wait_vm_le_n<(R - 1) * SLOT_VM>((R - 1 - s) * SLOT_VM);
       if (base + s < kb1) {
         // bf16: the k-block's activation sum of each token, by the matrix
         // instruction against a fragment of ones (every output row the same)
@@ -406,27 +439,40 @@ struct W4Ring {
 };
 
 // one k-tile: weights of kt + 2 into `rl`, multiply kt, then publish kt + 1
-// (X already copied, weights from `rs`)
+// (X already copied, weights from `rs`).  With exact integer weights (bf16)
+// the multiply accumulates into `part`, which the last k-tile of each scale
+// group folds into `acc` with the group's scales.
 template <class Cfg, int DT, class ALd, class BLd>
 __device__ __forceinline__ void w4_step(char* lds, const ALd& al, const BLd& bl, int kt, int nk,
                                         typename BLd::Regs& rl, const typename BLd::Regs& rs, const FragAddr<Cfg>& ad,
-                                        f32x16 (&acc)[Cfg::TM][Cfg::TN], frag_t<Cfg> (&fa)[2][Cfg::TM],
-                                        frag_t<Cfg> (&fb)[2][Cfg::TN]) {
+                                        f32x16 (&acc)[Cfg::TM][Cfg::TN], f32x16 (&part)[Cfg::TM][Cfg::TN],
+                                        frag_t<Cfg> (&fa)[2][Cfg::TM], frag_t<Cfg> (&fb)[2][Cfg::TN]) {
   using Ring = W4Ring<Cfg>;
-  constexpr int YOUNG = ALd::P + 3 * BLd::P;  // one k-tile's copies and loads
+  constexpr int YOUNG = ALd::P + BLd::LOADS;  // one k-tile's copies and loads
   // The wait below counts outstanding loads in issue order, and the compiler
   // does not track the direct-to-LDS copies: the fences keep every load and
   // copy of k-tile kt + 2 between the previous step's wait and this one's.
+  // The scale loads of a fold are issued first, so they are older than every
+  // load the wait leaves in flight.
   __builtin_amdgcn_sched_barrier(0);
+  u32x2 sc[Cfg::TN][4];
+  bool fold = false;
+  if constexpr (BLd::EXACT) {
+    fold = bl.group_ends(kt, nk);
+    if (fold) bl.fold_scales(kt, sc);
+  }
   bl.load(kt + 2, rl);
   const char* ca = Ring::a(lds, kt % 3);
   const char* cb = Ring::b(lds, kt & 1);
   read_frags<Cfg>(ad, ca, cb, 0, fa[0], fb[0]);
-  multiply_stage<Cfg, DT, false, 2>(ad, ca, cb, ca, cb, acc, fa, fb, al, kt + 2, Ring::a(lds, (kt + 2) % 3), bl, 0,
-                                    nullptr);
+  multiply_stage<Cfg, DT, false, 2>(ad, ca, cb, ca, cb, BLd::EXACT ? part : acc, fa, fb, al, kt + 2,
+                                    Ring::a(lds, (kt + 2) % 3), bl, 0, nullptr);
   __builtin_amdgcn_sched_barrier(0);
   wait_vm_le<YOUNG>();
   if (kt + 1 < nk) bl.store(Ring::b(lds, (kt + 1) & 1), rs);
+  if constexpr (BLd::EXACT) {
+    if (fold) bl.fold(acc, part, sc);
+  }
   wait_lgkm();
   __builtin_amdgcn_s_barrier();
 }
@@ -436,11 +482,15 @@ __device__ __forceinline__ void mainloop_w4(char* lds, const ALd& al, const BLd&
                                             f32x16 (&acc)[Cfg::TM][Cfg::TN]) {
   using Ring = W4Ring<Cfg>;
   static_assert(ALd::kDMA && !BLd::kDMA, "X by direct copies, weights through registers");
-  constexpr int YOUNG = ALd::P + 3 * BLd::P;
+  constexpr int YOUNG = ALd::P + BLd::LOADS;
+  f32x16 part[Cfg::TM][Cfg::TN];
 #pragma unroll
   for (int i = 0; i < Cfg::TM; ++i)
 #pragma unroll
-    for (int j = 0; j < Cfg::TN; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < Cfg::TN; ++j) {
+      acc[i][j] = f32x16{};
+      part[i][j] = f32x16{};
+    }
   // the previous tile's epilogue may still be reading the stages
   __builtin_amdgcn_s_barrier();
   if (nk <= 0) return;
@@ -466,8 +516,8 @@ __device__ __forceinline__ void mainloop_w4(char* lds, const ALd& al, const BLd&
   __builtin_amdgcn_s_barrier();
   // two k-tiles per trip so each register set keeps a fixed name
   for (int kt = 0; kt < nk; kt += 2) {
-    w4_step<Cfg, DT>(lds, al, bl, kt, nk, r0, r1, ad, acc, fa, fb);
-    if (kt + 1 < nk) w4_step<Cfg, DT>(lds, al, bl, kt + 1, nk, r1, r0, ad, acc, fa, fb);
+    w4_step<Cfg, DT>(lds, al, bl, kt, nk, r0, r1, ad, acc, part, fa, fb);
+    if (kt + 1 < nk) w4_step<Cfg, DT>(lds, al, bl, kt + 1, nk, r1, r0, ad, acc, part, fa, fb);
   }
   // copies and loads past the last k-tile are still landing: drain them
   // before anyone reuses the stages
@@ -577,17 +627,21 @@ static hipError_t launch_w4a16_dt(const W4Launch& a, hipStream_t stream) {
     return hipGetLastError();
   }
   const int cus = device_cu_count();
-  const bool big = w4_big_tiles(a.M, a.N, cus);
+  // bf16 keeps a second set of fp32 partial sums (exact integer weights,
+  // scaled per group), which fits the registers of the 128 x 128 tile only
+  const bool big = DT == DT_F16 && w4_big_tiles(a.M, a.N, cus);
   const int bm = big ? 256 : 128, bn = big ? 256 : 128;
   const int tiles_m = (a.M + bm - 1) / bm;
   const int total = tiles_m * ((a.N + bn - 1) / bn) * a.split;
   const int resident = cus * (big ? 1 : 2);
   int grid = (total + XCDS - 1) / XCDS * XCDS;
   if (grid > resident) grid = resident / XCDS * XCDS;
-  if (big)
-    hipLaunchKernelGGL((k_w4a16_tiled<W4Cfg256, DT>), dim3(grid), dim3(W4Cfg256::THREADS), 0, stream, a, tiles_m,
-                       total);
-  else
+  if constexpr (DT == DT_F16) {
+    if (big)
+      hipLaunchKernelGGL((k_w4a16_tiled<W4Cfg256, DT>), dim3(grid), dim3(W4Cfg256::THREADS), 0, stream, a, tiles_m,
+                         total);
+  }
+  if (!big)
     hipLaunchKernelGGL((k_w4a16_tiled<W4Cfg128, DT>), dim3(grid), dim3(W4Cfg128::THREADS), 0, stream, a, tiles_m,
                        total);
   if (a.split > 1) {

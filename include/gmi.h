@@ -236,12 +236,13 @@ typedef enum { GMI_W4_UINT4 = 0, GMI_W4_INT4 = 1 } gmi_w4_type;
  *                (the page's fp16 and bf16 activation / scale types).
  *   group_size   as for gmi_gemm_w4a16; ignored when scales == NULL.
  *   other arguments, layouts, workspace and errors as for gmi_gemm_w4a16.
- * Numerics: for M <= 32 the matrix instruction takes exact integer weights
- * and the scale multiplies each group's fp32 partial sum: v(q) - v(z) for
- * fp16; for bf16 the offset-binary nibble plus 128, with (128 + zero point)
- * times the group's activation sum taken off that partial sum.  Otherwise
- * every weight is first rounded to the activation type,
- * RN((v(q) - v(z)) * s).  fp32 accumulation; Y is rounded to nearest even. */
+ * Numerics: with bf16 activations, and with fp16 for M <= 32, the matrix
+ * instruction takes exact integer weights and the scale multiplies each
+ * group's fp32 partial sum: v(q) - v(z) (for the bf16 decode kernel the
+ * offset-binary nibble plus 128, with (128 + zero point) times the group's
+ * activation sum taken off that partial sum).  fp16 with M > 32 rounds every
+ * weight first, RN16((v(q) - v(z)) * s), as the page does.  fp32
+ * accumulation; Y is rounded to nearest even. */
 gmi_status gmi_gemm_mixed(int32_t M, int32_t N, int32_t K, gmi_dtype x_dtype, const void* X, int64_t ldx,
                           const uint8_t* w_prepacked, gmi_w4_type w_type, const void* scales, const uint8_t* zeros,
                           int32_t group_size, void* Y, int64_t ldy, void* workspace, size_t workspace_bytes,

@@ -4,13 +4,11 @@ activations, against the fp64 oracle.  The decode (M <= 32: one or two 16-row
 tiles), skinny (M <= 64) and tiled (larger M, also split over K) kernels are
 each covered.
 
-Tolerance: |d - ref| <= 1e-2 |ref| + 1e-2.  With bf16 activations the skinny
-and tiled kernels round every dequantised weight to bf16 before the multiply
-(as the page's bf16 conversion does), an error of up to half a bf16 ulp,
-2^-9 |w|, per weight; that adds at most 2^-9 sum_k |x_k w_k| to an output, and
-their bf16 bar adds twice that bound.  The decode kernel feeds the matrix
-instruction exact integer weights, so its results (M <= 32) keep the plain
-bar."""
+Tolerance: |d - ref| <= 1e-2 |ref| + 1e-2 for every kernel and type.  With
+bf16 activations every kernel feeds the matrix instruction exact integer
+weights (rounding each dequantised weight to bf16 instead, as the page's bf16
+conversion does, costs up to 2^-9 |w| per weight, which over K = 8192 terms
+reaches this bar) and applies the group scales to fp32 partial sums."""
 import numpy as np
 import pytest
 import torch
@@ -41,22 +39,8 @@ def _case(M, N, K, group, dtype, seed):
     return X, W, S, Z
 
 
-DECODE_ROWS = 32  # calls of at most this many rows run the exact-integer decode kernel
-
-
-def _check(got, ref, X, W, S, Z, N, K, group, dtype, w_type, mode, what):
-    if dtype == "f16" or X.shape[0] <= DECODE_ROWS:
-        check_close(got, ref, dtype, what)
-        return
-    w = oracle.dequant_mixed(W, S if mode != "direct" else None, Z if mode == "zero" else None, N, K, group, w_type,
-                             dtype)
-    mag = np.abs(oracle.decode(X, dtype)[:, :K]) @ np.abs(w).T
-    d = oracle.decode(got, dtype)
-    bad = ~(np.abs(d - ref) <= 1e-2 * np.abs(ref) + 1e-2 + 2.0**-8 * mag)
-    if bad.any():
-        i = tuple(np.argwhere(bad)[0])
-        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} outside tolerance; {i}: got {d[i]:.6g} "
-                             f"want {ref[i]:.6g} bound term {2.0**-8 * mag[i]:.3g}")
+def _check(got, ref, dtype, what):
+    check_close(got, ref, dtype, what)
 
 
 def _run(gmi, X, W, S, Z, M, N, K, group, dtype, w_type, mode, workspace=None, ldy_pad=8):
@@ -80,7 +64,7 @@ def test_mixed_modes(gmi, dtype, w_type, mode, M):
     N, K, group = 256, 1024, 128
     X, W, S, Z = _case(M, N, K, group, dtype, seed=M * 7 + len(mode))
     got, ref = _run(gmi, X, W, S, Z, M, N, K, group, dtype, w_type, mode)
-    _check(got, ref, X, W, S, Z, N, K, group, dtype, w_type, mode, f"mixed {dtype} {w_type} {mode} M={M}")
+    _check(got, ref, dtype, f"mixed {dtype} {w_type} {mode} M={M}")
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
@@ -89,8 +73,7 @@ def test_mixed_per_channel_int4_and_group_256(gmi, dtype):
     for group, M in ((1024, 8), (1024, 30), (1024, 96), (256, 20), (256, 33)):
         X, W, S, Z = _case(M, 128, 1024, group, dtype, seed=group + M)
         got, ref = _run(gmi, X, W, S, Z, M, 128, 1024, group, dtype, "int4", "zero")
-        _check(got, ref, X, W, S, Z, 128, 1024, group, dtype, "int4", "zero",
-               f"mixed {dtype} int4 group {group} M={M}")
+        _check(got, ref, dtype, f"mixed {dtype} int4 group {group} M={M}")
 
 
 def test_mixed_bf16_split_k(gmi):
@@ -100,7 +83,7 @@ def test_mixed_bf16_split_k(gmi):
     X, W, S, Z = _case(M, N, K, group, "bf16", seed=21)
     ws = torch.empty(gmi.w4a16_workspace_bytes(M, N, K), dtype=torch.uint8, device=dev())
     got, ref = _run(gmi, X, W, S, Z, M, N, K, group, "bf16", "int4", "scale", workspace=ws)
-    _check(got, ref, X, W, S, Z, N, K, group, "bf16", "int4", "scale", "mixed bf16 split-K")
+    _check(got, ref, "bf16", "mixed bf16 split-K")
 
 
 def test_mixed_f16_uint4_zero_mode_is_w4a16_bit_for_bit(gmi):
@@ -115,14 +98,20 @@ def test_mixed_f16_uint4_zero_mode_is_w4a16_bit_for_bit(gmi):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16)), M
 
 
-@pytest.mark.parametrize("M", [16, 128])
+@pytest.mark.parametrize("M", [16, 48, 128, 1024])
 def test_mixed_bf16_full_size_sampled(gmi, M):
-    # N = K = 8192, group 128, int4 with zero points: the decode kernel (M = 16) and the split tiled path
-    # (M = 128); the oracle on 24 sampled output columns
+    # N = K = 8192, group 128, int4 with zero points: the decode kernel (M = 16), the skinny kernel (M = 48),
+    # the tiled path split over K into fp32 partials (M = 128: 64 output tiles) and unsplit (M = 1024); the
+    # oracle on 24 sampled output columns.  Over K = 8192 terms, weights rounded to bf16 would miss the bar on
+    # some outputs of this size; the exact integer weights do not.
     N, K, group = 8192, 8192, 128
     X, W, S, Z = _case(M, N, K, group, "bf16", seed=M + 5)
     wpp = gmi.prepack_w4(bytes_to_dev(W), N, K)
-    Y = gmi.gemm_mixed(to_dev(X, "bf16"), wpp, to_dev(S, "bf16"), bytes_to_dev(Z), group, N, w_type="int4")
+    need = gmi.w4a16_workspace_bytes(M, N, K)
+    assert (need > 0) == (M == 128)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev()) if need else None
+    Y = gmi.gemm_mixed(to_dev(X, "bf16"), wpp, to_dev(S, "bf16"), bytes_to_dev(Z), group, N, w_type="int4",
+                       workspace=ws)
     torch.cuda.synchronize()
     cols = np.sort(np.random.default_rng(M).choice(N, 24, replace=False))
     got = Y.cpu().view(torch.int16).numpy().view(np.uint16)[:, cols]
@@ -135,7 +124,25 @@ def test_mixed_bf16_full_size_sampled(gmi, M):
     zs = zn[:, cols]
     Zs = (zs[:, 0::2] | (zs[:, 1::2] << 4)).astype(np.uint8)
     ref = oracle.mixed(X, Ws, Ss, Zs, len(cols), K, group, "int4", "bf16")
-    _check(got, ref, X, Ws, Ss, Zs, len(cols), K, group, "bf16", "int4", "zero", f"mixed bf16 8192^2 M={M}")
+    _check(got, ref, "bf16", f"mixed bf16 8192^2 M={M}")
+
+
+def test_mixed_bf16_long_k_near_zero_outputs(gmi):
+    # the outputs most sensitive to per-weight rounding are those whose exact value is near zero: at K = 8192
+    # the bar there is the absolute 1e-2, against a rounding noise of about 3e-3 per output had each weight
+    # been rounded to bf16; 128 rows x 256 columns through the split tiled path, every output checked
+    M, N, K, group = 128, 256, 8192, 128
+    X, W, S, Z = _case(M, N, K, group, "bf16", seed=77)
+    ws = torch.empty(gmi.w4a16_workspace_bytes(M, N, K), dtype=torch.uint8, device=dev())
+    got, ref = _run(gmi, X, W, S, Z, M, N, K, group, "bf16", "int4", "zero", workspace=ws)
+    assert (np.abs(ref) < 1e-2).sum() > 50
+    # the case has the power to tell: weights rounded once to bf16 (on the CPU, through the oracle's dequant)
+    # would put outputs outside the bar
+    w = oracle.dequant_mixed(W, S, Z, N, K, group, "int4", "bf16")
+    rounded = oracle.decode(X, "bf16") @ oracle.decode(oracle.round_to(w, "bf16"), "bf16").T
+    d = oracle.decode(oracle.round_to(rounded, "bf16"), "bf16")
+    assert (~(np.abs(d - ref) <= 1e-2 * np.abs(ref) + 1e-2)).sum() > 20
+    _check(got, ref, "bf16", "mixed bf16 K=8192 every output")
 
 
 # Outputs that fall exactly on, just above and just below the midpoint of two representable values: the
