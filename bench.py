@@ -318,6 +318,14 @@ def bench_conv(torch, gmi, gi, dev, out):
     tm = time_launches(torch, lambda i: gmi.conv2d_dgrad(sets[i][2], sets[i][1], 56, 56, pad=(1, 1), dx=sets[i][0],
                                                          workspace=wsd), R, 5)
     out["conv_dgrad_bf16"] = roof(2.0 * 100352 * 256 * 2304, ws, tm)
+    # the data gradient of the same layer at stride 2 (dy 32 x 28 x 28 x 256 back to 56 x 56): one launch per
+    # output phase, each with only the taps that reach it; FLOPs of the forward view (every tap of every dy pixel)
+    dy2 = [torch.empty((32, 28, 28, 256), dtype=torch.bfloat16, device=dev).normal_() for _ in range(R)]
+    tm = time_launches(torch, lambda i: gmi.conv2d_dgrad(dy2[i], sets[i][1], 56, 56, pad=(1, 1), stride=(2, 2),
+                                                         dx=sets[i][0], workspace=wsd), R, 5)
+    out["conv_dgrad_stride2_bf16"] = roof(2.0 * 32 * 28 * 28 * 256 * 2304, 2 * (32 * 28 * 28 * 256 + wf.size)
+                                          + 2 * x.size, tm)
+    del dy2
     # and its weight gradient (x and dy of the same shapes; transposes and the split sum included)
     dws = torch.empty((256, 3, 3, 256), dtype=torch.bfloat16, device=dev)
     wsw = torch.empty(gmi.conv2d_wgrad_workspace_bytes((32, 56, 56, 256), (32, 56, 56, 256), 3, 3, (1, 1)),
@@ -373,31 +381,10 @@ def bench_w4(torch, gmi, gi, dev, out):
     log("bench: W4A16 done")
 
 
-def bench_workloads(torch, gmi, gi, dev, args):
-    out = {}
-    # 1. grouped fp16, 4 groups, beta 0.5 (launch-latency bound)
-    probs = gi.grouped_f16()
-    As = [t16(torch, p["A"], torch.float16, dev) for p in probs]
-    Bs = [t16(torch, p["B"], torch.float16, dev) for p in probs]
-    Cs = [t16(torch, p["C"], torch.float16, dev) for p in probs]
-    Ds = [torch.empty((p["M"], p["N"]), dtype=torch.float16, device=dev) for p in probs]
-    table = gmi.make_problems(As, Bs, Cs, Ds)
-    wsb = torch.empty(gmi.workspace_bytes(4), dtype=torch.uint8, device=dev)
-    fl = sum(2.0 * p["M"] * p["N"] * p["K"] for p in probs)
-    by = sum(2 * (p["M"] * p["K"] + p["N"] * p["K"] + 2 * p["M"] * p["N"]) for p in probs)
-    tm = time_launches(torch, lambda i: gmi.gemm_grouped_raw(table, 4, gmi.GMI_F16, 1.0, 0.5, wsb), 1, 20)
-    out["grouped_f16_4groups"] = roof(fl, by, tm, bound="launch")
-    log("bench: grouped fp16 done")
-
-    counts, off = bench_moe(torch, gmi, gi, dev, out)
-
-    bench_w4(torch, gmi, gi, dev, out)
-
-    bench_moe_w4(torch, gmi, gi, dev, out)
-
-    bench_conv(torch, gmi, gi, dev, out)
-
-    # 6. fp8 (E4M3) inputs, bf16 results: the pointer-array headline shape and the MoE layer
+def bench_fp8(torch, gmi, gi, dev, out):
+    """fp8 (E4M3) inputs, bf16 results: the pointer-array headline shape and the MoE layer."""
+    counts = gi.moe_counts()
+    off = np.concatenate([[0], np.cumsum(counts)])
     A8, B8 = gi.ptr_array_f8(L=16)
     ws = 16 * (1024 * 1024 + 1024 * 1024 + 1024 * 1024 * 2)  # A, B fp8 read once; D bf16 written once
     R = copies_for(ws)
@@ -427,6 +414,33 @@ def bench_workloads(torch, gmi, gi, dev, args):
     del Bw, A, D
     torch.cuda.empty_cache()
     log("bench: fp8 done")
+
+
+def bench_workloads(torch, gmi, gi, dev, args):
+    out = {}
+    # 1. grouped fp16, 4 groups, beta 0.5 (launch-latency bound)
+    probs = gi.grouped_f16()
+    As = [t16(torch, p["A"], torch.float16, dev) for p in probs]
+    Bs = [t16(torch, p["B"], torch.float16, dev) for p in probs]
+    Cs = [t16(torch, p["C"], torch.float16, dev) for p in probs]
+    Ds = [torch.empty((p["M"], p["N"]), dtype=torch.float16, device=dev) for p in probs]
+    table = gmi.make_problems(As, Bs, Cs, Ds)
+    wsb = torch.empty(gmi.workspace_bytes(4), dtype=torch.uint8, device=dev)
+    fl = sum(2.0 * p["M"] * p["N"] * p["K"] for p in probs)
+    by = sum(2 * (p["M"] * p["K"] + p["N"] * p["K"] + 2 * p["M"] * p["N"]) for p in probs)
+    tm = time_launches(torch, lambda i: gmi.gemm_grouped_raw(table, 4, gmi.GMI_F16, 1.0, 0.5, wsb), 1, 20)
+    out["grouped_f16_4groups"] = roof(fl, by, tm, bound="launch")
+    log("bench: grouped fp16 done")
+
+    bench_moe(torch, gmi, gi, dev, out)
+
+    bench_w4(torch, gmi, gi, dev, out)
+
+    bench_moe_w4(torch, gmi, gi, dev, out)
+
+    bench_conv(torch, gmi, gi, dev, out)
+
+    bench_fp8(torch, gmi, gi, dev, out)
     return out
 
 
@@ -461,9 +475,12 @@ def main():
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the W4A16 decode workload (M = 16, N = K = 8192, g = 128) and print one line "
                          "for it (for the decode kernel's profiles)")
-    ap.add_argument("--only", choices=["moe", "moe_w4", "conv", "w4"],
+    ap.add_argument("--only", choices=["moe", "moe_w4", "conv", "w4", "fp8"],
                     help="time only the bf16 MoE layers, the 4-bit MoE layers, the conv layers or the W4A16 / mixed-input "
-                         "lines and print their lines (for those kernels' profiles)")
+                         "lines or the fp8 lines and print their lines (for those kernels' profiles)")
+    ap.add_argument("--no-clock-sample", action="store_true",
+                    help="skip the 1.5 s of back-to-back headline launches that sample the shader clock (for "
+                         "counter runs, which serialize every launch)")
     ap.add_argument("--copy-ref", action="store_true",
                     help="after the timed region, run one plain 256 MiB device copy (a known-size kernel that "
                          "calibrates hardware byte counters)")
@@ -489,7 +506,7 @@ def main():
         return
     if args.only:
         out = {}
-        {"moe": bench_moe, "moe_w4": bench_moe_w4, "conv": bench_conv, "w4": bench_w4}[args.only](torch, gmi, gi, dev, out)
+        {"moe": bench_moe, "moe_w4": bench_moe_w4, "conv": bench_conv, "w4": bench_w4, "fp8": bench_fp8}[args.only](torch, gmi, gi, dev, out)
         copy_ref(torch, dev, args)
         print(json.dumps(out), flush=True)
         return
@@ -503,7 +520,7 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"bench: headline {ms * 1e3:.1f} us/step (median of {tm['windows']} windows of {tm['launches_per_window']} "
         f"steps; {tm['min_ms'] * 1e3:.1f} to {tm['max_ms'] * 1e3:.1f}), {tflops:.1f} TFLOP/s")
-    clock = shader_clock(torch, fn, R)
+    clock = None if args.no_clock_sample else shader_clock(torch, fn, R)
     log(f"bench: shader clock under the headline load {clock}")
 
     result = {

@@ -320,8 +320,8 @@ def conv2d_fprop(x: torch.Tensor, w: torch.Tensor, pad=(0, 0), stride=(1, 1), di
 def conv2d_dgrad(dy: torch.Tensor, w: torch.Tensor, H: int, W: int, pad=(0, 0), dil=(1, 1), c_in=None, alpha=1.0,
                  beta=0.0, dx: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stride=(1, 1),
                  stream=None) -> torch.Tensor:
-    """Data gradient of conv2d_fprop: dy NPQK, w KRSC, the forward input's H, W -> dx NHWC (stride 1, 2, 4 or
-    8, the same in both dimensions)."""
+    """Data gradient of conv2d_fprop: dy NPQK, w KRSC, the forward input's H, W -> dx NHWC (strides 1 .. 8 in
+    each dimension)."""
     N, P, Q, K = dy.shape
     K2, R, S, C = w.shape
     if K2 != K:

@@ -89,6 +89,10 @@ static int choose_shape(F tiles_at) {
 
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+int conv_shape(int64_t M, int64_t N) {
+  return choose_shape([&](int bm, int bn) { return cdiv(M, bm) * cdiv(N, bn); });
+}
+
 // Scratch of the allocation-free grouped call (gmi_gemm_grouped_offsets_noalloc):
 // what gmi_gemm_grouped_offsets keeps in the caller's workspace -- the tile
 // total in the header, then one descriptor per group -- for the largest
@@ -602,8 +606,8 @@ gmi_status gmi_conv2d_dgrad_implicit(int32_t N, int32_t H, int32_t W, int32_t C,
     return fail(GMI_ERR_INVALID_ARG, "%s: sizes must be positive (N >= 0)", who);
   if (pad_h < 0 || pad_w < 0 || stride_h < 1 || stride_w < 1 || dil_h < 1 || dil_w < 1)
     return fail(GMI_ERR_INVALID_ARG, "%s: padding >= 0, stride >= 1 and dilation >= 1 required", who);
-  if (stride_h != stride_w || (stride_h != 1 && stride_h != 2 && stride_h != 4 && stride_h != 8))
-    return fail(GMI_ERR_UNSUPPORTED, "%s: the traversal stride must be 1, 2, 4 or 8 in both dimensions", who);
+  if (stride_h > 8 || stride_w > 8)
+    return fail(GMI_ERR_UNSUPPORTED, "%s: the traversal stride must be in [1, 8]", who);
   if (!dtype_ok(dtype)) return fail(GMI_ERR_UNSUPPORTED, "%s: dtype %d not supported", who, (int)dtype);
   if (C % 8 || K % 8) return fail(GMI_ERR_MISALIGNED, "%s: C and K must be multiples of 8", who);
   const int64_t Ph = (int64_t)H + 2 * (int64_t)pad_h - (int64_t)dil_h * (R - 1) - 1;
@@ -611,8 +615,10 @@ gmi_status gmi_conv2d_dgrad_implicit(int32_t N, int32_t H, int32_t W, int32_t C,
   if (Ph < 0 || Qw < 0) return fail(GMI_ERR_INVALID_ARG, "%s: the filter does not fit the padded image", who);
   const int64_t P = Ph / stride_h + 1, Q = Qw / stride_w + 1;
   if ((int64_t)N * H * W > INT32_MAX || (int64_t)N * P * Q > INT32_MAX || (int64_t)R * S * K > kMaxLd ||
-      (int64_t)N * P * Q * K * 2 > INT32_MAX || C > kMaxLd)
-    return fail(GMI_ERR_UNSUPPORTED, "%s: dy above 2^31 bytes, R*S*K above 2^22 or too many pixels", who);
+      (int64_t)N * P * Q * K * 2 > INT32_MAX || C > kMaxLd ||
+      ((stride_h > 1 || stride_w > 1) && (int64_t)N * H * W * C * 2 > INT32_MAX))
+    return fail(GMI_ERR_UNSUPPORTED,
+                "%s: dy (or, for a stride above 1, dx) above 2^31 bytes, R*S*K above 2^22 or too many pixels", who);
   if (N == 0) return GMI_OK;
   const bool use_c = beta != 0.0f;
   if (!dy || !w || !dx || (use_c && !c_in)) return fail(GMI_ERR_INVALID_ARG, "%s: NULL pointer", who);
@@ -642,10 +648,7 @@ gmi_status gmi_conv2d_dgrad_implicit(int32_t N, int32_t H, int32_t W, int32_t C,
   a.sw = stride_w;
   a.dh = dil_h;
   a.dw = dil_w;
-  const int64_t Mg = (int64_t)N * H * W;
-  const int shape = choose_shape([&](int bm, int bn) { return cdiv(Mg, bm) * cdiv(C, bn); });
-  return hip_status(launch_conv_dgrad(a, (uint16_t*)workspace, shape, (int)dtype, alpha, beta, (hipStream_t)stream),
-                    who);
+  return hip_status(launch_conv_dgrad(a, (uint16_t*)workspace, (int)dtype, alpha, beta, (hipStream_t)stream), who);
 }
 
 // the forward pass, with or without the fused epilogue (bias NULL and act 0)

@@ -275,6 +275,21 @@ struct Tile {
 };
 constexpr int ACT_NONE = 0, ACT_RELU = 1;
 
+// Output rows that are the pixels of a strided grid inside a larger
+// channel-innermost tensor (one phase of the strided data gradient): GEMM row
+// m = (n Hp + i) Wp + j is stored, and C read, at element
+// off0 + n img + i rstep + j cstep (the row's N elements contiguous from
+// there), inside a tensor of `bytes` bytes that starts at the tile's D (C).
+struct RowMap {
+  int Hp, Wp;
+  int64_t off0, img, rstep, cstep;
+  uint32_t bytes;
+  __device__ __forceinline__ uint32_t offset(int m) const {
+    const int n = m / (Hp * Wp), r = m - n * Hp * Wp, i = r / Wp, j = r - i * Wp;
+    return (uint32_t)(off0 + n * img + i * rstep + j * cstep);
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Dense K-contiguous operand (direct to LDS): ROWS rows x BK k per k-tile
 // through a buffer resource spanning exactly the tile's rows inside the
@@ -369,11 +384,6 @@ struct ConvGeom {
   int P, Q;
   int ph, pw, sh, sw, dh, dw;
   int Kg;  // R * S * C
-  // Zero insertion (the strided data gradient): the gather addresses a
-  // virtual input of Hv x Wv pixels in which only coordinates divisible by
-  // 2^ush hold data, pixel (h, w) of x at (h << ush, w << ush).  ush = 0,
-  // Hv = H, Wv = W for the forward pass.
-  int Hv, Wv, ush;
   // k-tile order.  prs = 0: the GEMM's own order, taps (r, s) outer and
   // channels inner.  prs = R * S (only when C is a whole number pcb of
   // k-tiles): loop step t takes channel block t / prs of tap t % prs, so the
@@ -397,7 +407,7 @@ struct ConvLoader {
   static constexpr int P = ROWS * Cfg::ROWB / (1024 * Cfg::NW);
   static_assert(P >= 1 && ROWS % (Cfg::NW * Cfg::RPI) == 0, "rows must fill whole copy passes");
   rsrc_t rs;
-  int H, W, C, S, dh, dw, Kg, Hv, Wv, ush, umask, kt0, prs, pcb;
+  int H, W, C, S, dh, dw, Kg, kt0, prs, pcb;
   int pix[P];        // first pixel of the row's image: n * H * W
   int h0[P], w0[P];  // (virtual) input coordinates of tap (0, 0); far negative for rows past M
 
@@ -407,10 +417,6 @@ struct ConvLoader {
     kt0 = kt_first;
     H = g.H;
     W = g.W;
-    Hv = g.Hv;
-    Wv = g.Wv;
-    ush = g.ush;
-    umask = (1 << g.ush) - 1;
     C = g.C;
     S = g.S;
     dh = g.dh;
@@ -451,8 +457,8 @@ struct ConvLoader {
   }
   __device__ __forceinline__ void issue_one(int i, const Prep& p, char* tile) const {
     const int ih = h0[i] + p.dr, iw = w0[i] + p.ds;
-    const bool in = p.kin && (unsigned)ih < (unsigned)Hv && (unsigned)iw < (unsigned)Wv && ((ih | iw) & umask) == 0;
-    dma16(rs, in ? (uint32_t)((pix[i] + (ih >> ush) * W + (iw >> ush)) * C + p.c) * 2u : OOB,
+    const bool in = p.kin && (unsigned)ih < (unsigned)H && (unsigned)iw < (unsigned)W;
+    dma16(rs, in ? (uint32_t)((pix[i] + ih * W + iw) * C + p.c) * 2u : OOB,
           Cfg::dma_dst(tile, i));
   }
   __device__ __forceinline__ void issue(int kt, char* tile) const {
@@ -1104,9 +1110,9 @@ __device__ __forceinline__ void store_partial(const Tile& t, const f32x16 (&acc)
       }
 }
 
-template <class Cfg, int DT>
+template <class Cfg, int DT, bool MAPPED = false>
 __device__ __forceinline__ void store_tile(const Tile& t, const f32x16 (&acc)[Cfg::TM][Cfg::TN], float alpha,
-                                           float beta, char* lds) {
+                                           float beta, char* lds, const RowMap& map = RowMap{}) {
   constexpr int ROWB = Cfg::WTN * 4;  // fp32 row of the wave tile
   constexpr int PASS = (Cfg::NW * 2 * 32 * ROWB <= Cfg::LDS_BYTES) ? 2 : 1;  // 32-row blocks per pass
   constexpr int REGION = PASS * 32 * ROWB;
@@ -1131,9 +1137,23 @@ __device__ __forceinline__ void store_tile(const Tile& t, const f32x16 (&acc)[Cf
   if (rows > Cfg::BM) rows = Cfg::BM;
   const bool use_c = beta != 0.0f;
   const bool full_n = t.n0 + Cfg::BN <= t.N;
-  const rsrc_t rd = make_rsrc(t.D + (int64_t)t.m0 * t.ldd, (uint32_t)rows * (uint32_t)t.ldd * 2u);
-  const rsrc_t rc = use_c ? make_rsrc(t.C + (int64_t)t.m0 * t.ldc, (uint32_t)rows * (uint32_t)t.ldc * 2u) : rd;
+  // plain rows: resources from the tile's first row, row pitch ld, rows past
+  // M outside the range; mapped rows: resources over the whole tensor, each
+  // row at its mapped offset, rows past M pointed out of range
+  const rsrc_t rd = MAPPED ? make_rsrc(t.D, map.bytes)
+                           : make_rsrc(t.D + (int64_t)t.m0 * t.ldd, (uint32_t)rows * (uint32_t)t.ldd * 2u);
+  const rsrc_t rc = !use_c ? rd
+                    : MAPPED ? make_rsrc(t.C, map.bytes)
+                             : make_rsrc(t.C + (int64_t)t.m0 * t.ldc, (uint32_t)rows * (uint32_t)t.ldc * 2u);
   const uint32_t ldd2 = (uint32_t)t.ldd * 2u, ldc2 = (uint32_t)t.ldc * 2u;
+  auto row_d = [&](uint32_t row) -> uint32_t {
+    if constexpr (MAPPED) return (int)row < rows ? map.offset(t.m0 + (int)row) * 2u : OOB;
+    return row * ldd2;
+  };
+  auto row_c = [&](uint32_t row) -> uint32_t {
+    if constexpr (MAPPED) return (int)row < rows ? map.offset(t.m0 + (int)row) * 2u : OOB;
+    return row * ldc2;
+  };
   const bool use_bias = t.bias != nullptr, relu = t.act == ACT_RELU;
   const rsrc_t rbias = use_bias ? make_rsrc(t.bias, (uint32_t)t.N * 2u) : rd;
 
@@ -1160,10 +1180,11 @@ __device__ __forceinline__ void store_tile(const Tile& t, const f32x16 (&acc)[Cf
       float v[8] = {alpha * a0[0], alpha * a0[1], alpha * a0[2], alpha * a0[3],
                     alpha * a1[0], alpha * a1[1], alpha * a1[2], alpha * a1[3]};
       const uint32_t row = (uint32_t)(wm + p0 * 32 + r);
+      const uint32_t od = row_d(row), oc = use_c ? row_c(row) : 0u;
       const int col = t.n0 + wn + 8 * c;
       if (full_n || col + 8 <= t.N) {
         if (use_c) {
-          const u32x4 c4 = buf_load16(rc, row * ldc2 + (uint32_t)col * 2u);
+          const u32x4 c4 = buf_load16(rc, oc + (uint32_t)col * 2u);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             v[2 * e] += beta * from_bits<DT>(c4[e] & 0xffffu);
@@ -1182,17 +1203,17 @@ __device__ __forceinline__ void store_tile(const Tile& t, const f32x16 (&acc)[Cf
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = v[e] > 0.0f ? v[e] : 0.0f;
         }
-        buf_store16(rd, row * ldd2 + (uint32_t)col * 2u,
+        buf_store16(rd, od + (uint32_t)col * 2u,
                     u32x4{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3]), pack2<DT>(v[4], v[5]), pack2<DT>(v[6], v[7])});
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           if (col + e < t.N) {
             float x = v[e];
-            if (use_c) x += beta * from_bits<DT>(buf_load2(rc, row * ldc2 + (uint32_t)(col + e) * 2u));
+            if (use_c) x += beta * from_bits<DT>(buf_load2(rc, oc + (uint32_t)(col + e) * 2u));
             if (use_bias) x += from_bits<DT>(buf_load2(rbias, (uint32_t)(col + e) * 2u));
             if (relu) x = x > 0.0f ? x : 0.0f;
-            buf_store2(rd, row * ldd2 + (uint32_t)(col + e) * 2u, to_bits<DT>(x));
+            buf_store2(rd, od + (uint32_t)(col + e) * 2u, to_bits<DT>(x));
           }
         }
       }

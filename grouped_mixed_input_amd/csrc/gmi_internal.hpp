@@ -64,7 +64,6 @@ struct ConvLaunch {
   const uint16_t* c;
   uint16_t* y;
   int N, H, W, C, K, R, S, P, Q, ph, pw, sh, sw, dh, dw;
-  int ush = 0;  // log2 of the zero insertion of the gathered input (data gradient of a strided pass)
   // split over the taps into fp32 partials (see k_conv_fprop); 1 / NULL: none
   int split = 1, kt_split = 1 << 30;
   float* partial = nullptr;
@@ -75,7 +74,16 @@ struct ConvLaunch {
   // and activation (0: none, 1: ReLU); unsplit launches only
   const uint16_t* bias = nullptr;
   int act = 0;
+  // output pixels on a strided grid of a larger NHWC tensor (one phase of the
+  // strided data gradient): pixel (n, i, j) of the N x P x Q grid goes to
+  // element map_off0 + n map_img + i map_rstep + j map_cstep of y (and c),
+  // a tensor of map_bytes bytes; map_bytes == 0: the plain NPQK layout
+  int64_t map_off0 = 0, map_img = 0, map_rstep = 0, map_cstep = 0;
+  uint32_t map_bytes = 0;
 };
+// tile shape of a convolution launch's GEMM view (M pixels, N channels),
+// by the rule of the GEMM calls
+int conv_shape(int64_t M, int64_t N);
 
 struct W4Launch {
   int M, N, K, group;
@@ -129,7 +137,7 @@ hipError_t launch_grouped_offsets(const OffsetsLaunch& p, int shape, int dtype, 
 hipError_t launch_ptr_array(const PtrArrayLaunch& a, int shape, int dtype, float alpha, float beta,
                             hipStream_t stream);
 hipError_t launch_conv_fprop(const ConvLaunch& a, int shape, int dtype, float alpha, float beta, hipStream_t stream);
-hipError_t launch_conv_dgrad(const ConvLaunch& a, uint16_t* wt, int shape, int dtype, float alpha, float beta,
+hipError_t launch_conv_dgrad(const ConvLaunch& a, uint16_t* wt, int dtype, float alpha, float beta,
                              hipStream_t stream);
 
 // Weight gradient as a forward pass over transposed operands (see

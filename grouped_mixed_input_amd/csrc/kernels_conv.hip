@@ -34,11 +34,13 @@ struct ConvArgs {
   // fused epilogue (see Tile): per-output-channel bias, activation
   const uint16_t* bias;
   int act;
+  // output rows on a strided pixel grid (MAPPED launches)
+  RowMap map;
 };
 
 // Tile ids run n-tile fastest: the few n-tiles of a pixel block are
 // consecutive, so one XCD gathers each activation panel once into its L2.
-template <class Cfg, int DT>
+template <class Cfg, int DT, bool MAPPED>
 __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_conv_fprop(ConvArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
   const int G = gridDim.x;
@@ -76,7 +78,7 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_conv_fprop(Co
     if (a.partial)
       store_partial<Cfg>(t, acc, a.partial + grp * a.part_group + (int64_t)sidx * a.M * a.Nk);
     else
-      store_tile<Cfg, DT>(t, acc, a.alpha, a.beta, lds);
+      store_tile<Cfg, DT, MAPPED>(t, acc, a.alpha, a.beta, lds, a.map);
   }
 }
 
@@ -99,8 +101,6 @@ hipError_t launch_conv_fprop(const ConvLaunch& p, int shape, int dtype, float al
                  p.sh,  p.sw,
                  p.dh,  p.dw,
                  p.R * p.S * p.C,
-                 ((p.H - 1) << p.ush) + 1, ((p.W - 1) << p.ush) + 1,
-                 p.ush,
                  0,     0};
   // channel-block-major k order when the channels fill whole k-tiles and the
   // launch is not split over k (a split keeps each range's taps together)
@@ -128,56 +128,75 @@ hipError_t launch_conv_fprop(const ConvLaunch& p, int shape, int dtype, float al
   a.part_group = p.part_group;
   a.bias = p.bias;
   a.act = p.act;
+  const bool mapped = p.map_bytes > 0;
+  a.map = RowMap{p.P, p.Q, p.map_off0, p.map_img, p.map_rstep, p.map_cstep, p.map_bytes};
   const int resident = device_cu_count() * tile_wgs_per_cu(shape);
   int grid = (a.total_tiles * a.split * a.groups + XCDS - 1) / XCDS * XCDS;
   if (grid > resident) grid = resident / XCDS * XCDS;
   if (grid < XCDS) grid = XCDS;
-  if (shape == TILE_256x256) {
-    if (dtype == DT_F16)
-      hipLaunchKernelGGL((k_conv_fprop<ConvCfg256, DT_F16>), dim3(grid), dim3(ConvCfg256::THREADS), 0, stream, a);
-    else
-      hipLaunchKernelGGL((k_conv_fprop<ConvCfg256, DT_BF16>), dim3(grid), dim3(ConvCfg256::THREADS), 0, stream, a);
-  } else if (shape == TILE_256x128) {
-    if (dtype == DT_F16)
-      hipLaunchKernelGGL((k_conv_fprop<ConvCfg256x128, DT_F16>), dim3(grid), dim3(ConvCfg256x128::THREADS), 0, stream, a);
-    else
-      hipLaunchKernelGGL((k_conv_fprop<ConvCfg256x128, DT_BF16>), dim3(grid), dim3(ConvCfg256x128::THREADS), 0, stream, a);
-  } else {
-    if (dtype == DT_F16)
-      hipLaunchKernelGGL((k_conv_fprop<ConvCfg128, DT_F16>), dim3(grid), dim3(ConvCfg128::THREADS), 0, stream, a);
-    else
-      hipLaunchKernelGGL((k_conv_fprop<ConvCfg128, DT_BF16>), dim3(grid), dim3(ConvCfg128::THREADS), 0, stream, a);
-  }
+#define GMI_CONV_LAUNCH(CFG)                                                                              \
+  do {                                                                                                    \
+    if (dtype == DT_F16) {                                                                                \
+      if (mapped) hipLaunchKernelGGL((k_conv_fprop<CFG, DT_F16, true>), dim3(grid), dim3(CFG::THREADS), 0, stream, a);   \
+      else hipLaunchKernelGGL((k_conv_fprop<CFG, DT_F16, false>), dim3(grid), dim3(CFG::THREADS), 0, stream, a);        \
+    } else {                                                                                              \
+      if (mapped) hipLaunchKernelGGL((k_conv_fprop<CFG, DT_BF16, true>), dim3(grid), dim3(CFG::THREADS), 0, stream, a);  \
+      else hipLaunchKernelGGL((k_conv_fprop<CFG, DT_BF16, false>), dim3(grid), dim3(CFG::THREADS), 0, stream, a);       \
+    }                                                                                                     \
+  } while (0)
+  if (shape == TILE_256x256)
+    GMI_CONV_LAUNCH(ConvCfg256);
+  else if (shape == TILE_256x128)
+    GMI_CONV_LAUNCH(ConvCfg256x128);
+  else
+    GMI_CONV_LAUNCH(ConvCfg128);
+#undef GMI_CONV_LAUNCH
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// Data gradient.  The page runs the non-strided dgrad through the same
-// im2col operand with the filter-tap strides negated: dx[n][h][w][c] sums
-// dy[n][h + ph - r dh][w + pw - s dw][k] w[k][r][s][c], which is the forward
-// gather over dy with padding -ph and dilation -dh.  A forward stride s
-// (a power of two here) puts dy on every s-th coordinate of a virtual
-// zero-inserted image, dy[n][p][q] at (s p, s q): the same gather, which
-// reads only coordinates divisible by s (the others are zeros, and their
-// products are wasted matrix work, a factor s^2).  The GEMM's B operand is
-// the filter with its reduction (r, s, k) contiguous per column c, i.e. w
-// transposed to [C][R][S][K].
+// Data gradient, the page's dgrad operator:
+//   dx[n][h][w][c] = sum over (p, q, k, r, s) with p sh - ph + r dh = h and
+//                    q sw - pw + s dw = w of dy[n][p][q][k] w[k][r][s][c].
+// For stride 1 the page runs it through the same im2col operand with the
+// filter-tap strides negated: the forward gather over dy with padding -ph and
+// dilation -dh.  For a stride s > 1 the page's strided dgrad walks, for each
+// output pixel, only the taps that reach it: p = (h + ph - r dh) / s must be
+// an integer, so the taps of output row h are those with r dh = h + ph
+// (mod s).  The rows h with h + ph = a (mod s) form one phase; its taps are
+// r = r_a + t s / g (g = gcd(dh, s), r_a the first), and with h = a - ph +
+// s (lo + i) the tap t reads dy row p = i + shift - t dh / g.  So each phase
+// is a stride-1 forward gather over dy with padding -shift and dilation
+// -dh / g over its own slice of the filter, writing the strided grid of dx
+// pixels of that phase; the phases partition both the dx pixels and the
+// taps, so no multiply touches a tap that misses.  Each dimension splits
+// this way; a phase with pixels but no taps writes beta C (or zeros).
+// The GEMM's B operand is each phase's filter slice with its reduction
+// (t, u, k) contiguous per column c: [C][taps][K].
 // ---------------------------------------------------------------------------
-// out[c][b][a] = in[a][b][c] for a < A, 0 for A <= a < Ap: one 64 x 64 (a, c)
-// block of one b per workgroup (b in grid z, looping past 65535), moved in
-// 16-byte runs: 8 consecutive c on the way in, 8 consecutive a on the way out
-// (C % 8 == 0 and Ap % 8 == 0).
+// The filter taps of one phase: output tap b (of the phase's Rp x Sp, row
+// major) is input tap (r0 + (b / Sp) rstep) S + s0 + (b % Sp) sstep.
+struct TapMap {
+  int Sp, r0, rstep, s0, sstep, S;
+  __device__ __forceinline__ int operator()(int b) const { return (r0 + (b / Sp) * rstep) * S + s0 + (b % Sp) * sstep; }
+};
+
+// out[c][b][a] = in[a][taps(b)][c] for a < A, 0 for A <= a < Ap (in holds
+// Bin taps per a, out Bout): one 64 x 64 (a, c) block of one b per workgroup
+// (b in grid z, looping past 65535), moved in 16-byte runs: 8 consecutive c
+// on the way in, 8 consecutive a on the way out (C % 8 == 0, Ap % 8 == 0).
 __global__ __launch_bounds__(256) void k_transpose_outer(const uint16_t* __restrict__ in, uint16_t* __restrict__ out,
-                                                         int A, int B, int C, int Ap) {
+                                                         int A, int Bin, int Bout, int C, int Ap, TapMap taps) {
   __shared__ uint16_t t[64][72];
   const int a0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   const int row = threadIdx.x / 8, vec = threadIdx.x % 8;
-  for (int b = blockIdx.z; b < B; b += gridDim.z) {
+  for (int b = blockIdx.z; b < Bout; b += gridDim.z) {
+    const int bi = taps(b);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int aa = row + 32 * j, a = a0 + aa, c = c0 + vec * 8;
       u32x4 v = {0, 0, 0, 0};
-      if (a < A && c < C) v = *(const u32x4*)(in + ((int64_t)a * B + b) * C + c);
+      if (a < A && c < C) v = *(const u32x4*)(in + ((int64_t)a * Bin + bi) * C + c);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         t[aa][vec * 8 + 2 * e] = (uint16_t)(v[e] & 0xffffu);
@@ -192,48 +211,109 @@ __global__ __launch_bounds__(256) void k_transpose_outer(const uint16_t* __restr
         u32x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = (uint32_t)t[vec * 8 + 2 * e][cc] | ((uint32_t)t[vec * 8 + 2 * e + 1][cc] << 16);
-        *(u32x4*)(out + ((int64_t)c * B + b) * Ap + a) = v;
+        *(u32x4*)(out + ((int64_t)c * Bout + b) * Ap + a) = v;
       }
     }
     __syncthreads();
   }
 }
 
+// out[c][b][a] = in[a][b][c], every tap in order
 static hipError_t transpose_outer(const uint16_t* in, uint16_t* out, int A, int B, int C, int Ap,
-                                  hipStream_t stream) {
+                                  hipStream_t stream, TapMap taps = TapMap{1 << 30, 0, 0, 0, 1, 1}, int Bin = -1) {
   const dim3 grid((C + 63) / 64, (Ap + 63) / 64, B < 65535 ? B : 65535);
-  hipLaunchKernelGGL(k_transpose_outer, grid, dim3(256), 0, stream, in, out, A, B, C, Ap);
+  hipLaunchKernelGGL(k_transpose_outer, grid, dim3(256), 0, stream, in, out, A, Bin < 0 ? B : Bin, B, C, Ap, taps);
   return hipGetLastError();
 }
 
-hipError_t launch_conv_dgrad(const ConvLaunch& p, uint16_t* wt, int shape, int dtype, float alpha, float beta,
+static int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }  // b > 0
+static int gcd_int(int a, int b) {
+  while (b) {
+    const int t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
+}
+
+// One dimension of one phase: output rows h = a - pad + stride (lo + i),
+// i < size; taps first + t step, t < count; tap t of row i reads input row
+// i + shift - t (dil / gcd(dil, stride)).
+struct Phase1D {
+  int first, step, count, lo, size, shift, dil;
+};
+static Phase1D phase_1d(int a, int R, int pad, int stride, int dil, int H) {
+  Phase1D p;
+  const int g = gcd_int(dil, stride);
+  p.step = stride / g;
+  p.dil = dil / g;
+  p.first = -1;
+  for (int r = 0; r < R && r < p.step; ++r)
+    if ((r * dil) % stride == a) {
+      p.first = r;
+      break;
+    }
+  p.count = p.first < 0 ? 0 : (R - 1 - p.first) / p.step + 1;
+  p.lo = -floor_div(a - pad, stride);  // the first i with a - pad + stride i >= 0
+  const int last = floor_div(H - 1 - a + pad, stride);
+  p.size = last >= p.lo ? last - p.lo + 1 : 0;
+  p.shift = p.first < 0 ? 0 : p.lo + (a - p.first * dil) / stride;  // an exact quotient
+  return p;
+}
+
+hipError_t launch_conv_dgrad(const ConvLaunch& p, uint16_t* wt, int dtype, float alpha, float beta,
                              hipStream_t stream) {
   // p describes the forward problem (x: N x H x W x C, y: N x P x Q x K);
-  // here p.x is dy, p.y is dx
-  const hipError_t e = transpose_outer(p.w, wt, p.K, p.R * p.S, p.C, p.K, stream);
-  if (e != hipSuccess) return e;
-  ConvLaunch f;  // the forward view: gather over dy, filter [C][R][S][K]
-  f.x = p.x;
-  f.w = wt;
-  f.c = p.c;
-  f.y = p.y;
-  f.N = p.N;
-  f.H = p.P;
-  f.W = p.Q;
-  f.C = p.K;
-  f.K = p.C;
-  f.R = p.R;
-  f.S = p.S;
-  f.P = p.H;
-  f.Q = p.W;
-  f.ph = -p.ph;
-  f.pw = -p.pw;
-  f.sh = 1;
-  f.sw = 1;
-  f.dh = -p.dh;
-  f.dw = -p.dw;
-  f.ush = p.sh == 1 ? 0 : p.sh == 2 ? 1 : p.sh == 4 ? 2 : 3;  // sh == sw, a power of two
-  return launch_conv_fprop(f, shape, dtype, alpha, beta, stream);
+  // here p.x is dy, p.y is dx and p.c the dx-shaped C
+  const bool strided = p.sh > 1 || p.sw > 1;
+  int64_t woff = 0;  // the phases' filter slices, one after another
+  for (int a = 0; a < p.sh; ++a) {
+    const Phase1D ph = phase_1d(a, p.R, p.ph, p.sh, p.dh, p.H);
+    if (ph.size == 0) continue;
+    for (int b = 0; b < p.sw; ++b) {
+      const Phase1D pw = phase_1d(b, p.S, p.pw, p.sw, p.dw, p.W);
+      if (pw.size == 0) continue;
+      uint16_t* wp = wt + woff;
+      const int taps = ph.count * pw.count;
+      if (taps > 0) {
+        const hipError_t e = transpose_outer(p.w, wp, p.K, taps, p.C, p.K, stream,
+                                             TapMap{pw.count, ph.first, ph.step, pw.first, pw.step, p.S}, p.R * p.S);
+        if (e != hipSuccess) return e;
+        woff += (int64_t)taps * p.C * p.K;
+      }
+      ConvLaunch f;  // the phase's forward view: a gather over dy, its filter slice [C][taps][K]
+      f.x = p.x;
+      f.w = wp;
+      f.c = p.c;
+      f.y = p.y;
+      f.N = p.N;
+      f.H = p.P;
+      f.W = p.Q;
+      f.C = p.K;
+      f.K = p.C;
+      f.R = ph.count;
+      f.S = pw.count;
+      f.P = ph.size;
+      f.Q = pw.size;
+      f.ph = -ph.shift;
+      f.pw = -pw.shift;
+      f.sh = 1;
+      f.sw = 1;
+      f.dh = -ph.dil;
+      f.dw = -pw.dil;
+      if (strided) {
+        f.map_off0 = ((int64_t)(a - p.ph + p.sh * ph.lo) * p.W + (b - p.pw + p.sw * pw.lo)) * p.C;
+        f.map_img = (int64_t)p.H * p.W * p.C;
+        f.map_rstep = (int64_t)p.sh * p.W * p.C;
+        f.map_cstep = (int64_t)p.sw * p.C;
+        f.map_bytes = (uint32_t)((int64_t)p.N * p.H * p.W * p.C * 2);
+      }
+      const hipError_t e =
+          launch_conv_fprop(f, conv_shape((int64_t)p.N * ph.size * pw.size, p.C), dtype, alpha, beta, stream);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------

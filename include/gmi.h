@@ -375,16 +375,20 @@ gmi_status gmi_conv2d_wgrad_implicit(int32_t N, int32_t H, int32_t W, int32_t C,
  * w KRSC, dy is N x P x Q x K with P, Q as for the forward pass; dx and c_in
  * are NHWC.  As on the page, dgrad gathers dy through the im2col addressing
  * with the filter-tap strides negated (padding -ph and dilation -dh over
- * dy); the GEMM view is M = N*H*W, N = C, K = R*S*K.  A forward stride s
- * places dy on every s-th coordinate of a zero-inserted image that the same
- * gather reads; the skipped coordinates cost matrix work (a factor s^2 over
- * the stride-1 cost), unlike the page's separate strided-dgrad operator.
+ * dy); the GEMM view is M = N*H*W, N = C, K = R*S*K.  A forward stride above
+ * 1 runs the page's strided dgrad: the dx pixels split into sh x sw phases
+ * (rows h with h + ph in one residue class of sh, crossed with the columns'
+ * classes), and each phase gathers dy over only the taps that reach it
+ * (r*dh = h + ph mod sh), so no multiply touches a tap that misses; a phase
+ * that no tap reaches gets alpha * 0 + beta * c_in.
  *   workspace  at least gmi_conv2d_dgrad_workspace_bytes(C, K, R, S) bytes,
- *              16-byte aligned: a first launch writes the filter there as
- *              [C][R][S][K], the GEMM launch reads it.
- * The traversal stride must be 1, 2, 4 or 8 and equal in both dimensions,
- * else GMI_ERR_UNSUPPORTED.  Other rules as for the forward pass: C % 8 == 0
- * and K % 8 == 0, 16-byte aligned pointers, c_in NULL iff beta == 0. */
+ *              16-byte aligned: the filter rearranged per phase, [C][taps of
+ *              the phase][K], one phase after another (the phases partition
+ *              the taps), written and read by the call's launches.
+ * Traversal strides in [1, 8] in each dimension, else GMI_ERR_UNSUPPORTED;
+ * for a stride above 1, dx must stay below 2^31 bytes.  Other rules as for
+ * the forward pass: C % 8 == 0 and K % 8 == 0, 16-byte aligned pointers, c_in
+ * NULL iff beta == 0. */
 gmi_status gmi_conv2d_dgrad_implicit(int32_t N, int32_t H, int32_t W, int32_t C, int32_t K, int32_t R, int32_t S,
                                      int32_t pad_h, int32_t pad_w, int32_t stride_h, int32_t stride_w,
                                      int32_t dil_h, int32_t dil_w, const void* dy, const void* w, const void* c_in,
