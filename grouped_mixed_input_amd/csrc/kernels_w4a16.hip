@@ -14,6 +14,8 @@
 //   * k_w4a16_tiled (M > 64) is the dense mainloop with the weight loader
 //     (W4Loader) dequantising into the LDS B tile.
 
+#include <type_traits>
+
 #include "gmi_device.hpp"
 #include "gmi_internal.hpp"
 
@@ -417,70 +419,84 @@ __global__ __launch_bounds__(64 * KW) void k_w4a16_decode(W4Launch a) {
 // X as the A operand, the prepacked weight (dequantised on its way into LDS)
 // as the column-major B operand.
 //
-// Mainloop of the tiled kernel: three X stages (direct-to-LDS copies) and two
-// weight stages (dequantised from registers into LDS), with the weight
-// registers double-buffered.  While k-tile kt is multiplied, the X copies and
-// weight loads of kt + 2 are issued and those of kt + 1 are still landing, so
-// every load has two stage times to arrive; the end of step kt waits for
-// k-tile kt + 1 only (the loads of kt + 2 are the younger ones), dequantises
-// its weights into the free weight stage and publishes both.  Every step
-// issues the same loads (past the last k-tile they re-read valid data or land
-// as zeros and are never multiplied), so the wait counts are fixed.
+// Mainloop of the tiled kernel, prefetch distance D: D + 1 X stages
+// (direct-to-LDS copies), two weight stages (dequantised from registers into
+// LDS) and D register sets of raw weights.  While k-tile kt is multiplied,
+// the X copies and weight loads of kt + D are issued and those of kt + 1 ..
+// kt + D - 1 are still landing, so every load has D stage times to arrive;
+// the end of step kt waits for k-tile kt + 1 only (the loads of kt + 2 ..
+// kt + D are the younger ones), dequantises its weights into the free weight
+// stage and publishes both.  Every step issues the same loads (past the last
+// k-tile they re-read valid data or land as zeros and are never multiplied),
+// so the wait counts are fixed.  D = 2 keeps two workgroups per CU.  (Deeper
+// rings, D = 4 and 6 at one workgroup per CU, measured the same at M = 128:
+// the k-steps there do not wait on load latency.)
 // ---------------------------------------------------------------------------
-template <class Cfg>
+template <class Cfg, int D>
 struct W4Ring {
-  static constexpr int A_STAGES = 3, B_STAGES = 2;
+  static constexpr int A_STAGES = D + 1, B_STAGES = 2;
   static constexpr int BYTES = A_STAGES * Cfg::A_BYTES + B_STAGES * Cfg::B_BYTES;
-  static_assert(BYTES <= 160 * 1024 && BYTES * Cfg::WGS_PER_CU <= 160 * 1024, "LDS budget");
+  static constexpr int WGS = D == 2 ? Cfg::WGS_PER_CU : 1;  // workgroups per CU
+  static_assert(D >= 2 && BYTES * WGS <= 160 * 1024, "LDS budget");
   __device__ static __forceinline__ char* a(char* lds, int s) { return lds + s * Cfg::A_BYTES; }
   __device__ static __forceinline__ char* b(char* lds, int s) {
     return lds + A_STAGES * Cfg::A_BYTES + s * Cfg::B_BYTES;
   }
 };
 
-// one k-tile: weights of kt + 2 into `rl`, multiply kt, then publish kt + 1
+template <int J, int D, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (J < D) {
+    f(std::integral_constant<int, J>{});
+    static_for<J + 1, D>(f);
+  }
+}
+
+// one k-tile: weights of kt + D into `rl`, multiply kt, then publish kt + 1
 // (X already copied, weights from `rs`).  With exact integer weights (bf16)
 // the multiply accumulates into `part`, which the last k-tile of each scale
-// group folds into `acc` with the group's scales.
-template <class Cfg, int DT, class ALd, class BLd>
+// group folds into `acc` with the group's scales `sc`; those are loaded one
+// step ahead, at the start of the step before the fold.
+template <class Cfg, int DT, int D, class ALd, class BLd>
 __device__ __forceinline__ void w4_step(char* lds, const ALd& al, const BLd& bl, int kt, int nk,
                                         typename BLd::Regs& rl, const typename BLd::Regs& rs, const FragAddr<Cfg>& ad,
                                         f32x16 (&acc)[Cfg::TM][Cfg::TN], f32x16 (&part)[Cfg::TM][Cfg::TN],
-                                        frag_t<Cfg> (&fa)[2][Cfg::TM], frag_t<Cfg> (&fb)[2][Cfg::TN]) {
-  using Ring = W4Ring<Cfg>;
+                                        u32x2 (&sc)[Cfg::TN][4], frag_t<Cfg> (&fa)[2][Cfg::TM],
+                                        frag_t<Cfg> (&fb)[2][Cfg::TN]) {
+  using Ring = W4Ring<Cfg, D>;
   constexpr int YOUNG = ALd::P + BLd::LOADS;  // one k-tile's copies and loads
+  static_assert((D - 1) * YOUNG < 64, "the k-tiles left in flight fit the vmcnt counter");
   // The wait below counts outstanding loads in issue order, and the compiler
   // does not track the direct-to-LDS copies: the fences keep every load and
-  // copy of k-tile kt + 2 between the previous step's wait and this one's.
-  // The scale loads of a fold are issued first, so they are older than every
-  // load the wait leaves in flight.
+  // copy of k-tile kt + D between the previous step's wait and this one's.
+  // Scale loads for the next step's fold go out first, before those of
+  // k-tile kt + D: the wait then only waits longer (it still leaves at most
+  // the (D - 1) YOUNG youngest in flight), and the next step's wait covers
+  // them, so the fold itself never waits on a load.
   __builtin_amdgcn_sched_barrier(0);
-  u32x2 sc[Cfg::TN][4];
-  bool fold = false;
   if constexpr (BLd::EXACT) {
-    fold = bl.group_ends(kt, nk);
-    if (fold) bl.fold_scales(kt, sc);
+    if (kt + 1 < nk && bl.group_ends(kt + 1, nk)) bl.fold_scales(kt + 1, sc);
   }
-  bl.load(kt + 2, rl);
-  const char* ca = Ring::a(lds, kt % 3);
+  bl.load(kt + D, rl);
+  const char* ca = Ring::a(lds, kt % (D + 1));
   const char* cb = Ring::b(lds, kt & 1);
   read_frags<Cfg>(ad, ca, cb, 0, fa[0], fb[0]);
-  multiply_stage<Cfg, DT, false, 2>(ad, ca, cb, ca, cb, BLd::EXACT ? part : acc, fa, fb, al, kt + 2,
-                                    Ring::a(lds, (kt + 2) % 3), bl, 0, nullptr);
+  multiply_stage<Cfg, DT, false, 2>(ad, ca, cb, ca, cb, BLd::EXACT ? part : acc, fa, fb, al, kt + D,
+                                    Ring::a(lds, (kt + D) % (D + 1)), bl, 0, nullptr);
   __builtin_amdgcn_sched_barrier(0);
-  wait_vm_le<YOUNG>();
+  wait_vm_le<(D - 1) * YOUNG>();
   if (kt + 1 < nk) bl.store(Ring::b(lds, (kt + 1) & 1), rs);
   if constexpr (BLd::EXACT) {
-    if (fold) bl.fold(acc, part, sc);
+    if (bl.group_ends(kt, nk)) bl.fold(acc, part, sc);
   }
   wait_lgkm();
   __builtin_amdgcn_s_barrier();
 }
 
-template <class Cfg, int DT, class ALd, class BLd>
+template <class Cfg, int DT, int D, class ALd, class BLd>
 __device__ __forceinline__ void mainloop_w4(char* lds, const ALd& al, const BLd& bl, int nk,
                                             f32x16 (&acc)[Cfg::TM][Cfg::TN]) {
-  using Ring = W4Ring<Cfg>;
+  using Ring = W4Ring<Cfg, D>;
   static_assert(ALd::kDMA && !BLd::kDMA, "X by direct copies, weights through registers");
   constexpr int YOUNG = ALd::P + BLd::LOADS;
   f32x16 part[Cfg::TM][Cfg::TN];
@@ -497,27 +513,31 @@ __device__ __forceinline__ void mainloop_w4(char* lds, const ALd& al, const BLd&
   frag_t<Cfg> fa[2][Cfg::TM], fb[2][Cfg::TN];
   FragAddr<Cfg> ad;
   ad.init();
-  typename BLd::Regs r0, r1;
-  // prologue: k-tiles 0 and 1 in flight; 0 landed and published.  The wait
-  // leaves k-tile 1's loads and copies in flight, so all of k-tile 0's must
-  // be issued before any of them: the compiler may otherwise hoist a weight
-  // load of k-tile 1 (a plain load into registers) above a copy of k-tile 0
-  // (which it does not track), and the wait would then release before that
-  // copy has landed.
-  bl.load(0, r0);
-  al.issue(0, Ring::a(lds, 0));
-  __builtin_amdgcn_sched_barrier(0);
-  bl.load(1, r1);
-  al.issue(1, Ring::a(lds, 1));
-  __builtin_amdgcn_sched_barrier(0);
-  wait_vm_le<YOUNG>();
-  bl.store(Ring::b(lds, 0), r0);
+  typename BLd::Regs r[D];
+  u32x2 sc[Cfg::TN][4];  // scales of the next fold (exact integer weights)
+  // prologue: k-tiles 0 .. D - 1 in flight; 0 landed and published.  The
+  // wait leaves k-tiles 1 .. D - 1 in flight, so all of k-tile 0's loads must
+  // be issued before any of theirs (and so on): the compiler may otherwise
+  // hoist a weight load of a later k-tile (a plain load into registers) above
+  // a copy of an earlier one (which it does not track), and the wait would
+  // then release before that copy has landed.
+  static_for<0, D>([&](auto j) {
+    bl.load(j, r[j]);
+    al.issue(j, Ring::a(lds, j));
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  wait_vm_le<(D - 1) * YOUNG>();
+  bl.store(Ring::b(lds, 0), r[0]);
   wait_lgkm();
   __builtin_amdgcn_s_barrier();
-  // two k-tiles per trip so each register set keeps a fixed name
-  for (int kt = 0; kt < nk; kt += 2) {
-    w4_step<Cfg, DT>(lds, al, bl, kt, nk, r0, r1, ad, acc, part, fa, fb);
-    if (kt + 1 < nk) w4_step<Cfg, DT>(lds, al, bl, kt + 1, nk, r1, r0, ad, acc, part, fa, fb);
+  // D k-tiles per trip so each register set keeps a fixed name: step kt
+  // loads k-tile kt + D into set kt % D and publishes kt + 1 from set
+  // (kt + 1) % D
+  for (int kt = 0; kt < nk; kt += D) {
+    static_for<0, D>([&](auto j) {
+      if (kt + j < nk)
+        w4_step<Cfg, DT, D>(lds, al, bl, kt + j, nk, r[j], r[(j + 1) % D], ad, acc, part, sc, fa, fb);
+    });
   }
   // copies and loads past the last k-tile are still landing: drain them
   // before anyone reuses the stages
@@ -531,9 +551,10 @@ __device__ __forceinline__ void mainloop_w4(char* lds, const ALd& al, const BLd&
 // into Y; split, the fp32 partial goes to partial[s] and k_w4a16_sum adds
 // the ranges afterwards.  The ranges of a tile are consecutive work items,
 // so they run in one XCD round and share the tile's X panel in its L2.
-template <class Cfg, int DT>
-__global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_w4a16_tiled(W4Launch a, int tiles_m, int total_work) {
-  __shared__ __attribute__((aligned(16))) char lds[W4Ring<Cfg>::BYTES];
+template <class Cfg, int DT, int D>
+__global__ __launch_bounds__(Cfg::THREADS, (W4Ring<Cfg, D>::WGS)) void k_w4a16_tiled(W4Launch a, int tiles_m,
+                                                                                  int total_work) {
+  __shared__ __attribute__((aligned(16))) char lds[W4Ring<Cfg, D>::BYTES];
   const int G = gridDim.x;
   const W4Geom g{a.w, a.scales, a.zeros, a.N, a.K, a.group, a.s_bytes, a.z_bytes, a.sor, a.wxor, a.zxor};
   const int Ks = a.K / a.split;
@@ -557,11 +578,229 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_w4a16_tiled(W
     al.init(a.X + k0, a.ldx, t.m0, t.M, Ks);
     bl.init(g, t.n0, k0 / Cfg::BK);
     f32x16 acc[Cfg::TM][Cfg::TN];
-    mainloop_w4<Cfg, DT>(lds, al, bl, Ks / Cfg::BK, acc);
+    mainloop_w4<Cfg, DT, D>(lds, al, bl, Ks / Cfg::BK, acc);
     if (a.split == 1)
       store_tile<Cfg, DT>(t, acc, 1.0f, 0.0f, lds);
     else
       store_partial<Cfg>(t, acc, a.partial + (int64_t)sidx * a.M * a.N);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Register-sourced kernel (the page's design: the narrow weight is the
+// operand that lives in registers, dequantised right before the multiply).
+// The prepacked 16-row block is laid out so that lane L's 16 bytes are its
+// v_mfma_f32_16x16x32 A fragments (row L % 16, k-group L / 16) for the four
+// 32-k steps of the 128-k block, so a wave loads its own weight words
+// straight into VGPRs, dequantises them there, and multiplies them against
+// X fragments (token L % 16, the same k-group) that the workgroup's waves
+// share through an LDS ring of X k-tiles.  No weight tile goes through LDS,
+// so nothing waits on a dequantised tile being written and published.
+//
+// Workgroup: 4 waves, 16 MT tokens (an X tile of 16 MT rows x 64 k per
+// stage), wave w owning weight blocks WB w .. WB w + WB - 1 of its 64 WB-row
+// slice.  Pipeline distance D: the X copies and weight loads of k-tile
+// kt + D go out at the start of step kt, into the X stage and register set
+// of k-tile kt - 1 (both free after the previous step's barrier); the end
+// of step kt waits for k-tile kt + 1 (the loads of kt + 2 .. kt + D stay in
+// flight) and a barrier publishes its X stage.  Accumulator lane l, element
+// i: weight row 4 (l / 16) + i of block b, token 16 mt + l % 16.
+// bf16: exact q - z into a per-group fp32 partial, folded with the scales of
+// the lane's four rows at the end of each scale group (or k-range).
+// ---------------------------------------------------------------------------
+using RsXCfg = TileCfg<128, 128, 2, 2, 64, 2>;  // X tile layout: 4 waves, 64-k rows of 128 bytes
+
+template <int WB>
+struct RsRegs {
+  u32x2 w[WB];   // words 2 (kt % 2) + {0, 1} of each block's lane entry
+  uint32_t z[WB];  // zero point of row L % 16 (after the mode fix-up)
+  u32x2 s[WB];   // fp16: scale of row L % 16 in s[b][0]; bf16: scales of rows 4 (L / 16) + {0..3}
+};
+
+template <int DT, int WB>
+struct RsWeights {
+  static constexpr bool EXACT = DT == DT_BF16;
+  static constexpr int LOADS = 3 * WB;  // weight words, zero point, scales per block
+  rsrc_t rw, rs, rz;
+  uint32_t kblocks, N, group, blk0, kt0, sor, wxor, zxor;
+  __device__ __forceinline__ void init(const W4Launch& a, int n_base, int kt_first) {
+    rw = make_rsrc(a.w, (uint32_t)((int64_t)a.N * a.K / 2));
+    rs = make_rsrc(a.scales, a.s_bytes);
+    rz = make_rsrc(a.zeros, a.z_bytes);
+    kblocks = a.K / 128;
+    N = a.N;
+    group = a.group;
+    blk0 = n_base / 16 + wave_id() * WB;
+    kt0 = kt_first;
+    sor = a.sor;
+    wxor = a.wxor;
+    zxor = a.zxor;
+  }
+  __device__ __forceinline__ void load(int kt_local, RsRegs<WB>& r) const {
+    const uint32_t kt = kt_local + kt0, lane = threadIdx.x & 63;
+    const uint32_t grp = (kt * 64) / group;
+#pragma unroll
+    for (int b = 0; b < WB; ++b) {
+      const uint32_t blk = blk0 + b, n = blk * 16 + lane % 16;
+      const bool ok = blk * 16 < N;
+      r.w[b] = buf_load8(rw, ok ? (blk * kblocks + kt / 2) * 1024u + lane * 16u + (kt & 1) * 8u : OOB);
+      r.z[b] = buf_load1(rz, ok ? grp * (N / 2) + n / 2 : OOB);
+      if constexpr (EXACT)
+        r.s[b] = buf_load8(rs, ok ? (grp * N + blk * 16 + 4 * (lane / 16)) * 2u : OOB);
+      else
+        r.s[b] = u32x2{buf_load2(rs, ok ? (grp * N + n) * 2u : OOB), 0u};
+    }
+  }
+  __device__ __forceinline__ bool group_ends(int kt_local, int nk) const {
+    return kt_local + 1 == nk || (((kt_local + kt0 + 1) * 64) % group) == 0;
+  }
+};
+
+template <int DT, int WB, int MT, int D>
+struct RsRing {
+  static constexpr int XSTAGE = MT * 16 * 128;  // X tile bytes per k-tile
+  static constexpr int BYTES = (D + 1) * XSTAGE;
+  static_assert(MT * 16 == RsXCfg::BM, "the X loader moves 128-row tiles");
+  static_assert(2 * BYTES <= 160 * 1024, "two workgroups per CU");
+};
+
+template <int DT, int WB, int MT, int D>
+__device__ __forceinline__ void rs_mainloop(char* lds, const DenseLoader<RsXCfg, RsXCfg::BM>& xl,
+                                            const RsWeights<DT, WB>& wl, int nk, f32x4 (&acc)[WB][MT]) {
+  using Ring = RsRing<DT, WB, MT, D>;
+  constexpr bool EXACT = DT == DT_BF16;
+  constexpr int YOUNG = RsXCfg::NW == 4 ? DenseLoader<RsXCfg, RsXCfg::BM>::P + RsWeights<DT, WB>::LOADS : 0;
+  static_assert((D - 1) * YOUNG < 64, "the k-tiles left in flight fit the vmcnt counter");
+  const int lane = threadIdx.x & 63;
+  f32x4 part[WB][MT];
+#pragma unroll
+  for (int b = 0; b < WB; ++b)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      acc[b][mt] = f32x4{0, 0, 0, 0};
+      part[b][mt] = f32x4{0, 0, 0, 0};
+    }
+  __builtin_amdgcn_s_barrier();  // the previous item's waves are done with the ring
+  if (nk <= 0) return;
+  // X fragment of token row (16 mt + lane % 16), 32-k step j: chunk 4 j + lane / 16
+  uint32_t xoff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) xoff[j] = (uint32_t)RsXCfg::off(lane % 16, 4 * j + lane / 16);
+  RsRegs<WB> r[D + 1];
+  // prologue: k-tiles 0 .. D - 1 in flight, each one's loads before the
+  // next one's (the waits count in issue order), k-tile 0 landed and published
+  static_for<0, D>([&](auto j) {
+    wl.load(j, r[j]);
+    xl.issue(j, lds + j * Ring::XSTAGE);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  wait_vm_le<(D - 1) * YOUNG>();
+  __builtin_amdgcn_s_barrier();
+  for (int kt0 = 0; kt0 < nk; kt0 += D + 1) {
+    static_for<0, D + 1>([&](auto jj) {
+      constexpr int J = decltype(jj)::value;
+      const int kt = kt0 + J;
+      if (kt < nk) {
+        // the loads of k-tile kt + D: into the register set and X stage of kt - 1
+        __builtin_amdgcn_sched_barrier(0);
+        wl.load(kt + D, r[(J + D) % (D + 1)]);
+        xl.issue(kt + D, lds + ((kt + D) % (D + 1)) * Ring::XSTAGE);
+        __builtin_amdgcn_sched_barrier(0);
+        const char* xs = lds + (kt % (D + 1)) * Ring::XSTAGE;
+        // this step's weights, loaded D steps ago: passed through an empty asm
+        // here so that no arithmetic on them is scheduled next to their loads
+        // (where the compiler would wait for loads just issued)
+        RsRegs<WB> cur = r[J];
+#pragma unroll
+        for (int b = 0; b < WB; ++b) asm volatile("" : "+v"(cur.w[b]), "+v"(cur.z[b]), "+v"(cur.s[b]));
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          u32x4 xf[MT];
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) xf[mt] = *(const u32x4*)(xs + xoff[j] + mt * 16 * RsXCfg::ROWB);
+#pragma unroll
+          for (int b = 0; b < WB; ++b) {
+            const uint32_t wq = cur.w[b][j] ^ wl.wxor;
+            const uint32_t z = ((cur.z[b] >> ((lane & 1) * 4)) & 15u) ^ wl.zxor;
+            u32x4 wf;
+            if constexpr (EXACT)
+              wf = exact8_bf16(wq, (float)z);
+            else
+              wf = dequant8(wq, zero_pair(z), scale_pair((cur.s[b][0] & 0xffffu) | wl.sor));
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+              if constexpr (EXACT)
+                part[b][mt] = mfma16<DT>(wf, xf[mt], part[b][mt]);
+              else
+                acc[b][mt] = mfma16<DT>(wf, xf[mt], acc[b][mt]);
+            }
+          }
+        }
+        if constexpr (EXACT) {
+          if (wl.group_ends(kt, nk)) {
+#pragma unroll
+            for (int b = 0; b < WB; ++b)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float si = from_bits<DT_BF16>(((cur.s[b][i / 2] >> (16 * (i % 2))) & 0xffffu) | wl.sor);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                  acc[b][mt][i] = __builtin_fmaf(si, part[b][mt][i], acc[b][mt][i]);
+                  part[b][mt][i] = 0.0f;
+                }
+              }
+          }
+        }
+        // k-tile kt + 1 landed (kt + 2 .. kt + D stay in flight), then published
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm_le<(D - 1) * YOUNG>();
+        __builtin_amdgcn_s_barrier();
+      }
+    });
+  }
+  wait_vm_le<0>();  // loads past the last k-tile are still landing
+  __builtin_amdgcn_s_barrier();
+}
+
+constexpr int kRsTokens = 128;  // tokens per workgroup (MT = 8)
+constexpr int kRsDepth = 3;
+
+// work item w = tile * split + s over tiles (m-tile fastest) of kRsTokens
+// tokens x 64 WB weight rows
+template <int DT, int WB>
+__global__ __launch_bounds__(256, 2) void k_w4a16_rs(W4Launch a, int tiles_m, int total_work) {
+  constexpr int MT = kRsTokens / 16, D = kRsDepth;
+  __shared__ __attribute__((aligned(16))) char lds[RsRing<DT, WB, MT, D>::BYTES];
+  const int G = gridDim.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int Ks = a.K / a.split;
+  for (int base = 0; base < total_work; base += G) {
+    const int work = base + remap_slot(blockIdx.x, G);
+    if (work >= total_work) break;
+    const int tile = work / a.split, sidx = work - tile * a.split;
+    const int m0 = (tile % tiles_m) * kRsTokens, n_base = (tile / tiles_m) * 64 * WB;
+    const int k0 = sidx * Ks;
+    DenseLoader<RsXCfg, RsXCfg::BM> xl;
+    xl.init(a.X + k0, a.ldx, m0, a.M, Ks);
+    RsWeights<DT, WB> wl;
+    wl.init(a, n_base, k0 / 64);
+    f32x4 acc[WB][MT];
+    rs_mainloop<DT, WB, MT, D>(lds, xl, wl, Ks / 64, acc);
+    // lane l, element i: row n_base + 16 (WB wave + b) + 4 (l / 16) + i, token m0 + 16 mt + l % 16
+#pragma unroll
+    for (int b = 0; b < WB; ++b) {
+      const int n = n_base + 16 * (WB * wave + b) + 4 * (lane / 16);
+      if (n >= a.N) continue;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int tok = m0 + 16 * mt + lane % 16;
+        if (tok >= a.M) continue;
+        const f32x4 v = acc[b][mt];
+        if (a.split == 1)
+          *(gu32x2*)(a.Y + (int64_t)tok * a.ldy + n) = u32x2{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
+        else
+          *(f32x4*)(a.partial + (int64_t)sidx * a.M * a.N + (int64_t)tok * a.N + n) = v;
+      }
+    }
   }
 }
 
@@ -627,23 +866,25 @@ static hipError_t launch_w4a16_dt(const W4Launch& a, hipStream_t stream) {
     return hipGetLastError();
   }
   const int cus = device_cu_count();
-  // bf16 keeps a second set of fp32 partial sums (exact integer weights,
-  // scaled per group), which fits the registers of the 128 x 128 tile only
-  const bool big = DT == DT_F16 && w4_big_tiles(a.M, a.N, cus);
-  const int bm = big ? 256 : 128, bn = big ? 256 : 128;
-  const int tiles_m = (a.M + bm - 1) / bm;
-  const int total = tiles_m * ((a.N + bn - 1) / bn) * a.split;
-  const int resident = cus * (big ? 1 : 2);
-  int grid = (total + XCDS - 1) / XCDS * XCDS;
-  if (grid > resident) grid = resident / XCDS * XCDS;
-  if constexpr (DT == DT_F16) {
-    if (big)
-      hipLaunchKernelGGL((k_w4a16_tiled<W4Cfg256, DT>), dim3(grid), dim3(W4Cfg256::THREADS), 0, stream, a, tiles_m,
-                         total);
+  // fp16 with enough rows for 256 x 256 tiles on every CU: the LDS-dequant
+  // tiles (their B tile serves 256 rows of X); otherwise the register-sourced
+  // kernel, 128 tokens x 128 weight rows per work item, k-ranges as
+  // w4a16_split chose them, two workgroups per CU
+  if (DT == DT_F16 && w4_big_tiles(a.M, a.N, cus)) {
+    const int tiles_m = (a.M + 255) / 256;
+    const int total = tiles_m * ((a.N + 255) / 256) * a.split;
+    int grid = (total + XCDS - 1) / XCDS * XCDS;
+    if (grid > cus) grid = cus / XCDS * XCDS;
+    hipLaunchKernelGGL((k_w4a16_tiled<W4Cfg256, DT_F16, 2>), dim3(grid), dim3(W4Cfg256::THREADS), 0, stream, a,
+                       tiles_m, total);
+  } else {
+    constexpr int WB = 2;
+    const int tiles_m = (a.M + kRsTokens - 1) / kRsTokens;
+    const int total = tiles_m * ((a.N + 64 * WB - 1) / (64 * WB)) * a.split;
+    int grid = (total + XCDS - 1) / XCDS * XCDS;
+    if (grid > 2 * cus) grid = 2 * cus / XCDS * XCDS;
+    hipLaunchKernelGGL((k_w4a16_rs<DT, WB>), dim3(grid), dim3(256), 0, stream, a, tiles_m, total);
   }
-  if (!big)
-    hipLaunchKernelGGL((k_w4a16_tiled<W4Cfg128, DT>), dim3(grid), dim3(W4Cfg128::THREADS), 0, stream, a, tiles_m,
-                       total);
   if (a.split > 1) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -720,7 +961,7 @@ __device__ __forceinline__ int wave_sum(int v) {
 
 template <class Cfg, int DT>
 __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_w4a16_grouped_tiled(W4Grouped a) {
-  __shared__ __attribute__((aligned(16))) char lds[W4Ring<Cfg>::BYTES];
+  __shared__ __attribute__((aligned(16))) char lds[W4Ring<Cfg, 2>::BYTES];
   const int lane = threadIdx.x & 63;
   const int tn = (a.base.N + Cfg::BN - 1) / Cfg::BN;
   auto clip = [&](int v) { return min(max(v, 0), a.rows); };
@@ -788,7 +1029,7 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_w4a16_grouped
     al.init(b.X + (int64_t)row0 * b.ldx, b.ldx, tt.m0, rows, b.K);
     bl.init(geo, tt.n0, 0);
     f32x16 acc[Cfg::TM][Cfg::TN];
-    mainloop_w4<Cfg, DT>(lds, al, bl, b.K / Cfg::BK, acc);
+    mainloop_w4<Cfg, DT, 2>(lds, al, bl, b.K / Cfg::BK, acc);
     store_tile<Cfg, DT>(tt, acc, 1.0f, 0.0f, lds);
   }
 }
