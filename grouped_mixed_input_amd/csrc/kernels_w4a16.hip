@@ -765,13 +765,38 @@ __device__ __forceinline__ void rs_mainloop(char* lds, const DenseLoader<RsXCfg,
 constexpr int kRsTokens = 128;  // tokens per workgroup (MT = 8)
 constexpr int kRsDepth = 3;
 
+// Results of one register-sourced tile: lane l, element i of acc[b][mt] is
+// weight row n_base + 16 (WB wave + b) + 4 (l / 16) + i and token
+// m0 + 16 mt + l % 16; rounded into Y, or as fp32 into partial[sidx] when
+// the call is split over K.
+template <int DT, int WB, int MT>
+__device__ __forceinline__ void rs_store(const W4Launch& a, const f32x4 (&acc)[WB][MT], int m0, int n_base,
+                                         int sidx) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int b = 0; b < WB; ++b) {
+    const int n = n_base + 16 * (WB * wave + b) + 4 * (lane / 16);
+    if (n >= a.N) continue;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int tok = m0 + 16 * mt + lane % 16;
+      if (tok >= a.M) continue;
+      const f32x4 v = acc[b][mt];
+      if (a.split == 1)
+        *(gu32x2*)(a.Y + (int64_t)tok * a.ldy + n) = u32x2{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
+      else
+        *(f32x4*)(a.partial + (int64_t)sidx * a.M * a.N + (int64_t)tok * a.N + n) = v;
+    }
+  }
+}
+
 // work item w = tile * split + s over tiles (m-tile fastest) of kRsTokens
 // tokens x 64 WB weight rows
 template <int DT, int WB>
 __global__ __launch_bounds__(256, 2) void k_w4a16_rs(W4Launch a, int tiles_m, int total_work) {
   constexpr int MT = kRsTokens / 16, D = kRsDepth;
   __shared__ __attribute__((aligned(16))) char lds[RsRing<DT, WB, MT, D>::BYTES];
-  const int G = gridDim.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int G = gridDim.x;
   const int Ks = a.K / a.split;
   for (int base = 0; base < total_work; base += G) {
     const int work = base + remap_slot(blockIdx.x, G);
@@ -785,22 +810,7 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_rs(W4Launch a, int tiles_m, in
     wl.init(a, n_base, k0 / 64);
     f32x4 acc[WB][MT];
     rs_mainloop<DT, WB, MT, D>(lds, xl, wl, Ks / 64, acc);
-    // lane l, element i: row n_base + 16 (WB wave + b) + 4 (l / 16) + i, token m0 + 16 mt + l % 16
-#pragma unroll
-    for (int b = 0; b < WB; ++b) {
-      const int n = n_base + 16 * (WB * wave + b) + 4 * (lane / 16);
-      if (n >= a.N) continue;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int tok = m0 + 16 * mt + lane % 16;
-        if (tok >= a.M) continue;
-        const f32x4 v = acc[b][mt];
-        if (a.split == 1)
-          *(gu32x2*)(a.Y + (int64_t)tok * a.ldy + n) = u32x2{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
-        else
-          *(f32x4*)(a.partial + (int64_t)sidx * a.M * a.N + (int64_t)tok * a.N + n) = v;
-      }
-    }
+    rs_store<DT, WB, MT>(a, acc, m0, n_base, sidx);
   }
 }
 
@@ -959,11 +969,12 @@ __device__ __forceinline__ int wave_sum(int v) {
   return v;
 }
 
-template <class Cfg, int DT>
-__global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_w4a16_grouped_tiled(W4Grouped a) {
-  __shared__ __attribute__((aligned(16))) char lds[W4Ring<Cfg, 2>::BYTES];
+template <int DT>
+__global__ __launch_bounds__(256, 2) void k_w4a16_grouped_tiled(W4Grouped a) {
+  constexpr int WB = 2, MT = kRsTokens / 16, D = kRsDepth, BM = kRsTokens, BN = 64 * WB;
+  __shared__ __attribute__((aligned(16))) char lds[RsRing<DT, WB, MT, D>::BYTES];
   const int lane = threadIdx.x & 63;
-  const int tn = (a.base.N + Cfg::BN - 1) / Cfg::BN;
+  const int tn = (a.base.N + BN - 1) / BN;
   auto clip = [&](int v) { return min(max(v, 0), a.rows); };
 
   // tiles of groups 16 lane .. + 15 (0 for those the decode launch takes),
@@ -976,7 +987,7 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_w4a16_grouped
     int c = 0;
     if (g < a.count) {
       const int rows = clip(a.offsets[g + 1]) - clip(a.offsets[g]);
-      if (rows > kGroupedDecodeRows) c = ((rows + Cfg::BM - 1) / Cfg::BM) * tn;
+      if (rows > kGroupedDecodeRows) c = ((rows + BM - 1) / BM) * tn;
     }
     first[i] = c;  // the count for now
     sum += c;
@@ -1009,28 +1020,25 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_w4a16_grouped
     for (int i = 0; i < kGroupsPerLane; ++i) mine = (i == g % kGroupsPerLane) ? first[i] : mine;
     const int g_first = __builtin_amdgcn_readfirstlane(__shfl(mine, g / kGroupsPerLane, 64));
     const int row0 = clip(a.offsets[g]), rows = clip(a.offsets[g + 1]) - row0;
-    const int tm = (rows + Cfg::BM - 1) / Cfg::BM;
+    const int tm = (rows + BM - 1) / BM;
     const int local = t - g_first;
-    Tile tt;
-    tt.M = rows;
-    tt.N = a.base.N;
-    tt.K = a.base.K;
-    tt.m0 = (local % tm) * Cfg::BM;
-    tt.n0 = (local / tm) * Cfg::BN;
-    tt.C = nullptr;
-    tt.ldc = 0;
-    tt.D = a.base.Y + (int64_t)row0 * a.base.ldy;
-    tt.ldd = a.base.ldy;
-    const W4Launch& b = a.base;
-    const W4Geom geo{b.w + g * a.w_stride, b.scales + g * a.s_stride, b.zeros + g * a.z_stride, b.N, b.K, b.group,
-                     b.s_bytes, b.z_bytes, b.sor, b.wxor, b.zxor};
-    DenseLoader<Cfg, Cfg::BM> al;
-    W4Loader<Cfg, Cfg::BN, DT> bl;
-    al.init(b.X + (int64_t)row0 * b.ldx, b.ldx, tt.m0, rows, b.K);
-    bl.init(geo, tt.n0, 0);
-    f32x16 acc[Cfg::TM][Cfg::TN];
-    mainloop_w4<Cfg, DT, 2>(lds, al, bl, b.K / Cfg::BK, acc);
-    store_tile<Cfg, DT>(tt, acc, 1.0f, 0.0f, lds);
+    // the group as a plain call: its rows of X and Y, its weight, scales and zero points
+    W4Launch p = a.base;
+    p.M = rows;
+    p.X = a.base.X + (int64_t)row0 * a.base.ldx;
+    p.Y = a.base.Y + (int64_t)row0 * a.base.ldy;
+    p.w = a.base.w + g * a.w_stride;
+    p.scales = a.base.scales + g * a.s_stride;
+    p.zeros = a.base.zeros + g * a.z_stride;
+    p.split = 1;
+    const int m0 = (local % tm) * BM, n_base = (local / tm) * BN;
+    DenseLoader<RsXCfg, RsXCfg::BM> xl;
+    xl.init(p.X, p.ldx, m0, rows, p.K);
+    RsWeights<DT, WB> wl;
+    wl.init(p, n_base, 0);
+    f32x4 acc[WB][MT];
+    rs_mainloop<DT, WB, MT, D>(lds, xl, wl, p.K / 64, acc);
+    rs_store<DT, WB, MT>(p, acc, m0, n_base, 0);
   }
 }
 
@@ -1086,12 +1094,12 @@ hipError_t launch_w4a16_grouped(const W4Grouped& a, hipStream_t stream) {
     hipLaunchKernelGGL(k_w4a16_grouped_pair<DT_F16>, pgrid, dim3(64 * kGroupedWaves), 0, stream, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  int g1 = device_cu_count() * W4Cfg128::WGS_PER_CU / XCDS * XCDS;
+  int g1 = device_cu_count() * 2 / XCDS * XCDS;
   if (g1 < XCDS) g1 = XCDS;
   if (a.base.dt == DT_BF16)
-    hipLaunchKernelGGL((k_w4a16_grouped_tiled<W4Cfg128, DT_BF16>), dim3(g1), dim3(W4Cfg128::THREADS), 0, stream, a);
+    hipLaunchKernelGGL(k_w4a16_grouped_tiled<DT_BF16>, dim3(g1), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((k_w4a16_grouped_tiled<W4Cfg128, DT_F16>), dim3(g1), dim3(W4Cfg128::THREADS), 0, stream, a);
+    hipLaunchKernelGGL(k_w4a16_grouped_tiled<DT_F16>, dim3(g1), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
