@@ -281,7 +281,7 @@ static gmi_status grouped_offsets(const char* who, int32_t count, const int32_t*
   // tiles the rows can make (all rows in one group), and the tile total is
   // bounded by every group adding at most one partial tile row.
   const int shape = choose_shape([&](int bm, int bn) { return cdiv(rows, bm) * cdiv(N, bn); });
-  const int64_t bound = (cdiv(rows, SMALL_M) + count) * cdiv(N, tile_bn(shape));
+  const int64_t bound = (cdiv(rows, TINY_M) + count) * cdiv(N, tile_bn(shape));
   if (bound > INT32_MAX) return fail(GMI_ERR_INVALID_ARG, "%s: more than 2^31 - 1 output tiles", who);
   OffsetsLaunch p;
   p.offsets = offsets;

@@ -297,12 +297,31 @@ struct RowMap {
 // pointed out of range; a chunk that straddles K (K % 8 != 0, KTAIL) is
 // masked in LDS after it lands.
 // ---------------------------------------------------------------------------
+//
+// A tile of fewer 1 KB copies than waves (the 32-row grouped class on eight
+// waves) is copied by the first COPIES waves, and every further wave repeats
+// the copy of wave w % COPIES -- the same bytes to the same LDS addresses --
+// so that each wave issues one copy per k-tile and the waits, which count
+// copies per wave, stay uniform.
 template <class Cfg, int ROWS, bool KTAIL = false>
 struct DenseLoader {
   static constexpr bool kDMA = true;
   static constexpr bool kFIX = KTAIL;  // fix_tail may write LDS
-  static constexpr int P = ROWS * Cfg::ROWB / (1024 * Cfg::NW);  // 1 KB copies per wave per k-tile
-  static_assert(P >= 1 && ROWS % (Cfg::NW * Cfg::RPI) == 0, "rows must fill whole copy passes");
+  static constexpr int COPIES = ROWS * Cfg::ROWB / 1024;  // 1 KB copies per k-tile
+  static constexpr int P = COPIES >= Cfg::NW ? COPIES / Cfg::NW : 1;  // per wave
+  static_assert(COPIES >= 1 && (COPIES % Cfg::NW == 0 || Cfg::NW % COPIES == 0) && ROWS % Cfg::RPI == 0,
+                "rows must fill whole copy passes");
+  // the wave whose copies this one issues, and its rows / LDS destinations
+  __device__ static __forceinline__ int copy_wave() {
+    return COPIES >= Cfg::NW ? wave_id() : wave_id() % COPIES;
+  }
+  __device__ static __forceinline__ int row_of(int i, int lane) {
+    return Cfg::RPI * (Cfg::NW * i + copy_wave()) + lane / Cfg::CPR;
+  }
+  __device__ static __forceinline__ int chunk_of(int lane) { return (lane % Cfg::CPR) ^ Cfg::swz(row_of(0, lane)); }
+  __device__ static __forceinline__ char* dst_of(char* tile, int i) {
+    return tile + (Cfg::NW * i + copy_wave()) * 1024;
+  }
   rsrc_t rs;
   uint32_t voff[P];  // lane offset of copy i within k-tile 0, bytes
   int K, nk;
@@ -323,7 +342,7 @@ struct DenseLoader {
     const uint32_t ldb = (uint32_t)ld * Cfg::EB;  // row pitch, bytes
     rs = make_rsrc((const char*)base + (int64_t)row0 * ld * Cfg::EB, (uint32_t)left * ldb);
     const int lane = threadIdx.x & 63;
-    const uint32_t v0 = (uint32_t)Cfg::dma_row(0, lane) * ldb + (uint32_t)Cfg::dma_chunk(lane) * 16u;
+    const uint32_t v0 = (uint32_t)row_of(0, lane) * ldb + (uint32_t)chunk_of(lane) * 16u;
     const uint32_t step = (uint32_t)(Cfg::NW * Cfg::RPI) * ldb;
 #pragma unroll
     for (int i = 0; i < P; ++i) voff[i] = v0 + i * step;
@@ -335,7 +354,7 @@ struct DenseLoader {
     const int ke = kt < nk ? kt : nk - 1;
     Prep p;
     p.soff = (uint32_t)ke * Cfg::ROWB;
-    const bool in = (ke * Cfg::BK + Cfg::dma_chunk(threadIdx.x & 63) * Cfg::CE) < K;
+    const bool in = (ke * Cfg::BK + chunk_of(threadIdx.x & 63) * Cfg::CE) < K;
 #pragma unroll
     for (int i = 0; i < P; ++i) p.vo[i] = in ? voff[i] : OOB;
     return p;
@@ -343,7 +362,7 @@ struct DenseLoader {
   // copy i of the prepared k-tile: rows past the problem land as zeros (the
   // lane offset is past the resource), and so do chunks at or past K
   __device__ __forceinline__ void issue_one(int i, const Prep& p, char* tile) const {
-    dma16s(rs, p.vo[i], p.soff, Cfg::dma_dst(tile, i));
+    dma16s(rs, p.vo[i], p.soff, dst_of(tile, i));
   }
   __device__ __forceinline__ void issue(int kt, char* tile) const {
     const Prep p = prep(kt);
@@ -356,11 +375,11 @@ struct DenseLoader {
     if constexpr (!KTAIL) return;
     if ((K & 7) == 0 || kt >= nk || (kt + 1) * Cfg::BK <= K) return;
     const int lane = threadIdx.x & 63;
-    const int n = K - (kt * Cfg::BK + Cfg::dma_chunk(lane) * 8);
+    const int n = K - (kt * Cfg::BK + chunk_of(lane) * 8);
     if (n <= 0 || n >= 8) return;
 #pragma unroll
     for (int i = 0; i < P; ++i) {
-      u32x4* p = (u32x4*)(Cfg::dma_dst(tile, i) + lane * 16);
+      u32x4* p = (u32x4*)(dst_of(tile, i) + lane * 16);
       *p = mask_tail(*p, n);
     }
   }
@@ -1114,7 +1133,7 @@ template <class Cfg, int DT, bool MAPPED = false>
 __device__ __forceinline__ void store_tile(const Tile& t, const f32x16 (&acc)[Cfg::TM][Cfg::TN], float alpha,
                                            float beta, char* lds, const RowMap& map = RowMap{}) {
   constexpr int ROWB = Cfg::WTN * 4;  // fp32 row of the wave tile
-  constexpr int PASS = (Cfg::NW * 2 * 32 * ROWB <= Cfg::LDS_BYTES) ? 2 : 1;  // 32-row blocks per pass
+  constexpr int PASS = (Cfg::NW * 2 * 32 * ROWB <= Cfg::LDS_BYTES && Cfg::TM % 2 == 0) ? 2 : 1;  // 32-row blocks per pass
   constexpr int REGION = PASS * 32 * ROWB;
   static_assert(Cfg::NW * REGION <= Cfg::LDS_BYTES && Cfg::TM % PASS == 0, "the wave regions must fit the stages");
   constexpr int LPR = Cfg::WTN / 8;  // lanes per row on read-back (8 floats each)

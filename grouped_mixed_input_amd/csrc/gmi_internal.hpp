@@ -26,12 +26,15 @@ inline int tile_bm(int s) { return s == TILE_128x128 ? 128 : 256; }
 inline int tile_bn(int s) { return s == TILE_256x256 ? 256 : 128; }
 inline int tile_wgs_per_cu(int s) { return s == TILE_256x256 ? 1 : 2; }  // matches TileCfg::WGS_PER_CU
 // Grouped GEMM with 256x256 tiles: a problem of at most SMALL_M rows takes
-// SMALL_M x 256 tiles instead (same kernel, its own tile configuration), so
-// short groups -- the rare experts of a mixture-of-experts layer -- do not pay
-// for 256 rows of matrix work.  Host tile counting and the kernel use this rule.
-constexpr int SMALL_M = 64;
+// SMALL_M x 256 tiles instead, and one of at most TINY_M rows TINY_M x 256
+// tiles (same kernel, their own tile configurations), so short groups -- the
+// rare experts of a mixture-of-experts layer -- do not pay for 256 rows of
+// matrix work.  Host tile counting, the device table builder and the kernel
+// use this rule.
+constexpr int SMALL_M = 64, TINY_M = 32;
 inline int grouped_tile_rows(int shape, int M) {
-  return (shape == TILE_256x256 && M <= SMALL_M) ? SMALL_M : tile_bm(shape);
+  if (shape != TILE_256x256) return tile_bm(shape);
+  return M <= TINY_M ? TINY_M : M <= SMALL_M ? SMALL_M : 256;
 }
 
 // Grouped launch whose group sizes are device-held row offsets; `desc` and

@@ -43,11 +43,15 @@ struct GroupedArgs {
 // of m-tiles (raster), so one XCD's share of a round -- consecutive tiles --
 // reuses a few A and B panels, e.g. one expert weight in a mixture-of-experts
 // layer.
-// Tile configuration a grouped 256x256 launch uses for problems of at most
-// SMALL_M rows: SMALL_M x 256 over the same 8 waves (one wave row, eight wave
-// columns), a four-stage ring of 40 KB.
+// Tile configurations a grouped 256x256 launch uses for problems of at most
+// SMALL_M and at most TINY_M rows: SMALL_M x 256 and TINY_M x 256 over the
+// same 8 waves (one wave row, eight wave columns), four-stage rings.
 template <class Cfg>
 struct SmallOf {
+  using type = void;
+};
+template <class Cfg>
+struct TinyOf {
   using type = void;
 };
 template <int DT, bool KTAIL, class Cfg>
@@ -77,6 +81,7 @@ template <class Cfg, int DT, bool KTAIL, class Table>
 __device__ __forceinline__ void grouped_walk(char* lds, const Table& desc, int count, int total, float alpha,
                                              float beta) {
   using Small = typename SmallOf<Cfg>::type;
+  using Tiny = typename TinyOf<Cfg>::type;
   const int G = gridDim.x;
   int g = 0;
   for (int base = 0; base < total; base += G) {
@@ -85,6 +90,12 @@ __device__ __forceinline__ void grouped_walk(char* lds, const Table& desc, int c
     while (g + 1 < count && desc[g + 1].tile_start <= tile) ++g;
     const GroupDesc& d = desc[g];
     const int local = tile - d.tile_start;
+    if constexpr (!std::is_void<Tiny>::value) {
+      if (d.M <= TINY_M) {
+        grouped_tile<DT, KTAIL, Tiny>(lds, d, local, alpha, beta);
+        continue;
+      }
+    }
     if constexpr (!std::is_void<Small>::value) {
       if (d.M <= SMALL_M) {
         grouped_tile<DT, KTAIL, Small>(lds, d, local, alpha, beta);
@@ -97,8 +108,8 @@ __device__ __forceinline__ void grouped_walk(char* lds, const Table& desc, int c
 
 template <class Cfg>
 constexpr int grouped_lds() {
-  using Small = typename SmallOf<Cfg>::type;
-  return Cfg::LDS_BYTES > lds_of<Small>() ? Cfg::LDS_BYTES : lds_of<Small>();
+  constexpr int a = Cfg::LDS_BYTES, b = lds_of<typename SmallOf<Cfg>::type>(), c = lds_of<typename TinyOf<Cfg>::type>();
+  return a > b ? (a > c ? a : c) : (b > c ? b : c);
 }
 
 template <class Cfg, int DT, bool KTAIL>
@@ -156,7 +167,7 @@ __global__ __launch_bounds__(kMaxOffsetGroupCount) void k_group_table(OffsetsTab
     const int hi = min(max(a.offsets[g + 1], 0), a.rows);
     m = hi > lo ? hi - lo : 0;
     if (m > 0 && a.N > 0) {
-      const int tr = (a.small_class && m <= SMALL_M) ? SMALL_M : a.bm;
+      const int tr = !a.small_class ? a.bm : m <= TINY_M ? TINY_M : m <= SMALL_M ? SMALL_M : a.bm;
       tiles = (m + tr - 1) / tr * ((a.N + a.bn - 1) / a.bn);
       work = min(m, tr);
     }
@@ -242,12 +253,14 @@ using Cfg256 = TileCfg<256, 256, 4, 2, 64, 2, 5>;
 using Cfg256x128 = TileCfg<256, 128, 2, 2, 32, 3>;
 using Cfg128 = TileCfg<128, 128, 2, 2, 32, 4>;
 using CfgSmall256 = TileCfg<SMALL_M, 256, 1, 8, 64, 4>;
+using CfgTiny256 = TileCfg<TINY_M, 256, 1, 8, 64, 4>;
 // fp8 inputs: the same row bytes (128 k per 128-byte row), so the same rings
 // where they fit; 256x128 and 128x128 on two stages of 48 KB and 32 KB.
 using Cfg256F8 = TileCfg<256, 256, 4, 2, 128, 2, 5, 1>;
 using Cfg256x128F8 = TileCfg<256, 128, 2, 2, 128, 2, 0, 1>;
 using Cfg128F8 = TileCfg<128, 128, 2, 2, 128, 2, 0, 1>;
 using CfgSmall256F8 = TileCfg<SMALL_M, 256, 1, 8, 128, 4, 0, 1>;
+using CfgTiny256F8 = TileCfg<TINY_M, 256, 1, 8, 128, 4, 0, 1>;
 template <>
 struct SmallOf<Cfg256> {
   using type = CfgSmall256;
@@ -256,8 +269,17 @@ template <>
 struct SmallOf<Cfg256F8> {
   using type = CfgSmall256F8;
 };
-static_assert(CfgSmall256::THREADS == Cfg256::THREADS && CfgSmall256F8::THREADS == Cfg256F8::THREADS,
-              "both tile shapes run on the same workgroup");
+template <>
+struct TinyOf<Cfg256> {
+  using type = CfgTiny256;
+};
+template <>
+struct TinyOf<Cfg256F8> {
+  using type = CfgTiny256F8;
+};
+static_assert(CfgSmall256::THREADS == Cfg256::THREADS && CfgSmall256F8::THREADS == Cfg256F8::THREADS &&
+                  CfgTiny256::THREADS == Cfg256::THREADS && CfgTiny256F8::THREADS == Cfg256F8::THREADS,
+              "every tile shape of a grouped launch runs on the same workgroup");
 
 // Persistent grid: a whole number of XCD rounds, no more workgroups than can
 // be resident at once and no more than the tiles need.

@@ -68,9 +68,10 @@ def test_fp8_integer_inputs_bit_exact(gmi):
 
 @pytest.mark.parametrize("K", [128, 1040])
 def test_fp8_grouped_mixed_tile_classes(gmi, K):
-    # enough 256 x 256 tiles for the launch to use them, problems of at most 64 rows on the small class
+    # enough 256 x 256 tiles for the launch to use them, problems of at most 64 rows on the small class and of
+    # at most 32 rows on the tiny one
     r = np.random.default_rng(K)
-    Ms = [1, 40, 64, 65, 200, 256, 300] + list(r.integers(1, 500, 65))
+    Ms = [1, 8, 32, 33, 40, 64, 65, 200, 256, 300] + list(r.integers(1, 500, 62))
     N = 1024
     As = [_codes(r, (int(M), K)) for M in Ms]
     Bs = [_codes(r, (N, K)) for _ in Ms]

@@ -190,10 +190,10 @@ def test_empty_calls_are_noops(gmi):
 @pytest.mark.parametrize("K", [128, 100])
 def test_grouped_mixed_tile_classes(gmi, K):
     # 72 problems with N = 1024 and M from 1 to 600: enough 256 x 256 tiles to fill the device, so the launch
-    # uses them, and every problem of at most 64 rows takes the 64 x 256 tile class in the same kernel.
-    # K = 100 also exercises the K-tail copies in both classes.
+    # uses them, and every problem of at most 64 rows takes the 64 x 256 tile class, of at most 32 rows the
+    # 32 x 256 class, in the same kernel.  K = 100 also exercises the K-tail copies in every class.
     r = np.random.default_rng(K)
-    Ms = [1, 17, 63, 64, 65, 100, 255, 256, 257, 600] + list(r.integers(1, 600, 62))
+    Ms = [1, 17, 31, 32, 33, 63, 64, 65, 100, 255, 256, 257, 600] + list(r.integers(1, 600, 59))
     shapes = [(int(M), 1024, K) for M in Ms]
     assert sum((M + 255) // 256 * 4 for M, _, _ in shapes) >= 256
     for got, ref, shp in run_grouped(gmi, shapes, "bf16", 1.5, 0.5, seed=K, ld_pad=8):
