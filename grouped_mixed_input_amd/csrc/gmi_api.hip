@@ -386,8 +386,7 @@ gmi_status gmi_prepack_w4(const uint8_t* w_u4, int32_t N, int32_t K, uint8_t* w_
 
 size_t gmi_w4a16_workspace_bytes(int32_t M, int32_t N, int32_t K) {
   if (M <= 0 || N <= 0 || K <= 0 || N % 16 || K % 128) return 0;
-  const int split = w4a16_split(M, N, K);
-  return split > 1 ? (size_t)split * (size_t)M * (size_t)N * sizeof(float) : 0;
+  return w4a16_workspace(M, N, K);
 }
 
 // Shared by the two mixed-input entry points: every rule checked, then one

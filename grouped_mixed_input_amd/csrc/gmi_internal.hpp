@@ -105,7 +105,7 @@ struct W4Launch {
   uint16_t* Y;
   int64_t ldy;
   int split;       // k-ranges per output tile (1: no split)
-  float* partial;  // split > 1: fp32 [split][M][N] partial products
+  float* partial;  // split > 1: fp32 partial products, in the layout of the kernel that writes them
 };
 
 // Grouped (mixture-of-experts) mixed-input launch: group g owns rows
@@ -124,6 +124,8 @@ int device_cu_count();  // cached per device
 // k-ranges per output tile the W4A16 GEMM uses for this shape on the current
 // device (1 when the tiles alone fill the device or the path is skinny)
 int w4a16_split(int M, int N, int K);
+// bytes of fp32 partial products that split needs (0 without a split)
+size_t w4a16_workspace(int M, int N, int K);
 
 hipError_t launch_grouped(const GroupDesc* desc_dev, int count, int total_tiles, int shape, int dtype, bool ktail,
                           float alpha, float beta, hipStream_t stream);

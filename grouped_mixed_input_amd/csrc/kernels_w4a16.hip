@@ -546,27 +546,22 @@ __device__ __forceinline__ void mainloop_w4(char* lds, const ALd& al, const BLd&
 }
 
 // ---------------------------------------------------------------------------
-// Work item w = tile * split + s: output tile `tile`, k-range s of `split`
-// equal ranges (whole 128-k blocks).  Unsplit, the epilogue rounds to fp16
-// into Y; split, the fp32 partial goes to partial[s] and k_w4a16_sum adds
-// the ranges afterwards.  The ranges of a tile are consecutive work items,
-// so they run in one XCD round and share the tile's X panel in its L2.
+// One output tile per work item, the whole K, rounded into Y by the
+// epilogue: used only where the tiles alone cover every CU, so it never
+// splits over K.
 template <class Cfg, int DT, int D>
 __global__ __launch_bounds__(Cfg::THREADS, (W4Ring<Cfg, D>::WGS)) void k_w4a16_tiled(W4Launch a, int tiles_m,
                                                                                   int total_work) {
   __shared__ __attribute__((aligned(16))) char lds[W4Ring<Cfg, D>::BYTES];
   const int G = gridDim.x;
   const W4Geom g{a.w, a.scales, a.zeros, a.N, a.K, a.group, a.s_bytes, a.z_bytes, a.sor, a.wxor, a.zxor};
-  const int Ks = a.K / a.split;
   for (int base = 0; base < total_work; base += G) {
-    const int work = base + remap_slot(blockIdx.x, G);
-    if (work >= total_work) break;
-    const int tile = work / a.split, sidx = work - tile * a.split;
-    const int k0 = sidx * Ks;
+    const int tile = base + remap_slot(blockIdx.x, G);
+    if (tile >= total_work) break;
     Tile t;
     t.M = a.M;
     t.N = a.N;
-    t.K = Ks;
+    t.K = a.K;
     t.m0 = (tile % tiles_m) * Cfg::BM;
     t.n0 = (tile / tiles_m) * Cfg::BN;
     t.C = nullptr;
@@ -575,14 +570,11 @@ __global__ __launch_bounds__(Cfg::THREADS, (W4Ring<Cfg, D>::WGS)) void k_w4a16_t
     t.ldd = a.ldy;
     DenseLoader<Cfg, Cfg::BM> al;
     W4Loader<Cfg, Cfg::BN, DT> bl;
-    al.init(a.X + k0, a.ldx, t.m0, t.M, Ks);
-    bl.init(g, t.n0, k0 / Cfg::BK);
+    al.init(a.X, a.ldx, t.m0, t.M, a.K);
+    bl.init(g, t.n0, 0);
     f32x16 acc[Cfg::TM][Cfg::TN];
-    mainloop_w4<Cfg, DT, D>(lds, al, bl, Ks / Cfg::BK, acc);
-    if (a.split == 1)
-      store_tile<Cfg, DT>(t, acc, 1.0f, 0.0f, lds);
-    else
-      store_partial<Cfg>(t, acc, a.partial + (int64_t)sidx * a.M * a.N);
+    mainloop_w4<Cfg, DT, D>(lds, al, bl, a.K / Cfg::BK, acc);
+    store_tile<Cfg, DT>(t, acc, 1.0f, 0.0f, lds);
   }
 }
 
@@ -767,12 +759,26 @@ constexpr int kRsDepth = 3;
 
 // Results of one register-sourced tile: lane l, element i of acc[b][mt] is
 // weight row n_base + 16 (WB wave + b) + 4 (l / 16) + i and token
-// m0 + 16 mt + l % 16; rounded into Y, or as fp32 into partial[sidx] when
-// the call is split over K.
+// m0 + 16 mt + l % 16; rounded into Y.  When the call is split over K the
+// fp32 partials go to the workspace in this register layout instead: work
+// item (tile, s) owns kRsTileFloats floats at (tile split + s) kRsTileFloats,
+// accumulator (wave, b, mt) the 1 KB run ((wave WB + b) MT + mt) 256 floats
+// in, lane l's four values at 4 l -- one contiguous 1 KB store per
+// accumulator; k_w4a16_rs_sum reads them back the same way.
+constexpr int kRsTileFloats = kRsTokens * 128;  // one 128-token x 128-row tile
 template <int DT, int WB, int MT>
 __device__ __forceinline__ void rs_store(const W4Launch& a, const f32x4 (&acc)[WB][MT], int m0, int n_base,
-                                         int sidx) {
+                                         int tile, int sidx) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  static_assert(4 * WB * MT * 256 == kRsTileFloats, "four waves cover one tile");
+  if (a.split > 1) {
+    float* pt = a.partial + ((int64_t)tile * a.split + sidx) * kRsTileFloats;
+#pragma unroll
+    for (int b = 0; b < WB; ++b)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) *(f32x4*)(pt + ((wave * WB + b) * MT + mt) * 256 + 4 * lane) = acc[b][mt];
+    return;
+  }
 #pragma unroll
   for (int b = 0; b < WB; ++b) {
     const int n = n_base + 16 * (WB * wave + b) + 4 * (lane / 16);
@@ -782,11 +788,29 @@ __device__ __forceinline__ void rs_store(const W4Launch& a, const f32x4 (&acc)[W
       const int tok = m0 + 16 * mt + lane % 16;
       if (tok >= a.M) continue;
       const f32x4 v = acc[b][mt];
-      if (a.split == 1)
-        *(gu32x2*)(a.Y + (int64_t)tok * a.ldy + n) = u32x2{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
-      else
-        *(f32x4*)(a.partial + (int64_t)sidx * a.M * a.N + (int64_t)tok * a.N + n) = v;
+      *(gu32x2*)(a.Y + (int64_t)tok * a.ldy + n) = u32x2{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
     }
+  }
+}
+
+// Y = RN(sum over s of the k-ranges' partials) in s order, from the register
+// layout of rs_store: one thread per lane quad of one accumulator of one tile
+template <int DT, int WB, int MT>
+__global__ __launch_bounds__(256) void k_w4a16_rs_sum(const float* __restrict__ P, int split, int tiles_m, int tiles,
+                                                      int M, int N, uint16_t* __restrict__ Y, int64_t ldy) {
+  constexpr int QUADS = kRsTileFloats / 4;
+  const int64_t total = (int64_t)tiles * QUADS;
+  for (int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; id < total;
+       id += (int64_t)gridDim.x * blockDim.x) {
+    const int tile = (int)(id / QUADS), r = (int)(id - (int64_t)tile * QUADS);
+    const int lane = r % 64, mt = (r / 64) % MT, wb = r / (64 * MT);  // wb = wave WB + b
+    const float* src = P + (int64_t)tile * split * kRsTileFloats + 4 * r;
+    f32x4 v = *(const f32x4*)src;
+    for (int sp = 1; sp < split; ++sp) v += *(const f32x4*)(src + (int64_t)sp * kRsTileFloats);
+    const int tok = (tile % tiles_m) * kRsTokens + 16 * mt + lane % 16;
+    const int n = (tile / tiles_m) * 128 + 16 * wb + 4 * (lane / 16);
+    if (tok < M && n < N)
+      *(u32x2*)(Y + (int64_t)tok * ldy + n) = u32x2{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
   }
 }
 
@@ -810,27 +834,7 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_rs(W4Launch a, int tiles_m, in
     wl.init(a, n_base, k0 / 64);
     f32x4 acc[WB][MT];
     rs_mainloop<DT, WB, MT, D>(lds, xl, wl, Ks / 64, acc);
-    rs_store<DT, WB, MT>(a, acc, m0, n_base, sidx);
-  }
-}
-
-// Y = RN(sum over s of partial[s]) in s order: 8 consecutive n per thread
-template <int DT>
-__global__ __launch_bounds__(256) void k_w4a16_sum(const float* __restrict__ P, int split, int M, int N,
-                                                   uint16_t* __restrict__ Y, int64_t ldy) {
-  const int64_t groups = (int64_t)M * N / 8;
-  const int64_t plane = (int64_t)M * N;
-  for (int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; id < groups;
-       id += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t e = id * 8;
-    const int m = (int)(e / N), n = (int)(e - (int64_t)m * N);
-    f32x4 lo = *(const f32x4*)(P + e), hi = *(const f32x4*)(P + e + 4);
-    for (int s = 1; s < split; ++s) {
-      lo += *(const f32x4*)(P + s * plane + e);
-      hi += *(const f32x4*)(P + s * plane + e + 4);
-    }
-    *(u32x4*)(Y + (int64_t)m * ldy + n) =
-        u32x4{pack2<DT>(lo[0], lo[1]), pack2<DT>(lo[2], lo[3]), pack2<DT>(hi[0], hi[1]), pack2<DT>(hi[2], hi[3])};
+    rs_store<DT, WB, MT>(a, acc, m0, n_base, tile, sidx);
   }
 }
 
@@ -840,6 +844,13 @@ using W4Cfg128 = TileCfg<128, 128, 2, 2, 64, 2>;
 // Tile shape of the tiled path: 256 x 256 when those tiles alone fill the
 // device, else 128 x 128 (two workgroups per CU).
 static bool w4_big_tiles(int M, int N, int cus) { return ((M + 255) / 256) * ((N + 255) / 256) >= cus; }
+
+size_t w4a16_workspace(int M, int N, int K) {
+  const int split = w4a16_split(M, N, K);
+  if (split <= 1) return 0;
+  const size_t tiles = (size_t)((M + kRsTokens - 1) / kRsTokens) * (size_t)((N + 127) / 128);
+  return (size_t)split * tiles * kRsTileFloats * sizeof(float);
+}
 
 int w4a16_split(int M, int N, int K) {
   if (M <= 64) return 1;  // decode / skinny kernels
@@ -882,27 +893,27 @@ static hipError_t launch_w4a16_dt(const W4Launch& a, hipStream_t stream) {
   // w4a16_split chose them, two workgroups per CU
   if (DT == DT_F16 && w4_big_tiles(a.M, a.N, cus)) {
     const int tiles_m = (a.M + 255) / 256;
-    const int total = tiles_m * ((a.N + 255) / 256) * a.split;
+    const int total = tiles_m * ((a.N + 255) / 256);  // w4a16_split gave 1
     int grid = (total + XCDS - 1) / XCDS * XCDS;
     if (grid > cus) grid = cus / XCDS * XCDS;
     hipLaunchKernelGGL((k_w4a16_tiled<W4Cfg256, DT_F16, 2>), dim3(grid), dim3(W4Cfg256::THREADS), 0, stream, a,
                        tiles_m, total);
   } else {
-    constexpr int WB = 2;
+    constexpr int WB = 2, MT = kRsTokens / 16;
     const int tiles_m = (a.M + kRsTokens - 1) / kRsTokens;
-    const int total = tiles_m * ((a.N + 64 * WB - 1) / (64 * WB)) * a.split;
+    const int tiles = tiles_m * ((a.N + 64 * WB - 1) / (64 * WB));
+    const int total = tiles * a.split;
     int grid = (total + XCDS - 1) / XCDS * XCDS;
     if (grid > 2 * cus) grid = 2 * cus / XCDS * XCDS;
     hipLaunchKernelGGL((k_w4a16_rs<DT, WB>), dim3(grid), dim3(256), 0, stream, a, tiles_m, total);
-  }
-  if (a.split > 1) {
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int64_t groups = (int64_t)a.M * a.N / 8;
-    int64_t blocks = (groups + 255) / 256;
-    if (blocks > 4 * cus) blocks = 4 * cus;
-    hipLaunchKernelGGL(k_w4a16_sum<DT>, dim3((unsigned)blocks), dim3(256), 0, stream, a.partial, a.split, a.M, a.N,
-                       a.Y, a.ldy);
+    if (a.split > 1) {
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      int64_t blocks = ((int64_t)tiles * (kRsTileFloats / 4) + 255) / 256;
+      if (blocks > 4 * cus) blocks = 4 * cus;
+      hipLaunchKernelGGL((k_w4a16_rs_sum<DT, WB, MT>), dim3((unsigned)blocks), dim3(256), 0, stream, a.partial,
+                         a.split, tiles_m, tiles, a.M, a.N, a.Y, a.ldy);
+    }
   }
   return hipGetLastError();
 }
@@ -1038,7 +1049,7 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_grouped_tiled(W4Grouped a) {
     wl.init(p, n_base, 0);
     f32x4 acc[WB][MT];
     rs_mainloop<DT, WB, MT, D>(lds, xl, wl, p.K / 64, acc);
-    rs_store<DT, WB, MT>(p, acc, m0, n_base, 0);
+    rs_store<DT, WB, MT>(p, acc, m0, n_base, 0, 0);
   }
 }
 

@@ -94,9 +94,10 @@ def test_w4a16_prepack_layout_matters(gmi):
 
 def test_w4a16_split_and_unsplit_agree(gmi):
     # M = 160, N = 256, K = 2048: four output tiles, so with a workspace K is split into four k-ranges whose
-    # fp32 partials a second launch sums; without one the same tiles run unsplit.  Both meet the oracle.
+    # fp32 partials (a whole 128 x 128 tile each, the ragged second row of tiles included) a second launch
+    # sums; without one the same tiles run unsplit.  Both meet the oracle.
     M, N, K = 160, 256, 2048
-    assert gmi.w4a16_workspace_bytes(M, N, K) == 4 * M * N * 4
+    assert gmi.w4a16_workspace_bytes(M, N, K) == 4 * 4 * 128 * 128 * 4
     d = gi.w4a16(seed=11, M=M, N=N, K=K, group=128)
     ref = oracle.w4a16(d["X"], d["W"], d["scales"], d["zeros"], N, K, 128)
     wpp = gmi.prepack_w4(bytes_to_dev(d["W"]), N, K)
