@@ -29,13 +29,15 @@ PEAK_MFMA_16 = 2516.6  # TFLOP/s, dense fp16 / bf16: 256 CU x 4096 FLOP/clk x 2.
 PEAK_MFMA_8 = 5033.2  # TFLOP/s, dense fp8: twice the 16-bit rate
 PEAK_HBM = 8000.0  # GB/s
 # HBM bytes per launch of the headline kernel: rocprofv3 FETCH_SIZE and WRITE_SIZE of the headline command,
-# each scaled by what the same counter reads for a plain 256 MiB device copy (FETCH x 1.99972, WRITE x 1.0);
+# each scaled by what the same counter reads for a plain 256 MiB device copy (FETCH x 1.99973, WRITE x 1.0);
 # summary and commands in profiles/k_gemm_ptr_array_256x256_bf16_ptr_array_L16_1024.md.  Valid for the
 # kernel named here only.
 HEADLINE_KERNEL = "k_gemm_ptr_array<TileCfg<256,256,4,2,64,2,5>, bf16, false>"
-HEADLINE_TRAFFIC_BYTES = 101441928
+HEADLINE_TRAFFIC_BYTES = 100992876
 HEADLINE_PROFILE = "k_gemm_ptr_array_256x256_bf16_ptr_array_L16_1024.md"
-HEADLINE_PMC_CLOCK_MHZ = None  # GRBM_GUI_ACTIVE cycles / kernel ns of the headline kernel, from that profile
+# GRBM_GUI_ACTIVE cycles (summed over the 8 XCDs) / 8 / kernel time of the headline kernel in that profile's
+# counter run, where every dispatch is serialized by the profiler
+HEADLINE_PMC_CLOCK_MHZ = 2401
 MALL_BYTES = 256 << 20
 ROTATE_TARGET = 512 << 20
 METRIC = "TFLOP/s and % of MFMA peak: grouped bf16 GEMM, w4a16 GEMM, conv fprop"
@@ -180,8 +182,9 @@ def shader_clock(torch, fn, n_copies, seconds=1.5):
         torch.cuda.synchronize()
     stop.set()
     th.join(timeout=15)
-    pmc = {"mhz": HEADLINE_PMC_CLOCK_MHZ, "source": "rocprofv3 GRBM_GUI_ACTIVE / kernel duration of the headline "
-                                                    "kernel, profiles/" + HEADLINE_PROFILE}
+    pmc = {"mhz": HEADLINE_PMC_CLOCK_MHZ, "source": "rocprofv3 GRBM_GUI_ACTIVE / 8 XCDs / kernel duration of the "
+                                                    "headline kernel with the profiler serializing dispatches, "
+                                                    "profiles/" + HEADLINE_PROFILE}
     if not samples:
         return {"amd_smi_mhz": None, "amd_smi_error": errors[-1] if errors else "no sample", "pmc": pmc}
     samples.sort()

@@ -1254,12 +1254,12 @@ __device__ __forceinline__ int remap_slot(int w, int G) { return (w % XCDS) * (G
 // tiles then covers a block of at most RASTER_M m-tiles by a few n-tiles, so
 // at every k-step its CUs fetch few distinct A and B panel slices into its L2.
 constexpr int RASTER_M = 8;
-__device__ __forceinline__ void raster(int local, int tm, int tn, int& mi, int& ni) {
-  const int band = local / (RASTER_M * tn);
-  const int r = local - band * RASTER_M * tn;
-  const int left = tm - band * RASTER_M;
-  const int rows = left < RASTER_M ? left : RASTER_M;
-  mi = band * RASTER_M + r % rows;
+__device__ __forceinline__ void raster(int local, int tm, int tn, int& mi, int& ni, int band_m = RASTER_M) {
+  const int band = local / (band_m * tn);
+  const int r = local - band * band_m * tn;
+  const int left = tm - band * band_m;
+  const int rows = left < band_m ? left : band_m;
+  mi = band * band_m + r % rows;
   ni = r / rows;
 }
 

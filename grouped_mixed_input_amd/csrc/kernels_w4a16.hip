@@ -814,8 +814,9 @@ __global__ __launch_bounds__(256) void k_w4a16_rs_sum(const float* __restrict__ 
   }
 }
 
-// work item w = tile * split + s over tiles (m-tile fastest) of kRsTokens
-// tokens x 64 WB weight rows
+// work item w = s * tiles + tile over tiles (m-tile fastest) of kRsTokens
+// tokens x 64 WB weight rows: k-range major, so an XCD's run of consecutive
+// items shares one k-range of X in its L2 (each item's weights are its own)
 template <int DT, int WB>
 __global__ __launch_bounds__(256, 2) void k_w4a16_rs(W4Launch a, int tiles_m, int total_work) {
   constexpr int MT = kRsTokens / 16, D = kRsDepth;
@@ -825,7 +826,8 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_rs(W4Launch a, int tiles_m, in
   for (int base = 0; base < total_work; base += G) {
     const int work = base + remap_slot(blockIdx.x, G);
     if (work >= total_work) break;
-    const int tile = work / a.split, sidx = work - tile * a.split;
+    const int tiles = total_work / a.split;
+    const int sidx = work / tiles, tile = work - sidx * tiles;
     const int m0 = (tile % tiles_m) * kRsTokens, n_base = (tile / tiles_m) * 64 * WB;
     const int k0 = sidx * Ks;
     DenseLoader<RsXCfg, RsXCfg::BM> xl;
@@ -980,6 +982,7 @@ __device__ __forceinline__ int wave_sum(int v) {
   return v;
 }
 
+constexpr int kW4Band = 2;  // row tiles per raster band of the grouped tiled launch
 template <int DT>
 __global__ __launch_bounds__(256, 2) void k_w4a16_grouped_tiled(W4Grouped a) {
   constexpr int WB = 2, MT = kRsTokens / 16, D = kRsDepth, BM = kRsTokens, BN = 64 * WB;
@@ -1042,7 +1045,11 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_grouped_tiled(W4Grouped a) {
     p.scales = a.base.scales + g * a.s_stride;
     p.zeros = a.base.zeros + g * a.z_stride;
     p.split = 1;
-    const int m0 = (local % tm) * BM, n_base = (local / tm) * BN;
+    // bands of RASTER_M row tiles, row tile fastest: an XCD's run of
+    // consecutive items shares a few X row tiles and weight panels in its L2
+    int mi, ni;
+    raster(local, tm, tn, mi, ni, kW4Band);
+    const int m0 = mi * BM, n_base = ni * BN;
     DenseLoader<RsXCfg, RsXCfg::BM> xl;
     xl.init(p.X, p.ldx, m0, rows, p.K);
     RsWeights<DT, WB> wl;
