@@ -546,6 +546,11 @@ __device__ __forceinline__ void mainloop_w4(char* lds, const ALd& al, const BLd&
 }
 
 // ---------------------------------------------------------------------------
+// Row tiles per raster band of the tiled launches: an XCD's run of
+// consecutive work items covers at most this many X row tiles
+constexpr int kW4Band = 4;
+constexpr int kW4GroupBand = 2;  // the grouped launch, per expert
+
 // One output tile per work item, the whole K, rounded into Y by the
 // epilogue: used only where the tiles alone cover every CU, so it never
 // splits over K.
@@ -558,12 +563,14 @@ __global__ __launch_bounds__(Cfg::THREADS, (W4Ring<Cfg, D>::WGS)) void k_w4a16_t
   for (int base = 0; base < total_work; base += G) {
     const int tile = base + remap_slot(blockIdx.x, G);
     if (tile >= total_work) break;
+    int mi, ni;
+    raster(tile, tiles_m, total_work / tiles_m, mi, ni, kW4Band);
     Tile t;
     t.M = a.M;
     t.N = a.N;
     t.K = a.K;
-    t.m0 = (tile % tiles_m) * Cfg::BM;
-    t.n0 = (tile / tiles_m) * Cfg::BN;
+    t.m0 = mi * Cfg::BM;
+    t.n0 = ni * Cfg::BN;
     t.C = nullptr;
     t.ldc = 0;
     t.D = a.Y;
@@ -814,9 +821,11 @@ __global__ __launch_bounds__(256) void k_w4a16_rs_sum(const float* __restrict__ 
   }
 }
 
-// work item w = s * tiles + tile over tiles (m-tile fastest) of kRsTokens
-// tokens x 64 WB weight rows: k-range major, so an XCD's run of consecutive
-// items shares one k-range of X in its L2 (each item's weights are its own)
+// work item w = s * tiles + tile over tiles of kRsTokens tokens x 64 WB
+// weight rows: k-range major, so an XCD's run of consecutive items shares
+// one k-range of X in its L2 (each item's weights are its own); inside a
+// k-range the tiles go in bands of kW4Band row tiles, row tile fastest, so
+// the run covers a few X row tiles by a few weight panels
 template <int DT, int WB>
 __global__ __launch_bounds__(256, 2) void k_w4a16_rs(W4Launch a, int tiles_m, int total_work) {
   constexpr int MT = kRsTokens / 16, D = kRsDepth;
@@ -828,7 +837,9 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_rs(W4Launch a, int tiles_m, in
     if (work >= total_work) break;
     const int tiles = total_work / a.split;
     const int sidx = work / tiles, tile = work - sidx * tiles;
-    const int m0 = (tile % tiles_m) * kRsTokens, n_base = (tile / tiles_m) * 64 * WB;
+    int mi, ni;
+    raster(tile, tiles_m, tiles / tiles_m, mi, ni, kW4Band);
+    const int m0 = mi * kRsTokens, n_base = ni * 64 * WB;
     const int k0 = sidx * Ks;
     DenseLoader<RsXCfg, RsXCfg::BM> xl;
     xl.init(a.X + k0, a.ldx, m0, a.M, Ks);
@@ -982,7 +993,6 @@ __device__ __forceinline__ int wave_sum(int v) {
   return v;
 }
 
-constexpr int kW4Band = 2;  // row tiles per raster band of the grouped tiled launch
 template <int DT>
 __global__ __launch_bounds__(256, 2) void k_w4a16_grouped_tiled(W4Grouped a) {
   constexpr int WB = 2, MT = kRsTokens / 16, D = kRsDepth, BM = kRsTokens, BN = 64 * WB;
@@ -1048,7 +1058,7 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_grouped_tiled(W4Grouped a) {
     // bands of RASTER_M row tiles, row tile fastest: an XCD's run of
     // consecutive items shares a few X row tiles and weight panels in its L2
     int mi, ni;
-    raster(local, tm, tn, mi, ni, kW4Band);
+    raster(local, tm, tn, mi, ni, kW4GroupBand);
     const int m0 = mi * BM, n_base = ni * BN;
     DenseLoader<RsXCfg, RsXCfg::BM> xl;
     xl.init(p.X, p.ldx, m0, rows, p.K);
