@@ -93,6 +93,8 @@ def lib() -> ctypes.CDLL:
     L.gmi_w4a16_workspace_bytes.argtypes = [_i32, _i32, _i32]
     L.gmi_conv2d_fprop_implicit.restype = ctypes.c_int
     L.gmi_conv2d_fprop_implicit.argtypes = [_i32] * 13 + [_p, _p, _p, _p, ctypes.c_int, _f32, _f32, _p]
+    L.gmi_time_next_gemm.restype = ctypes.c_int
+    L.gmi_time_next_gemm.argtypes = [_p, _p]
     _lib = L
     return L
 
@@ -119,6 +121,17 @@ def _ld(t: torch.Tensor) -> int:
 
 
 # ---------------------------------------------------------------- grouped
+def time_next_gemm(start, stop) -> None:
+    """Let the next GEMM kernel launched on this thread (grouped, grouped-offsets or pointer-array call) record
+    `start` and `stop` around itself, so start.elapsed_time(stop) is that kernel's execution time.  Both are
+    torch.cuda.Event(enable_timing=True) objects that have been recorded once (torch creates the HIP event on
+    its first record); None, None cancels a pending request."""
+    if start is None and stop is None:
+        _check(lib().gmi_time_next_gemm(None, None))
+        return
+    _check(lib().gmi_time_next_gemm(start.cuda_event, stop.cuda_event))
+
+
 def workspace_bytes(count: int) -> int:
     return lib().gmi_workspace_bytes(count)
 

@@ -130,6 +130,11 @@ static gmi_status scratch_address(const char* who, void** out) {
   return GMI_OK;
 }
 
+LaunchTimer& launch_timer() {
+  static thread_local LaunchTimer t;
+  return t;
+}
+
 }  // namespace gmi
 
 using namespace gmi;
@@ -137,6 +142,14 @@ using namespace gmi;
 extern "C" {
 
 const char* gmi_last_error(void) { return g_last_error.c_str(); }
+
+gmi_status gmi_time_next_gemm(void* start, void* stop) {
+  g_last_error.clear();
+  if ((start == nullptr) != (stop == nullptr))
+    return fail(GMI_ERR_INVALID_ARG, "time_next_gemm: start and stop must both be events or both NULL");
+  launch_timer() = LaunchTimer{(hipEvent_t)start, (hipEvent_t)stop};
+  return GMI_OK;
+}
 
 size_t gmi_workspace_bytes(int32_t problem_count) {
   if (problem_count < 0) return 0;

@@ -121,6 +121,13 @@ struct W4Grouped {
 };
 
 int device_cu_count();  // cached per device
+
+// Event pair that the next GEMM kernel launch on the calling thread records
+// around itself (set by gmi_time_next_gemm, cleared when used)
+struct LaunchTimer {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchTimer& launch_timer();
 // k-ranges per output tile the W4A16 GEMM uses for this shape on the current
 // device (1 when the tiles alone fill the device or the path is skinny)
 int w4a16_split(int M, int N, int K);

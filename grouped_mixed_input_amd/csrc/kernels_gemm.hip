@@ -8,6 +8,8 @@
 // mode shares one shape and one stride per operand over L batches.
 #include <type_traits>
 
+#include <hip/hip_ext.h>
+
 #include "gmi_device.hpp"
 #include "gmi_internal.hpp"
 
@@ -293,9 +295,21 @@ static int persistent_grid(int total_tiles, int wgs_per_cu) {
 // Instantiate and launch KER for the tile shape, element type and K-tail mode
 // (KT: some K is not a multiple of 8, so a chunk can straddle K; fp8 requires
 // K % 16 == 0 and has no tail mode).
-#define GMI_LAUNCH1(KER, CFG, DT, KT, tiles, args, stream)                                              \
-  hipLaunchKernelGGL((KER<CFG, DT, KT>), dim3(persistent_grid(tiles, CFG::WGS_PER_CU)), dim3(CFG::THREADS), 0, \
-                     stream, args)
+// A pending gmi_time_next_gemm request goes to this launch: the runtime then
+// stamps the pair with the kernel's own start and end.
+template <class F, class A>
+static void launch_gemm(F kernel, dim3 grid, dim3 block, hipStream_t stream, const A& args) {
+  LaunchTimer& t = launch_timer();
+  if (t.start) {
+    const LaunchTimer ev = t;
+    t = LaunchTimer{};
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev.start, ev.stop, 0, args);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, args);
+  }
+}
+#define GMI_LAUNCH1(KER, CFG, DT, KT, tiles, args, stream)                                                    \
+  launch_gemm(KER<CFG, DT, KT>, dim3(persistent_grid(tiles, CFG::WGS_PER_CU)), dim3(CFG::THREADS), stream, args)
 #define GMI_LAUNCH_DT(KER, CFG, CFG8, dtype, kt, tiles, args, stream)                         \
   do {                                                                                       \
     if ((dtype) == DT_F16) {                                                                 \

@@ -401,6 +401,21 @@ gmi_status gmi_conv2d_dgrad_implicit(int32_t N, int32_t H, int32_t W, int32_t C,
  * none).  The pointer stays valid until the next gmi_* call on that thread. */
 const char* gmi_last_error(void);
 
+/* Measurement hook, for benchmarks and profilers of the GEMM path.  `start`
+ * and `stop` are hipEvent_t handles that the caller created (with timing
+ * enabled) and owns.  The next GEMM kernel that gmi_gemm_grouped,
+ * gmi_gemm_grouped_offsets(_noalloc) or gmi_gemm_ptr_array launches on the
+ * calling thread is launched through hipExtLaunchKernel with this pair, so
+ * the runtime stamps them with that kernel's own start and end: their
+ * elapsed time is the kernel's execution time, without the dispatch and
+ * completion work that events recorded before and after the launch also
+ * time.  The request is used by one kernel and then cleared; a call that
+ * launches no GEMM kernel (a failed check, no work) leaves it pending.  The
+ * table-building launches of the grouped calls are not timed.  Both NULL
+ * cancels a pending request; exactly one NULL returns GMI_ERR_INVALID_ARG.
+ * Makes no HIP call. */
+gmi_status gmi_time_next_gemm(void* start, void* stop);
+
 #ifdef __cplusplus
 }
 #endif

@@ -35,7 +35,7 @@ def test_header_declares_the_boundary():
                  "gmi_gemm_grouped_offsets", "gmi_w4a16_workspace_bytes", "gmi_gemm_mixed",
                  "gmi_gemm_mixed_grouped", "gmi_conv2d_dgrad_implicit", "gmi_conv2d_dgrad_workspace_bytes",
                  "gmi_conv2d_wgrad_implicit", "gmi_conv2d_wgrad_workspace_bytes", "gmi_conv2d_fprop_implicit_fused",
-                 "gmi_gemm_grouped_offsets_noalloc"]:
+                 "gmi_gemm_grouped_offsets_noalloc", "gmi_time_next_gemm"]:
         assert want in names
 
 
@@ -355,3 +355,14 @@ def test_conv_fused_validation(gmi):
     assert _conv_fused(gmi, dt=3) == gmi.GMI_ERR_UNSUPPORTED
     assert _conv_fused(gmi, x=None) == gmi.GMI_ERR_INVALID_ARG
     assert _conv_fused(gmi, N=0) == gmi.GMI_OK  # no images: nothing to do, nothing launched
+
+
+def test_time_next_gemm_checks_its_pair(gmi):
+    # no HIP call: both NULL cancels, exactly one NULL is rejected (a real pair is exercised on the GPU)
+    import ctypes
+    L = gmi.lib()
+    assert L.gmi_time_next_gemm(None, None) == 0
+    assert L.gmi_time_next_gemm(ctypes.c_void_p(64), None) == gmi.GMI_ERR_INVALID_ARG
+    assert L.gmi_time_next_gemm(None, ctypes.c_void_p(64)) == gmi.GMI_ERR_INVALID_ARG
+    assert b"both" in L.gmi_last_error()
+    assert L.gmi_time_next_gemm(None, None) == 0

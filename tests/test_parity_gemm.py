@@ -177,6 +177,39 @@ def test_ptr_array_one_batch_fully_checked(gmi):
     check_close(host_bits(Dd[1]), ref, "bf16", "ptr-array full batch")
 
 
+def test_timed_launch_matches_untimed_and_is_used_once(gmi):
+    # gmi_time_next_gemm sends the next GEMM kernel through hipExtLaunchKernel with the caller's events: the
+    # result is the same bits, the pair holds a positive duration no longer than events around the whole call,
+    # and the request is consumed (the following call leaves the pair as it was)
+    L, M, N, K = 4, 256, 512, 384
+    A, B = gi.ptr_array_bf16(L=L, M=M, N=N, K=K)
+    Ad = [to_dev(a, "bf16") for a in A]
+    Bd = [to_dev(b, "bf16") for b in B]
+    D0 = [torch.empty((M, N), dtype=torch.bfloat16, device=dev()) for _ in range(L)]
+    D1 = [torch.empty((M, N), dtype=torch.bfloat16, device=dev()) for _ in range(L)]
+    pa = lambda ts: gmi.pointer_array(ts, dev())
+    pA, pB, p0, p1 = pa(Ad), pa(Bd), pa(D0), pa(D1)
+    run = lambda pD: gmi.gemm_ptr_array(L, M, N, K, pA, K, pB, K, None, N, pD, N, torch.bfloat16, 1.0, 0.0)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+    ev[2].record()
+    gmi.time_next_gemm(ev[0], ev[1])
+    run(p0)
+    ev[3].record()
+    torch.cuda.synchronize()
+    t_kernel, t_call = ev[0].elapsed_time(ev[1]), ev[2].elapsed_time(ev[3])
+    assert 0.0 < t_kernel <= t_call
+    run(p1)
+    torch.cuda.synchronize()
+    assert ev[0].elapsed_time(ev[1]) == t_kernel
+    for l in range(L):
+        assert np.array_equal(host_bits(D0[l]), host_bits(D1[l]))
+    ref = oracle.gemm(A[1], B[1], dtype="bf16")
+    check_close(host_bits(D0[1]), ref, "bf16", "timed ptr-array launch")
+
+
 def test_empty_calls_are_noops(gmi):
     D = torch.full((4, 8), 3.0, dtype=torch.float16, device=dev())
     gmi.gemm_grouped([torch.empty((4, 8), dtype=torch.float16, device=dev())],
