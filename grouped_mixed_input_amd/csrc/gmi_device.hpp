@@ -549,14 +549,23 @@ __device__ __forceinline__ u32x4 unpack8_biased_bf16(uint32_t w, uint32_t magic)
   return out;
 }
 
-__device__ __forceinline__ u32x4 dequant8(uint32_t w, f16x2 zz, f16x2 ss) {
+// Pairs 1 and 3 (nibble slots 1, 5 and 3, 7) are used in place, four bits
+// up: OR-ed into 0x6400 they give 1024 + 16 q exactly, and 1/16 of that
+// minus 64 + z is again q - z exactly (64 + z also has ulp 1/16 at most), so
+// only one shift is needed per word and every pair costs one mask-and-OR,
+// one add or multiply-add, and the scale multiply.  The results are those of
+// the shifted form bit for bit.  `magic` is 0x64006400 passed in a VGPR, so
+// that mask-and-OR is one v_and_or_b32.
+__device__ __forceinline__ u32x4 dequant8(uint32_t w, uint32_t z, f16x2 ss, uint32_t magic = 0x64006400u) {
+  const f16x2 zl = zero_pair(z);                                                    // 1024 + z
+  const f16x2 zh = __builtin_bit_cast(f16x2, (0x5400u | (z << 4)) * 0x00010001u);  // 64 + z
+  const f16x2 sixteenth = __builtin_bit_cast(f16x2, 0x2C002C00u);                   // 1/16
+  const uint32_t w8 = w >> 8;
   u32x4 out;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f16x2 h = __builtin_bit_cast(f16x2, ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u);
-    h = (h - zz) * ss;
-    out[i] = __builtin_bit_cast(uint32_t, h);
-  }
+  out[0] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, (w & 0x000F000Fu) | magic) - zl) * ss);
+  out[1] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, (w & 0x00F000F0u) | magic) * sixteenth - zh) * ss);
+  out[2] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, (w8 & 0x000F000Fu) | magic) - zl) * ss);
+  out[3] = __builtin_bit_cast(uint32_t, (__builtin_bit_cast(f16x2, (w8 & 0x00F000F0u) | magic) * sixteenth - zh) * ss);
   return out;
 }
 
@@ -600,7 +609,7 @@ __device__ __forceinline__ u32x4 exact8_bf16(uint32_t w, float zf) {
 template <int DT>
 __device__ __forceinline__ u32x4 dequant8_dt(uint32_t w, uint32_t s_bits, uint32_t z) {
   if constexpr (DT == DT_F16) {
-    return dequant8(w, zero_pair(z), scale_pair(s_bits));
+    return dequant8(w, z, scale_pair(s_bits));
   } else {
     const float s = from_bits<DT_BF16>(s_bits);
     return dequant8_bf16(w, s, -(float)z * s);

@@ -685,6 +685,8 @@ __device__ __forceinline__ void rs_mainloop(char* lds, const DenseLoader<RsXCfg,
   uint32_t xoff[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) xoff[j] = (uint32_t)RsXCfg::off(lane % 16, 4 * j + lane / 16);
+  uint32_t magic = 0x64006400u;  // in a VGPR: the conversion's mask-and-OR is one instruction
+  asm volatile("" : "+v"(magic));
   RsRegs<WB> r[D + 1];
   // prologue: k-tiles 0 .. D - 1 in flight, each one's loads before the
   // next one's (the waits count in issue order), k-tile 0 landed and published
@@ -725,7 +727,7 @@ __device__ __forceinline__ void rs_mainloop(char* lds, const DenseLoader<RsXCfg,
             if constexpr (EXACT)
               wf = exact8_bf16(wq, (float)z);
             else
-              wf = dequant8(wq, zero_pair(z), scale_pair((cur.s[b][0] & 0xffffu) | wl.sor));
+              wf = dequant8(wq, z, scale_pair((cur.s[b][0] & 0xffffu) | wl.sor), magic);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
               if constexpr (EXACT)
