@@ -80,6 +80,28 @@ def test_workload4_full_size(gmi, M):
     check_close(got[rows], ref, "f16", f"workload 4 M={M}")
 
 
+def test_w4a16_ragged_raster_band_full(gmi):
+    # M = 600 is five 128-token row tiles, so the register-sourced launch's bands of four row tiles end in a
+    # band of one (N = 2048: 16 weight panels; K = 512 keeps the call unsplit); every output is checked
+    d = gi.w4a16(seed=600, M=600, N=2048, K=512, group=128)
+    assert gmi.w4a16_workspace_bytes(600, 2048, 512) == 0
+    got = _w4_run(gmi, d)
+    ref = oracle.w4a16(d["X"], d["W"], d["scales"], d["zeros"], d["N"], d["K"], d["group"])
+    check_close(got, ref, "f16", "w4a16 M=600 ragged band")
+
+
+def test_w4a16_big_tiles_ragged_raster_band_sampled(gmi):
+    # M = 2304 at N = K = 8192 takes the 256 x 256 tiles (9 x 32 = 288 of them): bands of four row tiles end
+    # in a band of one; 24 sampled rows, 16 of them from that last row tile
+    M = 2304
+    d = gi.w4a16(seed=2304, M=M, N=8192, K=8192, group=128)
+    got = _w4_run(gmi, d)
+    r = np.random.default_rng(2304)
+    rows = np.concatenate([r.choice(2048, 8, replace=False), 2048 + r.choice(256, 16, replace=False)])
+    ref = oracle.w4a16(d["X"][rows], d["W"], d["scales"], d["zeros"], d["N"], d["K"], d["group"])
+    check_close(got[rows], ref, "f16", "w4a16 M=2304 last band")
+
+
 def test_w4a16_prepack_layout_matters(gmi):
     # feeding the plain (un-prepacked) bytes must give a different answer: the
     # kernels really consume the permuted layout
