@@ -51,18 +51,34 @@ def copies_for(ws_bytes: int) -> int:
     return 1 if ws_bytes >= ROTATE_TARGET else int(math.ceil(ROTATE_TARGET / ws_bytes))
 
 
-def time_launches(torch, fn, n_copies, warmup, group=1, min_window_ms=2.0, windows=7):
+RAMP_MS = 50.0
+
+
+def time_launches(torch, fn, n_copies, warmup, group=1, min_window_ms=2.0, windows=7, ramp_ms=RAMP_MS):
     """Per-launch time of fn (cycling over the rotating copies), HIP events on the launch stream.
 
-    After `warmup` untimed launches and one untimed calibration window of `group` launches, the loop times
-    `windows` windows; each is a whole number of `group`-launch runs, enough to last at least min_window_ms.
-    Returns the median per-launch time over the windows (ms) with the spread and the window size."""
+    After `warmup` untimed launches, untimed back-to-back launches continue until they have taken at least
+    `ramp_ms` of GPU time: after an idle spell the same launches run up to 20% slower for the first 15-20 ms
+    of load, until the device's power management settles, and the timed region starts once it has.  Then one untimed calibration window of `group` launches, and
+    the loop times `windows` windows; each is a whole number of `group`-launch runs, enough to last at least
+    min_window_ms.  Returns the median per-launch time over the windows (ms) with the spread, the window size
+    and the number of ramp launches."""
     i = 0
     for _ in range(warmup):
         fn(i % n_copies)
         i += 1
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ramped, ramp_launches, chunk = 0.0, 0, max(group, 8)
+    while ramped < ramp_ms:
+        s.record()
+        for _ in range(chunk):
+            fn(i % n_copies)
+            i += 1
+        e.record()
+        torch.cuda.synchronize()
+        ramped += s.elapsed_time(e)
+        ramp_launches += chunk
 
     def window(n):
         nonlocal i
@@ -79,7 +95,7 @@ def time_launches(torch, fn, n_copies, warmup, group=1, min_window_ms=2.0, windo
     n = group * reps
     per = sorted(window(n) / n for _ in range(windows))
     return {"ms": per[len(per) // 2], "min_ms": per[0], "max_ms": per[-1], "windows": windows,
-            "launches_per_window": n}
+            "launches_per_window": n, "ramp_launches": ramp_launches}
 
 
 def time_isolated_kernels(torch, gmi, fn, n_copies, launches):
@@ -533,7 +549,8 @@ def main():
     log("bench: building inputs")
     fn, R, flops, ws, keep = setup_ptr_array(torch, gmi, gi, dev)
     log(f"bench: headline rotates {R} copies of {ws / 2**20:.0f} MiB")
-    # W untimed warm-up steps, then windows of whole K-step runs (each window at least 2 ms, bracketed by
+    # W untimed warm-up steps, an untimed ramp of back-to-back steps (at least RAMP_MS of GPU time, while the
+    # device settles after idling), then windows of whole K-step runs (each window at least 2 ms, bracketed by
     # synchronizations); the step time is the median over the windows
     tm = time_launches(torch, fn, R, args.warmup, group=args.steps)
     ms = tm["ms"]
@@ -553,7 +570,8 @@ def main():
         "config": {"workload": "pointer-array bf16 GEMM, L=16 separately allocated M=N=K=1024 problems, "
                                "beta=0, fp32 accumulate, bf16 D", "L": 16, "M": 1024, "N": 1024, "K": 1024,
                    "cache": f"cold: {R} rotating copies of the {ws / 2**20:.0f} MiB working set"},
-        "timing": {"windows": tm["windows"], "steps_per_window": tm["launches_per_window"],
+        "timing": {"ramp_ms": RAMP_MS, "ramp_steps": tm["ramp_launches"], "windows": tm["windows"],
+                   "steps_per_window": tm["launches_per_window"],
                    "us_per_step_median": round(ms * 1e3, 3), "us_per_step_min": round(tm["min_ms"] * 1e3, 3),
                    "us_per_step_max": round(tm["max_ms"] * 1e3, 3)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_MFMA_16, "unit": "TFLOP/s",
