@@ -354,8 +354,9 @@ def bench_conv(torch, gmi, gi, dev, out):
     tm = time_launches(torch, lambda i: gmi.conv2d_dgrad(sets[i][2], sets[i][1], 56, 56, pad=(1, 1), dx=sets[i][0],
                                                          workspace=wsd), R, 5)
     out["conv_dgrad_bf16"] = roof(2.0 * 100352 * 256 * 2304, ws, tm)
-    # the data gradient of the same layer at stride 2 (dy 32 x 28 x 28 x 256 back to 56 x 56): one launch per
-    # output phase, each with only the taps that reach it; FLOPs of the forward view (every tap of every dy pixel)
+    # the data gradient of the same layer at stride 2 (dy 32 x 28 x 28 x 256 back to 56 x 56): the four output
+    # phases in one launch, each with only the taps that reach it; FLOPs of the forward view (every tap of every
+    # dy pixel)
     dy2 = [torch.empty((32, 28, 28, 256), dtype=torch.bfloat16, device=dev).normal_() for _ in range(R)]
     tm = time_launches(torch, lambda i: gmi.conv2d_dgrad(dy2[i], sets[i][1], 56, 56, pad=(1, 1), stride=(2, 2),
                                                          dx=sets[i][0], workspace=wsd), R, 5)

@@ -93,6 +93,14 @@ int conv_shape(int64_t M, int64_t N) {
   return choose_shape([&](int bm, int bn) { return cdiv(M, bm) * cdiv(N, bn); });
 }
 
+int conv_shape_multi(const int64_t* M, int count, int64_t N) {
+  return choose_shape([&](int bm, int bn) {
+    int64_t t = 0;
+    for (int i = 0; i < count; ++i) t += cdiv(M[i], bm) * cdiv(N, bn);
+    return t;
+  });
+}
+
 // Scratch of the allocation-free grouped call (gmi_gemm_grouped_offsets_noalloc):
 // what gmi_gemm_grouped_offsets keeps in the caller's workspace -- the tile
 // total in the header, then one descriptor per group -- for the largest

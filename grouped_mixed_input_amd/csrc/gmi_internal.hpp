@@ -87,6 +87,8 @@ struct ConvLaunch {
 // tile shape of a convolution launch's GEMM view (M pixels, N channels),
 // by the rule of the GEMM calls
 int conv_shape(int64_t M, int64_t N);
+// the same for one launch over several problems of M[i] rows and N columns
+int conv_shape_multi(const int64_t* M, int count, int64_t N);
 
 struct W4Launch {
   int M, N, K, group;

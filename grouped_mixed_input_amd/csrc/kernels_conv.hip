@@ -82,6 +82,67 @@ __global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_conv_fprop(Co
   }
 }
 
+// The phases of a strided data gradient in one persistent launch.  Phase p
+// is the forward gather over dy of its own geometry and filter slice,
+// writing its strided grid of dx pixels through the row map (off0 its own,
+// the strides shared).  Its tiles are ids tile_start .. of the launch, in
+// the order the host sorted the phases (longest reduction first, so the
+// static walk hands out the long tiles first); a tile finds its phase by a
+// scan of the prefix, which every lane does alike.
+constexpr int kMaxConvPhases = 16;
+struct PhaseDesc {
+  ConvGeom g;
+  const uint16_t* w;  // the phase's filter slice [C][taps][K]
+  int64_t map_off0;
+  int M, Hp, Wp;    // GEMM rows N * Hp * Wp: the phase's pixel grid
+  int tile_start;  // first tile id of the phase
+};
+struct PhasesArgs {
+  PhaseDesc ph[kMaxConvPhases];
+  int count, total_tiles, tiles_n, Nk;
+  const uint16_t* c;
+  uint16_t* y;
+  float alpha, beta;
+  int64_t map_img, map_rstep, map_cstep;
+  uint32_t map_bytes;
+};
+static_assert(sizeof(PhasesArgs) <= 4096, "kernel arguments are limited to 4 KB");
+
+template <class Cfg, int DT>
+__global__ __launch_bounds__(Cfg::THREADS, Cfg::WGS_PER_CU) void k_conv_phases(PhasesArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
+  const int G = gridDim.x;
+  const PhaseDesc* ph = a.ph;
+  for (int base = 0; base < a.total_tiles; base += G) {
+    const int work = base + remap_slot(blockIdx.x, G);
+    if (work >= a.total_tiles) break;
+    int p = 0;
+    for (int i = 1; i < a.count; ++i) p = work >= ph[i].tile_start ? i : p;
+    const PhaseDesc& d = ph[p];
+    const int tile = work - d.tile_start;
+    Tile t;
+    t.M = d.M;
+    t.N = a.Nk;
+    t.K = d.g.Kg;
+    t.m0 = (tile / a.tiles_n) * Cfg::BM;
+    t.n0 = (tile % a.tiles_n) * Cfg::BN;
+    t.C = a.c;
+    t.ldc = a.Nk;
+    t.D = a.y;
+    t.ldd = a.Nk;
+    t.bias = nullptr;
+    t.act = 0;
+    ConvLoader<Cfg, Cfg::BM> al;
+    FilterLoader<Cfg, Cfg::BN> bl;
+    al.init(d.g, t.m0, t.M, 0);
+    bl.init(d.w, d.g, t.n0, t.N, 0);
+    f32x16 acc[Cfg::TM][Cfg::TN];
+    mainloop<Cfg, DT>(lds, al, bl, (d.g.Kg + Cfg::BK - 1) / Cfg::BK, acc);
+    const RowMap map{d.Hp, d.Wp, d.map_off0, a.map_img, a.map_rstep, a.map_cstep, a.map_bytes};
+    store_tile<Cfg, DT, true>(t, acc, a.alpha, a.beta, lds, map);
+  }
+}
+
 using ConvCfg256 = TileCfg<256, 256, 4, 2, 64, 2, 5>;
 using ConvCfg256x128 = TileCfg<256, 128, 2, 2, 32, 3>;
 using ConvCfg128 = TileCfg<128, 128, 2, 2, 32, 4>;
@@ -261,11 +322,56 @@ static Phase1D phase_1d(int a, int R, int pad, int stride, int dil, int H) {
   return p;
 }
 
+// The geometry of one phase's forward view: a stride-1 gather over dy with
+// padding -shift and dilation -dil, its filter slice [C][taps][K]
+static ConvLaunch phase_view(const ConvLaunch& p, const Phase1D& ph, const Phase1D& pw, const uint16_t* wp) {
+  ConvLaunch f;
+  f.x = p.x;
+  f.w = wp;
+  f.c = p.c;
+  f.y = p.y;
+  f.N = p.N;
+  f.H = p.P;
+  f.W = p.Q;
+  f.C = p.K;
+  f.K = p.C;
+  f.R = ph.count;
+  f.S = pw.count;
+  f.P = ph.size;
+  f.Q = pw.size;
+  f.ph = -ph.shift;
+  f.pw = -pw.shift;
+  f.sh = 1;
+  f.sw = 1;
+  f.dh = -ph.dil;
+  f.dw = -pw.dil;
+  return f;
+}
+
+template <class Cfg>
+static hipError_t launch_phases(PhasesArgs& a, int dtype, hipStream_t stream) {
+  const int resident = device_cu_count() * Cfg::WGS_PER_CU;
+  int grid = (a.total_tiles + XCDS - 1) / XCDS * XCDS;
+  if (grid > resident) grid = resident / XCDS * XCDS;
+  if (grid < XCDS) grid = XCDS;
+  if (dtype == DT_F16)
+    hipLaunchKernelGGL((k_conv_phases<Cfg, DT_F16>), dim3(grid), dim3(Cfg::THREADS), 0, stream, a);
+  else
+    hipLaunchKernelGGL((k_conv_phases<Cfg, DT_BF16>), dim3(grid), dim3(Cfg::THREADS), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_conv_dgrad(const ConvLaunch& p, uint16_t* wt, int dtype, float alpha, float beta,
                              hipStream_t stream) {
   // p describes the forward problem (x: N x H x W x C, y: N x P x Q x K);
   // here p.x is dy, p.y is dx and p.c the dx-shaped C
   const bool strided = p.sh > 1 || p.sw > 1;
+  struct Phase {
+    ConvLaunch f;
+    int64_t off0;
+  };
+  Phase phases[64];
+  int count = 0;
   int64_t woff = 0;  // the phases' filter slices, one after another
   for (int a = 0; a < p.sh; ++a) {
     const Phase1D ph = phase_1d(a, p.R, p.ph, p.sh, p.dh, p.H);
@@ -281,37 +387,78 @@ hipError_t launch_conv_dgrad(const ConvLaunch& p, uint16_t* wt, int dtype, float
         if (e != hipSuccess) return e;
         woff += (int64_t)taps * p.C * p.K;
       }
-      ConvLaunch f;  // the phase's forward view: a gather over dy, its filter slice [C][taps][K]
-      f.x = p.x;
-      f.w = wp;
-      f.c = p.c;
-      f.y = p.y;
-      f.N = p.N;
-      f.H = p.P;
-      f.W = p.Q;
-      f.C = p.K;
-      f.K = p.C;
-      f.R = ph.count;
-      f.S = pw.count;
-      f.P = ph.size;
-      f.Q = pw.size;
-      f.ph = -ph.shift;
-      f.pw = -pw.shift;
-      f.sh = 1;
-      f.sw = 1;
-      f.dh = -ph.dil;
-      f.dw = -pw.dil;
-      if (strided) {
-        f.map_off0 = ((int64_t)(a - p.ph + p.sh * ph.lo) * p.W + (b - p.pw + p.sw * pw.lo)) * p.C;
-        f.map_img = (int64_t)p.H * p.W * p.C;
-        f.map_rstep = (int64_t)p.sh * p.W * p.C;
-        f.map_cstep = (int64_t)p.sw * p.C;
-        f.map_bytes = (uint32_t)((int64_t)p.N * p.H * p.W * p.C * 2);
-      }
-      const hipError_t e =
-          launch_conv_fprop(f, conv_shape((int64_t)p.N * ph.size * pw.size, p.C), dtype, alpha, beta, stream);
-      if (e != hipSuccess) return e;
+      phases[count].f = phase_view(p, ph, pw, wp);
+      phases[count].off0 = ((int64_t)(a - p.ph + p.sh * ph.lo) * p.W + (b - p.pw + p.sw * pw.lo)) * p.C;
+      ++count;
     }
+  }
+  const int64_t img = (int64_t)p.H * p.W * p.C, rstep = (int64_t)p.sh * p.W * p.C, cstep = (int64_t)p.sw * p.C;
+  const uint32_t bytes = (uint32_t)((int64_t)p.N * p.H * p.W * p.C * 2);
+  if (strided && count <= kMaxConvPhases) {
+    // every phase in one launch, longest reduction first
+    int order[kMaxConvPhases];
+    for (int i = 0; i < count; ++i) order[i] = i;
+    for (int i = 1; i < count; ++i)  // insertion sort: stable, by taps descending
+      for (int j = i; j > 0 && phases[order[j]].f.R * phases[order[j]].f.S >
+                                   phases[order[j - 1]].f.R * phases[order[j - 1]].f.S;
+           --j) {
+        const int t = order[j];
+        order[j] = order[j - 1];
+        order[j - 1] = t;
+      }
+    int64_t Ms[kMaxConvPhases];
+    for (int i = 0; i < count; ++i) Ms[i] = (int64_t)p.N * phases[i].f.P * phases[i].f.Q;
+    const int shape = conv_shape_multi(Ms, count, p.C);
+    const int bm = tile_bm(shape), bn = tile_bn(shape), bk = conv_bk(shape);
+    PhasesArgs a;
+    a.count = count;
+    a.tiles_n = (p.C + bn - 1) / bn;
+    a.Nk = p.C;
+    a.c = p.c;
+    a.y = p.y;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.map_img = img;
+    a.map_rstep = rstep;
+    a.map_cstep = cstep;
+    a.map_bytes = bytes;
+    int64_t tiles = 0;
+    for (int i = 0; i < count; ++i) {
+      const ConvLaunch& f = phases[order[i]].f;
+      PhaseDesc& d = a.ph[i];
+      d.g = ConvGeom{f.x, (uint32_t)((int64_t)f.N * f.H * f.W * f.C * 2), f.H, f.W, f.C, f.S, f.P, f.Q,
+                     f.ph, f.pw, 1, 1, f.dh, f.dw, f.R * f.S * f.C, 0, 0};
+      if (f.R * f.S > 1 && f.C % bk == 0) {  // channel-block-major k order, as in the single launch
+        d.g.prs = f.R * f.S;
+        d.g.pcb = f.C / bk;
+      }
+      d.w = f.w;
+      d.map_off0 = phases[order[i]].off0;
+      d.M = f.N * f.P * f.Q;
+      d.Hp = f.P;
+      d.Wp = f.Q;
+      d.tile_start = (int)tiles;
+      tiles += (int64_t)((d.M + bm - 1) / bm) * a.tiles_n;
+    }
+    if (tiles > INT32_MAX) return hipErrorInvalidValue;
+    a.total_tiles = (int)tiles;
+    if (shape == TILE_256x256) return launch_phases<ConvCfg256>(a, dtype, stream);
+    if (shape == TILE_256x128) return launch_phases<ConvCfg256x128>(a, dtype, stream);
+    return launch_phases<ConvCfg128>(a, dtype, stream);
+  }
+  // stride 1, or more phases than one launch carries: a launch per phase
+  for (int i = 0; i < count; ++i) {
+    ConvLaunch f = phases[i].f;
+    if (strided) {
+      f.map_off0 = phases[i].off0;
+      f.map_img = img;
+      f.map_rstep = rstep;
+      f.map_cstep = cstep;
+      f.map_bytes = bytes;
+    }
+    const hipError_t e =
+        launch_conv_fprop(f, conv_shape((int64_t)p.N * f.P * f.Q, p.C), dtype, alpha, beta, stream);
+    if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }

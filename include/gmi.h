@@ -382,7 +382,8 @@ gmi_status gmi_conv2d_wgrad_implicit(int32_t N, int32_t H, int32_t W, int32_t C,
  * (rows h with h + ph in one residue class of sh, crossed with the columns'
  * classes), and each phase gathers dy over only the taps that reach it
  * (r*dh = h + ph mod sh), so no multiply touches a tap that misses; a phase
- * that no tap reaches gets alpha * 0 + beta * c_in.
+ * that no tap reaches gets alpha * 0 + beta * c_in.  Up to 16 phases run as
+ * one launch (longest reduction first), more as a launch per phase.
  *   workspace  at least gmi_conv2d_dgrad_workspace_bytes(C, K, R, S) bytes,
  *              16-byte aligned: the filter rearranged per phase, [C][taps of
  *              the phase][K], one phase after another (the phases partition

@@ -1,10 +1,12 @@
 """GPU parity of the implicit-GEMM conv2d data gradient against the fp64
 oracle, which computes it as the adjoint of the forward convolution.  A
-stride above 1 runs one launch per output phase (the rows h with h + pad in
+stride above 1 runs by output phase (the rows h with h + pad in
 one residue class of the stride, crossed with the columns' classes), each
 gathering only the filter taps that reach that phase; the strided cases cover
 unequal and odd strides, filters narrower than the stride, and dilations that
-share a factor with the stride, which leave whole phases without a tap."""
+share a factor with the stride, which leave whole phases without a tap.
+Up to 16 phases (strides up to 4 x 4) run as one launch, more as a launch
+per phase; the cases cover both."""
 import numpy as np
 import pytest
 import torch
