@@ -135,7 +135,8 @@ def roof(flops, bytes_, t, peak=PEAK_MFMA_16, bound=None):
     gbs = bytes_ / sec / 1e9
     f_mfma, f_hbm = tf / peak, gbs / PEAK_HBM
     return dict(us=round(ms * 1e3, 3), us_min=round(t["min_ms"] * 1e3, 3), us_max=round(t["max_ms"] * 1e3, 3),
-                launches_per_window=t["launches_per_window"], tflops=round(tf, 2), frac_mfma=round(f_mfma, 4),
+                launches_per_window=t["launches_per_window"], ramp_launches=t["ramp_launches"], tflops=round(tf, 2),
+                frac_mfma=round(f_mfma, 4),
                 gbps=round(gbs, 1), frac_hbm=round(f_hbm, 4), roofline_frac=round(max(f_mfma, f_hbm), 4),
                 bound=bound or ("mfma" if f_mfma >= f_hbm else "hbm"))
 

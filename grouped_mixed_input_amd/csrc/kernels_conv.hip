@@ -243,21 +243,42 @@ struct TapMap {
 };
 
 // out[c][b][a] = in[a][taps(b)][c] for a < A, 0 for A <= a < Ap (in holds
-// Bin taps per a, out Bout): one 64 x 64 (a, c) block of one b per workgroup
-// (b in grid z, looping past 65535), moved in 16-byte runs: 8 consecutive c
-// on the way in, 8 consecutive a on the way out (C % 8 == 0, Ap % 8 == 0).
-__global__ __launch_bounds__(256) void k_transpose_outer(const uint16_t* __restrict__ in, uint16_t* __restrict__ out,
-                                                         int A, int Bin, int Bout, int C, int Ap, TapMap taps) {
+// Bin taps per a, out Bout): one 64 x 64 (a, c) block of one b per workgroup,
+// moved in 16-byte runs: 8 consecutive c on the way in, 8 consecutive a on
+// the way out (C % 8 == 0, Ap % 8 == 0).  One launch runs a table of such
+// jobs (the filter slices of every phase of a strided data gradient, or x
+// and dy of a weight gradient): grid z walks the jobs' b one after another,
+// and each job ignores the (a, c) blocks past its own extent.
+constexpr int kMaxTransposeJobs = 16;
+struct TransposeJob {
+  const uint16_t* in;
+  uint16_t* out;
+  int A, Bin, Bout, C, Ap;
+  TapMap taps;
+  int z0;  // first b of the job in the launch's walk
+};
+struct TransposeJobs {
+  TransposeJob job[kMaxTransposeJobs];
+  int count, total;  // jobs; sum of their Bout
+};
+static_assert(sizeof(TransposeJobs) <= 4096, "kernel arguments are limited to 4 KB");
+
+__global__ __launch_bounds__(256) void k_transpose_outer(TransposeJobs jobs) {
   __shared__ uint16_t t[64][72];
-  const int a0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   const int row = threadIdx.x / 8, vec = threadIdx.x % 8;
-  for (int b = blockIdx.z; b < Bout; b += gridDim.z) {
-    const int bi = taps(b);
+  const TransposeJob* js = jobs.job;
+  for (int z = blockIdx.z; z < jobs.total; z += gridDim.z) {
+    int q = 0;
+    for (int i = 1; i < jobs.count; ++i) q = z >= js[i].z0 ? i : q;
+    const TransposeJob& jb = js[q];
+    const int a0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+    if (a0 >= jb.Ap || c0 >= jb.C) continue;  // past this job's extent: the whole workgroup skips alike
+    const int b = z - jb.z0, bi = jb.taps(b);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int aa = row + 32 * j, a = a0 + aa, c = c0 + vec * 8;
       u32x4 v = {0, 0, 0, 0};
-      if (a < A && c < C) v = *(const u32x4*)(in + ((int64_t)a * Bin + bi) * C + c);
+      if (a < jb.A && c < jb.C) v = *(const u32x4*)(jb.in + ((int64_t)a * jb.Bin + bi) * jb.C + c);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         t[aa][vec * 8 + 2 * e] = (uint16_t)(v[e] & 0xffffu);
@@ -268,23 +289,47 @@ __global__ __launch_bounds__(256) void k_transpose_outer(const uint16_t* __restr
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int cc = row + 32 * j, c = c0 + cc, a = a0 + vec * 8;
-      if (c < C && a < Ap) {
+      if (c < jb.C && a < jb.Ap) {
         u32x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = (uint32_t)t[vec * 8 + 2 * e][cc] | ((uint32_t)t[vec * 8 + 2 * e + 1][cc] << 16);
-        *(u32x4*)(out + ((int64_t)c * Bout + b) * Ap + a) = v;
+        *(u32x4*)(jb.out + ((int64_t)c * jb.Bout + b) * jb.Ap + a) = v;
       }
     }
     __syncthreads();
   }
 }
 
-// out[c][b][a] = in[a][b][c], every tap in order
-static hipError_t transpose_outer(const uint16_t* in, uint16_t* out, int A, int B, int C, int Ap,
-                                  hipStream_t stream, TapMap taps = TapMap{1 << 30, 0, 0, 0, 1, 1}, int Bin = -1) {
-  const dim3 grid((C + 63) / 64, (Ap + 63) / 64, B < 65535 ? B : 65535);
-  hipLaunchKernelGGL(k_transpose_outer, grid, dim3(256), 0, stream, in, out, A, Bin < 0 ? B : Bin, B, C, Ap, taps);
+// every job of the table in one launch
+static hipError_t transpose_jobs(TransposeJobs& jobs, hipStream_t stream) {
+  int cmax = 0, amax = 0, z = 0;
+  for (int i = 0; i < jobs.count; ++i) {
+    jobs.job[i].z0 = z;
+    z += jobs.job[i].Bout;
+    cmax = jobs.job[i].C > cmax ? jobs.job[i].C : cmax;
+    amax = jobs.job[i].Ap > amax ? jobs.job[i].Ap : amax;
+  }
+  jobs.total = z;
+  if (z == 0) return hipSuccess;
+  const dim3 grid((cmax + 63) / 64, (amax + 63) / 64, z < 65535 ? z : 65535);
+  hipLaunchKernelGGL(k_transpose_outer, grid, dim3(256), 0, stream, jobs);
   return hipGetLastError();
+}
+
+// out[c][b][a] = in[a][taps(b)][c] as a job (every tap in order by default)
+static TransposeJob transpose_job(const uint16_t* in, uint16_t* out, int A, int B, int C, int Ap,
+                                  TapMap taps = TapMap{1 << 30, 0, 0, 0, 1, 1}, int Bin = -1) {
+  TransposeJob j;
+  j.in = in;
+  j.out = out;
+  j.A = A;
+  j.Bin = Bin < 0 ? B : Bin;
+  j.Bout = B;
+  j.C = C;
+  j.Ap = Ap;
+  j.taps = taps;
+  j.z0 = 0;
+  return j;
 }
 
 static int floor_div(int a, int b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }  // b > 0
@@ -373,6 +418,8 @@ hipError_t launch_conv_dgrad(const ConvLaunch& p, uint16_t* wt, int dtype, float
   Phase phases[64];
   int count = 0;
   int64_t woff = 0;  // the phases' filter slices, one after another
+  TransposeJobs jobs;  // their rearrangement, kMaxTransposeJobs slices per launch
+  jobs.count = 0;
   for (int a = 0; a < p.sh; ++a) {
     const Phase1D ph = phase_1d(a, p.R, p.ph, p.sh, p.dh, p.H);
     if (ph.size == 0) continue;
@@ -382,15 +429,23 @@ hipError_t launch_conv_dgrad(const ConvLaunch& p, uint16_t* wt, int dtype, float
       uint16_t* wp = wt + woff;
       const int taps = ph.count * pw.count;
       if (taps > 0) {
-        const hipError_t e = transpose_outer(p.w, wp, p.K, taps, p.C, p.K, stream,
-                                             TapMap{pw.count, ph.first, ph.step, pw.first, pw.step, p.S}, p.R * p.S);
-        if (e != hipSuccess) return e;
+        if (jobs.count == kMaxTransposeJobs) {
+          const hipError_t e = transpose_jobs(jobs, stream);
+          if (e != hipSuccess) return e;
+          jobs.count = 0;
+        }
+        jobs.job[jobs.count++] = transpose_job(p.w, wp, p.K, taps, p.C, p.K,
+                                               TapMap{pw.count, ph.first, ph.step, pw.first, pw.step, p.S}, p.R * p.S);
         woff += (int64_t)taps * p.C * p.K;
       }
       phases[count].f = phase_view(p, ph, pw, wp);
       phases[count].off0 = ((int64_t)(a - p.ph + p.sh * ph.lo) * p.W + (b - p.pw + p.sw * pw.lo)) * p.C;
       ++count;
     }
+  }
+  if (jobs.count > 0) {
+    const hipError_t e = transpose_jobs(jobs, stream);
+    if (e != hipSuccess) return e;
   }
   const int64_t img = (int64_t)p.H * p.W * p.C, rstep = (int64_t)p.sh * p.W * p.C, cstep = (int64_t)p.sw * p.C;
   const uint32_t bytes = (uint32_t)((int64_t)p.N * p.H * p.W * p.C * 2);
@@ -589,9 +644,11 @@ hipError_t launch_conv_wgrad(const WgradPlan& p, const uint16_t* x, const uint16
   uint16_t* xt = (uint16_t*)(workspace + p.x_off);
   uint16_t* gt = (uint16_t*)(workspace + p.dy_off);
   float* part = (float*)(workspace + p.part_off);
-  hipError_t e = transpose_outer(x, xt, p.N, p.H * p.W, p.C, p.N8, stream);
-  if (e != hipSuccess) return e;
-  e = transpose_outer(dy, gt, p.N, p.P * p.Q, p.K, p.N8, stream);
+  TransposeJobs jobs;  // x and dy to the channel-innermost layout, in one launch
+  jobs.count = 2;
+  jobs.job[0] = transpose_job(x, xt, p.N, p.H * p.W, p.C, p.N8);
+  jobs.job[1] = transpose_job(dy, gt, p.N, p.P * p.Q, p.K, p.N8);
+  hipError_t e = transpose_jobs(jobs, stream);
   if (e != hipSuccess) return e;
   ConvLaunch f;  // the forward view, one problem per channel group
   f.x = xt;
