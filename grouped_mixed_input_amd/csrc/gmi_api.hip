@@ -483,10 +483,10 @@ static gmi_status mixed_gemm(const char* who, int32_t M, int32_t N, int32_t K, g
   const gmi_status st = mixed_prepare(who, M, N, K, x_dtype, X, ldx, w_prepacked, w_type, scales, zeros, group_size,
                                       Y, ldy, a, nothing);
   if (st != GMI_OK || nothing) return st;
-  const size_t need = gmi_w4a16_workspace_bytes(M, N, K);
+  const size_t need = w4a16_workspace_for(M, N, K, a.dt);
   if (need > 0 && workspace && workspace_bytes >= need) {
     if (!aligned16(workspace)) return fail(GMI_ERR_MISALIGNED, "%s: workspace must be 16-byte aligned", who);
-    a.split = w4a16_split(M, N, K);
+    a.split = w4a16_split(M, N, K, a.dt);
     a.partial = (float*)workspace;
   }
   return hip_status(launch_w4a16(a, (hipStream_t)stream), who);

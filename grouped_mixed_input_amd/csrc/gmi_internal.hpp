@@ -130,10 +130,13 @@ struct LaunchTimer {
   hipEvent_t start = nullptr, stop = nullptr;
 };
 LaunchTimer& launch_timer();
-// k-ranges per output tile the W4A16 GEMM uses for this shape on the current
-// device (1 when the tiles alone fill the device or the path is skinny)
-int w4a16_split(int M, int N, int K);
-// bytes of fp32 partial products that split needs (0 without a split)
+// k-ranges per output tile the W4A16 GEMM uses for this shape and activation
+// type on the current device (1 when the tiles alone fill the device or the
+// path is skinny)
+int w4a16_split(int M, int N, int K, int dt);
+// bytes of fp32 partial products that split needs (0 without a split), for
+// one type and the larger of the two
+size_t w4a16_workspace_for(int M, int N, int K, int dt);
 size_t w4a16_workspace(int M, int N, int K);
 
 hipError_t launch_grouped(const GroupDesc* desc_dev, int count, int total_tiles, int shape, int dtype, bool ktail,

@@ -860,22 +860,30 @@ using W4Cfg128 = TileCfg<128, 128, 2, 2, 64, 2>;
 // device, else 128 x 128 (two workgroups per CU).
 static bool w4_big_tiles(int M, int N, int cus) { return ((M + 255) / 256) * ((N + 255) / 256) >= cus; }
 
-size_t w4a16_workspace(int M, int N, int K) {
-  const int split = w4a16_split(M, N, K);
+size_t w4a16_workspace_for(int M, int N, int K, int dt) {
+  const int split = w4a16_split(M, N, K, dt);
   if (split <= 1) return 0;
   const size_t tiles = (size_t)((M + kRsTokens - 1) / kRsTokens) * (size_t)((N + 127) / 128);
   return (size_t)split * tiles * kRsTileFloats * sizeof(float);
 }
 
-int w4a16_split(int M, int N, int K) {
+size_t w4a16_workspace(int M, int N, int K) {
+  const size_t f = w4a16_workspace_for(M, N, K, DT_F16), b = w4a16_workspace_for(M, N, K, DT_BF16);
+  return f > b ? f : b;
+}
+
+int w4a16_split(int M, int N, int K, int dt) {
   if (M <= 64) return 1;  // decode / skinny kernels
   const int cus = device_cu_count();
   if (w4_big_tiles(M, N, cus)) return 1;
   const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  // k-ranges of whole 128-k blocks, at least 8 k-tiles each, until the work
+  // items cover every CU once (fp16, up to four) or fill both workgroup slots
+  // of every CU (bf16, up to eight: its exact conversion and scale folds give
+  // a second wave per SIMD more to overlap than the extra partials cost)
+  const int most = dt == DT_BF16 ? 8 : 4, items = dt == DT_BF16 ? 2 * cus : cus;
   int split = 1;
-  // up to four k-ranges of whole 128-k blocks, at least 8 k-tiles each, until
-  // the work items cover every CU once
-  while (split < 4 && tiles * split < cus && K % (128 * split * 2) == 0 && K / (split * 2) >= 512) split *= 2;
+  while (split < most && tiles * split < items && K % (128 * split * 2) == 0 && K / (split * 2) >= 512) split *= 2;
   return split;
 }
 

@@ -183,11 +183,14 @@ size_t gmi_prepack_w4_bytes(int32_t N, int32_t K);
  * A bijection on the N*K/2 bytes; `w_u4` and `w_prepacked` must not overlap. */
 gmi_status gmi_prepack_w4(const uint8_t* w_u4, int32_t N, int32_t K, uint8_t* w_prepacked, void* stream);
 
-/* Bytes of the optional workspace that lets gmi_gemm_w4a16 split K across
- * workgroups for this shape on the current device: fp32 partial products of
- * the k-ranges for every 128 x 128 output tile (rows rounded up to 128
- * tokens, columns to 128 weight rows), summed in k-range order by a second
- * launch; 0 when no split is used.  The layout is private to the library. */
+/* Bytes of the optional workspace that lets gmi_gemm_w4a16 and
+ * gmi_gemm_mixed split K across workgroups for this shape on the current
+ * device: fp32 partial products of the k-ranges for every 128 x 128 output
+ * tile (rows rounded up to 128 tokens, columns to 128 weight rows), summed in
+ * k-range order by a second launch; 0 when no split is used.  bf16
+ * activations may use more k-ranges than fp16; the size covers either type,
+ * and a call whose workspace is smaller than its own type needs runs
+ * unsplit.  The layout is private to the library. */
 size_t gmi_w4a16_workspace_bytes(int32_t M, int32_t N, int32_t K);
 
 /* Mixed-input GEMM Y = X W^T, 4-bit weights with per-group scales and zero

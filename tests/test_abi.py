@@ -294,14 +294,17 @@ def test_conv_wgrad_validation(gmi):
 
 def test_w4a16_workspace_bytes(gmi):
     # without a device the library assumes 256 CUs, as on MI355X: 128 x 8192 has 64 output tiles of
-    # 128 x 128, so four k-ranges of fp32 partials, each a whole tile of 128 x 128 floats (ragged row
-    # counts round up to 128 tokens); decode shapes and shapes that fill the device use none
+    # 128 x 128; fp16 splits K into up to four k-ranges (until the items cover 256 CUs), bf16 into up to
+    # eight (until they cover 512 workgroup slots), and the size is the larger need: fp32 partials, a whole
+    # tile of 128 x 128 floats per range (ragged row counts round up to 128 tokens); decode shapes and
+    # shapes that fill the device use none
     L = gmi.lib()
     tile = 128 * 128 * 4
-    assert L.gmi_w4a16_workspace_bytes(128, 8192, 8192) == 4 * 64 * tile
-    assert L.gmi_w4a16_workspace_bytes(100, 8192, 8192) == 4 * 64 * tile
-    assert L.gmi_w4a16_workspace_bytes(200, 8192, 8192) == 2 * 128 * tile  # 128 tiles: two ranges cover 256 CUs
-    assert L.gmi_w4a16_workspace_bytes(128, 8000, 8192) == 4 * 63 * tile  # 8000 rows: 63 tiles of 128
+    assert L.gmi_w4a16_workspace_bytes(128, 8192, 8192) == 8 * 64 * tile
+    assert L.gmi_w4a16_workspace_bytes(100, 8192, 8192) == 8 * 64 * tile
+    assert L.gmi_w4a16_workspace_bytes(200, 8192, 8192) == 4 * 128 * tile  # 128 tiles: four bf16 ranges fill 512
+    assert L.gmi_w4a16_workspace_bytes(128, 8000, 8192) == 8 * 63 * tile  # 8000 rows: 63 tiles of 128
+    assert L.gmi_w4a16_workspace_bytes(128, 8192, 2048) == 4 * 64 * tile  # eight ranges would hold 256 k
     assert L.gmi_w4a16_workspace_bytes(16, 8192, 8192) == 0
     assert L.gmi_w4a16_workspace_bytes(4096, 8192, 8192) == 0
     assert L.gmi_w4a16_workspace_bytes(128, 8192, 1024) == 2 * 64 * tile  # k-ranges keep >= 512 k each

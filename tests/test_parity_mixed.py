@@ -86,6 +86,21 @@ def test_mixed_bf16_split_k(gmi):
     _check(got, ref, "bf16", "mixed bf16 split-K")
 
 
+def test_mixed_split_ranges_per_type_and_short_workspace(gmi):
+    # M = 160, N = 256, K = 4096: four output tiles.  bf16 splits K into eight k-ranges, fp16 into four, and
+    # the workspace size covers the larger; a bf16 call given only what fp16 needs runs unsplit.  Every
+    # variant meets the oracle on every output.
+    M, N, K, group = 160, 256, 4096, 128
+    tile = 128 * 128 * 4
+    assert gmi.w4a16_workspace_bytes(M, N, K) == 8 * 4 * tile
+    for dtype, sizes in (("bf16", (8 * 4 * tile, 4 * 4 * tile, 0)), ("f16", (8 * 4 * tile, 4 * 4 * tile))):
+        X, W, S, Z = _case(M, N, K, group, dtype, seed=31 + len(dtype))
+        for nbytes in sizes:
+            ws = torch.full((nbytes,), 0x7F, dtype=torch.uint8, device=dev())
+            got, ref = _run(gmi, X, W, S, Z, M, N, K, group, dtype, "int4", "zero", workspace=ws)
+            _check(got, ref, dtype, f"mixed {dtype} workspace {nbytes} bytes")
+
+
 def test_mixed_f16_uint4_zero_mode_is_w4a16_bit_for_bit(gmi):
     # gmi_gemm_w4a16 is the fp16 / uint4 / zero-point case of gmi_gemm_mixed
     for M in (8, 48, 160):
