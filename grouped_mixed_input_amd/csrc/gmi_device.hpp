@@ -594,7 +594,8 @@ __device__ __forceinline__ u32x4 dequant8_bf16(uint32_t w, float s, float nzs) {
 // at most 4 significant bits), in the order of dequant8_bf16: the integer
 // part only, for kernels that apply the group scale to fp32 partial sums.
 __device__ __forceinline__ u32x4 exact8_bf16(uint32_t w, float zf) {
-  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  asm("" : "+v"(lo), "+v"(hi));
   auto d = [&](uint32_t v, int i) { return ubyte_f32(v, i) - zf; };
   u32x4 out;
   out[0] = pack2<DT_BF16>(d(lo, 0), d(lo, 2));

@@ -663,11 +663,16 @@ struct RsRing {
   static_assert(2 * BYTES <= 160 * 1024, "two workgroups per CU");
 };
 
-template <int DT, int WB, int MT, int D>
+// GK: k-tiles per scale group when the caller knows it (0: found per k-tile).
+// With GK fixed, the group boundaries fall on fixed steps of the unrolled
+// loop: a group's first multiply starts its partial from zero and its last
+// k-tile folds the partial in, with no per-step test and no reset.
+template <int DT, int WB, int MT, int D, int GK = 0>
 __device__ __forceinline__ void rs_mainloop(char* lds, const DenseLoader<RsXCfg, RsXCfg::BM>& xl,
                                             const RsWeights<DT, WB>& wl, int nk, f32x4 (&acc)[WB][MT]) {
   using Ring = RsRing<DT, WB, MT, D>;
   constexpr bool EXACT = DT == DT_BF16;
+  static_assert(GK == 0 || (EXACT && (D + 1) % GK == 0), "fixed groups align with the unrolled steps");
   constexpr int YOUNG = RsXCfg::NW == 4 ? DenseLoader<RsXCfg, RsXCfg::BM>::P + RsWeights<DT, WB>::LOADS : 0;
   static_assert((D - 1) * YOUNG < 64, "the k-tiles left in flight fit the vmcnt counter");
   const int lane = threadIdx.x & 63;
@@ -730,14 +735,29 @@ __device__ __forceinline__ void rs_mainloop(char* lds, const DenseLoader<RsXCfg,
               wf = dequant8(wq, z, scale_pair((cur.s[b][0] & 0xffffu) | wl.sor), magic);
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-              if constexpr (EXACT)
-                part[b][mt] = mfma16<DT>(wf, xf[mt], part[b][mt]);
-              else
+              if constexpr (EXACT) {
+                if (GK != 0 && J % (GK == 0 ? 1 : GK) == 0 && j == 0)
+                  part[b][mt] = mfma16<DT>(wf, xf[mt], f32x4{0, 0, 0, 0});
+                else
+                  part[b][mt] = mfma16<DT>(wf, xf[mt], part[b][mt]);
+              } else {
                 acc[b][mt] = mfma16<DT>(wf, xf[mt], acc[b][mt]);
+              }
             }
           }
         }
-        if constexpr (EXACT) {
+        if constexpr (EXACT && GK != 0) {
+          if constexpr (J % (GK == 0 ? 1 : GK) == (GK == 0 ? 0 : GK - 1)) {
+#pragma unroll
+            for (int b = 0; b < WB; ++b)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float si = from_bits<DT_BF16>(((cur.s[b][i / 2] >> (16 * (i % 2))) & 0xffffu) | wl.sor);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) acc[b][mt][i] = __builtin_fmaf(si, part[b][mt][i], acc[b][mt][i]);
+              }
+          }
+        } else if constexpr (EXACT) {
           if (wl.group_ends(kt, nk)) {
 #pragma unroll
             for (int b = 0; b < WB; ++b)
@@ -828,7 +848,9 @@ __global__ __launch_bounds__(256) void k_w4a16_rs_sum(const float* __restrict__ 
 // one k-range of X in its L2 (each item's weights are its own); inside a
 // k-range the tiles go in bands of kW4Band row tiles, row tile fastest, so
 // the run covers a few X row tiles by a few weight panels
-template <int DT, int WB>
+// GK: k-tiles per scale group, fixed at compile time (2: bf16 with 128-k
+// groups, whose k-ranges are whole 128-k blocks), or 0 to test per k-tile
+template <int DT, int WB, int GK>
 __global__ __launch_bounds__(256, 2) void k_w4a16_rs(W4Launch a, int tiles_m, int total_work) {
   constexpr int MT = kRsTokens / 16, D = kRsDepth;
   __shared__ __attribute__((aligned(16))) char lds[RsRing<DT, WB, MT, D>::BYTES];
@@ -848,7 +870,7 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_rs(W4Launch a, int tiles_m, in
     RsWeights<DT, WB> wl;
     wl.init(a, n_base, k0 / 64);
     f32x4 acc[WB][MT];
-    rs_mainloop<DT, WB, MT, D>(lds, xl, wl, Ks / 64, acc);
+    rs_mainloop<DT, WB, MT, D, GK>(lds, xl, wl, Ks / 64, acc);
     rs_store<DT, WB, MT>(a, acc, m0, n_base, tile, sidx);
   }
 }
@@ -928,7 +950,11 @@ static hipError_t launch_w4a16_dt(const W4Launch& a, hipStream_t stream) {
     const int total = tiles * a.split;
     int grid = (total + XCDS - 1) / XCDS * XCDS;
     if (grid > 2 * cus) grid = 2 * cus / XCDS * XCDS;
-    hipLaunchKernelGGL((k_w4a16_rs<DT, WB>), dim3(grid), dim3(256), 0, stream, a, tiles_m, total);
+    if (DT == DT_BF16 && a.group == 128)
+      hipLaunchKernelGGL((k_w4a16_rs<DT, WB, DT == DT_BF16 ? 2 : 0>), dim3(grid), dim3(256), 0, stream, a, tiles_m,
+                         total);
+    else
+      hipLaunchKernelGGL((k_w4a16_rs<DT, WB, 0>), dim3(grid), dim3(256), 0, stream, a, tiles_m, total);
     if (a.split > 1) {
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
@@ -1003,7 +1029,7 @@ __device__ __forceinline__ int wave_sum(int v) {
   return v;
 }
 
-template <int DT>
+template <int DT, int GK>
 __global__ __launch_bounds__(256, 2) void k_w4a16_grouped_tiled(W4Grouped a) {
   constexpr int WB = 2, MT = kRsTokens / 16, D = kRsDepth, BM = kRsTokens, BN = 64 * WB;
   __shared__ __attribute__((aligned(16))) char lds[RsRing<DT, WB, MT, D>::BYTES];
@@ -1075,7 +1101,7 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_grouped_tiled(W4Grouped a) {
     RsWeights<DT, WB> wl;
     wl.init(p, n_base, 0);
     f32x4 acc[WB][MT];
-    rs_mainloop<DT, WB, MT, D>(lds, xl, wl, p.K / 64, acc);
+    rs_mainloop<DT, WB, MT, D, GK>(lds, xl, wl, p.K / 64, acc);
     rs_store<DT, WB, MT>(p, acc, m0, n_base, 0, 0);
   }
 }
@@ -1134,10 +1160,12 @@ hipError_t launch_w4a16_grouped(const W4Grouped& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   int g1 = device_cu_count() * 2 / XCDS * XCDS;
   if (g1 < XCDS) g1 = XCDS;
-  if (a.base.dt == DT_BF16)
-    hipLaunchKernelGGL(k_w4a16_grouped_tiled<DT_BF16>, dim3(g1), dim3(256), 0, stream, a);
+  if (a.base.dt == DT_BF16 && a.base.group == 128)
+    hipLaunchKernelGGL((k_w4a16_grouped_tiled<DT_BF16, 2>), dim3(g1), dim3(256), 0, stream, a);
+  else if (a.base.dt == DT_BF16)
+    hipLaunchKernelGGL((k_w4a16_grouped_tiled<DT_BF16, 0>), dim3(g1), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(k_w4a16_grouped_tiled<DT_F16>, dim3(g1), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((k_w4a16_grouped_tiled<DT_F16, 0>), dim3(g1), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
