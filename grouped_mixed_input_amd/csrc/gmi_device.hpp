@@ -149,6 +149,17 @@ __device__ __forceinline__ uint32_t buf_load2(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ uint32_t buf_load1(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
 }
+// as above, with a wave-uniform byte offset soff (an SGPR) added to the lane
+// offset; a lane at OOB stays past the resource for any soff below 2^31
+__device__ __forceinline__ u32x2 buf_load8s(rsrc_t r, uint32_t off, uint32_t soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, (int)soff, 0));
+}
+__device__ __forceinline__ uint32_t buf_load2s(rsrc_t r, uint32_t off, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, (int)soff, 0);
+}
+__device__ __forceinline__ uint32_t buf_load1s(rsrc_t r, uint32_t off, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, (int)off, (int)soff, 0);
+}
 // Output stores are streaming (nt): each result is written once and not read
 // back by the kernel, so the L2 sends it on toward memory instead of holding it
 // dirty until the end-of-kernel writeback, which would serialize the whole

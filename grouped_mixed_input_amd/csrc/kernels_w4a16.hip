@@ -621,33 +621,42 @@ struct RsWeights {
   static constexpr bool EXACT = DT == DT_BF16;
   static constexpr int LOADS = 3 * WB;  // weight words, zero point, scales per block
   rsrc_t rw, rs, rz;
-  uint32_t kblocks, N, group, blk0, kt0, sor, wxor, zxor;
+  uint32_t N, group, kt0, sor, wxor, zxor;
+  // lane offsets of each block's weight entry, zero point and scales (OOB for
+  // a block past N); the k-tile's offsets are wave-uniform and go in soffset
+  uint32_t vw[WB], vz[WB], vs[WB];
   __device__ __forceinline__ void init(const W4Launch& a, int n_base, int kt_first) {
     rw = make_rsrc(a.w, (uint32_t)((int64_t)a.N * a.K / 2));
     rs = make_rsrc(a.scales, a.s_bytes);
     rz = make_rsrc(a.zeros, a.z_bytes);
-    kblocks = a.K / 128;
     N = a.N;
     group = a.group;
-    blk0 = n_base / 16 + wave_id() * WB;
     kt0 = kt_first;
     sor = a.sor;
     wxor = a.wxor;
     zxor = a.zxor;
-  }
-  __device__ __forceinline__ void load(int kt_local, RsRegs<WB>& r) const {
-    const uint32_t kt = kt_local + kt0, lane = threadIdx.x & 63;
-    const uint32_t grp = (kt * 64) / group;
+    const uint32_t kblocks = a.K / 128, blk0 = n_base / 16 + wave_id() * WB, lane = threadIdx.x & 63;
 #pragma unroll
     for (int b = 0; b < WB; ++b) {
       const uint32_t blk = blk0 + b, n = blk * 16 + lane % 16;
       const bool ok = blk * 16 < N;
-      r.w[b] = buf_load8(rw, ok ? (blk * kblocks + kt / 2) * 1024u + lane * 16u + (kt & 1) * 8u : OOB);
-      r.z[b] = buf_load1(rz, ok ? grp * (N / 2) + n / 2 : OOB);
+      vw[b] = ok ? blk * kblocks * 1024u + lane * 16u : OOB;
+      vz[b] = ok ? n / 2 : OOB;
+      vs[b] = ok ? (EXACT ? (blk * 16 + 4 * (lane / 16)) * 2u : n * 2u) : OOB;
+    }
+  }
+  __device__ __forceinline__ void load(int kt_local, RsRegs<WB>& r) const {
+    const uint32_t kt = kt_local + kt0;
+    const uint32_t grp = (kt * 64) / group;
+    const uint32_t sw = (kt / 2) * 1024u + (kt & 1) * 8u, sz = grp * (N / 2), ss = grp * N * 2u;
+#pragma unroll
+    for (int b = 0; b < WB; ++b) {
+      r.w[b] = buf_load8s(rw, vw[b], sw);
+      r.z[b] = buf_load1s(rz, vz[b], sz);
       if constexpr (EXACT)
-        r.s[b] = buf_load8(rs, ok ? (grp * N + blk * 16 + 4 * (lane / 16)) * 2u : OOB);
+        r.s[b] = buf_load8s(rs, vs[b], ss);
       else
-        r.s[b] = u32x2{buf_load2(rs, ok ? (grp * N + n) * 2u : OOB), 0u};
+        r.s[b] = u32x2{buf_load2s(rs, vs[b], ss), 0u};
     }
   }
   __device__ __forceinline__ bool group_ends(int kt_local, int nk) const {
