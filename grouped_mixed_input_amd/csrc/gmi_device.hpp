@@ -606,6 +606,9 @@ __device__ __forceinline__ u32x4 dequant8_bf16(uint32_t w, float s, float nzs) {
 // part only, for kernels that apply the group scale to fp32 partial sums.
 __device__ __forceinline__ u32x4 exact8_bf16(uint32_t w, float zf) {
   uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  // hide the masks from the compiler: knowing each byte's high bits are
+  // zero, it extracts every nibble with a bit-field extract before a byte-0
+  // convert; opaque, each byte converts with one v_cvt_f32_ubyteN
   asm("" : "+v"(lo), "+v"(hi));
   auto d = [&](uint32_t v, int i) { return ubyte_f32(v, i) - zf; };
   u32x4 out;
