@@ -569,8 +569,12 @@ bool plan_wgrad(int N, int H, int W, int C, int K, int R, int S, int ph, int pw,
   const int64_t tiles =
       groups * ((Mv + WgradCfg::BM - 1) / WgradCfg::BM * ((p.kg + WgradCfg::BN - 1) / WgradCfg::BN));
   const int64_t nkt = (Kg + WgradCfg::BK - 1) / WgradCfg::BK;
-  int64_t split = (device_cu_count() + tiles - 1) / tiles;  // one work item per CU at least
-  if (split > nkt / 8) split = nkt / 8;                     // at least 8 k-tiles per item
+  // as many k-ranges as keep every work item in one round of the resident
+  // workgroups (a second round for a few items would double the launch), with
+  // at least 8 k-tiles per item
+  const int64_t slots = (int64_t)device_cu_count() * WgradCfg::WGS_PER_CU;
+  int64_t split = slots / tiles;
+  if (split > nkt / 8) split = nkt / 8;
   if (split < 1) split = 1;
   p.kt_split = (int)((nkt + split - 1) / split);
   p.split = (int)((nkt + p.kt_split - 1) / p.kt_split);
