@@ -168,6 +168,12 @@ constexpr int CPOL_NT = 2;
 __device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, CPOL_NT);
 }
+// a plain (write-back) 16-byte store: for data written in pieces of a line
+// by several instructions and read again soon, which the L2 then merges
+// into whole lines instead of sending each piece on
+__device__ __forceinline__ void buf_store16_wb(rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
 __device__ __forceinline__ void buf_store8(rsrc_t r, uint32_t off, u32x2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, CPOL_NT);
 }
@@ -1147,7 +1153,7 @@ __device__ __forceinline__ void store_partial(const Tile& t, const f32x16 (&acc)
         const uint32_t row = wm + 32 * i + (lane & 31);
         const int col = t.n0 + wn + 32 * j + 8 * q + 4 * (lane >> 5);
         if (col < t.N)
-          buf_store16(rp, (row * (uint32_t)t.N + col) * 4u,
+          buf_store16_wb(rp, (row * (uint32_t)t.N + col) * 4u,
                       __builtin_bit_cast(u32x4, f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                                                       acc[i][j][4 * q + 3]}));
       }
