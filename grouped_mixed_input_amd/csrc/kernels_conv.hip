@@ -243,23 +243,28 @@ struct TapMap {
 };
 
 // out[c][b][a] = in[a][taps(b)][c] for a < A, 0 for A <= a < Ap (in holds
-// Bin taps per a, out Bout): one 64 x 64 (a, c) block of one b per workgroup,
-// moved in 16-byte runs: 8 consecutive c on the way in, 8 consecutive a on
-// the way out (C % 8 == 0, Ap % 8 == 0).  One launch runs a table of such
-// jobs (the filter slices of every phase of a strided data gradient, or x
-// and dy of a weight gradient): grid z walks the jobs' b one after another,
-// and each job ignores the (a, c) blocks past its own extent.
+// Bin taps per a, out Bout): one 64 x 64 (a, c) block per workgroup, moved
+// in 16-byte runs: 8 consecutive c on the way in, 8 consecutive a on the way
+// out (C % 8 == 0, Ap % 8 == 0).  When Ap < 64 a block takes nb = 64 / Ap
+// consecutive b instead of one, so each of its rows is whole (every a of one
+// b) and each c's output run covers nb b: 128 bytes at Ap = 32, a whole
+// line, where one b per block wrote half lines from two workgroups.  One
+// launch runs a table of such jobs (the filter slices of every phase of a
+// strided data gradient, or x and dy of a weight gradient): grid z walks the
+// jobs' b groups one after another, and each job ignores the (a, c) blocks
+// past its own extent.
 constexpr int kMaxTransposeJobs = 16;
 struct TransposeJob {
   const uint16_t* in;
   uint16_t* out;
   int A, Bin, Bout, C, Ap;
   TapMap taps;
-  int z0;  // first b of the job in the launch's walk
+  int nb;  // b per workgroup
+  int z0;  // first b group of the job in the launch's walk
 };
 struct TransposeJobs {
   TransposeJob job[kMaxTransposeJobs];
-  int count, total;  // jobs; sum of their Bout
+  int count, total;  // jobs; sum of their b groups
 };
 static_assert(sizeof(TransposeJobs) <= 4096, "kernel arguments are limited to 4 KB");
 
@@ -273,27 +278,33 @@ __global__ __launch_bounds__(256) void k_transpose_outer(TransposeJobs jobs) {
     const TransposeJob& jb = js[q];
     const int a0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
     if (a0 >= jb.Ap || c0 >= jb.C) continue;  // past this job's extent: the whole workgroup skips alike
-    const int b = z - jb.z0, bi = jb.taps(b);
+    // tile row r: b = b0 + r / ab, a = a0 + r % ab (ab a multiple of 8, so
+    // an 8-row run never spans two b)
+    const int ab = jb.Ap < 64 ? jb.Ap : 64, b0 = (z - jb.z0) * jb.nb;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int aa = row + 32 * j, a = a0 + aa, c = c0 + vec * 8;
+      const int r = row + 32 * j, bl = r / ab, a = a0 + r % ab, b = b0 + bl, c = c0 + vec * 8;
       u32x4 v = {0, 0, 0, 0};
-      if (a < jb.A && c < jb.C) v = *(const u32x4*)(jb.in + ((int64_t)a * jb.Bin + bi) * jb.C + c);
+      if (bl < jb.nb && b < jb.Bout && a < jb.A && c < jb.C)
+        v = *(const u32x4*)(jb.in + ((int64_t)a * jb.Bin + jb.taps(b)) * jb.C + c);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        t[aa][vec * 8 + 2 * e] = (uint16_t)(v[e] & 0xffffu);
-        t[aa][vec * 8 + 2 * e + 1] = (uint16_t)(v[e] >> 16);
+        t[r][vec * 8 + 2 * e] = (uint16_t)(v[e] & 0xffffu);
+        t[r][vec * 8 + 2 * e + 1] = (uint16_t)(v[e] >> 16);
       }
     }
     __syncthreads();
+    {
+      const int r = vec * 8, bl = r / ab, a = a0 + r % ab, b = b0 + bl;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int cc = row + 32 * j, c = c0 + cc, a = a0 + vec * 8;
-      if (c < jb.C && a < jb.Ap) {
-        u32x4 v;
+      for (int j = 0; j < 2; ++j) {
+        const int cc = row + 32 * j, c = c0 + cc;
+        if (bl < jb.nb && b < jb.Bout && c < jb.C && a < jb.Ap) {
+          u32x4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (uint32_t)t[vec * 8 + 2 * e][cc] | ((uint32_t)t[vec * 8 + 2 * e + 1][cc] << 16);
-        *(u32x4*)(jb.out + ((int64_t)c * jb.Bout + b) * jb.Ap + a) = v;
+          for (int e = 0; e < 4; ++e) v[e] = (uint32_t)t[r + 2 * e][cc] | ((uint32_t)t[r + 2 * e + 1][cc] << 16);
+          *(u32x4*)(jb.out + ((int64_t)c * jb.Bout + b) * jb.Ap + a) = v;
+        }
       }
     }
     __syncthreads();
@@ -304,10 +315,12 @@ __global__ __launch_bounds__(256) void k_transpose_outer(TransposeJobs jobs) {
 static hipError_t transpose_jobs(TransposeJobs& jobs, hipStream_t stream) {
   int cmax = 0, amax = 0, z = 0;
   for (int i = 0; i < jobs.count; ++i) {
-    jobs.job[i].z0 = z;
-    z += jobs.job[i].Bout;
-    cmax = jobs.job[i].C > cmax ? jobs.job[i].C : cmax;
-    amax = jobs.job[i].Ap > amax ? jobs.job[i].Ap : amax;
+    TransposeJob& jb = jobs.job[i];
+    jb.nb = jb.Ap < 64 ? 64 / jb.Ap : 1;
+    jb.z0 = z;
+    z += (jb.Bout + jb.nb - 1) / jb.nb;
+    cmax = jb.C > cmax ? jb.C : cmax;
+    amax = jb.Ap > amax ? jb.Ap : amax;
   }
   jobs.total = z;
   if (z == 0) return hipSuccess;
@@ -328,6 +341,7 @@ static TransposeJob transpose_job(const uint16_t* in, uint16_t* out, int A, int 
   j.C = C;
   j.Ap = Ap;
   j.taps = taps;
+  j.nb = 1;
   j.z0 = 0;
   return j;
 }
