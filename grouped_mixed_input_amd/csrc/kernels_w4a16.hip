@@ -676,10 +676,13 @@ struct RsRing {
 // With GK fixed, the group boundaries fall on fixed steps of the unrolled
 // loop: a group's first multiply starts its partial from zero and its last
 // k-tile folds the partial in, with no per-step test and no reset.
+// MT: 16-token tiles multiplied (the X stages always hold the loader's 128
+// rows; a tile of at most 64 tokens multiplies the first four).
 template <int DT, int WB, int MT, int D, int GK = 0>
 __device__ __forceinline__ void rs_mainloop(char* lds, const DenseLoader<RsXCfg, RsXCfg::BM>& xl,
                                             const RsWeights<DT, WB>& wl, int nk, f32x4 (&acc)[WB][MT]) {
-  using Ring = RsRing<DT, WB, MT, D>;
+  using Ring = RsRing<DT, WB, RsXCfg::BM / 16, D>;
+  static_assert(MT >= 1 && MT <= RsXCfg::BM / 16, "the multiplied tiles lie in the X stage");
   constexpr bool EXACT = DT == DT_BF16;
   static_assert(GK == 0 || (EXACT && (D + 1) % GK == 0), "fixed groups align with the unrolled steps");
   constexpr int YOUNG = RsXCfg::NW == 4 ? DenseLoader<RsXCfg, RsXCfg::BM>::P + RsWeights<DT, WB>::LOADS : 0;
@@ -808,14 +811,15 @@ template <int DT, int WB, int MT>
 __device__ __forceinline__ void rs_store(const W4Launch& a, const f32x4 (&acc)[WB][MT], int m0, int n_base,
                                          int tile, int sidx) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  static_assert(4 * WB * MT * 256 == kRsTileFloats, "four waves cover one tile");
-  if (a.split > 1) {
-    float* pt = a.partial + ((int64_t)tile * a.split + sidx) * kRsTileFloats;
+  if constexpr (4 * WB * MT * 256 == kRsTileFloats) {  // whole tiles only: the split partials' layout
+    if (a.split > 1) {
+      float* pt = a.partial + ((int64_t)tile * a.split + sidx) * kRsTileFloats;
 #pragma unroll
-    for (int b = 0; b < WB; ++b)
+      for (int b = 0; b < WB; ++b)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) *(f32x4*)(pt + ((wave * WB + b) * MT + mt) * 256 + 4 * lane) = acc[b][mt];
-    return;
+        for (int mt = 0; mt < MT; ++mt) *(f32x4*)(pt + ((wave * WB + b) * MT + mt) * 256 + 4 * lane) = acc[b][mt];
+      return;
+    }
   }
 #pragma unroll
   for (int b = 0; b < WB; ++b) {
@@ -1023,7 +1027,9 @@ __global__ __launch_bounds__(64 * kGroupedWaves, 4) void k_w4a16_grouped(W4Group
 // decrease, and an empty group shares its successor's).  No LDS beyond the
 // mainloop's, so two workgroups share a CU.  Inside a group the tiles run
 // m-fastest, so the workgroups that share a weight panel run together and
-// find it in L2.
+// find it in L2.  A group's last row tile of at most 64 rows multiplies only
+// its first four 16-token tiles (the same products per token, so the same
+// bits as the whole tile).
 // ---------------------------------------------------------------------------
 constexpr int kGroupedDecodeRows = 32;
 // calls of at most this many rows run every group through the decode body:
@@ -1109,9 +1115,16 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_grouped_tiled(W4Grouped a) {
     xl.init(p.X, p.ldx, m0, rows, p.K);
     RsWeights<DT, WB> wl;
     wl.init(p, n_base, 0);
-    f32x4 acc[WB][MT];
-    rs_mainloop<DT, WB, MT, D, GK>(lds, xl, wl, p.K / 64, acc);
-    rs_store<DT, WB, MT>(p, acc, m0, n_base, 0, 0);
+    if (rows - m0 <= BM / 2) {
+      // a group's last row tile of at most 64 rows: half the tile's multiplies
+      f32x4 acc[WB][MT / 2];
+      rs_mainloop<DT, WB, MT / 2, D, GK>(lds, xl, wl, p.K / 64, acc);
+      rs_store<DT, WB, MT / 2>(p, acc, m0, n_base, 0, 0);
+    } else {
+      f32x4 acc[WB][MT];
+      rs_mainloop<DT, WB, MT, D, GK>(lds, xl, wl, p.K / 64, acc);
+      rs_store<DT, WB, MT>(p, acc, m0, n_base, 0, 0);
+    }
   }
 }
 
