@@ -1138,9 +1138,10 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_grouped_tiled(W4Grouped a) {
 // the bytes of its weight slice, so wider slices halve that traffic); every
 // larger or empty group returns at once.  The second tile's X fragments
 // double the registers a slot holds, so two workgroups share a CU instead of
-// four.
+// four; a two-slot ring (rounds of two k-blocks per wave) measured faster
+// than four slots.
 // ---------------------------------------------------------------------------
-constexpr int kPairBlocks = 4, kPairRing = 4, kPairWgsPerCu = 2;
+constexpr int kPairBlocks = 4, kPairRing = 2, kPairWgsPerCu = 2;
 constexpr int kPairLds = kGroupedWaves * DecodeLds<kPairBlocks, kPairRing>::WAVE;
 
 template <int DT>
