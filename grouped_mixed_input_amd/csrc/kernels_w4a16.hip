@@ -1027,9 +1027,9 @@ __global__ __launch_bounds__(64 * kGroupedWaves, 4) void k_w4a16_grouped(W4Group
 // decrease, and an empty group shares its successor's).  No LDS beyond the
 // mainloop's, so two workgroups share a CU.  Inside a group the tiles run
 // m-fastest, so the workgroups that share a weight panel run together and
-// find it in L2.  A group's last row tile of at most 64 rows multiplies only
-// its first four 16-token tiles (the same products per token, so the same
-// bits as the whole tile).
+// find it in L2.  A group's last row tile multiplies only its 16-token tiles
+// up to the next quarter of the tile that holds rows (2, 4 or 6 of the 8;
+// the same products per token, so the same bits as the whole tile).
 // ---------------------------------------------------------------------------
 constexpr int kGroupedDecodeRows = 32;
 // calls of at most this many rows run every group through the decode body:
@@ -1115,11 +1115,20 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_grouped_tiled(W4Grouped a) {
     xl.init(p.X, p.ldx, m0, rows, p.K);
     RsWeights<DT, WB> wl;
     wl.init(p, n_base, 0);
-    if (rows - m0 <= BM / 2) {
-      // a group's last row tile of at most 64 rows: half the tile's multiplies
+    const int left = rows - m0;
+    if (left <= BM / 4) {
+      // a group's last row tile: only its 16-token tiles that hold rows
+      f32x4 acc[WB][MT / 4];
+      rs_mainloop<DT, WB, MT / 4, D, GK>(lds, xl, wl, p.K / 64, acc);
+      rs_store<DT, WB, MT / 4>(p, acc, m0, n_base, 0, 0);
+    } else if (left <= BM / 2) {
       f32x4 acc[WB][MT / 2];
       rs_mainloop<DT, WB, MT / 2, D, GK>(lds, xl, wl, p.K / 64, acc);
       rs_store<DT, WB, MT / 2>(p, acc, m0, n_base, 0, 0);
+    } else if (left <= 3 * BM / 4) {
+      f32x4 acc[WB][3 * MT / 4];
+      rs_mainloop<DT, WB, 3 * MT / 4, D, GK>(lds, xl, wl, p.K / 64, acc);
+      rs_store<DT, WB, 3 * MT / 4>(p, acc, m0, n_base, 0, 0);
     } else {
       f32x4 acc[WB][MT];
       rs_mainloop<DT, WB, MT, D, GK>(lds, xl, wl, p.K / 64, acc);
