@@ -268,9 +268,15 @@ struct TransposeJobs {
 };
 static_assert(sizeof(TransposeJobs) <= 4096, "kernel arguments are limited to 4 KB");
 
+// In LDS the block is held as 32-bit pairs of rows: word (c, p) packs rows
+// 2p and 2p + 1 of column c (one v_perm per word on the way in), so a
+// column's 8 consecutive rows are one 16-byte read on the way out.  Column c
+// holds its 32 words in 16-byte groups whose order is XOR-ed with c / 8: the
+// 8 writes of an instruction touch each bank at most twice, and a read
+// instruction's 16-lane groups (8 row groups of 2 columns) none twice.
 __global__ __launch_bounds__(256) void k_transpose_outer(TransposeJobs jobs) {
-  __shared__ uint16_t t[64][72];
-  const int row = threadIdx.x / 8, vec = threadIdx.x % 8;
+  __shared__ __attribute__((aligned(16))) uint32_t t[64 * 32];
+  const int hi = threadIdx.x / 8, lo = threadIdx.x % 8;
   const TransposeJob* js = jobs.job;
   for (int z = blockIdx.z; z < jobs.total; z += gridDim.z) {
     int q = 0;
@@ -278,33 +284,33 @@ __global__ __launch_bounds__(256) void k_transpose_outer(TransposeJobs jobs) {
     const TransposeJob& jb = js[q];
     const int a0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
     if (a0 >= jb.Ap || c0 >= jb.C) continue;  // past this job's extent: the whole workgroup skips alike
-    // tile row r: b = b0 + r / ab, a = a0 + r % ab (ab a multiple of 8, so
+    // block row r: b = b0 + r / ab, a = a0 + r % ab (ab a multiple of 8, so
     // an 8-row run never spans two b)
     const int ab = jb.Ap < 64 ? jb.Ap : 64, b0 = (z - jb.z0) * jb.nb;
+    {
+      // rows 2 hi and 2 hi + 1, columns 8 lo .. 8 lo + 7
+      u32x4 v[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = row + 32 * j, bl = r / ab, a = a0 + r % ab, b = b0 + bl, c = c0 + vec * 8;
-      u32x4 v = {0, 0, 0, 0};
-      if (bl < jb.nb && b < jb.Bout && a < jb.A && c < jb.C)
-        v = *(const u32x4*)(jb.in + ((int64_t)a * jb.Bin + jb.taps(b)) * jb.C + c);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        t[r][vec * 8 + 2 * e] = (uint16_t)(v[e] & 0xffffu);
-        t[r][vec * 8 + 2 * e + 1] = (uint16_t)(v[e] >> 16);
+      for (int h = 0; h < 2; ++h) {
+        const int r = 2 * hi + h, bl = r / ab, a = a0 + r % ab, b = b0 + bl, c = c0 + lo * 8;
+        v[h] = u32x4{0, 0, 0, 0};
+        if (bl < jb.nb && b < jb.Bout && a < jb.A && c < jb.C)
+          v[h] = *(const u32x4*)(jb.in + ((int64_t)a * jb.Bin + jb.taps(b)) * jb.C + c);
       }
+      const int slot = (((hi >> 2) ^ lo) << 2) + (hi & 3);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)  // column 8 lo + k: the two rows' element k
+        t[(lo * 8 + k) * 32 + slot] = __builtin_amdgcn_perm(v[1][k / 2], v[0][k / 2], k % 2 ? 0x07060302u : 0x05040100u);
     }
     __syncthreads();
     {
-      const int r = vec * 8, bl = r / ab, a = a0 + r % ab, b = b0 + bl;
+      // rows 8 lo .. 8 lo + 7 of columns hi and hi + 32
+      const int r = lo * 8, bl = r / ab, a = a0 + r % ab, b = b0 + bl;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int cc = row + 32 * j, c = c0 + cc;
-        if (bl < jb.nb && b < jb.Bout && c < jb.C && a < jb.Ap) {
-          u32x4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (uint32_t)t[r + 2 * e][cc] | ((uint32_t)t[r + 2 * e + 1][cc] << 16);
-          *(u32x4*)(jb.out + ((int64_t)c * jb.Bout + b) * jb.Ap + a) = v;
-        }
+        const int cc = hi + 32 * j, c = c0 + cc;
+        if (bl < jb.nb && b < jb.Bout && c < jb.C && a < jb.Ap)
+          *(u32x4*)(jb.out + ((int64_t)c * jb.Bout + b) * jb.Ap + a) = *(const u32x4*)(t + cc * 32 + ((lo ^ (cc >> 3)) << 2));
       }
     }
     __syncthreads();
