@@ -1027,9 +1027,10 @@ __global__ __launch_bounds__(64 * kGroupedWaves, 4) void k_w4a16_grouped(W4Group
 // decrease, and an empty group shares its successor's).  No LDS beyond the
 // mainloop's, so two workgroups share a CU.  Inside a group the tiles run
 // m-fastest, so the workgroups that share a weight panel run together and
-// find it in L2.  A group's last row tile multiplies only its 16-token tiles
-// up to the next quarter of the tile that holds rows (2, 4 or 6 of the 8;
-// the same products per token, so the same bits as the whole tile).
+// find it in L2.  A group's last row tile of at most 64 (96) rows multiplies
+// only its first 4 (6) 16-token tiles (the same products per token, so the
+// same bits as the whole tile; a quarter-tile body as well measured slower,
+// its registers spilling).
 // ---------------------------------------------------------------------------
 constexpr int kGroupedDecodeRows = 32;
 // calls of at most this many rows run every group through the decode body:
@@ -1116,12 +1117,9 @@ __global__ __launch_bounds__(256, 2) void k_w4a16_grouped_tiled(W4Grouped a) {
     RsWeights<DT, WB> wl;
     wl.init(p, n_base, 0);
     const int left = rows - m0;
-    if (left <= BM / 4) {
-      // a group's last row tile: only its 16-token tiles that hold rows
-      f32x4 acc[WB][MT / 4];
-      rs_mainloop<DT, WB, MT / 4, D, GK>(lds, xl, wl, p.K / 64, acc);
-      rs_store<DT, WB, MT / 4>(p, acc, m0, n_base, 0, 0);
-    } else if (left <= BM / 2) {
+    if (left <= BM / 2) {
+      // a group's last row tile: only its 16-token tiles up to the half or
+      // three quarters that hold rows
       f32x4 acc[WB][MT / 2];
       rs_mainloop<DT, WB, MT / 2, D, GK>(lds, xl, wl, p.K / 64, acc);
       rs_store<DT, WB, MT / 2>(p, acc, m0, n_base, 0, 0);

@@ -133,9 +133,9 @@ def test_mixed_grouped_groups_are_independent(gmi):
                                                ("bf16", "uint4", "scale"), ("f16", "int4", "direct")])
 def test_mixed_grouped_prefill_groups_tiled(gmi, dtype, w_type, mode):
     # groups above 32 rows run the tiled launch (128 x 128 tiles, ragged in rows and in N; a last row tile
-    # multiplies only the 16-token tiles up to the next quarter of the tile that holds rows: 1 of 129 and
-    # of 513 a quarter, 33, 44 of 300 and 64 half, 80 and 72 of 200 three quarters, 100 all), the others
-    # the two-tile decode launch, in one call; empty groups between them
+    # of at most 64 rows -- 1 of 129 and of 513, 33, 44 of 300, 64 -- multiplies half the tile, one of at
+    # most 96 rows -- 80, 72 of 200 -- three quarters, 100 all of it), the others the two-tile decode
+    # launch, in one call; empty groups between them
     counts = np.array([0, 3, 32, 33, 0, 300, 129, 1, 513, 16, 17, 64, 80, 200, 100])
     N, K, group = 320, 512, 128
     rows = int(counts.sum()) + 7
