@@ -677,7 +677,7 @@ struct RsRing {
 // loop: a group's first multiply starts its partial from zero and its last
 // k-tile folds the partial in, with no per-step test and no reset.
 // MT: 16-token tiles multiplied (the X stages always hold the loader's 128
-// rows; a tile of at most 64 tokens multiplies the first four).
+// rows; a shortened last tile multiplies only the first MT of them).
 template <int DT, int WB, int MT, int D, int GK = 0>
 __device__ __forceinline__ void rs_mainloop(char* lds, const DenseLoader<RsXCfg, RsXCfg::BM>& xl,
                                             const RsWeights<DT, WB>& wl, int nk, f32x4 (&acc)[WB][MT]) {
@@ -811,7 +811,9 @@ template <int DT, int WB, int MT>
 __device__ __forceinline__ void rs_store(const W4Launch& a, const f32x4 (&acc)[WB][MT], int m0, int n_base,
                                          int tile, int sidx) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if constexpr (4 * WB * MT * 256 == kRsTileFloats) {  // whole tiles only: the split partials' layout
+  // whole tiles only have the split partials' layout (shortened tiles come
+  // from the grouped launch, which never splits)
+  if constexpr (4 * WB * MT * 256 == kRsTileFloats) {
     if (a.split > 1) {
       float* pt = a.partial + ((int64_t)tile * a.split + sidx) * kRsTileFloats;
 #pragma unroll
