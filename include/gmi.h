@@ -198,7 +198,7 @@ size_t gmi_w4a16_workspace_bytes(int32_t M, int32_t N, int32_t K);
  * "convert, scale, add zero" of machete_mainloop.cuh (ConversionMode
  * ConvertAndScaleWithZero; scale_k = ceil(K / group_size) from
  * to_underlying_arguments; transform_A_kblock).  The zero point is read here
- * as an unsigned 4-bit offset subtracted before scaling.  For M <= 32 the
+ * as an unsigned 4-bit offset subtracted before scaling.  For M <= 48 the
  * matrix instruction takes the exact integers q - z (fp16) and each group's
  * scale multiplies the fp32 partial sum over that group; otherwise each
  * weight is dequantised to fp16 as RN16((q - z) * s) and multiplied in fp16.
@@ -241,11 +241,11 @@ typedef enum { GMI_W4_UINT4 = 0, GMI_W4_INT4 = 1 } gmi_w4_type;
  *                (the page's fp16 and bf16 activation / scale types).
  *   group_size   as for gmi_gemm_w4a16; ignored when scales == NULL.
  *   other arguments, layouts, workspace and errors as for gmi_gemm_w4a16.
- * Numerics: with bf16 activations, and with fp16 for M <= 32, the matrix
+ * Numerics: with bf16 activations, and with fp16 for M <= 48, the matrix
  * instruction takes exact integer weights and the scale multiplies each
  * group's fp32 partial sum: v(q) - v(z) (for the bf16 decode kernel the
  * offset-binary nibble plus 128, with (128 + zero point) times the group's
- * activation sum taken off that partial sum).  fp16 with M > 32 rounds every
+ * activation sum taken off that partial sum).  fp16 with M > 48 rounds every
  * weight first, RN16((v(q) - v(z)) * s), as the page does.  fp32
  * accumulation; Y is rounded to nearest even. */
 gmi_status gmi_gemm_mixed(int32_t M, int32_t N, int32_t K, gmi_dtype x_dtype, const void* X, int64_t ldx,
@@ -272,9 +272,9 @@ gmi_status gmi_gemm_mixed(int32_t M, int32_t N, int32_t K, gmi_dtype x_dtype, co
  *            (K/group)*N scales, (K/group)*N/2 zero bytes) and keeping every
  *            group's data 16-byte aligned; ignored for a NULL array.
  * Modes, types and layouts as for gmi_gemm_mixed.  By default a group runs
- * 16 rows at a time through the M <= 32 kernel body (exact integer weights
+ * 16 rows at a time through the decode kernel body (exact integer weights
  * into the matrix instruction, each group's scale on the fp32 partial sums,
- * as gmi_gemm_mixed does for M <= 32).  When count <= 1024 and rows > 256, groups of at most 32
+ * as gmi_gemm_mixed does for M <= 48).  When count <= 1024 and rows > 256, groups of at most 32
  * rows instead run the same body over both 16-row tiles at once (each weight
  * streamed once; the same bits), and larger groups a second launch over
  * their 128 x 128 output tiles through the tiled mainloop (each weight

@@ -1,6 +1,6 @@
 """GPU parity of the mixed-input GEMM in every conversion mode (direct, scale,
 scale with zero point), for uint4 and int4 weights and fp16 and bf16
-activations, against the fp64 oracle.  The decode (M <= 32: one or two 16-row
+activations, against the fp64 oracle.  The decode (M <= 48: one to three 16-row
 tiles), skinny (M <= 64) and tiled (larger M, also split over K) kernels are
 each covered.
 
@@ -115,7 +115,7 @@ def test_mixed_f16_uint4_zero_mode_is_w4a16_bit_for_bit(gmi):
 
 @pytest.mark.parametrize("M", [16, 48, 128, 1024])
 def test_mixed_bf16_full_size_sampled(gmi, M):
-    # N = K = 8192, group 128, int4 with zero points: the decode kernel (M = 16), the skinny kernel (M = 48),
+    # N = K = 8192, group 128, int4 with zero points: the decode kernel (M = 16; M = 48 as three 16-row tiles),
     # the tiled path split over K into fp32 partials (M = 128: 64 output tiles) and unsplit (M = 1024); the
     # oracle on 24 sampled output columns.  Over K = 8192 terms, weights rounded to bf16 would miss the bar on
     # some outputs of this size; the exact integer weights do not.

@@ -38,7 +38,7 @@ def _w4_run(gmi, d, ldy_pad=0):
     return out.bits()
 
 
-@pytest.mark.parametrize("M", [1, 5, 16, 17, 33, 64, 65, 128, 200, 257])
+@pytest.mark.parametrize("M", [1, 5, 16, 17, 33, 48, 49, 64, 65, 128, 200, 257])
 def test_w4a16_shapes(gmi, M):
     d = gi.w4a16(seed=M, M=M, N=512, K=1024, group=128)
     got = _w4_run(gmi, d, ldy_pad=8)
