@@ -70,9 +70,10 @@ def test_w4a16_exact_small_integers(gmi, M):
     assert np.array_equal(_w4_run(gmi, d), oracle.round_to(ref, "f16"))
 
 
-@pytest.mark.parametrize("M", [16, 128, 1024, 4096])
+@pytest.mark.parametrize("M", [16, 48, 128, 1024, 4096])
 def test_workload4_full_size(gmi, M):
-    # N = K = 8192, g = 128: all rows checked for M = 16, 32 sampled rows otherwise
+    # N = K = 8192, g = 128: all rows checked for M = 16, 32 sampled rows otherwise (M = 48 runs the decode
+    # body over three token tiles)
     d = gi.w4a16(M=M)
     got = _w4_run(gmi, d)
     rows = np.arange(M) if M <= 16 else np.random.default_rng(M).choice(M, 32, replace=False)
